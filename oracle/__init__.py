@@ -1,0 +1,207 @@
+"""float64 CPU oracle for the ReplaySSM Mamba-2 decode step -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import this package. The GPU
+library and its Python binding never import it; the two share no code. Inputs are the exact fp32
+values the GPU sees; every result is float64.
+
+Functions (all arrays numpy, C-contiguous):
+  step(S, x, B, C, dt, A, D) -> y              O1, one token, S (float64) updated in place
+  spec_stepwise(S, T, x, B, C, dt, A, D, acc)  O5, the per-draft definition of spec decoding
+  Replay(...)                                  O3 + O4, the replay form and its pointer machine
+  bf16_encode / e4m3_encode_tiles / e4m3_encode_at / e4m3_decode / bf16_decode    O7
+
+Pinning (what each function is checked against, independent of itself) is in tests/test_oracle_*.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+_u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+def lib():
+    """Load liboracle.so, building it first if it is missing or older than its source."""
+    global _lib
+    if _lib is None:
+        src = os.path.join(_HERE, "oracle.c")
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+            _build.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_step.argtypes = [_i] * 5 + [_f64p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f64p]
+        L.oracle_step.restype = None
+        L.oracle_spec_stepwise.argtypes = [_i] * 6 + [_f64p, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                                      _f32p, _i32p, _f64p]
+        L.oracle_spec_stepwise.restype = _i
+        L.oracle_bf16_encode.argtypes = [ctypes.c_float]
+        L.oracle_bf16_encode.restype = ctypes.c_uint16
+        L.oracle_encode_bf16.argtypes = [_f32p, _u16p, _sz]
+        L.oracle_encode_e4m3_tiles.argtypes = [_f32p, _u8p, _f32p, _sz, _sz]
+        L.oracle_encode_e4m3_at.argtypes = [_f32p, _u8p, _sz, ctypes.c_float]
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = ctypes.c_float
+        L.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_decode.restype = ctypes.c_float
+        L.oracle_replay_create.argtypes = [_i] * 8 + [_f32p, _f32p, _f32p]
+        L.oracle_replay_create.restype = ctypes.c_void_p
+        L.oracle_replay_destroy.argtypes = [ctypes.c_void_p]
+        L.oracle_replay_step.argtypes = [ctypes.c_void_p, _f32p, _f32p, _f32p, _f32p, _f64p]
+        L.oracle_replay_step.restype = _i
+        L.oracle_replay_verify.argtypes = [ctypes.c_void_p, _i, _f32p, _f32p, _f32p, _f32p, _f64p]
+        L.oracle_replay_verify.restype = _i
+        L.oracle_replay_rollback.argtypes = [ctypes.c_void_p, _i32p]
+        L.oracle_replay_rollback.restype = _i
+        L.oracle_replay_flush.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_replay_flush.restype = _i
+        L.oracle_replay_pointers.argtypes = [ctypes.c_void_p, _i32p, _i32p]
+        L.oracle_replay_checkpoint.argtypes = [ctypes.c_void_p, _f64p]
+        L.oracle_replay_read_copy.argtypes = [ctypes.c_void_p, _f64p]
+        L.oracle_replay_materialize.argtypes = [ctypes.c_void_p, _f64p]
+        L.oracle_threads.restype = _i
+        _lib = L
+    return _lib
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS or the cores available)."""
+    return int(lib().oracle_threads())
+
+
+def step(S, x, B, C, dt, A, D):
+    """O1 for one token. S: float64 [Bt,H,P,N], updated in place. Returns y float64 [Bt,H,P]."""
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    Bt, H, P, N = S.shape
+    G = B.shape[1]
+    y = np.empty((Bt, H, P), np.float64)
+    lib().oracle_step(Bt, H, P, N, G, S, _f32(x), _f32(B), _f32(C), _f32(dt), _f32(A), _f32(D), y)
+    return y
+
+
+def spec_stepwise(S, T, x, B, C, dt, A, D, accepted):
+    """O5: all T draft outputs from the committed state S (float64, updated to the accepted
+    prefix). Inputs carry the draft index second: x [Bt,T,H,P], B/C [Bt,T,G,N], dt [Bt,T,H]."""
+    Bt, H, P, N = S.shape
+    G = B.shape[2]
+    y = np.empty((Bt, T, H, P), np.float64)
+    acc = np.ascontiguousarray(accepted, dtype=np.int32)
+    rc = lib().oracle_spec_stepwise(Bt, H, P, N, G, T, S, _f32(x), _f32(B), _f32(C), _f32(dt),
+                                    _f32(A), _f32(D), acc, y)
+    if rc != 0:
+        raise ValueError("accepted count outside [0, T]")
+    return y
+
+
+READ_FP32, READ_BF16, READ_FP8 = 0, 1, 2
+
+
+class Replay:
+    """O3 + O4: the replay form (checkpoint + records) with its pointer and flush machine."""
+
+    def __init__(self, S0, A, D, G, L, Tmax=1, read_prec=READ_FP32):
+        S0 = _f32(S0)
+        self.Bt, self.H, self.P, self.N = S0.shape
+        self.G, self.L, self.Tmax = G, L, Tmax
+        self._h = lib().oracle_replay_create(self.Bt, self.H, self.P, self.N, G, L, Tmax,
+                                             read_prec, S0, _f32(A), _f32(D))
+        if not self._h:
+            raise ValueError("invalid replay configuration")
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            lib().oracle_replay_destroy(self._h)
+            self._h = None
+
+    def step(self, x, B, C, dt):
+        y = np.empty((self.Bt, self.H, self.P), np.float64)
+        if lib().oracle_replay_step(self._h, _f32(x), _f32(B), _f32(C), _f32(dt), y) != 0:
+            raise RuntimeError("oracle replay: step rejected by the state machine")
+        return y
+
+    def verify(self, T, x, B, C, dt):
+        y = np.empty((self.Bt, T, self.H, self.P), np.float64)
+        if lib().oracle_replay_verify(self._h, T, _f32(x), _f32(B), _f32(C), _f32(dt), y) != 0:
+            raise RuntimeError("oracle replay: verify rejected by the state machine")
+        return y
+
+    def rollback(self, accepted):
+        acc = np.ascontiguousarray(accepted, dtype=np.int32)
+        if lib().oracle_replay_rollback(self._h, acc) != 0:
+            raise RuntimeError("oracle replay: rollback rejected by the state machine")
+
+    def flush(self, seq_mask=None):
+        if seq_mask is None:
+            rc = lib().oracle_replay_flush(self._h, None)
+        else:
+            m = np.ascontiguousarray(seq_mask, dtype=np.int32)
+            rc = lib().oracle_replay_flush(self._h, m.ctypes.data_as(ctypes.c_void_p))
+        if rc != 0:
+            raise RuntimeError("oracle replay: flush rejected by the state machine")
+
+    def pointers(self):
+        pos = np.empty(self.Bt, np.int32)
+        ck = np.empty(self.Bt, np.int32)
+        lib().oracle_replay_pointers(self._h, pos, ck)
+        return pos, ck
+
+    def _state(self, fn):
+        out = np.empty((self.Bt, self.H, self.P, self.N), np.float64)
+        fn(self._h, out)
+        return out
+
+    def checkpoint(self):
+        return self._state(lib().oracle_replay_checkpoint)
+
+    def read_copy(self):
+        return self._state(lib().oracle_replay_read_copy)
+
+    def materialize(self):
+        return self._state(lib().oracle_replay_materialize)
+
+
+def bf16_encode(a):
+    a = _f32(a)
+    out = np.empty(a.shape, np.uint16)
+    lib().oracle_encode_bf16(a.reshape(-1), out.reshape(-1), a.size)
+    return out
+
+
+def bf16_decode(codes):
+    return (np.asarray(codes, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_encode_tiles(a, tile_elems):
+    """Per-tile scaled e4m3 encode (read-copy reading R6). Returns (codes uint8, scales f32)."""
+    a = _f32(a).reshape(-1)
+    ntiles = a.size // tile_elems
+    codes = np.empty(a.size, np.uint8)
+    scales = np.empty(ntiles, np.float32)
+    lib().oracle_encode_e4m3_tiles(a, codes, scales, ntiles, tile_elems)
+    return codes, scales
+
+
+def e4m3_encode_at(a, inv_scale=1.0):
+    a = _f32(a)
+    out = np.empty(a.shape, np.uint8)
+    lib().oracle_encode_e4m3_at(a.reshape(-1), out.reshape(-1), a.size, float(inv_scale))
+    return out
+
+
+def e4m3_decode_table():
+    """float32 value of each of the 256 codes (NaN for the two NaN codes)."""
+    return np.array([lib().oracle_e4m3_decode(c) for c in range(256)], np.float32)

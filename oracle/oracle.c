@@ -1,0 +1,558 @@
+/*
+ * oracle.c -- float64 CPU oracle for the ReplaySSM Mamba-2 decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY. The test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark are the only code that loads this library. The GPU library never links it, includes
+ * nothing from it and shares no source with it; the two meet only in the tests, which feed both
+ * the same seeded fp32 inputs.
+ *
+ * Sources. The method is described in prose by three web pages; nothing below copies code from
+ * anywhere (the pages print none):
+ *   [AT Pulse]   "NVIDIA and Princeton's ReplaySSM stores a checkpoint and recent inputs instead of
+ *                full SSM state to speed up hybrid-model decoding" (at-pulse.com, story 2558)
+ *   [Clarity]    "NVIDIA and Princeton cache SSM inputs in place of state to speed hybrid-model
+ *                decoding" (theclarity.today)
+ *   [WittyWires] "ReplaySSM cuts memory traffic to speed up hybrid-model decoding"
+ *                (wittywires.com forums)
+ *
+ * The pages print no formulas. What is computed here is the plain Mamba-2 reading of their prose;
+ * each reading is stated where it is used:
+ *   R1  update, then read: the output of token t already includes token t ([Clarity] "Why it
+ *       matters" and claim ledger [6]: a conventional step updates the state, reads the output
+ *       from it and stores it).
+ *   R2  the flush happens on the step whose append fills the buffer, and that step's output is
+ *       read from the folded state ([WittyWires] "What happened": the checkpoint is updated when
+ *       the buffer fills; [AT Pulse] "Technical analysis": a flush every L steps).
+ *   R3  a record is (x, B, C, dt); replay and flush read x, B and dt of stored records. The pages
+ *       call the record "(decay, value, key)": decay <-> dt*A, value <-> x, key <-> B, query <-> C.
+ *   R4  dt arrives positive (softplus applied by the caller); A and D are scalars per head;
+ *       head h uses group g(h) = h / (H/G).
+ *   R5  spec-decode buffer capacity is L; after a commit the layer flushes when more than L - T
+ *       records are pending, so T drafts always fit; with T = 1 this is rule R2.
+ *   R6  read copy: bf16 by round-to-nearest-even, or OCP fp8 E4M3FN with one fp32 scale per
+ *       (sequence, head) = amax/448 (1 when amax is 0), values multiplied by 1/scale in fp32,
+ *       clamped to +-448 and rounded to nearest even. It is written from the master when a state
+ *       is loaded and at every flush, never otherwise.
+ *
+ * Layouts (row-major, last index fastest): x [Bt,H,P]; B, C [Bt,G,N]; dt [Bt,H]; A, D [H];
+ * state [Bt,H,P,N]; y [Bt,H,P]. Spec-decode inputs carry the draft index after the batch index:
+ * x [Bt,T,H,P]; B, C [Bt,T,G,N]; dt [Bt,T,H]; y [Bt,T,H,P].
+ *
+ * All arithmetic is float64 on the exact fp32 input values, with libm exp.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------------------------- */
+/* O1: the stepwise Mamba-2 recurrence (the truth).                                             */
+/* For one token and every (b, h, p, n), with a = exp(dt*A_h):                                 */
+/*     S[p,n] <- a*S[p,n] + dt * x[p] * B[n]       (state update)                              */
+/*     y[p]    = sum_n S[p,n]*C[n] + D_h*x[p]      (read from the updated state, reading R1)   */
+/* [Clarity] claim ledger [6] and "Why it matters": the conventional step updates, reads and   */
+/* stores the state in one pass.                                                               */
+/* ------------------------------------------------------------------------------------------- */
+void oracle_step(int Bt, int H, int P, int N, int G, double *S, const float *x, const float *B,
+                 const float *C, const float *dt, const float *A, const float *D, double *y)
+{
+    const int hpg = H / G;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < Bt; ++b) {
+        for (int h = 0; h < H; ++h) {
+            const int g = h / hpg;
+            const double dtv = (double)dt[(size_t)b * H + h];
+            const double a = exp(dtv * (double)A[h]);
+            const float *xb = x + ((size_t)b * H + h) * P;
+            const float *Bb = B + ((size_t)b * G + g) * N;
+            const float *Cb = C + ((size_t)b * G + g) * N;
+            double *Sb = S + ((size_t)b * H + h) * (size_t)P * N;
+            double *yb = y + ((size_t)b * H + h) * P;
+            for (int p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    double s = a * Sb[(size_t)p * N + n] + dtv * (double)xb[p] * (double)Bb[n];
+                    Sb[(size_t)p * N + n] = s;
+                    acc += s * (double)Cb[n];
+                }
+                yb[p] = acc + (double)D[h] * (double)xb[p];
+            }
+        }
+    }
+}
+
+/* O5: speculative decoding by the plain definition. From the committed state, the T drafts are */
+/* run one by one with O1; all T outputs are produced (rejected drafts included), and the       */
+/* committed state becomes the state after the first accepted[b] drafts. This is the per-draft  */
+/* snapshot method of [Clarity] claim ledger [13], carried out in float64.                      */
+/* Returns 0, or -1 when an accepted count lies outside [0, T].                                 */
+int oracle_spec_stepwise(int Bt, int H, int P, int N, int G, int T, double *S, const float *x,
+                         const float *B, const float *C, const float *dt, const float *A,
+                         const float *D, const int *accepted, double *y)
+{
+    for (int b = 0; b < Bt; ++b)
+        if (accepted[b] < 0 || accepted[b] > T) return -1;
+    const size_t tile = (size_t)P * N;
+    const size_t seq_state = (size_t)H * tile;
+    double *work = (double *)malloc(seq_state * sizeof(double));
+    float *xs = (float *)malloc((size_t)H * P * sizeof(float));
+    float *Bs = (float *)malloc((size_t)G * N * sizeof(float));
+    float *Cs = (float *)malloc((size_t)G * N * sizeof(float));
+    float *ds = (float *)malloc((size_t)H * sizeof(float));
+    double *ys = (double *)malloc((size_t)H * P * sizeof(double));
+    for (int b = 0; b < Bt; ++b) {
+        memcpy(work, S + b * seq_state, seq_state * sizeof(double));
+        for (int i = 0; i < T; ++i) {
+            memcpy(xs, x + ((size_t)b * T + i) * H * P, (size_t)H * P * sizeof(float));
+            memcpy(Bs, B + ((size_t)b * T + i) * G * N, (size_t)G * N * sizeof(float));
+            memcpy(Cs, C + ((size_t)b * T + i) * G * N, (size_t)G * N * sizeof(float));
+            memcpy(ds, dt + ((size_t)b * T + i) * H, (size_t)H * sizeof(float));
+            oracle_step(1, H, P, N, G, work, xs, Bs, Cs, ds, A, D, ys);
+            memcpy(y + ((size_t)b * T + i) * H * P, ys, (size_t)H * P * sizeof(double));
+            if (i + 1 == accepted[b]) memcpy(S + b * seq_state, work, seq_state * sizeof(double));
+        }
+    }
+    free(work); free(xs); free(Bs); free(Cs); free(ds); free(ys);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------- */
+/* O7: read-copy quantizers, written from the format definitions.                               */
+/* ------------------------------------------------------------------------------------------- */
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* bf16 keeps the top 16 bits of an fp32 value. Round to nearest, ties to the even 16-bit code:  */
+/* the dropped low half is compared with one half of the kept unit. NaN is out of contract.     */
+uint16_t oracle_bf16_encode(float f)
+{
+    uint32_t u = f32_bits(f);
+    uint32_t kept = u >> 16, dropped = u & 0xFFFFu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u; /* may carry into */
+    return (uint16_t)kept;                                             /* the exponent: correct */
+}
+
+float oracle_bf16_decode(uint16_t v) { return bits_f32((uint32_t)v << 16); }
+
+/* OCP FP8 E4M3FN: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is   */
+/* subnormal (value m * 2^-9); no infinities; S.1111.111 is NaN, so the largest finite value is */
+/* 1.75 * 2^8 = 448.                                                                             */
+float oracle_e4m3_decode(uint8_t code)
+{
+    int sign = code >> 7, e = (code >> 3) & 0xF, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return (float)(sign ? -mag : mag);
+}
+
+/* Encode an fp32 value already divided by the scale: clamp to +-448, then round to the nearest  */
+/* representable magnitude with ties to the even code. Within one binade [2^e, 2^(e+1)) the      */
+/* codes are spaced 2^(e-3) apart; below 2^-6 the spacing is the subnormal step 2^-9. The        */
+/* quotient |v| / spacing is exact in float64, and rint() rounds it to nearest even.             */
+uint8_t oracle_e4m3_encode_scaled(float v)
+{
+    double t = (double)v;
+    int sign = t < 0.0 || (t == 0.0 && signbit(t));
+    double mag = fabs(t);
+    if (mag > 448.0) mag = 448.0;
+    int e;
+    if (mag < ldexp(1.0, -6)) {
+        e = -6; /* subnormal range shares the spacing of the lowest binade */
+    } else {
+        e = (int)floor(log2(mag));
+        if (ldexp(1.0, e) > mag) e -= 1;      /* guard log2 rounding at binade edges */
+        if (ldexp(1.0, e + 1) <= mag) e += 1;
+    }
+    double spacing = ldexp(1.0, e - 3);
+    double k = rint(mag / spacing);           /* round half to even on the multiple */
+    double q = k * spacing;                   /* may reach 2^(e+1): the next binade's first code */
+    /* convert the quantized magnitude to a code */
+    uint8_t code;
+    if (q < ldexp(1.0, -6)) {
+        code = (uint8_t)(int)(q / ldexp(1.0, -9));               /* subnormal: m = q / 2^-9 */
+    } else {
+        int qe = (int)floor(log2(q));
+        if (ldexp(1.0, qe) > q) qe -= 1;
+        if (ldexp(1.0, qe + 1) <= q) qe += 1;
+        int m = (int)(q / ldexp(1.0, qe - 3)) - 8;
+        code = (uint8_t)(((qe + 7) << 3) | m);
+    }
+    return (uint8_t)(code | (sign ? 0x80 : 0));
+}
+
+/* Per-(sequence, head) scale for the fp8 read copy (reading R6): scale = amax / 448 in fp32,    */
+/* or 1 when amax is 0; codes are RNE(clamp(S * (1/scale))) with the product taken in fp32.    */
+float oracle_e4m3_scale(const float *tile, size_t n)
+{
+    float amax = 0.0f;
+    for (size_t i = 0; i < n; ++i) {
+        float a = fabsf(tile[i]);
+        if (a > amax) amax = a;
+    }
+    return amax == 0.0f ? 1.0f : amax / 448.0f;
+}
+
+void oracle_encode_bf16(const float *in, uint16_t *out, size_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (size_t i = 0; i < n; ++i) out[i] = oracle_bf16_encode(in[i]);
+}
+
+/* Encode ntiles tiles of tile_elems values each with the per-tile scale. */
+void oracle_encode_e4m3_tiles(const float *in, uint8_t *out, float *scale, size_t ntiles,
+                              size_t tile_elems)
+{
+#pragma omp parallel for schedule(static)
+    for (size_t t = 0; t < ntiles; ++t) {
+        const float *tl = in + t * tile_elems;
+        float s = oracle_e4m3_scale(tl, tile_elems);
+        float inv = 1.0f / s;
+        scale[t] = s;
+        for (size_t i = 0; i < tile_elems; ++i)
+            out[t * tile_elems + i] = oracle_e4m3_encode_scaled(tl[i] * inv);
+    }
+}
+
+/* Element-wise e4m3 encode at a given inverse scale (used by the quantizer pins). */
+void oracle_encode_e4m3_at(const float *in, uint8_t *out, size_t n, float inv)
+{
+#pragma omp parallel for schedule(static)
+    for (size_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode_scaled(in[i] * inv);
+}
+
+/* ------------------------------------------------------------------------------------------- */
+/* O3 + O4: the replay form with its pointer and flush state machine.                           */
+/*                                                                                             */
+/* [AT Pulse] "Technical analysis": the recurrence is unrolled over a window of L tokens; most  */
+/* steps form the output from the checkpoint plus the buffered records and store only the new  */
+/* record; a flush every L steps folds the buffer into the checkpoint; rolling back rejected    */
+/* drafts is a move of the buffer pointer. [Clarity] claim ledger [17], [18]: over a window the */
+/* state is a checkpoint plus a small buffer of recent input records; non-flush steps append    */
+/* and compute the output without storing a state.                                             */
+/*                                                                                             */
+/* Unrolling O1 from the checkpoint S_c (all tokens before c folded) over records c..t gives,   */
+/* per (b, h), with g = g(h):                                                                   */
+/*     decay_t = exp(A_h * sum_{i=c..t} dt_i)                                                   */
+/*     w_j     = dt_j * exp(A_h * sum_{i=j+1..t} dt_i)              (so w_t = dt_t)            */
+/*     y_t[p]  = decay_t * (S_c[p,:] . C_t) + sum_{j=c..t} w_j * (B_j . C_t) * x_j[p]            */
+/*               + D_h * x_t[p]                                                                 */
+/*     fold:     S_c <- decay_t * S_c + sum_{j=c..t} w_j * x_j (outer) B_j ;  c <- t + 1        */
+/*                                                                                             */
+/* Pointers per sequence: pos = tokens committed, ckpt_pos = tokens folded into S_c;           */
+/* count = pos - ckpt_pos, always in [0, L - Tmax] between calls (readings R2, R5).            */
+/* Records are kept by their offset from ckpt_pos (not as a ring): the record of absolute      */
+/* position q sits at index q - ckpt_pos. Unused entries hold NaN so a stray read shows up.    */
+/* ------------------------------------------------------------------------------------------- */
+
+typedef struct oracle_replay {
+    int Bt, H, P, N, G, L, Tmax, read_prec; /* read_prec: 0 fp32 master, 1 bf16, 2 fp8 e4m3 */
+    double *A, *D;                          /* [H] */
+    double *ckpt;                           /* [Bt,H,P,N] master */
+    double *rcopy;                          /* [Bt,H,P,N] decoded read copy (read_prec != 0) */
+    float *rx, *rB, *rC, *rdt;              /* records: [Bt,L,H,P], [Bt,L,G,N] x2, [Bt,L,H] */
+    int *pos, *ckpt_pos;                    /* [Bt] */
+    int pending_T;                          /* drafts of an unresolved verify, else 0 */
+} oracle_replay;
+
+static size_t rx_at(const oracle_replay *r, int b, int idx, int h)
+{ return (((size_t)b * r->L + idx) * r->H + h) * r->P; }
+static size_t rg_at(const oracle_replay *r, int b, int idx, int g)
+{ return (((size_t)b * r->L + idx) * r->G + g) * r->N; }
+static size_t rdt_at(const oracle_replay *r, int b, int idx, int h)
+{ return ((size_t)b * r->L + idx) * r->H + h; }
+
+static void poison_records(oracle_replay *r, int b, int from_idx)
+{
+    for (int idx = from_idx; idx < r->L; ++idx) {
+        for (int h = 0; h < r->H; ++h) {
+            for (int p = 0; p < r->P; ++p) r->rx[rx_at(r, b, idx, h) + p] = NAN;
+            r->rdt[rdt_at(r, b, idx, h)] = NAN;
+        }
+        for (int g = 0; g < r->G; ++g)
+            for (int n = 0; n < r->N; ++n) {
+                r->rB[rg_at(r, b, idx, g) + n] = NAN;
+                r->rC[rg_at(r, b, idx, g) + n] = NAN;
+            }
+    }
+}
+
+/* Refresh sequence b's read copy from its master (reading R6): the master value is rounded to */
+/* fp32 (the precision the layer keeps it in), encoded, and decoded back to float64.           */
+static void refresh_copy(oracle_replay *r, int b)
+{
+    if (r->read_prec == 0) return;
+    const size_t tile = (size_t)r->P * r->N;
+    float *f = (float *)malloc(tile * sizeof(float));
+    for (int h = 0; h < r->H; ++h) {
+        const double *m = r->ckpt + ((size_t)b * r->H + h) * tile;
+        double *c = r->rcopy + ((size_t)b * r->H + h) * tile;
+        for (size_t i = 0; i < tile; ++i) f[i] = (float)m[i];
+        if (r->read_prec == 1) {
+            for (size_t i = 0; i < tile; ++i)
+                c[i] = (double)oracle_bf16_decode(oracle_bf16_encode(f[i]));
+        } else {
+            float s = oracle_e4m3_scale(f, tile);
+            float inv = 1.0f / s;
+            for (size_t i = 0; i < tile; ++i)
+                c[i] = (double)oracle_e4m3_decode(oracle_e4m3_encode_scaled(f[i] * inv)) * (double)s;
+        }
+    }
+    free(f);
+}
+
+oracle_replay *oracle_replay_create(int Bt, int H, int P, int N, int G, int L, int Tmax,
+                                    int read_prec, const float *S0, const float *A, const float *D)
+{
+    if (Bt < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G || L <= 0 || L > 64 ||
+        Tmax <= 0 || Tmax > L || read_prec < 0 || read_prec > 2)
+        return NULL;
+    oracle_replay *r = (oracle_replay *)calloc(1, sizeof(oracle_replay));
+    r->Bt = Bt; r->H = H; r->P = P; r->N = N; r->G = G; r->L = L; r->Tmax = Tmax;
+    r->read_prec = read_prec;
+    const size_t st = (size_t)Bt * H * P * N;
+    r->A = (double *)malloc(H * sizeof(double));
+    r->D = (double *)malloc(H * sizeof(double));
+    for (int h = 0; h < H; ++h) { r->A[h] = A[h]; r->D[h] = D[h]; }
+    r->ckpt = (double *)malloc((st ? st : 1) * sizeof(double));
+    for (size_t i = 0; i < st; ++i) r->ckpt[i] = (double)S0[i];
+    r->rcopy = read_prec ? (double *)malloc((st ? st : 1) * sizeof(double)) : NULL;
+    r->rx = (float *)malloc(((size_t)Bt * L * H * P + 1) * sizeof(float));
+    r->rB = (float *)malloc(((size_t)Bt * L * G * N + 1) * sizeof(float));
+    r->rC = (float *)malloc(((size_t)Bt * L * G * N + 1) * sizeof(float));
+    r->rdt = (float *)malloc(((size_t)Bt * L * H + 1) * sizeof(float));
+    r->pos = (int *)calloc(Bt + 1, sizeof(int));
+    r->ckpt_pos = (int *)calloc(Bt + 1, sizeof(int));
+    for (int b = 0; b < Bt; ++b) { poison_records(r, b, 0); refresh_copy(r, b); }
+    return r;
+}
+
+void oracle_replay_destroy(oracle_replay *r)
+{
+    if (!r) return;
+    free(r->A); free(r->D); free(r->ckpt); free(r->rcopy);
+    free(r->rx); free(r->rB); free(r->rC); free(r->rdt); free(r->pos); free(r->ckpt_pos);
+    free(r);
+}
+
+static void store_record(oracle_replay *r, int b, int idx, const float *x_bh /*[H,P]*/,
+                         const float *B_bg /*[G,N]*/, const float *C_bg, const float *dt_bh /*[H]*/)
+{
+    memcpy(r->rx + rx_at(r, b, idx, 0), x_bh, (size_t)r->H * r->P * sizeof(float));
+    memcpy(r->rB + rg_at(r, b, idx, 0), B_bg, (size_t)r->G * r->N * sizeof(float));
+    memcpy(r->rC + rg_at(r, b, idx, 0), C_bg, (size_t)r->G * r->N * sizeof(float));
+    memcpy(r->rdt + rdt_at(r, b, idx, 0), dt_bh, (size_t)r->H * sizeof(float));
+}
+
+/* Unrolled-window weights for records idx 0..last (relative to ckpt_pos) of (b, h):          */
+/* w[j] = dt_j * exp(A * sum_{i=j+1..last} dt_i) and the window decay exp(A * sum_{0..last}). */
+static double window_weights(const oracle_replay *r, int b, int h, int last, double *w)
+{
+    double tail = 0.0; /* sum of dt strictly after record j */
+    for (int j = last; j >= 0; --j) {
+        double dtj = (double)r->rdt[rdt_at(r, b, j, h)];
+        w[j] = dtj * exp(r->A[h] * tail);
+        tail += dtj;
+    }
+    return exp(r->A[h] * tail);
+}
+
+/* Output of the query token at record index `last` (its record is stored): reads the           */
+/* checkpoint through `S` (the master or the decoded read copy), and the records 0..last.      */
+static void replay_output(const oracle_replay *r, const double *S, int b, int last,
+                          const float *Cq_bg /*[G,N]: the query token's C*/, double *y_bh /*[H,P]*/)
+{
+    const int hpg = r->H / r->G;
+    double w[64 + 8];
+    for (int h = 0; h < r->H; ++h) {
+        const int g = h / hpg;
+        const double *Sc = S + ((size_t)b * r->H + h) * (size_t)r->P * r->N;
+        const float *Cq = Cq_bg + (size_t)g * r->N;
+        double decay = window_weights(r, b, h, last, w);
+        double score[64 + 8]; /* (B_j . C_t) */
+        for (int j = 0; j <= last; ++j) {
+            const float *Bj = r->rB + rg_at(r, b, j, g);
+            double s = 0.0;
+            for (int n = 0; n < r->N; ++n) s += (double)Bj[n] * (double)Cq[n];
+            score[j] = s;
+        }
+        for (int p = 0; p < r->P; ++p) {
+            double u = 0.0;
+            for (int n = 0; n < r->N; ++n) u += Sc[(size_t)p * r->N + n] * (double)Cq[n];
+            double acc = decay * u;
+            for (int j = 0; j <= last; ++j)
+                acc += w[j] * score[j] * (double)r->rx[rx_at(r, b, j, h) + p];
+            const double x_last = (double)r->rx[rx_at(r, b, last, h) + p];
+            y_bh[(size_t)h * r->P + p] = acc + r->D[h] * x_last;
+        }
+    }
+}
+
+/* Fold records 0..count-1 of sequence b into `dst` (the master when committing). */
+static void fold_into(const oracle_replay *r, int b, int count, double *dst)
+{
+    if (count <= 0) return;
+    const int hpg = r->H / r->G;
+    double w[64 + 8];
+    for (int h = 0; h < r->H; ++h) {
+        const int g = h / hpg;
+        double *S = dst + ((size_t)b * r->H + h) * (size_t)r->P * r->N;
+        double decay = window_weights(r, b, h, count - 1, w);
+        for (int p = 0; p < r->P; ++p)
+            for (int n = 0; n < r->N; ++n) {
+                double s = decay * S[(size_t)p * r->N + n];
+                for (int j = 0; j < count; ++j)
+                    s += w[j] * (double)r->rx[rx_at(r, b, j, h) + p] *
+                         (double)r->rB[rg_at(r, b, j, g) + n];
+                S[(size_t)p * r->N + n] = s;
+            }
+    }
+}
+
+/* Commit a flush of sequence b: fold its pos - ckpt_pos records, advance ckpt_pos to pos,     */
+/* forget the records and refresh the read copy.                                               */
+static void flush_seq(oracle_replay *r, int b)
+{
+    int count = r->pos[b] - r->ckpt_pos[b];
+    if (count <= 0) return;
+    fold_into(r, b, count, r->ckpt);
+    r->ckpt_pos[b] = r->pos[b];
+    poison_records(r, b, 0);
+    refresh_copy(r, b);
+}
+
+/* Standard decode step for all sequences: append the token's record, pos += 1; if more than   */
+/* L - Tmax records are now pending, flush and read the output from the folded master (R2,    */
+/* R5); else form the output by replay through the read copy. Returns 0, or -1 when a verify  */
+/* is pending or a sequence's pointers break the invariant.                                    */
+int oracle_replay_step(oracle_replay *r, const float *x, const float *B, const float *C,
+                       const float *dt, double *y)
+{
+    if (r->pending_T) return -1;
+    for (int b = 0; b < r->Bt; ++b) {
+        int count = r->pos[b] - r->ckpt_pos[b];
+        if (count < 0 || count > r->L - r->Tmax) return -1;
+    }
+    const int H = r->H, P = r->P, N = r->N, G = r->G;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < r->Bt; ++b) {
+        int idx = r->pos[b] - r->ckpt_pos[b];
+        store_record(r, b, idx, x + (size_t)b * H * P, B + (size_t)b * G * N,
+                     C + (size_t)b * G * N, dt + (size_t)b * H);
+        r->pos[b] += 1;
+        double *yb = y + (size_t)b * H * P;
+        if (r->pos[b] - r->ckpt_pos[b] > r->L - r->Tmax) {
+            flush_seq(r, b);
+            /* y_t = S_new . C_t + D x_t, from the fresh master */
+            const int hpg = H / G;
+            for (int h = 0; h < H; ++h) {
+                const double *S = r->ckpt + ((size_t)b * H + h) * (size_t)P * N;
+                const float *Ct = C + ((size_t)b * G + h / hpg) * N;
+                for (int p = 0; p < P; ++p) {
+                    double acc = 0.0;
+                    for (int n = 0; n < N; ++n) acc += S[(size_t)p * N + n] * (double)Ct[n];
+                    yb[(size_t)h * P + p] =
+                        acc + r->D[h] * (double)x[((size_t)b * H + h) * P + p];
+                }
+            }
+        } else {
+            const double *Sread = r->read_prec ? r->rcopy : r->ckpt;
+            replay_output(r, Sread, b, idx, C + (size_t)b * G * N, yb);
+        }
+    }
+    return 0;
+}
+
+/* Speculative verify (output-only evaluation): T draft records go after the committed ones,   */
+/* and each draft's output is formed by replay over the committed window plus the drafts up to */
+/* and including itself. No state is stored and no pointer moves ([AT Pulse] "Technical        */
+/* analysis": verification uses output-only evaluation and builds no intermediate state).      */
+/* Returns 0, or -1 (verify already pending, T out of range, or drafts would not fit).         */
+int oracle_replay_verify(oracle_replay *r, int T, const float *x, const float *B, const float *C,
+                         const float *dt, double *y)
+{
+    if (r->pending_T || T < 1 || T > r->Tmax) return -1;
+    for (int b = 0; b < r->Bt; ++b) {
+        int count = r->pos[b] - r->ckpt_pos[b];
+        if (count < 0 || count + T > r->L) return -1;
+    }
+    const int H = r->H, P = r->P, N = r->N, G = r->G;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < r->Bt; ++b) {
+        int count = r->pos[b] - r->ckpt_pos[b];
+        for (int i = 0; i < T; ++i)
+            store_record(r, b, count + i, x + ((size_t)b * T + i) * H * P,
+                         B + ((size_t)b * T + i) * G * N, C + ((size_t)b * T + i) * G * N,
+                         dt + ((size_t)b * T + i) * H);
+        const double *Sread = r->read_prec ? r->rcopy : r->ckpt;
+        for (int i = 0; i < T; ++i)
+            replay_output(r, Sread, b, count + i, C + ((size_t)b * T + i) * G * N,
+                          y + ((size_t)b * T + i) * H * P);
+    }
+    r->pending_T = T;
+    return 0;
+}
+
+/* Rollback and commit: the first accepted[b] drafts become committed (pos moves forward by    */
+/* accepted[b]; the rest are forgotten), then the sequence flushes when more than L - Tmax     */
+/* records are pending (R5). [AT Pulse] "Technical analysis": rollback is a pointer move.      */
+int oracle_replay_rollback(oracle_replay *r, const int *accepted)
+{
+    if (!r->pending_T) return -1;
+    for (int b = 0; b < r->Bt; ++b)
+        if (accepted[b] < 0 || accepted[b] > r->pending_T) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < r->Bt; ++b) {
+        r->pos[b] += accepted[b];
+        poison_records(r, b, r->pos[b] - r->ckpt_pos[b]);
+        if (r->pos[b] - r->ckpt_pos[b] > r->L - r->Tmax) flush_seq(r, b);
+    }
+    r->pending_T = 0;
+    return 0;
+}
+
+/* Explicit flush of the selected sequences (all when mask is NULL). */
+int oracle_replay_flush(oracle_replay *r, const int *seq_mask)
+{
+    if (r->pending_T) return -1;
+    for (int b = 0; b < r->Bt; ++b)
+        if (!seq_mask || seq_mask[b]) flush_seq(r, b);
+    return 0;
+}
+
+void oracle_replay_pointers(const oracle_replay *r, int *pos, int *ckpt_pos)
+{
+    for (int b = 0; b < r->Bt; ++b) { pos[b] = r->pos[b]; ckpt_pos[b] = r->ckpt_pos[b]; }
+}
+
+void oracle_replay_checkpoint(const oracle_replay *r, double *out)
+{
+    memcpy(out, r->ckpt, (size_t)r->Bt * r->H * r->P * r->N * sizeof(double));
+}
+
+/* The decoded read copy (equals the master when reads are fp32). */
+void oracle_replay_read_copy(const oracle_replay *r, double *out)
+{
+    memcpy(out, r->read_prec ? r->rcopy : r->ckpt,
+           (size_t)r->Bt * r->H * r->P * r->N * sizeof(double));
+}
+
+/* The full state after all committed tokens: the master with the pending committed records   */
+/* folded in, without committing anything.                                                    */
+void oracle_replay_materialize(const oracle_replay *r, double *out)
+{
+    memcpy(out, r->ckpt, (size_t)r->Bt * r->H * r->P * r->N * sizeof(double));
+    for (int b = 0; b < r->Bt; ++b) fold_into(r, b, r->pos[b] - r->ckpt_pos[b], out);
+}
+
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

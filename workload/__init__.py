@@ -1,0 +1,82 @@
+"""Seeded synthetic inputs for the Mamba-2 decode layer.
+
+This module holds no arithmetic of the method: it only draws random inputs. Both the GPU path's
+tests/benchmark and the float64 oracle are fed the same fp32 arrays from here.
+
+Value distributions (per the workload definitions for the layer; the pages themselves measure on
+served models whose weights are not available, so these synthetic inputs stand in for them):
+  initial state S0 ~ N(0, 1)
+  x ~ N(0, 1);  B, C ~ N(0, 1/N)
+  dt = softplus(z - 4), z ~ N(0, 1), fresh per (sequence, head, token)   (already positive)
+  A_h = -exp(u), u ~ U(0, ln 16), so A_h in [-16, -1];  D_h ~ N(0, 1)
+Everything is drawn in float64 with numpy's PCG64 and rounded once to float32.
+
+Streams are keyed by (seed, stream id, index) through numpy's SeedSequence, so the inputs of step
+k do not depend on how many other steps were drawn or in what order.
+"""
+import numpy as np
+
+STREAM_PARAMS, STREAM_STATE, STREAM_STEP, STREAM_ACCEPT, STREAM_DRAFT = 0, 1, 2, 3, 4
+
+
+def rng(seed: int, stream: int, index: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, index])))
+
+
+def softplus(z):
+    """log(1 + e^z), evaluated stably in float64 (input generation only)."""
+    return np.logaddexp(0.0, z)
+
+
+def layer_params(seed: int, H: int):
+    """(A, D) float32 [H]."""
+    g = rng(seed, STREAM_PARAMS)
+    A = -np.exp(g.uniform(0.0, np.log(16.0), size=H))
+    D = g.standard_normal(H)
+    return A.astype(np.float32), D.astype(np.float32)
+
+
+def initial_state(seed: int, Bt: int, H: int, P: int, N: int):
+    """S0 float32 [Bt,H,P,N] ~ N(0,1)."""
+    return rng(seed, STREAM_STATE).standard_normal((Bt, H, P, N), dtype=np.float64).astype(np.float32)
+
+
+def token_inputs(seed: int, index: int, lead: tuple, H: int, P: int, N: int, G: int,
+                 stream: int = STREAM_STEP):
+    """One token's (x [*lead,H,P], B [*lead,G,N], C [*lead,G,N], dt [*lead,H]) as float32."""
+    g = rng(seed, stream, index)
+    x = g.standard_normal(lead + (H, P))
+    B = g.standard_normal(lead + (G, N)) / np.sqrt(N)
+    C = g.standard_normal(lead + (G, N)) / np.sqrt(N)
+    dt = softplus(g.standard_normal(lead + (H,)) - 4.0)
+    return (x.astype(np.float32), B.astype(np.float32), C.astype(np.float32),
+            dt.astype(np.float32))
+
+
+def step_inputs(seed: int, step: int, Bt: int, H: int, P: int, N: int, G: int):
+    """Inputs of decode step `step` for the whole batch: x [Bt,H,P], B/C [Bt,G,N], dt [Bt,H]."""
+    return token_inputs(seed, step, (Bt,), H, P, N, G, STREAM_STEP)
+
+
+def draft_inputs(seed: int, step: int, Bt: int, T: int, H: int, P: int, N: int, G: int):
+    """T draft tokens per sequence: x [Bt,T,H,P], B/C [Bt,T,G,N], dt [Bt,T,H]."""
+    return token_inputs(seed, step, (Bt, T), H, P, N, G, STREAM_DRAFT)
+
+
+def accepted_counts(seed: int, step: int, Bt: int, T: int):
+    """Accepted-prefix length per sequence, uniform in {0..T}, int32 [Bt]."""
+    return rng(seed, STREAM_ACCEPT, step).integers(0, T + 1, size=Bt).astype(np.int32)
+
+
+def config_seed(config_index: int) -> int:
+    """Seed of a numbered workload configuration (1000 * index + 7)."""
+    return 1000 * config_index + 7
+
+
+# Named workloads (shapes from the layer definitions): (Bt, H, P, N, G, L, steps)
+TINY = dict(Bt=2, H=4, P=16, N=16, G=1, L=4, steps=64)
+SERVING = dict(Bt=256, H=128, P=64, N=128, G=8, L=16, steps=64)
+DUAL_PRECISION = dict(Bt=256, H=128, P=64, N=128, G=8, L=16, steps=256)
+SPEC = dict(Bt=512, H=128, P=64, N=128, G=8, L=16, T=4, steps=128)
+SWEEP = dict(H=128, P=64, N=128, G=8, batches=(1, 8, 64, 256, 512), Ls=(4, 8, 16, 32),
+             layers=10, steps=64)
