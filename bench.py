@@ -1,0 +1,201 @@
+"""Benchmark: ReplaySSM Mamba-2 decode step on one MI355X.
+
+Workload (default): one serving-size Mamba-2 layer -- batch 256, 128 heads, headdim 64, state 128
+(4 MiB fp32 state per sequence), 8 groups, buffer length 16, fp32 read path -- with synthetic
+seeded inputs already resident in HBM. One timed step = one replayssm_step over the batch (replay
+and append; every 16th step also folds the buffer in the same launch), i.e. one decode step of the
+layer. value = batch * steps / timed seconds = tokens/s/layer.
+
+Prints ONE JSON line (rank 0) with the metric, the dominant kernel's roofline (algorithmic bytes
+per launch / its mean duration from HIP events on the launch stream), the same-run conventional
+read-update-write step, and the float64 CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--read-prec fp32|bf16|fp8]
+                  [--no-cpu-baseline] [--kernels-only]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--read-prec", default="fp32", choices=["fp32", "bf16", "fp8"])
+    ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--buffer-len", type=int, default=16)
+    ap.add_argument("--pool", type=int, default=32, help="distinct input sets cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="only the replay steps (for profiler runs)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the decode step needs no communication; sharding by sequence or head is described "
+              "in the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hybrid_mamba_decode_amd as rs
+    from hybrid_mamba_decode_amd import traffic
+    import workload
+
+    torch.cuda.set_device(0)
+    H, P, N, G = 128, 64, 128, 8
+    Bt, L = args.batch, args.buffer_len
+    prec = args.read_prec
+    seed = workload.config_seed(1)
+    A, D = workload.layer_params(seed, H)
+    S0 = workload.initial_state(seed, Bt, H, P, N)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    A_d, D_d = dev(A), dev(D)
+    S0_d = dev(S0)
+    pool = [tuple(dev(a) for a in workload.step_inputs(seed, t, Bt, H, P, N, G)) for t in range(args.pool)]
+    y = torch.empty(Bt, H, P, device="cuda")
+
+    lay = rs.ReplaySSM(Bt, H, P, N, G, A_d, D_d, buffer_len=L, read_prec=prec)
+    lay.load_state(S0_d)
+    stream = torch.cuda.current_stream()
+
+    # warmup (also compiles nothing: kernels are prebuilt)
+    for k in range(args.warmup):
+        x, B, C, dt = pool[k % len(pool)]
+        lay.step(x, B, C, dt, y)
+    # restart from a window boundary so the timed steps cover whole windows
+    lay.load_state(S0_d)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t0 = time.perf_counter()
+    for k in range(K):
+        x, B, C, dt = pool[k % len(pool)]
+        ev0[k].record(stream)
+        lay.step(x, B, C, dt, y)
+        ev1[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert lay.check() == rs.RSSM_OK
+    assert torch.isfinite(y).all().item()
+
+    durs = np.array([ev0[k].elapsed_time(ev1[k]) * 1e-3 for k in range(K)])   # seconds
+    ks = np.array([(k % L) + 1 for k in range(K)])      # records in the window incl. this token
+    is_flush = ks == L
+    bytes_nf = np.array([traffic.replay_nonflush(H, P, N, G, int(kk), prec) * Bt for kk in ks])
+    bytes_fl = traffic.replay_flush_step(H, P, N, G, L, prec) * Bt
+    nf = ~is_flush
+    nf_gbps = bytes_nf[nf].sum() / durs[nf].sum() / 1e9
+    fl_gbps = (bytes_fl * is_flush.sum()) / durs[is_flush].sum() / 1e9 if is_flush.any() else None
+    amort_bytes = traffic.replay_window_amortized(H, P, N, G, L, prec) * Bt
+    value = Bt * K / wall
+
+    result = {
+        "metric": "SSM decode tokens/s/layer at batch 256 + achieved HBM GB/s (% of peak)",
+        "value": round(value, 1),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if prec == "fp32" else f"f32 master + {prec} read copy",
+        "data": "synthetic (seeded; value distributions of the layer definition)",
+        "config": {"workload": f"one Mamba-2 layer decode step, batch {Bt}, 128 heads, headdim 64, "
+                               f"state 128 (4 MiB fp32/sequence), 8 groups, buffer length {L}, "
+                               f"{prec} read path",
+                   "batch": Bt, "buffer_len": L, "read_prec": prec},
+        "roofline": {
+            "kernel": "replay step, non-flush (step_kernel<prec, 16, false>)",
+            "bound": "hbm",
+            "achieved": round(nf_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(nf_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "mean_launch_us": round(float(durs[nf].mean()) * 1e6, 2),
+            "alg_bytes_per_launch": int(bytes_nf[nf].mean()),
+        },
+        "hbm_gbps_all_steps": round((bytes_nf[nf].sum() + bytes_fl * is_flush.sum()) / durs.sum() / 1e9, 1),
+        "alg_bytes_per_step_amortized": int(amort_bytes),
+        "flush_step": {"mean_launch_us": round(float(durs[is_flush].mean()) * 1e6, 2) if is_flush.any() else None,
+                       "gbps": round(fl_gbps, 1) if fl_gbps else None,
+                       "alg_bytes_per_launch": int(bytes_fl)},
+    }
+
+    if not args.kernels_only:
+        # conventional read-update-write step on the same shapes, same stream, same inputs
+        cfg = rs.make_config(Bt, H, P, N, G)
+        state = S0_d.clone()
+        for k in range(min(args.warmup, 8)):
+            x, B, C, dt = pool[k % len(pool)]
+            rs.conventional_step(cfg, state, x, B, C, dt, A_d, D_d, y)
+        torch.cuda.synchronize()
+        Kc = max(16, K // 4)
+        c0 = [torch.cuda.Event(enable_timing=True) for _ in range(Kc)]
+        c1 = [torch.cuda.Event(enable_timing=True) for _ in range(Kc)]
+        tc = time.perf_counter()
+        for k in range(Kc):
+            x, B, C, dt = pool[k % len(pool)]
+            c0[k].record(stream)
+            rs.conventional_step(cfg, state, x, B, C, dt, A_d, D_d, y)
+            c1[k].record(stream)
+        torch.cuda.synchronize()
+        wall_c = time.perf_counter() - tc
+        dc = np.array([c0[k].elapsed_time(c1[k]) * 1e-3 for k in range(Kc)])
+        conv_bytes = traffic.conventional(H, P, N, G) * Bt
+        conv_tps = Bt * Kc / wall_c
+        result["conventional"] = {
+            "tokens_per_s_layer": round(conv_tps, 1),
+            "mean_launch_us": round(float(dc.mean()) * 1e6, 2),
+            "gbps": round(conv_bytes / dc.mean() / 1e9, 1),
+            "frac": round(conv_bytes / dc.mean() / 1e9 / HBM_PEAK_GBPS, 4),
+        }
+        result["speedup_vs_conventional"] = round(value / conv_tps, 3)
+        del state
+
+    if not args.no_cpu_baseline and not args.kernels_only:
+        result["cpu_baseline"] = cpu_baseline(args, workload, H, P, N, G, Bt, seed, A, D, S0)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, workload, H, P, N, G, Bt, seed, A, D, S0):
+    """The float64 stepwise oracle on the host cores: the full batch of the same layer, for as
+    many decode steps as fit in about --cpu-seconds (1..64), on the same seeded inputs. Only the
+    oracle calls are timed."""
+    import oracle
+    S = S0.astype(np.float64)
+    first = workload.step_inputs(seed, 0, Bt, H, P, N, G)
+    t = time.perf_counter()
+    oracle.step(S, *first, A, D)
+    one = time.perf_counter() - t
+    steps = int(max(1, min(64, args.cpu_seconds / max(one, 1e-6))))
+    toks = [workload.step_inputs(seed, s, Bt, H, P, N, G) for s in range(1, steps + 1)]
+    t0 = time.perf_counter()
+    for tok in toks:
+        oracle.step(S, *tok, A, D)
+    el = time.perf_counter() - t0
+    return {"value": round(Bt * steps / el, 1), "unit": "tokens/s/layer",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"full batch {Bt} of the same layer, {steps} decode steps, float64 stepwise "
+                      f"recurrence (OpenMP over sequence x head), {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

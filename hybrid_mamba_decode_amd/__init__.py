@@ -1,0 +1,332 @@
+"""Python binding of libreplayssm.so, the ReplaySSM Mamba-2 decode-step library for MI355X.
+
+Argument marshalling only: every step of the decode path runs in the library's HIP kernels.
+PyTorch supplies device memory (the caller's tensors and the layer workspace) and streams.
+
+The module-level functions carry the C ABI's names (``replayssm_step``, ``replayssm_flush``,
+``replayssm_spec_verify``, ``replayssm_rollback``, ``conventional_step``, ...); ``ReplaySSM`` is
+a small object around one layer handle. There is no CPU fallback: importing this package raises
+if the built library is missing.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libreplayssm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python hybrid_mamba_decode_amd/build.py` "
+        "(hipcc, gfx950). There is no fallback implementation.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+RSSM_OK, RSSM_E_INVAL, RSSM_E_WORKSPACE, RSSM_E_HIP, RSSM_E_STATE, RSSM_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+READ_FP32, READ_BF16, READ_FP8_E4M3 = 0, 1, 2
+_PREC_NAMES = {"fp32": READ_FP32, "bf16": READ_BF16, "fp8": READ_FP8_E4M3, "fp8_e4m3": READ_FP8_E4M3}
+
+EXPORTED = (
+    "replayssm_workspace_bytes", "replayssm_workspace_layout", "replayssm_create", "replayssm_destroy",
+    "replayssm_load_state", "replayssm_step", "replayssm_flush", "replayssm_spec_verify",
+    "replayssm_rollback", "replayssm_get_pointers", "replayssm_check", "replayssm_materialize_state",
+    "conventional_step", "snapshot_spec_verify", "snapshot_commit", "replayssm_status_string",
+)
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "nheads", "headdim", "dstate", "ngroups", "buffer_len", "max_draft", "read_prec",
+        "store_C")]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "master", "read_copy", "scale", "ring_x", "ring_B", "ring_C", "ring_dt", "pos", "ckpt_pos",
+        "counters", "flag", "total")]
+
+
+_vp = ctypes.c_void_p
+_cfgp = ctypes.POINTER(Config)
+_i32 = ctypes.c_int32
+_sig = {
+    "replayssm_workspace_bytes": (ctypes.c_size_t, [_cfgp]),
+    "replayssm_workspace_layout": (ctypes.c_int, [_cfgp, ctypes.POINTER(Layout)]),
+    "replayssm_create": (ctypes.c_int, [_cfgp, _vp, ctypes.c_size_t, _vp, _vp, ctypes.POINTER(_vp)]),
+    "replayssm_destroy": (ctypes.c_int, [_vp]),
+    "replayssm_load_state": (ctypes.c_int, [_vp, _vp, _vp]),
+    "replayssm_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "replayssm_flush": (ctypes.c_int, [_vp, _vp, _vp]),
+    "replayssm_spec_verify": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "replayssm_rollback": (ctypes.c_int, [_vp, _vp, _vp]),
+    "replayssm_get_pointers": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
+    "replayssm_check": (ctypes.c_int, [_vp, _vp]),
+    "replayssm_materialize_state": (ctypes.c_int, [_vp, _vp, _vp]),
+    "conventional_step": (ctypes.c_int, [_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "snapshot_spec_verify": (ctypes.c_int, [_cfgp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "snapshot_commit": (ctypes.c_int, [_cfgp, _vp, _vp, _i32, _vp]),
+    "replayssm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class ReplaySSMError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {_lib.replayssm_status_string(status).decode()} (status {status})")
+
+
+def _check(status, what):
+    if status != RSSM_OK:
+        raise ReplaySSMError(status, what)
+
+
+def _ptr(t, dtype=torch.float32, name="tensor"):
+    """Device pointer of a contiguous CUDA tensor of the given dtype (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def make_config(batch, nheads, headdim, dstate, ngroups, buffer_len=16, max_draft=1,
+                read_prec="fp32", store_C=True):
+    rp = _PREC_NAMES[read_prec] if isinstance(read_prec, str) else int(read_prec)
+    return Config(batch, nheads, headdim, dstate, ngroups, buffer_len, max_draft, rp, int(bool(store_C)))
+
+
+def _expect(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+# ---- C ABI, by name -------------------------------------------------------------------------
+
+def replayssm_workspace_bytes(cfg: Config) -> int:
+    return int(_lib.replayssm_workspace_bytes(ctypes.byref(cfg)))
+
+
+def replayssm_workspace_layout(cfg: Config) -> Layout:
+    lay = Layout()
+    _check(_lib.replayssm_workspace_layout(ctypes.byref(cfg), ctypes.byref(lay)), "replayssm_workspace_layout")
+    return lay
+
+
+def replayssm_create(cfg: Config, workspace: torch.Tensor, A: torch.Tensor, D: torch.Tensor):
+    h = _vp()
+    _check(_lib.replayssm_create(ctypes.byref(cfg), _ptr(workspace, torch.uint8, "workspace"),
+                                 workspace.numel(), _ptr(A, name="A"), _ptr(D, name="D"),
+                                 ctypes.byref(h)), "replayssm_create")
+    return h
+
+
+def replayssm_destroy(h):
+    _check(_lib.replayssm_destroy(h), "replayssm_destroy")
+
+
+def replayssm_load_state(h, state, stream=None):
+    _check(_lib.replayssm_load_state(h, _ptr(state, name="state"), _stream(stream)), "replayssm_load_state")
+
+
+def replayssm_step(h, x, B, C, dt, y, stream=None):
+    _check(_lib.replayssm_step(h, _ptr(x, name="x"), _ptr(B, name="B"), _ptr(C, name="C"),
+                               _ptr(dt, name="dt"), _ptr(y, name="y"), _stream(stream)), "replayssm_step")
+
+
+def replayssm_flush(h, seq_mask=None, stream=None):
+    _check(_lib.replayssm_flush(h, _ptr(seq_mask, torch.int32, "seq_mask"), _stream(stream)), "replayssm_flush")
+
+
+def replayssm_spec_verify(h, T, x, B, C, dt, y, stream=None):
+    _check(_lib.replayssm_spec_verify(h, int(T), _ptr(x, name="x"), _ptr(B, name="B"), _ptr(C, name="C"),
+                                      _ptr(dt, name="dt"), _ptr(y, name="y"), _stream(stream)),
+           "replayssm_spec_verify")
+
+
+def replayssm_rollback(h, accepted, stream=None):
+    _check(_lib.replayssm_rollback(h, _ptr(accepted, torch.int32, "accepted"), _stream(stream)),
+           "replayssm_rollback")
+
+
+def replayssm_get_pointers(h, batch, stream=None):
+    pos = (ctypes.c_int32 * max(batch, 1))()
+    ck = (ctypes.c_int32 * max(batch, 1))()
+    _check(_lib.replayssm_get_pointers(h, ctypes.cast(pos, _vp), ctypes.cast(ck, _vp), _stream(stream)),
+           "replayssm_get_pointers")
+    return list(pos)[:batch], list(ck)[:batch]
+
+
+def replayssm_check(h, stream=None):
+    return int(_lib.replayssm_check(h, _stream(stream)))
+
+
+def replayssm_materialize_state(h, out, stream=None):
+    _check(_lib.replayssm_materialize_state(h, _ptr(out, name="out"), _stream(stream)),
+           "replayssm_materialize_state")
+
+
+def _check_token_shapes(cfg, x, B, C, dt, lead=()):
+    Bt, H, P, N, G = cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
+    _expect(x, (Bt, *lead, H, P), "x")
+    _expect(B, (Bt, *lead, G, N), "B")
+    _expect(C, (Bt, *lead, G, N), "C")
+    _expect(dt, (Bt, *lead, H), "dt")
+
+
+def conventional_step(cfg: Config, state, x, B, C, dt, A, D, y, stream=None):
+    _check_token_shapes(cfg, x, B, C, dt)
+    _expect(state, (cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), "state")
+    _expect(y, (cfg.batch, cfg.nheads, cfg.headdim), "y")
+    _expect(A, (cfg.nheads,), "A")
+    _expect(D, (cfg.nheads,), "D")
+    _check(_lib.conventional_step(ctypes.byref(cfg), _ptr(state, name="state"), _ptr(x, name="x"),
+                                  _ptr(B, name="B"), _ptr(C, name="C"), _ptr(dt, name="dt"),
+                                  _ptr(A, name="A"), _ptr(D, name="D"), _ptr(y, name="y"),
+                                  _stream(stream)), "conventional_step")
+
+
+def snapshot_spec_verify(cfg: Config, slots, cur, T, x, B, C, dt, A, D, y, stream=None):
+    _check_token_shapes(cfg, x, B, C, dt, (T,))
+    _expect(slots, (cfg.batch, T + 1, cfg.nheads, cfg.headdim, cfg.dstate), "slots")
+    _expect(cur, (cfg.batch,), "cur")
+    _expect(y, (cfg.batch, T, cfg.nheads, cfg.headdim), "y")
+    _expect(A, (cfg.nheads,), "A")
+    _expect(D, (cfg.nheads,), "D")
+    _check(_lib.snapshot_spec_verify(ctypes.byref(cfg), _ptr(slots, name="slots"),
+                                     _ptr(cur, torch.int32, "cur"), int(T), _ptr(x, name="x"),
+                                     _ptr(B, name="B"), _ptr(C, name="C"), _ptr(dt, name="dt"),
+                                     _ptr(A, name="A"), _ptr(D, name="D"), _ptr(y, name="y"),
+                                     _stream(stream)), "snapshot_spec_verify")
+
+
+def snapshot_commit(cfg: Config, cur, accepted, T, stream=None):
+    _expect(cur, (cfg.batch,), "cur")
+    _expect(accepted, (cfg.batch,), "accepted")
+    _check(_lib.snapshot_commit(ctypes.byref(cfg), _ptr(cur, torch.int32, "cur"),
+                                _ptr(accepted, torch.int32, "accepted"), int(T), _stream(stream)),
+           "snapshot_commit")
+
+
+def replayssm_status_string(status: int) -> str:
+    return _lib.replayssm_status_string(int(status)).decode()
+
+
+# ---- one layer as an object -------------------------------------------------------------------
+
+class ReplaySSM:
+    """One Mamba-2 layer's decode state kept as checkpoint + record ring, on one GPU.
+
+    The workspace (fp32 master, read copy, ring, pointers) is one uint8 CUDA tensor owned here.
+    """
+
+    def __init__(self, batch, nheads, headdim, dstate, ngroups, A, D, buffer_len=16, max_draft=1,
+                 read_prec="fp32", store_C=True, device="cuda"):
+        self.cfg = make_config(batch, nheads, headdim, dstate, ngroups, buffer_len, max_draft,
+                               read_prec, store_C)
+        nbytes = replayssm_workspace_bytes(self.cfg)
+        if nbytes == 0:
+            raise ReplaySSMError(RSSM_E_INVAL, "replayssm_workspace_bytes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if self.workspace.data_ptr() % 256:
+            raise RuntimeError("workspace allocation is not 256-byte aligned")
+        self.A = A.contiguous()
+        self.D = D.contiguous()
+        self.layout = replayssm_workspace_layout(self.cfg)
+        self.handle = replayssm_create(self.cfg, self.workspace, self.A, self.D)
+        self.batch, self.nheads, self.headdim, self.dstate, self.ngroups = batch, nheads, headdim, dstate, ngroups
+        self.buffer_len, self.max_draft = buffer_len, max_draft
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            _lib.replayssm_destroy(h)
+            self.handle = None
+
+    # shapes
+    def _tok(self, lead=()):
+        Bt, H, P, N, G = self.batch, self.nheads, self.headdim, self.dstate, self.ngroups
+        return ((Bt, *lead, H, P), (Bt, *lead, G, N), (Bt, *lead, G, N), (Bt, *lead, H))
+
+    def load_state(self, state, stream=None):
+        _expect(state, (self.batch, self.nheads, self.headdim, self.dstate), "state")
+        replayssm_load_state(self.handle, state, stream)
+
+    def step(self, x, B, C, dt, y=None, stream=None):
+        for t, s, n in zip((x, B, C, dt), self._tok(), "xBCd"):
+            _expect(t, s, n)
+        if y is None:
+            y = torch.empty_like(x)
+        replayssm_step(self.handle, x, B, C, dt, y, stream)
+        return y
+
+    def flush(self, seq_mask=None, stream=None):
+        replayssm_flush(self.handle, seq_mask, stream)
+
+    def spec_verify(self, x, B, C, dt, y=None, stream=None):
+        T = x.shape[1]
+        for t, s, n in zip((x, B, C, dt), self._tok((T,)), "xBCd"):
+            _expect(t, s, n)
+        if y is None:
+            y = torch.empty_like(x)
+        replayssm_spec_verify(self.handle, T, x, B, C, dt, y, stream)
+        return y
+
+    def rollback(self, accepted, stream=None):
+        _expect(accepted, (self.batch,), "accepted")
+        replayssm_rollback(self.handle, accepted, stream)
+
+    def get_pointers(self, stream=None):
+        return replayssm_get_pointers(self.handle, self.batch, stream)
+
+    def check(self, stream=None):
+        return replayssm_check(self.handle, stream)
+
+    def materialize_state(self, out=None, stream=None):
+        if out is None:
+            out = torch.empty((self.batch, self.nheads, self.headdim, self.dstate),
+                              dtype=torch.float32, device=self.workspace.device)
+        replayssm_materialize_state(self.handle, out, stream)
+        return out
+
+    # workspace views (inspection)
+    def region(self, name, dtype, shape):
+        off = getattr(self.layout, name)
+        n = 1
+        for s in shape:
+            n *= s
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.workspace[off:off + nbytes].view(dtype).view(*shape)
+
+    def master(self):
+        return self.region("master", torch.float32, (self.batch, self.nheads, self.headdim, self.dstate))
+
+    def read_copy(self):
+        shape = (self.batch, self.nheads, self.headdim, self.dstate)
+        if self.cfg.read_prec == READ_BF16:
+            return self.region("read_copy", torch.int16, shape)
+        if self.cfg.read_prec == READ_FP8_E4M3:
+            return self.region("read_copy", torch.uint8, shape)
+        return None
+
+    def scales(self):
+        return self.region("scale", torch.float32, (self.batch, self.nheads))
+
+    def pointer_arrays(self):
+        return (self.region("pos", torch.int32, (self.batch,)),
+                self.region("ckpt_pos", torch.int32, (self.batch,)))

@@ -1,0 +1,429 @@
+// api.hip -- the C ABI of replayssm.h: argument and state-machine validation, workspace layout,
+// the host-side flush hint, and kernel dispatch by state size N.
+//
+// Everything that can be checked on the host is checked before any HIP call, so the error paths
+// run without a GPU.
+#include "../../include/replayssm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "launch.h"
+
+using namespace rssm;
+
+struct replayssm_layer {
+    replayssm_config cfg;
+    replayssm_layout lay;
+    Layer dev;
+    int lmax;       // window bucket for kernel instances (16, 32 or 64)
+    int loaded;     // replayssm_load_state has run
+    int poisoned;   // device flag observed: refuse work until the next load
+    int pending_T;  // drafts of an unresolved verify, else 0
+    // Host hint: bounds on the number of pending committed records over all sequences. Exact for
+    // lockstep decoding, conservative otherwise; it only selects the kernel variant (whether a
+    // launch may meet a flush). The device decides every flush per sequence, bit-exactly.
+    int cmin, cmax;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool supported_n(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+
+int psplit_of(const replayssm_config &c) { return (c.headdim + kRows - 1) / kRows; }
+
+// Shape checks shared by every entry point (the baselines use only these fields).
+rssm_status check_shape(const replayssm_config *c)
+{
+    if (!c) return RSSM_E_INVAL;
+    if (c->batch < 0 || c->nheads <= 0 || c->headdim <= 0 || c->dstate <= 0 || c->ngroups <= 0)
+        return RSSM_E_INVAL;
+    if (c->nheads % c->ngroups) return RSSM_E_INVAL;
+    if (c->headdim % 4) return RSSM_E_INVAL;
+    if (!supported_n(c->dstate) || c->headdim > 256) return RSSM_E_UNSUPPORTED;
+    const uint64_t blocks = (uint64_t)c->batch * c->nheads * psplit_of(*c);
+    if (blocks * kThreads >= (1ull << 32)) return RSSM_E_UNSUPPORTED;
+    return RSSM_OK;
+}
+
+rssm_status check_config(const replayssm_config *c)
+{
+    rssm_status s = check_shape(c);
+    if (s != RSSM_OK) return s;
+    if (c->buffer_len < 1 || c->max_draft < 1 || c->max_draft > c->buffer_len) return RSSM_E_INVAL;
+    if (c->read_prec < RSSM_READ_FP32 || c->read_prec > RSSM_READ_FP8_E4M3) return RSSM_E_INVAL;
+    if (c->store_C != 0 && c->store_C != 1) return RSSM_E_INVAL;
+    if (c->buffer_len > 64 || c->max_draft > 8) return RSSM_E_UNSUPPORTED;
+    if (c->read_prec == RSSM_READ_FP8_E4M3 && c->headdim > kRows) return RSSM_E_UNSUPPORTED;
+    return RSSM_OK;
+}
+
+void make_layout(const replayssm_config &c, replayssm_layout *L)
+{
+    const size_t Bt = (size_t)c.batch, H = c.nheads, P = c.headdim, N = c.dstate, G = c.ngroups,
+                 Lb = c.buffer_len;
+    const size_t elems = Bt * H * P * N;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    L->master = take(elems * 4);
+    L->read_copy = take(c.read_prec == RSSM_READ_BF16 ? elems * 2 : c.read_prec == RSSM_READ_FP8_E4M3 ? elems : 0);
+    L->scale = take(c.read_prec == RSSM_READ_FP8_E4M3 ? Bt * H * 4 : 0);
+    L->ring_x = take(Bt * H * Lb * P * 4);
+    L->ring_B = take(Bt * G * Lb * N * 4);
+    L->ring_C = take(c.store_C ? Bt * G * Lb * N * 4 : 0);
+    L->ring_dt = take(Bt * H * Lb * 4);
+    L->pos = take(Bt * 4);
+    L->ckpt_pos = take(Bt * 4);
+    L->counters = take(Bt * 4);
+    L->flag = take(4);
+    L->total = off;
+}
+
+// A Layer carrying only shapes and A/D, for the baselines.
+Layer shape_layer(const replayssm_config &c, const float *A, const float *D)
+{
+    Layer L;
+    std::memset(&L, 0, sizeof(L));
+    L.A = A;
+    L.D = D;
+    L.Bt = c.batch;
+    L.H = c.nheads;
+    L.P = c.headdim;
+    L.G = c.ngroups;
+    L.L = 1;
+    L.Tmax = 1;
+    L.hpg = c.nheads / c.ngroups;
+    L.psplit = psplit_of(c);
+    return L;
+}
+
+rssm_status hip_status(hipError_t e) { return e == hipSuccess ? RSSM_OK : RSSM_E_HIP; }
+
+// Snapshot baseline commit: the committed slot moves forward by the accepted count, modulo the
+// T + 1 slots. One thread per sequence; out-of-range counts leave the slot unchanged.
+__global__ void snapshot_commit_kernel(int *cur, const int *accepted, int T, int Bt)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= Bt) return;
+    const int a = accepted[b], c = cur[b];
+    if (a >= 0 && a <= T && c >= 0 && c <= T) cur[b] = (c + a) % (T + 1);
+}
+
+hipError_t launch_snapshot_commit(int *cur, const int *accepted, int T, int Bt, hipStream_t st)
+{
+    hipLaunchKernelGGL(snapshot_commit_kernel, dim3((Bt + 255) / 256), dim3(256), 0, st, cur, accepted, T, Bt);
+    return hipGetLastError();
+}
+
+#define RSSM_BY_N(NV, CALL)                 \
+    switch (NV) {                           \
+    case 16: return hip_status(CALL(16));   \
+    case 32: return hip_status(CALL(32));   \
+    case 64: return hip_status(CALL(64));   \
+    case 128: return hip_status(CALL(128)); \
+    case 256: return hip_status(CALL(256)); \
+    default: return RSSM_E_UNSUPPORTED;     \
+    }
+
+rssm_status ready(replayssm_t h)
+{
+    if (!h) return RSSM_E_INVAL;
+    if (!h->loaded || h->poisoned) return RSSM_E_STATE;
+    return RSSM_OK;
+}
+
+bool ok_ptr(const void *p) { return p && aligned(p, 16); }
+
+// Bounds on the pending-record count after every sequence commits `lo..hi` more records and
+// those with more than L - Tmax pending flush.
+void commit_bounds(replayssm_t h, int lo, int hi)
+{
+    const int lim = h->cfg.buffer_len - h->cfg.max_draft;
+    const int nmin = h->cmin + lo, nmax = h->cmax + hi;
+    if (nmax <= lim) {
+        h->cmin = nmin;
+        h->cmax = nmax;
+    } else if (nmin > lim) {
+        h->cmin = h->cmax = 0;
+    } else {
+        h->cmin = 0;
+        h->cmax = lim;
+    }
+}
+
+rssm_status read_flag(replayssm_t h, hipStream_t st)
+{
+    if (hipStreamSynchronize(st) != hipSuccess) return RSSM_E_HIP;
+    unsigned flag = 0;
+    if (h->cfg.batch > 0) {
+        if (hipMemcpy(&flag, h->dev.flag, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) return RSSM_E_HIP;
+    }
+    if (flag) {
+        h->poisoned = 1;
+        return RSSM_E_STATE;
+    }
+    return RSSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t replayssm_workspace_bytes(const replayssm_config *cfg)
+{
+    if (check_config(cfg) != RSSM_OK) return 0;
+    replayssm_layout L;
+    make_layout(*cfg, &L);
+    return L.total;
+}
+
+rssm_status replayssm_workspace_layout(const replayssm_config *cfg, replayssm_layout *out)
+{
+    const rssm_status s = check_config(cfg);
+    if (s != RSSM_OK) return s;
+    if (!out) return RSSM_E_INVAL;
+    make_layout(*cfg, out);
+    return RSSM_OK;
+}
+
+rssm_status replayssm_create(const replayssm_config *cfg, void *workspace, size_t bytes,
+                             const float *A, const float *D, replayssm_t *out)
+{
+    if (!out) return RSSM_E_INVAL;
+    *out = nullptr;
+    const rssm_status s = check_config(cfg);
+    if (s != RSSM_OK) return s;
+    if (!A || !D || !aligned(A, 4) || !aligned(D, 4)) return RSSM_E_INVAL;
+    replayssm_layout lay;
+    make_layout(*cfg, &lay);
+    if (!workspace || !aligned(workspace, kAlign) || bytes < lay.total) return RSSM_E_WORKSPACE;
+    replayssm_layer *h = new (std::nothrow) replayssm_layer;
+    if (!h) return RSSM_E_INVAL;
+    std::memset(h, 0, sizeof(*h));
+    h->cfg = *cfg;
+    h->lay = lay;
+    char *ws = (char *)workspace;
+    Layer &d = h->dev;
+    d.master = (float *)(ws + lay.master);
+    d.rcopy = cfg->read_prec == RSSM_READ_FP32 ? nullptr : (void *)(ws + lay.read_copy);
+    d.scale = cfg->read_prec == RSSM_READ_FP8_E4M3 ? (float *)(ws + lay.scale) : nullptr;
+    d.ring_x = (float *)(ws + lay.ring_x);
+    d.ring_B = (float *)(ws + lay.ring_B);
+    d.ring_C = cfg->store_C ? (float *)(ws + lay.ring_C) : nullptr;
+    d.ring_dt = (float *)(ws + lay.ring_dt);
+    d.pos = (int *)(ws + lay.pos);
+    d.ckpt = (int *)(ws + lay.ckpt_pos);
+    d.counter = (unsigned *)(ws + lay.counters);
+    d.flag = (unsigned *)(ws + lay.flag);
+    d.A = A;
+    d.D = D;
+    d.Bt = cfg->batch;
+    d.H = cfg->nheads;
+    d.P = cfg->headdim;
+    d.G = cfg->ngroups;
+    d.L = cfg->buffer_len;
+    d.Tmax = cfg->max_draft;
+    d.hpg = cfg->nheads / cfg->ngroups;
+    d.psplit = psplit_of(*cfg);
+    h->lmax = cfg->buffer_len <= 16 ? 16 : cfg->buffer_len <= 32 ? 32 : 64;
+    *out = h;
+    return RSSM_OK;
+}
+
+rssm_status replayssm_destroy(replayssm_t h)
+{
+    delete h;
+    return RSSM_OK;
+}
+
+rssm_status replayssm_load_state(replayssm_t h, const float *state, void *stream)
+{
+    if (!h) return RSSM_E_INVAL;
+    if (!ok_ptr(state)) return RSSM_E_INVAL;
+    h->loaded = 1;
+    h->poisoned = 0;
+    h->pending_T = 0;
+    h->cmin = h->cmax = 0;
+    if (h->cfg.batch == 0) return RSSM_OK;
+    const hipStream_t st = (hipStream_t)stream;
+#define CALL(NV) launch_load_n##NV(h->cfg.read_prec, h->dev, state, st)
+    RSSM_BY_N(h->cfg.dstate, CALL)
+#undef CALL
+}
+
+rssm_status replayssm_step(replayssm_t h, const float *x, const float *B, const float *C,
+                           const float *dt, float *y, void *stream)
+{
+    rssm_status s = ready(h);
+    if (s != RSSM_OK) return s;
+    if (h->pending_T) return RSSM_E_STATE;
+    if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(dt) || !ok_ptr(y)) return RSSM_E_INVAL;
+    const bool flush_capable = h->cmax + 1 > h->cfg.buffer_len - h->cfg.max_draft;
+    commit_bounds(h, 1, 1);
+    if (h->cfg.batch == 0) return RSSM_OK;
+    const TokenIO io{x, B, C, dt, y};
+    const hipStream_t st = (hipStream_t)stream;
+#define CALL(NV) launch_step_n##NV(h->cfg.read_prec, h->lmax, h->dev, io, flush_capable, st)
+    RSSM_BY_N(h->cfg.dstate, CALL)
+#undef CALL
+}
+
+rssm_status replayssm_flush(replayssm_t h, const int32_t *seq_mask, void *stream)
+{
+    rssm_status s = ready(h);
+    if (s != RSSM_OK) return s;
+    if (h->pending_T) return RSSM_E_STATE;
+    if (seq_mask && !aligned(seq_mask, 4)) return RSSM_E_INVAL;
+    if (!seq_mask) h->cmin = h->cmax = 0;
+    else h->cmin = 0;
+    if (h->cfg.batch == 0) return RSSM_OK;
+    const hipStream_t st = (hipStream_t)stream;
+#define CALL(NV) launch_flush_n##NV(h->cfg.read_prec, h->lmax, h->dev, MODE_MASK, seq_mask, 0, nullptr, st)
+    RSSM_BY_N(h->cfg.dstate, CALL)
+#undef CALL
+}
+
+rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float *x, const float *B,
+                                  const float *C, const float *dt, float *y, void *stream)
+{
+    rssm_status s = ready(h);
+    if (s != RSSM_OK) return s;
+    if (h->pending_T) return RSSM_E_STATE;
+    if (T < 1 || T > h->cfg.max_draft) return RSSM_E_INVAL;
+    if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(dt) || !ok_ptr(y)) return RSSM_E_INVAL;
+    h->pending_T = T;
+    if (h->cfg.batch == 0) return RSSM_OK;
+    const TokenIO io{x, B, C, dt, y};
+    const hipStream_t st = (hipStream_t)stream;
+#define CALL(NV) launch_verify_n##NV(h->cfg.read_prec, h->lmax, h->dev, io, T, st)
+    RSSM_BY_N(h->cfg.dstate, CALL)
+#undef CALL
+}
+
+rssm_status replayssm_rollback(replayssm_t h, const int32_t *accepted, void *stream)
+{
+    rssm_status s = ready(h);
+    if (s != RSSM_OK) return s;
+    if (!h->pending_T) return RSSM_E_STATE;
+    if (!accepted || !aligned(accepted, 4)) return RSSM_E_INVAL;
+    const int T = h->pending_T;
+    h->pending_T = 0;
+    commit_bounds(h, 0, T);
+    if (h->cfg.batch == 0) return RSSM_OK;
+    const hipStream_t st = (hipStream_t)stream;
+#define CALL(NV) launch_flush_n##NV(h->cfg.read_prec, h->lmax, h->dev, MODE_ROLLBACK, accepted, T, nullptr, st)
+    RSSM_BY_N(h->cfg.dstate, CALL)
+#undef CALL
+}
+
+rssm_status replayssm_get_pointers(replayssm_t h, int32_t *pos, int32_t *ckpt_pos, void *stream)
+{
+    if (!h) return RSSM_E_INVAL;
+    if (!h->loaded) return RSSM_E_STATE;
+    const hipStream_t st = (hipStream_t)stream;
+    const rssm_status s = read_flag(h, st);
+    if (s != RSSM_OK) return s;
+    const size_t bytes = (size_t)h->cfg.batch * sizeof(int32_t);
+    if (bytes == 0) return RSSM_OK;
+    if (pos && hipMemcpy(pos, h->dev.pos, bytes, hipMemcpyDeviceToHost) != hipSuccess) return RSSM_E_HIP;
+    if (ckpt_pos && hipMemcpy(ckpt_pos, h->dev.ckpt, bytes, hipMemcpyDeviceToHost) != hipSuccess) return RSSM_E_HIP;
+    return RSSM_OK;
+}
+
+rssm_status replayssm_check(replayssm_t h, void *stream)
+{
+    if (!h) return RSSM_E_INVAL;
+    if (!h->loaded) return RSSM_E_STATE;
+    if (h->poisoned) return RSSM_E_STATE;
+    return read_flag(h, (hipStream_t)stream);
+}
+
+rssm_status replayssm_materialize_state(replayssm_t h, float *out, void *stream)
+{
+    rssm_status s = ready(h);
+    if (s != RSSM_OK) return s;
+    if (!ok_ptr(out)) return RSSM_E_INVAL;
+    if (h->cfg.batch == 0) return RSSM_OK;
+    const hipStream_t st = (hipStream_t)stream;
+#define CALL(NV) launch_flush_n##NV(h->cfg.read_prec, h->lmax, h->dev, MODE_MATERIALIZE, nullptr, 0, out, st)
+    RSSM_BY_N(h->cfg.dstate, CALL)
+#undef CALL
+}
+
+rssm_status conventional_step(const replayssm_config *cfg, float *state, const float *x,
+                              const float *B, const float *C, const float *dt, const float *A,
+                              const float *D, float *y, void *stream)
+{
+    const rssm_status s = check_shape(cfg);
+    if (s != RSSM_OK) return s;
+    if (!ok_ptr(state) || !ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(dt) || !ok_ptr(y)) return RSSM_E_INVAL;
+    if (!A || !D || !aligned(A, 4) || !aligned(D, 4)) return RSSM_E_INVAL;
+    if (cfg->batch == 0) return RSSM_OK;
+    const Layer Ld = shape_layer(*cfg, A, D);
+    const TokenIO io{x, B, C, dt, y};
+    const hipStream_t st = (hipStream_t)stream;
+#define CALL(NV) launch_conventional_n##NV(Ld, state, io, st)
+    RSSM_BY_N(cfg->dstate, CALL)
+#undef CALL
+}
+
+rssm_status snapshot_spec_verify(const replayssm_config *cfg, float *slots, const int32_t *cur,
+                                 int32_t T, const float *x, const float *B, const float *C,
+                                 const float *dt, const float *A, const float *D, float *y,
+                                 void *stream)
+{
+    const rssm_status s = check_shape(cfg);
+    if (s != RSSM_OK) return s;
+    if (T < 1 || T > 8) return RSSM_E_INVAL;
+    if (!ok_ptr(slots) || !cur || !aligned(cur, 4) || !ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) ||
+        !ok_ptr(dt) || !ok_ptr(y))
+        return RSSM_E_INVAL;
+    if (!A || !D || !aligned(A, 4) || !aligned(D, 4)) return RSSM_E_INVAL;
+    if (cfg->batch == 0) return RSSM_OK;
+    const Layer Ld = shape_layer(*cfg, A, D);
+    const TokenIO io{x, B, C, dt, y};
+    const hipStream_t st = (hipStream_t)stream;
+#define CALL(NV) launch_snapshot_n##NV(Ld, slots, cur, T, io, st)
+    RSSM_BY_N(cfg->dstate, CALL)
+#undef CALL
+}
+
+rssm_status snapshot_commit(const replayssm_config *cfg, int32_t *cur, const int32_t *accepted,
+                            int32_t T, void *stream)
+{
+    const rssm_status s = check_shape(cfg);
+    if (s != RSSM_OK) return s;
+    if (T < 1 || T > 8) return RSSM_E_INVAL;
+    if (!cur || !accepted || !aligned(cur, 4) || !aligned(accepted, 4)) return RSSM_E_INVAL;
+    if (cfg->batch == 0) return RSSM_OK;
+    return hip_status(launch_snapshot_commit(cur, accepted, T, cfg->batch, (hipStream_t)stream));
+}
+
+const char *replayssm_status_string(rssm_status s)
+{
+    switch (s) {
+    case RSSM_OK: return "ok";
+    case RSSM_E_INVAL: return "invalid argument, pointer, alignment or shape";
+    case RSSM_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case RSSM_E_HIP: return "HIP runtime error";
+    case RSSM_E_STATE: return "state-machine misuse or device invariant flag set";
+    case RSSM_E_UNSUPPORTED: return "unsupported configuration";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,289 @@
+// device.h -- device-side building blocks shared by the ReplaySSM kernels (gfx950, wave64).
+//
+// Tiling. One work-group (256 threads = 4 wave64s) owns up to kRows = 64 rows (headdim entries
+// p) of one (sequence, head) state tile [P, N]; a head with P > 64 is split over ceil(P/64)
+// work-groups. Within a wave the lanes run along N: each lane loads one 16-byte chunk of a row
+// per load slot (4 fp32, 8 bf16 or 16 fp8 values), LPR = N / VEC lanes cover a row and one wave
+// instruction covers RPI = 64 / LPR consecutive rows, so every wave instruction reads a
+// contiguous, fully coalesced 1 KiB. Per-row dot products are finished by a transpose-reduce
+// across the LPR lanes of a row (NL - 1 + log2(LPR/NL) lane exchanges instead of
+// NL * log2(LPR)).
+//
+// Work-group -> tile order is XCD-aware: MI355X dispatches consecutive work-groups round-robin
+// over its 8 XCDs (each with its own L2), so block i is given tile (i % 8) * (nblk / 8) + i / 8.
+// Each XCD then walks a contiguous range of tiles, and the heads of one group -- which share that
+// group's B window -- hit the same L2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rssm {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRows = 64;
+
+enum { PREC_F32 = 0, PREC_BF16 = 1, PREC_FP8 = 2 };
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Everything a kernel needs to know about one layer's workspace (passed by value).
+struct Layer {
+    float *master;      // [Bt,H,P,N] fp32 checkpoint
+    void *rcopy;        // [Bt,H,P,N] bf16 / e4m3 read copy (unused for fp32 reads)
+    float *scale;       // [Bt,H] fp8 per-head scale
+    float *ring_x;      // [Bt,H,L,P]
+    float *ring_B;      // [Bt,G,L,N]
+    float *ring_C;      // [Bt,G,L,N] or nullptr
+    float *ring_dt;     // [Bt,H,L]
+    int *pos;           // [Bt]
+    int *ckpt;          // [Bt]
+    unsigned *counter;  // [Bt]
+    unsigned *flag;     // [1]
+    const float *A;     // [H]
+    const float *D;     // [H]
+    int Bt, H, P, G, L, Tmax, hpg, psplit;
+};
+
+// Per-token inputs of one call (layouts in replayssm.h).
+struct TokenIO {
+    const float *x, *B, *C, *dt;
+    float *y;
+};
+
+// Device flag bits.
+enum : unsigned { FLAG_POINTERS = 1u, FLAG_ACCEPTED = 2u };
+
+template <int N, int PREC>
+struct Geo {
+    static constexpr int VEC = PREC == PREC_F32 ? 4 : PREC == PREC_BF16 ? 8 : 16;
+    static constexpr int LPR = N / VEC;          // lanes per row
+    static constexpr int RPI = 64 / LPR;         // rows per wave instruction
+    static constexpr int RPB = kWaves * RPI;     // rows per work-group instruction
+    static constexpr int NL = (kRows + RPB - 1) / RPB;  // load slots per lane for kRows rows
+    static_assert(N % VEC == 0 && LPR >= 1 && LPR <= 64, "unsupported N for this precision");
+    static_assert(NL <= LPR || LPR == 1 || NL == 1, "transpose-reduce needs NL <= LPR");
+};
+
+struct Tile {
+    int b, h, g, split, row0, nrows;
+};
+
+__device__ inline Tile map_tile(const Layer &Ld)
+{
+    const unsigned nblk = gridDim.x, i = blockIdx.x;
+    const unsigned id = (nblk % 8u == 0u) ? (i % 8u) * (nblk / 8u) + i / 8u : i;
+    Tile t;
+    t.split = (int)(id % (unsigned)Ld.psplit);
+    const unsigned bh = id / (unsigned)Ld.psplit;
+    t.h = (int)(bh % (unsigned)Ld.H);
+    t.b = (int)(bh / (unsigned)Ld.H);
+    t.g = t.h / Ld.hpg;
+    t.row0 = t.split * kRows;
+    t.nrows = min(kRows, Ld.P - t.row0);
+    return t;
+}
+
+// ------------------------------------------------------------------------------------------
+// Loads and stores. State tiles stream through once per call: non-temporal, so they do not
+// evict the record windows that several work-groups share from L2.
+// ------------------------------------------------------------------------------------------
+__device__ inline u32x4 load_nt(const void *p) { return __builtin_nontemporal_load((const u32x4 *)p); }
+__device__ inline void store_nt(void *p, u32x4 v) { __builtin_nontemporal_store(v, (u32x4 *)p); }
+__device__ inline f32x4 as_f32x4(u32x4 v) { return __builtin_bit_cast(f32x4, v); }
+__device__ inline u32x4 as_u32x4(f32x4 v) { return __builtin_bit_cast(u32x4, v); }
+
+// ------------------------------------------------------------------------------------------
+// Read-copy codecs.
+// bf16: the top half of an fp32 word, rounded to nearest, ties to the even 16-bit code.
+// e4m3: OCP FP8 E4M3FN (bias 7, 3 mantissa bits, max 448, no infinities), saturating.
+// ------------------------------------------------------------------------------------------
+__device__ inline unsigned bf16_rne(float f)
+{
+    const unsigned u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Encode v (already multiplied by 1/scale) to an e4m3fn code. |v| is clamped to 448. Below 2^-6
+// the codes are the multiples of 2^-9, so the code is rint(|v| * 512) (exact scaling, RNE).
+// Above, the fp32 exponent/mantissa are rounded from 23 to 3 mantissa bits with ties to even;
+// a mantissa carry moves into the exponent as it should, and re-biasing 127 -> 7 subtracts
+// 120 << 3 from the (exponent:mantissa) field.
+__device__ inline unsigned e4m3_encode(float v)
+{
+    const unsigned sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float m = fminf(fabsf(v), 448.0f);
+    unsigned code;
+    if (m < 0.015625f) {
+        code = (unsigned)rintf(m * 512.0f);
+    } else {
+        const unsigned u = __float_as_uint(m);
+        unsigned base = u >> 20;
+        const unsigned rem = u & 0xFFFFFu;
+        base += (rem > 0x80000u || (rem == 0x80000u && (base & 1u))) ? 1u : 0u;
+        code = base - (120u << 3);
+    }
+    return code | sign;
+}
+
+// Decode an e4m3fn code (NaN codes never occur: the encoder saturates).
+__device__ inline float e4m3_decode(unsigned c)
+{
+    const unsigned mag = c & 0x7Fu;
+    const float f = mag < 8u ? (float)mag * 0.001953125f : __uint_as_float((mag << 20) + (120u << 23));
+    return (c & 0x80u) ? -f : f;
+}
+
+// Dot product of one 16-byte chunk of a state row with the matching slice of C.
+template <int PREC>
+__device__ inline float chunk_dot(u32x4 v, const float *c);
+
+template <>
+__device__ inline float chunk_dot<PREC_F32>(u32x4 v, const float *c)
+{
+    const f32x4 f = as_f32x4(v);
+    float s = f.x * c[0];
+    s = fmaf(f.y, c[1], s);
+    s = fmaf(f.z, c[2], s);
+    return fmaf(f.w, c[3], s);
+}
+
+template <>
+__device__ inline float chunk_dot<PREC_BF16>(u32x4 v, const float *c)
+{
+    float s = bf16_lo(v.x) * c[0];
+    s = fmaf(bf16_hi(v.x), c[1], s);
+    s = fmaf(bf16_lo(v.y), c[2], s);
+    s = fmaf(bf16_hi(v.y), c[3], s);
+    s = fmaf(bf16_lo(v.z), c[4], s);
+    s = fmaf(bf16_hi(v.z), c[5], s);
+    s = fmaf(bf16_lo(v.w), c[6], s);
+    return fmaf(bf16_hi(v.w), c[7], s);
+}
+
+template <>
+__device__ inline float chunk_dot<PREC_FP8>(u32x4 v, const float *c)
+{
+    float s = 0.0f;
+    const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s = fmaf(e4m3_decode((w[i] >> (8 * j)) & 0xFFu), c[4 * i + j], s);
+    return s;
+}
+
+// ------------------------------------------------------------------------------------------
+// Transpose-reduce. Each lane holds M partial sums (M a power of two); the LPR consecutive lanes
+// of a row group must each sum over the group. At every exchange step with lane offset o the
+// pair (l, l^o) splits its list: the lane with bit o clear keeps the first half and receives the
+// partner's first half, the other keeps the second half. Once one value is left, the remaining
+// offsets are plain butterflies. Afterwards a lane holds max(1, M/LPR) complete sums: those of
+// list entries [first, first + count) with first = its selected bits, see tr_first().
+// ------------------------------------------------------------------------------------------
+template <int M, int O, int NCUR>
+struct TransposeStep {
+    __device__ static inline void run(float (&v)[M], int lane)
+    {
+        if constexpr (O >= 1) {
+            if constexpr (NCUR > 1) {
+                constexpr int half = NCUR / 2;
+                const bool upper = (lane & O) != 0;
+#pragma unroll
+                for (int m = 0; m < half; ++m) {
+                    const float send = upper ? v[m] : v[half + m];
+                    const float keep = upper ? v[half + m] : v[m];
+                    v[m] = keep + __shfl_xor(send, O, 64);
+                }
+                TransposeStep<M, O / 2, half>::run(v, lane);
+            } else {
+                v[0] += __shfl_xor(v[0], O, 64);
+                TransposeStep<M, O / 2, 1>::run(v, lane);
+            }
+        }
+    }
+};
+
+template <int M, int LPR>
+__device__ inline void transpose_reduce(float (&v)[M], int lane)
+{
+    TransposeStep<M, LPR / 2, M>::run(v, lane);
+}
+
+// Index (into the original list) of the first complete sum a lane holds after transpose_reduce,
+// and whether the lane is the designated writer among its replicas.
+template <int M, int LPR>
+__device__ inline int tr_first(int lane, bool *writer)
+{
+    int n = M, first = 0;
+    bool w = true;
+    for (int o = LPR / 2; o >= 1; o >>= 1) {
+        if (n > 1) {
+            if (lane & o) first += n / 2;
+            n /= 2;
+        } else if (lane & o) {
+            w = false;
+        }
+    }
+    *writer = w;
+    return first;
+}
+
+template <int M, int LPR>
+constexpr int tr_count() { return M / LPR > 1 ? M / LPR : 1; }
+
+__device__ inline float group_max(float v, int width)
+{
+    for (int o = width / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Block-wide max of a non-negative value (all threads return it). `red` holds kWaves floats.
+__device__ inline float block_max(float v, float *red)
+{
+    v = group_max(v, 64);
+    const int wave = threadIdx.x / 64;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
+    __syncthreads();
+    return m;
+}
+
+// ------------------------------------------------------------------------------------------
+// Per-sequence completion: every work-group of sequence b increments counter[b] once per
+// launch, after all its reads of the pointers; the last one to arrive writes the new pointers
+// and re-arms the counter. Pointers can therefore be updated in place within the launch that
+// reads them, which keeps every call a single launch and safe to replay in a captured graph.
+// ------------------------------------------------------------------------------------------
+__device__ inline void seq_done(const Layer &Ld, int b, int new_pos, int new_ckpt)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned expected = (unsigned)(Ld.H * Ld.psplit);
+        const unsigned prev = __hip_atomic_fetch_add(&Ld.counter[b], 1u, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (prev + 1u == expected) {
+            Ld.pos[b] = new_pos;
+            Ld.ckpt[b] = new_ckpt;
+            __hip_atomic_store(&Ld.counter[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+__device__ inline void raise_flag(const Layer &Ld, unsigned bits)
+{
+    if (threadIdx.x == 0) __hip_atomic_fetch_or(Ld.flag, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline float fast_exp(float v) { return __expf(v); }
+
+}  // namespace rssm

@@ -1,0 +1,79 @@
+"""Algorithmic HBM bytes of each kernel class, per sequence and step (the roofline's numerator).
+
+Counted once per byte the method must move: each state/copy element read or written once, every
+input read once, every record written once and every stored record the window needs read once
+(B of a group counted once per sequence, as it is shared by the group's heads). Indices, pointers
+and the per-head fp8 scales of a read are tiny and are counted where they are part of the format.
+
+Shapes: H heads, P headdim, N state, G groups; `k` = records in the window including the current
+token (1..L).
+"""
+
+F32 = 4
+ELEM = {"fp32": 4, "bf16": 2, "fp8": 1}
+
+
+def state_bytes(H, P, N, prec="fp32"):
+    b = H * P * N * ELEM[prec]
+    return b + (H * F32 if prec == "fp8" else 0)
+
+
+def token_input_bytes(H, P, N, G):
+    """x, B, C, dt of one token (read by every call that consumes a token)."""
+    return F32 * (H * P + 2 * G * N + H)
+
+
+def record_write_bytes(H, P, N, G, store_C=True):
+    return F32 * (H * P + (2 if store_C else 1) * G * N + H)
+
+
+def record_read_bytes(H, P, N, G):
+    """A stored record as replay and flush read it: x, B, dt (C of past tokens is never read)."""
+    return F32 * (H * P + G * N + H)
+
+
+def output_bytes(H, P):
+    return F32 * H * P
+
+
+def replay_nonflush(H, P, N, G, k, prec="fp32", store_C=True):
+    return (state_bytes(H, P, N, prec) + token_input_bytes(H, P, N, G) +
+            record_write_bytes(H, P, N, G, store_C) + output_bytes(H, P) +
+            (k - 1) * record_read_bytes(H, P, N, G))
+
+
+def replay_flush_step(H, P, N, G, L, prec="fp32"):
+    """Fused flush step: read the fp32 master, write it and the read copy; read the L-1 stored
+    records and this token's inputs; write y. The token's record is folded, not stored."""
+    copy = 0 if prec == "fp32" else state_bytes(H, P, N, prec)
+    return (2 * state_bytes(H, P, N, "fp32") + copy + token_input_bytes(H, P, N, G) +
+            output_bytes(H, P) + (L - 1) * record_read_bytes(H, P, N, G))
+
+
+def replay_window_amortized(H, P, N, G, L, prec="fp32", store_C=True):
+    """Mean bytes per step over one window of L steps (L-1 non-flush steps + 1 flush step)."""
+    tot = sum(replay_nonflush(H, P, N, G, k, prec, store_C) for k in range(1, L))
+    return (tot + replay_flush_step(H, P, N, G, L, prec)) / L
+
+
+def conventional(H, P, N, G):
+    return 2 * state_bytes(H, P, N) + token_input_bytes(H, P, N, G) + output_bytes(H, P)
+
+
+def verify(H, P, N, G, T, k_old, prec="fp32", store_C=True):
+    """Spec verify: one read of the checkpoint copy for T queries, T token inputs, T record
+    writes, T outputs, and the k_old committed records."""
+    return (state_bytes(H, P, N, prec) + T * (token_input_bytes(H, P, N, G) +
+            record_write_bytes(H, P, N, G, store_C) + output_bytes(H, P)) +
+            k_old * record_read_bytes(H, P, N, G))
+
+
+def rollback_flush(H, P, N, G, count, prec="fp32"):
+    """Commit-time flush of `count` records (master read + write, read copy write)."""
+    copy = 0 if prec == "fp32" else state_bytes(H, P, N, prec)
+    return 2 * state_bytes(H, P, N, "fp32") + copy + count * record_read_bytes(H, P, N, G)
+
+
+def snapshot_verify(H, P, N, G, T):
+    """Per-draft snapshot baseline: one state read and T state writes, plus T tokens of I/O."""
+    return (1 + T) * state_bytes(H, P, N) + T * (token_input_bytes(H, P, N, G) + output_bytes(H, P))

@@ -1,0 +1,190 @@
+/*
+ * replayssm.h -- C ABI of the ReplaySSM Mamba-2 decode-step library for AMD MI355X (gfx950).
+ *
+ * The method (described in prose by three web pages; cited by page and section):
+ *   [AT Pulse]   "NVIDIA and Princeton's ReplaySSM stores a checkpoint and recent inputs instead of
+ *                full SSM state to speed up hybrid-model decoding" (at-pulse.com, story 2558)
+ *   [Clarity]    "NVIDIA and Princeton cache SSM inputs in place of state to speed hybrid-model
+ *                decoding" (theclarity.today)
+ *   [WittyWires] "ReplaySSM cuts memory traffic to speed up hybrid-model decoding"
+ *
+ * A Mamba-2 layer's per-sequence state S[h,p,n] is kept as a checkpoint S_c (all tokens before
+ * ckpt_pos folded in) plus a buffer of per-token records (x, B, C, dt) for the tokens since. A
+ * decode step forms its output from the checkpoint and the records and stores only its own record;
+ * when the buffer fills, a flush folds it into the checkpoint. With a = exp(dt*A_h), the layer
+ * computes exactly the Mamba-2 recurrence S <- a*S + dt * x (outer) B, y = S.C + D*x (update,
+ * then read), unrolled over the window of records since the checkpoint:
+ *     y_t[p] = decay_t * (S_c[p,:] . C_t) + sum_{j=c..t} w_j * (B_j . C_t) * x_j[p] + D_h * x_t[p]
+ *     decay_t = exp(A_h * sum_{i=c..t} dt_i),   w_j = dt_j * exp(A_h * sum_{i=j+1..t} dt_i)
+ *     flush:  S_c <- decay_t * S_c + sum_j w_j * x_j (outer) B_j
+ *
+ * Shapes: batch Bt sequences, H heads of headdim P, state size N, G groups (head h reads group
+ * h / (H/G) of B and C), buffer length L. All arrays are row-major, last index fastest:
+ *     x [Bt,H,P]  B, C [Bt,G,N]  dt [Bt,H] (positive: softplus already applied)  A, D [H]
+ *     state [Bt,H,P,N]  y [Bt,H,P]
+ *     spec-decode inputs: x [Bt,T,H,P]  B, C [Bt,T,G,N]  dt [Bt,T,H]  y [Bt,T,H,P]
+ * All float arrays are fp32. Supported: N in {16, 32, 64, 128, 256}; P a multiple of 4, at most
+ * 256; 1 <= L <= 64; 1 <= max_draft <= min(L, 8); H a multiple of G. The fp8 read copy needs
+ * P <= 64 (one work-group owns a whole head tile, so the per-head scale is exact).
+ *
+ * Memory. The caller owns every device buffer: inputs, outputs, A, D and the workspace (from
+ * PyTorch or hipMalloc). The library allocates no device memory. The handle is host memory.
+ * Device pointers must be 16-byte aligned; the workspace 256-byte aligned.
+ *
+ * Streams. `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work on
+ * it, except replayssm_get_pointers / replayssm_check / replayssm_materialize_state's status, which
+ * synchronize it. Inputs must stay valid until the stream reaches the call.
+ *
+ * Errors. Every call returns rssm_status; nothing aborts and nothing throws across the ABI.
+ * Argument, shape and state-machine errors are detected on the host before any launch (so they
+ * never touch the GPU). Kernels validate each sequence's pointers before any indexed access; a
+ * breach (e.g. a pointer array corrupted by the caller) sets a device flag, the affected
+ * sequences are skipped, and replayssm_check / replayssm_get_pointers return RSSM_E_STATE; from then
+ * on the handle refuses work until replayssm_load_state. A handle is not thread-safe; separate
+ * handles are independent.
+ */
+#ifndef REPLAYSSM_H
+#define REPLAYSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct replayssm_layer *replayssm_t;
+
+typedef enum {
+    RSSM_OK = 0,
+    RSSM_E_INVAL = -1,        /* bad argument, pointer, alignment or shape */
+    RSSM_E_WORKSPACE = -2,    /* workspace NULL, misaligned or smaller than required */
+    RSSM_E_HIP = -3,          /* a HIP runtime call or kernel launch failed */
+    RSSM_E_STATE = -4,        /* state-machine misuse, or the device invariant flag is set */
+    RSSM_E_UNSUPPORTED = -5   /* valid but unsupported configuration */
+} rssm_status;
+
+typedef enum { RSSM_READ_FP32 = 0, RSSM_READ_BF16 = 1, RSSM_READ_FP8_E4M3 = 2 } rssm_read_prec;
+
+typedef struct {
+    int32_t batch;       /* Bt >= 0 (0: every call is a no-op) */
+    int32_t nheads;      /* H */
+    int32_t headdim;     /* P */
+    int32_t dstate;      /* N */
+    int32_t ngroups;     /* G */
+    int32_t buffer_len;  /* L: records kept before a flush ([AT Pulse] "Technical analysis") */
+    int32_t max_draft;   /* T_max: 1 = standard decode only; >1 enables spec verify/rollback */
+    int32_t read_prec;   /* rssm_read_prec: precision of the checkpoint copy that serves reads */
+    int32_t store_C;     /* 1: records also keep C (the record is (x, B, C, dt)); 0: (x, B, dt) */
+} replayssm_config;
+
+/* Byte offsets of the workspace regions (for inspection by tests and tools). */
+typedef struct {
+    size_t master;     /* fp32 checkpoint [Bt,H,P,N] -- updated only by flushes */
+    size_t read_copy;  /* bf16 [Bt,H,P,N] or fp8 e4m3fn [Bt,H,P,N]; 0 bytes for fp32 reads */
+    size_t scale;      /* fp32 [Bt,H] per-head scale of the fp8 copy (0 bytes otherwise) */
+    size_t ring_x;     /* fp32 [Bt,H,L,P]: record of absolute position q sits in slot q mod L */
+    size_t ring_B;     /* fp32 [Bt,G,L,N] */
+    size_t ring_C;     /* fp32 [Bt,G,L,N] (0 bytes when store_C = 0) */
+    size_t ring_dt;    /* fp32 [Bt,H,L] */
+    size_t pos;        /* int32 [Bt]: tokens committed */
+    size_t ckpt_pos;   /* int32 [Bt]: tokens folded into the checkpoint */
+    size_t counters;   /* uint32 [Bt]: per-launch completion counters (zero between launches) */
+    size_t flag;       /* uint32 [1]: device invariant flag */
+    size_t total;      /* bytes required */
+} replayssm_layout;
+
+/* Workspace bytes for a configuration; 0 if the configuration is invalid. */
+size_t replayssm_workspace_bytes(const replayssm_config *cfg);
+
+/* Fill `out` with the workspace layout of a valid configuration. */
+rssm_status replayssm_workspace_layout(const replayssm_config *cfg, replayssm_layout *out);
+
+/* Validate `cfg`, carve the caller's device workspace (>= replayssm_workspace_bytes bytes,
+ * 256-byte aligned, owned by the caller and outliving the handle) and return a host handle.
+ * A and D are device arrays [H] (per-head decay rate, negative, and skip weight), read at every
+ * call, so they must outlive the handle too. No device work is done: call replayssm_load_state
+ * before the first step. */
+rssm_status replayssm_create(const replayssm_config *cfg, void *workspace, size_t bytes,
+                             const float *A, const float *D, replayssm_t *out);
+
+/* Free the host handle (the workspace stays the caller's). NULL is accepted. */
+rssm_status replayssm_destroy(replayssm_t layer);
+
+/* Start every sequence from `state` (device fp32 [Bt,H,P,N]): the checkpoint master becomes a
+ * copy of it, the read copy is encoded from it, pos = ckpt_pos = 0, the buffers are emptied and
+ * the device flag and any pending verify are cleared. */
+rssm_status replayssm_load_state(replayssm_t layer, const float *state, void *stream);
+
+/* Standard decode step for every sequence ([AT Pulse] lede and "Technical analysis"; [Clarity]
+ * claim ledger [18]): store the token's record in ring slot pos mod L, form
+ * y (device fp32 [Bt,H,P]) by replay from the checkpoint read copy plus the window's records, and
+ * advance pos by 1. When more than L - max_draft records are then pending (for standard decode:
+ * when the buffer is full, i.e. every L steps -- [WittyWires] "What happened"), the same launch
+ * flushes the sequence: it folds the records into the fp32 master, rewrites the read copy, sets
+ * ckpt_pos = pos and reads y from the folded fp32 state. Inputs: x [Bt,H,P], B, C [Bt,G,N],
+ * dt [Bt,H]. RSSM_E_STATE if a verify is pending. */
+rssm_status replayssm_step(replayssm_t layer, const float *x, const float *B, const float *C,
+                           const float *dt, float *y, void *stream);
+
+/* Fold every committed record of the selected sequences into the checkpoint (seq_mask: device
+ * int32 [Bt], nonzero = flush; NULL = all), rewrite their read copy, set ckpt_pos = pos.
+ * Sequences with no pending record are untouched. RSSM_E_STATE if a verify is pending. */
+rssm_status replayssm_flush(replayssm_t layer, const int32_t *seq_mask, void *stream);
+
+/* Speculative verify, output-only ([AT Pulse] "Technical analysis": output-only evaluation that
+ * builds no intermediate state): for T draft tokens per sequence (1 <= T <= max_draft), write
+ * their records into ring slots (pos + i) mod L and their outputs y [Bt,T,H,P], each formed by
+ * replay over the committed window plus the drafts up to and including itself. No state is
+ * written and no pointer moves. Requires no pending verify; leaves one pending. */
+rssm_status replayssm_spec_verify(replayssm_t layer, int32_t T, const float *x, const float *B,
+                                  const float *C, const float *dt, float *y, void *stream);
+
+/* Resolve the pending verify ([AT Pulse] "Technical analysis" and [Clarity] "Why it matters":
+ * rejected drafts are discarded by moving the buffer pointer): pos += accepted[b] (device int32
+ * [Bt], each in [0, T]); then sequences with more than L - max_draft pending records flush.
+ * Accepted counts outside [0, T] set the device flag and leave that sequence unchanged. */
+rssm_status replayssm_rollback(replayssm_t layer, const int32_t *accepted, void *stream);
+
+/* Copy pos and ckpt_pos (host int32 [Bt] each; either may be NULL) after synchronizing the
+ * stream. RSSM_E_STATE if the device flag is set. */
+rssm_status replayssm_get_pointers(replayssm_t layer, int32_t *pos, int32_t *ckpt_pos,
+                                   void *stream);
+
+/* Synchronize the stream and report the device flag (RSSM_E_STATE when set). */
+rssm_status replayssm_check(replayssm_t layer, void *stream);
+
+/* Write the full current state (checkpoint with all committed records folded in) to `out`
+ * (device fp32 [Bt,H,P,N]) without committing anything. For tests and for saving a state. */
+rssm_status replayssm_materialize_state(replayssm_t layer, float *out, void *stream);
+
+/* Baseline: conventional Mamba-2 decode step ([Clarity] "Why it matters" and claim ledger [6],
+ * [7]): read the state, update it, read the output from it and write it back, in place.
+ * state [Bt,H,P,N] in/out; y [Bt,H,P]. Only batch, nheads, headdim, dstate, ngroups of cfg are
+ * used. */
+rssm_status conventional_step(const replayssm_config *cfg, float *state, const float *x,
+                              const float *B, const float *C, const float *dt, const float *A,
+                              const float *D, float *y, void *stream);
+
+/* Baseline for speculative decoding with per-draft snapshots ([Clarity] "What happened" and claim
+ * ledger [13]): slots [Bt,T+1,H,P,N] hold T+1 states per sequence, cur [Bt] (device int32) the
+ * committed one. Reads slot cur once, runs the T drafts stepwise, writes the state after draft i
+ * to slot (cur + i) mod (T+1) and y [Bt,T,H,P]. cur is not changed. */
+rssm_status snapshot_spec_verify(const replayssm_config *cfg, float *slots, const int32_t *cur,
+                                 int32_t T, const float *x, const float *B, const float *C,
+                                 const float *dt, const float *A, const float *D, float *y,
+                                 void *stream);
+
+/* Commit for the snapshot baseline: cur[b] <- (cur[b] + accepted[b]) mod (T+1). Accepted counts
+ * outside [0, T] leave cur unchanged. */
+rssm_status snapshot_commit(const replayssm_config *cfg, int32_t *cur, const int32_t *accepted,
+                            int32_t T, void *stream);
+
+/* Static description of a status code. */
+const char *replayssm_status_string(rssm_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REPLAYSSM_H */

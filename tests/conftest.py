@@ -9,3 +9,18 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+def pytest_collection_modifyitems(config, items):
+    import pytest
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:
+        has_gpu = False
+    if has_gpu:
+        return
+    skip = pytest.mark.skip(reason="needs a GPU")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

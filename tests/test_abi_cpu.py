@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the header declares,
+sizes and lays out the workspace, and rejects bad arguments and state-machine misuse on the host
+before any HIP call (batch 0 makes every accepted call a no-op, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_mamba_decode_amd as rs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "replayssm.h")
+FAKE = 0x10000  # a 256-byte-aligned fake device address; never dereferenced in these tests
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(rs._lib, n), f"{n} declared in replayssm.h but not exported"
+    assert set(names) == set(rs.EXPORTED)
+
+
+def cfg(**kw):
+    base = dict(batch=0, nheads=128, headdim=64, dstate=128, ngroups=8, buffer_len=16, max_draft=1,
+                read_prec="fp32", store_C=True)
+    base.update(kw)
+    return rs.make_config(**base)
+
+
+def test_workspace_layout_serving_shape():
+    c = cfg(batch=256)
+    lay = rs.replayssm_workspace_layout(c)
+    Bt, H, P, N, G, L = 256, 128, 64, 128, 8, 16
+    assert lay.master == 0
+    assert lay.read_copy == Bt * H * P * N * 4                 # fp32 reads: no copy
+    assert lay.ring_B - lay.ring_x == Bt * H * L * P * 4
+    assert lay.ring_C - lay.ring_B == Bt * G * L * N * 4
+    assert lay.ring_dt - lay.ring_C == Bt * G * L * N * 4
+    assert lay.total == rs.replayssm_workspace_bytes(c)
+    for name in ("master", "read_copy", "scale", "ring_x", "ring_B", "ring_C", "ring_dt", "pos",
+                 "ckpt_pos", "counters", "flag"):
+        assert getattr(lay, name) % 256 == 0
+    c8 = cfg(batch=256, read_prec="fp8")
+    l8 = rs.replayssm_workspace_layout(c8)
+    assert l8.scale - l8.read_copy == Bt * H * P * N           # one byte per element
+    assert l8.ring_x - l8.scale == Bt * H * 4
+    cb = cfg(batch=256, read_prec="bf16", store_C=False)
+    lb = rs.replayssm_workspace_layout(cb)
+    assert lb.scale - lb.read_copy == Bt * H * P * N * 2
+    assert lb.ring_C == lb.ring_dt                               # no C in the records
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dstate=48), rs.RSSM_E_UNSUPPORTED),
+    (dict(dstate=512), rs.RSSM_E_UNSUPPORTED),
+    (dict(headdim=66), rs.RSSM_E_INVAL),
+    (dict(headdim=260), rs.RSSM_E_UNSUPPORTED),
+    (dict(nheads=6, ngroups=4), rs.RSSM_E_INVAL),
+    (dict(buffer_len=0), rs.RSSM_E_INVAL),
+    (dict(buffer_len=4, max_draft=5), rs.RSSM_E_INVAL),
+    (dict(buffer_len=65), rs.RSSM_E_UNSUPPORTED),
+    (dict(buffer_len=16, max_draft=9), rs.RSSM_E_UNSUPPORTED),
+    (dict(read_prec=3), rs.RSSM_E_INVAL),
+    (dict(read_prec="fp8", headdim=128), rs.RSSM_E_UNSUPPORTED),
+    (dict(batch=-1), rs.RSSM_E_INVAL),
+    (dict(store_C=2), rs.RSSM_E_INVAL),
+])
+def test_invalid_configs_rejected(kw, status):
+    c = cfg(**kw)
+    if kw.get("store_C") == 2:
+        c.store_C = 2
+    assert rs.replayssm_workspace_bytes(c) == 0
+    h = ctypes.c_void_p()
+    st = rs._lib.replayssm_create(ctypes.byref(c), FAKE, 1 << 40, FAKE, FAKE, ctypes.byref(h))
+    assert st == status
+    assert not h.value
+
+
+def test_workspace_errors():
+    c = cfg(batch=4)
+    need = rs.replayssm_workspace_bytes(c)
+    h = ctypes.c_void_p()
+    create = rs._lib.replayssm_create
+    assert create(ctypes.byref(c), None, need, FAKE, FAKE, ctypes.byref(h)) == rs.RSSM_E_WORKSPACE
+    assert create(ctypes.byref(c), FAKE + 16, need, FAKE, FAKE, ctypes.byref(h)) == rs.RSSM_E_WORKSPACE
+    assert create(ctypes.byref(c), FAKE, need - 1, FAKE, FAKE, ctypes.byref(h)) == rs.RSSM_E_WORKSPACE
+    assert create(ctypes.byref(c), FAKE, need, None, FAKE, ctypes.byref(h)) == rs.RSSM_E_INVAL
+    assert create(ctypes.byref(c), FAKE, need, FAKE, FAKE, None) == rs.RSSM_E_INVAL
+    assert create(ctypes.byref(c), FAKE, need, FAKE, FAKE, ctypes.byref(h)) == rs.RSSM_OK
+    assert rs._lib.replayssm_destroy(h) == rs.RSSM_OK
+    assert rs._lib.replayssm_destroy(None) == rs.RSSM_OK
+
+
+def _handle(**kw):
+    c = cfg(**kw)
+    h = ctypes.c_void_p()
+    assert rs._lib.replayssm_create(ctypes.byref(c), FAKE, rs.replayssm_workspace_bytes(c), FAKE, FAKE,
+                                    ctypes.byref(h)) == rs.RSSM_OK
+    return h
+
+
+def test_state_machine_on_host():
+    L = rs._lib
+    h = _handle(max_draft=4)
+    io = [FAKE] * 5
+    assert L.replayssm_step(h, *io, None) == rs.RSSM_E_STATE            # before load_state
+    assert L.replayssm_spec_verify(h, 2, *io, None) == rs.RSSM_E_STATE
+    assert L.replayssm_load_state(h, None, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_load_state(h, FAKE, None) == rs.RSSM_OK          # batch 0: nothing launched
+    assert L.replayssm_step(h, *io, None) == rs.RSSM_OK
+    assert L.replayssm_step(h, FAKE, FAKE, None, FAKE, FAKE, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_step(h, FAKE + 4, FAKE, FAKE, FAKE, FAKE, None) == rs.RSSM_E_INVAL  # misaligned
+    assert L.replayssm_rollback(h, FAKE, None) == rs.RSSM_E_STATE         # no verify pending
+    assert L.replayssm_spec_verify(h, 0, *io, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_spec_verify(h, 5, *io, None) == rs.RSSM_E_INVAL    # T > max_draft
+    assert L.replayssm_spec_verify(h, 4, *io, None) == rs.RSSM_OK
+    assert L.replayssm_spec_verify(h, 2, *io, None) == rs.RSSM_E_STATE    # verify twice
+    assert L.replayssm_step(h, *io, None) == rs.RSSM_E_STATE              # step while pending
+    assert L.replayssm_flush(h, None, None) == rs.RSSM_E_STATE            # flush while pending
+    assert L.replayssm_rollback(h, None, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_rollback(h, FAKE, None) == rs.RSSM_OK
+    assert L.replayssm_rollback(h, FAKE, None) == rs.RSSM_E_STATE
+    assert L.replayssm_flush(h, None, None) == rs.RSSM_OK
+    assert L.replayssm_materialize_state(h, None, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_materialize_state(h, FAKE, None) == rs.RSSM_OK
+    assert L.replayssm_destroy(h) == rs.RSSM_OK
+
+
+def test_baselines_validate():
+    L = rs._lib
+    c = cfg()
+    args = [FAKE] * 8
+    assert L.conventional_step(ctypes.byref(c), *args, None) == rs.RSSM_OK
+    bad = cfg(dstate=24)
+    assert L.conventional_step(ctypes.byref(bad), *args, None) == rs.RSSM_E_UNSUPPORTED
+    assert L.conventional_step(None, *args, None) == rs.RSSM_E_INVAL
+    assert L.conventional_step(ctypes.byref(c), None, *args[1:], None) == rs.RSSM_E_INVAL
+    assert L.snapshot_spec_verify(ctypes.byref(c), FAKE, FAKE, 4, *([FAKE] * 7), None) == rs.RSSM_OK
+    assert L.snapshot_spec_verify(ctypes.byref(c), FAKE, FAKE, 0, *([FAKE] * 7), None) == rs.RSSM_E_INVAL
+    assert L.snapshot_spec_verify(ctypes.byref(c), FAKE, FAKE, 9, *([FAKE] * 7), None) == rs.RSSM_E_INVAL
+    assert L.snapshot_commit(ctypes.byref(c), FAKE, FAKE, 4, None) == rs.RSSM_OK
+    assert L.snapshot_commit(ctypes.byref(c), FAKE, None, 4, None) == rs.RSSM_E_INVAL
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(rs.replayssm_status_string(s), str) and rs.replayssm_status_string(s)
