@@ -146,7 +146,10 @@ rssm_status ready(replayssm_t h)
     return RSSM_OK;
 }
 
-bool ok_ptr(const void *p) { return p && aligned(p, 16); }
+// Device array arguments: 16-byte aligned and non-NULL; with batch 0 (empty arrays) NULL is
+// accepted too.
+bool ok_ptr(const void *p, int batch) { return p ? aligned(p, 16) : batch == 0; }
+bool ok_ptr4(const void *p, int batch) { return p ? aligned(p, 4) : batch == 0; }
 
 // Bounds on the pending-record count after every sequence commits `lo..hi` more records and
 // those with more than L - Tmax pending flush.
@@ -253,7 +256,7 @@ rssm_status replayssm_destroy(replayssm_t h)
 rssm_status replayssm_load_state(replayssm_t h, const float *state, void *stream)
 {
     if (!h) return RSSM_E_INVAL;
-    if (!ok_ptr(state)) return RSSM_E_INVAL;
+    if (!ok_ptr(state, h->cfg.batch)) return RSSM_E_INVAL;
     h->loaded = 1;
     h->poisoned = 0;
     h->pending_T = 0;
@@ -268,10 +271,13 @@ rssm_status replayssm_load_state(replayssm_t h, const float *state, void *stream
 rssm_status replayssm_step(replayssm_t h, const float *x, const float *B, const float *C,
                            const float *dt, float *y, void *stream)
 {
+    if (!h) return RSSM_E_INVAL;
+    const int bt = h->cfg.batch;
+    if (!ok_ptr(x, bt) || !ok_ptr(B, bt) || !ok_ptr(C, bt) || !ok_ptr(dt, bt) || !ok_ptr(y, bt))
+        return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
     if (h->pending_T) return RSSM_E_STATE;
-    if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(dt) || !ok_ptr(y)) return RSSM_E_INVAL;
     const bool flush_capable = h->cmax + 1 > h->cfg.buffer_len - h->cfg.max_draft;
     commit_bounds(h, 1, 1);
     if (h->cfg.batch == 0) return RSSM_OK;
@@ -284,10 +290,11 @@ rssm_status replayssm_step(replayssm_t h, const float *x, const float *B, const 
 
 rssm_status replayssm_flush(replayssm_t h, const int32_t *seq_mask, void *stream)
 {
+    if (!h) return RSSM_E_INVAL;
+    if (seq_mask && !aligned(seq_mask, 4)) return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
     if (h->pending_T) return RSSM_E_STATE;
-    if (seq_mask && !aligned(seq_mask, 4)) return RSSM_E_INVAL;
     if (!seq_mask) h->cmin = h->cmax = 0;
     else h->cmin = 0;
     if (h->cfg.batch == 0) return RSSM_OK;
@@ -300,11 +307,14 @@ rssm_status replayssm_flush(replayssm_t h, const int32_t *seq_mask, void *stream
 rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float *x, const float *B,
                                   const float *C, const float *dt, float *y, void *stream)
 {
+    if (!h) return RSSM_E_INVAL;
+    const int bt = h->cfg.batch;
+    if (T < 1 || T > h->cfg.max_draft) return RSSM_E_INVAL;
+    if (!ok_ptr(x, bt) || !ok_ptr(B, bt) || !ok_ptr(C, bt) || !ok_ptr(dt, bt) || !ok_ptr(y, bt))
+        return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
     if (h->pending_T) return RSSM_E_STATE;
-    if (T < 1 || T > h->cfg.max_draft) return RSSM_E_INVAL;
-    if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(dt) || !ok_ptr(y)) return RSSM_E_INVAL;
     h->pending_T = T;
     if (h->cfg.batch == 0) return RSSM_OK;
     const TokenIO io{x, B, C, dt, y};
@@ -316,10 +326,11 @@ rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float *x, cons
 
 rssm_status replayssm_rollback(replayssm_t h, const int32_t *accepted, void *stream)
 {
+    if (!h) return RSSM_E_INVAL;
+    if (!ok_ptr4(accepted, h->cfg.batch)) return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
     if (!h->pending_T) return RSSM_E_STATE;
-    if (!accepted || !aligned(accepted, 4)) return RSSM_E_INVAL;
     const int T = h->pending_T;
     h->pending_T = 0;
     commit_bounds(h, 0, T);
@@ -354,9 +365,10 @@ rssm_status replayssm_check(replayssm_t h, void *stream)
 
 rssm_status replayssm_materialize_state(replayssm_t h, float *out, void *stream)
 {
+    if (!h) return RSSM_E_INVAL;
+    if (!ok_ptr(out, h->cfg.batch)) return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (!ok_ptr(out)) return RSSM_E_INVAL;
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) launch_flush_n##NV(h->cfg.read_prec, h->lmax, h->dev, MODE_MATERIALIZE, nullptr, 0, out, st)
@@ -370,7 +382,10 @@ rssm_status conventional_step(const replayssm_config *cfg, float *state, const f
 {
     const rssm_status s = check_shape(cfg);
     if (s != RSSM_OK) return s;
-    if (!ok_ptr(state) || !ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(dt) || !ok_ptr(y)) return RSSM_E_INVAL;
+    const int bt = cfg->batch;
+    if (!ok_ptr(state, bt) || !ok_ptr(x, bt) || !ok_ptr(B, bt) || !ok_ptr(C, bt) || !ok_ptr(dt, bt) ||
+        !ok_ptr(y, bt))
+        return RSSM_E_INVAL;
     if (!A || !D || !aligned(A, 4) || !aligned(D, 4)) return RSSM_E_INVAL;
     if (cfg->batch == 0) return RSSM_OK;
     const Layer Ld = shape_layer(*cfg, A, D);
@@ -389,8 +404,9 @@ rssm_status snapshot_spec_verify(const replayssm_config *cfg, float *slots, cons
     const rssm_status s = check_shape(cfg);
     if (s != RSSM_OK) return s;
     if (T < 1 || T > 8) return RSSM_E_INVAL;
-    if (!ok_ptr(slots) || !cur || !aligned(cur, 4) || !ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) ||
-        !ok_ptr(dt) || !ok_ptr(y))
+    const int bt = cfg->batch;
+    if (!ok_ptr(slots, bt) || !ok_ptr4(cur, bt) || !ok_ptr(x, bt) || !ok_ptr(B, bt) || !ok_ptr(C, bt) ||
+        !ok_ptr(dt, bt) || !ok_ptr(y, bt))
         return RSSM_E_INVAL;
     if (!A || !D || !aligned(A, 4) || !aligned(D, 4)) return RSSM_E_INVAL;
     if (cfg->batch == 0) return RSSM_OK;
@@ -408,7 +424,7 @@ rssm_status snapshot_commit(const replayssm_config *cfg, int32_t *cur, const int
     const rssm_status s = check_shape(cfg);
     if (s != RSSM_OK) return s;
     if (T < 1 || T > 8) return RSSM_E_INVAL;
-    if (!cur || !accepted || !aligned(cur, 4) || !aligned(accepted, 4)) return RSSM_E_INVAL;
+    if (!ok_ptr4(cur, cfg->batch) || !ok_ptr4(accepted, cfg->batch)) return RSSM_E_INVAL;
     if (cfg->batch == 0) return RSSM_OK;
     return hip_status(launch_snapshot_commit(cur, accepted, T, cfg->batch, (hipStream_t)stream));
 }

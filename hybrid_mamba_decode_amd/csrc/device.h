@@ -263,13 +263,20 @@ __device__ inline float block_max(float v, float *red)
 // launch, after all its reads of the pointers; the last one to arrive writes the new pointers
 // and re-arms the counter. Pointers can therefore be updated in place within the launch that
 // reads them, which keeps every call a single launch and safe to replay in a captured graph.
+//
+// The increment is a relaxed device-scope atomic. Ordering needs no fence: the pointer loads of
+// every thread have returned before the work-group barrier below (it waits for all outstanding
+// memory operations), so they precede the increment, and the new values are read only by later
+// launches, which see them through the kernel-boundary cache maintenance. An acquire/release
+// atomic here would add an L2 write-back and invalidate per work-group (MI355X keeps one L2
+// per XCD), which costs more than the whole tile stream.
 // ------------------------------------------------------------------------------------------
 __device__ inline void seq_done(const Layer &Ld, int b, int new_pos, int new_ckpt)
 {
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned expected = (unsigned)(Ld.H * Ld.psplit);
-        const unsigned prev = __hip_atomic_fetch_add(&Ld.counter[b], 1u, __ATOMIC_ACQ_REL,
+        const unsigned prev = __hip_atomic_fetch_add(&Ld.counter[b], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         if (prev + 1u == expected) {
             Ld.pos[b] = new_pos;

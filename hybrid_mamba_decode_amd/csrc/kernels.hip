@@ -127,49 +127,72 @@ __device__ inline RecSrc ring_src(const Layer &Ld, const Tile &t, int ck, int nr
 
 template <int LMAX>
 struct Window {
-    float xw[LMAX][kRows];  // x of each record, this work-group's rows
-    float Bw[LMAX][NN];     // B of each record (the head's group)
+    float xw[LMAX][kRows] __attribute__((aligned(16)));  // x of each record, this work-group's rows
+    float Bw[LMAX][NN] __attribute__((aligned(16)));     // B of each record (the head's group)
     float dts[LMAX];
 };
 
-// Stage k <= LMAX records into LDS. All global loads of a chunk are issued before any LDS store.
+// Registers holding a window in flight: issue_window() starts every global load of the k <= LMAX
+// records, commit_window() stores them to LDS. Callers issue all their other global loads (state
+// rows, C) before committing, so one wait covers every load of the work-group.
 template <int LMAX>
-__device__ inline void stage_window(Window<LMAX> &w, const RecSrc &src, int k, int nrows)
+struct WindowRegs {
+    static constexpr int XU = kRows / 4, BU = NN / 4;
+    static constexpr int XS = (LMAX * XU + kThreads - 1) / kThreads;
+    static constexpr int BS = (LMAX * BU + kThreads - 1) / kThreads;
+    static constexpr int BCH = BS < 8 ? BS : 8;  // B loads held in registers at once
+    f32x4 xv[XS];
+    f32x4 bv[BCH];
+    float dv;
+};
+
+template <int LMAX>
+__device__ inline void issue_window(WindowRegs<LMAX> &r, const RecSrc &src, int k, int nrows)
 {
-    constexpr int XU = kRows / 4, BU = NN / 4;
-    constexpr int XS = (LMAX * XU + kThreads - 1) / kThreads;
-    constexpr int BS = (LMAX * BU + kThreads - 1) / kThreads;
+    using R = WindowRegs<LMAX>;
     const int tid = threadIdx.x;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    float dv = 0.f;
-    if (tid < k) dv = src.dt(tid);
-    f32x4 xv[XS];
+    r.dv = tid < k ? src.dt(tid) : 0.f;
 #pragma unroll
-    for (int s = 0; s < XS; ++s) {
-        const int e = tid + s * kThreads, j = e / XU, c = e % XU;
-        xv[s] = (j < k && 4 * c < nrows) ? *(const f32x4 *)(src.x(j) + 4 * c) : zero;
+    for (int s = 0; s < R::XS; ++s) {
+        const int e = tid + s * kThreads, j = e / R::XU, c = e % R::XU;
+        r.xv[s] = (j < k && 4 * c < nrows) ? *(const f32x4 *)(src.x(j) + 4 * c) : zero;
     }
-    constexpr int BCH = 8;  // at most 8 B loads in flight per lane per chunk
 #pragma unroll
-    for (int s0 = 0; s0 < BS; s0 += BCH) {
-        f32x4 bv[BCH];
+    for (int s = 0; s < R::BCH; ++s) {
+        const int e = tid + s * kThreads, j = e / R::BU, c = e % R::BU;
+        r.bv[s] = (j < k) ? *(const f32x4 *)(src.B(j) + 4 * c) : zero;
+    }
+}
+
+template <int LMAX>
+__device__ inline void commit_window(Window<LMAX> &w, WindowRegs<LMAX> &r, const RecSrc &src, int k)
+{
+    using R = WindowRegs<LMAX>;
+    const int tid = threadIdx.x;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < BCH; ++s) {
-            const int e = tid + (s0 + s) * kThreads, j = e / BU, c = e % BU;
-            bv[s] = (s0 + s < BS && j < k) ? *(const f32x4 *)(src.B(j) + 4 * c) : zero;
+    for (int s = 0; s < R::XS; ++s) {
+        const int e = tid + s * kThreads, j = e / R::XU, c = e % R::XU;
+        if (j < LMAX) *(f32x4 *)&w.xw[j][4 * c] = r.xv[s];
+    }
+    if (tid < LMAX) w.dts[tid] = r.dv;
+    // B rows beyond the first BCH slots (large windows of wide states) go in further chunks.
+#pragma unroll
+    for (int s0 = 0; s0 < R::BS; s0 += R::BCH) {
+        if (s0 > 0) {
+#pragma unroll
+            for (int s = 0; s < R::BCH; ++s) {
+                const int e = tid + (s0 + s) * kThreads, j = e / R::BU, c = e % R::BU;
+                r.bv[s] = (s0 + s < R::BS && j < k) ? *(const f32x4 *)(src.B(j) + 4 * c) : zero;
+            }
         }
 #pragma unroll
-        for (int s = 0; s < BCH; ++s) {
-            const int e = tid + (s0 + s) * kThreads, j = e / BU, c = e % BU;
-            if (s0 + s < BS && j < LMAX) *(f32x4 *)&w.Bw[j][4 * c] = bv[s];
+        for (int s = 0; s < R::BCH; ++s) {
+            const int e = tid + (s0 + s) * kThreads, j = e / R::BU, c = e % R::BU;
+            if (s0 + s < R::BS && j < LMAX) *(f32x4 *)&w.Bw[j][4 * c] = r.bv[s];
         }
     }
-#pragma unroll
-    for (int s = 0; s < XS; ++s) {
-        const int e = tid + s * kThreads, j = e / XU, c = e % XU;
-        if (j < LMAX) *(f32x4 *)&w.xw[j][4 * c] = xv[s];
-    }
-    if (tid < LMAX) w.dts[tid] = dv;
 }
 
 // Unrolled-window weights over records 0..last ([AT Pulse] "Technical analysis": the recurrence
@@ -314,7 +337,7 @@ __device__ inline void append_record(const Layer &Ld, const Tile &t, const Windo
 template <int LMAX>
 struct StepLds {
     Window<LMAX> win;
-    float Cq[NN];
+    float Cq[NN] __attribute__((aligned(16)));
     float w[LMAX];
     float coef[LMAX];
     float u[kRows];
@@ -357,9 +380,10 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io)
     src.fx = io.x + bh * Ld.P + t.row0;
     src.fB = io.B + ((size_t)t.b * Ld.G + t.g) * NN;
     src.fdt = io.dt + bh;
-    if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = *(const f32x4 *)(Ct + 4 * tid);
+    const f32x4 cq = tid < NN / 4 ? *(const f32x4 *)(Ct + 4 * tid) : f32x4{0.f, 0.f, 0.f, 0.f};
     const float A = Ld.A[t.h], Dh = Ld.D[t.h];
     const int slot = (int)((unsigned)pos % (unsigned)Ld.L);
+    WindowRegs<LMAX> wr;
 
     if (FLUSH && flush) {
         // Fused flush: fold all k records into the fp32 master rows.
@@ -375,7 +399,8 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io)
         }
         float cf[4];
         load_cchunk<PREC_F32>(cf, Ct, lane);
-        stage_window<LMAX>(s.win, src, k, t.nrows);
+        issue_window<LMAX>(wr, src, k, t.nrows);
+        commit_window<LMAX>(s.win, wr, src, k);
         __syncthreads();
         window_weights<LMAX, false>(s.win, nullptr, k - 1, A, s.w, nullptr, &s.decay);
         __syncthreads();
@@ -400,7 +425,9 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io)
     if (!kPreload) load_rows<PREC>(v, rrows, t.nrows, wave, lane);
     float cc[G::VEC];
     load_cchunk<PREC>(cc, Ct, lane);
-    stage_window<LMAX>(s.win, src, k, t.nrows);
+    issue_window<LMAX>(wr, src, k, t.nrows);
+    commit_window<LMAX>(s.win, wr, src, k);
+    if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = cq;
     float part[G::NL];
 #pragma unroll
     for (int i = 0; i < G::NL; ++i) part[i] = chunk_dot<PREC>(v[i], cc);
@@ -471,7 +498,9 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(Layer Ld, int mode, con
         u32x4 m[GF::NL];
         load_rows<PREC_F32>(m, (const char *)(Ld.master + elem0), t.nrows, wave, lane);
         const RecSrc src = ring_src(Ld, t, ck, count);
-        stage_window<LMAX>(s.win, src, count, t.nrows);
+        WindowRegs<LMAX> wr;
+        issue_window<LMAX>(wr, src, count, t.nrows);
+        commit_window<LMAX>(s.win, wr, src, count);
         __syncthreads();
         window_weights<LMAX, false>(s.win, nullptr, count - 1, Ld.A[t.h], s.w, nullptr, &s.decay);
         __syncthreads();
@@ -498,7 +527,7 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(Layer Ld, int mode, con
 template <int LMAX, int TQ>
 struct VerifyLds {
     Window<LMAX> win;
-    float Cq[TQ][NN];
+    float Cq[TQ][NN] __attribute__((aligned(16)));
     float coef[TQ][LMAX];
     float u[TQ][kRows];
     float decay[TQ];
@@ -543,11 +572,22 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
             for (int e = 0; e < G::VEC; ++e) cc[q][e] = 0.f;
         }
     }
-    for (int e = tid; e < T * (NN / 4); e += kThreads) {
-        const int q = e / (NN / 4), c = e % (NN / 4);
-        *(f32x4 *)&s.Cq[q][4 * c] = *(const f32x4 *)(io.C + (((size_t)t.b * T + q) * Ld.G + t.g) * NN + 4 * c);
+    constexpr int CQS = (TQ * (NN / 4) + kThreads - 1) / kThreads;
+    f32x4 cqr[CQS];
+#pragma unroll
+    for (int i = 0; i < CQS; ++i) {
+        const int e = tid + i * kThreads, q = e / (NN / 4), c = e % (NN / 4);
+        cqr[i] = q < T ? *(const f32x4 *)(io.C + (((size_t)t.b * T + q) * Ld.G + t.g) * NN + 4 * c)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    stage_window<LMAX>(s.win, src, kw, t.nrows);
+    WindowRegs<LMAX> wr;
+    issue_window<LMAX>(wr, src, kw, t.nrows);
+    commit_window<LMAX>(s.win, wr, src, kw);
+#pragma unroll
+    for (int i = 0; i < CQS; ++i) {
+        const int e = tid + i * kThreads, q = e / (NN / 4), c = e % (NN / 4);
+        if (q < TQ) *(f32x4 *)&s.Cq[q][4 * c] = cqr[i];
+    }
 
     float part[G::NL * TQ];
 #pragma unroll

@@ -29,7 +29,8 @@
  *
  * Memory. The caller owns every device buffer: inputs, outputs, A, D and the workspace (from
  * PyTorch or hipMalloc). The library allocates no device memory. The handle is host memory.
- * Device pointers must be 16-byte aligned; the workspace 256-byte aligned.
+ * Device float arrays must be 16-byte aligned, int32 arrays 4-byte aligned, the workspace
+ * 256-byte aligned. With batch 0 the (empty) batch arrays may be NULL.
  *
  * Streams. `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work on
  * it, except replayssm_get_pointers / replayssm_check / replayssm_materialize_state's status, which
@@ -37,11 +38,11 @@
  *
  * Errors. Every call returns rssm_status; nothing aborts and nothing throws across the ABI.
  * Argument, shape and state-machine errors are detected on the host before any launch (so they
- * never touch the GPU). Kernels validate each sequence's pointers before any indexed access; a
- * breach (e.g. a pointer array corrupted by the caller) sets a device flag, the affected
- * sequences are skipped, and replayssm_check / replayssm_get_pointers return RSSM_E_STATE; from then
- * on the handle refuses work until replayssm_load_state. A handle is not thread-safe; separate
- * handles are independent.
+ * never touch the GPU); argument errors are reported before state-machine errors. Kernels
+ * validate each sequence's pointers before any indexed access; a breach (e.g. a pointer array
+ * corrupted by the caller) sets a device flag, the affected sequences are skipped, and
+ * replayssm_check / replayssm_get_pointers return RSSM_E_STATE; from then on the handle refuses
+ * work until replayssm_load_state. A handle is not thread-safe; separate handles are independent.
  */
 #ifndef REPLAYSSM_H
 #define REPLAYSSM_H

@@ -109,15 +109,16 @@ def _handle(**kw):
 
 
 def test_state_machine_on_host():
+    """Batch 0: every accepted call is a no-op on the device, so the host state machine can be
+    driven completely without a GPU. Empty arrays may be NULL at batch 0."""
     L = rs._lib
     h = _handle(max_draft=4)
     io = [FAKE] * 5
     assert L.replayssm_step(h, *io, None) == rs.RSSM_E_STATE            # before load_state
     assert L.replayssm_spec_verify(h, 2, *io, None) == rs.RSSM_E_STATE
-    assert L.replayssm_load_state(h, None, None) == rs.RSSM_E_INVAL
-    assert L.replayssm_load_state(h, FAKE, None) == rs.RSSM_OK          # batch 0: nothing launched
+    assert L.replayssm_load_state(h, None, None) == rs.RSSM_OK          # batch 0: nothing launched
     assert L.replayssm_step(h, *io, None) == rs.RSSM_OK
-    assert L.replayssm_step(h, FAKE, FAKE, None, FAKE, FAKE, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_step(h, None, None, None, None, None, None) == rs.RSSM_OK
     assert L.replayssm_step(h, FAKE + 4, FAKE, FAKE, FAKE, FAKE, None) == rs.RSSM_E_INVAL  # misaligned
     assert L.replayssm_rollback(h, FAKE, None) == rs.RSSM_E_STATE         # no verify pending
     assert L.replayssm_spec_verify(h, 0, *io, None) == rs.RSSM_E_INVAL
@@ -126,12 +127,38 @@ def test_state_machine_on_host():
     assert L.replayssm_spec_verify(h, 2, *io, None) == rs.RSSM_E_STATE    # verify twice
     assert L.replayssm_step(h, *io, None) == rs.RSSM_E_STATE              # step while pending
     assert L.replayssm_flush(h, None, None) == rs.RSSM_E_STATE            # flush while pending
-    assert L.replayssm_rollback(h, None, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_rollback(h, FAKE + 2, None) == rs.RSSM_E_INVAL     # misaligned counts
     assert L.replayssm_rollback(h, FAKE, None) == rs.RSSM_OK
     assert L.replayssm_rollback(h, FAKE, None) == rs.RSSM_E_STATE
     assert L.replayssm_flush(h, None, None) == rs.RSSM_OK
-    assert L.replayssm_materialize_state(h, None, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_flush(h, FAKE + 2, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_materialize_state(h, FAKE + 8, None) == rs.RSSM_E_INVAL
     assert L.replayssm_materialize_state(h, FAKE, None) == rs.RSSM_OK
+    assert L.replayssm_destroy(h) == rs.RSSM_OK
+
+
+def test_pointer_validation_before_state():
+    """With a non-empty batch, NULL or misaligned device arrays are rejected before any state or
+    device work (the handle here is never loaded, so valid arguments stop at RSSM_E_STATE)."""
+    L = rs._lib
+    h = _handle(batch=2, max_draft=2)
+    io = [FAKE] * 5
+    assert L.replayssm_load_state(h, None, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_load_state(h, FAKE + 4, None) == rs.RSSM_E_INVAL
+    for i in range(5):
+        bad = list(io)
+        bad[i] = None
+        assert L.replayssm_step(h, *bad, None) == rs.RSSM_E_INVAL
+        assert L.replayssm_spec_verify(h, 2, *bad, None) == rs.RSSM_E_INVAL
+        bad[i] = FAKE + 8
+        assert L.replayssm_step(h, *bad, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_step(h, *io, None) == rs.RSSM_E_STATE
+    assert L.replayssm_spec_verify(h, 3, *io, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_spec_verify(h, 2, *io, None) == rs.RSSM_E_STATE
+    assert L.replayssm_rollback(h, None, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_rollback(h, FAKE, None) == rs.RSSM_E_STATE
+    assert L.replayssm_materialize_state(h, None, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_flush(h, None, None) == rs.RSSM_E_STATE
     assert L.replayssm_destroy(h) == rs.RSSM_OK
 
 
@@ -143,12 +170,16 @@ def test_baselines_validate():
     bad = cfg(dstate=24)
     assert L.conventional_step(ctypes.byref(bad), *args, None) == rs.RSSM_E_UNSUPPORTED
     assert L.conventional_step(None, *args, None) == rs.RSSM_E_INVAL
-    assert L.conventional_step(ctypes.byref(c), None, *args[1:], None) == rs.RSSM_E_INVAL
+    assert L.conventional_step(ctypes.byref(c), None, *args[1:], None) == rs.RSSM_OK      # batch 0
+    c1 = cfg(batch=1)
+    assert L.conventional_step(ctypes.byref(c1), None, *args[1:], None) == rs.RSSM_E_INVAL
+    assert L.conventional_step(ctypes.byref(c1), FAKE + 4, *args[1:], None) == rs.RSSM_E_INVAL
     assert L.snapshot_spec_verify(ctypes.byref(c), FAKE, FAKE, 4, *([FAKE] * 7), None) == rs.RSSM_OK
     assert L.snapshot_spec_verify(ctypes.byref(c), FAKE, FAKE, 0, *([FAKE] * 7), None) == rs.RSSM_E_INVAL
     assert L.snapshot_spec_verify(ctypes.byref(c), FAKE, FAKE, 9, *([FAKE] * 7), None) == rs.RSSM_E_INVAL
     assert L.snapshot_commit(ctypes.byref(c), FAKE, FAKE, 4, None) == rs.RSSM_OK
-    assert L.snapshot_commit(ctypes.byref(c), FAKE, None, 4, None) == rs.RSSM_E_INVAL
+    assert L.snapshot_commit(ctypes.byref(c1), FAKE, None, 4, None) == rs.RSSM_E_INVAL
+    assert L.snapshot_spec_verify(ctypes.byref(c1), None, FAKE, 4, *([FAKE] * 7), None) == rs.RSSM_E_INVAL
 
 
 def test_status_strings():
