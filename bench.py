@@ -37,6 +37,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--kernels-only", action="store_true",
                     help="only the replay steps (for profiler runs)")
+    ap.add_argument("--workload", default="serving", choices=["serving", "spec", "sweep"],
+                    help="serving: the headline line; spec: batch 512, T=4 verify+rollback vs "
+                         "per-draft snapshots; sweep: batch x L over a 10-layer stack")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
     return ap.parse_args()
 
 
@@ -54,6 +59,10 @@ def main():
     import workload
 
     torch.cuda.set_device(0)
+    if args.workload != "serving":
+        import bench_workloads
+        bench_workloads.run(args)
+        return
     H, P, N, G = 128, 64, 128, 8
     Bt, L = args.batch, args.buffer_len
     prec = args.read_prec
@@ -137,6 +146,14 @@ def main():
                        "gbps": round(fl_gbps, 1) if fl_gbps else None,
                        "alg_bytes_per_launch": int(bytes_fl)},
     }
+
+    if args.calib_copy:
+        a = torch.ones(1 << 28, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
 
     if not args.kernels_only:
         # conventional read-update-write step on the same shapes, same stream, same inputs

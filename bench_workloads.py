@@ -1,0 +1,207 @@
+"""Secondary benchmark workloads (each prints JSON lines; the headline line is bench.py's default).
+
+spec:  speculative decode on the serving layer -- batch 512, T = 4 drafts, accepted prefix uniform
+       in {0..4} per sequence (seeded), 128 verify steps. Buffer-pointer rollback (verify launch +
+       rollback/commit-flush launch) against per-draft state snapshots (verify-with-snapshots launch
+       + commit launch), same inputs, same stream.
+sweep: the serving head shape stacked as 10 independent layers, batch in {1, 8, 64, 256, 512} x
+       buffer length in {4, 8, 16, 32}, 64 decode steps: per-layer tokens/s of the replay step
+       (amortized over whole windows) and of the conventional step, the flush-step time per layer,
+       and the crossover batch.
+
+States and per-step inputs are drawn on the GPU from a seeded torch generator with the layer
+definition's distributions (x ~ N(0,1); B, C ~ N(0, 1/N); dt = softplus(N(0,1) - 4); S0 ~ N(0,1)),
+so that large stacks are set up in seconds.
+"""
+import json
+import time
+
+import numpy as np
+import torch
+
+import hybrid_mamba_decode_amd as rs
+from hybrid_mamba_decode_amd import traffic
+import workload
+
+H, P, N, G = 128, 64, 128, 8
+PEAK = 8000.0
+
+
+def _gen(seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return g
+
+
+def _tokens(g, lead, n):
+    x = torch.randn(*lead, H, P, device="cuda", generator=g)
+    B = torch.randn(*lead, G, N, device="cuda", generator=g) / n ** 0.5
+    C = torch.randn(*lead, G, N, device="cuda", generator=g) / n ** 0.5
+    dt = torch.nn.functional.softplus(torch.randn(*lead, H, device="cuda", generator=g) - 4.0)
+    return x, B, C, dt
+
+
+def _layer_params():
+    A, D = workload.layer_params(workload.config_seed(1), H)
+    return torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+
+
+def _timed(fn, reps):
+    st = torch.cuda.current_stream()
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(reps):
+        e0[r].record(st)
+        fn(r)
+        e1[r].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, np.array([e0[r].elapsed_time(e1[r]) * 1e-3 for r in range(reps)])
+
+
+def spec(args):
+    Bt, T, L, iters = 512, 4, 16, 128
+    A, D = _layer_params()
+    g = _gen(3007)
+    S0 = torch.randn(Bt, H, P, N, device="cuda", generator=g)
+    pool = [_tokens(g, (Bt, T), N) for _ in range(8)]
+    acc = torch.from_numpy(np.stack([workload.accepted_counts(workload.config_seed(3), it, Bt, T)
+                                     for it in range(iters)])).cuda()
+    y = torch.empty(Bt, T, H, P, device="cuda")
+    lay = rs.ReplaySSM(Bt, H, P, N, G, A, D, buffer_len=L, max_draft=T)
+    ev = {"verify": [], "rollback": []}
+    st = torch.cuda.current_stream()
+
+    def run_replay(warm):
+        lay.load_state(S0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        marks = []
+        for it in range(iters):
+            x, B, C, dt = pool[it % len(pool)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(st)
+            rs.replayssm_spec_verify(lay.handle, T, x, B, C, dt, y)
+            e[1].record(st)
+            rs.replayssm_rollback(lay.handle, acc[it])
+            e[2].record(st)
+            marks.append(e)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, marks
+
+    run_replay(True)
+    wall_r, marks = run_replay(False)
+    assert lay.check() == rs.RSSM_OK
+    tv = np.array([m[0].elapsed_time(m[1]) for m in marks]) * 1e-3
+    tr = np.array([m[1].elapsed_time(m[2]) for m in marks]) * 1e-3
+    accepted = int(acc.sum().item())
+    # per-draft snapshot baseline
+    cfg = rs.make_config(Bt, H, P, N, G)
+    slots = torch.empty(Bt, T + 1, H, P, N, device="cuda")
+    slots[:, 0].copy_(S0)
+    cur = torch.zeros(Bt, dtype=torch.int32, device="cuda")
+
+    def run_snap():
+        cur.zero_()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        marks = []
+        for it in range(iters):
+            x, B, C, dt = pool[it % len(pool)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(st)
+            rs.snapshot_spec_verify(cfg, slots, cur, T, x, B, C, dt, A, D, y)
+            e[1].record(st)
+            rs.snapshot_commit(cfg, cur, acc[it], T)
+            e[2].record(st)
+            marks.append(e)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, marks
+
+    run_snap()
+    wall_s, smarks = run_snap()
+    sv = np.array([m[0].elapsed_time(m[1]) for m in smarks]) * 1e-3
+    # verify bytes at the mean committed window (k_old ~ count before verify)
+    snap_bytes = traffic.snapshot_verify(H, P, N, G, T) * Bt
+    out = {
+        "workload": "spec decode, serving layer, batch 512, T=4, accepted ~ U{0..4}, 128 verify steps, fp32",
+        "replay": {"verify_steps_per_s": round(iters / wall_r, 1),
+                   "accepted_tokens_per_s_layer": round(accepted / wall_r, 1),
+                   "verify_mean_us": round(tv.mean() * 1e6, 2),
+                   "verify_gbps_at_state_read": round(traffic.verify(H, P, N, G, T, 0) * Bt / tv.mean() / 1e9, 1),
+                   "rollback_mean_us": round(tr.mean() * 1e6, 2),
+                   "rollback_max_us": round(tr.max() * 1e6, 2)},
+        "snapshot": {"verify_steps_per_s": round(iters / wall_s, 1),
+                     "accepted_tokens_per_s_layer": round(accepted / wall_s, 1),
+                     "verify_mean_us": round(sv.mean() * 1e6, 2),
+                     "gbps": round(snap_bytes / sv.mean() / 1e9, 1),
+                     "state_memory_gib": round(slots.numel() * 4 / 2 ** 30, 2)},
+        "replay_state_memory_gib": round(lay.workspace.numel() / 2 ** 30, 2),
+        "speedup_vs_snapshot": round(wall_s / wall_r, 3),
+        "accepted_tokens": accepted,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def sweep(args):
+    A, D = _layer_params()
+    layers = 10
+    steps = 64
+    results = []
+    for Bt in (1, 8, 64, 256, 512):
+        g = _gen(4007 + Bt)
+        states = [torch.randn(Bt, H, P, N, device="cuda", generator=g) for _ in range(layers)]
+        pool = [_tokens(g, (Bt,), N) for _ in range(4)]
+        y = torch.empty(Bt, H, P, device="cuda")
+        # conventional: 10 independent layers per step, in place
+        cfg = rs.make_config(Bt, H, P, N, G)
+        cst = [s.clone() for s in states]
+
+        def conv_step(r):
+            x, B, C, dt = pool[r % len(pool)]
+            for l in range(layers):
+                rs.conventional_step(cfg, cst[l], x, B, C, dt, A, D, y)
+        _timed(conv_step, 4)
+        wall_c, _ = _timed(conv_step, steps)
+        conv_tps = Bt * steps * layers / wall_c   # tokens/s per layer: each step runs every layer
+        del cst
+        for L in (4, 8, 16, 32):
+            lays = [rs.ReplaySSM(Bt, H, P, N, G, A, D, buffer_len=L) for _ in range(layers)]
+            for l in range(layers):
+                lays[l].load_state(states[l])
+
+            def rep_step(r):
+                x, B, C, dt = pool[r % len(pool)]
+                for l in range(layers):
+                    rs.replayssm_step(lays[l].handle, x, B, C, dt, y)
+            _timed(rep_step, L)                      # warm one whole window
+            wall_r, d = _timed(rep_step, steps)      # 64 steps = whole windows for every L
+            flush_idx = [r for r in range(steps) if (r + 1) % L == 0]
+            nonflush_idx = [r for r in range(steps) if (r + 1) % L != 0]
+            rec = {"batch": Bt, "L": L, "layers": layers,
+                   "replay_tokens_per_s_layer": round(Bt * steps * layers / wall_r, 1),
+                   "conventional_tokens_per_s_layer": round(conv_tps, 1),
+                   "speedup": round((Bt * steps * layers / wall_r) / conv_tps, 3),
+                   "flush_step_us_per_layer": round(float(d[flush_idx].mean()) * 1e6 / layers, 2),
+                   "nonflush_step_us_per_layer": round(float(d[nonflush_idx].mean()) * 1e6 / layers, 2),
+                   "replay_gbps_amortized": round(traffic.replay_window_amortized(H, P, N, G, L) * Bt * layers * steps / wall_r / 1e9, 1),
+                   "working_set_mib": round(layers * lays[0].workspace.numel() / 2 ** 20, 1)}
+            for l in range(layers):
+                assert lays[l].check() == rs.RSSM_OK
+            print(json.dumps(rec), flush=True)
+            results.append(rec)
+            del lays
+        del states
+        torch.cuda.empty_cache()
+    for L in (4, 8, 16, 32):
+        wins = [r["batch"] for r in results if r["L"] == L and r["speedup"] > 1.0]
+        print(json.dumps({"L": L, "smallest_batch_where_replay_wins": min(wins) if wins else None}), flush=True)
+
+
+def run(args):
+    if args.workload == "spec":
+        spec(args)
+    elif args.workload == "sweep":
+        sweep(args)

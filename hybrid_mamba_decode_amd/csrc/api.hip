@@ -28,6 +28,10 @@ struct replayssm_layer {
     // lockstep decoding, conservative otherwise; it only selects the kernel variant (whether a
     // launch may meet a flush). The device decides every flush per sequence, bit-exactly.
     int cmin, cmax;
+    // Lockstep: after a load, standard steps and unmasked flushes keep every sequence at the same
+    // (pos, ckpt_pos), known here; the step kernel then takes them as arguments. A rollback or a
+    // masked flush makes sequences diverge: from then on kernels read the device pointers.
+    int uni, upos, uck;
 };
 
 namespace {
@@ -261,6 +265,8 @@ rssm_status replayssm_load_state(replayssm_t h, const float *state, void *stream
     h->poisoned = 0;
     h->pending_T = 0;
     h->cmin = h->cmax = 0;
+    h->uni = 1;
+    h->upos = h->uck = 0;
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) launch_load_n##NV(h->cfg.read_prec, h->dev, state, st)
@@ -278,12 +284,20 @@ rssm_status replayssm_step(replayssm_t h, const float *x, const float *B, const 
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
     if (h->pending_T) return RSSM_E_STATE;
-    const bool flush_capable = h->cmax + 1 > h->cfg.buffer_len - h->cfg.max_draft;
+    const int lim = h->cfg.buffer_len - h->cfg.max_draft;
+    bool flush_capable = h->cmax + 1 > lim;
+    Lockstep ls{-1, -1};
+    if (h->uni) {
+        ls = Lockstep{h->upos, h->uck};
+        flush_capable = h->upos + 1 - h->uck > lim;  // every sequence flushes, or none does
+        h->upos += 1;
+        if (flush_capable) h->uck = h->upos;
+    }
     commit_bounds(h, 1, 1);
     if (h->cfg.batch == 0) return RSSM_OK;
     const TokenIO io{x, B, C, dt, y};
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_step_n##NV(h->cfg.read_prec, h->lmax, h->dev, io, flush_capable, st)
+#define CALL(NV) launch_step_n##NV(h->cfg.read_prec, h->lmax, h->dev, io, flush_capable, ls, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
 }
@@ -295,8 +309,13 @@ rssm_status replayssm_flush(replayssm_t h, const int32_t *seq_mask, void *stream
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
     if (h->pending_T) return RSSM_E_STATE;
-    if (!seq_mask) h->cmin = h->cmax = 0;
-    else h->cmin = 0;
+    if (!seq_mask) {
+        h->cmin = h->cmax = 0;
+        h->uck = h->upos;
+    } else {
+        h->cmin = 0;
+        h->uni = 0;
+    }
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) launch_flush_n##NV(h->cfg.read_prec, h->lmax, h->dev, MODE_MASK, seq_mask, 0, nullptr, st)
@@ -333,6 +352,7 @@ rssm_status replayssm_rollback(replayssm_t h, const int32_t *accepted, void *str
     if (!h->pending_T) return RSSM_E_STATE;
     const int T = h->pending_T;
     h->pending_T = 0;
+    h->uni = 0;
     commit_bounds(h, 0, T);
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;

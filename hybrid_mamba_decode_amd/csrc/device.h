@@ -54,6 +54,12 @@ struct TokenIO {
     float *y;
 };
 
+// Lockstep pointers: when every sequence is known (on the host) to hold the same (pos, ckpt_pos),
+// kernels take them as arguments; pos < 0 means "read each sequence's device pointers".
+struct Lockstep {
+    int pos, ckpt;
+};
+
 // Device flag bits.
 enum : unsigned { FLAG_POINTERS = 1u, FLAG_ACCEPTED = 2u };
 

@@ -346,7 +346,7 @@ struct StepLds {
 };
 
 template <int PREC, int LMAX, bool FLUSH>
-__global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io)
+__global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lockstep ls)
 {
     using G = Geo<NN, PREC>;
     __shared__ StepLds<LMAX> s;
@@ -362,17 +362,28 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io)
     u32x4 v[G::NL];
     if (kPreload) load_rows<PREC>(v, rrows, t.nrows, wave, lane);
 
-    // 2. Pointers (uniform per sequence) and the flush decision.
-    const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
-    const int count0 = pos - ck;
-    const bool ok = ck >= 0 && count0 >= 0 && count0 <= Ld.L - Ld.Tmax;
-    const int k = count0 + 1;
-    const bool flush = k > Ld.L - Ld.Tmax;
-    if (!ok || (!FLUSH && flush)) {
-        raise_flag(Ld, FLAG_POINTERS);
-        seq_done(Ld, t.b, pos, ck);
-        return;
+    // 2. Pointers. Lockstep: every sequence has the host-known (pos, ckpt_pos), so the window
+    //    loads below need no device read first. Otherwise: this sequence's device pointers,
+    //    validated before any address is formed from them.
+    const bool uni = ls.pos >= 0;
+    int pos, ck;
+    if (uni) {
+        pos = ls.pos;
+        ck = ls.ckpt;
+    } else {
+        pos = Ld.pos[t.b];
+        ck = Ld.ckpt[t.b];
+        const int c0 = pos - ck;
+        const bool ok = ck >= 0 && c0 >= 0 && c0 <= Ld.L - Ld.Tmax;
+        if (!ok || (!FLUSH && c0 + 1 > Ld.L - Ld.Tmax)) {
+            raise_flag(Ld, FLAG_POINTERS);
+            seq_done(Ld, t.b, pos, ck);
+            return;
+        }
     }
+    const int k = pos - ck + 1;                 // records in the window, this token included
+    const bool flush = k > Ld.L - Ld.Tmax;
+    const int new_ck = flush ? pos + 1 : ck;
 
     // 3. This token's C (chunk for the row dots, all of it for the window scores) and the window.
     const float *Ct = io.C + ((size_t)t.b * Ld.G + t.g) * NN;
@@ -384,6 +395,26 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io)
     const float A = Ld.A[t.h], Dh = Ld.D[t.h];
     const int slot = (int)((unsigned)pos % (unsigned)Ld.L);
     WindowRegs<LMAX> wr;
+
+    // Lockstep: the device copy of the pointers must hold the host's values (or, if this
+    // sequence's writer work-group already ran, the new ones); anything else means the caller
+    // corrupted them, and the sequence is skipped with the flag raised.
+    bool valid = true;
+    if (uni) {
+        const int dp = Ld.pos[t.b], dc = Ld.ckpt[t.b];
+        valid = (dp == pos || dp == pos + 1) && (dc == ck || dc == new_ck);
+    }
+    auto finish = [&](bool wrote) {
+        if (uni) {
+            if (!wrote) raise_flag(Ld, FLAG_POINTERS);
+            else if (t.h == 0 && t.split == 0 && tid == 0) {
+                Ld.pos[t.b] = pos + 1;
+                Ld.ckpt[t.b] = new_ck;
+            }
+        } else {
+            seq_done(Ld, t.b, pos + 1, new_ck);
+        }
+    };
 
     if (FLUSH && flush) {
         // Fused flush: fold all k records into the fp32 master rows.
@@ -400,6 +431,10 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io)
         float cf[4];
         load_cchunk<PREC_F32>(cf, Ct, lane);
         issue_window<LMAX>(wr, src, k, t.nrows);
+        if (!valid) {
+            finish(false);
+            return;
+        }
         commit_window<LMAX>(s.win, wr, src, k);
         __syncthreads();
         window_weights<LMAX, false>(s.win, nullptr, k - 1, A, s.w, nullptr, &s.decay);
@@ -417,7 +452,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io)
             io.y[bh * Ld.P + t.row0 + tid] = fmaf(Dh, xt, s.u[tid]);
         }
         // The token's own record is folded already: nothing is appended on a flush step.
-        seq_done(Ld, t.b, pos + 1, pos + 1);
+        finish(true);
         return;
     }
 
@@ -426,6 +461,10 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io)
     float cc[G::VEC];
     load_cchunk<PREC>(cc, Ct, lane);
     issue_window<LMAX>(wr, src, k, t.nrows);
+    if (!valid) {
+        finish(false);
+        return;
+    }
     commit_window<LMAX>(s.win, wr, src, k);
     if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = cq;
     float part[G::NL];
@@ -445,7 +484,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io)
         io.y[bh * Ld.P + t.row0 + tid] = acc;
     }
     append_record<LMAX>(Ld, t, s.win, k - 1, s.Cq, slot);
-    seq_done(Ld, t.b, pos + 1, ck);
+    finish(true);
 }
 
 // ==========================================================================================
@@ -772,12 +811,12 @@ __global__ void __launch_bounds__(kThreads) snapshot_verify_kernel(Layer Ld, flo
 inline unsigned nblocks(const Layer &Ld) { return (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)Ld.psplit; }
 
 template <int PREC, int LMAX>
-hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, hipStream_t st)
+hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockstep ls, hipStream_t st)
 {
     if (flush_capable)
-        hipLaunchKernelGGL((step_kernel<PREC, LMAX, true>), dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, io);
+        hipLaunchKernelGGL((step_kernel<PREC, LMAX, true>), dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
     else
-        hipLaunchKernelGGL((step_kernel<PREC, LMAX, false>), dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, io);
+        hipLaunchKernelGGL((step_kernel<PREC, LMAX, false>), dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
     return hipGetLastError();
 }
 
@@ -822,7 +861,10 @@ hipError_t by_prec_lmax(int prec, int lmax, Args... args)
 
 template <int PREC, int LMAX>
 struct StepF {
-    static hipError_t run(const Layer &Ld, const TokenIO &io, bool fc, hipStream_t st) { return step_t<PREC, LMAX>(Ld, io, fc, st); }
+    static hipError_t run(const Layer &Ld, const TokenIO &io, bool fc, Lockstep ls, hipStream_t st)
+    {
+        return step_t<PREC, LMAX>(Ld, io, fc, ls, st);
+    }
 };
 template <int PREC, int LMAX>
 struct FlushF {
@@ -842,9 +884,10 @@ struct VerifyF {
 #define RSSM_CAT2(a, b) a##b
 #define RSSM_CAT(a, b) RSSM_CAT2(a, b)
 
-hipError_t RSSM_CAT(launch_step_n, RSSM_N)(int prec, int lmax, const Layer &Ld, const TokenIO &io, bool flush_capable, hipStream_t st)
+hipError_t RSSM_CAT(launch_step_n, RSSM_N)(int prec, int lmax, const Layer &Ld, const TokenIO &io, bool flush_capable,
+                                           Lockstep ls, hipStream_t st)
 {
-    return by_prec_lmax<StepF>(prec, lmax, Ld, io, flush_capable, st);
+    return by_prec_lmax<StepF>(prec, lmax, Ld, io, flush_capable, ls, st);
 }
 
 hipError_t RSSM_CAT(launch_flush_n, RSSM_N)(int prec, int lmax, const Layer &Ld, int mode, const int *arg, int T, float *out, hipStream_t st)
