@@ -272,28 +272,33 @@ __device__ inline void write_copy_rows(const Layer &Ld, size_t bh, size_t elem0,
     }
 }
 
-// Fold `k` staged records into the fp32 rows vf (f32 geometry), in registers:
+// Fold `k` staged records into one head's fp32 rows vf (f32 geometry), in registers:
 // S' = decay * S + sum_j (w_j * x_j[p]) * B_j[n]   ([AT Pulse] "Technical analysis": a flush
-// folds the buffer into the checkpoint). wts/decay come from window_weights.
-template <int LMAX>
-__device__ inline void fold_rows(f32x4 (&vf)[GF::NL], const Window<LMAX> &w, const float *wts,
-                                 float decay, int k, int wave, int lane)
+// folds the buffer into the checkpoint). xw rows of this head start at column `col0`. Records
+// are the outer loop, so each lane reads its B chunk of a record once for all its rows.
+template <int LMAX, int XCOLS>
+__device__ inline void fold_head(f32x4 (&vf)[GF::NL], const float (&xw)[LMAX][XCOLS], const float (&Bw)[LMAX][NN],
+                                 const float *wts, float decay, int col0, int k, int wave, int lane)
 {
     const int c = lane % GF::LPR;
+    int col[GF::NL];
 #pragma unroll
     for (int i = 0; i < GF::NL; ++i) {
         const int r = row_of<PREC_F32>(i, wave, lane);
-        const int rr = r < kRows ? r : 0;
-        f32x4 acc = vf[i] * decay;
-        for (int j = 0; j < k; ++j) {
-            const float wx = wts[j] * w.xw[j][rr];
-            const f32x4 bj = *(const f32x4 *)&w.Bw[j][4 * c];
-            acc.x = fmaf(wx, bj.x, acc.x);
-            acc.y = fmaf(wx, bj.y, acc.y);
-            acc.z = fmaf(wx, bj.z, acc.z);
-            acc.w = fmaf(wx, bj.w, acc.w);
+        col[i] = col0 + (r < kRows ? r : 0);
+        vf[i] = vf[i] * decay;
+    }
+    for (int j = 0; j < k; ++j) {
+        const f32x4 bj = *(const f32x4 *)&Bw[j][4 * c];
+        const float wj = wts[j];
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            const float wx = wj * xw[j][col[i]];
+            vf[i].x = fmaf(wx, bj.x, vf[i].x);
+            vf[i].y = fmaf(wx, bj.y, vf[i].y);
+            vf[i].z = fmaf(wx, bj.z, vf[i].z);
+            vf[i].w = fmaf(wx, bj.w, vf[i].w);
         }
-        vf[i] = acc;
     }
 }
 
@@ -333,34 +338,76 @@ __device__ inline void append_record(const Layer &Ld, const Tile &t, const Windo
 // window, then store only the new record. FLUSH = the launch may meet sequences whose buffer
 // fills ([WittyWires] "What happened": the checkpoint is updated when the buffer fills); those
 // fold all records into the fp32 master, rewrite the read copy and read y from the new state.
+//
+// A work-group covers ROWS/64 heads of one group (ROWS = 64 for fp32; 128 for a bf16 copy and
+// 256 for an fp8 copy), so that every work-group streams about 32 KiB of checkpoint whatever the
+// read precision, and the group's B window and scores B_j . C_t are staged once for its heads.
 // ==========================================================================================
-template <int LMAX>
-struct StepLds {
-    Window<LMAX> win;
-    float Cq[NN] __attribute__((aligned(16)));
-    float w[LMAX];
-    float coef[LMAX];
-    float u[kRows];
-    float red[kWaves];
-    float decay;
+template <int PREC, int ROWS>
+struct SGeo {
+    using G = Geo<NN, PREC>;
+    static constexpr int HPB = ROWS / kRows;                 // heads per work-group
+    static constexpr int NL = (ROWS + G::RPB - 1) / G::RPB;  // state load slots per lane
+    static_assert(NL <= G::LPR || NL == 1, "transpose-reduce needs NL <= LPR");
 };
 
-template <int PREC, int LMAX, bool FLUSH>
+template <int LMAX, int ROWS>
+struct StepLds {
+    float xw[LMAX][ROWS] __attribute__((aligned(16)));  // x of each record, rows of every head
+    float Bw[LMAX][NN] __attribute__((aligned(16)));    // B of each record (the group's)
+    float Cq[NN] __attribute__((aligned(16)));          // C of this token
+    float g[LMAX];                                      // B_j . C_t
+    float u[ROWS];                                      // S_c . C_t per row
+    float w[ROWS / kRows][LMAX];                        // per head: w_j
+    float coef[ROWS / kRows][LMAX];                     // per head: w_j * g_j
+    float decay[ROWS / kRows];
+    float red[kWaves];
+};
+
+// Work-group -> (sequence, first head, row split); same XCD-aware order as map_tile.
+__device__ inline Tile map_heads(const Layer &Ld, int hpb)
+{
+    const unsigned nblk = gridDim.x, i = blockIdx.x;
+    const unsigned id = (nblk % 8u == 0u) ? (i % 8u) * (nblk / 8u) + i / 8u : i;
+    const unsigned hblocks = (unsigned)(Ld.H / hpb);
+    Tile t;
+    t.split = (int)(id % (unsigned)Ld.psplit);
+    const unsigned rest = id / (unsigned)Ld.psplit;
+    t.h = (int)(rest % hblocks) * hpb;  // first head
+    t.b = (int)(rest / hblocks);
+    t.g = t.h / Ld.hpg;
+    t.row0 = t.split * kRows;
+    t.nrows = min(kRows, Ld.P - t.row0);
+    return t;
+}
+
+template <int PREC, int LMAX, int ROWS, bool FLUSH>
 __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lockstep ls)
 {
     using G = Geo<NN, PREC>;
-    __shared__ StepLds<LMAX> s;
-    const Tile t = map_tile(Ld);
+    using SG = SGeo<PREC, ROWS>;
+    constexpr int HPB = SG::HPB, NL = SG::NL;
+    __shared__ StepLds<LMAX, ROWS> s;
+    const Tile t = map_heads(Ld, HPB);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t bh = (size_t)t.b * Ld.H + t.h;
-    const size_t elem0 = (bh * Ld.P + t.row0) * NN;
-    const char *rrows = (PREC == PREC_F32 ? (const char *)Ld.master : (const char *)Ld.rcopy) +
-                        elem0 * elem_bytes<PREC>();
+    const size_t bh0 = (size_t)t.b * Ld.H + t.h;
+    const int c = lane % G::LPR;
 
     // 1. Checkpoint rows through the read copy, issued first: this is the stream that matters.
-    constexpr bool kPreload = !FLUSH || PREC == PREC_F32;
-    u32x4 v[G::NL];
-    if (kPreload) load_rows<PREC>(v, rrows, t.nrows, wave, lane);
+    //    Row r of the work-group is row (r % 64) of head r / 64.
+    constexpr bool kPreload = !FLUSH || (PREC == PREC_F32 && HPB == 1);
+    u32x4 v[NL];
+    auto load_state = [&]() {
+        const char *base = PREC == PREC_F32 ? (const char *)Ld.master : (const char *)Ld.rcopy;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int r = i * G::RPB + wave * G::RPI + lane / G::LPR;
+            const int hh = r / kRows, p = r % kRows;
+            const size_t e = ((bh0 + hh) * Ld.P + t.row0 + p) * NN + (size_t)c * G::VEC;
+            v[i] = (r < ROWS && p < t.nrows) ? load_nt(base + e * elem_bytes<PREC>()) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    if (kPreload) load_state();
 
     // 2. Pointers. Lockstep: every sequence has the host-known (pos, ckpt_pos), so the window
     //    loads below need no device read first. Otherwise: this sequence's device pointers,
@@ -374,117 +421,198 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         pos = Ld.pos[t.b];
         ck = Ld.ckpt[t.b];
         const int c0 = pos - ck;
-        const bool ok = ck >= 0 && c0 >= 0 && c0 <= Ld.L - Ld.Tmax;
-        if (!ok || (!FLUSH && c0 + 1 > Ld.L - Ld.Tmax)) {
+        if (!(ck >= 0 && c0 >= 0 && c0 <= Ld.L - Ld.Tmax) || (!FLUSH && c0 + 1 > Ld.L - Ld.Tmax)) {
             raise_flag(Ld, FLAG_POINTERS);
-            seq_done(Ld, t.b, pos, ck);
+            seq_done(Ld, t.b, pos, ck, HPB);
             return;
         }
     }
-    const int k = pos - ck + 1;                 // records in the window, this token included
+    const int k = pos - ck + 1;  // records in the window, this token included
     const bool flush = k > Ld.L - Ld.Tmax;
     const int new_ck = flush ? pos + 1 : ck;
+    auto slot_of = [&](int q) { return (int)((unsigned)q % (unsigned)Ld.L); };
 
-    // 3. This token's C (chunk for the row dots, all of it for the window scores) and the window.
+    // 3. Window loads into registers: x rows of every head, the group's B rows, this token's C,
+    //    and (wave w, lane j) <- dt_j of head w.
+    constexpr int XS = (LMAX * ROWS / 4 + kThreads - 1) / kThreads;
+    constexpr int BS = (LMAX * NN / 4 + kThreads - 1) / kThreads;
+    constexpr int BCH = BS < 8 ? BS : 8;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const float *rx = Ld.ring_x + bh0 * Ld.L * Ld.P + t.row0;
+    const float *fx = io.x + bh0 * Ld.P + t.row0;
+    const float *rB = Ld.ring_B + ((size_t)t.b * Ld.G + t.g) * Ld.L * NN;
+    const float *fB = io.B + ((size_t)t.b * Ld.G + t.g) * NN;
     const float *Ct = io.C + ((size_t)t.b * Ld.G + t.g) * NN;
-    RecSrc src = ring_src(Ld, t, ck, k - 1);
-    src.fx = io.x + bh * Ld.P + t.row0;
-    src.fB = io.B + ((size_t)t.b * Ld.G + t.g) * NN;
-    src.fdt = io.dt + bh;
-    const f32x4 cq = tid < NN / 4 ? *(const f32x4 *)(Ct + 4 * tid) : f32x4{0.f, 0.f, 0.f, 0.f};
-    const float A = Ld.A[t.h], Dh = Ld.D[t.h];
-    const int slot = (int)((unsigned)pos % (unsigned)Ld.L);
-    WindowRegs<LMAX> wr;
+    f32x4 xv[XS], bv[BCH];
+#pragma unroll
+    for (int sl = 0; sl < XS; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (ROWS / 4), rem = e % (ROWS / 4);
+        const int hh = rem / (kRows / 4), c4 = rem % (kRows / 4);
+        const float *src = j < k - 1 ? rx + ((size_t)hh * Ld.L + slot_of(ck + j)) * Ld.P : fx + (size_t)hh * Ld.P;
+        xv[sl] = (j < k && 4 * c4 < t.nrows) ? *(const f32x4 *)(src + 4 * c4) : zero;
+    }
+#pragma unroll
+    for (int sl = 0; sl < BCH; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+        const float *src = j < k - 1 ? rB + (size_t)slot_of(ck + j) * NN : fB;
+        bv[sl] = j < k ? *(const f32x4 *)(src + 4 * c4) : zero;
+    }
+    const f32x4 cq = tid < NN / 4 ? *(const f32x4 *)(Ct + 4 * tid) : zero;
+    float dtj = 0.f;
+    if (wave < HPB && lane < k)
+        dtj = lane < k - 1 ? Ld.ring_dt[(bh0 + wave) * Ld.L + slot_of(ck + lane)] : io.dt[bh0 + wave];
+    const float Aw = wave < HPB ? Ld.A[t.h + wave] : 0.f;
+    const float scl_r = (PREC == PREC_FP8 && tid < ROWS) ? Ld.scale[bh0 + tid / kRows] : 1.0f;
 
-    // Lockstep: the device copy of the pointers must hold the host's values (or, if this
-    // sequence's writer work-group already ran, the new ones); anything else means the caller
-    // corrupted them, and the sequence is skipped with the flag raised.
-    bool valid = true;
+    // Lockstep: the device copy of the pointers must hold the host's values (or, if the
+    // sequence's pointer-writing work-group already ran, the new ones); anything else means the
+    // caller corrupted them, and the sequence is skipped with the flag raised.
     if (uni) {
         const int dp = Ld.pos[t.b], dc = Ld.ckpt[t.b];
-        valid = (dp == pos || dp == pos + 1) && (dc == ck || dc == new_ck);
+        if (!((dp == pos || dp == pos + 1) && (dc == ck || dc == new_ck))) {
+            raise_flag(Ld, FLAG_POINTERS);
+            return;
+        }
     }
-    auto finish = [&](bool wrote) {
+
+    // 4. Commit the window to LDS (B rows beyond the first chunk load here).
+#pragma unroll
+    for (int sl = 0; sl < XS; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (ROWS / 4), rem = e % (ROWS / 4);
+        if (j < LMAX) *(f32x4 *)&s.xw[j][4 * rem] = xv[sl];
+    }
+#pragma unroll
+    for (int s0 = 0; s0 < BS; s0 += BCH) {
+        if (s0 > 0) {
+#pragma unroll
+            for (int sl = 0; sl < BCH; ++sl) {
+                const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+                const float *src = j < k - 1 ? rB + (size_t)slot_of(ck + j) * NN : fB;
+                bv[sl] = (s0 + sl < BS && j < k) ? *(const f32x4 *)(src + 4 * c4) : zero;
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < BCH; ++sl) {
+            const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+            if (s0 + sl < BS && j < LMAX) *(f32x4 *)&s.Bw[j][4 * c4] = bv[sl];
+        }
+    }
+    if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = cq;
+
+    // 5. Window weights of head w in wave w: suffix sums of dt by lane shuffles,
+    //    w_j = dt_j * exp(A * sum_{i>j} dt_i), decay = exp(A * sum_i dt_i) ([AT Pulse]
+    //    "Technical analysis": the recurrence unrolled over the window).
+    float wj = 0.f;
+    if (wave < HPB) {
+        float sfx = dtj;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float nb = __shfl_down(sfx, o, 64);
+            sfx += lane + o < 64 ? nb : 0.f;
+        }
+        const float nxt = __shfl_down(sfx, 1, 64);
+        const float tail = lane + 1 < 64 ? nxt : 0.f;
+        const float total = __shfl(sfx, 0, 64);
+        wj = lane < k ? dtj * expf(Aw * tail) : 0.f;
+        if (lane < LMAX) s.w[wave][lane] = wj;
+        if (lane == 0) s.decay[wave] = expf(Aw * total);
+    }
+    __syncthreads();
+
+    if (FLUSH && flush) {
+        // Fused flush, head by head: fold all k records into the fp32 master rows, rewrite the
+        // read copy, and read y from the folded state.
+        float cf[4];
+        load_cchunk<PREC_F32>(cf, Ct, lane);
+        for (int hh = 0; hh < HPB; ++hh) {
+            f32x4 vf[GF::NL];
+            const size_t elem0 = ((bh0 + hh) * Ld.P + t.row0) * NN;
+            if constexpr (kPreload) {
+#pragma unroll
+                for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(v[i]);
+            } else {
+                u32x4 m[GF::NL];
+                load_rows<PREC_F32>(m, (const char *)(Ld.master + elem0), t.nrows, wave, lane);
+#pragma unroll
+                for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(m[i]);
+            }
+            fold_head<LMAX, ROWS>(vf, s.xw, s.Bw, s.w[hh], s.decay[hh], hh * kRows, k, wave, lane);
+            store_rows_f32(Ld.master + elem0, vf, t.nrows, wave, lane);
+            write_copy_rows<PREC>(Ld, bh0 + hh, elem0, vf, t.nrows, wave, lane, s.red);
+            float part[GF::NL];
+#pragma unroll
+            for (int i = 0; i < GF::NL; ++i) part[i] = chunk_dot<PREC_F32>(as_u32x4(vf[i]), cf);
+            rows_to_lds<PREC_F32, GF::NL>(part, s.u + hh * kRows, 0, 1, GF::NL, 1.0f, wave, lane);
+        }
+        __syncthreads();
+        if (tid < ROWS && tid % kRows < t.nrows) {
+            const int hh = tid / kRows;
+            io.y[(bh0 + hh) * Ld.P + t.row0 + tid % kRows] = fmaf(Ld.D[t.h + hh], s.xw[k - 1][tid], s.u[tid]);
+        }
+        // The token's own record is folded already: nothing is appended on a flush step.
         if (uni) {
-            if (!wrote) raise_flag(Ld, FLAG_POINTERS);
-            else if (t.h == 0 && t.split == 0 && tid == 0) {
+            if (t.h == 0 && t.split == 0 && tid == 0) {
                 Ld.pos[t.b] = pos + 1;
                 Ld.ckpt[t.b] = new_ck;
             }
         } else {
-            seq_done(Ld, t.b, pos + 1, new_ck);
+            seq_done(Ld, t.b, pos + 1, new_ck, HPB);
         }
-    };
-
-    if (FLUSH && flush) {
-        // Fused flush: fold all k records into the fp32 master rows.
-        f32x4 vf[GF::NL];
-        if constexpr (PREC == PREC_F32) {
-#pragma unroll
-            for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(v[i]);
-        } else {
-            u32x4 m[GF::NL];
-            load_rows<PREC_F32>(m, (const char *)(Ld.master + elem0), t.nrows, wave, lane);
-#pragma unroll
-            for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(m[i]);
-        }
-        float cf[4];
-        load_cchunk<PREC_F32>(cf, Ct, lane);
-        issue_window<LMAX>(wr, src, k, t.nrows);
-        if (!valid) {
-            finish(false);
-            return;
-        }
-        commit_window<LMAX>(s.win, wr, src, k);
-        __syncthreads();
-        window_weights<LMAX, false>(s.win, nullptr, k - 1, A, s.w, nullptr, &s.decay);
-        __syncthreads();
-        fold_rows<LMAX>(vf, s.win, s.w, s.decay, k, wave, lane);
-        store_rows_f32(Ld.master + elem0, vf, t.nrows, wave, lane);
-        write_copy_rows<PREC>(Ld, bh, elem0, vf, t.nrows, wave, lane, s.red);
-        float part[GF::NL];
-#pragma unroll
-        for (int i = 0; i < GF::NL; ++i) part[i] = chunk_dot<PREC_F32>(as_u32x4(vf[i]), cf);
-        rows_to_lds<PREC_F32, GF::NL>(part, s.u, 0, 1, GF::NL, 1.0f, wave, lane);
-        __syncthreads();
-        if (tid < t.nrows) {
-            const float xt = s.win.xw[k - 1][tid];
-            io.y[bh * Ld.P + t.row0 + tid] = fmaf(Dh, xt, s.u[tid]);
-        }
-        // The token's own record is folded already: nothing is appended on a flush step.
-        finish(true);
         return;
     }
 
-    // 4. Replay: row dots with C_t through the read copy.
-    if (!kPreload) load_rows<PREC>(v, rrows, t.nrows, wave, lane);
+    // 6. Replay: row dots with C_t through the read copy (scores B_j . C_t alongside).
+    if (!kPreload) load_state();
     float cc[G::VEC];
-    load_cchunk<PREC>(cc, Ct, lane);
-    issue_window<LMAX>(wr, src, k, t.nrows);
-    if (!valid) {
-        finish(false);
-        return;
-    }
-    commit_window<LMAX>(s.win, wr, src, k);
-    if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = cq;
-    float part[G::NL];
 #pragma unroll
-    for (int i = 0; i < G::NL; ++i) part[i] = chunk_dot<PREC>(v[i], cc);
-    const float scl = PREC == PREC_FP8 ? Ld.scale[bh] : 1.0f;
-    rows_to_lds<PREC, G::NL>(part, s.u, 0, 1, G::NL, scl, wave, lane);
+    for (int e = 0; e < G::VEC; ++e) cc[e] = s.Cq[c * G::VEC + e];
+    {
+        constexpr int GS = kThreads / LMAX;
+        const int j = tid / GS, sub = tid % GS;
+        float gj = 0.f;
+        for (int n = sub; n < NN; n += GS) gj = fmaf(s.Bw[j][n], s.Cq[n], gj);
+#pragma unroll
+        for (int o = GS / 2; o >= 1; o >>= 1) gj += __shfl_xor(gj, o, 64);
+        if (sub == 0) s.g[j] = gj;
+    }
+    float part[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) part[i] = chunk_dot<PREC>(v[i], cc);
+    {
+        transpose_reduce<NL, G::LPR>(part, lane);
+        bool writer;
+        const int first = tr_first<NL, G::LPR>(lane, &writer);
+        const int r = first * G::RPB + wave * G::RPI + lane / G::LPR;
+        if (writer && r < ROWS) s.u[r] = part[0];
+    }
     __syncthreads();
-    window_weights<LMAX, true>(s.win, s.Cq, k - 1, A, s.w, s.coef, &s.decay);
+    if (wave < HPB && lane < LMAX) s.coef[wave][lane] = wj * s.g[lane];
     __syncthreads();
 
-    // 5. Combine and append.
-    if (tid < t.nrows) {
-        float acc = s.decay * s.u[tid];
-        for (int j = 0; j < k; ++j) acc = fmaf(s.coef[j], s.win.xw[j][tid], acc);
-        acc = fmaf(Dh, s.win.xw[k - 1][tid], acc);
-        io.y[bh * Ld.P + t.row0 + tid] = acc;
+    // 7. Combine and append.
+    if (tid < ROWS && tid % kRows < t.nrows) {
+        const int hh = tid / kRows, p = tid % kRows;
+        float acc = s.decay[hh] * (s.u[tid] * scl_r);
+        for (int j = 0; j < k; ++j) acc = fmaf(s.coef[hh][j], s.xw[j][tid], acc);
+        const float xt = s.xw[k - 1][tid];
+        acc = fmaf(Ld.D[t.h + hh], xt, acc);
+        io.y[(bh0 + hh) * Ld.P + t.row0 + p] = acc;
+        Ld.ring_x[((bh0 + hh) * Ld.L + slot_of(pos)) * Ld.P + t.row0 + p] = xt;
     }
-    append_record<LMAX>(Ld, t, s.win, k - 1, s.Cq, slot);
-    finish(true);
+    if (t.split == 0 && wave < HPB && lane == k - 1) Ld.ring_dt[(bh0 + wave) * Ld.L + slot_of(pos)] = dtj;
+    if (t.split == 0 && t.h % Ld.hpg == 0 && tid < NN / 4) {
+        const size_t off = (((size_t)t.b * Ld.G + t.g) * Ld.L + slot_of(pos)) * NN + 4 * tid;
+        *(f32x4 *)(Ld.ring_B + off) = *(const f32x4 *)&s.Bw[k - 1][4 * tid];
+        if (Ld.ring_C) *(f32x4 *)(Ld.ring_C + off) = *(const f32x4 *)&s.Cq[4 * tid];
+    }
+    if (uni) {
+        if (t.h == 0 && t.split == 0 && tid == 0) {
+            Ld.pos[t.b] = pos + 1;
+            Ld.ckpt[t.b] = new_ck;
+        }
+    } else {
+        seq_done(Ld, t.b, pos + 1, new_ck, HPB);
+    }
 }
 
 // ==========================================================================================
@@ -546,7 +674,7 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(Layer Ld, int mode, con
         f32x4 vf[GF::NL];
 #pragma unroll
         for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(m[i]);
-        fold_rows<LMAX>(vf, s.win, s.w, s.decay, count, wave, lane);
+        fold_head<LMAX, kRows>(vf, s.win.xw, s.win.Bw, s.w, s.decay, 0, count, wave, lane);
         if (mode == MODE_MATERIALIZE) {
             store_rows_f32(out + elem0, vf, t.nrows, wave, lane);
         } else {
@@ -810,14 +938,29 @@ __global__ void __launch_bounds__(kThreads) snapshot_verify_kernel(Layer Ld, flo
 // ------------------------------------------------------------------------------------------
 inline unsigned nblocks(const Layer &Ld) { return (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)Ld.psplit; }
 
+template <int PREC, int LMAX, int ROWS>
+hipError_t step_rows(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockstep ls, hipStream_t st)
+{
+    const unsigned grid = nblocks(Ld) / (ROWS / kRows);
+    if (flush_capable)
+        hipLaunchKernelGGL((step_kernel<PREC, LMAX, ROWS, true>), dim3(grid), dim3(kThreads), 0, st, Ld, io, ls);
+    else
+        hipLaunchKernelGGL((step_kernel<PREC, LMAX, ROWS, false>), dim3(grid), dim3(kThreads), 0, st, Ld, io, ls);
+    return hipGetLastError();
+}
+
+// Heads per work-group: 1 for fp32 (two fp32 heads per work-group measured no faster: the
+// occupancy drops from 8 to 4 work-groups per CU); for the narrow copies as many as make
+// ~32 KiB of checkpoint per work-group (bf16 2, fp8 4), when the head tile fits one work-group
+// (P <= 64), the group divides evenly and the launch keeps at least 2048 work-groups (8 per CU).
+// Flush-capable launches use one head per work-group (their fold loop is per head).
 template <int PREC, int LMAX>
 hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockstep ls, hipStream_t st)
 {
-    if (flush_capable)
-        hipLaunchKernelGGL((step_kernel<PREC, LMAX, true>), dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
-    else
-        hipLaunchKernelGGL((step_kernel<PREC, LMAX, false>), dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
-    return hipGetLastError();
+    constexpr int wide = PREC == PREC_F32 ? 1 : PREC == PREC_BF16 ? 2 : 4;
+    if (!flush_capable && wide > 1 && Ld.psplit == 1 && Ld.hpg % wide == 0 && nblocks(Ld) / wide >= 2048)
+        return step_rows<PREC, LMAX, kRows * wide>(Ld, io, flush_capable, ls, st);
+    return step_rows<PREC, LMAX, kRows>(Ld, io, flush_capable, ls, st);
 }
 
 template <int PREC, int LMAX>
