@@ -356,7 +356,7 @@ rssm_status replayssm_rollback(replayssm_t h, const int32_t *accepted, void *str
     commit_bounds(h, 0, T);
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_flush_n##NV(h->cfg.read_prec, h->lmax, h->dev, MODE_ROLLBACK, accepted, T, nullptr, st)
+#define CALL(NV) launch_flush_n##NV(h->cfg.read_prec, h->lmax, h->dev, MODE_OVERFULL, accepted, T, nullptr, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
 }

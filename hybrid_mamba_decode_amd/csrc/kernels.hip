@@ -616,10 +616,11 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
 }
 
 // ==========================================================================================
-// Flush / rollback / materialize. MODE_MASK: fold every committed record of the selected
-// sequences. MODE_ROLLBACK: pos += accepted (rejected drafts are dropped by the pointer move,
-// [AT Pulse] "Technical analysis"), then fold if more than L - Tmax records are pending.
-// MODE_MATERIALIZE: write checkpoint + committed records to `out`, commit nothing.
+// Flush / commit-flush / materialize. MODE_MASK: fold every committed record of the selected
+// sequences. MODE_OVERFULL (after a rollback moved pos by the accepted count -- rejected drafts
+// are dropped by that pointer move, [AT Pulse] "Technical analysis"): fold the sequences with
+// more than L - Tmax pending records. MODE_MATERIALIZE: write checkpoint + committed records to
+// `out`, commit nothing. Work-groups of sequences that do not fold exit at once.
 // ==========================================================================================
 template <int LMAX>
 struct FlushLds {
@@ -630,7 +631,7 @@ struct FlushLds {
 };
 
 template <int PREC, int LMAX>
-__global__ void __launch_bounds__(kThreads) flush_kernel(Layer Ld, int mode, const int *arg, int T, float *out)
+__global__ void __launch_bounds__(kThreads) flush_kernel(Layer Ld, int mode, const int *arg, float *out)
 {
     __shared__ FlushLds<LMAX> s;
     const Tile t = map_tile(Ld);
@@ -639,29 +640,18 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(Layer Ld, int mode, con
     const size_t elem0 = (bh * Ld.P + t.row0) * NN;
 
     const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
-    const int count0 = pos - ck;
-    if (!(ck >= 0 && count0 >= 0 && count0 <= Ld.L - Ld.Tmax)) {
+    const int count = pos - ck;
+    const int cap = mode == MODE_OVERFULL ? Ld.L : Ld.L - Ld.Tmax;
+    if (!(ck >= 0 && count >= 0 && count <= cap)) {
         raise_flag(Ld, FLAG_POINTERS);
-        if (mode != MODE_MATERIALIZE) seq_done(Ld, t.b, pos, ck);
         return;
     }
-    int new_pos = pos, count = count0;
     bool fold;
-    if (mode == MODE_ROLLBACK) {
-        int a = arg[t.b];
-        if (a < 0 || a > T) {
-            raise_flag(Ld, FLAG_ACCEPTED);
-            a = 0;
-        }
-        new_pos = pos + a;
-        count = new_pos - ck;
-        fold = count > Ld.L - Ld.Tmax;
-    } else if (mode == MODE_MASK) {
-        fold = (arg == nullptr || arg[t.b] != 0) && count > 0;
-    } else {
-        fold = true;
-    }
-    if (fold) {
+    if (mode == MODE_OVERFULL) fold = count > Ld.L - Ld.Tmax;
+    else if (mode == MODE_MASK) fold = (arg == nullptr || arg[t.b] != 0) && count > 0;
+    else fold = true;
+    if (!fold) return;  // pointers unchanged: no completion count needed
+    {
         u32x4 m[GF::NL];
         load_rows<PREC_F32>(m, (const char *)(Ld.master + elem0), t.nrows, wave, lane);
         const RecSrc src = ring_src(Ld, t, ck, count);
@@ -682,7 +672,26 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(Layer Ld, int mode, con
             write_copy_rows<PREC>(Ld, bh, elem0, vf, t.nrows, wave, lane, s.red);
         }
     }
-    if (mode != MODE_MATERIALIZE) seq_done(Ld, t.b, new_pos, fold ? new_pos : ck);
+    if (mode != MODE_MATERIALIZE) seq_done(Ld, t.b, pos, pos);
+}
+
+// Rollback pointer move: pos += accepted[b] (0..T). One thread per sequence; a count out of
+// range, or pointers that break the invariant, raise the flag and leave the sequence as it was.
+__global__ void advance_kernel(Layer Ld, const int *accepted, int T)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= Ld.Bt) return;
+    const int pos = Ld.pos[b], ck = Ld.ckpt[b];
+    if (!(ck >= 0 && pos - ck >= 0 && pos - ck <= Ld.L - Ld.Tmax)) {
+        __hip_atomic_fetch_or(Ld.flag, FLAG_POINTERS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const int a = accepted[b];
+    if (a < 0 || a > T) {
+        __hip_atomic_fetch_or(Ld.flag, FLAG_ACCEPTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    Ld.pos[b] = pos + a;
 }
 
 // ==========================================================================================
@@ -695,6 +704,7 @@ template <int LMAX, int TQ>
 struct VerifyLds {
     Window<LMAX> win;
     float Cq[TQ][NN] __attribute__((aligned(16)));
+    float gq[TQ][LMAX];  // B_j . C_q
     float coef[TQ][LMAX];
     float u[TQ][kRows];
     float decay[TQ];
@@ -765,40 +775,71 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
     rows_to_lds<PREC, G::NL * TQ>(part, &s.u[0][0], kRows, T, G::NL, scl, wave, lane);
     __syncthreads();
 
-    // Window scores and weights for every (query, record) pair: GS threads per record.
-    const float A = Ld.A[t.h];
+    // Scores B_j . C_q for every query: GS threads per record, the B row read once for all q.
     {
         constexpr int GS = kThreads / LMAX;
         const int j = tid / GS, sub = tid % GS;
-        for (int q = 0; q < T; ++q) {
-            const int last = count0 + q;
-            float g = 0.f;
-            if (j <= last)
-                for (int n = sub; n < NN; n += GS) g = fmaf(s.win.Bw[j][n], s.Cq[q][n], g);
+        float g[TQ];
 #pragma unroll
-            for (int o = GS / 2; o >= 1; o >>= 1) g += __shfl_xor(g, o, 64);
-            if (sub == 0 && j <= last) {
-                float tail = 0.f;
-                for (int i = j + 1; i <= last; ++i) tail += s.win.dts[i];
-                s.coef[q][j] = s.win.dts[j] * expf(A * tail) * g;
-                if (j == 0) s.decay[q] = expf(A * (tail + s.win.dts[0]));
+        for (int q = 0; q < TQ; ++q) g[q] = 0.f;
+        if (j < kw) {
+            for (int n = sub; n < NN; n += GS) {
+                const float bjn = s.win.Bw[j][n];
+#pragma unroll
+                for (int q = 0; q < TQ; ++q) g[q] = fmaf(bjn, s.Cq[q][n], g[q]);
             }
         }
+#pragma unroll
+        for (int q = 0; q < TQ; ++q)
+#pragma unroll
+            for (int o = GS / 2; o >= 1; o >>= 1) g[q] += __shfl_xor(g[q], o, 64);
+        if (sub == 0)
+#pragma unroll
+            for (int q = 0; q < TQ; ++q) s.gq[q][j] = g[q];
     }
     __syncthreads();
 
+    // Weights of query q (its window: records 0 .. count0 + q) in wave q mod 4: suffix sums of
+    // dt by lane shuffles ([AT Pulse] "Technical analysis": the unrolled window).
+    const float A = Ld.A[t.h];
+    for (int q = wave; q < T; q += kWaves) {
+        const int last = count0 + q;
+        const float d = lane <= last && lane < LMAX ? s.win.dts[lane] : 0.f;
+        float sfx = d;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float nb = __shfl_down(sfx, o, 64);
+            sfx += lane + o < 64 ? nb : 0.f;
+        }
+        const float nxt = __shfl_down(sfx, 1, 64);
+        const float tail = lane + 1 < 64 ? nxt : 0.f;
+        const float total = __shfl(sfx, 0, 64);
+        if (lane < LMAX) s.coef[q][lane] = lane <= last ? d * expf(A * tail) * s.gq[q][lane] : 0.f;
+        if (lane == 0) s.decay[q] = expf(A * total);
+    }
+    __syncthreads();
+
+    // Combine: wave q mod 4 forms query q's output rows; then the tentative appends.
     const float Dh = Ld.D[t.h];
-    if (tid < t.nrows) {
-        for (int q = 0; q < T; ++q) {
+    for (int q = wave; q < T; q += kWaves) {
+        if (lane < t.nrows) {
             const int last = count0 + q;
-            float acc = s.decay[q] * s.u[q][tid];
-            for (int j = 0; j <= last; ++j) acc = fmaf(s.coef[q][j], s.win.xw[j][tid], acc);
-            acc = fmaf(Dh, s.win.xw[last][tid], acc);
-            io.y[(((size_t)t.b * T + q) * Ld.H + t.h) * Ld.P + t.row0 + tid] = acc;
+            float acc = s.decay[q] * s.u[q][lane];
+            for (int j = 0; j <= last; ++j) acc = fmaf(s.coef[q][j], s.win.xw[j][lane], acc);
+            acc = fmaf(Dh, s.win.xw[last][lane], acc);
+            io.y[(((size_t)t.b * T + q) * Ld.H + t.h) * Ld.P + t.row0 + lane] = acc;
+            Ld.ring_x[(bh * Ld.L + (unsigned)(pos + q) % (unsigned)Ld.L) * Ld.P + t.row0 + lane] = s.win.xw[last][lane];
+        }
+        if (t.split == 0 && lane == 0) Ld.ring_dt[bh * Ld.L + (unsigned)(pos + q) % (unsigned)Ld.L] = s.win.dts[count0 + q];
+    }
+    if (t.split == 0 && t.h % Ld.hpg == 0) {
+        for (int e = tid; e < T * (NN / 4); e += kThreads) {
+            const int q = e / (NN / 4), c4 = e % (NN / 4);
+            const size_t off = (((size_t)t.b * Ld.G + t.g) * Ld.L + (unsigned)(pos + q) % (unsigned)Ld.L) * NN + 4 * c4;
+            *(f32x4 *)(Ld.ring_B + off) = *(const f32x4 *)&s.win.Bw[count0 + q][4 * c4];
+            if (Ld.ring_C) *(f32x4 *)(Ld.ring_C + off) = *(const f32x4 *)&s.Cq[q][4 * c4];
         }
     }
-    for (int q = 0; q < T; ++q)
-        append_record<LMAX>(Ld, t, s.win, count0 + q, s.Cq[q], (int)((unsigned)(pos + q) % (unsigned)Ld.L));
 }
 
 // ==========================================================================================
@@ -966,7 +1007,13 @@ hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockst
 template <int PREC, int LMAX>
 hipError_t flush_t(const Layer &Ld, int mode, const int *arg, int T, float *out, hipStream_t st)
 {
-    hipLaunchKernelGGL((flush_kernel<PREC, LMAX>), dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, mode, arg, T, out);
+    if (mode == MODE_OVERFULL) {
+        hipLaunchKernelGGL(advance_kernel, dim3((Ld.Bt + 255) / 256), dim3(256), 0, st, Ld, arg, T);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((flush_kernel<PREC, LMAX>), dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, mode,
+                       mode == MODE_OVERFULL ? nullptr : arg, out);
     return hipGetLastError();
 }
 

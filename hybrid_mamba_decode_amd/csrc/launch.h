@@ -6,7 +6,9 @@
 
 namespace rssm {
 
-enum { MODE_MASK = 0, MODE_ROLLBACK = 1, MODE_MATERIALIZE = 2 };
+// MODE_OVERFULL: advance pos by the accepted counts, then fold sequences with more than L - Tmax
+// pending records (the rollback commit).
+enum { MODE_MASK = 0, MODE_OVERFULL = 1, MODE_MATERIALIZE = 2 };
 
 #define RSSM_DECLARE_LAUNCHERS(NV)                                                                     \
     hipError_t launch_step_n##NV(int prec, int lmax, const Layer &Ld, const TokenIO &io,               \
