@@ -22,6 +22,25 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def measured_traffic(prec):
+    """HBM bytes per non-flush replay launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs (profiles/traffic_counters.json), or None when the kernel sources changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_counters.json")))
+        csrc = os.path.join(ROOT, "hybrid_mamba_decode_amd", "csrc")
+        h = hashlib.sha256(open(os.path.join(csrc, "kernels.hip"), "rb").read() +
+                           open(os.path.join(csrc, "device.h"), "rb").read()).hexdigest()[:16]
+        if h != rec["kernel_source_sha256_16"] or prec not in rec["kernels"]:
+            return None
+        k = rec["kernels"][prec]
+        return {"bytes_per_launch": k["read_bytes_per_launch"] + k["write_bytes_per_launch"],
+                "over_algorithmic": k["traffic_over_alg"]}
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -130,18 +149,20 @@ def main():
                                f"{prec} read path",
                    "batch": Bt, "buffer_len": L, "read_prec": prec},
         "roofline": {
-            "kernel": "replay step, non-flush (step_kernel<prec, 16, false>)",
+            "kernel": "replay step, non-flush (step_kernel<prec, L bucket 16, rows, false>)",
             "bound": "hbm",
             "achieved": round(nf_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(nf_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(prec),
             "mean_launch_us": round(float(durs[nf].mean()) * 1e6, 2),
             "alg_bytes_per_launch": int(bytes_nf[nf].mean()),
         },
         "hbm_gbps_all_steps": round((bytes_nf[nf].sum() + bytes_fl * is_flush.sum()) / durs.sum() / 1e9, 1),
         "alg_bytes_per_step_amortized": int(amort_bytes),
+        "nonflush_us_by_k": {int(kk): round(float(durs[ks == kk].mean()) * 1e6, 1) for kk in range(1, L)
+                             if (ks == kk).any()},
         "flush_step": {"mean_launch_us": round(float(durs[is_flush].mean()) * 1e6, 2) if is_flush.any() else None,
                        "gbps": round(fl_gbps, 1) if fl_gbps else None,
                        "alg_bytes_per_launch": int(bytes_fl)},

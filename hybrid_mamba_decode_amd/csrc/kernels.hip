@@ -356,7 +356,6 @@ struct StepLds {
     float xw[LMAX][ROWS] __attribute__((aligned(16)));  // x of each record, rows of every head
     float Bw[LMAX][NN] __attribute__((aligned(16)));    // B of each record (the group's)
     float Cq[NN] __attribute__((aligned(16)));          // C of this token
-    float g[LMAX];                                      // B_j . C_t
     float u[ROWS];                                      // S_c . C_t per row
     float w[ROWS / kRows][LMAX];                        // per head: w_j
     float coef[ROWS / kRows][LMAX];                     // per head: w_j * g_j
@@ -458,6 +457,8 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         bv[sl] = j < k ? *(const f32x4 *)(src + 4 * c4) : zero;
     }
     const f32x4 cq = tid < NN / 4 ? *(const f32x4 *)(Ct + 4 * tid) : zero;
+    float cc[G::VEC];
+    load_cchunk<PREC>(cc, Ct, lane);
     float dtj = 0.f;
     if (wave < HPB && lane < k)
         dtj = lane < k - 1 ? Ld.ring_dt[(bh0 + wave) * Ld.L + slot_of(ck + lane)] : io.dt[bh0 + wave];
@@ -561,20 +562,9 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         return;
     }
 
-    // 6. Replay: row dots with C_t through the read copy (scores B_j . C_t alongside).
+    // 6. Replay: row dots with C_t through the read copy, then the scores B_j . C_t times the
+    //    weights of every head (GS threads per record).
     if (!kPreload) load_state();
-    float cc[G::VEC];
-#pragma unroll
-    for (int e = 0; e < G::VEC; ++e) cc[e] = s.Cq[c * G::VEC + e];
-    {
-        constexpr int GS = kThreads / LMAX;
-        const int j = tid / GS, sub = tid % GS;
-        float gj = 0.f;
-        for (int n = sub; n < NN; n += GS) gj = fmaf(s.Bw[j][n], s.Cq[n], gj);
-#pragma unroll
-        for (int o = GS / 2; o >= 1; o >>= 1) gj += __shfl_xor(gj, o, 64);
-        if (sub == 0) s.g[j] = gj;
-    }
     float part[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) part[i] = chunk_dot<PREC>(v[i], cc);
@@ -585,14 +575,24 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         const int r = first * G::RPB + wave * G::RPI + lane / G::LPR;
         if (writer && r < ROWS) s.u[r] = part[0];
     }
-    __syncthreads();
-    if (wave < HPB && lane < LMAX) s.coef[wave][lane] = wj * s.g[lane];
+    {
+        constexpr int GS = kThreads / LMAX;
+        const int j = tid / GS, sub = tid % GS;
+        float gj = 0.f;
+        for (int n = sub; n < NN; n += GS) gj = fmaf(s.Bw[j][n], s.Cq[n], gj);
+#pragma unroll
+        for (int o = GS / 2; o >= 1; o >>= 1) gj += __shfl_xor(gj, o, 64);
+        if (sub == 0)
+#pragma unroll
+            for (int hh = 0; hh < HPB; ++hh) s.coef[hh][j] = s.w[hh][j] * gj;
+    }
     __syncthreads();
 
     // 7. Combine and append.
     if (tid < ROWS && tid % kRows < t.nrows) {
         const int hh = tid / kRows, p = tid % kRows;
         float acc = s.decay[hh] * (s.u[tid] * scl_r);
+#pragma unroll 4
         for (int j = 0; j < k; ++j) acc = fmaf(s.coef[hh][j], s.xw[j][tid], acc);
         const float xt = s.xw[k - 1][tid];
         acc = fmaf(Ld.D[t.h + hh], xt, acc);
