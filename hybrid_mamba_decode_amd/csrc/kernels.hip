@@ -263,9 +263,15 @@ __device__ inline void write_copy_rows(const Layer &Ld, size_t bh, size_t elem0,
             const int r = row_of<PREC_F32>(i, wave, lane);
             if (r < nrows) {
                 const f32x4 f = vf[i];
-                const unsigned q = e4m3_encode(f.x * inv) | (e4m3_encode(f.y * inv) << 8) |
-                                   (e4m3_encode(f.z * inv) << 16) | (e4m3_encode(f.w * inv) << 24);
-                *(unsigned *)(dst + (size_t)r * NN + 4 * c) = q;
+                // clamp to the largest finite code, then gfx950's converter rounds to nearest even
+                // (four codes per dword, two per instruction)
+                const float a0 = fminf(fmaxf(f.x * inv, -448.0f), 448.0f);
+                const float a1 = fminf(fmaxf(f.y * inv, -448.0f), 448.0f);
+                const float a2 = fminf(fmaxf(f.z * inv, -448.0f), 448.0f);
+                const float a3 = fminf(fmaxf(f.w * inv, -448.0f), 448.0f);
+                int q = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+                q = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, q, true);
+                *(unsigned *)(dst + (size_t)r * NN + 4 * c) = (unsigned)q;
             }
         }
         if (threadIdx.x == 0) Ld.scale[bh] = scale;
@@ -979,14 +985,11 @@ __global__ void __launch_bounds__(kThreads) snapshot_verify_kernel(Layer Ld, flo
 // ------------------------------------------------------------------------------------------
 inline unsigned nblocks(const Layer &Ld) { return (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)Ld.psplit; }
 
-template <int PREC, int LMAX, int ROWS>
-hipError_t step_rows(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockstep ls, hipStream_t st)
+template <int PREC, int LMAX, int ROWS, bool FLUSH>
+hipError_t step_rows(const Layer &Ld, const TokenIO &io, Lockstep ls, hipStream_t st)
 {
     const unsigned grid = nblocks(Ld) / (ROWS / kRows);
-    if (flush_capable)
-        hipLaunchKernelGGL((step_kernel<PREC, LMAX, ROWS, true>), dim3(grid), dim3(kThreads), 0, st, Ld, io, ls);
-    else
-        hipLaunchKernelGGL((step_kernel<PREC, LMAX, ROWS, false>), dim3(grid), dim3(kThreads), 0, st, Ld, io, ls);
+    hipLaunchKernelGGL((step_kernel<PREC, LMAX, ROWS, FLUSH>), dim3(grid), dim3(kThreads), 0, st, Ld, io, ls);
     return hipGetLastError();
 }
 
@@ -999,9 +1002,10 @@ template <int PREC, int LMAX>
 hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockstep ls, hipStream_t st)
 {
     constexpr int wide = PREC == PREC_F32 ? 1 : PREC == PREC_BF16 ? 2 : 4;
-    if (!flush_capable && wide > 1 && Ld.psplit == 1 && Ld.hpg % wide == 0 && nblocks(Ld) / wide >= 2048)
-        return step_rows<PREC, LMAX, kRows * wide>(Ld, io, flush_capable, ls, st);
-    return step_rows<PREC, LMAX, kRows>(Ld, io, flush_capable, ls, st);
+    if (flush_capable) return step_rows<PREC, LMAX, kRows, true>(Ld, io, ls, st);
+    if (wide > 1 && Ld.psplit == 1 && Ld.hpg % wide == 0 && nblocks(Ld) / wide >= 2048)
+        return step_rows<PREC, LMAX, kRows * wide, false>(Ld, io, ls, st);
+    return step_rows<PREC, LMAX, kRows, false>(Ld, io, ls, st);
 }
 
 template <int PREC, int LMAX>
