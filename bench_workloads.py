@@ -6,8 +6,9 @@ spec:  speculative decode on the serving layer -- batch 512, T = 4 drafts, accep
        + commit launch), same inputs, same stream.
 sweep: the serving head shape stacked as 10 independent layers, batch in {1, 8, 64, 256, 512} x
        buffer length in {4, 8, 16, 32}, 64 decode steps: per-layer tokens/s of the replay step
-       (amortized over whole windows) and of the conventional step, the flush-step time per layer,
-       and the crossover batch.
+       (amortized over whole windows) and of the conventional step, eager and as HIP graphs
+       (a captured window of L steps x 10 layers), the flush-step time per layer, and the
+       crossover batch.
 
 States and per-step inputs are drawn on the GPU from a seeded torch generator with the layer
 definition's distributions (x ~ N(0,1); B, C ~ N(0, 1/N); dt = softplus(N(0,1) - 4); S0 ~ N(0,1)),
@@ -166,6 +167,14 @@ def sweep(args):
         _timed(conv_step, 4)
         wall_c, _ = _timed(conv_step, steps)
         conv_tps = Bt * steps * layers / wall_c   # tokens/s per layer: each step runs every layer
+        gc = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gc):
+            for r in range(16):
+                conv_step(r)
+        gc.replay()
+        wall_cg, _ = _timed(lambda r: gc.replay(), max(1, steps // 16))
+        conv_graph_tps = Bt * max(1, steps // 16) * 16 * layers / wall_cg
+        del gc
         del cst
         for L in (4, 8, 16, 32):
             lays = [rs.ReplaySSM(Bt, H, P, N, G, A, D, buffer_len=L) for _ in range(layers)]
@@ -180,7 +189,22 @@ def sweep(args):
             wall_r, d = _timed(rep_step, steps)      # 64 steps = whole windows for every L
             flush_idx = [r for r in range(steps) if (r + 1) % L == 0]
             nonflush_idx = [r for r in range(steps) if (r + 1) % L != 0]
+            # the same window captured once as a HIP graph (from a window boundary: the lockstep
+            # arguments repeat every window, so the graph replays correctly)
+            for l in range(layers):
+                lays[l].load_state(states[l])
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for r in range(L):
+                    rep_step(r)
+            gr.replay()
+            reps = max(1, steps // L)
+            wall_g, _ = _timed(lambda r: gr.replay(), reps)
+            graph_tps = Bt * reps * L * layers / wall_g
             rec = {"batch": Bt, "L": L, "layers": layers,
+                   "replay_graph_tokens_per_s_layer": round(graph_tps, 1),
+                   "conventional_graph_tokens_per_s_layer": round(conv_graph_tps, 1),
+                   "speedup_graph": round(graph_tps / conv_graph_tps, 3),
                    "replay_tokens_per_s_layer": round(Bt * steps * layers / wall_r, 1),
                    "conventional_tokens_per_s_layer": round(conv_tps, 1),
                    "speedup": round((Bt * steps * layers / wall_r) / conv_tps, 3),
@@ -192,7 +216,7 @@ def sweep(args):
                 assert lays[l].check() == rs.RSSM_OK
             print(json.dumps(rec), flush=True)
             results.append(rec)
-            del lays
+            del gr, lays
         del states
         torch.cuda.empty_cache()
     for L in (4, 8, 16, 32):

@@ -30,7 +30,8 @@ _PREC_NAMES = {"fp32": READ_FP32, "bf16": READ_BF16, "fp8": READ_FP8_E4M3, "fp8_
 EXPORTED = (
     "replayssm_workspace_bytes", "replayssm_workspace_layout", "replayssm_create", "replayssm_destroy",
     "replayssm_load_state", "replayssm_step", "replayssm_flush", "replayssm_spec_verify",
-    "replayssm_rollback", "replayssm_get_pointers", "replayssm_check", "replayssm_materialize_state",
+    "replayssm_rollback", "replayssm_set_lockstep", "replayssm_get_pointers", "replayssm_check",
+    "replayssm_materialize_state",
     "conventional_step", "snapshot_spec_verify", "snapshot_commit", "replayssm_status_string",
 )
 
@@ -60,6 +61,7 @@ _sig = {
     "replayssm_flush": (ctypes.c_int, [_vp, _vp, _vp]),
     "replayssm_spec_verify": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "replayssm_rollback": (ctypes.c_int, [_vp, _vp, _vp]),
+    "replayssm_set_lockstep": (ctypes.c_int, [_vp, ctypes.c_int]),
     "replayssm_get_pointers": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
     "replayssm_check": (ctypes.c_int, [_vp, _vp]),
     "replayssm_materialize_state": (ctypes.c_int, [_vp, _vp, _vp]),
@@ -162,6 +164,10 @@ def replayssm_spec_verify(h, T, x, B, C, dt, y, stream=None):
 def replayssm_rollback(h, accepted, stream=None):
     _check(_lib.replayssm_rollback(h, _ptr(accepted, torch.int32, "accepted"), _stream(stream)),
            "replayssm_rollback")
+
+
+def replayssm_set_lockstep(h, enable):
+    _check(_lib.replayssm_set_lockstep(h, int(bool(enable))), "replayssm_set_lockstep")
 
 
 def replayssm_get_pointers(h, batch, stream=None):
@@ -290,6 +296,9 @@ class ReplaySSM:
     def rollback(self, accepted, stream=None):
         _expect(accepted, (self.batch,), "accepted")
         replayssm_rollback(self.handle, accepted, stream)
+
+    def set_lockstep(self, enable):
+        replayssm_set_lockstep(self.handle, enable)
 
     def get_pointers(self, stream=None):
         return replayssm_get_pointers(self.handle, self.batch, stream)

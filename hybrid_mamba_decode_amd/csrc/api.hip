@@ -29,9 +29,12 @@ struct replayssm_layer {
     // launch may meet a flush). The device decides every flush per sequence, bit-exactly.
     int cmin, cmax;
     // Lockstep: after a load, standard steps and unmasked flushes keep every sequence at the same
-    // (pos, ckpt_pos), known here; the step kernel then takes them as arguments. A rollback or a
-    // masked flush makes sequences diverge: from then on kernels read the device pointers.
-    int uni, upos, uck;
+    // window position, known here as (pos mod L, ckpt_pos mod L, pending count); the step kernel
+    // takes it as arguments. These values repeat with every whole window, so a captured window
+    // replays correctly. A rollback or a masked flush makes sequences diverge: from then on
+    // kernels read the device pointers.
+    int uni, pslot, cslot, lcount;
+    int lockstep_ok;  // replayssm_set_lockstep: the fast path may be used at all
 };
 
 namespace {
@@ -247,6 +250,7 @@ rssm_status replayssm_create(const replayssm_config *cfg, void *workspace, size_
     d.hpg = cfg->nheads / cfg->ngroups;
     d.psplit = psplit_of(*cfg);
     h->lmax = cfg->buffer_len <= 16 ? 16 : cfg->buffer_len <= 32 ? 32 : 64;
+    h->lockstep_ok = 1;
     *out = h;
     return RSSM_OK;
 }
@@ -265,8 +269,8 @@ rssm_status replayssm_load_state(replayssm_t h, const float *state, void *stream
     h->poisoned = 0;
     h->pending_T = 0;
     h->cmin = h->cmax = 0;
-    h->uni = 1;
-    h->upos = h->uck = 0;
+    h->uni = h->lockstep_ok;
+    h->pslot = h->cslot = h->lcount = 0;
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) launch_load_n##NV(h->cfg.read_prec, h->dev, state, st)
@@ -286,12 +290,17 @@ rssm_status replayssm_step(replayssm_t h, const float *x, const float *B, const 
     if (h->pending_T) return RSSM_E_STATE;
     const int lim = h->cfg.buffer_len - h->cfg.max_draft;
     bool flush_capable = h->cmax + 1 > lim;
-    Lockstep ls{-1, -1};
+    Lockstep ls{0, 0, 0};
     if (h->uni) {
-        ls = Lockstep{h->upos, h->uck};
-        flush_capable = h->upos + 1 - h->uck > lim;  // every sequence flushes, or none does
-        h->upos += 1;
-        if (flush_capable) h->uck = h->upos;
+        ls = Lockstep{h->pslot, h->cslot, h->lcount + 1};
+        flush_capable = h->lcount + 1 > lim;  // every sequence flushes, or none does
+        h->pslot = (h->pslot + 1) % h->cfg.buffer_len;
+        if (flush_capable) {
+            h->lcount = 0;
+            h->cslot = h->pslot;
+        } else {
+            h->lcount += 1;
+        }
     }
     commit_bounds(h, 1, 1);
     if (h->cfg.batch == 0) return RSSM_OK;
@@ -311,7 +320,8 @@ rssm_status replayssm_flush(replayssm_t h, const int32_t *seq_mask, void *stream
     if (h->pending_T) return RSSM_E_STATE;
     if (!seq_mask) {
         h->cmin = h->cmax = 0;
-        h->uck = h->upos;
+        h->lcount = 0;
+        h->cslot = h->pslot;
     } else {
         h->cmin = 0;
         h->uni = 0;
@@ -359,6 +369,14 @@ rssm_status replayssm_rollback(replayssm_t h, const int32_t *accepted, void *str
 #define CALL(NV) launch_flush_n##NV(h->cfg.read_prec, h->lmax, h->dev, MODE_OVERFULL, accepted, T, nullptr, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
+}
+
+rssm_status replayssm_set_lockstep(replayssm_t h, int enable)
+{
+    if (!h || (enable != 0 && enable != 1)) return RSSM_E_INVAL;
+    h->lockstep_ok = enable;
+    if (!enable) h->uni = 0;
+    return RSSM_OK;
 }
 
 rssm_status replayssm_get_pointers(replayssm_t h, int32_t *pos, int32_t *ckpt_pos, void *stream)

@@ -54,10 +54,11 @@ struct TokenIO {
     float *y;
 };
 
-// Lockstep pointers: when every sequence is known (on the host) to hold the same (pos, ckpt_pos),
-// kernels take them as arguments; pos < 0 means "read each sequence's device pointers".
+// Lockstep window position: when every sequence is known (on the host) to be at the same window
+// position, kernels take it as (pos mod L, ckpt_pos mod L, records in the window including this
+// token); k = 0 means "read each sequence's device pointers".
 struct Lockstep {
-    int pos, ckpt;
+    int pslot, cslot, k;
 };
 
 // Device flag bits.

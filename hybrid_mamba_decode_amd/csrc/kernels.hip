@@ -414,28 +414,51 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     };
     if (kPreload) load_state();
 
-    // 2. Pointers. Lockstep: every sequence has the host-known (pos, ckpt_pos), so the window
-    //    loads below need no device read first. Otherwise: this sequence's device pointers,
-    //    validated before any address is formed from them.
-    const bool uni = ls.pos >= 0;
-    int pos, ck;
+    // 2. Pointers. Lockstep: every sequence is at the same, host-known window position, passed
+    //    as (pos mod L, ckpt_pos mod L, window count): the window loads below need no device read
+    //    first, and the arguments are the same on every replay of a captured whole window.
+    //    Otherwise: this sequence's device pointers, validated before any address is formed.
+    const bool uni = ls.k > 0;
+    int pslot, cslot, k;
     if (uni) {
-        pos = ls.pos;
-        ck = ls.ckpt;
+        pslot = ls.pslot;
+        cslot = ls.cslot;
+        k = ls.k;
     } else {
-        pos = Ld.pos[t.b];
-        ck = Ld.ckpt[t.b];
+        const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
         const int c0 = pos - ck;
         if (!(ck >= 0 && c0 >= 0 && c0 <= Ld.L - Ld.Tmax) || (!FLUSH && c0 + 1 > Ld.L - Ld.Tmax)) {
             raise_flag(Ld, FLAG_POINTERS);
             seq_done(Ld, t.b, pos, ck, HPB);
             return;
         }
+        pslot = (int)((unsigned)pos % (unsigned)Ld.L);
+        cslot = (int)((unsigned)ck % (unsigned)Ld.L);
+        k = c0 + 1;  // records in the window, this token included
     }
-    const int k = pos - ck + 1;  // records in the window, this token included
     const bool flush = k > Ld.L - Ld.Tmax;
-    const int new_ck = flush ? pos + 1 : ck;
-    auto slot_of = [&](int q) { return (int)((unsigned)q % (unsigned)Ld.L); };
+    auto slot_of = [&](int j) { return (int)((unsigned)(cslot + j) % (unsigned)Ld.L); };  // record j
+    // Pointer update, once per sequence. Lockstep: the work-group owning head 0 checks the device
+    // pointers against the window position (a mismatch means they were corrupted: flag, no
+    // update) and advances them; device mode: the last work-group of the sequence writes them.
+    auto advance_pointers = [&]() {
+        if (uni) {
+            if (t.h == 0 && t.split == 0 && tid == 0) {
+                const int dp = Ld.pos[t.b], dc = Ld.ckpt[t.b];
+                const bool ok = dc >= 0 && dp - dc == k - 1 && (int)((unsigned)dp % (unsigned)Ld.L) == pslot &&
+                                (int)((unsigned)dc % (unsigned)Ld.L) == cslot;
+                if (ok) {
+                    Ld.pos[t.b] = dp + 1;
+                    Ld.ckpt[t.b] = flush ? dp + 1 : dc;
+                } else {
+                    __hip_atomic_fetch_or(Ld.flag, FLAG_POINTERS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        } else {
+            const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];  // unchanged until every work-group counted
+            seq_done(Ld, t.b, pos + 1, flush ? pos + 1 : ck, HPB);
+        }
+    };
 
     // 3. Window loads into registers: x rows of every head, the group's B rows, this token's C,
     //    and (wave w, lane j) <- dt_j of head w.
@@ -453,13 +476,13 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     for (int sl = 0; sl < XS; ++sl) {
         const int e = tid + sl * kThreads, j = e / (ROWS / 4), rem = e % (ROWS / 4);
         const int hh = rem / (kRows / 4), c4 = rem % (kRows / 4);
-        const float *src = j < k - 1 ? rx + ((size_t)hh * Ld.L + slot_of(ck + j)) * Ld.P : fx + (size_t)hh * Ld.P;
+        const float *src = j < k - 1 ? rx + ((size_t)hh * Ld.L + slot_of(j)) * Ld.P : fx + (size_t)hh * Ld.P;
         xv[sl] = (j < k && 4 * c4 < t.nrows) ? *(const f32x4 *)(src + 4 * c4) : zero;
     }
 #pragma unroll
     for (int sl = 0; sl < BCH; ++sl) {
         const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
-        const float *src = j < k - 1 ? rB + (size_t)slot_of(ck + j) * NN : fB;
+        const float *src = j < k - 1 ? rB + (size_t)slot_of(j) * NN : fB;
         bv[sl] = j < k ? *(const f32x4 *)(src + 4 * c4) : zero;
     }
     const f32x4 cq = tid < NN / 4 ? *(const f32x4 *)(Ct + 4 * tid) : zero;
@@ -467,20 +490,9 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     load_cchunk<PREC>(cc, Ct, lane);
     float dtj = 0.f;
     if (wave < HPB && lane < k)
-        dtj = lane < k - 1 ? Ld.ring_dt[(bh0 + wave) * Ld.L + slot_of(ck + lane)] : io.dt[bh0 + wave];
+        dtj = lane < k - 1 ? Ld.ring_dt[(bh0 + wave) * Ld.L + slot_of(lane)] : io.dt[bh0 + wave];
     const float Aw = wave < HPB ? Ld.A[t.h + wave] : 0.f;
     const float scl_r = (PREC == PREC_FP8 && tid < ROWS) ? Ld.scale[bh0 + tid / kRows] : 1.0f;
-
-    // Lockstep: the device copy of the pointers must hold the host's values (or, if the
-    // sequence's pointer-writing work-group already ran, the new ones); anything else means the
-    // caller corrupted them, and the sequence is skipped with the flag raised.
-    if (uni) {
-        const int dp = Ld.pos[t.b], dc = Ld.ckpt[t.b];
-        if (!((dp == pos || dp == pos + 1) && (dc == ck || dc == new_ck))) {
-            raise_flag(Ld, FLAG_POINTERS);
-            return;
-        }
-    }
 
     // 4. Commit the window to LDS (B rows beyond the first chunk load here).
 #pragma unroll
@@ -494,7 +506,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
 #pragma unroll
             for (int sl = 0; sl < BCH; ++sl) {
                 const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
-                const float *src = j < k - 1 ? rB + (size_t)slot_of(ck + j) * NN : fB;
+                const float *src = j < k - 1 ? rB + (size_t)slot_of(j) * NN : fB;
                 bv[sl] = (s0 + sl < BS && j < k) ? *(const f32x4 *)(src + 4 * c4) : zero;
             }
         }
@@ -557,14 +569,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
             io.y[(bh0 + hh) * Ld.P + t.row0 + tid % kRows] = fmaf(Ld.D[t.h + hh], s.xw[k - 1][tid], s.u[tid]);
         }
         // The token's own record is folded already: nothing is appended on a flush step.
-        if (uni) {
-            if (t.h == 0 && t.split == 0 && tid == 0) {
-                Ld.pos[t.b] = pos + 1;
-                Ld.ckpt[t.b] = new_ck;
-            }
-        } else {
-            seq_done(Ld, t.b, pos + 1, new_ck, HPB);
-        }
+        advance_pointers();
         return;
     }
 
@@ -603,22 +608,15 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         const float xt = s.xw[k - 1][tid];
         acc = fmaf(Ld.D[t.h + hh], xt, acc);
         io.y[(bh0 + hh) * Ld.P + t.row0 + p] = acc;
-        Ld.ring_x[((bh0 + hh) * Ld.L + slot_of(pos)) * Ld.P + t.row0 + p] = xt;
+        Ld.ring_x[((bh0 + hh) * Ld.L + pslot) * Ld.P + t.row0 + p] = xt;
     }
-    if (t.split == 0 && wave < HPB && lane == k - 1) Ld.ring_dt[(bh0 + wave) * Ld.L + slot_of(pos)] = dtj;
+    if (t.split == 0 && wave < HPB && lane == k - 1) Ld.ring_dt[(bh0 + wave) * Ld.L + pslot] = dtj;
     if (t.split == 0 && t.h % Ld.hpg == 0 && tid < NN / 4) {
-        const size_t off = (((size_t)t.b * Ld.G + t.g) * Ld.L + slot_of(pos)) * NN + 4 * tid;
+        const size_t off = (((size_t)t.b * Ld.G + t.g) * Ld.L + pslot) * NN + 4 * tid;
         *(f32x4 *)(Ld.ring_B + off) = *(const f32x4 *)&s.Bw[k - 1][4 * tid];
         if (Ld.ring_C) *(f32x4 *)(Ld.ring_C + off) = *(const f32x4 *)&s.Cq[4 * tid];
     }
-    if (uni) {
-        if (t.h == 0 && t.split == 0 && tid == 0) {
-            Ld.pos[t.b] = pos + 1;
-            Ld.ckpt[t.b] = new_ck;
-        }
-    } else {
-        seq_done(Ld, t.b, pos + 1, new_ck, HPB);
-    }
+    advance_pointers();
 }
 
 // ==========================================================================================

@@ -147,6 +147,17 @@ rssm_status replayssm_spec_verify(replayssm_t layer, int32_t T, const float *x, 
  * Accepted counts outside [0, T] set the device flag and leave that sequence unchanged. */
 rssm_status replayssm_rollback(replayssm_t layer, const int32_t *accepted, void *stream);
 
+/* Lockstep fast path on (enable = 1, the default) or off (0). While every sequence is known on
+ * the host to be at the same window position -- after a load, standard steps and unmasked
+ * flushes -- replayssm_step passes (pos mod L, ckpt_pos mod L, window count) to the kernel as
+ * arguments instead of reading the device pointers first; the work-group owning head 0 of each
+ * sequence checks and advances that sequence's device pointers. These arguments repeat every L
+ * steps, so a captured HIP graph of whole windows (starting at a window boundary) replays
+ * correctly. A caller that captures other step sequences turns the fast path off: every launch
+ * then reads and updates the device pointers in place, which replays correctly for any graph.
+ * Switching on takes effect at the next replayssm_load_state. */
+rssm_status replayssm_set_lockstep(replayssm_t layer, int enable);
+
 /* Copy pos and ckpt_pos (host int32 [Bt] each; either may be NULL) after synchronizing the
  * stream. RSSM_E_STATE if the device flag is set. */
 rssm_status replayssm_get_pointers(replayssm_t layer, int32_t *pos, int32_t *ckpt_pos,

@@ -134,6 +134,11 @@ def test_state_machine_on_host():
     assert L.replayssm_flush(h, FAKE + 2, None) == rs.RSSM_E_INVAL
     assert L.replayssm_materialize_state(h, FAKE + 8, None) == rs.RSSM_E_INVAL
     assert L.replayssm_materialize_state(h, FAKE, None) == rs.RSSM_OK
+    assert L.replayssm_set_lockstep(h, 2) == rs.RSSM_E_INVAL
+    assert L.replayssm_set_lockstep(None, 0) == rs.RSSM_E_INVAL
+    assert L.replayssm_set_lockstep(h, 0) == rs.RSSM_OK
+    assert L.replayssm_step(h, *io, None) == rs.RSSM_OK
+    assert L.replayssm_set_lockstep(h, 1) == rs.RSSM_OK
     assert L.replayssm_destroy(h) == rs.RSSM_OK
 
 

@@ -272,3 +272,48 @@ def test_device_flag_on_corrupted_pointers():
     lay.load_state(dev(case.S0))
     assert lay.check() == rs.RSSM_OK
     assert lay.get_pointers() == ([0, 0], [0, 0])
+
+
+@pytest.mark.parametrize("prec,tol,lockstep", [("fp32", TOL_F32, True), ("fp32", TOL_F32, False),
+                                               ("fp8", TOL_FP8, True), ("bf16", TOL_BF16, False)])
+def test_graph_replay_of_whole_windows(prec, tol, lockstep):
+    """A captured HIP graph of one whole window (L steps, from a window boundary) replays
+    correctly with the lockstep fast path on (its arguments repeat every window) and off (device
+    pointers in place): each replay, with new inputs copied into the captured buffers and eager
+    work and synchronizations in between, matches the oracle, and the pointers advance by L per
+    replay; eager steps afterwards continue from the replayed state."""
+    Bt, H, P, N, G, L = 4, 8, 64, 128, 2, 4
+    case = Case(Bt, H, P, N, G, L, 91)
+    lay = case.layer(prec)
+    lay.set_lockstep(lockstep)
+    lay.load_state(dev(case.S0))
+    toks = [case.step_inputs(t) for t in range(L)]
+    bufs = [tuple(dev(a) for a in tk) for tk in toks]
+    ys = [torch.empty(Bt, H, P, device="cuda") for _ in range(L)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(L):
+            lay.step(*bufs[i], ys[i])
+    S = case.S0.astype(np.float64)
+    for r in range(4):
+        for i in range(L):
+            x, B, C, dt = case.step_inputs(r * L + i)
+            for d, src in zip(bufs[i], (x, B, C, dt)):
+                d.copy_(dev(src))
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(L):
+            x, B, C, dt = case.step_inputs(r * L + i)
+            y_ref = oracle.step(S, x, B, C, dt, case.A, case.D)
+            bound = TOL_F32 if i == L - 1 else tol
+            assert rel(host(ys[i]), y_ref) <= bound, f"replay {r} step {i}"
+        pos, ck = lay.get_pointers()
+        assert pos == [(r + 1) * L] * Bt and ck == [(r + 1) * L] * Bt
+        _ = torch.ones(1 << 20, device="cuda").sum().item()   # eager work between replays
+    assert rel(host(lay.master()), S) <= TOL_F32
+    for t in range(4 * L, 6 * L + 1):
+        x, B, C, dt = case.step_inputs(t)
+        y = lay.step(dev(x), dev(B), dev(C), dev(dt))
+        bound = TOL_F32 if (t + 1) % L == 0 else tol
+        assert rel(host(y), oracle.step(S, x, B, C, dt, case.A, case.D)) <= bound, f"eager step {t}"
+    assert lay.check() == rs.RSSM_OK
