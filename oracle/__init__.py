@@ -9,6 +9,7 @@ Functions (all arrays numpy, C-contiguous):
   spec_stepwise(S, T, x, B, C, dt, A, D, acc)  O5, the per-draft definition of spec decoding
   Replay(...)                                  O3 + O4, the replay form and its pointer machine
   bf16_encode / e4m3_encode_tiles / e4m3_encode_at / e4m3_decode / bf16_decode    O7
+  mxfp4_encode / mxfp4_decode / mx_scale_code / e2m1_encode_scaled / e2m1_decode   O7 (MXFP4)
 
 Pinning (what each function is checked against, independent of itself) is in tests/test_oracle_*.
 """
@@ -54,6 +55,13 @@ def lib():
         L.oracle_e4m3_decode.restype = ctypes.c_float
         L.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_decode.restype = ctypes.c_float
+        L.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_decode.restype = ctypes.c_float
+        L.oracle_encode_e2m1_scaled.argtypes = [_f64p, _u8p, _sz]
+        L.oracle_mx_scale_code.argtypes = [_f32p, _sz]
+        L.oracle_mx_scale_code.restype = ctypes.c_uint8
+        L.oracle_encode_mxfp4.argtypes = [_f32p, _u8p, _u8p, _sz]
+        L.oracle_decode_mxfp4.argtypes = [_u8p, _u8p, _f64p, _sz]
         L.oracle_replay_create.argtypes = [_i] * 8 + [_f32p, _f32p, _f32p]
         L.oracle_replay_create.restype = ctypes.c_void_p
         L.oracle_replay_destroy.argtypes = [ctypes.c_void_p]
@@ -107,7 +115,7 @@ def spec_stepwise(S, T, x, B, C, dt, A, D, accepted):
     return y
 
 
-READ_FP32, READ_BF16, READ_FP8 = 0, 1, 2
+READ_FP32, READ_BF16, READ_FP8, READ_MXFP4 = 0, 1, 2, 3
 
 
 class Replay:
@@ -205,3 +213,44 @@ def e4m3_encode_at(a, inv_scale=1.0):
 def e4m3_decode_table():
     """float32 value of each of the 256 codes (NaN for the two NaN codes)."""
     return np.array([lib().oracle_e4m3_decode(c) for c in range(256)], np.float32)
+
+
+def e2m1_decode(code):
+    """Value of a 4-bit OCP FP4 E2M1 code."""
+    return float(lib().oracle_e2m1_decode(int(code) & 15))
+
+
+def e2m1_encode_scaled(v):
+    """E2M1 codes (uint8, one per value) of values already divided by their block scale."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, np.uint8)
+    lib().oracle_encode_e2m1_scaled(v.reshape(-1), out.reshape(-1), v.size)
+    return out
+
+
+def mx_scale_code(block):
+    """E8M0 scale code of one block of values (reading R7)."""
+    b = _f32(block).reshape(-1)
+    return int(lib().oracle_mx_scale_code(b, b.size))
+
+
+def mxfp4_encode(a):
+    """MXFP4 encode along the last axis (a multiple of 32). Returns (codes uint8 [..., n/2],
+    scales uint8 [..., n/32]): element 2i in the low nibble of byte i."""
+    a = _f32(a)
+    assert a.shape[-1] % 32 == 0
+    nb = a.size // 32
+    codes = np.empty(a.shape[:-1] + (a.shape[-1] // 2,), np.uint8)
+    scales = np.empty(a.shape[:-1] + (a.shape[-1] // 32,), np.uint8)
+    lib().oracle_encode_mxfp4(a.reshape(-1), codes.reshape(-1), scales.reshape(-1), nb)
+    return codes, scales
+
+
+def mxfp4_decode(codes, scales):
+    """float64 values of MXFP4 codes [..., n/2] with scales [..., n/32]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    nb = scales.size
+    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), np.float64)
+    lib().oracle_decode_mxfp4(codes.reshape(-1), scales.reshape(-1), out.reshape(-1), nb)
+    return out

@@ -31,8 +31,16 @@
  *       records are pending, so T drafts always fit; with T = 1 this is rule R2.
  *   R6  read copy: bf16 by round-to-nearest-even, or OCP fp8 E4M3FN with one fp32 scale per
  *       (sequence, head) = amax/448 (1 when amax is 0), values multiplied by 1/scale in fp32,
- *       clamped to +-448 and rounded to nearest even. It is written from the master when a state
- *       is loaded and at every flush, never otherwise.
+ *       clamped to +-448 and rounded to nearest even, or OCP MXFP4 (reading R7). It is written
+ *       from the master when a state is loaded and at every flush, never otherwise.
+ *   R7  MXFP4 read copy (the pages' 4-bit state reads are NVFP4, which has no gfx950 form; MXFP4
+ *       is the OCP microscaling format gfx950 converts natively): per state row, blocks of 32
+ *       consecutive n share one E8M0 scale; elements are FP4 E2M1. Scale and rounding follow the
+ *       OCP "Microscaling Formats (MX)" specification v1.0: shared exponent = floor(log2(block
+ *       amax)) - 2 (2 = the exponent of E2M1's largest value, 6 = 1.5 * 2^2), elements = the value
+ *       divided by the scale, rounded to nearest with ties to even, clamped to +-6. The spec
+ *       leaves the scale of an all-zero block open: it takes the smallest code. Two elements per
+ *       byte, element 2i in the low nibble.
  *
  * Layouts (row-major, last index fastest): x [Bt,H,P]; B, C [Bt,G,N]; dt [Bt,H]; A, D [H];
  * state [Bt,H,P,N]; y [Bt,H,P]. Spec-decode inputs carry the draft index after the batch index:
@@ -224,6 +232,83 @@ void oracle_encode_e4m3_at(const float *in, uint8_t *out, size_t n, float inv)
     for (size_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode_scaled(in[i] * inv);
 }
 
+/* OCP FP4 E2M1 (MX specification v1.0, element data types): 1 sign bit, 2 exponent bits with */
+/* bias 1, 1 mantissa bit; exponent field 0 is subnormal (value m * 0.5); no infinities or NaN. */
+float oracle_e2m1_decode(uint8_t code)
+{
+    int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (float)(sign ? -mag : mag);
+}
+
+/* Code of a value already divided by its block scale (reading R7): the nearest of the eight    */
+/* magnitudes, on a tie the one with an even code (mantissa bit 0); beyond 6 the nearest is 6,  */
+/* which is the clamp. The sign bit follows the value's sign, so a negative that rounds to zero */
+/* is -0.                                                                                        */
+uint8_t oracle_e2m1_encode_scaled(double v)
+{
+    double mag = fabs(v), best_d = INFINITY;
+    int best = 0;
+    for (int c = 0; c < 8; ++c) {
+        double d = fabs(mag - (double)oracle_e2m1_decode((uint8_t)c));
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(best | (signbit(v) ? 8 : 0));
+}
+
+void oracle_encode_e2m1_scaled(const double *in, uint8_t *out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) out[i] = oracle_e2m1_encode_scaled(in[i]);
+}
+
+/* E8M0 scale code of one block of 32 (reading R7): X = 2^(floor(log2 amax) - 2), code = the    */
+/* exponent + 127, limited to the finite codes 0..254; 0 for an all-zero block.                 */
+uint8_t oracle_mx_scale_code(const float *blk, size_t n)
+{
+    double amax = 0.0;
+    for (size_t i = 0; i < n; ++i) amax = fmax(amax, fabs((double)blk[i]));
+    if (amax == 0.0) return 0;
+    int e;
+    frexp(amax, &e); /* amax = f * 2^e with 0.5 <= f < 1, so floor(log2 amax) = e - 1 */
+    int code = (e - 1) - 2 + 127;
+    if (code < 0) code = 0;
+    if (code > 254) code = 254;
+    return (uint8_t)code;
+}
+
+/* Encode nblocks blocks of 32 values: codes (16 bytes per block, element 2i in the low nibble  */
+/* of byte i) and one scale code per block. The division by the scale is exact in float64.      */
+void oracle_encode_mxfp4(const float *in, uint8_t *codes, uint8_t *scales, size_t nblocks)
+{
+#pragma omp parallel for schedule(static)
+    for (size_t b = 0; b < nblocks; ++b) {
+        const float *blk = in + b * 32;
+        uint8_t sc = oracle_mx_scale_code(blk, 32);
+        scales[b] = sc;
+        double inv = ldexp(1.0, 127 - (int)sc);
+        for (int i = 0; i < 32; i += 2) {
+            uint8_t lo = oracle_e2m1_encode_scaled((double)blk[i] * inv);
+            uint8_t hi = oracle_e2m1_encode_scaled((double)blk[i + 1] * inv);
+            codes[b * 16 + i / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+/* Decoded values of nblocks encoded blocks, in float64: E2M1 value times 2^(scale code - 127). */
+void oracle_decode_mxfp4(const uint8_t *codes, const uint8_t *scales, double *out, size_t nblocks)
+{
+    for (size_t b = 0; b < nblocks; ++b) {
+        for (int i = 0; i < 32; ++i) {
+            uint8_t byte = codes[b * 16 + i / 2];
+            uint8_t c = (i & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+            out[b * 32 + i] = ldexp((double)oracle_e2m1_decode(c), (int)scales[b] - 127);
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------------------------- */
 /* O3 + O4: the replay form with its pointer and flush state machine.                           */
 /*                                                                                             */
@@ -249,7 +334,7 @@ void oracle_encode_e4m3_at(const float *in, uint8_t *out, size_t n, float inv)
 /* ------------------------------------------------------------------------------------------- */
 
 typedef struct oracle_replay {
-    int Bt, H, P, N, G, L, Tmax, read_prec; /* read_prec: 0 fp32 master, 1 bf16, 2 fp8 e4m3 */
+    int Bt, H, P, N, G, L, Tmax, read_prec; /* 0 fp32 master, 1 bf16, 2 fp8 e4m3, 3 mxfp4 */
     double *A, *D;                          /* [H] */
     double *ckpt;                           /* [Bt,H,P,N] master */
     double *rcopy;                          /* [Bt,H,P,N] decoded read copy (read_prec != 0) */
@@ -294,6 +379,14 @@ static void refresh_copy(oracle_replay *r, int b)
         if (r->read_prec == 1) {
             for (size_t i = 0; i < tile; ++i)
                 c[i] = (double)oracle_bf16_decode(oracle_bf16_encode(f[i]));
+        } else if (r->read_prec == 3) {
+            /* blocks of 32 along n never cross a row, since N is a multiple of 32 */
+            const size_t nb = tile / 32;
+            uint8_t *codes = (uint8_t *)malloc(nb * 16), *sc = (uint8_t *)malloc(nb);
+            oracle_encode_mxfp4(f, codes, sc, nb);
+            oracle_decode_mxfp4(codes, sc, c, nb);
+            free(codes);
+            free(sc);
         } else {
             float s = oracle_e4m3_scale(f, tile);
             float inv = 1.0f / s;
@@ -308,7 +401,7 @@ oracle_replay *oracle_replay_create(int Bt, int H, int P, int N, int G, int L, i
                                     int read_prec, const float *S0, const float *A, const float *D)
 {
     if (Bt < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G || L <= 0 || L > 64 ||
-        Tmax <= 0 || Tmax > L || read_prec < 0 || read_prec > 2)
+        Tmax <= 0 || Tmax > L || read_prec < 0 || read_prec > 3 || (read_prec == 3 && N % 32))
         return NULL;
     oracle_replay *r = (oracle_replay *)calloc(1, sizeof(oracle_replay));
     r->Bt = Bt; r->H = H; r->P = P; r->N = N; r->G = G; r->L = L; r->Tmax = Tmax;
