@@ -10,7 +10,7 @@ Prints ONE JSON line (rank 0) with the metric, the dominant kernel's roofline (a
 per launch / its mean duration from HIP events on the launch stream), the same-run conventional
 read-update-write step, and the float64 CPU oracle timed on a bounded sample of the same workload.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--read-prec fp32|bf16|fp8]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--read-prec fp32|bf16|fp8|mxfp4]
                   [--no-cpu-baseline] [--kernels-only]
 """
 import argparse
@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--read-prec", default="fp32", choices=["fp32", "bf16", "fp8"])
+    ap.add_argument("--read-prec", default="fp32", choices=["fp32", "bf16", "fp8", "mxfp4"])
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--buffer-len", type=int, default=16)
     ap.add_argument("--pool", type=int, default=32, help="distinct input sets cycled through")

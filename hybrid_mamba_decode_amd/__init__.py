@@ -24,8 +24,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 RSSM_OK, RSSM_E_INVAL, RSSM_E_WORKSPACE, RSSM_E_HIP, RSSM_E_STATE, RSSM_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
-READ_FP32, READ_BF16, READ_FP8_E4M3 = 0, 1, 2
-_PREC_NAMES = {"fp32": READ_FP32, "bf16": READ_BF16, "fp8": READ_FP8_E4M3, "fp8_e4m3": READ_FP8_E4M3}
+READ_FP32, READ_BF16, READ_FP8_E4M3, READ_MXFP4 = 0, 1, 2, 3
+_PREC_NAMES = {"fp32": READ_FP32, "bf16": READ_BF16, "fp8": READ_FP8_E4M3, "fp8_e4m3": READ_FP8_E4M3,
+               "mxfp4": READ_MXFP4, "fp4": READ_MXFP4}
 
 EXPORTED = (
     "replayssm_workspace_bytes", "replayssm_workspace_layout", "replayssm_create", "replayssm_destroy",
@@ -331,9 +332,14 @@ class ReplaySSM:
             return self.region("read_copy", torch.int16, shape)
         if self.cfg.read_prec == READ_FP8_E4M3:
             return self.region("read_copy", torch.uint8, shape)
+        if self.cfg.read_prec == READ_MXFP4:
+            return self.region("read_copy", torch.uint8, shape[:3] + (self.dstate // 2,))
         return None
 
     def scales(self):
+        """fp8: fp32 per-head scales [Bt,H]; MXFP4: E8M0 block-scale bytes [Bt,H,P,N/32]."""
+        if self.cfg.read_prec == READ_MXFP4:
+            return self.region("scale", torch.uint8, (self.batch, self.nheads, self.headdim, self.dstate // 32))
         return self.region("scale", torch.float32, (self.batch, self.nheads))
 
     def pointer_arrays(self):

@@ -68,10 +68,11 @@ rssm_status check_config(const replayssm_config *c)
     rssm_status s = check_shape(c);
     if (s != RSSM_OK) return s;
     if (c->buffer_len < 1 || c->max_draft < 1 || c->max_draft > c->buffer_len) return RSSM_E_INVAL;
-    if (c->read_prec < RSSM_READ_FP32 || c->read_prec > RSSM_READ_FP8_E4M3) return RSSM_E_INVAL;
+    if (c->read_prec < RSSM_READ_FP32 || c->read_prec > RSSM_READ_MXFP4) return RSSM_E_INVAL;
     if (c->store_C != 0 && c->store_C != 1) return RSSM_E_INVAL;
     if (c->buffer_len > 64 || c->max_draft > 8) return RSSM_E_UNSUPPORTED;
     if (c->read_prec == RSSM_READ_FP8_E4M3 && c->headdim > kRows) return RSSM_E_UNSUPPORTED;
+    if (c->read_prec == RSSM_READ_MXFP4 && c->dstate < 32) return RSSM_E_UNSUPPORTED;
     return RSSM_OK;
 }
 
@@ -87,8 +88,10 @@ void make_layout(const replayssm_config &c, replayssm_layout *L)
         return at;
     };
     L->master = take(elems * 4);
-    L->read_copy = take(c.read_prec == RSSM_READ_BF16 ? elems * 2 : c.read_prec == RSSM_READ_FP8_E4M3 ? elems : 0);
-    L->scale = take(c.read_prec == RSSM_READ_FP8_E4M3 ? Bt * H * 4 : 0);
+    const int rp = c.read_prec;
+    L->read_copy = take(rp == RSSM_READ_BF16 ? elems * 2 : rp == RSSM_READ_FP8_E4M3 ? elems
+                        : rp == RSSM_READ_MXFP4 ? elems / 2 : 0);
+    L->scale = take(rp == RSSM_READ_FP8_E4M3 ? Bt * H * 4 : rp == RSSM_READ_MXFP4 ? elems / 32 : 0);
     L->ring_x = take(Bt * H * Lb * P * 4);
     L->ring_B = take(Bt * G * Lb * N * 4);
     L->ring_C = take(c.store_C ? Bt * G * Lb * N * 4 : 0);
@@ -231,6 +234,7 @@ rssm_status replayssm_create(const replayssm_config *cfg, void *workspace, size_
     d.master = (float *)(ws + lay.master);
     d.rcopy = cfg->read_prec == RSSM_READ_FP32 ? nullptr : (void *)(ws + lay.read_copy);
     d.scale = cfg->read_prec == RSSM_READ_FP8_E4M3 ? (float *)(ws + lay.scale) : nullptr;
+    d.mxscale = cfg->read_prec == RSSM_READ_MXFP4 ? (unsigned char *)(ws + lay.scale) : nullptr;
     d.ring_x = (float *)(ws + lay.ring_x);
     d.ring_B = (float *)(ws + lay.ring_B);
     d.ring_C = cfg->store_C ? (float *)(ws + lay.ring_C) : nullptr;

@@ -3,7 +3,8 @@
 // Tiling. One work-group (256 threads = 4 wave64s) owns up to kRows = 64 rows (headdim entries
 // p) of one (sequence, head) state tile [P, N]; a head with P > 64 is split over ceil(P/64)
 // work-groups. Within a wave the lanes run along N: each lane loads one 16-byte chunk of a row
-// per load slot (4 fp32, 8 bf16 or 16 fp8 values), LPR = N / VEC lanes cover a row and one wave
+// per load slot (4 fp32, 8 bf16, 16 fp8 or 32 fp4 values -- one fp4 chunk is exactly one MXFP4
+// scale block), LPR = N / VEC lanes cover a row and one wave
 // instruction covers RPI = 64 / LPR consecutive rows, so every wave instruction reads a
 // contiguous, fully coalesced 1 KiB. Per-row dot products are finished by a transpose-reduce
 // across the LPR lanes of a row (NL - 1 + log2(LPR/NL) lane exchanges instead of
@@ -24,7 +25,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRows = 64;
 
-enum { PREC_F32 = 0, PREC_BF16 = 1, PREC_FP8 = 2 };
+enum { PREC_F32 = 0, PREC_BF16 = 1, PREC_FP8 = 2, PREC_FP4 = 3 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -33,8 +34,9 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 // Everything a kernel needs to know about one layer's workspace (passed by value).
 struct Layer {
     float *master;      // [Bt,H,P,N] fp32 checkpoint
-    void *rcopy;        // [Bt,H,P,N] bf16 / e4m3 read copy (unused for fp32 reads)
+    void *rcopy;        // [Bt,H,P,N] bf16 / e4m3 read copy, or [Bt,H,P,N/2] MXFP4 bytes
     float *scale;       // [Bt,H] fp8 per-head scale
+    unsigned char *mxscale;  // [Bt,H,P,N/32] MXFP4 E8M0 block-scale codes
     float *ring_x;      // [Bt,H,L,P]
     float *ring_B;      // [Bt,G,L,N]
     float *ring_C;      // [Bt,G,L,N] or nullptr
@@ -66,7 +68,7 @@ enum : unsigned { FLAG_POINTERS = 1u, FLAG_ACCEPTED = 2u };
 
 template <int N, int PREC>
 struct Geo {
-    static constexpr int VEC = PREC == PREC_F32 ? 4 : PREC == PREC_BF16 ? 8 : 16;
+    static constexpr int VEC = PREC == PREC_F32 ? 4 : PREC == PREC_BF16 ? 8 : PREC == PREC_FP8 ? 16 : 32;
     static constexpr int LPR = N / VEC;          // lanes per row
     static constexpr int RPI = 64 / LPR;         // rows per wave instruction
     static constexpr int RPB = kWaves * RPI;     // rows per work-group instruction
@@ -169,6 +171,61 @@ __device__ inline float chunk_dot<PREC_FP8>(u32x4 v, const float *c)
         s = fmaf(hi.y, c[4 * i + 3], s);
     }
     return s;
+}
+
+// MXFP4 codes: 32 E2M1 values per chunk (one scale block), decoded by gfx950's converter two per
+// instruction, low nibble first (checked on the GPU against the E2M1 table for every byte value
+// and byte position, signed zeros included). The block scale 2^(code - 127) is applied to the
+// lane's partial sum (mx_scaled).
+template <>
+__device__ inline float chunk_dot<PREC_FP4>(u32x4 v, const float *c)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    float s = 0.0f;
+    const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 0);
+        const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 1);
+        const f32x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 2);
+        const f32x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 3);
+        s = fmaf(b0.x, c[8 * i + 0], s);
+        s = fmaf(b0.y, c[8 * i + 1], s);
+        s = fmaf(b1.x, c[8 * i + 2], s);
+        s = fmaf(b1.y, c[8 * i + 3], s);
+        s = fmaf(b2.x, c[8 * i + 4], s);
+        s = fmaf(b2.y, c[8 * i + 5], s);
+        s = fmaf(b3.x, c[8 * i + 6], s);
+        s = fmaf(b3.y, c[8 * i + 7], s);
+    }
+    return s;
+}
+
+// A partial sum over one MXFP4 block times the block scale 2^(code - 127) (exact: v_ldexp_f32).
+__device__ inline float mx_scaled(float part, unsigned code) { return __builtin_amdgcn_ldexpf(part, (int)code - 127); }
+
+// MXFP4 encode of four consecutive fp32 values of one block, given the block's amax: returns the
+// E8M0 code; `codes` gets the two code bytes (element order low nibble first). Scale exponent =
+// max(biased exponent of amax - 2, 0), so every value / scale is below 8; the division is exact
+// (multiplication by 2^(127 - code), a normal fp32 for codes 0..253). Quotients of magnitude
+// below 0.25 are set to a signed zero first (they round to zero; this keeps fp32 denormals out
+// of the converter); gfx950's v_cvt_scalef32_pk_fp4_f32 then rounds to nearest even and clamps
+// to +-6 (checked on the GPU against that rule over dense sweeps of [2^-4, 8], ties included).
+__device__ inline unsigned mx_code_of(float amax)
+{
+    const int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+    return (unsigned)(e > 2 ? e - 2 : 0);
+}
+
+__device__ inline unsigned short mx_encode4(f32x4 f, unsigned code)
+{
+    const float inv = __uint_as_float((254u - code) << 23);  // 2^(127 - code)
+    float a[4] = {f.x * inv, f.y * inv, f.z * inv, f.w * inv};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = fabsf(a[i]) < 0.25f ? copysignf(0.0f, a[i]) : a[i];
+    const unsigned lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a[0], a[1], 1.0f, 0) & 0xFFu;
+    const unsigned hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a[2], a[3], 1.0f, 0) & 0xFFu;
+    return (unsigned short)(lo | (hi << 8));
 }
 
 // ------------------------------------------------------------------------------------------

@@ -24,8 +24,17 @@ namespace {
 constexpr int NN = RSSM_N;
 using GF = Geo<NN, PREC_F32>;  // fp32 geometry (master tile, records)
 
+// Byte offset of element e of a state array in precision PREC (fp4: two elements per byte; e is
+// always a chunk start, hence even).
 template <int PREC>
-constexpr int elem_bytes() { return PREC == PREC_F32 ? 4 : PREC == PREC_BF16 ? 2 : 1; }
+constexpr size_t byte_off(size_t e)
+{
+    return PREC == PREC_F32 ? e * 4 : PREC == PREC_BF16 ? e * 2 : PREC == PREC_FP8 ? e : e / 2;
+}
+
+// MXFP4 needs N >= 32 (a scale block is 32 consecutive n of one row).
+template <int PREC>
+constexpr bool kPrecOk = !(PREC == PREC_FP4 && NN < 32);
 
 template <int PREC>
 constexpr int kNL = Geo<NN, PREC>::NL;
@@ -45,8 +54,23 @@ __device__ inline void load_rows(u32x4 (&v)[kNL<PREC>], const char *rows, int nr
 #pragma unroll
     for (int i = 0; i < G::NL; ++i) {
         const int r = i * G::RPB + wave * G::RPI + lane / G::LPR;
-        v[i] = (r < nrows) ? load_nt(rows + ((size_t)r * NN + (size_t)c * G::VEC) * elem_bytes<PREC>())
+        v[i] = (r < nrows) ? load_nt(rows + byte_off<PREC>((size_t)r * NN + (size_t)c * G::VEC))
                            : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// MXFP4 block-scale codes of the chunks load_rows reads (a chunk is one block); rows at or
+// beyond nrows get 127 (scale 1; their sums are never used).
+template <int PREC>
+__device__ inline void load_mxscales(unsigned (&sc)[kNL<PREC>], const unsigned char *rows, int nrows,
+                                     int wave, int lane)
+{
+    using G = Geo<NN, PREC>;
+    const int c = lane % G::LPR;
+#pragma unroll
+    for (int i = 0; i < G::NL; ++i) {
+        const int r = i * G::RPB + wave * G::RPI + lane / G::LPR;
+        sc[i] = r < nrows ? rows[(size_t)r * (NN / 32) + c] : 127u;
     }
 }
 
@@ -275,6 +299,27 @@ __device__ inline void write_copy_rows(const Layer &Ld, size_t bh, size_t elem0,
             }
         }
         if (threadIdx.x == 0) Ld.scale[bh] = scale;
+    } else if constexpr (PREC == PREC_FP4) {
+        // One 32-value block = 8 consecutive lanes of a row (4 values each); its amax by three
+        // lane exchanges, then each lane encodes its 4 values into 2 bytes and the block's first
+        // lane writes the scale byte.
+        unsigned char *dst = (unsigned char *)Ld.rcopy + elem0 / 2;
+        unsigned char *sdst = Ld.mxscale + elem0 / 32;
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            const int r = row_of<PREC_F32>(i, wave, lane);
+            const f32x4 f = vf[i];
+            float amax = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
+            amax = group_max(amax, 8);
+            const unsigned code = mx_code_of(amax);
+            if (r < nrows) {
+                const size_t e = (size_t)r * NN + 4 * c;
+                *(unsigned short *)(dst + e / 2) = mx_encode4(f, code);
+                if (c % 8 == 0) sdst[e / 32] = (unsigned char)code;
+            }
+        }
+        (void)bh;
+        (void)red;
     }
 }
 
@@ -402,6 +447,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     //    Row r of the work-group is row (r % 64) of head r / 64.
     constexpr bool kPreload = !FLUSH || (PREC == PREC_F32 && HPB == 1);
     u32x4 v[NL];
+    unsigned sc[NL];  // MXFP4: block-scale code of each chunk
     // All loads are issued unconditionally, so the issue sequence is straight-line and each wait
     // covers exactly the loads it needs. Lanes outside the tile load this tile's first row and
     // keep it: rows are independent in every use below, and those rows are never written.
@@ -414,7 +460,8 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
             const bool in = r < ROWS && p < t.nrows;
             const size_t e = in ? ((bh0 + hh) * Ld.P + t.row0 + p) * NN + (size_t)c * G::VEC
                                 : (bh0 * Ld.P + t.row0) * NN + (size_t)c * G::VEC;
-            v[i] = load_nt(base + e * elem_bytes<PREC>());
+            v[i] = load_nt(base + byte_off<PREC>(e));
+            if constexpr (PREC == PREC_FP4) sc[i] = Ld.mxscale[e / 32];
         }
     };
     // 2. Pointers. Lockstep: every sequence is at the same, host-known window position, passed
@@ -614,7 +661,10 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     }
     float part[NL];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) part[i] = chunk_dot<PREC>(v[i], cc);
+    for (int i = 0; i < NL; ++i) {
+        part[i] = chunk_dot<PREC>(v[i], cc);
+        if constexpr (PREC == PREC_FP4) part[i] = mx_scaled(part[i], sc[i]);
+    }
     {
         transpose_reduce<NL, G::LPR>(part, lane);
         bool writer;
@@ -749,9 +799,11 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
     const size_t bh = (size_t)t.b * Ld.H + t.h;
     const size_t elem0 = (bh * Ld.P + t.row0) * NN;
     const char *rrows = (PREC == PREC_F32 ? (const char *)Ld.master : (const char *)Ld.rcopy) +
-                        elem0 * elem_bytes<PREC>();
+                        byte_off<PREC>(elem0);
     u32x4 v[G::NL];
     load_rows<PREC>(v, rrows, t.nrows, wave, lane);
+    unsigned sc[G::NL];
+    if constexpr (PREC == PREC_FP4) load_mxscales<PREC>(sc, Ld.mxscale + elem0 / 32, t.nrows, wave, lane);
 
     const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
     const int count0 = pos - ck;
@@ -799,7 +851,10 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
 #pragma unroll
     for (int q = 0; q < TQ; ++q)
 #pragma unroll
-        for (int i = 0; i < G::NL; ++i) part[q * G::NL + i] = chunk_dot<PREC>(v[i], cc[q]);
+        for (int i = 0; i < G::NL; ++i) {
+            part[q * G::NL + i] = chunk_dot<PREC>(v[i], cc[q]);
+            if constexpr (PREC == PREC_FP4) part[q * G::NL + i] = mx_scaled(part[q * G::NL + i], sc[i]);
+        }
     const float scl = PREC == PREC_FP8 ? Ld.scale[bh] : 1.0f;
     rows_to_lds<PREC, G::NL * TQ>(part, &s.u[0][0], kRows, T, G::NL, scl, wave, lane);
     __syncthreads();
@@ -1018,15 +1073,17 @@ hipError_t step_rows(const Layer &Ld, const TokenIO &io, Lockstep ls, hipStream_
 
 // Heads per work-group: 1 for fp32 (two fp32 heads per work-group measured no faster: the
 // occupancy drops from 8 to 4 work-groups per CU); for the narrow copies as many as make
-// ~32 KiB of checkpoint per work-group (bf16 2, fp8 4), when the head tile fits one work-group
-// (P <= 64), the group divides evenly and the launch keeps at least 2048 work-groups (8 per CU).
+// ~32 KiB of checkpoint per work-group (bf16 2, fp8 4; fp4 4 as well, 16 KiB, since the
+// transpose-reduce needs at most LPR load slots per lane), when the head tile fits one work-group
+// (P <= 64), the group divides evenly, the launch keeps at least 2048 work-groups (8 per CU) and
+// the window bucket is at most 32 (at 64 the x window of four heads fills 100 KiB of LDS).
 // Flush-capable launches use one head per work-group (their fold loop is per head).
 template <int PREC, int LMAX>
 hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockstep ls, hipStream_t st)
 {
-    constexpr int wide = PREC == PREC_F32 ? 1 : PREC == PREC_BF16 ? 2 : 4;
+    constexpr int wide = PREC == PREC_F32 ? 1 : PREC == PREC_BF16 ? 2 : 4;  // fp8 and fp4: 4
     if (flush_capable) return step_rows<PREC, LMAX, kRows, true>(Ld, io, ls, st);
-    if (wide > 1 && Ld.psplit == 1 && Ld.hpg % wide == 0 && nblocks(Ld) / wide >= 2048)
+    if (wide > 1 && LMAX <= 32 && Ld.psplit == 1 && Ld.hpg % wide == 0 && nblocks(Ld) / wide >= 2048)
         return step_rows<PREC, LMAX, kRows * wide, false>(Ld, io, ls, st);
     return step_rows<PREC, LMAX, kRows, false>(Ld, io, ls, st);
 }
@@ -1072,6 +1129,9 @@ hipError_t by_prec_lmax(int prec, int lmax, Args... args)
     case PREC_FP8 * 100 + 16: return F<PREC_FP8, 16>::run(args...);
     case PREC_FP8 * 100 + 32: return F<PREC_FP8, 32>::run(args...);
     case PREC_FP8 * 100 + 64: return F<PREC_FP8, 64>::run(args...);
+    case PREC_FP4 * 100 + 16: return F<PREC_FP4, 16>::run(args...);
+    case PREC_FP4 * 100 + 32: return F<PREC_FP4, 32>::run(args...);
+    case PREC_FP4 * 100 + 64: return F<PREC_FP4, 64>::run(args...);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1080,20 +1140,37 @@ template <int PREC, int LMAX>
 struct StepF {
     static hipError_t run(const Layer &Ld, const TokenIO &io, bool fc, Lockstep ls, hipStream_t st)
     {
-        return step_t<PREC, LMAX>(Ld, io, fc, ls, st);
+        if constexpr (!kPrecOk<PREC>) return hipErrorInvalidValue;
+        else return step_t<PREC, LMAX>(Ld, io, fc, ls, st);
     }
 };
 template <int PREC, int LMAX>
 struct FlushF {
     static hipError_t run(const Layer &Ld, int mode, const int *arg, int T, float *out, hipStream_t st)
     {
-        return flush_t<PREC, LMAX>(Ld, mode, arg, T, out, st);
+        if constexpr (!kPrecOk<PREC>) return hipErrorInvalidValue;
+        else return flush_t<PREC, LMAX>(Ld, mode, arg, T, out, st);
     }
 };
 template <int PREC, int LMAX>
 struct VerifyF {
-    static hipError_t run(const Layer &Ld, const TokenIO &io, int T, hipStream_t st) { return verify_tq<PREC, LMAX>(Ld, io, T, st); }
+    static hipError_t run(const Layer &Ld, const TokenIO &io, int T, hipStream_t st)
+    {
+        if constexpr (!kPrecOk<PREC>) return hipErrorInvalidValue;
+        else return verify_tq<PREC, LMAX>(Ld, io, T, st);
+    }
 };
+
+template <int PREC>
+hipError_t load_p(const Layer &Ld, const float *state, hipStream_t st)
+{
+    if constexpr (!kPrecOk<PREC>) {
+        return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((load_state_kernel<PREC>), dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, state);
+        return hipGetLastError();
+    }
+}
 
 }  // namespace
 
@@ -1119,14 +1196,13 @@ hipError_t RSSM_CAT(launch_verify_n, RSSM_N)(int prec, int lmax, const Layer &Ld
 
 hipError_t RSSM_CAT(launch_load_n, RSSM_N)(int prec, const Layer &Ld, const float *state, hipStream_t st)
 {
-    const dim3 grid(nblocks(Ld)), block(kThreads);
     switch (prec) {
-    case PREC_F32: hipLaunchKernelGGL((load_state_kernel<PREC_F32>), grid, block, 0, st, Ld, state); break;
-    case PREC_BF16: hipLaunchKernelGGL((load_state_kernel<PREC_BF16>), grid, block, 0, st, Ld, state); break;
-    case PREC_FP8: hipLaunchKernelGGL((load_state_kernel<PREC_FP8>), grid, block, 0, st, Ld, state); break;
+    case PREC_F32: return load_p<PREC_F32>(Ld, state, st);
+    case PREC_BF16: return load_p<PREC_BF16>(Ld, state, st);
+    case PREC_FP8: return load_p<PREC_FP8>(Ld, state, st);
+    case PREC_FP4: return load_p<PREC_FP4>(Ld, state, st);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t RSSM_CAT(launch_conventional_n, RSSM_N)(const Layer &Ld, float *state, const TokenIO &io, hipStream_t st)

@@ -10,12 +10,18 @@ token (1..L).
 """
 
 F32 = 4
-ELEM = {"fp32": 4, "bf16": 2, "fp8": 1}
+ELEM = {"fp32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5}
 
 
 def state_bytes(H, P, N, prec="fp32"):
-    b = H * P * N * ELEM[prec]
-    return b + (H * F32 if prec == "fp8" else 0)
+    """One state (or read copy) of H heads: fp8 adds its fp32 per-head scales, MXFP4 its E8M0
+    byte per block of 32 values."""
+    b = int(H * P * N * ELEM[prec])
+    if prec == "fp8":
+        b += H * F32
+    elif prec == "mxfp4":
+        b += H * P * N // 32
+    return b
 
 
 def token_input_bytes(H, P, N, G):

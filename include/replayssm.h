@@ -25,7 +25,8 @@
  *     spec-decode inputs: x [Bt,T,H,P]  B, C [Bt,T,G,N]  dt [Bt,T,H]  y [Bt,T,H,P]
  * All float arrays are fp32. Supported: N in {16, 32, 64, 128, 256}; P a multiple of 4, at most
  * 256; 1 <= L <= 64; 1 <= max_draft <= min(L, 8); H a multiple of G. The fp8 read copy needs
- * P <= 64 (one work-group owns a whole head tile, so the per-head scale is exact).
+ * P <= 64 (one work-group owns a whole head tile, so the per-head scale is exact); the MXFP4 read
+ * copy needs N >= 32 (its scale blocks are 32 consecutive n of one row).
  *
  * Memory. The caller owns every device buffer: inputs, outputs, A, D and the workspace (from
  * PyTorch or hipMalloc). The library allocates no device memory. The handle is host memory.
@@ -65,7 +66,24 @@ typedef enum {
     RSSM_E_UNSUPPORTED = -5   /* valid but unsupported configuration */
 } rssm_status;
 
-typedef enum { RSSM_READ_FP32 = 0, RSSM_READ_BF16 = 1, RSSM_READ_FP8_E4M3 = 2 } rssm_read_prec;
+/* Precision of the checkpoint copy that serves replay reads; the checkpoint master is always
+ * fp32 and every flush re-encodes the copy from it. The pages' 4-bit state reads are NVFP4
+ * ([AT Pulse] lede, "Capabilities and access" and "Claims and evidence"), a format gfx950 has no
+ * instructions for; the copies here are gfx950-native formats:
+ *   BF16      round to nearest even.
+ *   FP8_E4M3  OCP E4M3FN codes, one fp32 scale per (sequence, head) = amax / 448 (1 if amax = 0);
+ *             codes = RNE of value / scale clamped to +-448.
+ *   MXFP4     OCP MX v1.0 FP4 (E2M1) codes in blocks of 32 consecutive n of a row, one E8M0 scale
+ *             byte per block: scale = 2^(e - 127) with e = max(biased fp32 exponent of the block's
+ *             amax - 2, 0) (so the largest element lands in [4, 8) before clamping to 6); codes =
+ *             RNE of value / scale clamped to +-6, sign kept (a negative rounding to 0 is -0).
+ *             Byte i of a block holds element 2i in its low nibble and 2i + 1 in its high nibble. */
+typedef enum {
+    RSSM_READ_FP32 = 0,
+    RSSM_READ_BF16 = 1,
+    RSSM_READ_FP8_E4M3 = 2,
+    RSSM_READ_MXFP4 = 3
+} rssm_read_prec;
 
 typedef struct {
     int32_t batch;       /* Bt >= 0 (0: every call is a no-op) */
@@ -82,8 +100,10 @@ typedef struct {
 /* Byte offsets of the workspace regions (for inspection by tests and tools). */
 typedef struct {
     size_t master;     /* fp32 checkpoint [Bt,H,P,N] -- updated only by flushes */
-    size_t read_copy;  /* bf16 [Bt,H,P,N] or fp8 e4m3fn [Bt,H,P,N]; 0 bytes for fp32 reads */
-    size_t scale;      /* fp32 [Bt,H] per-head scale of the fp8 copy (0 bytes otherwise) */
+    size_t read_copy;  /* bf16 [Bt,H,P,N], fp8 e4m3fn [Bt,H,P,N] or MXFP4 bytes [Bt,H,P,N/2];
+                          0 bytes for fp32 reads */
+    size_t scale;      /* fp8: fp32 [Bt,H] per-head scales; MXFP4: E8M0 bytes [Bt,H,P,N/32];
+                          0 bytes otherwise */
     size_t ring_x;     /* fp32 [Bt,H,L,P]: record of absolute position q sits in slot q mod L */
     size_t ring_B;     /* fp32 [Bt,G,L,N] */
     size_t ring_C;     /* fp32 [Bt,G,L,N] (0 bytes when store_C = 0) */

@@ -1,10 +1,39 @@
 """Shared helpers of the GPU parity tests: device transfer, the normwise error metric, and a
 driver that runs the HIP layer and the float64 oracle side by side on the same seeded inputs."""
+import json
+import os
+
 import numpy as np
 import torch
 
 import oracle
 import workload
+
+PREC_CODE = {"fp32": oracle.READ_FP32, "bf16": oracle.READ_BF16, "fp8": oracle.READ_FP8,
+             "mxfp4": oracle.READ_MXFP4}
+
+_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "mxfp4_codes.json")
+with open(_GOLDEN) as _f:
+    _E2M1 = np.array(json.load(_f)["e2m1_values"], np.float64)   # hand-derived code table
+
+
+def decode_copy(lay, prec, sample):
+    """Values of the layer's read copy for the sampled sequences, float64, decoded without the
+    oracle: bf16 by bit shift, fp8 by PyTorch's float8_e4m3fn, MXFP4 by the hand-derived E2M1
+    table times 2^(scale code - 127)."""
+    idx = torch.as_tensor(np.asarray(sample), device="cuda")
+    if prec == "bf16":
+        c = host(lay.read_copy()[idx]).view(np.uint16).astype(np.uint32) << 16
+        return c.view(np.float32).astype(np.float64)
+    if prec == "fp8":
+        v = host(lay.read_copy()[idx].view(torch.float8_e4m3fn).float()).astype(np.float64)
+        return v * host(lay.scales()[idx]).astype(np.float64)[:, :, None, None]
+    if prec == "mxfp4":
+        b = host(lay.read_copy()[idx])
+        codes = np.stack([b & 15, b >> 4], axis=-1).reshape(b.shape[:-1] + (b.shape[-1] * 2,))
+        sc = host(lay.scales()[idx]).astype(np.int64) - 127
+        return np.ldexp(_E2M1[codes], np.repeat(sc, 32, axis=-1))
+    raise ValueError(prec)
 
 
 def dev(a, dtype=None):

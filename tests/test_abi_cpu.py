@@ -53,6 +53,10 @@ def test_workspace_layout_serving_shape():
     l8 = rs.replayssm_workspace_layout(c8)
     assert l8.scale - l8.read_copy == Bt * H * P * N           # one byte per element
     assert l8.ring_x - l8.scale == Bt * H * 4
+    c4 = cfg(batch=256, read_prec="mxfp4", headdim=100)
+    l4 = rs.replayssm_workspace_layout(c4)
+    assert l4.scale - l4.read_copy == Bt * H * 100 * N // 2     # two codes per byte
+    assert l4.ring_x - l4.scale == Bt * H * 100 * N // 32       # one E8M0 byte per 32 values
     cb = cfg(batch=256, read_prec="bf16", store_C=False)
     lb = rs.replayssm_workspace_layout(cb)
     assert lb.scale - lb.read_copy == Bt * H * P * N * 2
@@ -69,8 +73,9 @@ def test_workspace_layout_serving_shape():
     (dict(buffer_len=4, max_draft=5), rs.RSSM_E_INVAL),
     (dict(buffer_len=65), rs.RSSM_E_UNSUPPORTED),
     (dict(buffer_len=16, max_draft=9), rs.RSSM_E_UNSUPPORTED),
-    (dict(read_prec=3), rs.RSSM_E_INVAL),
+    (dict(read_prec=4), rs.RSSM_E_INVAL),
     (dict(read_prec="fp8", headdim=128), rs.RSSM_E_UNSUPPORTED),
+    (dict(read_prec="mxfp4", dstate=16), rs.RSSM_E_UNSUPPORTED),
     (dict(batch=-1), rs.RSSM_E_INVAL),
     (dict(store_C=2), rs.RSSM_E_INVAL),
 ])

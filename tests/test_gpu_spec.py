@@ -13,7 +13,7 @@ import torch
 import hybrid_mamba_decode_amd as rs
 import oracle
 import workload
-from gpu_harness import Case, dev, host, log, rel
+from gpu_harness import PREC_CODE, Case, dev, host, log, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -34,6 +34,9 @@ def _run_spec(case, T, iters, sample, read_prec="fp32", tol=TOL_F32, accept=None
     sample = np.asarray(sample)
     S = case.S0[sample].astype(np.float64)
     ptr = _pointer_machine(case.Bt, case.L, T)
+    # replay form with the same read copy: until a sampled sequence first flushes, its copy is the
+    # oracle's encoding bit for bit, so the verify outputs must match this model to fp32 rounding
+    dual = oracle.Replay(case.S0[sample], case.A, case.D, case.G, case.L, T, PREC_CODE[read_prec])
     zeros_tok = [np.zeros((case.Bt, T, 1, 1), np.float32), np.zeros((case.Bt, T, 1, 1), np.float32),
                  np.zeros((case.Bt, T, 1, 1), np.float32), np.zeros((case.Bt, T, 1), np.float32)]
     cfg = rs.make_config(case.Bt, case.H, case.P, case.N, case.G)
@@ -55,6 +58,12 @@ def _run_spec(case, T, iters, sample, read_prec="fp32", tol=TOL_F32, accept=None
         e = rel(host(y)[sample], y_ref)
         worst = max(worst, e)
         assert e <= tol, f"verify {it}: output error {e:.3e}"
+        never_flushed = not dual.pointers()[1].any()
+        y_dual = dual.verify(T, x[sample], B[sample], C[sample], dt[sample])
+        dual.rollback(acc[sample])
+        if never_flushed or read_prec == "fp32":
+            e_dual = rel(host(y)[sample], y_dual)
+            assert e_dual <= TOL_F32, f"verify {it}: error vs the dual-precision model {e_dual:.3e}"
         ptr.verify(T, *zeros_tok)
         ptr.rollback(acc)
         pos, ck = lay.get_pointers()
@@ -73,6 +82,7 @@ def _run_spec(case, T, iters, sample, read_prec="fp32", tol=TOL_F32, accept=None
             xs, Bs, Cs, dts = workload.step_inputs(case.seed + 1, it, case.Bt, case.H, case.P, case.N, case.G)
             ys1 = lay.step(dev(xs), dev(Bs), dev(Cs), dev(dts))
             y1_ref = oracle.step(S, xs[sample], Bs[sample], Cs[sample], dts[sample], case.A, case.D)
+            dual.step(xs[sample], Bs[sample], Cs[sample], dts[sample])
             assert rel(host(ys1)[sample], y1_ref) <= tol
             one = [np.zeros((case.Bt, 1, 1), np.float32)] * 3 + [np.zeros((case.Bt, 1), np.float32)]
             ptr.step(*one)
@@ -111,7 +121,7 @@ def test_spec_accept_extremes_and_interleaved_steps():
     _run_spec(case, 3, 24, range(4), accept=lambda it: pattern[it % 3], interleave_steps=True)
 
 
-@pytest.mark.parametrize("prec,tol", [("bf16", 2e-2), ("fp8", 6e-2)])
+@pytest.mark.parametrize("prec,tol", [("bf16", 2e-2), ("fp8", 6e-2), ("mxfp4", 0.25)])
 def test_spec_dual_precision(prec, tol):
     case = Case(2, 8, 64, 128, 2, 16, 41, Tmax=4)
     _run_spec(case, 4, 40, range(2), read_prec=prec, tol=tol)
