@@ -327,13 +327,17 @@ class ReplaySSM:
         return self.region("master", torch.float32, (self.batch, self.nheads, self.headdim, self.dstate))
 
     def read_copy(self):
-        shape = (self.batch, self.nheads, self.headdim, self.dstate)
+        """The read copy in row-major order: bf16 bits int16 [Bt,H,P,N], fp8 codes uint8
+        [Bt,H,P,N], MXFP4 code bytes uint8 [Bt,H,P,N/2]. bf16 is a view of the workspace; the fp8
+        and MXFP4 copies are stored per head as 16-byte chunks in chunk-column-major order
+        ([N/VEC][P] chunks, see replayssm.h), so this returns a reordered copy."""
+        Bt, H, P, N = self.batch, self.nheads, self.headdim, self.dstate
         if self.cfg.read_prec == READ_BF16:
-            return self.region("read_copy", torch.int16, shape)
-        if self.cfg.read_prec == READ_FP8_E4M3:
-            return self.region("read_copy", torch.uint8, shape)
-        if self.cfg.read_prec == READ_MXFP4:
-            return self.region("read_copy", torch.uint8, shape[:3] + (self.dstate // 2,))
+            return self.region("read_copy", torch.int16, (Bt, H, P, N))
+        if self.cfg.read_prec in (READ_FP8_E4M3, READ_MXFP4):
+            row_bytes = N if self.cfg.read_prec == READ_FP8_E4M3 else N // 2
+            raw = self.region("read_copy", torch.uint8, (Bt, H, row_bytes // 16, P, 16))
+            return raw.permute(0, 1, 3, 2, 4).contiguous().view(Bt, H, P, row_bytes)
         return None
 
     def scales(self):

@@ -36,6 +36,21 @@ constexpr size_t byte_off(size_t e)
 template <int PREC>
 constexpr bool kPrecOk = !(PREC == PREC_FP4 && NN < 32);
 
+// Byte offset of 16-byte chunk q (elements [q*VEC, (q+1)*VEC)) of row p of head bh in a state
+// array of precision PREC. The fp32 master and the bf16 copy are row-major ([P][N] per head).
+// The fp8 and MXFP4 copies are chunk-column-major per head ([N/VEC][P] chunks): one wave
+// instruction over 64 consecutive rows of one chunk column then reads 1 KiB contiguously, which
+// is what the one-row-per-lane step kernel issues; lane-along-N kernels read them in runs of
+// RPI rows (128-256 bytes).
+template <int PREC>
+__device__ inline size_t chunk_off(size_t bh, int p, int q, int P)
+{
+    using G = Geo<NN, PREC>;
+    const size_t head = byte_off<PREC>(bh * (size_t)P * NN);
+    if constexpr (PREC == PREC_FP8 || PREC == PREC_FP4) return head + ((size_t)q * P + p) * 16;
+    else return head + ((size_t)p * (NN / G::VEC) + q) * 16;
+}
+
 template <int PREC>
 constexpr int kNL = Geo<NN, PREC>::NL;
 template <int PREC>
@@ -281,7 +296,8 @@ __device__ inline void write_copy_rows(const Layer &Ld, size_t bh, size_t elem0,
         amax = block_max(amax, red);
         const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
         const float inv = 1.0f / scale;
-        unsigned char *dst = (unsigned char *)Ld.rcopy + elem0;
+        unsigned char *dst = (unsigned char *)Ld.rcopy;
+        const int row0 = (int)(elem0 / NN - bh * (size_t)Ld.P);
 #pragma unroll
         for (int i = 0; i < GF::NL; ++i) {
             const int r = row_of<PREC_F32>(i, wave, lane);
@@ -295,7 +311,8 @@ __device__ inline void write_copy_rows(const Layer &Ld, size_t bh, size_t elem0,
                 const float a3 = fminf(fmaxf(f.w * inv, -448.0f), 448.0f);
                 int q = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
                 q = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, q, true);
-                *(unsigned *)(dst + (size_t)r * NN + 4 * c) = (unsigned)q;
+                const int n = 4 * c;
+                *(unsigned *)(dst + chunk_off<PREC_FP8>(bh, row0 + r, n / 16, Ld.P) + n % 16) = (unsigned)q;
             }
         }
         if (threadIdx.x == 0) Ld.scale[bh] = scale;
@@ -303,8 +320,9 @@ __device__ inline void write_copy_rows(const Layer &Ld, size_t bh, size_t elem0,
         // One 32-value block = 8 consecutive lanes of a row (4 values each); its amax by three
         // lane exchanges, then each lane encodes its 4 values into 2 bytes and the block's first
         // lane writes the scale byte.
-        unsigned char *dst = (unsigned char *)Ld.rcopy + elem0 / 2;
+        unsigned char *dst = (unsigned char *)Ld.rcopy;
         unsigned char *sdst = Ld.mxscale + elem0 / 32;
+        const int row0 = (int)(elem0 / NN - bh * (size_t)Ld.P);
 #pragma unroll
         for (int i = 0; i < GF::NL; ++i) {
             const int r = row_of<PREC_F32>(i, wave, lane);
@@ -313,12 +331,12 @@ __device__ inline void write_copy_rows(const Layer &Ld, size_t bh, size_t elem0,
             amax = group_max(amax, 8);
             const unsigned code = mx_code_of(amax);
             if (r < nrows) {
-                const size_t e = (size_t)r * NN + 4 * c;
-                *(unsigned short *)(dst + e / 2) = mx_encode4(f, code);
-                if (c % 8 == 0) sdst[e / 32] = (unsigned char)code;
+                const int n = 4 * c;
+                *(unsigned short *)(dst + chunk_off<PREC_FP4>(bh, row0 + r, n / 32, Ld.P) + (n % 32) / 2) =
+                    mx_encode4(f, code);
+                if (c % 8 == 0) sdst[((size_t)r * NN + n) / 32] = (unsigned char)code;
             }
         }
-        (void)bh;
         (void)red;
     }
 }
@@ -456,12 +474,10 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int r = i * G::RPB + wave * G::RPI + lane / G::LPR;
-            const int hh = r / kRows, p = r % kRows;
-            const bool in = r < ROWS && p < t.nrows;
-            const size_t e = in ? ((bh0 + hh) * Ld.P + t.row0 + p) * NN + (size_t)c * G::VEC
-                                : (bh0 * Ld.P + t.row0) * NN + (size_t)c * G::VEC;
-            v[i] = load_nt(base + byte_off<PREC>(e));
-            if constexpr (PREC == PREC_FP4) sc[i] = Ld.mxscale[e / 32];
+            const bool in = r < ROWS && r % kRows < t.nrows;
+            const int hh = in ? r / kRows : 0, pp = t.row0 + (in ? r % kRows : 0);
+            v[i] = load_nt(base + chunk_off<PREC>(bh0 + hh, pp, c, Ld.P));
+            if constexpr (PREC == PREC_FP4) sc[i] = Ld.mxscale[((bh0 + hh) * Ld.P + pp) * (NN / 32) + c];
         }
     };
     // 2. Pointers. Lockstep: every sequence is at the same, host-known window position, passed
@@ -695,6 +711,258 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
 }
 
 // ==========================================================================================
+// Replay step through a narrow read copy (fp8 or MXFP4), launches without flushes: one state
+// row per lane. Wave w owns head t.h + w and lane p its row p (P <= 64), so every lane of a wave
+// walks the same chunk column at the same time: C_t's slice for that column is wave-uniform and
+// comes from scalar loads (SGPR operands of the FMAs), the row's dot needs no cross-lane
+// reduction, and each lane reads its own row's x window directly. Compared with the lane-along-N
+// step this frees the C-chunk registers and the x-window LDS, so more work-groups -- and more
+// checkpoint bytes -- are in flight per CU. Same arithmetic as step_kernel ([AT Pulse]
+// "Technical analysis": the unrolled window).
+// ==========================================================================================
+template <int LMAX>
+struct NarrowLds {
+    float Bw[LMAX][NN] __attribute__((aligned(16)));  // B of each record (the group's)
+    float Cq[NN] __attribute__((aligned(16)));        // C of this token
+    float g[LMAX];                                    // scores B_j . C_t
+};
+
+template <int PREC, int LMAX>
+__global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO io, Lockstep ls)
+{
+    using G = Geo<NN, PREC>;
+    constexpr int NC = NN / G::VEC;  // chunks per row
+    constexpr int HPB = kWaves;      // heads per work-group, one per wave
+    __shared__ NarrowLds<LMAX> s;
+    const Tile t = map_heads(Ld, HPB);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar head index
+    const int h = t.h + wave;
+    const size_t bh = (size_t)t.b * Ld.H + h;
+    const bool prow = lane < Ld.P;
+    const int p = prow ? lane : 0;  // lanes beyond P read row 0 and store nothing
+
+    // 1. Checkpoint row through the read copy (and, for MXFP4, the row's block-scale codes).
+    u32x4 v[NC];
+    unsigned scw[(NC + 3) / 4];
+    auto load_state = [&]() {
+        const char *base = (const char *)Ld.rcopy;
+#pragma unroll
+        for (int q = 0; q < NC; ++q) v[q] = load_nt(base + chunk_off<PREC>(bh, p, q, Ld.P));
+        if constexpr (PREC == PREC_FP4) {
+            const unsigned char *sr = Ld.mxscale + (bh * Ld.P + p) * NC;
+            if constexpr (NC >= 4) {
+#pragma unroll
+                for (int w4 = 0; w4 < NC / 4; ++w4) scw[w4] = *(const unsigned *)(sr + 4 * w4);
+            } else if constexpr (NC == 2) {
+                scw[0] = *(const unsigned short *)sr;
+            } else {
+                scw[0] = *sr;
+            }
+        }
+    };
+
+    // 2. Pointers (as in step_kernel: lockstep arguments, or this sequence's device pointers).
+    const bool uni = ls.k > 0;
+    int pslot = 0, cslot = 0, k = 1;
+    auto slot_of = [&](int j) { return (int)((unsigned)(cslot + j) % (unsigned)Ld.L); };
+
+    // 3. Window. Issued in two groups so that the staging registers of the first are free before
+    //    the second is loaded: (a) the group's B rows and C_t, staged through LDS, and (lane j)
+    //    dt_j of this head; (b) this lane's x_j (record j of its row, 0 beyond the window) and the
+    //    token's x, loaded after (a) is committed.
+    constexpr int BS = (LMAX * NN / 4 + kThreads - 1) / kThreads;
+    constexpr int BCH = BS < 8 ? BS : 8;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const float *rB = Ld.ring_B + ((size_t)t.b * Ld.G + t.g) * Ld.L * NN;
+    const float *fB = io.B + ((size_t)t.b * Ld.G + t.g) * NN;
+    const float *Ct = io.C + ((size_t)t.b * Ld.G + t.g) * NN;
+    float xj[LMAX], xt = 0.f, dtj = 0.f, Ah = 0.f;
+    f32x4 bv[BCH], cq;
+    auto issue_bc = [&]() {
+#pragma unroll
+        for (int sl = 0; sl < BCH; ++sl) {
+            const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+            const float *src = (j < k - 1 ? rB + (size_t)slot_of(j) * NN : fB) + 4 * c4;
+            const f32x4 val = *(const f32x4 *)src;
+            bv[sl] = j < k ? val : zero;
+        }
+        {
+            const f32x4 val = *(const f32x4 *)(Ct + 4 * (tid % (NN / 4)));
+            cq = tid < NN / 4 ? val : zero;
+        }
+        {
+            const bool in = lane < k;
+            const float val = (in && lane < k - 1) ? Ld.ring_dt[bh * Ld.L + slot_of(lane)] : io.dt[bh];
+            dtj = in ? val : 0.f;
+            Ah = Ld.A[h];
+        }
+    };
+    auto issue_x = [&]() {
+        const float *fx = io.x + bh * Ld.P + p;
+        const float *rx = Ld.ring_x + bh * Ld.L * Ld.P + p;
+#pragma unroll
+        for (int j = 0; j < LMAX; ++j) {
+            const float *src = j < k - 1 ? rx + (size_t)slot_of(j) * Ld.P : fx;
+            const float val = *src;
+            xj[j] = j < k ? val : 0.f;
+        }
+        xt = *fx;
+    };
+
+    // Invalid device pointers are only noted here and reported after the row dots (with safe
+    // window values meanwhile, and no store): no memory write may precede the dots, or the
+    // compiler can no longer load C_t through the scalar cache.
+    bool bad = false;
+    if (uni) {
+        pslot = ls.pslot;
+        cslot = ls.cslot;
+        k = ls.k;
+        issue_bc();
+        load_state();
+    } else {
+        load_state();
+        const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
+        const int c0 = pos - ck;
+        bad = !(ck >= 0 && c0 >= 0 && c0 + 1 <= Ld.L - Ld.Tmax);
+        pslot = bad ? 0 : (int)((unsigned)pos % (unsigned)Ld.L);
+        cslot = bad ? 0 : (int)((unsigned)ck % (unsigned)Ld.L);
+        k = bad ? 1 : c0 + 1;
+        issue_bc();
+    }
+
+    // 4. B window and C_t to LDS; then the x window; this head's weights in its wave meanwhile.
+#pragma unroll
+    for (int s0 = 0; s0 < BS; s0 += BCH) {
+        if (s0 > 0) {
+#pragma unroll
+            for (int sl = 0; sl < BCH; ++sl) {
+                const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+                const float *src = j < k - 1 ? rB + (size_t)slot_of(j) * NN : fB;
+                bv[sl] = (s0 + sl < BS && j < k) ? *(const f32x4 *)(src + 4 * c4) : zero;
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < BCH; ++sl) {
+            const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+            if (s0 + sl < BS && j < LMAX) *(f32x4 *)&s.Bw[j][4 * c4] = bv[sl];
+        }
+    }
+    if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = cq;
+    issue_x();
+    // w_j = dt_j * exp(A * sum_{i>j} dt_i), decay = exp(A * sum_i dt_i): suffix sums by shuffles
+    float wj, decay;
+    {
+        float sfx = dtj;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float nb = __shfl_down(sfx, o, 64);
+            sfx += lane + o < 64 ? nb : 0.f;
+        }
+        const float nxt = __shfl_down(sfx, 1, 64);
+        const float tail = lane + 1 < 64 ? nxt : 0.f;
+        wj = lane < k ? dtj * expf(Ah * tail) : 0.f;
+        decay = expf(Ah * __shfl(sfx, 0, 64));
+    }
+    __syncthreads();
+    // 5. Scores g_j = B_j . C_t (GS threads per record).
+    {
+        constexpr int GS = kThreads / LMAX;
+        const int j = tid / GS, sub = tid % GS;
+        float gj = 0.f;
+        for (int n = sub; n < NN; n += GS) gj = fmaf(s.Bw[j][n], s.Cq[n], gj);
+#pragma unroll
+        for (int o = GS / 2; o >= 1; o >>= 1) gj += __shfl_xor(gj, o, 64);
+        if (sub == 0) s.g[j] = gj;
+    }
+    __syncthreads();
+    const float cj = lane < LMAX ? wj * s.g[lane < LMAX ? lane : 0] : 0.f;  // lane j: w_j * g_j
+
+    // 6. Row dot S_c[p,:] . C_t through the copy. C_t's chunk-column slice is the same for every
+    //    lane: broadcast reads of the staged C. The empty asm ties each chunk's decode to the
+    //    running sums, so chunks are decoded one at a time instead of all at once (which would
+    //    hold N decoded values per lane).
+    float u0 = 0.f, u1 = 0.f;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+        asm("" : "+v"(v[q]), "+v"(u0), "+v"(u1));
+        const float *cs = s.Cq + q * G::VEC;
+        const unsigned w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            if constexpr (PREC == PREC_FP8) {
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+                a0 = fmaf(lo.x, cs[4 * i + 0], a0);
+                a1 = fmaf(lo.y, cs[4 * i + 1], a1);
+                a0 = fmaf(hi.x, cs[4 * i + 2], a0);
+                a1 = fmaf(hi.y, cs[4 * i + 3], a1);
+            } else {
+                const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 0);
+                const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 1);
+                const f32x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 2);
+                const f32x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 3);
+                a0 = fmaf(b0.x, cs[8 * i + 0], a0);
+                a1 = fmaf(b0.y, cs[8 * i + 1], a1);
+                a0 = fmaf(b1.x, cs[8 * i + 2], a0);
+                a1 = fmaf(b1.y, cs[8 * i + 3], a1);
+                a0 = fmaf(b2.x, cs[8 * i + 4], a0);
+                a1 = fmaf(b2.y, cs[8 * i + 5], a1);
+                a0 = fmaf(b3.x, cs[8 * i + 6], a0);
+                a1 = fmaf(b3.y, cs[8 * i + 7], a1);
+            }
+        }
+        if constexpr (PREC == PREC_FP4) {
+            const unsigned code = (scw[q / 4] >> (8 * (q % 4))) & 0xFFu;
+            u0 += mx_scaled(a0 + a1, code);
+        } else {
+            u0 += a0;
+            u1 += a1;
+        }
+    }
+    float u = u0 + u1;
+    if constexpr (PREC == PREC_FP8) u *= Ld.scale[bh];
+
+    if (bad) {
+        raise_flag(Ld, FLAG_POINTERS);
+        seq_done(Ld, t.b, Ld.pos[t.b], Ld.ckpt[t.b], HPB);
+        return;
+    }
+
+    // 7. Combine: y = decay * u + sum_j (w_j g_j) x_j + D x_t; append the record.
+    float acc = decay * u;
+#pragma unroll
+    for (int j = 0; j < LMAX; ++j)
+        acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(cj), j)), xj[j], acc);
+    acc = fmaf(Ld.D[h], xt, acc);
+    if (prow) {
+        io.y[bh * Ld.P + p] = acc;
+        Ld.ring_x[(bh * Ld.L + pslot) * Ld.P + p] = xt;
+    }
+    if (lane == k - 1) Ld.ring_dt[bh * Ld.L + pslot] = dtj;
+    if (t.h % Ld.hpg == 0 && tid < NN / 4) {
+        const size_t off = (((size_t)t.b * Ld.G + t.g) * Ld.L + pslot) * NN + 4 * tid;
+        *(f32x4 *)(Ld.ring_B + off) = *(const f32x4 *)&s.Bw[k - 1][4 * tid];
+        if (Ld.ring_C) *(f32x4 *)(Ld.ring_C + off) = *(const f32x4 *)&s.Cq[4 * tid];
+    }
+    // pointer update, once per sequence (see step_kernel)
+    if (uni) {
+        if (t.h == 0 && tid == 0) {
+            const int dp = Ld.pos[t.b], dc = Ld.ckpt[t.b];
+            const bool ok = dc >= 0 && dp - dc == k - 1 && (int)((unsigned)dp % (unsigned)Ld.L) == pslot &&
+                            (int)((unsigned)dc % (unsigned)Ld.L) == cslot;
+            if (ok) Ld.pos[t.b] = dp + 1;
+            else __hip_atomic_fetch_or(Ld.flag, FLAG_POINTERS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
+        seq_done(Ld, t.b, pos + 1, ck, HPB);
+    }
+}
+
+// ==========================================================================================
 // Flush / commit-flush / materialize. MODE_MASK: fold every committed record of the selected
 // sequences. MODE_OVERFULL (after a rollback moved pos by the accepted count -- rejected drafts
 // are dropped by that pointer move, [AT Pulse] "Technical analysis"): fold the sequences with
@@ -798,10 +1066,14 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh = (size_t)t.b * Ld.H + t.h;
     const size_t elem0 = (bh * Ld.P + t.row0) * NN;
-    const char *rrows = (PREC == PREC_F32 ? (const char *)Ld.master : (const char *)Ld.rcopy) +
-                        byte_off<PREC>(elem0);
+    const char *rbase = PREC == PREC_F32 ? (const char *)Ld.master : (const char *)Ld.rcopy;
     u32x4 v[G::NL];
-    load_rows<PREC>(v, rrows, t.nrows, wave, lane);
+#pragma unroll
+    for (int i = 0; i < G::NL; ++i) {
+        const int r = row_of<PREC>(i, wave, lane);
+        v[i] = r < t.nrows ? load_nt(rbase + chunk_off<PREC>(bh, t.row0 + r, lane % G::LPR, Ld.P))
+                           : u32x4{0u, 0u, 0u, 0u};
+    }
     unsigned sc[G::NL];
     if constexpr (PREC == PREC_FP4) load_mxscales<PREC>(sc, Ld.mxscale + elem0 / 32, t.nrows, wave, lane);
 
@@ -1083,6 +1355,15 @@ hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockst
 {
     constexpr int wide = PREC == PREC_F32 ? 1 : PREC == PREC_BF16 ? 2 : 4;  // fp8 and fp4: 4
     if (flush_capable) return step_rows<PREC, LMAX, kRows, true>(Ld, io, ls, st);
+    if constexpr ((PREC == PREC_FP8 || PREC == PREC_FP4) && LMAX == 16 && NN <= 128) {
+        // one row per lane: P <= 64, four heads of one group per work-group; at N = 256 a row's
+        // chunks would hold 64 (fp8) registers per lane
+        if (Ld.P <= kRows && Ld.hpg % kWaves == 0) {
+            const unsigned grid = nblocks(Ld) / kWaves;
+            hipLaunchKernelGGL((narrow_step_kernel<PREC, LMAX>), dim3(grid), dim3(kThreads), 0, st, Ld, io, ls);
+            return hipGetLastError();
+        }
+    }
     if (wide > 1 && LMAX <= 32 && Ld.psplit == 1 && Ld.hpg % wide == 0 && nblocks(Ld) / wide >= 2048)
         return step_rows<PREC, LMAX, kRows * wide, false>(Ld, io, ls, st);
     return step_rows<PREC, LMAX, kRows, false>(Ld, io, ls, st);

@@ -100,7 +100,10 @@ typedef struct {
 /* Byte offsets of the workspace regions (for inspection by tests and tools). */
 typedef struct {
     size_t master;     /* fp32 checkpoint [Bt,H,P,N] -- updated only by flushes */
-    size_t read_copy;  /* bf16 [Bt,H,P,N], fp8 e4m3fn [Bt,H,P,N] or MXFP4 bytes [Bt,H,P,N/2];
+    size_t read_copy;  /* bf16 [Bt,H,P,N] row-major; fp8 e4m3fn codes or MXFP4 code bytes in
+                          16-byte chunks (16 fp8 / 32 fp4 values of one row), per head ordered
+                          [N/VEC][P]: chunk q of row p of head (b,h) at byte offset
+                          ((b*H + h)*P*N*s) + (q*P + p)*16, s = 1 (fp8) or 1/2 (fp4);
                           0 bytes for fp32 reads */
     size_t scale;      /* fp8: fp32 [Bt,H] per-head scales; MXFP4: E8M0 bytes [Bt,H,P,N/32];
                           0 bytes otherwise */

@@ -301,11 +301,15 @@ def test_batch_zero_is_a_no_op():
     assert lay.get_pointers() == ([], [])
 
 
-def test_device_flag_on_corrupted_pointers():
+@pytest.mark.parametrize("prec,lockstep", [("fp32", True), ("fp32", False), ("fp8", True), ("fp8", False),
+                                           ("mxfp4", False)])
+def test_device_flag_on_corrupted_pointers(prec, lockstep):
     """Pointers corrupted by the caller (ckpt_pos > pos): kernels detect the breach, skip the
-    sequence and set the device flag; the handle then refuses work until the next load."""
-    case = Case(2, 4, 16, 16, 1, 4, 11)
-    lay = case.layer()
+    sequence and set the device flag; the handle then refuses work until the next load. Covers
+    the lane-along-N and the one-row-per-lane step kernels, in lockstep and device-pointer mode."""
+    case = Case(2, 4, 16, 32, 1, 4, 11)
+    lay = case.layer(prec)
+    lay.set_lockstep(lockstep)
     x, B, C, dt = case.step_inputs(0)
     lay.step(dev(x), dev(B), dev(C), dev(dt))
     pos, ck = lay.pointer_arrays()
