@@ -10,6 +10,9 @@ Functions (all arrays numpy, C-contiguous):
   Replay(...)                                  O3 + O4, the replay form and its pointer machine
   bf16_encode / e4m3_encode_tiles / e4m3_encode_at / e4m3_decode / bf16_decode    O7
   mxfp4_encode / mxfp4_decode / mx_scale_code / e2m1_encode_scaled / e2m1_decode   O7 (MXFP4)
+  gdn_step(S, q, k, v, alpha, beta) -> o       O1g, one Gated DeltaNet token (oracle_gdn.c)
+  gdn_spec_stepwise(...)                       O5g, per-draft spec decoding on GDN
+  GDNReplay(...)                               O3g + O4, the GDN replay form and pointer machine
 
 Pinning (what each function is checked against, independent of itself) is in tests/test_oracle_*.
 """
@@ -37,8 +40,8 @@ def lib():
     """Load liboracle.so, building it first if it is missing or older than its source."""
     global _lib
     if _lib is None:
-        src = os.path.join(_HERE, "oracle.c")
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        srcs = [os.path.join(_HERE, f) for f in ("oracle.c", "oracle_gdn.c")]
+        if not os.path.exists(_LIB_PATH) or any(os.path.getmtime(_LIB_PATH) < os.path.getmtime(f) for f in srcs):
             _build.build()
         L = ctypes.CDLL(_LIB_PATH)
         L.oracle_step.argtypes = [_i] * 5 + [_f64p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f64p]
@@ -78,6 +81,23 @@ def lib():
         L.oracle_replay_read_copy.argtypes = [ctypes.c_void_p, _f64p]
         L.oracle_replay_materialize.argtypes = [ctypes.c_void_p, _f64p]
         L.oracle_threads.restype = _i
+        L.oracle_gdn_step.argtypes = [_i] * 5 + [_f64p] + [_f32p] * 5 + [_f64p]
+        L.oracle_gdn_spec_stepwise.argtypes = [_i] * 6 + [_f64p] + [_f32p] * 5 + [_i32p, _f64p]
+        L.oracle_gdn_spec_stepwise.restype = _i
+        L.oracle_gdn_create.argtypes = [_i] * 7 + [_f32p]
+        L.oracle_gdn_create.restype = ctypes.c_void_p
+        L.oracle_gdn_destroy.argtypes = [ctypes.c_void_p]
+        L.oracle_gdn_replay_step.argtypes = [ctypes.c_void_p] + [_f32p] * 5 + [_f64p]
+        L.oracle_gdn_replay_step.restype = _i
+        L.oracle_gdn_replay_verify.argtypes = [ctypes.c_void_p, _i] + [_f32p] * 5 + [_f64p]
+        L.oracle_gdn_replay_verify.restype = _i
+        L.oracle_gdn_replay_rollback.argtypes = [ctypes.c_void_p, _i32p]
+        L.oracle_gdn_replay_rollback.restype = _i
+        L.oracle_gdn_replay_flush.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_gdn_replay_flush.restype = _i
+        L.oracle_gdn_replay_pointers.argtypes = [ctypes.c_void_p, _i32p, _i32p]
+        L.oracle_gdn_replay_checkpoint.argtypes = [ctypes.c_void_p, _f64p]
+        L.oracle_gdn_replay_materialize.argtypes = [ctypes.c_void_p, _f64p]
         _lib = L
     return _lib
 
@@ -254,3 +274,91 @@ def mxfp4_decode(codes, scales):
     out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), np.float64)
     lib().oracle_decode_mxfp4(codes.reshape(-1), scales.reshape(-1), out.reshape(-1), nb)
     return out
+
+
+# --------------------------------------------------------------------------------------------
+# Gated DeltaNet (oracle_gdn.c). Shapes: H value heads of Dv, G key heads of Dk; q, k [Bt,G,Dk];
+# v [Bt,H,Dv]; alpha, beta [Bt,H]; state [Bt,H,Dv,Dk]; o [Bt,H,Dv].
+# --------------------------------------------------------------------------------------------
+def gdn_step(S, q, k, v, alpha, beta):
+    """O1g for one token. S float64 [Bt,H,Dv,Dk], updated in place. Returns o float64 [Bt,H,Dv]."""
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    Bt, H, Dv, Dk = S.shape
+    G = q.shape[1]
+    o = np.empty((Bt, H, Dv), np.float64)
+    lib().oracle_gdn_step(Bt, H, G, Dv, Dk, S, _f32(q), _f32(k), _f32(v), _f32(alpha), _f32(beta), o)
+    return o
+
+
+def gdn_spec_stepwise(S, T, q, k, v, alpha, beta, accepted):
+    """O5g: all T draft outputs from the committed state S (updated to the accepted prefix).
+    Inputs carry the draft index second: q, k [Bt,T,G,Dk], v [Bt,T,H,Dv], alpha, beta [Bt,T,H]."""
+    Bt, H, Dv, Dk = S.shape
+    G = q.shape[2]
+    o = np.empty((Bt, T, H, Dv), np.float64)
+    acc = np.ascontiguousarray(accepted, dtype=np.int32)
+    rc = lib().oracle_gdn_spec_stepwise(Bt, H, G, Dv, Dk, T, S, _f32(q), _f32(k), _f32(v), _f32(alpha),
+                                        _f32(beta), acc, o)
+    if rc != 0:
+        raise ValueError("accepted count outside [0, T]")
+    return o
+
+
+class GDNReplay:
+    """O3g + O4: the GDN replay form (checkpoint + records, backward sweep) and its pointer machine."""
+
+    def __init__(self, S0, G, L, Tmax=1):
+        S0 = _f32(S0)
+        self.Bt, self.H, self.Dv, self.Dk = S0.shape
+        self.G, self.L, self.Tmax = G, L, Tmax
+        self._h = lib().oracle_gdn_create(self.Bt, self.H, G, self.Dv, self.Dk, L, Tmax, S0)
+        if not self._h:
+            raise ValueError("invalid GDN replay configuration")
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            lib().oracle_gdn_destroy(self._h)
+            self._h = None
+
+    def step(self, q, k, v, alpha, beta):
+        o = np.empty((self.Bt, self.H, self.Dv), np.float64)
+        if lib().oracle_gdn_replay_step(self._h, _f32(q), _f32(k), _f32(v), _f32(alpha), _f32(beta), o) != 0:
+            raise RuntimeError("oracle GDN replay: step rejected by the state machine")
+        return o
+
+    def verify(self, T, q, k, v, alpha, beta):
+        o = np.empty((self.Bt, T, self.H, self.Dv), np.float64)
+        if lib().oracle_gdn_replay_verify(self._h, T, _f32(q), _f32(k), _f32(v), _f32(alpha), _f32(beta), o) != 0:
+            raise RuntimeError("oracle GDN replay: verify rejected by the state machine")
+        return o
+
+    def rollback(self, accepted):
+        acc = np.ascontiguousarray(accepted, dtype=np.int32)
+        if lib().oracle_gdn_replay_rollback(self._h, acc) != 0:
+            raise RuntimeError("oracle GDN replay: rollback rejected by the state machine")
+
+    def flush(self, seq_mask=None):
+        if seq_mask is None:
+            rc = lib().oracle_gdn_replay_flush(self._h, None)
+        else:
+            m = np.ascontiguousarray(seq_mask, dtype=np.int32)
+            rc = lib().oracle_gdn_replay_flush(self._h, m.ctypes.data_as(ctypes.c_void_p))
+        if rc != 0:
+            raise RuntimeError("oracle GDN replay: flush rejected by the state machine")
+
+    def pointers(self):
+        pos = np.empty(self.Bt, np.int32)
+        ck = np.empty(self.Bt, np.int32)
+        lib().oracle_gdn_replay_pointers(self._h, pos, ck)
+        return pos, ck
+
+    def _state(self, fn):
+        out = np.empty((self.Bt, self.H, self.Dv, self.Dk), np.float64)
+        fn(self._h, out)
+        return out
+
+    def checkpoint(self):
+        return self._state(lib().oracle_gdn_replay_checkpoint)
+
+    def materialize(self):
+        return self._state(lib().oracle_gdn_replay_materialize)

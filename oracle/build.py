@@ -7,13 +7,13 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "oracle.c")
+SRCS = [os.path.join(HERE, "oracle.c"), os.path.join(HERE, "oracle_gdn.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-shared", "-fPIC", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+           "-shared", "-fPIC", "-Wall", "-Wextra", "-o", LIB + ".tmp", *SRCS, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

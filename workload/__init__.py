@@ -17,6 +17,7 @@ k do not depend on how many other steps were drawn or in what order.
 import numpy as np
 
 STREAM_PARAMS, STREAM_STATE, STREAM_STEP, STREAM_ACCEPT, STREAM_DRAFT = 0, 1, 2, 3, 4
+STREAM_GDN_PARAMS, STREAM_GDN_STATE, STREAM_GDN_STEP, STREAM_GDN_DRAFT = 10, 11, 12, 14
 
 
 def rng(seed: int, stream: int, index: int = 0) -> np.random.Generator:
@@ -73,6 +74,45 @@ def config_seed(config_index: int) -> int:
     return 1000 * config_index + 7
 
 
+# --------------------------------------------------------------------------------------------
+# Gated DeltaNet layer inputs: H value heads of Dv, G key heads of Dk (value head h reads key head
+# h / (H/G)). q, k ~ N(0, 1) per key head, scaled to unit L2 norm (the layer normalizes them before
+# the recurrence); v ~ N(0, 1); gate alpha = exp(a_h * softplus(z - 4)), z ~ N(0, 1), with per-head
+# rates a_h = -exp(u), u ~ U(0, ln 16) (so alpha in (0, 1), mostly 0.6-0.99); write strength
+# beta = sigmoid(N(0, 1)); S0 ~ N(0, 1). float64 draws rounded once to float32.
+# --------------------------------------------------------------------------------------------
+def gdn_gate_rates(seed: int, H: int):
+    """a_h float64 [H] (negative)."""
+    return -np.exp(rng(seed, STREAM_GDN_PARAMS).uniform(0.0, np.log(16.0), size=H))
+
+
+def gdn_initial_state(seed: int, Bt: int, H: int, Dv: int, Dk: int):
+    return rng(seed, STREAM_GDN_STATE).standard_normal((Bt, H, Dv, Dk), dtype=np.float64).astype(np.float32)
+
+
+def gdn_token_inputs(seed: int, index: int, lead: tuple, H: int, G: int, Dv: int, Dk: int,
+                     stream: int = STREAM_GDN_STEP):
+    """One token's (q [*lead,G,Dk], k [*lead,G,Dk], v [*lead,H,Dv], alpha [*lead,H],
+    beta [*lead,H]) as float32."""
+    g = rng(seed, stream, index)
+    q = g.standard_normal(lead + (G, Dk))
+    k = g.standard_normal(lead + (G, Dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = g.standard_normal(lead + (H, Dv))
+    alpha = np.exp(gdn_gate_rates(seed, H) * softplus(g.standard_normal(lead + (H,)) - 4.0))
+    beta = 1.0 / (1.0 + np.exp(-g.standard_normal(lead + (H,))))
+    return tuple(a.astype(np.float32) for a in (q, k, v, alpha, beta))
+
+
+def gdn_step_inputs(seed: int, step: int, Bt: int, H: int, G: int, Dv: int, Dk: int):
+    return gdn_token_inputs(seed, step, (Bt,), H, G, Dv, Dk, STREAM_GDN_STEP)
+
+
+def gdn_draft_inputs(seed: int, step: int, Bt: int, T: int, H: int, G: int, Dv: int, Dk: int):
+    return gdn_token_inputs(seed, step, (Bt, T), H, G, Dv, Dk, STREAM_GDN_DRAFT)
+
+
 # Named workloads (shapes from the layer definitions): (Bt, H, P, N, G, L, steps)
 TINY = dict(Bt=2, H=4, P=16, N=16, G=1, L=4, steps=64)
 SERVING = dict(Bt=256, H=128, P=64, N=128, G=8, L=16, steps=64)
@@ -80,3 +120,8 @@ DUAL_PRECISION = dict(Bt=256, H=128, P=64, N=128, G=8, L=16, steps=256)
 SPEC = dict(Bt=512, H=128, P=64, N=128, G=8, L=16, T=4, steps=128)
 SWEEP = dict(H=128, P=64, N=128, G=8, batches=(1, 8, 64, 256, 512), Ls=(4, 8, 16, 32),
              layers=10, steps=64)
+# Gated DeltaNet: H value heads of Dv, G key heads of Dk (the pages give no GDN shape; this is a
+# common GDN layer shape: 32 value heads and 16 key heads of 128), 2 MiB fp32 state per sequence.
+GDN_TINY = dict(Bt=2, H=4, G=2, Dv=16, Dk=32, L=4, steps=64)
+GDN_SERVING = dict(Bt=256, H=32, G=16, Dv=128, Dk=128, L=16, steps=64)
+GDN_SPEC = dict(Bt=512, H=32, G=16, Dv=128, Dk=128, L=16, T=4, steps=64)
