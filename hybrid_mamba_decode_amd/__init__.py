@@ -35,6 +35,12 @@ EXPORTED = (
     "replayssm_materialize_state",
     "conventional_step", "snapshot_spec_verify", "snapshot_commit", "replayssm_status_string",
 )
+GDN_EXPORTED = (
+    "gdnreplay_workspace_bytes", "gdnreplay_workspace_layout", "gdnreplay_create", "gdnreplay_destroy",
+    "gdnreplay_load_state", "gdnreplay_step", "gdnreplay_flush", "gdnreplay_spec_verify",
+    "gdnreplay_rollback", "gdnreplay_get_pointers", "gdnreplay_check", "gdnreplay_materialize_state",
+    "gdn_conventional_step", "gdn_snapshot_spec_verify",
+)
 
 
 class Config(ctypes.Structure):
@@ -49,8 +55,19 @@ class Layout(ctypes.Structure):
         "counters", "flag", "total")]
 
 
+class GDNConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "nheads", "nkheads", "dv", "dk", "buffer_len", "max_draft")]
+
+
+class GDNLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "master", "ring_k", "ring_v", "ring_a", "ring_b", "pos", "ckpt_pos", "counters", "flag", "total")]
+
+
 _vp = ctypes.c_void_p
 _cfgp = ctypes.POINTER(Config)
+_gcfgp = ctypes.POINTER(GDNConfig)
 _i32 = ctypes.c_int32
 _sig = {
     "replayssm_workspace_bytes": (ctypes.c_size_t, [_cfgp]),
@@ -70,6 +87,20 @@ _sig = {
     "snapshot_spec_verify": (ctypes.c_int, [_cfgp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "snapshot_commit": (ctypes.c_int, [_cfgp, _vp, _vp, _i32, _vp]),
     "replayssm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "gdnreplay_workspace_bytes": (ctypes.c_size_t, [_gcfgp]),
+    "gdnreplay_workspace_layout": (ctypes.c_int, [_gcfgp, ctypes.POINTER(GDNLayout)]),
+    "gdnreplay_create": (ctypes.c_int, [_gcfgp, _vp, ctypes.c_size_t, ctypes.POINTER(_vp)]),
+    "gdnreplay_destroy": (ctypes.c_int, [_vp]),
+    "gdnreplay_load_state": (ctypes.c_int, [_vp, _vp, _vp]),
+    "gdnreplay_step": (ctypes.c_int, [_vp] + [_vp] * 6 + [_vp]),
+    "gdnreplay_flush": (ctypes.c_int, [_vp, _vp, _vp]),
+    "gdnreplay_spec_verify": (ctypes.c_int, [_vp, _i32] + [_vp] * 6 + [_vp]),
+    "gdnreplay_rollback": (ctypes.c_int, [_vp, _vp, _vp]),
+    "gdnreplay_get_pointers": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
+    "gdnreplay_check": (ctypes.c_int, [_vp, _vp]),
+    "gdnreplay_materialize_state": (ctypes.c_int, [_vp, _vp, _vp]),
+    "gdn_conventional_step": (ctypes.c_int, [_gcfgp, _vp] + [_vp] * 6 + [_vp]),
+    "gdn_snapshot_spec_verify": (ctypes.c_int, [_gcfgp, _vp, _vp, _i32] + [_vp] * 6 + [_vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -349,3 +380,169 @@ class ReplaySSM:
     def pointer_arrays(self):
         return (self.region("pos", torch.int32, (self.batch,)),
                 self.region("ckpt_pos", torch.int32, (self.batch,)))
+
+
+# ---- Gated DeltaNet layers (gdnreplay.h) ------------------------------------------------------
+
+def make_gdn_config(batch, nheads, nkheads, dv, dk, buffer_len=16, max_draft=1):
+    return GDNConfig(batch, nheads, nkheads, dv, dk, buffer_len, max_draft)
+
+
+def gdnreplay_workspace_bytes(cfg: GDNConfig) -> int:
+    return int(_lib.gdnreplay_workspace_bytes(ctypes.byref(cfg)))
+
+
+def gdnreplay_workspace_layout(cfg: GDNConfig) -> GDNLayout:
+    lay = GDNLayout()
+    _check(_lib.gdnreplay_workspace_layout(ctypes.byref(cfg), ctypes.byref(lay)), "gdnreplay_workspace_layout")
+    return lay
+
+
+def gdnreplay_create(cfg: GDNConfig, workspace: torch.Tensor):
+    h = _vp()
+    _check(_lib.gdnreplay_create(ctypes.byref(cfg), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                 ctypes.byref(h)), "gdnreplay_create")
+    return h
+
+
+def gdnreplay_destroy(h):
+    _check(_lib.gdnreplay_destroy(h), "gdnreplay_destroy")
+
+
+def gdnreplay_load_state(h, state, stream=None):
+    _check(_lib.gdnreplay_load_state(h, _ptr(state, name="state"), _stream(stream)), "gdnreplay_load_state")
+
+
+def _gio(q, k, v, alpha, beta, o):
+    return (_ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _ptr(alpha, name="alpha"),
+            _ptr(beta, name="beta"), _ptr(o, name="o"))
+
+
+def gdnreplay_step(h, q, k, v, alpha, beta, o, stream=None):
+    _check(_lib.gdnreplay_step(h, *_gio(q, k, v, alpha, beta, o), _stream(stream)), "gdnreplay_step")
+
+
+def gdnreplay_flush(h, seq_mask=None, stream=None):
+    _check(_lib.gdnreplay_flush(h, _ptr(seq_mask, torch.int32, "seq_mask"), _stream(stream)), "gdnreplay_flush")
+
+
+def gdnreplay_spec_verify(h, T, q, k, v, alpha, beta, o, stream=None):
+    _check(_lib.gdnreplay_spec_verify(h, int(T), *_gio(q, k, v, alpha, beta, o), _stream(stream)),
+           "gdnreplay_spec_verify")
+
+
+def gdnreplay_rollback(h, accepted, stream=None):
+    _check(_lib.gdnreplay_rollback(h, _ptr(accepted, torch.int32, "accepted"), _stream(stream)), "gdnreplay_rollback")
+
+
+def gdnreplay_get_pointers(h, batch, stream=None):
+    pos = (ctypes.c_int32 * max(batch, 1))()
+    ck = (ctypes.c_int32 * max(batch, 1))()
+    _check(_lib.gdnreplay_get_pointers(h, ctypes.cast(pos, _vp), ctypes.cast(ck, _vp), _stream(stream)),
+           "gdnreplay_get_pointers")
+    return list(pos)[:batch], list(ck)[:batch]
+
+
+def gdnreplay_check(h, stream=None):
+    return int(_lib.gdnreplay_check(h, _stream(stream)))
+
+
+def gdnreplay_materialize_state(h, out, stream=None):
+    _check(_lib.gdnreplay_materialize_state(h, _ptr(out, name="out"), _stream(stream)), "gdnreplay_materialize_state")
+
+
+def _check_gdn_tokens(cfg, q, k, v, alpha, beta, o, lead=()):
+    Bt, H, G, Dv, Dk = cfg.batch, cfg.nheads, cfg.nkheads, cfg.dv, cfg.dk
+    _expect(q, (Bt, *lead, G, Dk), "q")
+    _expect(k, (Bt, *lead, G, Dk), "k")
+    _expect(v, (Bt, *lead, H, Dv), "v")
+    _expect(alpha, (Bt, *lead, H), "alpha")
+    _expect(beta, (Bt, *lead, H), "beta")
+    _expect(o, (Bt, *lead, H, Dv), "o")
+
+
+def gdn_conventional_step(cfg: GDNConfig, state, q, k, v, alpha, beta, o, stream=None):
+    _check_gdn_tokens(cfg, q, k, v, alpha, beta, o)
+    _expect(state, (cfg.batch, cfg.nheads, cfg.dv, cfg.dk), "state")
+    _check(_lib.gdn_conventional_step(ctypes.byref(cfg), _ptr(state, name="state"), *_gio(q, k, v, alpha, beta, o),
+                                      _stream(stream)), "gdn_conventional_step")
+
+
+def gdn_snapshot_spec_verify(cfg: GDNConfig, slots, cur, T, q, k, v, alpha, beta, o, stream=None):
+    _check_gdn_tokens(cfg, q, k, v, alpha, beta, o, (T,))
+    _expect(slots, (cfg.batch, T + 1, cfg.nheads, cfg.dv, cfg.dk), "slots")
+    _expect(cur, (cfg.batch,), "cur")
+    _check(_lib.gdn_snapshot_spec_verify(ctypes.byref(cfg), _ptr(slots, name="slots"), _ptr(cur, torch.int32, "cur"),
+                                         int(T), *_gio(q, k, v, alpha, beta, o), _stream(stream)),
+           "gdn_snapshot_spec_verify")
+
+
+class GDNReplay:
+    """One Gated DeltaNet layer's decode state kept as checkpoint + record ring, on one GPU."""
+
+    def __init__(self, batch, nheads, nkheads, dv, dk, buffer_len=16, max_draft=1, device="cuda"):
+        self.cfg = make_gdn_config(batch, nheads, nkheads, dv, dk, buffer_len, max_draft)
+        nbytes = gdnreplay_workspace_bytes(self.cfg)
+        if nbytes == 0:
+            raise ReplaySSMError(RSSM_E_INVAL, "gdnreplay_workspace_bytes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if self.workspace.data_ptr() % 256:
+            raise RuntimeError("workspace allocation is not 256-byte aligned")
+        self.layout = gdnreplay_workspace_layout(self.cfg)
+        self.handle = gdnreplay_create(self.cfg, self.workspace)
+        self.batch, self.nheads, self.nkheads, self.dv, self.dk = batch, nheads, nkheads, dv, dk
+        self.buffer_len, self.max_draft = buffer_len, max_draft
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            _lib.gdnreplay_destroy(h)
+            self.handle = None
+
+    def load_state(self, state, stream=None):
+        _expect(state, (self.batch, self.nheads, self.dv, self.dk), "state")
+        gdnreplay_load_state(self.handle, state, stream)
+
+    def step(self, q, k, v, alpha, beta, o=None, stream=None):
+        if o is None:
+            o = torch.empty_like(v)
+        _check_gdn_tokens(self.cfg, q, k, v, alpha, beta, o)
+        gdnreplay_step(self.handle, q, k, v, alpha, beta, o, stream)
+        return o
+
+    def flush(self, seq_mask=None, stream=None):
+        gdnreplay_flush(self.handle, seq_mask, stream)
+
+    def spec_verify(self, q, k, v, alpha, beta, o=None, stream=None):
+        T = q.shape[1]
+        if o is None:
+            o = torch.empty_like(v)
+        _check_gdn_tokens(self.cfg, q, k, v, alpha, beta, o, (T,))
+        gdnreplay_spec_verify(self.handle, T, q, k, v, alpha, beta, o, stream)
+        return o
+
+    def rollback(self, accepted, stream=None):
+        _expect(accepted, (self.batch,), "accepted")
+        gdnreplay_rollback(self.handle, accepted, stream)
+
+    def get_pointers(self, stream=None):
+        return gdnreplay_get_pointers(self.handle, self.batch, stream)
+
+    def check(self, stream=None):
+        return gdnreplay_check(self.handle, stream)
+
+    def materialize_state(self, out=None, stream=None):
+        if out is None:
+            out = torch.empty(self.batch, self.nheads, self.dv, self.dk, device=self.workspace.device)
+        gdnreplay_materialize_state(self.handle, out, stream)
+        return out
+
+    def master(self):
+        off = self.layout.master
+        n = self.batch * self.nheads * self.dv * self.dk
+        return self.workspace[off:off + 4 * n].view(torch.float32).view(self.batch, self.nheads, self.dv, self.dk)
+
+    def pointer_arrays(self):
+        def region(off, n):
+            return self.workspace[off:off + 4 * n].view(torch.int32)
+        return region(self.layout.pos, self.batch), region(self.layout.ckpt_pos, self.batch)

@@ -1,7 +1,8 @@
 """Build libreplayssm.so (HIP, gfx950) in-tree.
 
-kernels.hip is compiled once per supported state size N (in parallel), api.hip once, and the
-objects are linked into hybrid_mamba_decode_amd/libreplayssm.so. Objects go to _build/.
+kernels.hip (Mamba-2) and gdn_kernels.hip (Gated DeltaNet) are compiled once per supported state
+/ key size N (in parallel), api.hip and gdn_api.hip once, and the objects are linked into
+hybrid_mamba_decode_amd/libreplayssm.so. Objects go to _build/.
 """
 import os
 import subprocess
@@ -37,14 +38,19 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     os.makedirs(OBJ, exist_ok=True)
     jobs = jobs or min(8, (os.cpu_count() or 4))
     steps = []
-    for n in STATE_SIZES:
-        steps.append([HIPCC, *FLAGS, f"-DRSSM_N={n}", "-c", os.path.join(CSRC, "kernels.hip"),
-                      "-o", os.path.join(OBJ, f"kernels_n{n}.o")])
-    steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "api.hip"), "-o", os.path.join(OBJ, "api.o")])
+    objs = []
+    for src in ("kernels", "gdn_kernels"):
+        for n in STATE_SIZES:
+            obj = os.path.join(OBJ, f"{src}_n{n}.o")
+            steps.append([HIPCC, *FLAGS, f"-DRSSM_N={n}", "-c", os.path.join(CSRC, f"{src}.hip"), "-o", obj])
+            objs.append(obj)
+    for src in ("api", "gdn_api"):
+        obj = os.path.join(OBJ, f"{src}.o")
+        steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, f"{src}.hip"), "-o", obj])
+        objs.append(obj)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         for f in [ex.submit(_run, s, verbose) for s in steps]:
             f.result()
-    objs = [os.path.join(OBJ, f"kernels_n{n}.o") for n in STATE_SIZES] + [os.path.join(OBJ, "api.o")]
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB

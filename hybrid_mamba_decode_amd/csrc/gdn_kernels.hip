@@ -1,0 +1,656 @@
+// gdn_kernels.hip -- ReplaySSM decode-step kernels for Gated DeltaNet layers on gfx950, for one
+// key size Dk (compiled once per supported Dk with -DRSSM_N=<Dk>).
+//
+// Layer (per value head h, key head g = h / (H/G); the published Gated DeltaNet recurrence, the
+// plain reading of the pages' second layer type, [AT Pulse] "Capabilities and access"):
+//     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t
+// with S [Dv, Dk] per (sequence, value head), row p = value index. Replay form ([AT Pulse]
+// "Technical analysis": output from a checkpoint plus the window's records): a backward sweep
+// over the window's records j = t..c gives z and c_j,
+//     z <- q_t;  c_j = beta_j (k_j . z);  z <- alpha_j (z - c_j k_j);   o_t = S_c z + sum_j c_j v_j
+// and a flush applies the records to the checkpoint in order.
+//
+// Tiling as for the Mamba-2 kernels (device.h): one 256-thread work-group per <= 64 rows of one
+// (sequence, value head) tile, lanes along Dk, 16-byte non-temporal loads, transpose-reduce for
+// row dots, XCD-aware tile order.
+//
+// Kernels:
+//   gdn_step_kernel       replay + append; the flush-capable variant folds the sequences whose
+//                         buffer fills and reads their output from the folded state
+//   gdn_flush_kernel      explicit flush, rollback commit, or materialize
+//   gdn_verify_kernel     output-only evaluation of T draft tokens + tentative append
+//   gdn_load_kernel       master <- state, pointers reset
+//   gdn_conventional_kernel   read-update-write baseline
+//   gdn_snapshot_kernel   per-draft snapshot baseline (one read, T writes)
+#include "device.h"
+#include "gdn_launch.h"
+
+#ifndef RSSM_N
+#error "compile with -DRSSM_N=<Dk>"
+#endif
+
+namespace rssm {
+namespace {
+
+constexpr int NN = RSSM_N;
+using GF = Geo<NN, PREC_F32>;
+constexpr int ZPL = NN >= 64 ? NN / 64 : 1;  // sweep vector elements per lane (n = lane + 64 e)
+
+// State row held by load slot i of a lane (f32 geometry).
+__device__ inline int row_of_f32(int i, int wave, int lane) { return i * GF::RPB + wave * GF::RPI + lane / GF::LPR; }
+
+__device__ inline Tile gmap_tile(const GLayer &Ld)
+{
+    const unsigned nblk = gridDim.x, i = blockIdx.x;
+    const unsigned id = (nblk % 8u == 0u) ? (i % 8u) * (nblk / 8u) + i / 8u : i;
+    Tile t;
+    t.split = (int)(id % (unsigned)Ld.psplit);
+    const unsigned bh = id / (unsigned)Ld.psplit;
+    t.h = (int)(bh % (unsigned)Ld.H);
+    t.b = (int)(bh / (unsigned)Ld.H);
+    t.g = t.h / Ld.hpg;
+    t.row0 = t.split * kRows;
+    t.nrows = min(kRows, Ld.Dv - t.row0);
+    return t;
+}
+
+__device__ inline void graise(const GLayer &Ld, unsigned bits)
+{
+    if (threadIdx.x == 0) __hip_atomic_fetch_or(Ld.flag, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Per-sequence completion (as seq_done in device.h): the last work-group of sequence b to finish
+// writes the new pointers and re-arms the counter.
+__device__ inline void gseq_done(const GLayer &Ld, int b, int new_pos, int new_ckpt)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned expected = (unsigned)(Ld.H * Ld.psplit);
+        const unsigned prev = __hip_atomic_fetch_add(&Ld.counter[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev + 1u == expected) {
+            Ld.pos[b] = new_pos;
+            Ld.ckpt[b] = new_ckpt;
+            __hip_atomic_store(&Ld.counter[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <int LMAX>
+struct GWin {
+    float K[LMAX][NN] __attribute__((aligned(16)));     // k_j of the key head
+    float V[LMAX][kRows] __attribute__((aligned(16)));  // v_j, this work-group's rows
+    float a[LMAX], b[LMAX];                             // alpha_j, beta_j of the value head
+};
+
+// Stage records 0..k-1 of the window in LDS: record j < nring from ring slot (ck + j) mod L, the
+// rest from the call's fresh inputs (fresh record f at fk + f*sk, fv + f*sv, fa/fb + f*ss).
+template <int LMAX>
+__device__ inline void stage_window(GWin<LMAX> &w, const GLayer &Ld, const Tile &t, int ck, int nring, int k,
+                                    const float *fk, int sk, const float *fv, int sv, const float *fa,
+                                    const float *fb, int ss)
+{
+    const int tid = threadIdx.x;
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    const float *rk = Ld.ring_k + ((size_t)t.b * Ld.G + t.g) * Ld.L * NN;
+    const float *rv = Ld.ring_v + bh * Ld.L * Ld.Dv + t.row0;
+    auto slot = [&](int j) { return (int)((unsigned)(ck + j) % (unsigned)Ld.L); };
+    for (int e = tid; e < k * (NN / 4); e += kThreads) {
+        const int j = e / (NN / 4), c4 = e % (NN / 4);
+        const float *src = j < nring ? rk + (size_t)slot(j) * NN : fk + (size_t)(j - nring) * sk;
+        *(f32x4 *)&w.K[j][4 * c4] = *(const f32x4 *)(src + 4 * c4);
+    }
+    for (int e = tid; e < k * kRows; e += kThreads) {
+        const int j = e / kRows, p = e % kRows;
+        float val = 0.f;
+        if (p < t.nrows) val = j < nring ? rv[(size_t)slot(j) * Ld.Dv + p] : fv[(size_t)(j - nring) * sv + p];
+        w.V[j][p] = val;
+    }
+    if (tid < k) {
+        const int j = tid;
+        w.a[j] = j < nring ? Ld.ring_a[bh * Ld.L + slot(j)] : fa[(size_t)(j - nring) * ss];
+        w.b[j] = j < nring ? Ld.ring_b[bh * Ld.L + slot(j)] : fb[(size_t)(j - nring) * ss];
+    }
+}
+
+// Backward sweep of one query over records last..0 in the calling wave: z <- q; c_j = beta_j
+// (k_j . z); z <- alpha_j (z - c_j k_j). Writes c_j to c[j] and the final z to z_out (lane 0 and
+// lanes holding z elements; wave-wide shuffles, so the whole wave must call it).
+template <int LMAX>
+__device__ inline void gdn_sweep(const GWin<LMAX> &w, const float *q, int last, float *c, float *z_out, int lane)
+{
+    float z[ZPL];
+#pragma unroll
+    for (int e = 0; e < ZPL; ++e) {
+        const int n = lane + 64 * e;
+        z[e] = n < NN ? q[n] : 0.f;
+    }
+    for (int j = last; j >= 0; --j) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < ZPL; ++e) {
+            const int n = lane + 64 * e;
+            if (n < NN) part = fmaf(z[e], w.K[j][n], part);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+        const float cj = w.b[j] * part;
+        const float aj = w.a[j];
+#pragma unroll
+        for (int e = 0; e < ZPL; ++e) {
+            const int n = lane + 64 * e;
+            if (n < NN) z[e] = aj * (z[e] - cj * w.K[j][n]);
+        }
+        if (lane == 0) c[j] = cj;
+    }
+#pragma unroll
+    for (int e = 0; e < ZPL; ++e) {
+        const int n = lane + 64 * e;
+        if (n < NN) z_out[n] = z[e];
+    }
+}
+
+// Sum of a value over the LPR consecutive lanes of a row (all of them receive it).
+__device__ inline float row_allreduce(float v)
+{
+#pragma unroll
+    for (int o = GF::LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Apply records 0..k-1 to fp32 rows held in f32 geometry (vf), in order:
+// S_row <- alpha_j (S_row - beta_j (S_row . k_j) k_j) + beta_j v_j[row] k_j.
+template <int LMAX>
+__device__ inline void gdn_fold_rows(f32x4 (&vf)[GF::NL], const GWin<LMAX> &w, int k, int wave, int lane)
+{
+    const int c = lane % GF::LPR;
+    int row[GF::NL];
+#pragma unroll
+    for (int i = 0; i < GF::NL; ++i) {
+        const int r = row_of_f32(i, wave, lane);
+        row[i] = r < kRows ? r : 0;
+    }
+    for (int j = 0; j < k; ++j) {
+        const f32x4 kj = *(const f32x4 *)&w.K[j][4 * c];
+        const float aj = w.a[j], bj = w.b[j];
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            float part = vf[i].x * kj.x;
+            part = fmaf(vf[i].y, kj.y, part);
+            part = fmaf(vf[i].z, kj.z, part);
+            part = fmaf(vf[i].w, kj.w, part);
+            const float sk = row_allreduce(part);
+            // alpha (S - beta sk k) + beta v k = alpha S + (beta v - alpha beta sk) k
+            const float coef = bj * (w.V[j][row[i]] - aj * sk);
+            vf[i].x = fmaf(coef, kj.x, aj * vf[i].x);
+            vf[i].y = fmaf(coef, kj.y, aj * vf[i].y);
+            vf[i].z = fmaf(coef, kj.z, aj * vf[i].z);
+            vf[i].w = fmaf(coef, kj.w, aj * vf[i].w);
+        }
+    }
+}
+
+__device__ inline void store_rows(float *rows, const f32x4 (&vf)[GF::NL], int nrows, int wave, int lane)
+{
+    const int c = lane % GF::LPR;
+#pragma unroll
+    for (int i = 0; i < GF::NL; ++i) {
+        const int r = row_of_f32(i, wave, lane);
+        if (r < nrows) store_nt(rows + (size_t)r * NN + 4 * c, as_u32x4(vf[i]));
+    }
+}
+
+__device__ inline void load_rows_f32(f32x4 (&vf)[GF::NL], const float *rows, int nrows, int wave, int lane)
+{
+    const int c = lane % GF::LPR;
+#pragma unroll
+    for (int i = 0; i < GF::NL; ++i) {
+        const int r = row_of_f32(i, wave, lane);
+        vf[i] = r < nrows ? as_f32x4(load_nt(rows + (size_t)r * NN + 4 * c)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// Row dots of the tile with M vectors (vectors[m] in LDS, NN floats each), reduced into
+// u[m * kRows + row].
+template <int M>
+__device__ inline void rows_dot(const f32x4 (&vf)[GF::NL], const float *vectors, int nvec, float *u, int wave,
+                                int lane)
+{
+    const int c = lane % GF::LPR;
+    float part[GF::NL * M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const f32x4 z = m < nvec ? *(const f32x4 *)(vectors + (size_t)m * NN + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            float s = vf[i].x * z.x;
+            s = fmaf(vf[i].y, z.y, s);
+            s = fmaf(vf[i].z, z.z, s);
+            part[m * GF::NL + i] = fmaf(vf[i].w, z.w, s);
+        }
+    }
+    transpose_reduce<GF::NL * M, GF::LPR>(part, lane);
+    bool writer;
+    const int first = tr_first<GF::NL * M, GF::LPR>(lane, &writer);
+    constexpr int cnt = tr_count<GF::NL * M, GF::LPR>();
+    if (writer) {
+#pragma unroll
+        for (int e = 0; e < cnt; ++e) {
+            const int idx = first + e, m = idx / GF::NL, i = idx % GF::NL;
+            const int r = row_of_f32(i, wave, lane);
+            if (m < nvec && r < kRows) u[m * kRows + r] = part[e];
+        }
+    }
+}
+
+// ==========================================================================================
+// Standard decode step. FLUSH = the launch may meet sequences whose buffer fills ([WittyWires]
+// "What happened": the checkpoint is updated when the buffer fills); those apply all records to
+// the fp32 master and read o from the folded state (no record is stored for that token).
+// ==========================================================================================
+template <int LMAX>
+struct GStepLds {
+    GWin<LMAX> w;
+    float q[NN] __attribute__((aligned(16)));
+    float z[NN] __attribute__((aligned(16)));
+    float c[LMAX];
+    float u[kRows];
+};
+
+template <int LMAX, bool FLUSH>
+__global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO io)
+{
+    __shared__ GStepLds<LMAX> s;
+    const Tile t = gmap_tile(Ld);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    float *rows = Ld.master + (bh * Ld.Dv + t.row0) * NN;
+
+    f32x4 vf[GF::NL];
+    load_rows_f32(vf, rows, t.nrows, wave, lane);  // the checkpoint stream first
+
+    const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
+    const int c0 = pos - ck;
+    if (!(ck >= 0 && c0 >= 0 && c0 <= Ld.L - Ld.Tmax) || (!FLUSH && c0 + 1 > Ld.L - Ld.Tmax)) {
+        graise(Ld, FLAG_POINTERS);
+        gseq_done(Ld, t.b, pos, ck);
+        return;
+    }
+    const int k = c0 + 1;  // records in the window, this token included
+    const size_t bg = (size_t)t.b * Ld.G + t.g;
+    stage_window<LMAX>(s.w, Ld, t, ck, c0, k, io.k + bg * NN, 0, io.v + bh * Ld.Dv + t.row0, 0, io.alpha + bh,
+                       io.beta + bh, 0);
+    if (tid < NN / 4) *(f32x4 *)&s.q[4 * tid] = *(const f32x4 *)(io.q + bg * NN + 4 * tid);
+    __syncthreads();
+    const bool flush = k > Ld.L - Ld.Tmax;
+    const int pslot = (int)((unsigned)pos % (unsigned)Ld.L);
+
+    if (FLUSH && flush) {
+        gdn_fold_rows<LMAX>(vf, s.w, k, wave, lane);
+        store_rows(rows, vf, t.nrows, wave, lane);
+        rows_dot<1>(vf, s.q, 1, s.u, wave, lane);
+        __syncthreads();
+        if (tid < t.nrows) io.o[bh * Ld.Dv + t.row0 + tid] = s.u[tid];
+        gseq_done(Ld, t.b, pos + 1, pos + 1);
+        return;
+    }
+
+    if (wave == 0) gdn_sweep<LMAX>(s.w, s.q, k - 1, s.c, s.z, lane);
+    __syncthreads();
+    rows_dot<1>(vf, s.z, 1, s.u, wave, lane);
+    __syncthreads();
+    if (tid < t.nrows) {
+        float acc = s.u[tid];
+        for (int j = 0; j < k; ++j) acc = fmaf(s.c[j], s.w.V[j][tid], acc);
+        io.o[bh * Ld.Dv + t.row0 + tid] = acc;
+        Ld.ring_v[(bh * Ld.L + pslot) * Ld.Dv + t.row0 + tid] = s.w.V[k - 1][tid];
+    }
+    if (t.split == 0 && tid == 0) {
+        Ld.ring_a[bh * Ld.L + pslot] = s.w.a[k - 1];
+        Ld.ring_b[bh * Ld.L + pslot] = s.w.b[k - 1];
+    }
+    if (t.split == 0 && t.h % Ld.hpg == 0 && tid < NN / 4)
+        *(f32x4 *)(Ld.ring_k + (bg * Ld.L + pslot) * NN + 4 * tid) = *(const f32x4 *)&s.w.K[k - 1][4 * tid];
+    gseq_done(Ld, t.b, pos + 1, ck);
+}
+
+// ==========================================================================================
+// Flush / rollback commit / materialize (modes as for the Mamba-2 flush, launch.h).
+// ==========================================================================================
+template <int LMAX>
+__global__ void __launch_bounds__(kThreads) gdn_flush_kernel(GLayer Ld, int mode, const int *arg, float *out)
+{
+    __shared__ GWin<LMAX> w;
+    const Tile t = gmap_tile(Ld);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    const size_t elem0 = (bh * Ld.Dv + t.row0) * NN;
+    const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
+    const int count = pos - ck;
+    const int cap = mode == MODE_OVERFULL ? Ld.L : Ld.L - Ld.Tmax;
+    if (!(ck >= 0 && count >= 0 && count <= cap)) {
+        graise(Ld, FLAG_POINTERS);
+        return;
+    }
+    bool fold;
+    if (mode == MODE_OVERFULL) fold = count > Ld.L - Ld.Tmax;
+    else if (mode == MODE_MASK) fold = (arg == nullptr || arg[t.b] != 0) && count > 0;
+    else fold = true;
+    if (!fold) return;
+    f32x4 vf[GF::NL];
+    load_rows_f32(vf, Ld.master + elem0, t.nrows, wave, lane);
+    // every record comes from the ring (nring = count); the fresh-input pointers are never read
+    stage_window<LMAX>(w, Ld, t, ck, count, count, Ld.ring_k, 0, Ld.ring_v, 0, Ld.ring_a, Ld.ring_b, 0);
+    __syncthreads();
+    gdn_fold_rows<LMAX>(vf, w, count, wave, lane);
+    if (mode == MODE_MATERIALIZE) {
+        store_rows(out + elem0, vf, t.nrows, wave, lane);
+    } else {
+        store_rows(Ld.master + elem0, vf, t.nrows, wave, lane);
+        gseq_done(Ld, t.b, pos, pos);
+    }
+}
+
+__global__ void gdn_advance_kernel(GLayer Ld, const int *accepted, int T)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= Ld.Bt) return;
+    const int pos = Ld.pos[b], ck = Ld.ckpt[b];
+    if (!(ck >= 0 && pos - ck >= 0 && pos - ck <= Ld.L - Ld.Tmax)) {
+        __hip_atomic_fetch_or(Ld.flag, FLAG_POINTERS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const int a = accepted[b];
+    if (a < 0 || a > T) {
+        __hip_atomic_fetch_or(Ld.flag, FLAG_ACCEPTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    Ld.pos[b] = pos + a;
+}
+
+// ==========================================================================================
+// Speculative verify ([AT Pulse] "Technical analysis": output-only evaluation). Query q's window
+// is the committed records plus drafts 0..q; its sweep runs in wave q mod 4. One pass over the
+// checkpoint rows serves all T queries: U = S_c [z_1 .. z_T]. Drafts are appended tentatively at
+// slots (pos + q) mod L; no pointer moves.
+// ==========================================================================================
+template <int LMAX, int TQ>
+struct GVerifyLds {
+    GWin<LMAX> w;
+    float q[TQ][NN] __attribute__((aligned(16)));
+    float z[TQ][NN] __attribute__((aligned(16)));
+    float c[TQ][LMAX];
+    float u[TQ][kRows];
+};
+
+template <int LMAX, int TQ>
+__global__ void __launch_bounds__(kThreads) gdn_verify_kernel(GLayer Ld, GTokenIO io, int T)
+{
+    __shared__ GVerifyLds<LMAX, TQ> s;
+    const Tile t = gmap_tile(Ld);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    f32x4 vf[GF::NL];
+    load_rows_f32(vf, Ld.master + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
+    const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
+    const int count0 = pos - ck;
+    if (!(ck >= 0 && count0 >= 0 && count0 <= Ld.L - Ld.Tmax && count0 + T <= Ld.L)) {
+        graise(Ld, FLAG_POINTERS);
+        return;
+    }
+    const int kw = count0 + T;
+    const size_t bT = (size_t)t.b * T;
+    stage_window<LMAX>(s.w, Ld, t, ck, count0, kw, io.k + (bT * Ld.G + t.g) * NN, Ld.G * NN,
+                       io.v + (bT * Ld.H + t.h) * Ld.Dv + t.row0, Ld.H * Ld.Dv, io.alpha + bT * Ld.H + t.h,
+                       io.beta + bT * Ld.H + t.h, Ld.H);
+    for (int e = tid; e < T * (NN / 4); e += kThreads) {
+        const int q = e / (NN / 4), c4 = e % (NN / 4);
+        *(f32x4 *)&s.q[q][4 * c4] = *(const f32x4 *)(io.q + ((bT + q) * Ld.G + t.g) * NN + 4 * c4);
+    }
+    __syncthreads();
+    for (int q = wave; q < T; q += kWaves) gdn_sweep<LMAX>(s.w, s.q[q], count0 + q, s.c[q], s.z[q], lane);
+    __syncthreads();
+    rows_dot<TQ>(vf, &s.z[0][0], T, &s.u[0][0], wave, lane);
+    __syncthreads();
+    for (int q = wave; q < T; q += kWaves) {
+        if (lane < t.nrows) {
+            const int last = count0 + q;
+            float acc = s.u[q][lane];
+            for (int j = 0; j <= last; ++j) acc = fmaf(s.c[q][j], s.w.V[j][lane], acc);
+            io.o[((bT + q) * Ld.H + t.h) * Ld.Dv + t.row0 + lane] = acc;
+            const int slot = (int)((unsigned)(pos + q) % (unsigned)Ld.L);
+            Ld.ring_v[(bh * Ld.L + slot) * Ld.Dv + t.row0 + lane] = s.w.V[last][lane];
+        }
+        if (t.split == 0 && lane == 0) {
+            const int slot = (int)((unsigned)(pos + q) % (unsigned)Ld.L);
+            Ld.ring_a[bh * Ld.L + slot] = s.w.a[count0 + q];
+            Ld.ring_b[bh * Ld.L + slot] = s.w.b[count0 + q];
+        }
+    }
+    if (t.split == 0 && t.h % Ld.hpg == 0) {
+        for (int e = tid; e < T * (NN / 4); e += kThreads) {
+            const int q = e / (NN / 4), c4 = e % (NN / 4);
+            const int slot = (int)((unsigned)(pos + q) % (unsigned)Ld.L);
+            *(f32x4 *)(Ld.ring_k + (((size_t)t.b * Ld.G + t.g) * Ld.L + slot) * NN + 4 * c4) =
+                *(const f32x4 *)&s.w.K[count0 + q][4 * c4];
+        }
+    }
+}
+
+// ==========================================================================================
+// Load: master <- state; pointers, counters and the flag reset.
+// ==========================================================================================
+__global__ void __launch_bounds__(kThreads) gdn_load_kernel(GLayer Ld, const float *state)
+{
+    const Tile t = gmap_tile(Ld);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const size_t elem0 = (((size_t)t.b * Ld.H + t.h) * Ld.Dv + t.row0) * NN;
+    f32x4 vf[GF::NL];
+    load_rows_f32(vf, state + elem0, t.nrows, wave, lane);
+    store_rows(Ld.master + elem0, vf, t.nrows, wave, lane);
+    if (t.h == 0 && t.split == 0 && threadIdx.x == 0) {
+        Ld.pos[t.b] = 0;
+        Ld.ckpt[t.b] = 0;
+        Ld.counter[t.b] = 0u;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *Ld.flag = 0u;
+}
+
+// ==========================================================================================
+// Baseline: conventional GDN decode step in place ([Clarity] "Why it matters", claim ledger [6]:
+// read the state, update it, read the output, write it back).
+// ==========================================================================================
+__global__ void __launch_bounds__(kThreads) gdn_conventional_kernel(GLayer Ld, float *state, GTokenIO io)
+{
+    __shared__ GWin<1> w;
+    __shared__ float q[NN] __attribute__((aligned(16)));
+    __shared__ float u[kRows];
+    const Tile t = gmap_tile(Ld);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t bh = (size_t)t.b * Ld.H + t.h, bg = (size_t)t.b * Ld.G + t.g;
+    float *rows = state + (bh * Ld.Dv + t.row0) * NN;
+    f32x4 vf[GF::NL];
+    load_rows_f32(vf, rows, t.nrows, wave, lane);
+    stage_window<1>(w, Ld, t, 0, 0, 1, io.k + bg * NN, 0, io.v + bh * Ld.Dv + t.row0, 0, io.alpha + bh, io.beta + bh, 0);
+    if (tid < NN / 4) *(f32x4 *)&q[4 * tid] = *(const f32x4 *)(io.q + bg * NN + 4 * tid);
+    __syncthreads();
+    gdn_fold_rows<1>(vf, w, 1, wave, lane);
+    store_rows(rows, vf, t.nrows, wave, lane);
+    rows_dot<1>(vf, q, 1, u, wave, lane);
+    __syncthreads();
+    if (tid < t.nrows) io.o[bh * Ld.Dv + t.row0 + tid] = u[tid];
+}
+
+// ==========================================================================================
+// Baseline: per-draft snapshots ([Clarity] "What happened", claim ledger [13]): read the
+// committed slot once, run the T drafts stepwise, write the state after draft q to slot
+// (cur + q + 1) mod (T + 1). One read and T writes of the state per verify.
+// ==========================================================================================
+template <int TQ>
+__global__ void __launch_bounds__(kThreads) gdn_snapshot_kernel(GLayer Ld, float *slots, const int *cur, int T,
+                                                                 GTokenIO io)
+{
+    __shared__ GWin<TQ> w;
+    __shared__ float q[TQ][NN] __attribute__((aligned(16)));
+    __shared__ float u[TQ][kRows];
+    const Tile t = gmap_tile(Ld);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c0 = cur[t.b];
+    if (c0 < 0 || c0 > T) return;
+    const size_t tile = (size_t)Ld.Dv * NN;
+    auto slot_rows = [&](int sl) {
+        return slots + (((size_t)t.b * (T + 1) + sl) * Ld.H + t.h) * tile + (size_t)t.row0 * NN;
+    };
+    f32x4 vf[GF::NL];
+    load_rows_f32(vf, slot_rows(c0), t.nrows, wave, lane);
+    const size_t bT = (size_t)t.b * T;
+    stage_window<TQ>(w, Ld, t, 0, 0, T, io.k + (bT * Ld.G + t.g) * NN, Ld.G * NN,
+                     io.v + (bT * Ld.H + t.h) * Ld.Dv + t.row0, Ld.H * Ld.Dv, io.alpha + bT * Ld.H + t.h,
+                     io.beta + bT * Ld.H + t.h, Ld.H);
+    for (int e = tid; e < T * (NN / 4); e += kThreads) {
+        const int qi = e / (NN / 4), c4 = e % (NN / 4);
+        *(f32x4 *)&q[qi][4 * c4] = *(const f32x4 *)(io.q + ((bT + qi) * Ld.G + t.g) * NN + 4 * c4);
+    }
+    __syncthreads();
+    const int c = lane % GF::LPR;
+    float part[GF::NL * TQ];
+#pragma unroll
+    for (int qi = 0; qi < TQ; ++qi) {
+        if (qi < T) {
+            // one record: the fold of record qi alone
+            const f32x4 kj = *(const f32x4 *)&w.K[qi][4 * c];
+            const float aj = w.a[qi], bj = w.b[qi];
+            const f32x4 qq = *(const f32x4 *)&q[qi][4 * c];
+#pragma unroll
+            for (int i = 0; i < GF::NL; ++i) {
+                const int r = row_of_f32(i, wave, lane);
+                float pk = vf[i].x * kj.x;
+                pk = fmaf(vf[i].y, kj.y, pk);
+                pk = fmaf(vf[i].z, kj.z, pk);
+                pk = fmaf(vf[i].w, kj.w, pk);
+                const float sk = row_allreduce(pk);
+                const float coef = bj * (w.V[qi][r < kRows ? r : 0] - aj * sk);
+                vf[i].x = fmaf(coef, kj.x, aj * vf[i].x);
+                vf[i].y = fmaf(coef, kj.y, aj * vf[i].y);
+                vf[i].z = fmaf(coef, kj.z, aj * vf[i].z);
+                vf[i].w = fmaf(coef, kj.w, aj * vf[i].w);
+                float s = vf[i].x * qq.x;
+                s = fmaf(vf[i].y, qq.y, s);
+                s = fmaf(vf[i].z, qq.z, s);
+                part[qi * GF::NL + i] = fmaf(vf[i].w, qq.w, s);
+            }
+            store_rows(slot_rows((c0 + qi + 1) % (T + 1)), vf, t.nrows, wave, lane);
+        } else {
+#pragma unroll
+            for (int i = 0; i < GF::NL; ++i) part[qi * GF::NL + i] = 0.f;
+        }
+    }
+    transpose_reduce<GF::NL * TQ, GF::LPR>(part, lane);
+    bool writer;
+    const int first = tr_first<GF::NL * TQ, GF::LPR>(lane, &writer);
+    constexpr int cnt = tr_count<GF::NL * TQ, GF::LPR>();
+    if (writer) {
+#pragma unroll
+        for (int e = 0; e < cnt; ++e) {
+            const int idx = first + e, qi = idx / GF::NL, i = idx % GF::NL;
+            const int r = row_of_f32(i, wave, lane);
+            if (qi < T && r < kRows) u[qi][r] = part[e];
+        }
+    }
+    __syncthreads();
+    if (tid < t.nrows)
+        for (int qi = 0; qi < T; ++qi) io.o[((bT + qi) * Ld.H + t.h) * Ld.Dv + t.row0 + tid] = u[qi][tid];
+}
+
+inline unsigned gblocks(const GLayer &Ld) { return (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)Ld.psplit; }
+
+template <int LMAX>
+hipError_t step_l(const GLayer &Ld, const GTokenIO &io, bool fc, hipStream_t st)
+{
+    if (fc) hipLaunchKernelGGL((gdn_step_kernel<LMAX, true>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io);
+    else hipLaunchKernelGGL((gdn_step_kernel<LMAX, false>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io);
+    return hipGetLastError();
+}
+
+template <int LMAX>
+hipError_t flush_l(const GLayer &Ld, int mode, const int *arg, int T, float *out, hipStream_t st)
+{
+    if (mode == MODE_OVERFULL) {
+        hipLaunchKernelGGL(gdn_advance_kernel, dim3((Ld.Bt + 255) / 256), dim3(256), 0, st, Ld, arg, T);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((gdn_flush_kernel<LMAX>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, mode,
+                       mode == MODE_OVERFULL ? nullptr : arg, out);
+    return hipGetLastError();
+}
+
+template <int LMAX>
+hipError_t verify_l(const GLayer &Ld, const GTokenIO &io, int T, hipStream_t st)
+{
+    const dim3 grid(gblocks(Ld)), block(kThreads);
+    if (T <= 2) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 2>), grid, block, 0, st, Ld, io, T);
+    else if (T <= 4) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 4>), grid, block, 0, st, Ld, io, T);
+    else hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 8>), grid, block, 0, st, Ld, io, T);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+#define RSSM_CAT2(a, b) a##b
+#define RSSM_CAT(a, b) RSSM_CAT2(a, b)
+
+hipError_t RSSM_CAT(gdn_launch_step_n, RSSM_N)(int lmax, const GLayer &Ld, const GTokenIO &io, bool flush_capable,
+                                               hipStream_t st)
+{
+    switch (lmax) {
+    case 16: return step_l<16>(Ld, io, flush_capable, st);
+    case 32: return step_l<32>(Ld, io, flush_capable, st);
+    case 64: return step_l<64>(Ld, io, flush_capable, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t RSSM_CAT(gdn_launch_flush_n, RSSM_N)(int lmax, const GLayer &Ld, int mode, const int *arg, int T,
+                                                float *out, hipStream_t st)
+{
+    switch (lmax) {
+    case 16: return flush_l<16>(Ld, mode, arg, T, out, st);
+    case 32: return flush_l<32>(Ld, mode, arg, T, out, st);
+    case 64: return flush_l<64>(Ld, mode, arg, T, out, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t RSSM_CAT(gdn_launch_verify_n, RSSM_N)(int lmax, const GLayer &Ld, const GTokenIO &io, int T, hipStream_t st)
+{
+    switch (lmax) {
+    case 16: return verify_l<16>(Ld, io, T, st);
+    case 32: return verify_l<32>(Ld, io, T, st);
+    case 64: return verify_l<64>(Ld, io, T, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t RSSM_CAT(gdn_launch_load_n, RSSM_N)(const GLayer &Ld, const float *state, hipStream_t st)
+{
+    hipLaunchKernelGGL(gdn_load_kernel, dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, state);
+    return hipGetLastError();
+}
+
+hipError_t RSSM_CAT(gdn_launch_conventional_n, RSSM_N)(const GLayer &Ld, float *state, const GTokenIO &io, hipStream_t st)
+{
+    hipLaunchKernelGGL(gdn_conventional_kernel, dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, state, io);
+    return hipGetLastError();
+}
+
+hipError_t RSSM_CAT(gdn_launch_snapshot_n, RSSM_N)(const GLayer &Ld, float *slots, const int *cur, int T,
+                                                   const GTokenIO &io, hipStream_t st)
+{
+    const dim3 grid(gblocks(Ld)), block(kThreads);
+    if (T <= 2) hipLaunchKernelGGL((gdn_snapshot_kernel<2>), grid, block, 0, st, Ld, slots, cur, T, io);
+    else if (T <= 4) hipLaunchKernelGGL((gdn_snapshot_kernel<4>), grid, block, 0, st, Ld, slots, cur, T, io);
+    else hipLaunchKernelGGL((gdn_snapshot_kernel<8>), grid, block, 0, st, Ld, slots, cur, T, io);
+    return hipGetLastError();
+}
+
+}  // namespace rssm

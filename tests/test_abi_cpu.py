@@ -195,3 +195,103 @@ def test_baselines_validate():
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(rs.replayssm_status_string(s), str) and rs.replayssm_status_string(s)
+
+
+# ---- Gated DeltaNet ABI (gdnreplay.h) ---------------------------------------------------------
+GDN_HEADER = os.path.join(ROOT, "include", "gdnreplay.h")
+
+
+def test_every_gdn_symbol_is_exported():
+    text = re.sub(r"/\*.*?\*/", "", open(GDN_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                                  text, re.M)))
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(rs._lib, n), f"{n} declared in gdnreplay.h but not exported"
+    assert set(names) == set(rs.GDN_EXPORTED)
+
+
+def gcfg(**kw):
+    base = dict(batch=0, nheads=32, nkheads=16, dv=128, dk=128, buffer_len=16, max_draft=1)
+    base.update(kw)
+    return rs.make_gdn_config(**base)
+
+
+def test_gdn_workspace_layout():
+    c = gcfg(batch=256)
+    lay = rs.gdnreplay_workspace_layout(c)
+    Bt, H, G, Dv, Dk, L = 256, 32, 16, 128, 128, 16
+    assert lay.master == 0 and lay.ring_k == Bt * H * Dv * Dk * 4
+    assert lay.ring_v - lay.ring_k == Bt * G * L * Dk * 4
+    assert lay.ring_a - lay.ring_v == Bt * H * L * Dv * 4
+    assert lay.ring_b - lay.ring_a == Bt * H * L * 4
+    assert lay.total == rs.gdnreplay_workspace_bytes(c)
+    for name in ("master", "ring_k", "ring_v", "ring_a", "ring_b", "pos", "ckpt_pos", "counters", "flag"):
+        assert getattr(lay, name) % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=48), rs.RSSM_E_UNSUPPORTED),
+    (dict(dk=512), rs.RSSM_E_UNSUPPORTED),
+    (dict(dv=66), rs.RSSM_E_INVAL),
+    (dict(dv=260), rs.RSSM_E_UNSUPPORTED),
+    (dict(nheads=6, nkheads=4), rs.RSSM_E_INVAL),
+    (dict(buffer_len=0), rs.RSSM_E_INVAL),
+    (dict(buffer_len=4, max_draft=5), rs.RSSM_E_INVAL),
+    (dict(buffer_len=65), rs.RSSM_E_UNSUPPORTED),
+    (dict(buffer_len=16, max_draft=9), rs.RSSM_E_UNSUPPORTED),
+    (dict(batch=-1), rs.RSSM_E_INVAL),
+])
+def test_gdn_invalid_configs_rejected(kw, status):
+    c = gcfg(**kw)
+    assert rs.gdnreplay_workspace_bytes(c) == 0
+    h = ctypes.c_void_p()
+    assert rs._lib.gdnreplay_create(ctypes.byref(c), FAKE, 1 << 40, ctypes.byref(h)) == status
+    assert not h.value
+
+
+def test_gdn_state_machine_on_host():
+    L = rs._lib
+    c = gcfg(max_draft=4)
+    h = ctypes.c_void_p()
+    need = rs.gdnreplay_workspace_bytes(c)
+    assert L.gdnreplay_create(ctypes.byref(c), None, need, ctypes.byref(h)) == rs.RSSM_E_WORKSPACE
+    assert L.gdnreplay_create(ctypes.byref(c), FAKE + 16, need, ctypes.byref(h)) == rs.RSSM_E_WORKSPACE
+    assert L.gdnreplay_create(ctypes.byref(c), FAKE, need, ctypes.byref(h)) == rs.RSSM_OK
+    io = [FAKE] * 6
+    assert L.gdnreplay_step(h, *io, None) == rs.RSSM_E_STATE              # before load_state
+    assert L.gdnreplay_load_state(h, None, None) == rs.RSSM_OK            # batch 0: nothing launched
+    assert L.gdnreplay_step(h, *io, None) == rs.RSSM_OK
+    assert L.gdnreplay_step(h, FAKE + 4, *io[1:], None) == rs.RSSM_E_INVAL  # misaligned
+    assert L.gdnreplay_rollback(h, FAKE, None) == rs.RSSM_E_STATE          # no verify pending
+    assert L.gdnreplay_spec_verify(h, 0, *io, None) == rs.RSSM_E_INVAL
+    assert L.gdnreplay_spec_verify(h, 5, *io, None) == rs.RSSM_E_INVAL     # T > max_draft
+    assert L.gdnreplay_spec_verify(h, 4, *io, None) == rs.RSSM_OK
+    assert L.gdnreplay_spec_verify(h, 2, *io, None) == rs.RSSM_E_STATE     # verify twice
+    assert L.gdnreplay_step(h, *io, None) == rs.RSSM_E_STATE               # step while pending
+    assert L.gdnreplay_flush(h, None, None) == rs.RSSM_E_STATE
+    assert L.gdnreplay_rollback(h, FAKE + 2, None) == rs.RSSM_E_INVAL
+    assert L.gdnreplay_rollback(h, FAKE, None) == rs.RSSM_OK
+    assert L.gdnreplay_flush(h, None, None) == rs.RSSM_OK
+    assert L.gdnreplay_materialize_state(h, FAKE + 8, None) == rs.RSSM_E_INVAL
+    assert L.gdnreplay_destroy(h) == rs.RSSM_OK
+    assert L.gdnreplay_destroy(None) == rs.RSSM_OK
+
+
+def test_gdn_pointer_validation_before_state():
+    L = rs._lib
+    c = gcfg(batch=2, max_draft=2)
+    h = ctypes.c_void_p()
+    assert L.gdnreplay_create(ctypes.byref(c), FAKE, rs.gdnreplay_workspace_bytes(c), ctypes.byref(h)) == rs.RSSM_OK
+    io = [FAKE] * 6
+    assert L.gdnreplay_load_state(h, None, None) == rs.RSSM_E_INVAL
+    for i in range(6):
+        bad = list(io)
+        bad[i] = None
+        assert L.gdnreplay_step(h, *bad, None) == rs.RSSM_E_INVAL
+        assert L.gdnreplay_spec_verify(h, 2, *bad, None) == rs.RSSM_E_INVAL
+    assert L.gdnreplay_step(h, *io, None) == rs.RSSM_E_STATE
+    assert L.gdn_conventional_step(ctypes.byref(c), None, *io, None) == rs.RSSM_E_INVAL
+    assert L.gdn_conventional_step(ctypes.byref(gcfg()), FAKE, *io, None) == rs.RSSM_OK   # batch 0
+    assert L.gdn_snapshot_spec_verify(ctypes.byref(c), FAKE, FAKE, 9, *io, None) == rs.RSSM_E_INVAL
+    assert L.gdnreplay_destroy(h) == rs.RSSM_OK
