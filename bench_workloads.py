@@ -4,6 +4,9 @@ spec:  speculative decode on the serving layer -- batch 512, T = 4 drafts, accep
        in {0..4} per sequence (seeded), 128 verify steps. Buffer-pointer rollback (verify launch +
        rollback/commit-flush launch) against per-draft state snapshots (verify-with-snapshots launch
        + commit launch), same inputs, same stream.
+gdn:   a Gated DeltaNet layer (32 value heads, 16 key heads, Dv = Dk = 128) at batch 256, L = 16:
+       the replay step (non-flush and flush launches, 256 steps = 16 windows) against the
+       conventional step, and speculative decode at batch 512, T = 4 against per-draft snapshots.
 sweep: the serving head shape stacked as 10 independent layers, batch in {1, 8, 64, 256, 512} x
        buffer length in {4, 8, 16, 32}, 64 decode steps: per-layer tokens/s of the replay step
        (amortized over whole windows) and of the conventional step, eager and as HIP graphs
@@ -224,8 +227,114 @@ def sweep(args):
         print(json.dumps({"L": L, "smallest_batch_where_replay_wins": min(wins) if wins else None}), flush=True)
 
 
+def _gdn_tokens(g, lead, Hv, Gk, Dv, Dk, rates):
+    q = torch.nn.functional.normalize(torch.randn(*lead, Gk, Dk, device="cuda", generator=g), dim=-1)
+    k = torch.nn.functional.normalize(torch.randn(*lead, Gk, Dk, device="cuda", generator=g), dim=-1)
+    v = torch.randn(*lead, Hv, Dv, device="cuda", generator=g)
+    alpha = torch.exp(rates * torch.nn.functional.softplus(torch.randn(*lead, Hv, device="cuda", generator=g) - 4.0))
+    beta = torch.sigmoid(torch.randn(*lead, Hv, device="cuda", generator=g))
+    return q, k, v, alpha, beta
+
+
+def gdn(args):
+    c = workload.GDN_SERVING
+    Bt, Hv, Gk, Dv, Dk, L = c["Bt"], c["H"], c["G"], c["Dv"], c["Dk"], c["L"]
+    rates = torch.from_numpy(workload.gdn_gate_rates(workload.config_seed(6), Hv)).float().cuda()
+    g = _gen(6007)
+    S0 = torch.randn(Bt, Hv, Dv, Dk, device="cuda", generator=g)
+    pool = [_gdn_tokens(g, (Bt,), Hv, Gk, Dv, Dk, rates) for _ in range(8)]
+    o = torch.empty(Bt, Hv, Dv, device="cuda")
+    lay = rs.GDNReplay(Bt, Hv, Gk, Dv, Dk, buffer_len=L)
+    lay.load_state(S0)
+
+    def rep_step(r):
+        rs.gdnreplay_step(lay.handle, *pool[r % len(pool)], o)
+    _timed(rep_step, 2 * L)
+    steps = 16 * L
+    wall, d = _timed(rep_step, steps)      # starts at a window boundary: step r has k = r % L + 1
+    assert lay.check() == rs.RSSM_OK
+    ks = np.array([r % L + 1 for r in range(steps)])
+    fl = ks == L
+    nf_bytes = np.array([traffic.gdn_replay_nonflush(Hv, Gk, Dv, Dk, int(k)) * Bt for k in ks[~fl]])
+    fl_bytes = traffic.gdn_replay_flush_step(Hv, Gk, Dv, Dk, L) * Bt
+    cfg = rs.make_gdn_config(Bt, Hv, Gk, Dv, Dk)
+    cst = S0.clone()
+
+    def conv_step(r):
+        rs.gdn_conventional_step(cfg, cst, *pool[r % len(pool)], o)
+    _timed(conv_step, 4)
+    wall_c, dc = _timed(conv_step, 64)
+    conv_bytes = traffic.gdn_conventional(Hv, Gk, Dv, Dk) * Bt
+    nf_gbps = float((nf_bytes / d[~fl]).mean()) / 1e9
+    out = {
+        "workload": f"Gated DeltaNet layer decode step, batch {Bt}, {Hv} value heads x {Gk} key heads, "
+                    f"Dv {Dv}, Dk {Dk}, L {L}, fp32 (2 MiB state per sequence)",
+        "replay": {"tokens_per_s_layer": round(Bt * steps / wall, 1),
+                   "nonflush_mean_us": round(float(d[~fl].mean()) * 1e6, 2),
+                   "nonflush_gbps": round(nf_gbps, 1), "nonflush_frac_of_8tbs": round(nf_gbps / PEAK, 4),
+                   "nonflush_alg_bytes_per_launch": int(nf_bytes.mean()),
+                   "flush_mean_us": round(float(d[fl].mean()) * 1e6, 2),
+                   "flush_gbps": round(fl_bytes / float(d[fl].mean()) / 1e9, 1),
+                   "nonflush_us_by_k": {int(k): round(float(d[ks == k].mean()) * 1e6, 1) for k in (1, 4, 8, 12, 15)}},
+        "conventional": {"tokens_per_s_layer": round(Bt * 64 / wall_c, 1),
+                         "mean_us": round(float(dc.mean()) * 1e6, 2),
+                         "gbps": round(conv_bytes / float(dc.mean()) / 1e9, 1)},
+        "speedup_vs_conventional": round((Bt * steps / wall) / (Bt * 64 / wall_c), 3),
+    }
+    print(json.dumps(out), flush=True)
+    del lay, cst
+    torch.cuda.empty_cache()
+
+    # speculative decode: batch 512, T = 4, accepted ~ U{0..4}
+    s = workload.GDN_SPEC
+    Bt, T, iters = s["Bt"], s["T"], s["steps"]
+    S0 = torch.randn(Bt, Hv, Dv, Dk, device="cuda", generator=g)
+    dpool = [_gdn_tokens(g, (Bt, T), Hv, Gk, Dv, Dk, rates) for _ in range(4)]
+    acc = torch.from_numpy(np.stack([workload.accepted_counts(workload.config_seed(7), it, Bt, T)
+                                     for it in range(iters)])).cuda()
+    od = torch.empty(Bt, T, Hv, Dv, device="cuda")
+    lay = rs.GDNReplay(Bt, Hv, Gk, Dv, Dk, buffer_len=L, max_draft=T)
+
+    def spec_iter(it):
+        rs.gdnreplay_spec_verify(lay.handle, T, *dpool[it % len(dpool)], od)
+        rs.gdnreplay_rollback(lay.handle, acc[it])
+    lay.load_state(S0)
+    _timed(spec_iter, 8)
+    lay.load_state(S0)
+    wall_r, dr = _timed(spec_iter, iters)
+    assert lay.check() == rs.RSSM_OK
+    accepted = int(acc.sum().item())
+    del lay
+    torch.cuda.empty_cache()
+    cfg = rs.make_gdn_config(Bt, Hv, Gk, Dv, Dk)
+    slots = torch.empty(Bt, T + 1, Hv, Dv, Dk, device="cuda")
+    slots[:, 0].copy_(S0)
+    cur = torch.zeros(Bt, dtype=torch.int32, device="cuda")
+    ccfg = rs.make_config(Bt, 4, 4, 16, 1)   # snapshot_commit reads only the batch size
+
+    def snap_iter(it):
+        rs.gdn_snapshot_spec_verify(cfg, slots, cur, T, *dpool[it % len(dpool)], od)
+        rs.snapshot_commit(ccfg, cur, acc[it], T)
+    _timed(snap_iter, 4)
+    cur.zero_()
+    wall_s, ds = _timed(snap_iter, iters)
+    out = {
+        "workload": f"Gated DeltaNet spec decode, batch {Bt}, T={T}, accepted ~ U{{0..{T}}}, {iters} verify steps, fp32",
+        "replay": {"accepted_tokens_per_s_layer": round(accepted / wall_r, 1),
+                   "verify_plus_rollback_mean_us": round(float(dr.mean()) * 1e6, 2)},
+        "snapshot": {"accepted_tokens_per_s_layer": round(accepted / wall_s, 1),
+                     "verify_plus_commit_mean_us": round(float(ds.mean()) * 1e6, 2),
+                     "gbps": round(traffic.gdn_snapshot_verify(Hv, Gk, Dv, Dk, T) * Bt / float(ds.mean()) / 1e9, 1),
+                     "state_memory_gib": round(slots.numel() * 4 / 2 ** 30, 2)},
+        "speedup_vs_snapshot": round(wall_s / wall_r, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def run(args):
     if args.workload == "spec":
         spec(args)
+    elif args.workload == "gdn":
+        gdn(args)
     elif args.workload == "sweep":
         sweep(args)

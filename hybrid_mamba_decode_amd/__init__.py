@@ -38,8 +38,8 @@ EXPORTED = (
 GDN_EXPORTED = (
     "gdnreplay_workspace_bytes", "gdnreplay_workspace_layout", "gdnreplay_create", "gdnreplay_destroy",
     "gdnreplay_load_state", "gdnreplay_step", "gdnreplay_flush", "gdnreplay_spec_verify",
-    "gdnreplay_rollback", "gdnreplay_get_pointers", "gdnreplay_check", "gdnreplay_materialize_state",
-    "gdn_conventional_step", "gdn_snapshot_spec_verify",
+    "gdnreplay_rollback", "gdnreplay_set_lockstep", "gdnreplay_get_pointers", "gdnreplay_check",
+    "gdnreplay_materialize_state", "gdn_conventional_step", "gdn_snapshot_spec_verify",
 )
 
 
@@ -96,6 +96,7 @@ _sig = {
     "gdnreplay_flush": (ctypes.c_int, [_vp, _vp, _vp]),
     "gdnreplay_spec_verify": (ctypes.c_int, [_vp, _i32] + [_vp] * 6 + [_vp]),
     "gdnreplay_rollback": (ctypes.c_int, [_vp, _vp, _vp]),
+    "gdnreplay_set_lockstep": (ctypes.c_int, [_vp, ctypes.c_int]),
     "gdnreplay_get_pointers": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
     "gdnreplay_check": (ctypes.c_int, [_vp, _vp]),
     "gdnreplay_materialize_state": (ctypes.c_int, [_vp, _vp, _vp]),
@@ -435,6 +436,10 @@ def gdnreplay_rollback(h, accepted, stream=None):
     _check(_lib.gdnreplay_rollback(h, _ptr(accepted, torch.int32, "accepted"), _stream(stream)), "gdnreplay_rollback")
 
 
+def gdnreplay_set_lockstep(h, enable):
+    _check(_lib.gdnreplay_set_lockstep(h, int(bool(enable))), "gdnreplay_set_lockstep")
+
+
 def gdnreplay_get_pointers(h, batch, stream=None):
     pos = (ctypes.c_int32 * max(batch, 1))()
     ck = (ctypes.c_int32 * max(batch, 1))()
@@ -524,6 +529,9 @@ class GDNReplay:
     def rollback(self, accepted, stream=None):
         _expect(accepted, (self.batch,), "accepted")
         gdnreplay_rollback(self.handle, accepted, stream)
+
+    def set_lockstep(self, enable):
+        gdnreplay_set_lockstep(self.handle, enable)
 
     def get_pointers(self, stream=None):
         return gdnreplay_get_pointers(self.handle, self.batch, stream)

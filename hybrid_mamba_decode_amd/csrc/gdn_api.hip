@@ -24,6 +24,11 @@ struct gdnreplay_layer {
     // Bounds on the pending-record count over all sequences: they only choose whether a step
     // launch may meet a flush (the device decides each flush per sequence).
     int cmin, cmax;
+    // Lockstep: after a load, standard steps and unmasked flushes keep every sequence at the same
+    // window position (pos mod L, ckpt_pos mod L, pending count), tracked here and passed to the
+    // step kernel; a rollback or masked flush ends it until the next load.
+    int uni, pslot, cslot, lcount;
+    int lockstep_ok;
 };
 
 namespace {
@@ -200,6 +205,7 @@ rssm_status gdnreplay_create(const gdnreplay_config *cfg, void *workspace, size_
     d.hpg = cfg->nheads / cfg->nkheads;
     d.psplit = psplit_of(*cfg);
     h->lmax = cfg->buffer_len <= 16 ? 16 : cfg->buffer_len <= 32 ? 32 : 64;
+    h->lockstep_ok = 1;
     *out = h;
     return RSSM_OK;
 }
@@ -218,6 +224,8 @@ rssm_status gdnreplay_load_state(gdnreplay_t h, const float *state, void *stream
     h->poisoned = 0;
     h->pending_T = 0;
     h->cmin = h->cmax = 0;
+    h->uni = h->lockstep_ok;
+    h->pslot = h->cslot = h->lcount = 0;
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) gdn_launch_load_n##NV(h->dev, state, st)
@@ -233,12 +241,25 @@ rssm_status gdnreplay_step(gdnreplay_t h, const float *q, const float *k, const 
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
     if (h->pending_T) return RSSM_E_STATE;
-    const bool flush_capable = h->cmax + 1 > h->cfg.buffer_len - h->cfg.max_draft;
+    const int lim = h->cfg.buffer_len - h->cfg.max_draft;
+    bool flush_capable = h->cmax + 1 > lim;
+    Lockstep ls{0, 0, 0};
+    if (h->uni) {
+        ls = Lockstep{h->pslot, h->cslot, h->lcount + 1};
+        flush_capable = h->lcount + 1 > lim;  // every sequence flushes, or none does
+        h->pslot = (h->pslot + 1) % h->cfg.buffer_len;
+        if (flush_capable) {
+            h->lcount = 0;
+            h->cslot = h->pslot;
+        } else {
+            h->lcount += 1;
+        }
+    }
     commit_bounds(h, 1, 1);
     if (h->cfg.batch == 0) return RSSM_OK;
     const GTokenIO io{q, k, v, alpha, beta, o};
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) gdn_launch_step_n##NV(h->lmax, h->dev, io, flush_capable, st)
+#define CALL(NV) gdn_launch_step_n##NV(h->lmax, h->dev, io, flush_capable, ls, st)
     GDN_BY_N(h->cfg.dk, CALL)
 #undef CALL
 }
@@ -250,8 +271,14 @@ rssm_status gdnreplay_flush(gdnreplay_t h, const int32_t *seq_mask, void *stream
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
     if (h->pending_T) return RSSM_E_STATE;
-    if (!seq_mask) h->cmin = h->cmax = 0;
-    else h->cmin = 0;
+    if (!seq_mask) {
+        h->cmin = h->cmax = 0;
+        h->lcount = 0;
+        h->cslot = h->pslot;
+    } else {
+        h->cmin = 0;
+        h->uni = 0;
+    }
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) gdn_launch_flush_n##NV(h->lmax, h->dev, MODE_MASK, seq_mask, 0, nullptr, st)
@@ -286,12 +313,21 @@ rssm_status gdnreplay_rollback(gdnreplay_t h, const int32_t *accepted, void *str
     if (!h->pending_T) return RSSM_E_STATE;
     const int T = h->pending_T;
     h->pending_T = 0;
+    h->uni = 0;
     commit_bounds(h, 0, T);
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) gdn_launch_flush_n##NV(h->lmax, h->dev, MODE_OVERFULL, accepted, T, nullptr, st)
     GDN_BY_N(h->cfg.dk, CALL)
 #undef CALL
+}
+
+rssm_status gdnreplay_set_lockstep(gdnreplay_t h, int enable)
+{
+    if (!h || (enable != 0 && enable != 1)) return RSSM_E_INVAL;
+    h->lockstep_ok = enable;
+    if (!enable) h->uni = 0;
+    return RSSM_OK;
 }
 
 rssm_status gdnreplay_get_pointers(gdnreplay_t h, int32_t *pos, int32_t *ckpt_pos, void *stream)

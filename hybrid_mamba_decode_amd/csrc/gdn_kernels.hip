@@ -112,6 +112,32 @@ __device__ inline void stage_window(GWin<LMAX> &w, const GLayer &Ld, const Tile 
     }
 }
 
+// Sum over aligned groups of W lanes (W a power of two, <= 64); every lane of a group receives
+// it. Lane exchanges by DPP within a row of 16 (quad permutes, then half-row and row mirrors:
+// after the quad steps a lane's value is its quad's sum, and a mirror pairs each lane with a
+// lane of the other half), a ds_swizzle xor 16 across the two rows of 32, and one ds_bpermute
+// across the halves of the wave.
+template <int CTRL>
+__device__ inline float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int W>
+__device__ inline float group_sum(float v)
+{
+    if constexpr (W >= 2) v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror
+    if constexpr (W >= 16) v += dpp_mov<0x140>(v);  // row_mirror
+    if constexpr (W >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // xor 16
+    if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Sum of a value over the LPR consecutive lanes of a row (all of them receive it).
+__device__ inline float row_allreduce(float v) { return group_sum<GF::LPR>(v); }
+
 // Backward sweep of one query over records last..0 in the calling wave: z <- q; c_j = beta_j
 // (k_j . z); z <- alpha_j (z - c_j k_j). Writes c_j to c[j] and the final z to z_out (lane 0 and
 // lanes holding z elements; wave-wide shuffles, so the whole wave must call it).
@@ -131,8 +157,7 @@ __device__ inline void gdn_sweep(const GWin<LMAX> &w, const float *q, int last, 
             const int n = lane + 64 * e;
             if (n < NN) part = fmaf(z[e], w.K[j][n], part);
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+        part = group_sum<64>(part);
         const float cj = w.b[j] * part;
         const float aj = w.a[j];
 #pragma unroll
@@ -149,13 +174,7 @@ __device__ inline void gdn_sweep(const GWin<LMAX> &w, const float *q, int last, 
     }
 }
 
-// Sum of a value over the LPR consecutive lanes of a row (all of them receive it).
-__device__ inline float row_allreduce(float v)
-{
-#pragma unroll
-    for (int o = GF::LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
+
 
 // Apply records 0..k-1 to fp32 rows held in f32 geometry (vf), in order:
 // S_row <- alpha_j (S_row - beta_j (S_row . k_j) k_j) + beta_j v_j[row] k_j.
@@ -257,32 +276,130 @@ struct GStepLds {
 };
 
 template <int LMAX, bool FLUSH>
-__global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO io)
+__global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO io, Lockstep ls)
 {
     __shared__ GStepLds<LMAX> s;
     const Tile t = gmap_tile(Ld);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    const size_t bh = (size_t)t.b * Ld.H + t.h, bg = (size_t)t.b * Ld.G + t.g;
     float *rows = Ld.master + (bh * Ld.Dv + t.row0) * NN;
 
-    f32x4 vf[GF::NL];
-    load_rows_f32(vf, rows, t.nrows, wave, lane);  // the checkpoint stream first
+    // Window in registers first (record j < k-1 from ring slot (cslot + j) mod L, the token's own
+    // record fresh), committed to LDS once the state stream is in flight.
+    constexpr int KS = (LMAX * NN / 4 + kThreads - 1) / kThreads;
+    constexpr int KCH = KS < 8 ? KS : 8;
+    constexpr int VS = (LMAX * kRows / 4 + kThreads - 1) / kThreads;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const float *rk = Ld.ring_k + bg * Ld.L * NN;
+    const float *rv = Ld.ring_v + bh * Ld.L * Ld.Dv + t.row0;
+    const bool uni = ls.k > 0;
+    int pslot = 0, cslot = 0, k = 1;
+    auto slot_of = [&](int j) { return (int)((unsigned)(cslot + j) % (unsigned)Ld.L); };
+    f32x4 kr[KCH], vr[VS], qr;
+    float ar = 0.f, br = 0.f;
+    auto kaddr = [&](int j, int c4) { return (j < k - 1 ? rk + (size_t)slot_of(j) * NN : io.k + bg * NN) + 4 * c4; };
+    auto issue_window = [&]() {
+#pragma unroll
+        for (int sl = 0; sl < KCH; ++sl) {
+            const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+            const f32x4 val = *(const f32x4 *)kaddr(j < k ? j : k - 1, c4);
+            kr[sl] = j < k ? val : zero;
+        }
+#pragma unroll
+        for (int sl = 0; sl < VS; ++sl) {
+            const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
+            const bool in = j < k && 4 * c4 < t.nrows;
+            const float *src = (in && j < k - 1) ? rv + (size_t)slot_of(j) * Ld.Dv + 4 * c4
+                                                 : io.v + bh * Ld.Dv + t.row0 + (in ? 4 * c4 : 0);
+            const f32x4 val = *(const f32x4 *)src;
+            vr[sl] = in ? val : zero;
+        }
+        {
+            const bool in = tid < k;
+            const bool ring = in && tid < k - 1;
+            const size_t ri = bh * Ld.L + (ring ? slot_of(tid) : 0);
+            const float a = ring ? Ld.ring_a[ri] : io.alpha[bh];
+            const float b = ring ? Ld.ring_b[ri] : io.beta[bh];
+            ar = in ? a : 0.f;
+            br = in ? b : 0.f;
+            const f32x4 q = *(const f32x4 *)(io.q + bg * NN + 4 * (tid % (NN / 4)));
+            qr = tid < NN / 4 ? q : zero;
+        }
+    };
+    auto commit_window = [&]() {
+#pragma unroll
+        for (int s0 = 0; s0 < KS; s0 += KCH) {
+            if (s0 > 0) {
+#pragma unroll
+                for (int sl = 0; sl < KCH; ++sl) {
+                    const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+                    kr[sl] = (s0 + sl < KS && j < k) ? *(const f32x4 *)kaddr(j, c4) : zero;
+                }
+            }
+#pragma unroll
+            for (int sl = 0; sl < KCH; ++sl) {
+                const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+                if (s0 + sl < KS && j < LMAX) *(f32x4 *)&s.w.K[j][4 * c4] = kr[sl];
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < VS; ++sl) {
+            const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
+            if (j < LMAX) *(f32x4 *)&s.w.V[j][4 * c4] = vr[sl];
+        }
+        if (tid < LMAX) {
+            s.w.a[tid] = ar;
+            s.w.b[tid] = br;
+        }
+        if (tid < NN / 4) *(f32x4 *)&s.q[4 * tid] = qr;
+    };
 
-    const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
-    const int c0 = pos - ck;
-    if (!(ck >= 0 && c0 >= 0 && c0 <= Ld.L - Ld.Tmax) || (!FLUSH && c0 + 1 > Ld.L - Ld.Tmax)) {
-        graise(Ld, FLAG_POINTERS);
-        gseq_done(Ld, t.b, pos, ck);
-        return;
+    f32x4 vf[GF::NL];
+    int pos = 0, ck = 0;
+    if (uni) {
+        pslot = ls.pslot;
+        cslot = ls.cslot;
+        k = ls.k;
+        issue_window();
+        load_rows_f32(vf, rows, t.nrows, wave, lane);
+    } else {
+        load_rows_f32(vf, rows, t.nrows, wave, lane);  // the checkpoint stream first
+        pos = Ld.pos[t.b];
+        ck = Ld.ckpt[t.b];
+        const int c0 = pos - ck;
+        if (!(ck >= 0 && c0 >= 0 && c0 <= Ld.L - Ld.Tmax) || (!FLUSH && c0 + 1 > Ld.L - Ld.Tmax)) {
+            graise(Ld, FLAG_POINTERS);
+            gseq_done(Ld, t.b, pos, ck);
+            return;
+        }
+        pslot = (int)((unsigned)pos % (unsigned)Ld.L);
+        cslot = (int)((unsigned)ck % (unsigned)Ld.L);
+        k = c0 + 1;  // records in the window, this token included
+        issue_window();
     }
-    const int k = c0 + 1;  // records in the window, this token included
-    const size_t bg = (size_t)t.b * Ld.G + t.g;
-    stage_window<LMAX>(s.w, Ld, t, ck, c0, k, io.k + bg * NN, 0, io.v + bh * Ld.Dv + t.row0, 0, io.alpha + bh,
-                       io.beta + bh, 0);
-    if (tid < NN / 4) *(f32x4 *)&s.q[4 * tid] = *(const f32x4 *)(io.q + bg * NN + 4 * tid);
+    commit_window();
     __syncthreads();
     const bool flush = k > Ld.L - Ld.Tmax;
-    const int pslot = (int)((unsigned)pos % (unsigned)Ld.L);
+    // Pointer update once per sequence. Lockstep: the work-group of head 0 checks the device
+    // pointers against the window position (a mismatch raises the flag) and advances them;
+    // otherwise the last work-group of the sequence writes them.
+    auto advance_pointers = [&]() {
+        if (uni) {
+            if (t.h == 0 && t.split == 0 && tid == 0) {
+                const int dp = Ld.pos[t.b], dc = Ld.ckpt[t.b];
+                const bool ok = dc >= 0 && dp - dc == k - 1 && (int)((unsigned)dp % (unsigned)Ld.L) == pslot &&
+                                (int)((unsigned)dc % (unsigned)Ld.L) == cslot;
+                if (ok) {
+                    Ld.pos[t.b] = dp + 1;
+                    Ld.ckpt[t.b] = flush ? dp + 1 : dc;
+                } else {
+                    __hip_atomic_fetch_or(Ld.flag, FLAG_POINTERS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        } else {
+            gseq_done(Ld, t.b, pos + 1, flush ? pos + 1 : ck);
+        }
+    };
 
     if (FLUSH && flush) {
         gdn_fold_rows<LMAX>(vf, s.w, k, wave, lane);
@@ -290,10 +407,12 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
         rows_dot<1>(vf, s.q, 1, s.u, wave, lane);
         __syncthreads();
         if (tid < t.nrows) io.o[bh * Ld.Dv + t.row0 + tid] = s.u[tid];
-        gseq_done(Ld, t.b, pos + 1, pos + 1);
+        advance_pointers();
         return;
     }
 
+    // The sweep needs only the window: wave 0 runs it while the checkpoint rows may still be in
+    // flight.
     if (wave == 0) gdn_sweep<LMAX>(s.w, s.q, k - 1, s.c, s.z, lane);
     __syncthreads();
     rows_dot<1>(vf, s.z, 1, s.u, wave, lane);
@@ -310,7 +429,7 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
     }
     if (t.split == 0 && t.h % Ld.hpg == 0 && tid < NN / 4)
         *(f32x4 *)(Ld.ring_k + (bg * Ld.L + pslot) * NN + 4 * tid) = *(const f32x4 *)&s.w.K[k - 1][4 * tid];
-    gseq_done(Ld, t.b, pos + 1, ck);
+    advance_pointers();
 }
 
 // ==========================================================================================
@@ -564,10 +683,10 @@ __global__ void __launch_bounds__(kThreads) gdn_snapshot_kernel(GLayer Ld, float
 inline unsigned gblocks(const GLayer &Ld) { return (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)Ld.psplit; }
 
 template <int LMAX>
-hipError_t step_l(const GLayer &Ld, const GTokenIO &io, bool fc, hipStream_t st)
+hipError_t step_l(const GLayer &Ld, const GTokenIO &io, bool fc, Lockstep ls, hipStream_t st)
 {
-    if (fc) hipLaunchKernelGGL((gdn_step_kernel<LMAX, true>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io);
-    else hipLaunchKernelGGL((gdn_step_kernel<LMAX, false>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io);
+    if (fc) hipLaunchKernelGGL((gdn_step_kernel<LMAX, true>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
+    else hipLaunchKernelGGL((gdn_step_kernel<LMAX, false>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
     return hipGetLastError();
 }
 
@@ -600,12 +719,12 @@ hipError_t verify_l(const GLayer &Ld, const GTokenIO &io, int T, hipStream_t st)
 #define RSSM_CAT(a, b) RSSM_CAT2(a, b)
 
 hipError_t RSSM_CAT(gdn_launch_step_n, RSSM_N)(int lmax, const GLayer &Ld, const GTokenIO &io, bool flush_capable,
-                                               hipStream_t st)
+                                               Lockstep ls, hipStream_t st)
 {
     switch (lmax) {
-    case 16: return step_l<16>(Ld, io, flush_capable, st);
-    case 32: return step_l<32>(Ld, io, flush_capable, st);
-    case 64: return step_l<64>(Ld, io, flush_capable, st);
+    case 16: return step_l<16>(Ld, io, flush_capable, ls, st);
+    case 32: return step_l<32>(Ld, io, flush_capable, ls, st);
+    case 64: return step_l<64>(Ld, io, flush_capable, ls, st);
     default: return hipErrorInvalidValue;
     }
 }

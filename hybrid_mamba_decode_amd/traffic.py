@@ -83,3 +83,41 @@ def rollback_flush(H, P, N, G, count, prec="fp32"):
 def snapshot_verify(H, P, N, G, T):
     """Per-draft snapshot baseline: one state read and T state writes, plus T tokens of I/O."""
     return (1 + T) * state_bytes(H, P, N) + T * (token_input_bytes(H, P, N, G) + output_bytes(H, P))
+
+
+# ---- Gated DeltaNet (H value heads of Dv, G key heads of Dk) -------------------------------------
+def gdn_state_bytes(H, Dv, Dk):
+    return F32 * H * Dv * Dk
+
+
+def gdn_token_input_bytes(H, G, Dv, Dk):
+    """q, k, v, alpha, beta of one token."""
+    return F32 * (2 * G * Dk + H * Dv + 2 * H)
+
+
+def gdn_record_bytes(H, G, Dv, Dk):
+    """A stored record (k, v, alpha, beta), written once and read once per window use."""
+    return F32 * (G * Dk + H * Dv + 2 * H)
+
+
+def gdn_replay_nonflush(H, G, Dv, Dk, k):
+    return (gdn_state_bytes(H, Dv, Dk) + gdn_token_input_bytes(H, G, Dv, Dk) + gdn_record_bytes(H, G, Dv, Dk)
+            + F32 * H * Dv + (k - 1) * gdn_record_bytes(H, G, Dv, Dk))
+
+
+def gdn_replay_flush_step(H, G, Dv, Dk, L):
+    return (2 * gdn_state_bytes(H, Dv, Dk) + gdn_token_input_bytes(H, G, Dv, Dk) + F32 * H * Dv
+            + (L - 1) * gdn_record_bytes(H, G, Dv, Dk))
+
+
+def gdn_conventional(H, G, Dv, Dk):
+    return 2 * gdn_state_bytes(H, Dv, Dk) + gdn_token_input_bytes(H, G, Dv, Dk) + F32 * H * Dv
+
+
+def gdn_verify(H, G, Dv, Dk, T, k_old):
+    return (gdn_state_bytes(H, Dv, Dk) + T * (gdn_token_input_bytes(H, G, Dv, Dk) + gdn_record_bytes(H, G, Dv, Dk)
+            + F32 * H * Dv) + k_old * gdn_record_bytes(H, G, Dv, Dk))
+
+
+def gdn_snapshot_verify(H, G, Dv, Dk, T):
+    return (1 + T) * gdn_state_bytes(H, Dv, Dk) + T * (gdn_token_input_bytes(H, G, Dv, Dk) + F32 * H * Dv)

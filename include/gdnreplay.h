@@ -103,6 +103,13 @@ rssm_status gdnreplay_spec_verify(gdnreplay_t layer, int32_t T, const float *q, 
  * L - max_draft pending records are then flushed. A count out of range sets the flag. */
 rssm_status gdnreplay_rollback(gdnreplay_t layer, const int32_t *accepted, void *stream);
 
+/* Lockstep fast path (as replayssm_set_lockstep): while every sequence has done the same standard
+ * steps since the last load, the host knows the common window position and the step kernel takes
+ * it as arguments, so window loads need no device pointer read first (device pointers are still
+ * checked and advanced). enable = 0 forces the device-pointer path; 1 (the default) re-allows the
+ * fast path from the next load. RSSM_E_INVAL for other values or a NULL handle. */
+rssm_status gdnreplay_set_lockstep(gdnreplay_t layer, int enable);
+
 rssm_status gdnreplay_get_pointers(gdnreplay_t layer, int32_t *pos, int32_t *ckpt_pos, void *stream);
 rssm_status gdnreplay_check(gdnreplay_t layer, void *stream);
 

@@ -32,17 +32,18 @@ class GCase:
     def draft_inputs(self, t, T):
         return workload.gdn_draft_inputs(self.seed, t, self.Bt, T, self.H, self.G, self.Dv, self.Dk)
 
-    def layer(self, Tmax=None):
+    def layer(self, Tmax=None, lockstep=True):
         lay = rs.GDNReplay(self.Bt, self.H, self.G, self.Dv, self.Dk, buffer_len=self.L,
                            max_draft=Tmax or self.Tmax)
+        lay.set_lockstep(lockstep)
         lay.load_state(dev(self.S0))
         return lay
 
 
-def _run(case, steps, sample, check_state_every=1):
+def _run(case, steps, sample, check_state_every=1, lockstep=True):
     log(f"[gdn replay] Bt={case.Bt} H={case.H} G={case.G} Dv={case.Dv} Dk={case.Dk} L={case.L} "
-        f"Tmax={case.Tmax} steps={steps} sample={list(sample)}")
-    lay = case.layer()
+        f"Tmax={case.Tmax} steps={steps} sample={list(sample)} lockstep={lockstep}")
+    lay = case.layer(lockstep=lockstep)
     sample = np.asarray(sample)
     S = case.S0[sample].astype(np.float64)
     rep = oracle.GDNReplay(case.S0[sample], case.G, case.L, case.Tmax)
@@ -70,9 +71,11 @@ def _run(case, steps, sample, check_state_every=1):
     return worst
 
 
-def test_gdn_tiny():
+@pytest.mark.parametrize("lockstep", [True, False])
+def test_gdn_tiny(lockstep):
     c = workload.GDN_TINY
-    _run(GCase(c["Bt"], c["H"], c["G"], c["Dv"], c["Dk"], c["L"], workload.config_seed(5)), c["steps"], range(c["Bt"]))
+    _run(GCase(c["Bt"], c["H"], c["G"], c["Dv"], c["Dk"], c["L"], workload.config_seed(5)), c["steps"], range(c["Bt"]),
+         lockstep=lockstep)
 
 
 def test_gdn_serving():
@@ -171,9 +174,10 @@ def test_gdn_masked_flush_and_materialize():
     assert rel(host(lay.master()), S) <= TOL
 
 
-def test_gdn_corrupted_pointers_flag():
+@pytest.mark.parametrize("lockstep", [True, False])
+def test_gdn_corrupted_pointers_flag(lockstep):
     case = GCase(2, 4, 2, 16, 32, 4, 11)
-    lay = case.layer()
+    lay = case.layer(lockstep=lockstep)
     ins = [dev(a) for a in case.step_inputs(0)]
     lay.step(*ins)
     pos, ck = lay.pointer_arrays()
@@ -259,12 +263,14 @@ def test_gdn_spec_accept_extremes_and_interleaved_steps():
     _run_spec(case, 3, 24, range(4), accept=lambda it: pattern[it % 3], interleave=True)
 
 
-def test_gdn_graph_replay_of_whole_windows():
-    """A captured graph of one whole window replays correctly (pointers are device-resident and
-    updated in place); each replay matches the oracle; eager steps continue afterwards."""
+@pytest.mark.parametrize("lockstep", [True, False])
+def test_gdn_graph_replay_of_whole_windows(lockstep):
+    """A captured graph of one whole window replays correctly, with the lockstep arguments (they
+    repeat every window) or the device pointers (updated in place); each replay matches the
+    oracle; eager steps continue afterwards."""
     Bt, H, G, Dv, Dk, L = 4, 4, 2, 64, 128, 4
     case = GCase(Bt, H, G, Dv, Dk, L, 91)
-    lay = case.layer()
+    lay = case.layer(lockstep=lockstep)
     bufs = [tuple(dev(a) for a in case.step_inputs(t)) for t in range(L)]
     outs = [torch.empty(Bt, H, Dv, device="cuda") for _ in range(L)]
     g = torch.cuda.CUDAGraph()
