@@ -284,6 +284,14 @@ def gdn(args):
     print(json.dumps(out), flush=True)
     del lay, cst
     torch.cuda.empty_cache()
+    if getattr(args, "calib_copy", False):
+        # counter calibration: a plain kernel that reads exactly 1 GiB and writes exactly 1 GiB
+        a = torch.ones(1 << 28, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
 
     # speculative decode: batch 512, T = 4, accepted ~ U{0..4}
     s = workload.GDN_SPEC
