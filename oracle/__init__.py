@@ -10,6 +10,7 @@ Functions (all arrays numpy, C-contiguous):
   Replay(...)                                  O3 + O4, the replay form and its pointer machine
   bf16_encode / e4m3_encode_tiles / e4m3_encode_at / e4m3_decode / bf16_decode    O7
   mxfp4_encode / mxfp4_decode / mx_scale_code / e2m1_encode_scaled / e2m1_decode   O7 (MXFP4)
+  philox4x32_10 / f16_encode / f16_decode      R8: the fp16 master's rounding and its random stream
   gdn_step(S, q, k, v, alpha, beta) -> o       O1g, one Gated DeltaNet token (oracle_gdn.c)
   gdn_spec_stepwise(...)                       O5g, per-draft spec decoding on GDN
   GDNReplay(...)                               O3g + O4, the GDN replay form and pointer machine
@@ -32,6 +33,7 @@ _f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
 _u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
 _u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+_u32p = np.ctypeslib.ndpointer(np.uint32, flags="C_CONTIGUOUS")
 _i = ctypes.c_int
 _sz = ctypes.c_size_t
 
@@ -65,7 +67,11 @@ def lib():
         L.oracle_mx_scale_code.restype = ctypes.c_uint8
         L.oracle_encode_mxfp4.argtypes = [_f32p, _u8p, _u8p, _sz]
         L.oracle_decode_mxfp4.argtypes = [_u8p, _u8p, _f64p, _sz]
-        L.oracle_replay_create.argtypes = [_i] * 8 + [_f32p, _f32p, _f32p]
+        L.oracle_replay_create.argtypes = [_i] * 8 + [_f32p, _f32p, _f32p, _i, ctypes.c_uint32]
+        L.oracle_philox4x32_10.argtypes = [_u32p, _u32p, _u32p]
+        L.oracle_f16_decode.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_decode.restype = ctypes.c_float
+        L.oracle_encode_f16.argtypes = [_f32p, _u16p, _sz, _i, ctypes.c_void_p]
         L.oracle_replay_create.restype = ctypes.c_void_p
         L.oracle_replay_destroy.argtypes = [ctypes.c_void_p]
         L.oracle_replay_step.argtypes = [ctypes.c_void_p, _f32p, _f32p, _f32p, _f32p, _f64p]
@@ -136,17 +142,18 @@ def spec_stepwise(S, T, x, B, C, dt, A, D, accepted):
 
 
 READ_FP32, READ_BF16, READ_FP8, READ_MXFP4 = 0, 1, 2, 3
+MASTER_FP32, MASTER_FP16, MASTER_FP16_SR = 0, 1, 2
 
 
 class Replay:
     """O3 + O4: the replay form (checkpoint + records) with its pointer and flush machine."""
 
-    def __init__(self, S0, A, D, G, L, Tmax=1, read_prec=READ_FP32):
+    def __init__(self, S0, A, D, G, L, Tmax=1, read_prec=READ_FP32, master_prec=MASTER_FP32, seed=0):
         S0 = _f32(S0)
         self.Bt, self.H, self.P, self.N = S0.shape
         self.G, self.L, self.Tmax = G, L, Tmax
         self._h = lib().oracle_replay_create(self.Bt, self.H, self.P, self.N, G, L, Tmax,
-                                             read_prec, S0, _f32(A), _f32(D))
+                                             read_prec, S0, _f32(A), _f32(D), int(master_prec), int(seed))
         if not self._h:
             raise ValueError("invalid replay configuration")
 
@@ -362,3 +369,30 @@ class GDNReplay:
 
     def materialize(self):
         return self._state(lib().oracle_gdn_replay_materialize)
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 of one 4-word counter and 2-word key (uint32 sequences) -> 4 uint32 words."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, np.uint32)
+    lib().oracle_philox4x32_10(c, k, out)
+    return out
+
+
+def f16_encode(a, r24=None):
+    """fp16 codes (uint16) of fp32 values: nearest even, or stochastic with 24-bit randoms r24."""
+    a = _f32(a)
+    out = np.empty(a.shape, np.uint16)
+    if r24 is None:
+        lib().oracle_encode_f16(a.reshape(-1), out.reshape(-1), a.size, 0, None)
+    else:
+        r = np.ascontiguousarray(r24, dtype=np.uint32).reshape(-1)
+        assert r.size == a.size
+        lib().oracle_encode_f16(a.reshape(-1), out.reshape(-1), a.size, 1, r.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def f16_decode(codes):
+    codes = np.asarray(codes, np.uint16)
+    return np.array([lib().oracle_f16_decode(int(c)) for c in codes.reshape(-1)], np.float32).reshape(codes.shape)

@@ -41,6 +41,18 @@
  *       divided by the scale, rounded to nearest with ties to even, clamped to +-6. The spec
  *       leaves the scale of an all-zero block open: it takes the smallest code. Two elements per
  *       byte, element 2i in the low nibble.
+ *   R8  low-precision master recurrence (the pages' FP16-with-stochastic-rounding recurrence,
+ *       [AT Pulse] "Capabilities and access" and "Claims and evidence"): the checkpoint itself is
+ *       kept in IEEE fp16. At load the fp32 state is rounded to nearest even; at every flush the
+ *       fold is computed at full precision from the fp16 checkpoint and the records, rounded to
+ *       fp32, clamped to +-65504 and rounded to fp16 either to nearest even or stochastically:
+ *       with q the fp16 value toward zero and ulp the fp16 spacing above it, the magnitude rounds
+ *       up iff r < (|v| - |q|) / ulp * 2^24, r the top 24 bits of a Philox4x32-10 word (Salmon et
+ *       al., SC'11) with counter (element / 4, sequence, new ckpt_pos, 0), key (seed, 0), word
+ *       element % 4 (elements numbered h*P*N + p*N + n within the sequence). That threshold is
+ *       exact in fp32; the rounding is unbiased over r (to within 2^-24 of a spacing for |v| below
+ *       2^-25, where the threshold is not an integer). Reads and the read copy then come from
+ *       the fp16 checkpoint; a flush step's output is read from the rounded checkpoint.
  *
  * Layouts (row-major, last index fastest): x [Bt,H,P]; B, C [Bt,G,N]; dt [Bt,H]; A, D [H];
  * state [Bt,H,P,N]; y [Bt,H,P]. Spec-decode inputs carry the draft index after the batch index:
@@ -309,6 +321,97 @@ void oracle_decode_mxfp4(const uint8_t *codes, const uint8_t *scales, double *ou
     }
 }
 
+/* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",  */
+/* SC'11): ten rounds of two 32x32->64 multiplications; the key is bumped by the Weyl constants */
+/* between rounds.                                                                               */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 mantissa bits; exponent field 0 is  */
+/* subnormal (m * 2^-24); the largest finite value is 65504.                                    */
+float oracle_f16_decode(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double mag = e == 31 ? (m ? NAN : INFINITY) : e == 0 ? ldexp((double)m, -24) : ldexp(1.0 + m / 1024.0, e - 15);
+    return (float)(sign ? -mag : mag);
+}
+
+/* fp16 spacing at magnitude q (an fp16 value): 2^(e - 10) in the binade [2^e, 2^(e+1)), 2^-24  */
+/* below 2^-14.                                                                                  */
+static double f16_spacing(double q)
+{
+    if (q < ldexp(1.0, -14)) return ldexp(1.0, -24);
+    int e;
+    frexp(q, &e); /* q = f * 2^e, 0.5 <= f < 1 */
+    return ldexp(1.0, e - 1 - 10);
+}
+
+static uint16_t f16_code_of(double mag) /* an exactly representable magnitude <= 65504 */
+{
+    if (mag < ldexp(1.0, -14)) return (uint16_t)(int)(mag / ldexp(1.0, -24));
+    int e;
+    frexp(mag, &e);
+    e -= 1; /* mag in [2^e, 2^(e+1)) */
+    int m = (int)(mag / ldexp(1.0, e - 10)) - 1024;
+    return (uint16_t)(((e + 15) << 10) | m);
+}
+
+/* Largest fp16 magnitude <= mag (mag <= 65504). */
+static double f16_toward_zero(double mag)
+{
+    double sp = f16_spacing(mag);
+    double q = floor(mag / sp) * sp;
+    if (f16_spacing(q) != sp) q = floor(mag / f16_spacing(q)) * f16_spacing(q); /* binade edge */
+    return q;
+}
+
+/* Round an fp32 value to fp16, to nearest even (reading R8; clamped to +-65504 first). */
+uint16_t oracle_f16_encode_rne(float v)
+{
+    double t = (double)v, mag = fabs(t);
+    int sign = signbit(t) ? 1 : 0;
+    if (mag > 65504.0) mag = 65504.0;
+    double q = f16_toward_zero(mag), sp = f16_spacing(q), up = q + sp;
+    double r = mag - q;
+    double out = q;
+    if (r > sp / 2 || (r == sp / 2 && (f16_code_of(q) & 1))) out = up;
+    if (out > 65504.0) out = 65504.0;
+    return (uint16_t)(f16_code_of(out) | (sign << 15));
+}
+
+/* Round an fp32 value to fp16 stochastically with the 24-bit random integer r24 (reading R8). */
+uint16_t oracle_f16_encode_sr(float v, uint32_t r24)
+{
+    double t = (double)v, mag = fabs(t);
+    int sign = signbit(t) ? 1 : 0;
+    if (mag > 65504.0) mag = 65504.0;
+    double q = f16_toward_zero(mag);
+    double out = q;
+    if (mag > q) {
+        double threshold = (mag - q) / f16_spacing(q) * 16777216.0; /* exact */
+        if ((double)r24 < threshold) out = q + f16_spacing(q);
+    }
+    return (uint16_t)(f16_code_of(out) | (sign << 15));
+}
+
+void oracle_encode_f16(const float *in, uint16_t *out, size_t n, int stochastic, const uint32_t *r24)
+{
+    for (size_t i = 0; i < n; ++i) out[i] = stochastic ? oracle_f16_encode_sr(in[i], r24[i]) : oracle_f16_encode_rne(in[i]);
+}
+
 /* ------------------------------------------------------------------------------------------- */
 /* O3 + O4: the replay form with its pointer and flush state machine.                           */
 /*                                                                                             */
@@ -335,6 +438,8 @@ void oracle_decode_mxfp4(const uint8_t *codes, const uint8_t *scales, double *ou
 
 typedef struct oracle_replay {
     int Bt, H, P, N, G, L, Tmax, read_prec; /* 0 fp32 master, 1 bf16, 2 fp8 e4m3, 3 mxfp4 */
+    int master_prec;                        /* 0 fp32, 1 fp16 nearest even, 2 fp16 stochastic (R8) */
+    uint32_t seed;
     double *A, *D;                          /* [H] */
     double *ckpt;                           /* [Bt,H,P,N] master */
     double *rcopy;                          /* [Bt,H,P,N] decoded read copy (read_prec != 0) */
@@ -362,6 +467,29 @@ static void poison_records(oracle_replay *r, int b, int from_idx)
                 r->rB[rg_at(r, b, idx, g) + n] = NAN;
                 r->rC[rg_at(r, b, idx, g) + n] = NAN;
             }
+    }
+}
+
+/* Keep sequence b's checkpoint in the master precision (reading R8): fp32 (rounded from the     */
+/* float64 fold), or fp16 to nearest even / stochastically with the Philox stream of flush      */
+/* position `ck` (stochastic rounding only after a flush; a load rounds to nearest even).       */
+static void round_master(oracle_replay *r, int b, int ck, int stochastic)
+{
+    const size_t n = (size_t)r->H * r->P * r->N;
+    double *m = r->ckpt + (size_t)b * n;
+    for (size_t e = 0; e < n; e += 4) {
+        uint32_t words[4] = {0, 0, 0, 0};
+        if (r->master_prec == 2 && stochastic) {
+            const uint32_t ctr[4] = {(uint32_t)(e / 4), (uint32_t)b, (uint32_t)ck, 0u};
+            const uint32_t key[2] = {r->seed, 0u};
+            oracle_philox4x32_10(ctr, key, words);
+        }
+        for (int w = 0; w < 4 && e + w < n; ++w) {
+            const float v = (float)m[e + w];
+            if (r->master_prec == 0) m[e + w] = (double)v;
+            else if (r->master_prec == 2 && stochastic) m[e + w] = (double)oracle_f16_decode(oracle_f16_encode_sr(v, words[w] >> 8));
+            else m[e + w] = (double)oracle_f16_decode(oracle_f16_encode_rne(v));
+        }
     }
 }
 
@@ -398,14 +526,18 @@ static void refresh_copy(oracle_replay *r, int b)
 }
 
 oracle_replay *oracle_replay_create(int Bt, int H, int P, int N, int G, int L, int Tmax,
-                                    int read_prec, const float *S0, const float *A, const float *D)
+                                    int read_prec, const float *S0, const float *A, const float *D,
+                                    int master_prec, uint32_t seed)
 {
     if (Bt < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G || L <= 0 || L > 64 ||
-        Tmax <= 0 || Tmax > L || read_prec < 0 || read_prec > 3 || (read_prec == 3 && N % 32))
+        Tmax <= 0 || Tmax > L || read_prec < 0 || read_prec > 3 || (read_prec == 3 && N % 32) ||
+        master_prec < 0 || master_prec > 2 || (master_prec != 0 && N % 4))
         return NULL;
     oracle_replay *r = (oracle_replay *)calloc(1, sizeof(oracle_replay));
     r->Bt = Bt; r->H = H; r->P = P; r->N = N; r->G = G; r->L = L; r->Tmax = Tmax;
     r->read_prec = read_prec;
+    r->master_prec = master_prec;
+    r->seed = seed;
     const size_t st = (size_t)Bt * H * P * N;
     r->A = (double *)malloc(H * sizeof(double));
     r->D = (double *)malloc(H * sizeof(double));
@@ -419,7 +551,7 @@ oracle_replay *oracle_replay_create(int Bt, int H, int P, int N, int G, int L, i
     r->rdt = (float *)malloc(((size_t)Bt * L * H + 1) * sizeof(float));
     r->pos = (int *)calloc(Bt + 1, sizeof(int));
     r->ckpt_pos = (int *)calloc(Bt + 1, sizeof(int));
-    for (int b = 0; b < Bt; ++b) { poison_records(r, b, 0); refresh_copy(r, b); }
+    for (int b = 0; b < Bt; ++b) { round_master(r, b, 0, 0); poison_records(r, b, 0); refresh_copy(r, b); }
     return r;
 }
 
@@ -513,6 +645,7 @@ static void flush_seq(oracle_replay *r, int b)
     if (count <= 0) return;
     fold_into(r, b, count, r->ckpt);
     r->ckpt_pos[b] = r->pos[b];
+    if (r->master_prec) round_master(r, b, r->ckpt_pos[b], 1);
     poison_records(r, b, 0);
     refresh_copy(r, b);
 }

@@ -1,0 +1,126 @@
+"""Pins for the oracle's low-precision master (reading R8 of oracle.c): the Philox4x32-10 stream,
+fp16 rounding to nearest even, stochastic rounding, and the dual model that keeps the checkpoint
+in fp16.
+
+Independent references: the generator's published known-answer vectors
+(tests/golden/philox_kat.json), numpy's float16 conversion (a library routine), fp16 neighbours
+and thresholds computed with numpy.nextafter and exact fractions, and an fp32-master replay whose
+flushed checkpoint numpy rounds to fp16.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workload
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "philox_kat.json")
+
+
+def test_philox_known_answers():
+    for vec in json.load(open(GOLDEN))["vectors"]:
+        ctr = [int(x, 16) for x in vec["ctr"]]
+        key = [int(x, 16) for x in vec["key"]]
+        want = [int(x, 16) for x in vec["out"]]
+        assert list(oracle.philox4x32_10(ctr, key)) == want
+
+
+def test_f16_nearest_even_vs_numpy():
+    """Every fp32 pattern with exponent field in [80, 143] (|v| from 2^-47 to 65536, subnormals of
+    fp16 included) on a mantissa stride of 97, plus fp16 midpoints and their neighbours."""
+    mant = np.arange(0, 1 << 23, 97, dtype=np.uint32)
+    vals = []
+    for e in range(80, 143):
+        bits = (np.uint32(e) << np.uint32(23)) | mant
+        vals.append(bits.view(np.float32))
+    h = np.arange(0, 0x7BFF, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = ((h[:-1] + h[1:]) / 2).astype(np.float32)
+    vals += [mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))]
+    v = np.concatenate(vals).astype(np.float32)
+    v = v[np.abs(v) <= 65504]
+    v = np.concatenate([v, -v])
+    assert np.array_equal(oracle.f16_encode(v), v.astype(np.float16).view(np.uint16))
+
+
+def test_f16_decode_vs_numpy():
+    codes = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (codes & 0x7C00) != 0x7C00
+    got = oracle.f16_decode(codes[finite])
+    assert np.array_equal(got, codes[finite].view(np.float16).astype(np.float32))
+
+
+def _threshold(v):
+    """Round-up threshold of stochastic rounding: (|v| - q) / ulp * 2^24 as an exact Fraction,
+    with q = the fp16 magnitude toward zero (numpy) and ulp the gap to the next one."""
+    a = abs(float(np.float32(v)))
+    q16 = np.float16(a)
+    if float(q16) > a:
+        q16 = np.nextafter(q16, np.float16(0))
+    nxt = np.nextafter(q16, np.float16(np.inf))
+    q, up = Fraction(float(q16)), Fraction(float(nxt))
+    return (Fraction(a) - q) / (up - q) * 2 ** 24, float(q16), float(nxt)
+
+
+def test_stochastic_rounding_threshold_and_unbiasedness():
+    """The magnitude rounds up iff r24 < T (T exact, an integer except deep in fp16's subnormal
+    range, |v| < 2^-25, where fp32 keeps finer bits than the fp16 spacing). Hence the mean over all
+    2^24 values of r24 is within 2^-24 of a spacing of v, and exactly v whenever T is an integer.
+    Representable values never change."""
+    rng = np.random.default_rng(3)
+    v = (rng.standard_normal(400) * np.exp2(rng.integers(-30, 14, 400))).astype(np.float32)
+    v = np.concatenate([v, np.float16(rng.standard_normal(50)).astype(np.float32)])
+    n_int = 0
+    for x in v:
+        T, q, nxt = _threshold(x)
+        assert 0 <= T < 2 ** 24
+        c = -(-T.numerator // T.denominator)              # ceil(T): the number of r24 that round up
+        sign = -1.0 if x < 0 else 1.0
+        rs = np.array(sorted({0, max(c - 1, 0), min(c, 2 ** 24 - 1), min(c + 1, 2 ** 24 - 1), 2 ** 24 - 1}), np.uint32)
+        got = oracle.f16_decode(oracle.f16_encode(np.full(len(rs), x, np.float32), rs)).astype(np.float64)
+        want = [sign * (nxt if Fraction(int(r)) < T else q) for r in rs]
+        assert np.array_equal(got, np.array(want)), (x, T)
+        mean = Fraction(c) * Fraction(nxt) + Fraction(2 ** 24 - c) * Fraction(q)   # times 2^24
+        err = abs(mean - Fraction(abs(float(x))) * 2 ** 24)
+        assert err <= Fraction(nxt) - Fraction(q)
+        if T.denominator == 1:
+            assert err == 0
+            n_int += 1
+    assert n_int > 300
+
+
+def test_fp16_master_dual_model():
+    """Checkpoint after load = numpy's fp16 of S0; after the first flush = numpy's fp16 (nearest
+    even) of an fp32-master replay's checkpoint started from that fp16 state; with stochastic
+    rounding, the code of each value is its toward-zero or next fp16 value, chosen by the
+    Philox word of its element; outputs stay within 1e-3 of the stepwise truth (2 u of fp16)."""
+    Bt, H, P, N, G, L = 2, 4, 16, 32, 2, 4
+    seed = 19
+    S0 = workload.initial_state(seed, Bt, H, P, N)
+    A, D = workload.layer_params(seed, H)
+    S16 = S0.astype(np.float16).astype(np.float32)
+    rne = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP16)
+    sr = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP16_SR, seed=77)
+    ref = oracle.Replay(S16, A, D, G, L, 1)            # fp32 master from the fp16 state
+    assert np.array_equal(rne.checkpoint(), S16.astype(np.float64))
+    assert np.array_equal(sr.checkpoint(), S16.astype(np.float64))
+    S = S0.astype(np.float64)
+    for t in range(L):
+        ins = workload.step_inputs(seed, t, Bt, H, P, N, G)
+        y_true = oracle.step(S, *ins, A, D)
+        for r in (rne, sr):
+            y = r.step(*ins)
+            assert np.abs(y - y_true).max() / np.abs(y_true).max() <= 1e-3
+        ref.step(*ins)
+    v32 = ref.checkpoint().astype(np.float32)           # fp32 fold of the same records
+    assert np.array_equal(rne.checkpoint(), v32.astype(np.float16).astype(np.float64))
+    flat = v32.reshape(Bt, -1)
+    words = np.empty_like(flat, dtype=np.uint32)
+    for b in range(Bt):
+        for g in range(flat.shape[1] // 4):
+            words[b, 4 * g:4 * g + 4] = oracle.philox4x32_10([g, b, L, 0], [77, 0])
+    want = oracle.f16_decode(oracle.f16_encode(flat, words >> 8)).astype(np.float64).reshape(S0.shape)
+    assert np.array_equal(sr.checkpoint(), want)
+    assert not np.array_equal(sr.checkpoint(), rne.checkpoint())
