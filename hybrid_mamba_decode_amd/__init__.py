@@ -27,6 +27,8 @@ RSSM_OK, RSSM_E_INVAL, RSSM_E_WORKSPACE, RSSM_E_HIP, RSSM_E_STATE, RSSM_E_UNSUPP
 READ_FP32, READ_BF16, READ_FP8_E4M3, READ_MXFP4 = 0, 1, 2, 3
 _PREC_NAMES = {"fp32": READ_FP32, "bf16": READ_BF16, "fp8": READ_FP8_E4M3, "fp8_e4m3": READ_FP8_E4M3,
                "mxfp4": READ_MXFP4, "fp4": READ_MXFP4}
+MASTER_FP32, MASTER_FP16, MASTER_FP16_SR = 0, 1, 2
+_MASTER_NAMES = {"fp32": MASTER_FP32, "fp16": MASTER_FP16, "fp16_sr": MASTER_FP16_SR}
 
 EXPORTED = (
     "replayssm_workspace_bytes", "replayssm_workspace_layout", "replayssm_create", "replayssm_destroy",
@@ -46,7 +48,7 @@ GDN_EXPORTED = (
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "nheads", "headdim", "dstate", "ngroups", "buffer_len", "max_draft", "read_prec",
-        "store_C")]
+        "store_C", "master_prec", "sr_seed")]
 
 
 class Layout(ctypes.Structure):
@@ -141,9 +143,11 @@ def _stream(stream=None):
 
 
 def make_config(batch, nheads, headdim, dstate, ngroups, buffer_len=16, max_draft=1,
-                read_prec="fp32", store_C=True):
+                read_prec="fp32", store_C=True, master_prec="fp32", sr_seed=0):
     rp = _PREC_NAMES[read_prec] if isinstance(read_prec, str) else int(read_prec)
-    return Config(batch, nheads, headdim, dstate, ngroups, buffer_len, max_draft, rp, int(bool(store_C)))
+    mp = _MASTER_NAMES[master_prec] if isinstance(master_prec, str) else int(master_prec)
+    return Config(batch, nheads, headdim, dstate, ngroups, buffer_len, max_draft, rp, int(bool(store_C)), mp,
+                  int(sr_seed))
 
 
 def _expect(t, shape, name):
@@ -275,9 +279,9 @@ class ReplaySSM:
     """
 
     def __init__(self, batch, nheads, headdim, dstate, ngroups, A, D, buffer_len=16, max_draft=1,
-                 read_prec="fp32", store_C=True, device="cuda"):
+                 read_prec="fp32", store_C=True, master_prec="fp32", sr_seed=0, device="cuda"):
         self.cfg = make_config(batch, nheads, headdim, dstate, ngroups, buffer_len, max_draft,
-                               read_prec, store_C)
+                               read_prec, store_C, master_prec, sr_seed)
         nbytes = replayssm_workspace_bytes(self.cfg)
         if nbytes == 0:
             raise ReplaySSMError(RSSM_E_INVAL, "replayssm_workspace_bytes")
@@ -356,7 +360,9 @@ class ReplaySSM:
         return self.workspace[off:off + nbytes].view(dtype).view(*shape)
 
     def master(self):
-        return self.region("master", torch.float32, (self.batch, self.nheads, self.headdim, self.dstate))
+        """The checkpoint as stored: float32, or float16 for an fp16 master."""
+        dt = torch.float32 if self.cfg.master_prec == MASTER_FP32 else torch.float16
+        return self.region("master", dt, (self.batch, self.nheads, self.headdim, self.dstate))
 
     def read_copy(self):
         """The read copy in row-major order: bf16 bits int16 [Bt,H,P,N], fp8 codes uint8

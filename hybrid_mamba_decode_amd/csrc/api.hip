@@ -73,7 +73,14 @@ rssm_status check_config(const replayssm_config *c)
     if (c->buffer_len > 64 || c->max_draft > 8) return RSSM_E_UNSUPPORTED;
     if (c->read_prec == RSSM_READ_FP8_E4M3 && c->headdim > kRows) return RSSM_E_UNSUPPORTED;
     if (c->read_prec == RSSM_READ_MXFP4 && c->dstate < 32) return RSSM_E_UNSUPPORTED;
+    if (c->master_prec < RSSM_MASTER_FP32 || c->master_prec > RSSM_MASTER_FP16_SR) return RSSM_E_INVAL;
     return RSSM_OK;
+}
+
+// Read precision of the kernels: the copy's, or the fp16 master read directly.
+int kernel_prec(const replayssm_config &c)
+{
+    return c.read_prec == RSSM_READ_FP32 && c.master_prec != RSSM_MASTER_FP32 ? PREC_F16 : c.read_prec;
 }
 
 void make_layout(const replayssm_config &c, replayssm_layout *L)
@@ -87,7 +94,7 @@ void make_layout(const replayssm_config &c, replayssm_layout *L)
         off = align_up(off + bytes);
         return at;
     };
-    L->master = take(elems * 4);
+    L->master = take(elems * (c.master_prec == RSSM_MASTER_FP32 ? 4 : 2));
     const int rp = c.read_prec;
     L->read_copy = take(rp == RSSM_READ_BF16 ? elems * 2 : rp == RSSM_READ_FP8_E4M3 ? elems
                         : rp == RSSM_READ_MXFP4 ? elems / 2 : 0);
@@ -253,6 +260,8 @@ rssm_status replayssm_create(const replayssm_config *cfg, void *workspace, size_
     d.Tmax = cfg->max_draft;
     d.hpg = cfg->nheads / cfg->ngroups;
     d.psplit = psplit_of(*cfg);
+    d.mprec = cfg->master_prec;
+    d.sr_seed = (unsigned)cfg->sr_seed;
     h->lmax = cfg->buffer_len <= 16 ? 16 : cfg->buffer_len <= 32 ? 32 : 64;
     h->lockstep_ok = 1;
     *out = h;
@@ -273,11 +282,11 @@ rssm_status replayssm_load_state(replayssm_t h, const float *state, void *stream
     h->poisoned = 0;
     h->pending_T = 0;
     h->cmin = h->cmax = 0;
-    h->uni = h->lockstep_ok;
+    h->uni = h->lockstep_ok && h->cfg.master_prec != RSSM_MASTER_FP16_SR;
     h->pslot = h->cslot = h->lcount = 0;
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_load_n##NV(h->cfg.read_prec, h->dev, state, st)
+#define CALL(NV) launch_load_n##NV(kernel_prec(h->cfg), h->dev, state, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
 }
@@ -310,7 +319,7 @@ rssm_status replayssm_step(replayssm_t h, const float *x, const float *B, const 
     if (h->cfg.batch == 0) return RSSM_OK;
     const TokenIO io{x, B, C, dt, y};
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_step_n##NV(h->cfg.read_prec, h->lmax, h->dev, io, flush_capable, ls, st)
+#define CALL(NV) launch_step_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, io, flush_capable, ls, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
 }
@@ -332,7 +341,7 @@ rssm_status replayssm_flush(replayssm_t h, const int32_t *seq_mask, void *stream
     }
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_flush_n##NV(h->cfg.read_prec, h->lmax, h->dev, MODE_MASK, seq_mask, 0, nullptr, st)
+#define CALL(NV) launch_flush_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, MODE_MASK, seq_mask, 0, nullptr, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
 }
@@ -352,7 +361,7 @@ rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float *x, cons
     if (h->cfg.batch == 0) return RSSM_OK;
     const TokenIO io{x, B, C, dt, y};
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_verify_n##NV(h->cfg.read_prec, h->lmax, h->dev, io, T, st)
+#define CALL(NV) launch_verify_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, io, T, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
 }
@@ -370,7 +379,7 @@ rssm_status replayssm_rollback(replayssm_t h, const int32_t *accepted, void *str
     commit_bounds(h, 0, T);
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_flush_n##NV(h->cfg.read_prec, h->lmax, h->dev, MODE_OVERFULL, accepted, T, nullptr, st)
+#define CALL(NV) launch_flush_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, MODE_OVERFULL, accepted, T, nullptr, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
 }
@@ -413,7 +422,7 @@ rssm_status replayssm_materialize_state(replayssm_t h, float *out, void *stream)
     if (s != RSSM_OK) return s;
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_flush_n##NV(h->cfg.read_prec, h->lmax, h->dev, MODE_MATERIALIZE, nullptr, 0, out, st)
+#define CALL(NV) launch_flush_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, MODE_MATERIALIZE, nullptr, 0, out, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
 }

@@ -25,15 +25,20 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRows = 64;
 
-enum { PREC_F32 = 0, PREC_BF16 = 1, PREC_FP8 = 2, PREC_FP4 = 3 };
+// Read precisions of the replay kernels. PREC_F16 reads an fp16 master directly (no copy).
+enum { PREC_F32 = 0, PREC_BF16 = 1, PREC_FP8 = 2, PREC_FP4 = 3, PREC_F16 = 4 };
+
+// Master (checkpoint) precisions: fp32, or fp16 rounded to nearest even / stochastically.
+enum { MASTER_F32 = 0, MASTER_F16 = 1, MASTER_F16_SR = 2 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Everything a kernel needs to know about one layer's workspace (passed by value).
 struct Layer {
-    float *master;      // [Bt,H,P,N] fp32 checkpoint
+    float *master;      // [Bt,H,P,N] checkpoint: fp32, or fp16 (reinterpret) when mprec != 0
     void *rcopy;        // [Bt,H,P,N] bf16 / e4m3 read copy, or [Bt,H,P,N/2] MXFP4 bytes
     float *scale;       // [Bt,H] fp8 per-head scale
     unsigned char *mxscale;  // [Bt,H,P,N/32] MXFP4 E8M0 block-scale codes
@@ -48,6 +53,8 @@ struct Layer {
     const float *A;     // [H]
     const float *D;     // [H]
     int Bt, H, P, G, L, Tmax, hpg, psplit;
+    int mprec;          // MASTER_*
+    unsigned sr_seed;   // key of the stochastic-rounding stream
 };
 
 // Per-token inputs of one call (layouts in replayssm.h).
@@ -68,7 +75,7 @@ enum : unsigned { FLAG_POINTERS = 1u, FLAG_ACCEPTED = 2u };
 
 template <int N, int PREC>
 struct Geo {
-    static constexpr int VEC = PREC == PREC_F32 ? 4 : PREC == PREC_BF16 ? 8 : PREC == PREC_FP8 ? 16 : 32;
+    static constexpr int VEC = PREC == PREC_F32 ? 4 : (PREC == PREC_BF16 || PREC == PREC_F16) ? 8 : PREC == PREC_FP8 ? 16 : 32;
     static constexpr int LPR = N / VEC;          // lanes per row
     static constexpr int RPI = 64 / LPR;         // rows per wave instruction
     static constexpr int RPB = kWaves * RPI;     // rows per work-group instruction
@@ -150,6 +157,85 @@ __device__ inline float chunk_dot<PREC_BF16>(u32x4 v, const float *c)
     s = fmaf(bf16_hi(v.z), c[5], s);
     s = fmaf(bf16_lo(v.w), c[6], s);
     return fmaf(bf16_hi(v.w), c[7], s);
+}
+
+// fp16 (the master read directly): eight values per chunk, converted exactly.
+__device__ inline f32x2 f16x2_to_f32(unsigned w)
+{
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = __builtin_bit_cast(h2, w);
+    return f32x2{(float)h.x, (float)h.y};
+}
+
+template <>
+__device__ inline float chunk_dot<PREC_F16>(u32x4 v, const float *c)
+{
+    const unsigned w[4] = {v.x, v.y, v.z, v.w};
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x2 f = f16x2_to_f32(w[i]);
+        s = fmaf(f.x, c[2 * i], s);
+        s = fmaf(f.y, c[2 * i + 1], s);
+    }
+    return s;
+}
+
+// ------------------------------------------------------------------------------------------
+// fp16 master rounding. Nearest even by gfx950's converter (values clamped to +-65504 first).
+// Stochastic: with q the fp16 magnitude toward zero from |v| and ulp the spacing above it, round
+// up iff r24 < (|v| - q) / ulp * 2^24. Both factors are exact in fp32 (Sterbenz; scaling by a
+// power of two), so the decision is exact; the rounding is unbiased over r24 (to within 2^-24 of
+// a spacing for |v| < 2^-25, where the threshold is not an integer).
+// r24 = top 24 bits of Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2,
+// 3", SC'11) of counter (element / 4, sequence, new ckpt_pos, 0) and key (seed, 0); word
+// element % 4 (elements numbered h*P*N + p*N + n within the sequence).
+// ------------------------------------------------------------------------------------------
+__device__ inline unsigned short f16_bits(float v) { return __builtin_bit_cast(unsigned short, (_Float16)v); }
+__device__ inline float f16_value(unsigned short h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+__device__ inline unsigned short f16_rne(float v)
+{
+    return f16_bits(fminf(fmaxf(v, -65504.0f), 65504.0f));
+}
+
+__device__ inline unsigned short f16_sr(float v, unsigned r24)
+{
+    const float a = fminf(fabsf(v), 65504.0f);
+    unsigned short h = f16_bits(a);  // nearest even
+    float q = f16_value(h);
+    if (q > a) {
+        h = (unsigned short)(h - 1);
+        q = f16_value(h);
+    }
+    if (a > q) {
+        const float ulp = f16_value((unsigned short)(h + 1)) - q;
+        if ((float)r24 < (a - q) * (16777216.0f / ulp)) h = (unsigned short)(h + 1);
+    }
+    return (unsigned short)(h | (__float_as_uint(v) >> 31 << 15));
+}
+
+struct U32x4 {
+    unsigned x, y, z, w;
+};
+
+__device__ inline U32x4 philox4x32_10(unsigned c0, unsigned c1, unsigned c2, unsigned c3, unsigned k0, unsigned k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const unsigned hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+        const unsigned hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        const unsigned n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    return U32x4{c0, c1, c2, c3};
 }
 
 // e4m3 codes are decoded by gfx950's converter, two per instruction (OCP E4M3FN on this

@@ -29,7 +29,7 @@ using GF = Geo<NN, PREC_F32>;  // fp32 geometry (master tile, records)
 template <int PREC>
 constexpr size_t byte_off(size_t e)
 {
-    return PREC == PREC_F32 ? e * 4 : PREC == PREC_BF16 ? e * 2 : PREC == PREC_FP8 ? e : e / 2;
+    return PREC == PREC_F32 ? e * 4 : (PREC == PREC_BF16 || PREC == PREC_F16) ? e * 2 : PREC == PREC_FP8 ? e : e / 2;
 }
 
 // MXFP4 needs N >= 32 (a scale block is 32 consecutive n of one row).
@@ -381,6 +381,72 @@ __device__ inline void store_rows_f32(float *rows, const f32x4 (&vf)[GF::NL], in
     }
 }
 
+// Master rows in f32 geometry: fp32 16-byte loads, or fp16 8-byte loads converted exactly.
+__device__ inline void load_master_rows(const Layer &Ld, size_t elem0, f32x4 (&vf)[GF::NL], int nrows, int wave,
+                                        int lane)
+{
+    const int c = lane % GF::LPR;
+    if (Ld.mprec == MASTER_F32) {
+        u32x4 m[GF::NL];
+        load_rows<PREC_F32>(m, (const char *)(Ld.master + elem0), nrows, wave, lane);
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(m[i]);
+    } else {
+        const unsigned short *base = (const unsigned short *)Ld.master + elem0;
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            const int r = row_of<PREC_F32>(i, wave, lane);
+            if (r < nrows) {
+                const u32x2 w = __builtin_nontemporal_load((const u32x2 *)(base + (size_t)r * NN + 4 * c));
+                const f32x2 lo = f16x2_to_f32(w.x), hi = f16x2_to_f32(w.y);
+                vf[i] = f32x4{lo.x, lo.y, hi.x, hi.y};
+            } else {
+                vf[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    }
+}
+
+// Store master rows from fp32 values vf. An fp16 master rounds them -- to nearest even, or, when
+// `stochastic`, with the Philox stream of sequence b and new checkpoint position `newck` -- and vf
+// receives the stored values (the flush's output and the read copy come from the checkpoint as
+// stored).
+__device__ inline void store_master_rows(const Layer &Ld, int b, size_t elem0, int newck, bool stochastic,
+                                         f32x4 (&vf)[GF::NL], int nrows, int wave, int lane)
+{
+    if (Ld.mprec == MASTER_F32) {
+        store_rows_f32(Ld.master + elem0, vf, nrows, wave, lane);
+        return;
+    }
+    const int c = lane % GF::LPR;
+    unsigned short *base = (unsigned short *)Ld.master + elem0;
+    const size_t seq0 = (size_t)b * Ld.H * Ld.P * NN;
+#pragma unroll
+    for (int i = 0; i < GF::NL; ++i) {
+        const int r = row_of<PREC_F32>(i, wave, lane);
+        const f32x4 f = vf[i];
+        unsigned short h0, h1, h2, h3;
+        if (stochastic) {
+            const size_t e = elem0 - seq0 + (size_t)r * NN + 4 * c;  // element within the sequence
+            const U32x4 rnd = philox4x32_10((unsigned)(e / 4), (unsigned)b, (unsigned)newck, 0u, Ld.sr_seed, 0u);
+            h0 = f16_sr(f.x, rnd.x >> 8);
+            h1 = f16_sr(f.y, rnd.y >> 8);
+            h2 = f16_sr(f.z, rnd.z >> 8);
+            h3 = f16_sr(f.w, rnd.w >> 8);
+        } else {
+            h0 = f16_rne(f.x);
+            h1 = f16_rne(f.y);
+            h2 = f16_rne(f.z);
+            h3 = f16_rne(f.w);
+        }
+        vf[i] = f32x4{f16_value(h0), f16_value(h1), f16_value(h2), f16_value(h3)};
+        if (r < nrows) {
+            const u32x2 w = {(unsigned)h0 | ((unsigned)h1 << 16), (unsigned)h2 | ((unsigned)h3 << 16)};
+            __builtin_nontemporal_store(w, (u32x2 *)(base + (size_t)r * NN + 4 * c));
+        }
+    }
+}
+
 // Append one record (LDS row j of the window, C from Cq) into ring slot `slot`. The head's x
 // rows and dt are written by each (sequence, head) work-group (dt by split 0 only); B and C by
 // the split-0 work-group of the group's first head.
@@ -470,7 +536,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     // covers exactly the loads it needs. Lanes outside the tile load this tile's first row and
     // keep it: rows are independent in every use below, and those rows are never written.
     auto load_state = [&]() {
-        const char *base = PREC == PREC_F32 ? (const char *)Ld.master : (const char *)Ld.rcopy;
+        const char *base = (PREC == PREC_F32 || PREC == PREC_F16) ? (const char *)Ld.master : (const char *)Ld.rcopy;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int r = i * G::RPB + wave * G::RPI + lane / G::LPR;
@@ -485,7 +551,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     //    first, and the arguments are the same on every replay of a captured whole window.
     //    Otherwise: this sequence's device pointers, validated before any address is formed.
     const bool uni = ls.k > 0;
-    int pslot = 0, cslot = 0, k = 1;
+    int pslot = 0, cslot = 0, k = 1, dpos = 0;  // dpos: this sequence's pos (device-pointer mode)
     auto slot_of = [&](int j) { return (int)((unsigned)(cslot + j) % (unsigned)Ld.L); };  // record j
 
     // 3. Window loads into registers: x rows of every head, the group's B rows, this token's C,
@@ -556,6 +622,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         pslot = (int)((unsigned)pos % (unsigned)Ld.L);
         cslot = (int)((unsigned)ck % (unsigned)Ld.L);
         k = c0 + 1;  // records in the window, this token included
+        dpos = pos;
         issue_window();
     }
     const bool flush = k > Ld.L - Ld.Tmax;
@@ -626,8 +693,10 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     __syncthreads();
 
     if (FLUSH && flush) {
-        // Fused flush, head by head: fold all k records into the fp32 master rows, rewrite the
-        // read copy, and read y from the folded state.
+        // Fused flush, head by head: fold all k records into the master rows (in fp32), store
+        // them at the master's precision, rewrite the read copy, and read y from the stored state.
+        // (A stochastically rounded master always runs in device-pointer mode: its stream is
+        // keyed by the new ckpt_pos, pos + 1.)
         float cf[4];
         load_cchunk<PREC_F32>(cf, Ct, lane);
         for (int hh = 0; hh < HPB; ++hh) {
@@ -637,13 +706,10 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
 #pragma unroll
                 for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(v[i]);
             } else {
-                u32x4 m[GF::NL];
-                load_rows<PREC_F32>(m, (const char *)(Ld.master + elem0), t.nrows, wave, lane);
-#pragma unroll
-                for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(m[i]);
+                load_master_rows(Ld, elem0, vf, t.nrows, wave, lane);
             }
             fold_head<LMAX, ROWS>(vf, s.xw, s.Bw, s.w[hh], s.decay[hh], hh * kRows, k, wave, lane);
-            store_rows_f32(Ld.master + elem0, vf, t.nrows, wave, lane);
+            store_master_rows(Ld, t.b, elem0, dpos + 1, Ld.mprec == MASTER_F16_SR, vf, t.nrows, wave, lane);
             write_copy_rows<PREC>(Ld, bh0 + hh, elem0, vf, t.nrows, wave, lane, s.red);
             float part[GF::NL];
 #pragma unroll
@@ -999,8 +1065,8 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(Layer Ld, int mode, con
     else fold = true;
     if (!fold) return;  // pointers unchanged: no completion count needed
     {
-        u32x4 m[GF::NL];
-        load_rows<PREC_F32>(m, (const char *)(Ld.master + elem0), t.nrows, wave, lane);
+        f32x4 vf[GF::NL];
+        load_master_rows(Ld, elem0, vf, t.nrows, wave, lane);
         const RecSrc src = ring_src(Ld, t, ck, count);
         WindowRegs<LMAX> wr;
         issue_window<LMAX>(wr, src, count, t.nrows);
@@ -1008,14 +1074,11 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(Layer Ld, int mode, con
         __syncthreads();
         window_weights<LMAX, false>(s.win, nullptr, count - 1, Ld.A[t.h], s.w, nullptr, &s.decay);
         __syncthreads();
-        f32x4 vf[GF::NL];
-#pragma unroll
-        for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(m[i]);
         fold_head<LMAX, kRows>(vf, s.win.xw, s.win.Bw, s.w, s.decay, 0, count, wave, lane);
         if (mode == MODE_MATERIALIZE) {
             store_rows_f32(out + elem0, vf, t.nrows, wave, lane);
         } else {
-            store_rows_f32(Ld.master + elem0, vf, t.nrows, wave, lane);
+            store_master_rows(Ld, t.b, elem0, pos, Ld.mprec == MASTER_F16_SR, vf, t.nrows, wave, lane);
             write_copy_rows<PREC>(Ld, bh, elem0, vf, t.nrows, wave, lane, s.red);
         }
     }
@@ -1066,7 +1129,7 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh = (size_t)t.b * Ld.H + t.h;
     const size_t elem0 = (bh * Ld.P + t.row0) * NN;
-    const char *rbase = PREC == PREC_F32 ? (const char *)Ld.master : (const char *)Ld.rcopy;
+    const char *rbase = (PREC == PREC_F32 || PREC == PREC_F16) ? (const char *)Ld.master : (const char *)Ld.rcopy;
     u32x4 v[G::NL];
 #pragma unroll
     for (int i = 0; i < G::NL; ++i) {
@@ -1214,7 +1277,7 @@ __global__ void __launch_bounds__(kThreads) load_state_kernel(Layer Ld, const fl
     f32x4 vf[GF::NL];
 #pragma unroll
     for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(m[i]);
-    store_rows_f32(Ld.master + elem0, vf, t.nrows, wave, lane);
+    store_master_rows(Ld, t.b, elem0, 0, false, vf, t.nrows, wave, lane);  // fp16: nearest even at load
     write_copy_rows<PREC>(Ld, bh, elem0, vf, t.nrows, wave, lane, red);
     if (t.h == 0 && t.split == 0 && threadIdx.x == 0) {
         Ld.pos[t.b] = 0;
@@ -1353,7 +1416,7 @@ hipError_t step_rows(const Layer &Ld, const TokenIO &io, Lockstep ls, hipStream_
 template <int PREC, int LMAX>
 hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockstep ls, hipStream_t st)
 {
-    constexpr int wide = PREC == PREC_F32 ? 1 : PREC == PREC_BF16 ? 2 : 4;  // fp8 and fp4: 4
+    constexpr int wide = PREC == PREC_F32 ? 1 : (PREC == PREC_BF16 || PREC == PREC_F16) ? 2 : 4;  // fp8, fp4: 4
     if (flush_capable) return step_rows<PREC, LMAX, kRows, true>(Ld, io, ls, st);
     if constexpr ((PREC == PREC_FP8 || PREC == PREC_FP4) && LMAX == 16 && NN <= 128) {
         // one row per lane: P <= 64, four heads of one group per work-group; at N = 256 a row's
@@ -1413,6 +1476,9 @@ hipError_t by_prec_lmax(int prec, int lmax, Args... args)
     case PREC_FP4 * 100 + 16: return F<PREC_FP4, 16>::run(args...);
     case PREC_FP4 * 100 + 32: return F<PREC_FP4, 32>::run(args...);
     case PREC_FP4 * 100 + 64: return F<PREC_FP4, 64>::run(args...);
+    case PREC_F16 * 100 + 16: return F<PREC_F16, 16>::run(args...);
+    case PREC_F16 * 100 + 32: return F<PREC_F16, 32>::run(args...);
+    case PREC_F16 * 100 + 64: return F<PREC_F16, 64>::run(args...);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1482,6 +1548,7 @@ hipError_t RSSM_CAT(launch_load_n, RSSM_N)(int prec, const Layer &Ld, const floa
     case PREC_BF16: return load_p<PREC_BF16>(Ld, state, st);
     case PREC_FP8: return load_p<PREC_FP8>(Ld, state, st);
     case PREC_FP4: return load_p<PREC_FP4>(Ld, state, st);
+    case PREC_F16: return load_p<PREC_F16>(Ld, state, st);
     default: return hipErrorInvalidValue;
     }
 }

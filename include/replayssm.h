@@ -85,6 +85,21 @@ typedef enum {
     RSSM_READ_MXFP4 = 3
 } rssm_read_prec;
 
+/* Precision the checkpoint (master) is kept in ([AT Pulse] "Capabilities and access" and "Claims
+ * and evidence": the pages pair 4-bit reads with an FP16 recurrence with stochastic rounding).
+ *   FP32     the default.
+ *   FP16     IEEE binary16, rounded to nearest even at load and at every flush (values clamped to
+ *            +-65504). Reads with read_prec FP32 then come from the fp16 master itself.
+ *   FP16_SR  as FP16 at load; at every flush each value rounds stochastically: with q the fp16
+ *            magnitude toward zero and ulp the spacing above it, up iff r < (|v| - q) / ulp * 2^24,
+ *            r = top 24 bits of word (e mod 4) of Philox4x32-10 (Salmon et al., SC'11) with counter
+ *            (e / 4, sequence, new ckpt_pos, 0) and key (sr_seed, 0), e = h*P*N + p*N + n.
+ *            Unbiased over r (to 2^-24 of a spacing below 2^-25); deterministic for a given
+ *            seed. Standard steps use the device pointers (the lockstep fast path is off) so
+ *            that every flush knows its ckpt_pos.
+ * The stored layout stays [Bt,H,P,N]; RSSM_E_INVAL for a value outside 0..2. */
+typedef enum { RSSM_MASTER_FP32 = 0, RSSM_MASTER_FP16 = 1, RSSM_MASTER_FP16_SR = 2 } rssm_master_prec;
+
 typedef struct {
     int32_t batch;       /* Bt >= 0 (0: every call is a no-op) */
     int32_t nheads;      /* H */
@@ -95,11 +110,13 @@ typedef struct {
     int32_t max_draft;   /* T_max: 1 = standard decode only; >1 enables spec verify/rollback */
     int32_t read_prec;   /* rssm_read_prec: precision of the checkpoint copy that serves reads */
     int32_t store_C;     /* 1: records also keep C (the record is (x, B, C, dt)); 0: (x, B, dt) */
+    int32_t master_prec; /* rssm_master_prec: precision of the checkpoint itself */
+    int32_t sr_seed;     /* key of the stochastic-rounding stream (RSSM_MASTER_FP16_SR) */
 } replayssm_config;
 
 /* Byte offsets of the workspace regions (for inspection by tests and tools). */
 typedef struct {
-    size_t master;     /* fp32 checkpoint [Bt,H,P,N] -- updated only by flushes */
+    size_t master;     /* checkpoint [Bt,H,P,N], fp32 or fp16 (master_prec) -- updated only by flushes */
     size_t read_copy;  /* bf16 [Bt,H,P,N] row-major; fp8 e4m3fn codes or MXFP4 code bytes in
                           16-byte chunks (16 fp8 / 32 fp4 values of one row), per head ordered
                           [N/VEC][P]: chunk q of row p of head (b,h) at byte offset

@@ -73,6 +73,8 @@ def lib():
         L.oracle_f16_decode.restype = ctypes.c_float
         L.oracle_encode_f16.argtypes = [_f32p, _u16p, _sz, _i, ctypes.c_void_p]
         L.oracle_replay_create.restype = ctypes.c_void_p
+        L.oracle_replay_set_seq_ids.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]
+        L.oracle_replay_set_seq_ids.restype = None
         L.oracle_replay_destroy.argtypes = [ctypes.c_void_p]
         L.oracle_replay_step.argtypes = [ctypes.c_void_p, _f32p, _f32p, _f32p, _f32p, _f64p]
         L.oracle_replay_step.restype = _i
@@ -148,7 +150,10 @@ MASTER_FP32, MASTER_FP16, MASTER_FP16_SR = 0, 1, 2
 class Replay:
     """O3 + O4: the replay form (checkpoint + records) with its pointer and flush machine."""
 
-    def __init__(self, S0, A, D, G, L, Tmax=1, read_prec=READ_FP32, master_prec=MASTER_FP32, seed=0):
+    def __init__(self, S0, A, D, G, L, Tmax=1, read_prec=READ_FP32, master_prec=MASTER_FP32, seed=0,
+                 seq_ids=None):
+        """seq_ids: the batch index each row of S0 stands for (default 0..Bt-1); it enters only
+        the stochastic-rounding counter, so rows sampled from a larger batch round as there."""
         S0 = _f32(S0)
         self.Bt, self.H, self.P, self.N = S0.shape
         self.G, self.L, self.Tmax = G, L, Tmax
@@ -156,6 +161,11 @@ class Replay:
                                              read_prec, S0, _f32(A), _f32(D), int(master_prec), int(seed))
         if not self._h:
             raise ValueError("invalid replay configuration")
+        if seq_ids is not None:
+            ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+            if ids.shape != (self.Bt,) or np.any(ids < 0):
+                raise ValueError("seq_ids must hold Bt non-negative indices")
+            lib().oracle_replay_set_seq_ids(self._h, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
 
     def __del__(self):
         if getattr(self, "_h", None):

@@ -440,6 +440,7 @@ typedef struct oracle_replay {
     int Bt, H, P, N, G, L, Tmax, read_prec; /* 0 fp32 master, 1 bf16, 2 fp8 e4m3, 3 mxfp4 */
     int master_prec;                        /* 0 fp32, 1 fp16 nearest even, 2 fp16 stochastic (R8) */
     uint32_t seed;
+    int *seq_id;                            /* [Bt] sequence index in the Philox counter */
     double *A, *D;                          /* [H] */
     double *ckpt;                           /* [Bt,H,P,N] master */
     double *rcopy;                          /* [Bt,H,P,N] decoded read copy (read_prec != 0) */
@@ -480,7 +481,7 @@ static void round_master(oracle_replay *r, int b, int ck, int stochastic)
     for (size_t e = 0; e < n; e += 4) {
         uint32_t words[4] = {0, 0, 0, 0};
         if (r->master_prec == 2 && stochastic) {
-            const uint32_t ctr[4] = {(uint32_t)(e / 4), (uint32_t)b, (uint32_t)ck, 0u};
+            const uint32_t ctr[4] = {(uint32_t)(e / 4), (uint32_t)r->seq_id[b], (uint32_t)ck, 0u};
             const uint32_t key[2] = {r->seed, 0u};
             oracle_philox4x32_10(ctr, key, words);
         }
@@ -551,13 +552,23 @@ oracle_replay *oracle_replay_create(int Bt, int H, int P, int N, int G, int L, i
     r->rdt = (float *)malloc(((size_t)Bt * L * H + 1) * sizeof(float));
     r->pos = (int *)calloc(Bt + 1, sizeof(int));
     r->ckpt_pos = (int *)calloc(Bt + 1, sizeof(int));
+    r->seq_id = (int *)calloc(Bt + 1, sizeof(int));
+    for (int b = 0; b < Bt; ++b) r->seq_id[b] = b;
     for (int b = 0; b < Bt; ++b) { round_master(r, b, 0, 0); poison_records(r, b, 0); refresh_copy(r, b); }
     return r;
+}
+
+/* Stand the oracle's rows for sequences ids[0..Bt) of a larger batch: only the stochastic   */
+/* rounding stream depends on a sequence's index, so a sample of a batch is modelled exactly. */
+void oracle_replay_set_seq_ids(oracle_replay *r, const int *ids)
+{
+    for (int b = 0; b < r->Bt; ++b) r->seq_id[b] = ids[b];
 }
 
 void oracle_replay_destroy(oracle_replay *r)
 {
     if (!r) return;
+    free(r->seq_id);
     free(r->A); free(r->D); free(r->ckpt); free(r->rcopy);
     free(r->rx); free(r->rB); free(r->rC); free(r->rdt); free(r->pos); free(r->ckpt_pos);
     free(r);

@@ -11,6 +11,7 @@ import workload
 
 PREC_CODE = {"fp32": oracle.READ_FP32, "bf16": oracle.READ_BF16, "fp8": oracle.READ_FP8,
              "mxfp4": oracle.READ_MXFP4}
+MASTER_CODE = {"fp32": oracle.MASTER_FP32, "fp16": oracle.MASTER_FP16, "fp16_sr": oracle.MASTER_FP16_SR}
 
 _GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "mxfp4_codes.json")
 with open(_GOLDEN) as _f:
@@ -74,10 +75,10 @@ class Case:
     def draft_inputs(self, t, T):
         return workload.draft_inputs(self.seed, t, self.Bt, T, self.H, self.P, self.N, self.G)
 
-    def layer(self, read_prec="fp32", store_C=True, Tmax=None):
+    def layer(self, read_prec="fp32", store_C=True, Tmax=None, master_prec="fp32", sr_seed=0):
         import hybrid_mamba_decode_amd as rs
         lay = rs.ReplaySSM(self.Bt, self.H, self.P, self.N, self.G, dev(self.A), dev(self.D),
                            buffer_len=self.L, max_draft=Tmax or self.Tmax, read_prec=read_prec,
-                           store_C=store_C)
+                           store_C=store_C, master_prec=master_prec, sr_seed=sr_seed)
         lay.load_state(dev(self.S0))
         return lay

@@ -61,6 +61,11 @@ def test_workspace_layout_serving_shape():
     lb = rs.replayssm_workspace_layout(cb)
     assert lb.scale - lb.read_copy == Bt * H * P * N * 2
     assert lb.ring_C == lb.ring_dt                               # no C in the records
+    ch = cfg(batch=256, master_prec="fp16_sr", read_prec="bf16")
+    lh = rs.replayssm_workspace_layout(ch)
+    assert lh.read_copy - lh.master == Bt * H * P * N * 2          # fp16 master
+    assert lh.scale - lh.read_copy == Bt * H * P * N * 2
+    assert lh.total < lb.total + Bt * H * P * N * 4
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -78,6 +83,8 @@ def test_workspace_layout_serving_shape():
     (dict(read_prec="mxfp4", dstate=16), rs.RSSM_E_UNSUPPORTED),
     (dict(batch=-1), rs.RSSM_E_INVAL),
     (dict(store_C=2), rs.RSSM_E_INVAL),
+    (dict(master_prec=3), rs.RSSM_E_INVAL),
+    (dict(master_prec=-1), rs.RSSM_E_INVAL),
 ])
 def test_invalid_configs_rejected(kw, status):
     c = cfg(**kw)

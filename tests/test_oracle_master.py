@@ -124,3 +124,23 @@ def test_fp16_master_dual_model():
     want = oracle.f16_decode(oracle.f16_encode(flat, words >> 8)).astype(np.float64).reshape(S0.shape)
     assert np.array_equal(sr.checkpoint(), want)
     assert not np.array_equal(sr.checkpoint(), rne.checkpoint())
+
+
+def test_sampled_rows_round_as_in_the_full_batch():
+    """A replay over rows [2, 0] of a batch, told their batch indices, rounds stochastically
+    exactly as those rows of the full-batch replay; without the indices it does not."""
+    Bt, H, P, N, G, L = 3, 2, 8, 16, 1, 3
+    seed = 23
+    S0 = workload.initial_state(seed, Bt, H, P, N)
+    A, D = workload.layer_params(seed, H)
+    rows = np.array([2, 0])
+    full = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP16_SR, seed=5)
+    part = oracle.Replay(S0[rows], A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP16_SR, seed=5, seq_ids=rows)
+    blind = oracle.Replay(S0[rows], A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP16_SR, seed=5)
+    for t in range(2 * L):
+        x, B, C, dt = workload.step_inputs(seed, t, Bt, H, P, N, G)
+        y = full.step(x, B, C, dt)
+        assert np.array_equal(part.step(x[rows], B[rows], C[rows], dt[rows]), y[rows])
+        blind.step(x[rows], B[rows], C[rows], dt[rows])
+    assert np.array_equal(part.checkpoint(), full.checkpoint()[rows])
+    assert not np.array_equal(blind.checkpoint(), full.checkpoint()[rows])
