@@ -11,7 +11,7 @@ per launch / its mean duration from HIP events on the launch stream), the same-r
 read-update-write step, and the float64 CPU oracle timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--read-prec fp32|bf16|fp8|mxfp4]
-                  [--no-cpu-baseline] [--kernels-only]
+                  [--master-prec fp32|fp16|fp16_sr] [--no-cpu-baseline] [--kernels-only]
 """
 import argparse
 import json
@@ -25,7 +25,7 @@ HBM_PEAK_GBPS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
-def measured_traffic(prec):
+def measured_traffic(key):
     """HBM bytes per non-flush replay launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     runs (profiles/traffic_counters.json), or None when the kernel sources changed since."""
     import hashlib
@@ -34,9 +34,9 @@ def measured_traffic(prec):
         csrc = os.path.join(ROOT, "hybrid_mamba_decode_amd", "csrc")
         h = hashlib.sha256(open(os.path.join(csrc, "kernels.hip"), "rb").read() +
                            open(os.path.join(csrc, "device.h"), "rb").read()).hexdigest()[:16]
-        if h != rec["kernel_source_sha256_16"] or prec not in rec["kernels"]:
+        if h != rec["kernel_source_sha256_16"] or key not in rec["kernels"]:
             return None
-        k = rec["kernels"][prec]
+        k = rec["kernels"][key]
         return {"bytes_per_launch": k["read_bytes_per_launch"] + k["write_bytes_per_launch"],
                 "over_algorithmic": k["traffic_over_alg"]}
     except (OSError, KeyError, ValueError):
@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--read-prec", default="fp32", choices=["fp32", "bf16", "fp8", "mxfp4"])
+    ap.add_argument("--master-prec", default="fp32", choices=["fp32", "fp16", "fp16_sr"],
+                    help="checkpoint precision: fp16 rounds to nearest even at each flush, fp16_sr "
+                         "stochastically")
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--buffer-len", type=int, default=16)
     ap.add_argument("--pool", type=int, default=32, help="distinct input sets cycled through")
@@ -85,6 +88,10 @@ def main():
     H, P, N, G = 128, 64, 128, 8
     Bt, L = args.batch, args.buffer_len
     prec = args.read_prec
+    mprec = args.master_prec
+    mstore = "fp32" if mprec == "fp32" else "fp16"
+    src = traffic.read_source(prec, mstore)            # precision the replay reads the state in
+    tkey = prec if mprec == "fp32" else f"{prec}+master_{mprec}"
     seed = workload.config_seed(1)
     A, D = workload.layer_params(seed, H)
     S0 = workload.initial_state(seed, Bt, H, P, N)
@@ -94,7 +101,8 @@ def main():
     pool = [tuple(dev(a) for a in workload.step_inputs(seed, t, Bt, H, P, N, G)) for t in range(args.pool)]
     y = torch.empty(Bt, H, P, device="cuda")
 
-    lay = rs.ReplaySSM(Bt, H, P, N, G, A_d, D_d, buffer_len=L, read_prec=prec)
+    lay = rs.ReplaySSM(Bt, H, P, N, G, A_d, D_d, buffer_len=L, read_prec=prec, master_prec=mprec,
+                       sr_seed=seed & 0x7FFFFFFF)
     lay.load_state(S0_d)
     stream = torch.cuda.current_stream()
 
@@ -123,12 +131,12 @@ def main():
     durs = np.array([ev0[k].elapsed_time(ev1[k]) * 1e-3 for k in range(K)])   # seconds
     ks = np.array([(k % L) + 1 for k in range(K)])      # records in the window incl. this token
     is_flush = ks == L
-    bytes_nf = np.array([traffic.replay_nonflush(H, P, N, G, int(kk), prec) * Bt for kk in ks])
-    bytes_fl = traffic.replay_flush_step(H, P, N, G, L, prec) * Bt
+    bytes_nf = np.array([traffic.replay_nonflush(H, P, N, G, int(kk), src) * Bt for kk in ks])
+    bytes_fl = traffic.replay_flush_step(H, P, N, G, L, prec, mstore) * Bt
     nf = ~is_flush
     nf_gbps = bytes_nf[nf].sum() / durs[nf].sum() / 1e9
     fl_gbps = (bytes_fl * is_flush.sum()) / durs[is_flush].sum() / 1e9 if is_flush.any() else None
-    amort_bytes = traffic.replay_window_amortized(H, P, N, G, L, prec) * Bt
+    amort_bytes = traffic.replay_window_amortized(H, P, N, G, L, prec, master=mstore) * Bt
     value = Bt * K / wall
 
     result = {
@@ -142,12 +150,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if prec == "fp32" else f"f32 master + {prec} read copy",
+        "dtype": ("f32" if mprec == "fp32" else "f16") + (" master" if prec != "fp32" or mprec != "fp32" else "")
+                 + ("" if prec == "fp32" else f" + {prec} read copy"),
         "data": "synthetic (seeded; value distributions of the layer definition)",
         "config": {"workload": f"one Mamba-2 layer decode step, batch {Bt}, 128 heads, headdim 64, "
                                f"state 128 (4 MiB fp32/sequence), 8 groups, buffer length {L}, "
-                               f"{prec} read path",
-                   "batch": Bt, "buffer_len": L, "read_prec": prec},
+                               f"{prec} read path" + ("" if mprec == "fp32" else f", {mprec} master"),
+                   "batch": Bt, "buffer_len": L, "read_prec": prec, "master_prec": mprec},
         "roofline": {
             "kernel": "replay step, non-flush (step_kernel<prec, L bucket 16, rows, false>)",
             "bound": "hbm",
@@ -155,7 +164,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(nf_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(prec),
+            "traffic": measured_traffic(tkey),
             "mean_launch_us": round(float(durs[nf].mean()) * 1e6, 2),
             "alg_bytes_per_launch": int(bytes_nf[nf].mean()),
         },

@@ -202,6 +202,14 @@ __device__ inline unsigned short f16_rne(float v)
 __device__ inline unsigned short f16_sr(float v, unsigned r24)
 {
     const float a = fminf(fabsf(v), 65504.0f);
+    if (a >= 0x1p-14f) {
+        // fp16 normal range: the spacing is 2^13 fp32 spacings of a and |v| - q is the low 13 bits
+        // of a's encoding (low13 of them), so the rule reads r24 < low13 * 2^11, i.e.
+        // (r24 >> 11) < low13: adding 2^13 - 1 - (r24 >> 11) to the encoding carries into bit 13
+        // exactly then; the truncated sum is the chosen fp16 value, converted exactly.
+        const unsigned u = (__float_as_uint(a) + (0x1FFFu - (r24 >> 11))) & ~0x1FFFu;
+        return (unsigned short)(f16_bits(__uint_as_float(u)) | (__float_as_uint(v) >> 31 << 15));
+    }
     unsigned short h = f16_bits(a);  // nearest even
     float q = f16_value(h);
     if (q > a) {
@@ -227,13 +235,14 @@ __device__ inline U32x4 philox4x32_10(unsigned c0, unsigned c1, unsigned c2, uns
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const unsigned hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-        const unsigned hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
-        const unsigned n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        // one 32x32 -> 64-bit multiply per product (v_mad_u64_u32), high and low halves
+        const unsigned long long p0 = (unsigned long long)0xD2511F53u * c0;
+        const unsigned long long p1 = (unsigned long long)0xCD9E8D57u * c2;
+        const unsigned n0 = (unsigned)(p1 >> 32) ^ c1 ^ k0, n2 = (unsigned)(p0 >> 32) ^ c3 ^ k1;
         c0 = n0;
-        c1 = lo1;
+        c1 = (unsigned)p1;
         c2 = n2;
-        c3 = lo0;
+        c3 = (unsigned)p0;
     }
     return U32x4{c0, c1, c2, c3};
 }

@@ -554,6 +554,25 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     int pslot = 0, cslot = 0, k = 1, dpos = 0;  // dpos: this sequence's pos (device-pointer mode)
     auto slot_of = [&](int j) { return (int)((unsigned)(cslot + j) % (unsigned)Ld.L); };  // record j
 
+    // Two-head flush launches serve fp16 masters only (the host picks them so). Both heads' master
+    // rows (8 bytes per lane and slot, in the fold's geometry) are issued as soon as the window
+    // position says this step flushes, ahead of the window loads: a work-group then has as many
+    // checkpoint bytes in flight as one fp32 head gives.
+    constexpr bool kHalfPre = FLUSH && HPB == 2;
+    u32x2 mh[kHalfPre ? HPB : 1][GF::NL];
+    auto load_master_half = [&]() {
+        const int cf4 = lane % GF::LPR;
+#pragma unroll
+        for (int hh = 0; hh < (kHalfPre ? HPB : 1); ++hh)
+#pragma unroll
+            for (int i = 0; i < GF::NL; ++i) {
+                const int r = row_of<PREC_F32>(i, wave, lane), rr = r < t.nrows ? r : 0;
+                const unsigned short *src =
+                    (const unsigned short *)Ld.master + ((bh0 + hh) * Ld.P + t.row0 + rr) * NN + 4 * cf4;
+                mh[hh][i] = __builtin_nontemporal_load((const u32x2 *)src);
+            }
+    };
+
     // 3. Window loads into registers: x rows of every head, the group's B rows, this token's C,
     //    and (wave w, lane j) <- dt_j of head w.
     constexpr int XS = (LMAX * ROWS / 4 + kThreads - 1) / kThreads;
@@ -607,6 +626,8 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         pslot = ls.pslot;
         cslot = ls.cslot;
         k = ls.k;
+        if constexpr (kHalfPre)
+            if (k > Ld.L - Ld.Tmax) load_master_half();
         issue_window();
         if (kPreload) load_state();
     } else {
@@ -623,6 +644,8 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         cslot = (int)((unsigned)ck % (unsigned)Ld.L);
         k = c0 + 1;  // records in the window, this token included
         dpos = pos;
+        if constexpr (kHalfPre)
+            if (k > Ld.L - Ld.Tmax) load_master_half();
         issue_window();
     }
     const bool flush = k > Ld.L - Ld.Tmax;
@@ -699,12 +722,19 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         // keyed by the new ckpt_pos, pos + 1.)
         float cf[4];
         load_cchunk<PREC_F32>(cf, Ct, lane);
+#pragma unroll
         for (int hh = 0; hh < HPB; ++hh) {
             f32x4 vf[GF::NL];
             const size_t elem0 = ((bh0 + hh) * Ld.P + t.row0) * NN;
             if constexpr (kPreload) {
 #pragma unroll
                 for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(v[i]);
+            } else if constexpr (kHalfPre) {
+#pragma unroll
+                for (int i = 0; i < GF::NL; ++i) {
+                    const f32x2 lo = f16x2_to_f32(mh[hh][i].x), hi = f16x2_to_f32(mh[hh][i].y);
+                    vf[i] = f32x4{lo.x, lo.y, hi.x, hi.y};
+                }
             } else {
                 load_master_rows(Ld, elem0, vf, t.nrows, wave, lane);
             }
@@ -1412,12 +1442,20 @@ hipError_t step_rows(const Layer &Ld, const TokenIO &io, Lockstep ls, hipStream_
 // transpose-reduce needs at most LPR load slots per lane), when the head tile fits one work-group
 // (P <= 64), the group divides evenly, the launch keeps at least 2048 work-groups (8 per CU) and
 // the window bucket is at most 32 (at 64 the x window of four heads fills 100 KiB of LDS).
-// Flush-capable launches use one head per work-group (their fold loop is per head).
+// Flush-capable launches use one head per work-group (their fold loop is per head), except with an
+// fp16 master: a head's fp16 rows are half the bytes, so two heads per work-group with their rows
+// issued together keep the flush's bytes in flight (one head each: 2.6 TB/s on the flush step).
 template <int PREC, int LMAX>
 hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockstep ls, hipStream_t st)
 {
     constexpr int wide = PREC == PREC_F32 ? 1 : (PREC == PREC_BF16 || PREC == PREC_F16) ? 2 : 4;  // fp8, fp4: 4
-    if (flush_capable) return step_rows<PREC, LMAX, kRows, true>(Ld, io, ls, st);
+    if (flush_capable) {
+        // fp16 master: two heads per work-group with the master rows issued early (see step_kernel)
+        if constexpr (LMAX <= 32)
+            if (Ld.mprec != MASTER_F32 && Ld.psplit == 1 && Ld.hpg % 2 == 0)
+                return step_rows<PREC, LMAX, 2 * kRows, true>(Ld, io, ls, st);
+        return step_rows<PREC, LMAX, kRows, true>(Ld, io, ls, st);
+    }
     if constexpr ((PREC == PREC_FP8 || PREC == PREC_FP4) && LMAX == 16 && NN <= 128) {
         // one row per lane: P <= 64, four heads of one group per work-group; at N = 256 a row's
         // chunks would hold 64 (fp8) registers per lane

@@ -6,11 +6,17 @@ input read once, every record written once and every stored record the window ne
 and the per-head fp8 scales of a read are tiny and are counted where they are part of the format.
 
 Shapes: H heads, P headdim, N state, G groups; `k` = records in the window including the current
-token (1..L).
+token (1..L). `prec` is the precision reads come from (the read copy's, or the master's when reads
+use no copy) and `master` the checkpoint's own ("fp32" or "fp16").
 """
 
 F32 = 4
-ELEM = {"fp32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5}
+ELEM = {"fp32": 4, "fp16": 2, "bf16": 2, "fp8": 1, "mxfp4": 0.5}
+
+
+def read_source(read_prec, master="fp32"):
+    """Precision a replay reads the state in: the copy's, or the master's when there is no copy."""
+    return master if read_prec == "fp32" else read_prec
 
 
 def state_bytes(H, P, N, prec="fp32"):
@@ -48,18 +54,20 @@ def replay_nonflush(H, P, N, G, k, prec="fp32", store_C=True):
             (k - 1) * record_read_bytes(H, P, N, G))
 
 
-def replay_flush_step(H, P, N, G, L, prec="fp32"):
-    """Fused flush step: read the fp32 master, write it and the read copy; read the L-1 stored
-    records and this token's inputs; write y. The token's record is folded, not stored."""
+def replay_flush_step(H, P, N, G, L, prec="fp32", master="fp32"):
+    """Fused flush step: read the master, write it and the read copy (`prec` here is the copy's
+    precision, "fp32" for none); read the L-1 stored records and this token's inputs; write y.
+    The token's record is folded, not stored."""
     copy = 0 if prec == "fp32" else state_bytes(H, P, N, prec)
-    return (2 * state_bytes(H, P, N, "fp32") + copy + token_input_bytes(H, P, N, G) +
+    return (2 * state_bytes(H, P, N, master) + copy + token_input_bytes(H, P, N, G) +
             output_bytes(H, P) + (L - 1) * record_read_bytes(H, P, N, G))
 
 
-def replay_window_amortized(H, P, N, G, L, prec="fp32", store_C=True):
+def replay_window_amortized(H, P, N, G, L, prec="fp32", store_C=True, master="fp32"):
     """Mean bytes per step over one window of L steps (L-1 non-flush steps + 1 flush step)."""
-    tot = sum(replay_nonflush(H, P, N, G, k, prec, store_C) for k in range(1, L))
-    return (tot + replay_flush_step(H, P, N, G, L, prec)) / L
+    src = read_source(prec, master)
+    tot = sum(replay_nonflush(H, P, N, G, k, src, store_C) for k in range(1, L))
+    return (tot + replay_flush_step(H, P, N, G, L, prec, master)) / L
 
 
 def conventional(H, P, N, G):
@@ -74,10 +82,10 @@ def verify(H, P, N, G, T, k_old, prec="fp32", store_C=True):
             k_old * record_read_bytes(H, P, N, G))
 
 
-def rollback_flush(H, P, N, G, count, prec="fp32"):
+def rollback_flush(H, P, N, G, count, prec="fp32", master="fp32"):
     """Commit-time flush of `count` records (master read + write, read copy write)."""
     copy = 0 if prec == "fp32" else state_bytes(H, P, N, prec)
-    return 2 * state_bytes(H, P, N, "fp32") + copy + count * record_read_bytes(H, P, N, G)
+    return 2 * state_bytes(H, P, N, master) + copy + count * record_read_bytes(H, P, N, G)
 
 
 def snapshot_verify(H, P, N, G, T):
