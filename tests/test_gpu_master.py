@@ -208,3 +208,24 @@ def test_fp16_sr_master_graph_replay_matches_eager():
         assert gl.get_pointers() == ([(r + 1) * L] * Bt, [(r + 1) * L] * Bt)
         _ = torch.ones(1 << 20, device="cuda").sum().item()
     assert gl.check() == rs.RSSM_OK and el.check() == rs.RSSM_OK
+
+
+def test_fp16_sr_master_avoids_stagnation():
+    """Increments of a sixteenth of a spacing per flush (decay 1, exact arithmetic; the oracle
+    test of the same case pins the statistics): the nearest-even master stays exactly 1.0 and the
+    stochastic one equals the oracle's codes bit for bit after every flush."""
+    (Bt, H, P, N, G, L), S0, A, D, tok = workload.stagnation_case()
+    lays = {m: rs.ReplaySSM(Bt, H, P, N, G, dev(A), dev(D), buffer_len=L, master_prec=m, sr_seed=9)
+            for m in ("fp16", "fp16_sr")}
+    for lay in lays.values():
+        lay.load_state(dev(S0))
+    sr = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP16_SR, seed=9)
+    toks = tuple(dev(a) for a in tok)
+    for t in range(32 * L):
+        for lay in lays.values():
+            lay.step(*toks)
+        sr.step(*tok)
+        if (t + 1) % L == 0:
+            assert np.array_equal(host(lays["fp16_sr"].master()).astype(np.float64), sr.checkpoint()), f"flush at {t}"
+    assert bool((lays["fp16"].master() == 1.0).all())
+    assert float(host(lays["fp16_sr"].master()).astype(np.float64).mean()) > 1.0 + 16 * 2.0 ** -14

@@ -144,3 +144,51 @@ def test_sampled_rows_round_as_in_the_full_batch():
         blind.step(x[rows], B[rows], C[rows], dt[rows])
     assert np.array_equal(part.checkpoint(), full.checkpoint()[rows])
     assert not np.array_equal(blind.checkpoint(), full.checkpoint()[rows])
+
+
+def test_stochastic_rounding_avoids_stagnation():
+    """workload.stagnation_case: increments of a sixteenth of fp16's spacing per flush (exact in
+    float32 and float64). Nearest even loses every one (the checkpoint stays 1.0),
+    stochastic rounding keeps them in expectation -- after 64 flushes the mean checkpoint is
+    within 10 standard deviations (binomial, p = 1/16 per flush and value) of 1 + 64 * 2^-14."""
+    (Bt, H, P, N, G, L), S0, A, D, tok = workload.stagnation_case()
+    rne = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP16)
+    sr = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP16_SR, seed=9)
+    flushes = 64
+    for _ in range(flushes * L):
+        rne.step(*tok)
+        sr.step(*tok)
+    assert np.all(rne.checkpoint() == 1.0)
+    truth = 1.0 + flushes * 2.0 ** -14
+    m = sr.checkpoint()
+    assert set(np.unique(m)) <= {1.0 + i * 2.0 ** -10 for i in range(flushes + 1)}
+    sd = 2.0 ** -10 * np.sqrt(flushes * (1 / 16) * (15 / 16) / m.size)
+    assert abs(float(m.mean()) - truth) <= 10 * sd
+
+
+@pytest.mark.parametrize("master", [oracle.MASTER_FP16, oracle.MASTER_FP16_SR])
+def test_rounding_at_flushes_only_compounds_less(master):
+    """[Clarity] "Why it matters": a state written on fewer steps gives its rounding error fewer
+    chances to re-enter the recurrence. With the same fp16 state, the replay form at L = 1 rounds
+    on every step (the conventional step) and at L = 16 on every 16th: over 128 steps its rms
+    state and output errors against float64 must be well below (here < 0.6x; measured 0.25-0.39x
+    over seeds) those of rounding every step."""
+    Bt, H, P, N, G = 2, 4, 16, 32, 2
+    seed = 4
+    A, D = workload.layer_params(seed, H)
+    S0 = workload.initial_state(seed, Bt, H, P, N)
+
+    def rms(a, ref):
+        return float(np.sqrt(np.mean((a - ref) ** 2)) / np.sqrt(np.mean(ref ** 2)))
+
+    res = {}
+    for L in (1, 16):
+        r = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, master, seed=5)
+        S = S0.astype(np.float64)
+        errs = []
+        for t in range(128):
+            ins = workload.step_inputs(seed, t, Bt, H, P, N, G)
+            y_true = oracle.step(S, *ins, A, D)
+            errs.append(rms(r.step(*ins), y_true))
+        res[L] = (rms(r.materialize(), S), float(np.mean(errs)))
+    assert res[16][0] < 0.6 * res[1][0] and res[16][1] < 0.6 * res[1][1], res

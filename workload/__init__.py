@@ -125,3 +125,19 @@ SWEEP = dict(H=128, P=64, N=128, G=8, batches=(1, 8, 64, 256, 512), Ls=(4, 8, 16
 GDN_TINY = dict(Bt=2, H=4, G=2, Dv=16, Dk=32, L=4, steps=64)
 GDN_SERVING = dict(Bt=256, H=32, G=16, Dv=128, Dk=128, L=16, steps=64)
 GDN_SPEC = dict(Bt=512, H=32, G=16, Dv=128, Dk=128, L=16, T=4, steps=64)
+
+
+def stagnation_case():
+    """Constant inputs for the master-precision stagnation case: decay 1 (A = 0, D = 0), every
+    state value 1.0, and every token adds dt * x * B = 2^-16 to every value (dt = 1, x = 1,
+    B = 2^-16, C = 1), so a flush of L = 4 tokens adds 2^-14. Returns ((Bt, H, P, N, G, L), S0, A,
+    D, (x, B, C, dt))."""
+    Bt, H, P, N, G, L = 2, 2, 64, 128, 1, 4
+    S0 = np.ones((Bt, H, P, N), np.float32)
+    A = np.zeros(H, np.float32)
+    D = np.zeros(H, np.float32)
+    x = np.ones((Bt, H, P), np.float32)
+    B = np.full((Bt, G, N), 2.0 ** -16, np.float32)
+    C = np.ones((Bt, G, N), np.float32)
+    dt = np.ones((Bt, H), np.float32)
+    return (Bt, H, P, N, G, L), S0, A, D, (x, B, C, dt)
