@@ -14,6 +14,8 @@ Functions (all arrays numpy, C-contiguous):
   gdn_step(S, q, k, v, alpha, beta) -> o       O1g, one Gated DeltaNet token (oracle_gdn.c)
   gdn_spec_stepwise(...)                       O5g, per-draft spec decoding on GDN
   GDNReplay(...)                               O3g + O4, the GDN replay form and pointer machine
+  mixer_edge / mixer_gate / silu / softplus    M1: the Mamba-2 mixer edges (oracle_mixer.c)
+  MixerStepwise(...) / MixerReplay(...)        edge + O1 / O5 + gate; edge + replay form + gate
 
 Pinning (what each function is checked against, independent of itself) is in tests/test_oracle_*.
 """
@@ -42,12 +44,20 @@ def lib():
     """Load liboracle.so, building it first if it is missing or older than its source."""
     global _lib
     if _lib is None:
-        srcs = [os.path.join(_HERE, f) for f in ("oracle.c", "oracle_gdn.c")]
+        srcs = [os.path.join(_HERE, f) for f in ("oracle.c", "oracle_gdn.c", "oracle_mixer.c")]
         if not os.path.exists(_LIB_PATH) or any(os.path.getmtime(_LIB_PATH) < os.path.getmtime(f) for f in srcs):
             _build.build()
         L = ctypes.CDLL(_LIB_PATH)
         L.oracle_step.argtypes = [_i] * 5 + [_f64p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f64p]
         L.oracle_step.restype = None
+        L.oracle_silu.argtypes = [ctypes.c_double]
+        L.oracle_silu.restype = ctypes.c_double
+        L.oracle_softplus.argtypes = [ctypes.c_double]
+        L.oracle_softplus.restype = ctypes.c_double
+        L.oracle_mixer_edge.argtypes = [_i] * 6 + [_f32p] * 10
+        L.oracle_mixer_edge.restype = None
+        L.oracle_mixer_gate.argtypes = [_sz, _f64p, _f32p, _f64p]
+        L.oracle_mixer_gate.restype = None
         L.oracle_spec_stepwise.argtypes = [_i] * 6 + [_f64p, _f32p, _f32p, _f32p, _f32p, _f32p,
                                                       _f32p, _i32p, _f64p]
         L.oracle_spec_stepwise.restype = _i
@@ -406,3 +416,117 @@ def f16_encode(a, r24=None):
 def f16_decode(codes):
     codes = np.asarray(codes, np.uint16)
     return np.array([lib().oracle_f16_decode(int(c)) for c in codes.reshape(-1)], np.float32).reshape(codes.shape)
+
+
+# ---- Mamba-2 mixer edges (oracle_mixer.c) --------------------------------------------------------
+def silu(v):
+    return float(lib().oracle_silu(float(v)))
+
+
+def softplus(v):
+    return float(lib().oracle_softplus(float(v)))
+
+
+def mixer_edge(hist, xbc, dt_raw, conv_w, conv_b, dt_bias, H, P, G, N):
+    """One token of the input edge. hist: float32 [Bt, K-1, CD] raw history (oldest first),
+    updated in place; xbc [Bt, CD]; dt_raw [Bt, H]; conv_w [CD, K]; conv_b [CD]; dt_bias [H].
+    Returns x [Bt,H,P], B, C [Bt,G,N], dt [Bt,H] (float32)."""
+    assert hist.dtype == np.float32 and hist.flags.c_contiguous
+    Bt, CD = xbc.shape
+    K = conv_w.shape[1]
+    assert CD == H * P + 2 * G * N and hist.shape == (Bt, K - 1, CD)
+    x = np.empty((Bt, H, P), np.float32)
+    B = np.empty((Bt, G, N), np.float32)
+    C = np.empty((Bt, G, N), np.float32)
+    dt = np.empty((Bt, H), np.float32)
+    h = hist if K > 1 else np.zeros(1, np.float32)
+    lib().oracle_mixer_edge(Bt, H, P, N, G, K, h, _f32(xbc), _f32(dt_raw), _f32(conv_w), _f32(conv_b),
+                            _f32(dt_bias), x, B, C, dt)
+    return x, B, C, dt
+
+
+def mixer_gate(y, z):
+    """o = y * silu(z); y float64, z float32 of the same shape."""
+    y = np.ascontiguousarray(y, np.float64)
+    o = np.empty_like(y)
+    lib().oracle_mixer_gate(y.size, y.reshape(-1), _f32(z).reshape(-1), o.reshape(-1))
+    return o
+
+
+class MixerStepwise:
+    """The truth for the fused mixer step: the input edge, O1 (or O5 for drafts), the gate.
+    S0 float32 [Bt,H,P,N]; hist0 float32 [Bt,K-1,CD] (zeros for a fresh sequence)."""
+
+    def __init__(self, S0, hist0, A, D, conv_w, conv_b, dt_bias, G):
+        self.S = np.ascontiguousarray(S0, np.float64)
+        self.hist = np.ascontiguousarray(hist0, np.float32).copy()
+        self.A, self.D, self.w, self.b, self.bias, self.G = A, D, conv_w, conv_b, dt_bias, G
+        _, self.H, self.P, self.N = self.S.shape
+
+    def edge(self, hist, xbc, dt_raw):
+        return mixer_edge(hist, xbc, dt_raw, self.w, self.b, self.bias, self.H, self.P, self.G, self.N)
+
+    def step(self, xbc, z, dt_raw):
+        x, B, C, dt = self.edge(self.hist, xbc, dt_raw)
+        return mixer_gate(step(self.S, x, B, C, dt, self.A, self.D), z)
+
+    def spec(self, T, xbc, z, dt_raw, accepted):
+        """All T draft outputs (xbc [Bt,T,CD], z [Bt,T,H,P], dt_raw [Bt,T,H]); the state and the
+        history then advance by the accepted prefix of each sequence."""
+        Bt = xbc.shape[0]
+        tent = self.hist.copy()
+        ins = [self.edge(tent, np.ascontiguousarray(xbc[:, i]), np.ascontiguousarray(dt_raw[:, i])) for i in range(T)]
+        x, B, C, dt = (np.ascontiguousarray(np.stack([t[j] for t in ins], axis=1)) for j in range(4))
+        y = spec_stepwise(self.S, T, x, B, C, dt, self.A, self.D, accepted)
+        for b in range(Bt):
+            for i in range(int(accepted[b])):
+                one = self.hist[b:b + 1]
+                mixer_edge(one, np.ascontiguousarray(xbc[b:b + 1, i]), np.ascontiguousarray(dt_raw[b:b + 1, i]),
+                           self.w, self.b, self.bias, self.H, self.P, self.G, self.N)
+                self.hist[b:b + 1] = one
+        return mixer_gate(y, z)
+
+
+class MixerReplay:
+    """The replay form with the mixer edges: the same edge and gate around Replay (O3 + O4). The
+    conv history follows the committed tokens, so a rollback cuts it back with the records."""
+
+    def __init__(self, S0, hist0, A, D, conv_w, conv_b, dt_bias, G, L, Tmax=1, read_prec=READ_FP32,
+                 master_prec=MASTER_FP32, seed=0, seq_ids=None):
+        self.rep = Replay(S0, A, D, G, L, Tmax, read_prec, master_prec, seed, seq_ids)
+        self.hist = np.ascontiguousarray(hist0, np.float32).copy()
+        self.w, self.b, self.bias, self.G = conv_w, conv_b, dt_bias, G
+        self.H, self.P, self.N = self.rep.H, self.rep.P, self.rep.N
+        self._drafts = None
+
+    def step(self, xbc, z, dt_raw):
+        x, B, C, dt = mixer_edge(self.hist, xbc, dt_raw, self.w, self.b, self.bias, self.H, self.P, self.G, self.N)
+        return mixer_gate(self.rep.step(x, B, C, dt), z)
+
+    def verify(self, T, xbc, z, dt_raw):
+        tent = self.hist.copy()
+        ins = [mixer_edge(tent, np.ascontiguousarray(xbc[:, i]), np.ascontiguousarray(dt_raw[:, i]), self.w,
+                          self.b, self.bias, self.H, self.P, self.G, self.N) for i in range(T)]
+        x, B, C, dt = (np.ascontiguousarray(np.stack([t[j] for t in ins], axis=1)) for j in range(4))
+        self._drafts = (T, np.ascontiguousarray(xbc), np.ascontiguousarray(dt_raw))
+        return mixer_gate(self.rep.verify(T, x, B, C, dt), z)
+
+    def rollback(self, accepted):
+        self.rep.rollback(accepted)
+        T, xbc, dt_raw = self._drafts
+        for b in range(self.hist.shape[0]):
+            for i in range(int(accepted[b])):
+                one = self.hist[b:b + 1]
+                mixer_edge(one, np.ascontiguousarray(xbc[b:b + 1, i]), np.ascontiguousarray(dt_raw[b:b + 1, i]),
+                           self.w, self.b, self.bias, self.H, self.P, self.G, self.N)
+                self.hist[b:b + 1] = one
+        self._drafts = None
+
+    def pointers(self):
+        return self.rep.pointers()
+
+    def checkpoint(self):
+        return self.rep.checkpoint()
+
+    def materialize(self):
+        return self.rep.materialize()

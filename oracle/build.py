@@ -7,7 +7,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRCS = [os.path.join(HERE, "oracle.c"), os.path.join(HERE, "oracle_gdn.c")]
+SRCS = [os.path.join(HERE, f) for f in ("oracle.c", "oracle_gdn.c", "oracle_mixer.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 

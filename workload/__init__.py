@@ -18,6 +18,7 @@ import numpy as np
 
 STREAM_PARAMS, STREAM_STATE, STREAM_STEP, STREAM_ACCEPT, STREAM_DRAFT = 0, 1, 2, 3, 4
 STREAM_GDN_PARAMS, STREAM_GDN_STATE, STREAM_GDN_STEP, STREAM_GDN_DRAFT = 10, 11, 12, 14
+STREAM_MIX_PARAMS, STREAM_MIX_HIST, STREAM_MIX_STEP, STREAM_MIX_DRAFT = 20, 21, 22, 24
 
 
 def rng(seed: int, stream: int, index: int = 0) -> np.random.Generator:
@@ -122,6 +123,8 @@ SWEEP = dict(H=128, P=64, N=128, G=8, batches=(1, 8, 64, 256, 512), Ls=(4, 8, 16
              layers=10, steps=64)
 # Gated DeltaNet: H value heads of Dv, G key heads of Dk (the pages give no GDN shape; this is a
 # common GDN layer shape: 32 value heads and 16 key heads of 128), 2 MiB fp32 state per sequence.
+MIXER_TINY = dict(Bt=2, H=4, P=16, N=32, G=2, L=4, K=4, steps=40)
+MIXER = dict(Bt=256, H=128, P=64, N=128, G=8, L=16, K=4, steps=64)
 GDN_TINY = dict(Bt=2, H=4, G=2, Dv=16, Dk=32, L=4, steps=64)
 GDN_SERVING = dict(Bt=256, H=32, G=16, Dv=128, Dk=128, L=16, steps=64)
 GDN_SPEC = dict(Bt=512, H=32, G=16, Dv=128, Dk=128, L=16, T=4, steps=64)
@@ -141,3 +144,49 @@ def stagnation_case():
     C = np.ones((Bt, G, N), np.float32)
     dt = np.ones((Bt, H), np.float32)
     return (Bt, H, P, N, G, L), S0, A, D, (x, B, C, dt)
+
+
+# ---- Mamba-2 mixer edges: in-projection outputs and edge parameters ------------------------------
+# Recipe: conv weights and bias ~ U(-1/sqrt(K), 1/sqrt(K)) (a depthwise conv's default init,
+# fan-in K); dt_bias = the inverse softplus of dt0, dt0 log-uniform in [1e-3, 1e-1] (Mamba-2's
+# dt init); in-projection outputs xBC, z, dt_raw ~ N(0, 1); the initial conv history (raw xBC of
+# the K-1 tokens before the first) ~ N(0, 1).
+def mixer_conv_dim(H: int, P: int, G: int, N: int) -> int:
+    return H * P + 2 * G * N
+
+
+def mixer_params(seed: int, H: int, P: int, G: int, N: int, K: int):
+    """conv_w [CD, K], conv_b [CD], dt_bias [H] (float32)."""
+    r = rng(seed, STREAM_MIX_PARAMS)
+    CD = mixer_conv_dim(H, P, G, N)
+    bound = 1.0 / np.sqrt(K)
+    conv_w = r.uniform(-bound, bound, (CD, K)).astype(np.float32)
+    conv_b = r.uniform(-bound, bound, CD).astype(np.float32)
+    dt0 = np.exp(r.uniform(np.log(1e-3), np.log(1e-1), H))
+    dt_bias = (dt0 + np.log(-np.expm1(-dt0))).astype(np.float32)
+    return conv_w, conv_b, dt_bias
+
+
+def mixer_history(seed: int, Bt: int, K: int, CD: int):
+    """Raw xBC of the K-1 tokens before the first, oldest first: float32 [Bt, K-1, CD]."""
+    return rng(seed, STREAM_MIX_HIST).standard_normal((Bt, K - 1, CD)).astype(np.float32)
+
+
+def mixer_token_inputs(seed: int, index: int, lead: tuple, H: int, P: int, G: int, N: int,
+                       stream: int = STREAM_MIX_STEP):
+    """xbc lead+(CD,), z lead+(H, P), dt_raw lead+(H,) (float32)."""
+    r = rng(seed, stream, index)
+    CD = mixer_conv_dim(H, P, G, N)
+    xbc = r.standard_normal(lead + (CD,)).astype(np.float32)
+    z = r.standard_normal(lead + (H, P)).astype(np.float32)
+    dt_raw = r.standard_normal(lead + (H,)).astype(np.float32)
+    return xbc, z, dt_raw
+
+
+def mixer_step_inputs(seed: int, step: int, Bt: int, H: int, P: int, G: int, N: int):
+    return mixer_token_inputs(seed, step, (Bt,), H, P, G, N)
+
+
+def mixer_draft_inputs(seed: int, step: int, Bt: int, T: int, H: int, P: int, G: int, N: int):
+    """Draft inputs with the draft index second: xbc [Bt,T,CD], z [Bt,T,H,P], dt_raw [Bt,T,H]."""
+    return mixer_token_inputs(seed, step, (Bt, T), H, P, G, N, STREAM_MIX_DRAFT)
