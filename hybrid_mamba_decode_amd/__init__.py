@@ -34,8 +34,10 @@ EXPORTED = (
     "replayssm_workspace_bytes", "replayssm_workspace_layout", "replayssm_create", "replayssm_destroy",
     "replayssm_load_state", "replayssm_step", "replayssm_flush", "replayssm_spec_verify",
     "replayssm_rollback", "replayssm_set_lockstep", "replayssm_get_pointers", "replayssm_check",
-    "replayssm_materialize_state",
-    "conventional_step", "snapshot_spec_verify", "snapshot_commit", "replayssm_status_string",
+    "replayssm_materialize_state", "replayssm_set_mixer", "replayssm_load_conv_state",
+    "replayssm_materialize_conv_state", "replayssm_mixer_step",
+    "conventional_step", "conventional_mixer_step", "snapshot_spec_verify", "snapshot_commit",
+    "replayssm_status_string",
 )
 GDN_EXPORTED = (
     "gdnreplay_workspace_bytes", "gdnreplay_workspace_layout", "gdnreplay_create", "gdnreplay_destroy",
@@ -48,13 +50,13 @@ GDN_EXPORTED = (
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "nheads", "headdim", "dstate", "ngroups", "buffer_len", "max_draft", "read_prec",
-        "store_C", "master_prec", "sr_seed")]
+        "store_C", "master_prec", "sr_seed", "d_conv")]
 
 
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "master", "read_copy", "scale", "ring_x", "ring_B", "ring_C", "ring_dt", "pos", "ckpt_pos",
-        "counters", "flag", "total")]
+        "master", "read_copy", "scale", "ring_x", "ring_B", "ring_C", "ring_dt", "conv_ring", "pos",
+        "ckpt_pos", "counters", "flag", "total")]
 
 
 class GDNConfig(ctypes.Structure):
@@ -85,6 +87,11 @@ _sig = {
     "replayssm_get_pointers": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
     "replayssm_check": (ctypes.c_int, [_vp, _vp]),
     "replayssm_materialize_state": (ctypes.c_int, [_vp, _vp, _vp]),
+    "replayssm_set_mixer": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
+    "replayssm_load_conv_state": (ctypes.c_int, [_vp, _vp, _vp]),
+    "replayssm_materialize_conv_state": (ctypes.c_int, [_vp, _vp, _vp]),
+    "replayssm_mixer_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
+    "conventional_mixer_step": (ctypes.c_int, [_cfgp, _vp, _vp, _i32] + [_vp] * 9 + [_vp]),
     "conventional_step": (ctypes.c_int, [_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "snapshot_spec_verify": (ctypes.c_int, [_cfgp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "snapshot_commit": (ctypes.c_int, [_cfgp, _vp, _vp, _i32, _vp]),
@@ -143,11 +150,16 @@ def _stream(stream=None):
 
 
 def make_config(batch, nheads, headdim, dstate, ngroups, buffer_len=16, max_draft=1,
-                read_prec="fp32", store_C=True, master_prec="fp32", sr_seed=0):
+                read_prec="fp32", store_C=True, master_prec="fp32", sr_seed=0, d_conv=0):
     rp = _PREC_NAMES[read_prec] if isinstance(read_prec, str) else int(read_prec)
     mp = _MASTER_NAMES[master_prec] if isinstance(master_prec, str) else int(master_prec)
     return Config(batch, nheads, headdim, dstate, ngroups, buffer_len, max_draft, rp, int(bool(store_C)), mp,
-                  int(sr_seed))
+                  int(sr_seed), int(d_conv))
+
+
+def conv_dim(cfg) -> int:
+    """Channels of the in-projection's xBC: H*P + 2*G*N."""
+    return cfg.nheads * cfg.headdim + 2 * cfg.ngroups * cfg.dstate
 
 
 def _expect(t, shape, name):
@@ -266,6 +278,41 @@ def snapshot_commit(cfg: Config, cur, accepted, T, stream=None):
            "snapshot_commit")
 
 
+def replayssm_set_mixer(h, conv_w, conv_b, dt_bias):
+    _check(_lib.replayssm_set_mixer(h, _ptr(conv_w, name="conv_w"), _ptr(conv_b, name="conv_b"),
+                                    _ptr(dt_bias, name="dt_bias")), "replayssm_set_mixer")
+
+
+def replayssm_load_conv_state(h, hist=None, stream=None):
+    _check(_lib.replayssm_load_conv_state(h, _ptr(hist, name="hist"), _stream(stream)), "replayssm_load_conv_state")
+
+
+def replayssm_materialize_conv_state(h, out, stream=None):
+    _check(_lib.replayssm_materialize_conv_state(h, _ptr(out, name="out"), _stream(stream)),
+           "replayssm_materialize_conv_state")
+
+
+def replayssm_mixer_step(h, xbc, z, dt_raw, o, stream=None):
+    _check(_lib.replayssm_mixer_step(h, _ptr(xbc, name="xbc"), _ptr(z, name="z"), _ptr(dt_raw, name="dt_raw"),
+                                     _ptr(o, name="o"), _stream(stream)), "replayssm_mixer_step")
+
+
+def conventional_mixer_step(cfg: Config, state, conv_ring, t, xbc, z, dt_raw, A, D, conv_w, conv_b, dt_bias, o,
+                            stream=None):
+    Bt, H, P, K, CD = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_conv, conv_dim(cfg)
+    _expect(state, (Bt, H, P, cfg.dstate), "state")
+    _expect(conv_ring, (Bt, K, CD), "conv_ring")
+    _expect(xbc, (Bt, CD), "xbc")
+    _expect(z, (Bt, H, P), "z")
+    _expect(dt_raw, (Bt, H), "dt_raw")
+    _expect(o, (Bt, H, P), "o")
+    _check(_lib.conventional_mixer_step(ctypes.byref(cfg), _ptr(state, name="state"), _ptr(conv_ring, name="conv_ring"),
+                                        int(t), _ptr(xbc, name="xbc"), _ptr(z, name="z"), _ptr(dt_raw, name="dt_raw"),
+                                        _ptr(A, name="A"), _ptr(D, name="D"), _ptr(conv_w, name="conv_w"),
+                                        _ptr(conv_b, name="conv_b"), _ptr(dt_bias, name="dt_bias"), _ptr(o, name="o"),
+                                        _stream(stream)), "conventional_mixer_step")
+
+
 def replayssm_status_string(status: int) -> str:
     return _lib.replayssm_status_string(int(status)).decode()
 
@@ -279,9 +326,9 @@ class ReplaySSM:
     """
 
     def __init__(self, batch, nheads, headdim, dstate, ngroups, A, D, buffer_len=16, max_draft=1,
-                 read_prec="fp32", store_C=True, master_prec="fp32", sr_seed=0, device="cuda"):
+                 read_prec="fp32", store_C=True, master_prec="fp32", sr_seed=0, d_conv=0, device="cuda"):
         self.cfg = make_config(batch, nheads, headdim, dstate, ngroups, buffer_len, max_draft,
-                               read_prec, store_C, master_prec, sr_seed)
+                               read_prec, store_C, master_prec, sr_seed, d_conv)
         nbytes = replayssm_workspace_bytes(self.cfg)
         if nbytes == 0:
             raise ReplaySSMError(RSSM_E_INVAL, "replayssm_workspace_bytes")
@@ -349,6 +396,37 @@ class ReplaySSM:
                               dtype=torch.float32, device=self.workspace.device)
         replayssm_materialize_state(self.handle, out, stream)
         return out
+
+    # mixer edges (d_conv > 0)
+    def set_mixer(self, conv_w, conv_b, dt_bias):
+        """conv_w [CD, K], conv_b [CD], dt_bias [H]; kept referenced by this object."""
+        CD, K = conv_dim(self.cfg), self.cfg.d_conv
+        _expect(conv_w, (CD, K), "conv_w")
+        _expect(conv_b, (CD,), "conv_b")
+        _expect(dt_bias, (self.nheads,), "dt_bias")
+        self._mixer = (conv_w.contiguous(), conv_b.contiguous(), dt_bias.contiguous())
+        replayssm_set_mixer(self.handle, *self._mixer)
+
+    def load_conv_state(self, hist=None, stream=None):
+        if hist is not None:
+            _expect(hist, (self.batch, self.cfg.d_conv - 1, conv_dim(self.cfg)), "hist")
+        replayssm_load_conv_state(self.handle, hist, stream)
+
+    def materialize_conv_state(self, out=None, stream=None):
+        if out is None:
+            out = torch.empty((self.batch, self.cfg.d_conv - 1, conv_dim(self.cfg)), dtype=torch.float32,
+                              device=self.workspace.device)
+        replayssm_materialize_conv_state(self.handle, out, stream)
+        return out
+
+    def mixer_step(self, xbc, z, dt_raw, o=None, stream=None):
+        _expect(xbc, (self.batch, conv_dim(self.cfg)), "xbc")
+        _expect(z, (self.batch, self.nheads, self.headdim), "z")
+        _expect(dt_raw, (self.batch, self.nheads), "dt_raw")
+        if o is None:
+            o = torch.empty_like(z)
+        replayssm_mixer_step(self.handle, xbc, z, dt_raw, o, stream)
+        return o
 
     # workspace views (inspection)
     def region(self, name, dtype, shape):

@@ -34,7 +34,9 @@ struct replayssm_layer {
     // replays correctly. A rollback or a masked flush makes sequences diverge: from then on
     // kernels read the device pointers.
     int uni, pslot, cslot, lcount;
+    int upos;         // lockstep: the common pos (the mixer edges' conv ring slot is upos mod R)
     int lockstep_ok;  // replayssm_set_lockstep: the fast path may be used at all
+    int mixer_set;    // replayssm_set_mixer has given the edge parameters
 };
 
 namespace {
@@ -74,8 +76,14 @@ rssm_status check_config(const replayssm_config *c)
     if (c->read_prec == RSSM_READ_FP8_E4M3 && c->headdim > kRows) return RSSM_E_UNSUPPORTED;
     if (c->read_prec == RSSM_READ_MXFP4 && c->dstate < 32) return RSSM_E_UNSUPPORTED;
     if (c->master_prec < RSSM_MASTER_FP32 || c->master_prec > RSSM_MASTER_FP16_SR) return RSSM_E_INVAL;
+    if (c->d_conv < 0 || c->d_conv == 1) return RSSM_E_INVAL;
+    if (c->d_conv > 4 || (c->d_conv > 0 && c->buffer_len > 32)) return RSSM_E_UNSUPPORTED;
     return RSSM_OK;
 }
+
+// Mixer edges: conv channels CD = H*P + 2*G*N and ring slots R = K - 1 + T_max.
+size_t conv_dim(const replayssm_config &c) { return (size_t)c.nheads * c.headdim + 2 * (size_t)c.ngroups * c.dstate; }
+int conv_slots(const replayssm_config &c) { return c.d_conv > 0 ? c.d_conv - 1 + c.max_draft : 0; }
 
 // Read precision of the kernels: the copy's, or the fp16 master read directly.
 int kernel_prec(const replayssm_config &c)
@@ -103,6 +111,7 @@ void make_layout(const replayssm_config &c, replayssm_layout *L)
     L->ring_B = take(Bt * G * Lb * N * 4);
     L->ring_C = take(c.store_C ? Bt * G * Lb * N * 4 : 0);
     L->ring_dt = take(Bt * H * Lb * 4);
+    L->conv_ring = take(Bt * conv_slots(c) * conv_dim(c) * 4);
     L->pos = take(Bt * 4);
     L->ckpt_pos = take(Bt * 4);
     L->counters = take(Bt * 4);
@@ -185,6 +194,31 @@ void commit_bounds(replayssm_t h, int lo, int hi)
     }
 }
 
+// Conv history of every sequence, relative to its device pos: row i (oldest first) is the raw
+// xBC of position pos - (K-1) + i, at ring slot (that position) mod R. load: from hist (zeros
+// when NULL); materialize (out != NULL): into out. One thread per (sequence, row, channel).
+__global__ void conv_hist_kernel(Layer Ld, const float *hist, float *out)
+{
+    const size_t rows = (size_t)Ld.K - 1, e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (size_t)Ld.Bt * rows * Ld.CD) return;
+    const int c = (int)(e % Ld.CD);
+    const int i = (int)(e / Ld.CD % rows);
+    const int b = (int)(e / Ld.CD / rows);
+    const int q = Ld.pos[b] - (Ld.K - 1) + i;
+    const int slot = ((q % Ld.R) + Ld.R) % Ld.R;
+    float *ring = Ld.conv_ring + ((size_t)b * Ld.R + slot) * Ld.CD + c;
+    if (out) out[e] = *ring;
+    else *ring = hist ? hist[e] : 0.f;
+}
+
+hipError_t launch_conv_hist(const Layer &Ld, const float *hist, float *out, hipStream_t st)
+{
+    const size_t n = (size_t)Ld.Bt * (Ld.K - 1) * Ld.CD;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(conv_hist_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Ld, hist, out);
+    return hipGetLastError();
+}
+
 rssm_status read_flag(replayssm_t h, hipStream_t st)
 {
     if (hipStreamSynchronize(st) != hipSuccess) return RSSM_E_HIP;
@@ -262,6 +296,10 @@ rssm_status replayssm_create(const replayssm_config *cfg, void *workspace, size_
     d.psplit = psplit_of(*cfg);
     d.mprec = cfg->master_prec;
     d.sr_seed = (unsigned)cfg->sr_seed;
+    d.conv_ring = cfg->d_conv > 0 ? (float *)(ws + lay.conv_ring) : nullptr;
+    d.K = cfg->d_conv;
+    d.R = conv_slots(*cfg);
+    d.CD = (int)conv_dim(*cfg);
     h->lmax = cfg->buffer_len <= 16 ? 16 : cfg->buffer_len <= 32 ? 32 : 64;
     h->lockstep_ok = 1;
     *out = h;
@@ -283,29 +321,33 @@ rssm_status replayssm_load_state(replayssm_t h, const float *state, void *stream
     h->pending_T = 0;
     h->cmin = h->cmax = 0;
     h->uni = h->lockstep_ok && h->cfg.master_prec != RSSM_MASTER_FP16_SR;
-    h->pslot = h->cslot = h->lcount = 0;
+    h->pslot = h->cslot = h->lcount = h->upos = 0;
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
+    rssm_status s = RSSM_OK;
+    {
 #define CALL(NV) launch_load_n##NV(kernel_prec(h->cfg), h->dev, state, st)
-    RSSM_BY_N(h->cfg.dstate, CALL)
+        s = [&]() -> rssm_status { RSSM_BY_N(h->cfg.dstate, CALL) }();
 #undef CALL
+    }
+    if (s != RSSM_OK || h->cfg.d_conv == 0) return s;
+    return hip_status(launch_conv_hist(h->dev, nullptr, nullptr, st));  // a fresh conv history: zeros
 }
 
-rssm_status replayssm_step(replayssm_t h, const float *x, const float *B, const float *C,
-                           const float *dt, float *y, void *stream)
+namespace {
+
+// One standard step (plain or with the mixer edges), after the entry point's argument checks.
+rssm_status do_step(replayssm_t h, const TokenIO &io, bool mix, void *stream)
 {
-    if (!h) return RSSM_E_INVAL;
-    const int bt = h->cfg.batch;
-    if (!ok_ptr(x, bt) || !ok_ptr(B, bt) || !ok_ptr(C, bt) || !ok_ptr(dt, bt) || !ok_ptr(y, bt))
-        return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
     if (h->pending_T) return RSSM_E_STATE;
     const int lim = h->cfg.buffer_len - h->cfg.max_draft;
     bool flush_capable = h->cmax + 1 > lim;
-    Lockstep ls{0, 0, 0};
+    Lockstep ls{0, 0, 0, 0};
     if (h->uni) {
-        ls = Lockstep{h->pslot, h->cslot, h->lcount + 1};
+        ls = Lockstep{h->pslot, h->cslot, h->lcount + 1, h->dev.R > 0 ? h->upos % h->dev.R : 0};
+        h->upos += 1;
         flush_capable = h->lcount + 1 > lim;  // every sequence flushes, or none does
         h->pslot = (h->pslot + 1) % h->cfg.buffer_len;
         if (flush_capable) {
@@ -317,11 +359,66 @@ rssm_status replayssm_step(replayssm_t h, const float *x, const float *B, const 
     }
     commit_bounds(h, 1, 1);
     if (h->cfg.batch == 0) return RSSM_OK;
-    const TokenIO io{x, B, C, dt, y};
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_step_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, io, flush_capable, ls, st)
+#define CALL(NV) launch_step_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, io, flush_capable, mix, ls, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
+}
+
+}  // namespace
+
+rssm_status replayssm_step(replayssm_t h, const float *x, const float *B, const float *C,
+                           const float *dt, float *y, void *stream)
+{
+    if (!h || h->cfg.d_conv > 0) return RSSM_E_INVAL;  // a mixer handle steps through replayssm_mixer_step
+    const int bt = h->cfg.batch;
+    if (!ok_ptr(x, bt) || !ok_ptr(B, bt) || !ok_ptr(C, bt) || !ok_ptr(dt, bt) || !ok_ptr(y, bt))
+        return RSSM_E_INVAL;
+    return do_step(h, TokenIO{x, B, C, dt, y, nullptr, nullptr}, false, stream);
+}
+
+rssm_status replayssm_set_mixer(replayssm_t h, const float *conv_w, const float *conv_b, const float *dt_bias)
+{
+    if (!h || h->cfg.d_conv == 0) return RSSM_E_INVAL;
+    if (!conv_w || !conv_b || !dt_bias || !aligned(conv_w, 4) || !aligned(conv_b, 4) || !aligned(dt_bias, 4))
+        return RSSM_E_INVAL;
+    h->dev.conv_w = conv_w;
+    h->dev.conv_b = conv_b;
+    h->dev.dt_bias = dt_bias;
+    h->mixer_set = 1;
+    return RSSM_OK;
+}
+
+rssm_status replayssm_load_conv_state(replayssm_t h, const float *hist, void *stream)
+{
+    if (!h || h->cfg.d_conv == 0) return RSSM_E_INVAL;
+    if (hist && !aligned(hist, 4)) return RSSM_E_INVAL;
+    rssm_status s = ready(h);
+    if (s != RSSM_OK) return s;
+    if (h->pending_T) return RSSM_E_STATE;
+    if (h->cfg.batch == 0) return RSSM_OK;
+    return hip_status(launch_conv_hist(h->dev, hist, nullptr, (hipStream_t)stream));
+}
+
+rssm_status replayssm_materialize_conv_state(replayssm_t h, float *out, void *stream)
+{
+    if (!h || h->cfg.d_conv == 0) return RSSM_E_INVAL;
+    if (!ok_ptr4(out, h->cfg.batch)) return RSSM_E_INVAL;
+    rssm_status s = ready(h);
+    if (s != RSSM_OK) return s;
+    if (h->pending_T) return RSSM_E_STATE;
+    if (h->cfg.batch == 0) return RSSM_OK;
+    return hip_status(launch_conv_hist(h->dev, nullptr, out, (hipStream_t)stream));
+}
+
+rssm_status replayssm_mixer_step(replayssm_t h, const float *xbc, const float *z, const float *dt_raw, float *o,
+                                 void *stream)
+{
+    if (!h || h->cfg.d_conv == 0) return RSSM_E_INVAL;
+    const int bt = h->cfg.batch;
+    if (!ok_ptr4(xbc, bt) || !ok_ptr4(z, bt) || !ok_ptr4(dt_raw, bt) || !ok_ptr4(o, bt)) return RSSM_E_INVAL;
+    if (!h->mixer_set) return RSSM_E_STATE;
+    return do_step(h, TokenIO{nullptr, nullptr, nullptr, dt_raw, o, xbc, z}, true, stream);
 }
 
 rssm_status replayssm_flush(replayssm_t h, const int32_t *seq_mask, void *stream)
@@ -349,7 +446,7 @@ rssm_status replayssm_flush(replayssm_t h, const int32_t *seq_mask, void *stream
 rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float *x, const float *B,
                                   const float *C, const float *dt, float *y, void *stream)
 {
-    if (!h) return RSSM_E_INVAL;
+    if (!h || h->cfg.d_conv > 0) return RSSM_E_INVAL;
     const int bt = h->cfg.batch;
     if (T < 1 || T > h->cfg.max_draft) return RSSM_E_INVAL;
     if (!ok_ptr(x, bt) || !ok_ptr(B, bt) || !ok_ptr(C, bt) || !ok_ptr(dt, bt) || !ok_ptr(y, bt))
@@ -443,6 +540,39 @@ rssm_status conventional_step(const replayssm_config *cfg, float *state, const f
     const TokenIO io{x, B, C, dt, y};
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) launch_conventional_n##NV(Ld, state, io, st)
+    RSSM_BY_N(cfg->dstate, CALL)
+#undef CALL
+}
+
+rssm_status conventional_mixer_step(const replayssm_config *cfg, float *state, float *conv_ring, int32_t t,
+                                    const float *xbc, const float *z, const float *dt_raw, const float *A,
+                                    const float *D, const float *conv_w, const float *conv_b,
+                                    const float *dt_bias, float *o, void *stream)
+{
+    const rssm_status s = check_shape(cfg);
+    if (s != RSSM_OK) return s;
+    if (cfg->d_conv < 2) return RSSM_E_INVAL;
+    if (cfg->d_conv > 4) return RSSM_E_UNSUPPORTED;
+    if (t < 0) return RSSM_E_INVAL;
+    const int bt = cfg->batch;
+    if (!ok_ptr(state, bt) || !ok_ptr4(conv_ring, bt) || !ok_ptr4(xbc, bt) || !ok_ptr4(z, bt) ||
+        !ok_ptr4(dt_raw, bt) || !ok_ptr4(o, bt))
+        return RSSM_E_INVAL;
+    if (!A || !D || !conv_w || !conv_b || !dt_bias || !aligned(A, 4) || !aligned(D, 4) || !aligned(conv_w, 4) ||
+        !aligned(conv_b, 4) || !aligned(dt_bias, 4))
+        return RSSM_E_INVAL;
+    if (cfg->batch == 0) return RSSM_OK;
+    Layer Ld = shape_layer(*cfg, A, D);
+    Ld.conv_ring = conv_ring;
+    Ld.conv_w = conv_w;
+    Ld.conv_b = conv_b;
+    Ld.dt_bias = dt_bias;
+    Ld.K = Ld.R = cfg->d_conv;
+    Ld.CD = (int)conv_dim(*cfg);
+    const TokenIO io{nullptr, nullptr, nullptr, dt_raw, o, xbc, z};
+    const int rslot = t % cfg->d_conv;
+    const hipStream_t st = (hipStream_t)stream;
+#define CALL(NV) launch_conventional_mixer_n##NV(Ld, state, io, rslot, st)
     RSSM_BY_N(cfg->dstate, CALL)
 #undef CALL
 }

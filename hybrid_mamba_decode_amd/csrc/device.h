@@ -55,12 +55,19 @@ struct Layer {
     int Bt, H, P, G, L, Tmax, hpg, psplit;
     int mprec;          // MASTER_*
     unsigned sr_seed;   // key of the stochastic-rounding stream
+    // Mixer edges (K > 0): raw in-projection xBC of recent positions, position q at slot q mod R
+    float *conv_ring;       // [Bt,R,CD]
+    const float *conv_w;    // [CD,K]
+    const float *conv_b;    // [CD]
+    const float *dt_bias;   // [H]
+    int K, R, CD;
 };
 
 // Per-token inputs of one call (layouts in replayssm.h).
 struct TokenIO {
-    const float *x, *B, *C, *dt;
+    const float *x, *B, *C, *dt;  // with the mixer edges: dt holds dt_raw, x/B/C are unused
     float *y;
+    const float *xbc, *z;         // mixer edges: raw in-projection xBC [..,CD] and gate input z
 };
 
 // Lockstep window position: when every sequence is known (on the host) to be at the same window
@@ -68,7 +75,29 @@ struct TokenIO {
 // token); k = 0 means "read each sequence's device pointers".
 struct Lockstep {
     int pslot, cslot, k;
+    int rslot;  // pos mod R (mixer edges' conv ring)
 };
+
+// Mixer-edge activations in fp32: silu(v) = v / (1 + e^-v); softplus(v) = log(1 + e^v), in the
+// overflow-free form v + log(1 + e^-v) for v > 0.
+__device__ inline float silu_f(float v) { return v / (1.0f + expf(-v)); }
+__device__ inline float softplus_f(float v) { return v > 0.f ? v + log1pf(expf(-v)) : log1pf(expf(v)); }
+
+// One channel c of the causal depthwise conv for sequence b at position pos (ring slot rslot):
+// bias + the K-1 history taps from the ring (oldest first) + this token's raw value `cur`,
+// then SiLU. The ring slots of positions pos-K+1 .. pos-1 are never the one written this step.
+__device__ inline float conv_channel(const Layer &Ld, int b, int c, int rslot, float cur)
+{
+    const float *w = Ld.conv_w + (size_t)c * Ld.K;
+    const float *ring = Ld.conv_ring + (size_t)b * Ld.R * Ld.CD + c;
+    float u = fmaf(w[Ld.K - 1], cur, Ld.conv_b[c]);
+    for (int i = 0; i < Ld.K - 1; ++i) {
+        const int d = Ld.K - 1 - i;  // position pos - d
+        const int sl = rslot >= d ? rslot - d : rslot - d + Ld.R;
+        u = fmaf(w[i], ring[(size_t)sl * Ld.CD], u);
+    }
+    return silu_f(u);
+}
 
 // Device flag bits.
 enum : unsigned { FLAG_POINTERS = 1u, FLAG_ACCEPTED = 2u };

@@ -515,7 +515,7 @@ __device__ inline Tile map_heads(const Layer &Ld, int hpb)
     return t;
 }
 
-template <int PREC, int LMAX, int ROWS, bool FLUSH>
+template <int PREC, int LMAX, int ROWS, bool FLUSH, bool MIX>
 __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lockstep ls)
 {
     using G = Geo<NN, PREC>;
@@ -580,10 +580,13 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     constexpr int BCH = BS < 8 ? BS : 8;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const float *rx = Ld.ring_x + bh0 * Ld.L * Ld.P + t.row0;
-    const float *fx = io.x + bh0 * Ld.P + t.row0;
     const float *rB = Ld.ring_B + ((size_t)t.b * Ld.G + t.g) * Ld.L * NN;
-    const float *fB = io.B + ((size_t)t.b * Ld.G + t.g) * NN;
-    const float *Ct = io.C + ((size_t)t.b * Ld.G + t.g) * NN;
+    // With the mixer edges this token's x, B, C are formed here (the conv prologue below); the
+    // unconditional loads that would read them then point at the ring, and their values are unused.
+    const float *fx = MIX ? rx : io.x + bh0 * Ld.P + t.row0;
+    const float *fB = MIX ? rB : io.B + ((size_t)t.b * Ld.G + t.g) * NN;
+    const float *Ct = MIX ? rB : io.C + ((size_t)t.b * Ld.G + t.g) * NN;
+    constexpr int KT = MIX ? 1 : 0;  // window records loaded from this token's inputs
     f32x4 xv[XS], bv[BCH], cq;
     float cc[G::VEC];
     float dtj = 0.f, Aw = 0.f, scl_r = 1.0f;
@@ -592,7 +595,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         for (int sl = 0; sl < XS; ++sl) {
             const int e = tid + sl * kThreads, j = e / (ROWS / 4), rem = e % (ROWS / 4);
             const int hh = rem / (kRows / 4), c4 = rem % (kRows / 4);
-            const bool in = j < k && 4 * c4 < t.nrows;
+            const bool in = j < k - KT && 4 * c4 < t.nrows;
             const float *src = (in && j < k - 1) ? rx + ((size_t)hh * Ld.L + slot_of(j)) * Ld.P + 4 * c4
                                                  : fx + (in ? (size_t)hh * Ld.P + 4 * c4 : 0);
             const f32x4 val = *(const f32x4 *)src;
@@ -603,18 +606,20 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
             const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
             const float *src = (j < k - 1 ? rB + (size_t)slot_of(j) * NN : fB) + 4 * c4;
             const f32x4 val = *(const f32x4 *)src;
-            bv[sl] = j < k ? val : zero;
+            bv[sl] = j < k - KT ? val : zero;
         }
-        {
+        if constexpr (!MIX) {
             const f32x4 val = *(const f32x4 *)(Ct + 4 * (tid % (NN / 4)));
             cq = tid < NN / 4 ? val : zero;
+            load_cchunk<PREC>(cc, Ct, lane);
         }
-        load_cchunk<PREC>(cc, Ct, lane);
         {
             const int hw = wave < HPB ? wave : 0;
             const bool in = wave < HPB && lane < k;
             const float val = (in && lane < k - 1) ? Ld.ring_dt[(bh0 + hw) * Ld.L + slot_of(lane)] : io.dt[bh0 + hw];
             dtj = in ? val : 0.f;
+            if constexpr (MIX)  // this token's dt = softplus(dt_raw + dt_bias)
+                if (in && lane == k - 1) dtj = softplus_f(val + Ld.dt_bias[t.h + hw]);
             const float a = Ld.A[t.h + hw];
             Aw = wave < HPB ? a : 0.f;
         }
@@ -649,6 +654,40 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         issue_window();
     }
     const bool flush = k > Ld.L - Ld.Tmax;
+
+    // Mixer edges: this token's x rows (one per thread), the group's B and C (channels e < 2N,
+    // B first) from the causal conv over the ring's history and this token's raw xBC, and the
+    // gate input z of this thread's output row. The raw values enter the ring at slot pos mod R
+    // (x channels by every work-group for its rows, B / C by the group's first work-group).
+    constexpr int BCT = (2 * NN + kThreads - 1) / kThreads;
+    float mx = 0.f, zg = 0.f, mbc[BCT];
+    if constexpr (MIX) {
+        const int rslot = uni ? ls.rslot : (int)((unsigned)dpos % (unsigned)Ld.R);
+        const float *raw = io.xbc + (size_t)t.b * Ld.CD;
+        float *ring_now = Ld.conv_ring + ((size_t)t.b * Ld.R + rslot) * Ld.CD;
+        if (tid < ROWS) {
+            const int hh = tid / kRows, p = tid % kRows;
+            const bool in = p < t.nrows;
+            const int c = (t.h + hh) * Ld.P + t.row0 + (in ? p : 0);
+            const float cur = raw[c];
+            const float v = conv_channel(Ld, t.b, c, rslot, cur);
+            mx = in ? v : 0.f;
+            zg = io.z[(bh0 + hh) * Ld.P + t.row0 + (in ? p : 0)];
+            if (in) ring_now[c] = cur;
+        }
+        const bool leader = t.split == 0 && t.h % Ld.hpg == 0;
+#pragma unroll
+        for (int i = 0; i < BCT; ++i) {
+            const int e = tid + i * kThreads;
+            mbc[i] = 0.f;
+            if (e < 2 * NN) {
+                const int c = Ld.H * Ld.P + (e < NN ? t.g * NN + e : Ld.G * NN + t.g * NN + (e - NN));
+                const float cur = raw[c];
+                mbc[i] = conv_channel(Ld, t.b, c, rslot, cur);
+                if (leader) ring_now[c] = cur;
+            }
+        }
+    }
     // Pointer update, once per sequence. Lockstep: the work-group owning head 0 checks the device
     // pointers against the window position (a mismatch means they were corrupted: flag, no
     // update) and advances them; device mode: the last work-group of the sequence writes them.
@@ -675,7 +714,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
 #pragma unroll
     for (int sl = 0; sl < XS; ++sl) {
         const int e = tid + sl * kThreads, j = e / (ROWS / 4), rem = e % (ROWS / 4);
-        if (j < LMAX) *(f32x4 *)&s.xw[j][4 * rem] = xv[sl];
+        if (j < LMAX && !(MIX && j == k - 1)) *(f32x4 *)&s.xw[j][4 * rem] = xv[sl];
     }
 #pragma unroll
     for (int s0 = 0; s0 < BS; s0 += BCH) {
@@ -690,10 +729,20 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
 #pragma unroll
         for (int sl = 0; sl < BCH; ++sl) {
             const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
-            if (s0 + sl < BS && j < LMAX) *(f32x4 *)&s.Bw[j][4 * c4] = bv[sl];
+            if (s0 + sl < BS && j < LMAX && !(MIX && j == k - 1)) *(f32x4 *)&s.Bw[j][4 * c4] = bv[sl];
         }
     }
-    if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = cq;
+    if constexpr (MIX) {
+        if (tid < ROWS) s.xw[k - 1][tid] = mx;
+#pragma unroll
+        for (int i = 0; i < BCT; ++i) {
+            const int e = tid + i * kThreads;
+            if (e < NN) s.Bw[k - 1][e] = mbc[i];
+            else if (e < 2 * NN) s.Cq[e - NN] = mbc[i];
+        }
+    } else {
+        if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = cq;
+    }
 
     // 5. Window weights of head w in wave w: suffix sums of dt by lane shuffles,
     //    w_j = dt_j * exp(A * sum_{i>j} dt_i), decay = exp(A * sum_i dt_i) ([AT Pulse]
@@ -721,7 +770,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         // (A stochastically rounded master always runs in device-pointer mode: its stream is
         // keyed by the new ckpt_pos, pos + 1.)
         float cf[4];
-        load_cchunk<PREC_F32>(cf, Ct, lane);
+        load_cchunk<PREC_F32>(cf, MIX ? s.Cq : Ct, lane);
 #pragma unroll
         for (int hh = 0; hh < HPB; ++hh) {
             f32x4 vf[GF::NL];
@@ -749,7 +798,8 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         __syncthreads();
         if (tid < ROWS && tid % kRows < t.nrows) {
             const int hh = tid / kRows;
-            io.y[(bh0 + hh) * Ld.P + t.row0 + tid % kRows] = fmaf(Ld.D[t.h + hh], s.xw[k - 1][tid], s.u[tid]);
+            const float yv = fmaf(Ld.D[t.h + hh], s.xw[k - 1][tid], s.u[tid]);
+            io.y[(bh0 + hh) * Ld.P + t.row0 + tid % kRows] = MIX ? yv * silu_f(zg) : yv;
         }
         // The token's own record is folded already: nothing is appended on a flush step.
         advance_pointers();
@@ -760,6 +810,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     //    only, while the checkpoint rows may still be in flight), then the row dots with C_t
     //    through the read copy.
     if (!kPreload) load_state();
+    if constexpr (MIX) load_cchunk<PREC>(cc, s.Cq, lane);
     {
         constexpr int GS = kThreads / LMAX;
         const int j = tid / GS, sub = tid % GS;
@@ -794,7 +845,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         for (int j = 0; j < k; ++j) acc = fmaf(s.coef[hh][j], s.xw[j][tid], acc);
         const float xt = s.xw[k - 1][tid];
         acc = fmaf(Ld.D[t.h + hh], xt, acc);
-        io.y[(bh0 + hh) * Ld.P + t.row0 + p] = acc;
+        io.y[(bh0 + hh) * Ld.P + t.row0 + p] = MIX ? acc * silu_f(zg) : acc;
         Ld.ring_x[((bh0 + hh) * Ld.L + pslot) * Ld.P + t.row0 + p] = xt;
     }
     if (t.split == 0 && wave < HPB && lane == k - 1) Ld.ring_dt[(bh0 + wave) * Ld.L + pslot] = dtj;
@@ -1359,6 +1410,67 @@ __global__ void __launch_bounds__(kThreads) conventional_kernel(Layer Ld, float 
 }
 
 // ==========================================================================================
+// Baseline with the mixer edges: the conventional step of the same layer with the same fused
+// edges as the replay's mixer step (conv over a ring of K raw inputs at slot rslot = t mod K,
+// softplus dt, gated output), so that the comparison measures the state traffic only.
+// ==========================================================================================
+__global__ void __launch_bounds__(kThreads) conventional_mixer_kernel(Layer Ld, float *state, TokenIO io, int rslot)
+{
+    __shared__ float u[kRows], xs[kRows], bs[NN], cs[NN];
+    const Tile t = map_tile(Ld);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    float *rows = state + (bh * Ld.P + t.row0) * NN;
+    u32x4 m[GF::NL];
+    load_rows<PREC_F32>(m, (const char *)rows, t.nrows, wave, lane);
+    const float dtv = softplus_f(io.dt[bh] + Ld.dt_bias[t.h]);
+    const float a = expf(dtv * Ld.A[t.h]);
+    const float *raw = io.xbc + (size_t)t.b * Ld.CD;
+    float *ring_now = Ld.conv_ring + ((size_t)t.b * Ld.R + rslot) * Ld.CD;
+    float zg = 0.f;
+    if (tid < kRows) {
+        const bool in = tid < t.nrows;
+        const int c = t.h * Ld.P + t.row0 + (in ? tid : 0);
+        const float cur = raw[c];
+        const float v = conv_channel(Ld, t.b, c, rslot, cur);
+        xs[tid] = in ? v : 0.f;
+        zg = io.z[bh * Ld.P + t.row0 + (in ? tid : 0)];
+        if (in) ring_now[c] = cur;
+    }
+    const bool leader = t.split == 0 && t.h % Ld.hpg == 0;
+    for (int e = tid; e < 2 * NN; e += kThreads) {
+        const int c = Ld.H * Ld.P + (e < NN ? t.g * NN + e : Ld.G * NN + t.g * NN + (e - NN));
+        const float cur = raw[c];
+        const float v = conv_channel(Ld, t.b, c, rslot, cur);
+        if (e < NN) bs[e] = v;
+        else cs[e - NN] = v;
+        if (leader) ring_now[c] = cur;
+    }
+    __syncthreads();
+    float bc[4], cc[4];
+    load_cchunk<PREC_F32>(bc, bs, lane);
+    load_cchunk<PREC_F32>(cc, cs, lane);
+    float part[GF::NL];
+    f32x4 vf[GF::NL];
+#pragma unroll
+    for (int i = 0; i < GF::NL; ++i) {
+        const int r = row_of<PREC_F32>(i, wave, lane);
+        const float dx = r < t.nrows ? dtv * xs[r] : 0.f;
+        f32x4 sv = as_f32x4(m[i]);
+        sv.x = fmaf(dx, bc[0], a * sv.x);
+        sv.y = fmaf(dx, bc[1], a * sv.y);
+        sv.z = fmaf(dx, bc[2], a * sv.z);
+        sv.w = fmaf(dx, bc[3], a * sv.w);
+        vf[i] = sv;
+        part[i] = chunk_dot<PREC_F32>(as_u32x4(sv), cc);
+    }
+    store_rows_f32(rows, vf, t.nrows, wave, lane);
+    rows_to_lds<PREC_F32, GF::NL>(part, u, 0, 1, GF::NL, 1.0f, wave, lane);
+    __syncthreads();
+    if (tid < t.nrows) io.y[bh * Ld.P + t.row0 + tid] = fmaf(Ld.D[t.h], xs[tid], u[tid]) * silu_f(zg);
+}
+
+// ==========================================================================================
 // Baseline: per-draft snapshots ([Clarity] "What happened", claim ledger [13]). Reads the
 // committed slot once, runs the T drafts stepwise and writes the state after draft q to slot
 // (cur + q + 1) mod (T + 1): one read and T writes of the state per verify.
@@ -1428,11 +1540,11 @@ __global__ void __launch_bounds__(kThreads) snapshot_verify_kernel(Layer Ld, flo
 // ------------------------------------------------------------------------------------------
 inline unsigned nblocks(const Layer &Ld) { return (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)Ld.psplit; }
 
-template <int PREC, int LMAX, int ROWS, bool FLUSH>
+template <int PREC, int LMAX, int ROWS, bool FLUSH, bool MIX>
 hipError_t step_rows(const Layer &Ld, const TokenIO &io, Lockstep ls, hipStream_t st)
 {
     const unsigned grid = nblocks(Ld) / (ROWS / kRows);
-    hipLaunchKernelGGL((step_kernel<PREC, LMAX, ROWS, FLUSH>), dim3(grid), dim3(kThreads), 0, st, Ld, io, ls);
+    hipLaunchKernelGGL((step_kernel<PREC, LMAX, ROWS, FLUSH, MIX>), dim3(grid), dim3(kThreads), 0, st, Ld, io, ls);
     return hipGetLastError();
 }
 
@@ -1445,7 +1557,8 @@ hipError_t step_rows(const Layer &Ld, const TokenIO &io, Lockstep ls, hipStream_
 // Flush-capable launches use one head per work-group (their fold loop is per head), except with an
 // fp16 master: a head's fp16 rows are half the bytes, so two heads per work-group with their rows
 // issued together keep the flush's bytes in flight (one head each: 2.6 TB/s on the flush step).
-template <int PREC, int LMAX>
+// MIX: the mixer edges fused in (no one-row-per-lane variant).
+template <int PREC, int LMAX, bool MIX>
 hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockstep ls, hipStream_t st)
 {
     constexpr int wide = PREC == PREC_F32 ? 1 : (PREC == PREC_BF16 || PREC == PREC_F16) ? 2 : 4;  // fp8, fp4: 4
@@ -1453,10 +1566,10 @@ hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockst
         // fp16 master: two heads per work-group with the master rows issued early (see step_kernel)
         if constexpr (LMAX <= 32)
             if (Ld.mprec != MASTER_F32 && Ld.psplit == 1 && Ld.hpg % 2 == 0)
-                return step_rows<PREC, LMAX, 2 * kRows, true>(Ld, io, ls, st);
-        return step_rows<PREC, LMAX, kRows, true>(Ld, io, ls, st);
+                return step_rows<PREC, LMAX, 2 * kRows, true, MIX>(Ld, io, ls, st);
+        return step_rows<PREC, LMAX, kRows, true, MIX>(Ld, io, ls, st);
     }
-    if constexpr ((PREC == PREC_FP8 || PREC == PREC_FP4) && LMAX == 16 && NN <= 128) {
+    if constexpr (!MIX && (PREC == PREC_FP8 || PREC == PREC_FP4) && LMAX == 16 && NN <= 128) {
         // one row per lane: P <= 64, four heads of one group per work-group; at N = 256 a row's
         // chunks would hold 64 (fp8) registers per lane
         if (Ld.P <= kRows && Ld.hpg % kWaves == 0) {
@@ -1466,8 +1579,8 @@ hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockst
         }
     }
     if (wide > 1 && LMAX <= 32 && Ld.psplit == 1 && Ld.hpg % wide == 0 && nblocks(Ld) / wide >= 2048)
-        return step_rows<PREC, LMAX, kRows * wide, false>(Ld, io, ls, st);
-    return step_rows<PREC, LMAX, kRows, false>(Ld, io, ls, st);
+        return step_rows<PREC, LMAX, kRows * wide, false, MIX>(Ld, io, ls, st);
+    return step_rows<PREC, LMAX, kRows, false, MIX>(Ld, io, ls, st);
 }
 
 template <int PREC, int LMAX>
@@ -1523,10 +1636,15 @@ hipError_t by_prec_lmax(int prec, int lmax, Args... args)
 
 template <int PREC, int LMAX>
 struct StepF {
-    static hipError_t run(const Layer &Ld, const TokenIO &io, bool fc, Lockstep ls, hipStream_t st)
+    static hipError_t run(const Layer &Ld, const TokenIO &io, bool fc, bool mix, Lockstep ls, hipStream_t st)
     {
-        if constexpr (!kPrecOk<PREC>) return hipErrorInvalidValue;
-        else return step_t<PREC, LMAX>(Ld, io, fc, ls, st);
+        if constexpr (!kPrecOk<PREC>) {
+            return hipErrorInvalidValue;
+        } else {
+            if (!mix) return step_t<PREC, LMAX, false>(Ld, io, fc, ls, st);
+            if constexpr (LMAX <= 32) return step_t<PREC, LMAX, true>(Ld, io, fc, ls, st);
+            else return hipErrorInvalidValue;  // the mixer edges need L <= 32 (host-checked)
+        }
     }
 };
 template <int PREC, int LMAX>
@@ -1564,9 +1682,9 @@ hipError_t load_p(const Layer &Ld, const float *state, hipStream_t st)
 #define RSSM_CAT(a, b) RSSM_CAT2(a, b)
 
 hipError_t RSSM_CAT(launch_step_n, RSSM_N)(int prec, int lmax, const Layer &Ld, const TokenIO &io, bool flush_capable,
-                                           Lockstep ls, hipStream_t st)
+                                           bool mix, Lockstep ls, hipStream_t st)
 {
-    return by_prec_lmax<StepF>(prec, lmax, Ld, io, flush_capable, ls, st);
+    return by_prec_lmax<StepF>(prec, lmax, Ld, io, flush_capable, mix, ls, st);
 }
 
 hipError_t RSSM_CAT(launch_flush_n, RSSM_N)(int prec, int lmax, const Layer &Ld, int mode, const int *arg, int T, float *out, hipStream_t st)
@@ -1594,6 +1712,13 @@ hipError_t RSSM_CAT(launch_load_n, RSSM_N)(int prec, const Layer &Ld, const floa
 hipError_t RSSM_CAT(launch_conventional_n, RSSM_N)(const Layer &Ld, float *state, const TokenIO &io, hipStream_t st)
 {
     hipLaunchKernelGGL(conventional_kernel, dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, state, io);
+    return hipGetLastError();
+}
+
+hipError_t RSSM_CAT(launch_conventional_mixer_n, RSSM_N)(const Layer &Ld, float *state, const TokenIO &io, int rslot,
+                                                       hipStream_t st)
+{
+    hipLaunchKernelGGL(conventional_mixer_kernel, dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, state, io, rslot);
     return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ enum { MODE_MASK = 0, MODE_OVERFULL = 1, MODE_MATERIALIZE = 2 };
 
 #define RSSM_DECLARE_LAUNCHERS(NV)                                                                     \
     hipError_t launch_step_n##NV(int prec, int lmax, const Layer &Ld, const TokenIO &io,               \
-                                 bool flush_capable, Lockstep ls, hipStream_t st);                     \
+                                 bool flush_capable, bool mix, Lockstep ls, hipStream_t st);           \
     hipError_t launch_flush_n##NV(int prec, int lmax, const Layer &Ld, int mode, const int *arg, int T,  \
                                   float *out, hipStream_t st);                                         \
     hipError_t launch_verify_n##NV(int prec, int lmax, const Layer &Ld, const TokenIO &io, int T,       \
@@ -20,6 +20,8 @@ enum { MODE_MASK = 0, MODE_OVERFULL = 1, MODE_MATERIALIZE = 2 };
     hipError_t launch_load_n##NV(int prec, const Layer &Ld, const float *state, hipStream_t st);        \
     hipError_t launch_conventional_n##NV(const Layer &Ld, float *state, const TokenIO &io,             \
                                          hipStream_t st);                                              \
+    hipError_t launch_conventional_mixer_n##NV(const Layer &Ld, float *state, const TokenIO &io,       \
+                                               int rslot, hipStream_t st);                             \
     hipError_t launch_snapshot_n##NV(const Layer &Ld, float *slots, const int *cur, int T,              \
                                      const TokenIO &io, hipStream_t st);
 

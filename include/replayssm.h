@@ -112,6 +112,8 @@ typedef struct {
     int32_t store_C;     /* 1: records also keep C (the record is (x, B, C, dt)); 0: (x, B, dt) */
     int32_t master_prec; /* rssm_master_prec: precision of the checkpoint itself */
     int32_t sr_seed;     /* key of the stochastic-rounding stream (RSSM_MASTER_FP16_SR) */
+    int32_t d_conv;      /* K: 0 = plain step inputs; 2..4 = the mixer edges are fused in (see
+                            replayssm_mixer_step; requires buffer_len <= 32) */
 } replayssm_config;
 
 /* Byte offsets of the workspace regions (for inspection by tests and tools). */
@@ -128,6 +130,8 @@ typedef struct {
     size_t ring_B;     /* fp32 [Bt,G,L,N] */
     size_t ring_C;     /* fp32 [Bt,G,L,N] (0 bytes when store_C = 0) */
     size_t ring_dt;    /* fp32 [Bt,H,L] */
+    size_t conv_ring;  /* fp32 [Bt,R,CD], R = d_conv - 1 + max_draft, CD = H*P + 2*G*N: raw
+                          in-projection xBC of position q in slot q mod R (0 bytes if d_conv = 0) */
     size_t pos;        /* int32 [Bt]: tokens committed */
     size_t ckpt_pos;   /* int32 [Bt]: tokens folded into the checkpoint */
     size_t counters;   /* uint32 [Bt]: per-launch completion counters (zero between launches) */
@@ -167,6 +171,43 @@ rssm_status replayssm_load_state(replayssm_t layer, const float *state, void *st
  * dt [Bt,H]. RSSM_E_STATE if a verify is pending. */
 rssm_status replayssm_step(replayssm_t layer, const float *x, const float *B, const float *C,
                            const float *dt, float *y, void *stream);
+
+/* ---- Mixer edges (d_conv = K > 0) ---------------------------------------------------------------
+ * The pages give the SSM step itself; in a Mamba-2 mixer it sits between the in-projection and
+ * the output gate ([Clarity] "Why it matters": the per-token state read and write of the decode
+ * path). A mixer handle fuses the edges of the published Mamba-2 block (Dao and Gu, 2024) into the
+ * step, per sequence and token:
+ *   in-projection output xBC [CD] (channels: x head-major [H*P], then B [G*N], then C [G*N]),
+ *   z [H,P], dt_raw [H];
+ *   u[c] = conv_b[c] + sum_{i<K} conv_w[c*K + i] * xBC_{pos-K+1+i}[c]  (causal depthwise conv
+ *   over this token and the K-1 before it), (x, B, C) = split(silu(u)), silu(v) = v/(1+e^-v);
+ *   dt = softplus(dt_raw + dt_bias[h]), softplus(v) = log(1 + e^v);
+ *   the step as replayssm_step on (x, B, C, dt), records as there;
+ *   o[h,p] = y[h,p] * silu(z[h,p]).
+ * The conv history is the raw xBC of the K-1 committed positions before pos, kept in the
+ * workspace ring keyed by position, so a rollback cuts it back with the records (no copy). A
+ * mixer handle takes mixer calls: replayssm_step and replayssm_spec_verify return RSSM_E_INVAL. */
+
+/* Give the edge parameters (device fp32, caller-owned, outliving their use): conv_w [CD,K],
+ * conv_b [CD], dt_bias [H]. RSSM_E_INVAL on a handle with d_conv = 0 or a NULL / misaligned
+ * pointer. Required before the first replayssm_mixer_step (RSSM_E_STATE otherwise). */
+rssm_status replayssm_set_mixer(replayssm_t layer, const float *conv_w, const float *conv_b,
+                                const float *dt_bias);
+
+/* Set every sequence's conv history, relative to its current pos: hist (device fp32
+ * [Bt,K-1,CD], raw xBC of the K-1 tokens before the next one, oldest first), or zeros if NULL.
+ * replayssm_load_state resets the history to zeros. RSSM_E_STATE if a verify is pending. */
+rssm_status replayssm_load_conv_state(replayssm_t layer, const float *hist, void *stream);
+
+/* The conv history after the committed tokens into out (device fp32 [Bt,K-1,CD]). */
+rssm_status replayssm_materialize_conv_state(replayssm_t layer, float *out, void *stream);
+
+/* Standard decode step with the mixer edges fused: inputs xbc [Bt,CD], z [Bt,H,P],
+ * dt_raw [Bt,H]; output o [Bt,H,P] (gated). Stores xbc in the conv ring at slot pos mod R and the
+ * token's record (the conv's x, B, C and the softplus dt) as replayssm_step does, with the same
+ * flush rule. Float arrays 4-byte aligned. */
+rssm_status replayssm_mixer_step(replayssm_t layer, const float *xbc, const float *z,
+                                 const float *dt_raw, float *o, void *stream);
 
 /* Fold every committed record of the selected sequences into the checkpoint (seq_mask: device
  * int32 [Bt], nonzero = flush; NULL = all), rewrite their read copy, set ckpt_pos = pos.
@@ -217,6 +258,15 @@ rssm_status replayssm_materialize_state(replayssm_t layer, float *out, void *str
 rssm_status conventional_step(const replayssm_config *cfg, float *state, const float *x,
                               const float *B, const float *C, const float *dt, const float *A,
                               const float *D, float *y, void *stream);
+
+/* Baseline with the mixer edges: conventional_step with the same fused edges as
+ * replayssm_mixer_step. conv_ring [Bt,K,CD] (device fp32, in/out) holds the raw xBC of position
+ * q in slot q mod K; t >= 0 is this token's position (the caller keeps it; positions before 0
+ * are the initial history). K = cfg->d_conv (2..4); state, A, D as conventional_step. */
+rssm_status conventional_mixer_step(const replayssm_config *cfg, float *state, float *conv_ring, int32_t t,
+                                    const float *xbc, const float *z, const float *dt_raw, const float *A,
+                                    const float *D, const float *conv_w, const float *conv_b,
+                                    const float *dt_bias, float *o, void *stream);
 
 /* Baseline for speculative decoding with per-draft snapshots ([Clarity] "What happened" and claim
  * ledger [13]): slots [Bt,T+1,H,P,N] hold T+1 states per sequence, cur [Bt] (device int32) the

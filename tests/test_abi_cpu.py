@@ -85,6 +85,10 @@ def test_workspace_layout_serving_shape():
     (dict(store_C=2), rs.RSSM_E_INVAL),
     (dict(master_prec=3), rs.RSSM_E_INVAL),
     (dict(master_prec=-1), rs.RSSM_E_INVAL),
+    (dict(d_conv=1), rs.RSSM_E_INVAL),
+    (dict(d_conv=-1), rs.RSSM_E_INVAL),
+    (dict(d_conv=5), rs.RSSM_E_UNSUPPORTED),
+    (dict(d_conv=4, buffer_len=64), rs.RSSM_E_UNSUPPORTED),
 ])
 def test_invalid_configs_rejected(kw, status):
     c = cfg(**kw)
@@ -302,3 +306,56 @@ def test_gdn_pointer_validation_before_state():
     assert L.gdn_conventional_step(ctypes.byref(gcfg()), FAKE, *io, None) == rs.RSSM_OK   # batch 0
     assert L.gdn_snapshot_spec_verify(ctypes.byref(c), FAKE, FAKE, 9, *io, None) == rs.RSSM_E_INVAL
     assert L.gdnreplay_destroy(h) == rs.RSSM_OK
+
+
+def test_mixer_layout():
+    Bt, H, P, N, G, K, T = 4, 8, 64, 128, 2, 4, 3
+    CD = H * P + 2 * G * N
+    lay = rs.replayssm_workspace_layout(cfg(batch=Bt, nheads=H, ngroups=G, d_conv=K, max_draft=T))
+    assert lay.conv_ring % 256 == 0
+    assert lay.pos - lay.conv_ring == -(-Bt * (K - 1 + T) * CD * 4 // 256) * 256   # R = K - 1 + T slots
+    plain = rs.replayssm_workspace_layout(cfg(batch=Bt, nheads=H, ngroups=G))
+    assert plain.pos == plain.conv_ring                                           # no ring without edges
+    assert rs.conv_dim(cfg(nheads=H, ngroups=G)) == CD
+
+
+def test_mixer_entry_points_on_host():
+    """Host-side rules of the mixer calls (batch 0, fake pointers; nothing reaches the GPU)."""
+    L = rs._lib
+    plain = _handle()
+    mix = _handle(d_conv=4, max_draft=2)
+    io = [FAKE] * 4
+    assert L.replayssm_set_mixer(plain, FAKE, FAKE, FAKE) == rs.RSSM_E_INVAL       # no edges on this handle
+    assert L.replayssm_mixer_step(plain, *io, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_load_conv_state(plain, None, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_mixer_step(mix, *io, None) == rs.RSSM_E_STATE             # parameters not given
+    assert L.replayssm_set_mixer(mix, None, FAKE, FAKE) == rs.RSSM_E_INVAL
+    assert L.replayssm_set_mixer(mix, FAKE, FAKE + 2, FAKE) == rs.RSSM_E_INVAL   # misaligned
+    assert L.replayssm_set_mixer(mix, FAKE, FAKE, FAKE) == rs.RSSM_OK
+    assert L.replayssm_mixer_step(mix, *io, None) == rs.RSSM_E_STATE             # before load_state
+    assert L.replayssm_load_conv_state(mix, None, None) == rs.RSSM_E_STATE
+    assert L.replayssm_load_state(mix, None, None) == rs.RSSM_OK
+    assert L.replayssm_load_conv_state(mix, None, None) == rs.RSSM_OK
+    assert L.replayssm_mixer_step(mix, *io, None) == rs.RSSM_OK
+    assert L.replayssm_mixer_step(mix, FAKE + 2, FAKE, FAKE, FAKE, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_step(mix, *([FAKE] * 5), None) == rs.RSSM_E_INVAL         # plain calls refused
+    assert L.replayssm_spec_verify(mix, 2, *([FAKE] * 5), None) == rs.RSSM_E_INVAL
+    assert L.replayssm_materialize_conv_state(mix, FAKE, None) == rs.RSSM_OK
+    assert L.replayssm_materialize_conv_state(mix, FAKE + 2, None) == rs.RSSM_E_INVAL
+    for h in (plain, mix):
+        assert L.replayssm_destroy(h) == rs.RSSM_OK
+
+
+def test_conventional_mixer_argument_checks():
+    L = rs._lib
+    c = cfg(d_conv=4)
+    args = [FAKE] * 9            # xbc, z, dt_raw, A, D, conv_w, conv_b, dt_bias, o
+    assert L.conventional_mixer_step(ctypes.byref(c), FAKE, FAKE, 0, *args, None) == rs.RSSM_OK   # batch 0
+    assert L.conventional_mixer_step(ctypes.byref(c), FAKE, FAKE, -1, *args, None) == rs.RSSM_E_INVAL
+    c0 = cfg()
+    assert L.conventional_mixer_step(ctypes.byref(c0), FAKE, FAKE, 0, *args, None) == rs.RSSM_E_INVAL
+    c5 = cfg(d_conv=5)
+    assert L.conventional_mixer_step(ctypes.byref(c5), FAKE, FAKE, 0, *args, None) == rs.RSSM_E_UNSUPPORTED
+    bad = list(args)
+    bad[5] = None                                                                     # conv_w NULL
+    assert L.conventional_mixer_step(ctypes.byref(c), FAKE, FAKE, 0, *bad, None) == rs.RSSM_E_INVAL

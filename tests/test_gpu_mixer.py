@@ -1,0 +1,190 @@
+"""GPU parity of the mixer-edge step (replayssm_mixer_step) and its conventional baseline against
+the oracle's mixer models (oracle_mixer.c + O1 / the replay form).
+
+Bars: pointers bit-exact; the conv history read back (replayssm_materialize_conv_state) equal to
+the oracle's raw history bit for bit (raw inputs are copied, never rounded); fp32 outputs,
+checkpoint and materialized state within 1e-5 of the float64 truth (the edge adds a K-term fp32
+conv, fp32 expf / log1pf in SiLU and softplus: a few fp32 roundings of O(1) values, below the
+step's own 1e-5 budget). Read copies: within 1e-5 of the oracle's replay-form mixer with the same
+copy until the first flush and on every flush step, within half the format gate of it after
+(rounding flips of the re-encoded copy); against the truth within the format gate (bf16 2e-2,
+fp8 6e-2, MXFP4 0.25) or, on a step where the oracle's own copy model exceeds it, 1.25x the
+model's error. fp16 masters at the bars of their own tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_mamba_decode_amd as rs
+import oracle
+import workload
+from gpu_harness import MASTER_CODE, PREC_CODE, dev, host, log, rel
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+
+
+class MixCase:
+    def __init__(self, Bt, H, P, N, G, L, K, seed, Tmax=1):
+        self.Bt, self.H, self.P, self.N, self.G, self.L, self.K, self.seed, self.Tmax = Bt, H, P, N, G, L, K, seed, Tmax
+        self.CD = workload.mixer_conv_dim(H, P, G, N)
+        self.A, self.D = workload.layer_params(seed, H)
+        self.w, self.b, self.bias = workload.mixer_params(seed, H, P, G, N, K)
+        self.S0 = workload.initial_state(seed, Bt, H, P, N)
+        self.h0 = workload.mixer_history(seed, Bt, K, self.CD)
+
+    def inputs(self, t):
+        return workload.mixer_step_inputs(self.seed, t, self.Bt, self.H, self.P, self.G, self.N)
+
+    def layer(self, read_prec="fp32", master_prec="fp32", lockstep=True, history=True, sr_seed=0):
+        lay = rs.ReplaySSM(self.Bt, self.H, self.P, self.N, self.G, dev(self.A), dev(self.D), buffer_len=self.L,
+                           max_draft=self.Tmax, read_prec=read_prec, master_prec=master_prec, sr_seed=sr_seed,
+                           d_conv=self.K)
+        lay.set_lockstep(lockstep)
+        lay.set_mixer(dev(self.w), dev(self.b), dev(self.bias))
+        lay.load_state(dev(self.S0))
+        if history:
+            lay.load_conv_state(dev(self.h0))
+        return lay
+
+
+def _run(case, steps, sample, read_prec="fp32", master_prec="fp32", lockstep=True, tol_nonflush=TOL_F32,
+         check_every=4):
+    log(f"[mixer] Bt={case.Bt} H={case.H} P={case.P} N={case.N} G={case.G} L={case.L} K={case.K} "
+        f"read={read_prec} master={master_prec} lockstep={lockstep} steps={steps} sample={list(sample)}")
+    lay = case.layer(read_prec, master_prec, lockstep, sr_seed=3)
+    sample = np.asarray(sample)
+    truth = oracle.MixerStepwise(case.S0[sample], case.h0[sample], case.A, case.D, case.w, case.b, case.bias, case.G)
+    model = oracle.MixerReplay(case.S0[sample], case.h0[sample], case.A, case.D, case.w, case.b, case.bias, case.G,
+                               case.L, 1, PREC_CODE[read_prec], MASTER_CODE[master_prec], 3, seq_ids=sample)
+    assert np.array_equal(host(lay.materialize_conv_state())[sample], case.h0[sample])
+    for t in range(steps):
+        xbc, z, dt_raw = case.inputs(t)
+        o = host(lay.mixer_step(dev(xbc), dev(z), dev(dt_raw)))[sample]
+        sub = (xbc[sample], z[sample], dt_raw[sample])
+        o_true = truth.step(*sub)
+        o_model = model.step(*sub)
+        flushes = (t + 1) // case.L
+        flush_step = (t + 1) % case.L == 0
+        if master_prec == "fp32":
+            e_true, e_model = rel(o, o_true), rel(o, o_model)
+            if read_prec == "fp32" or flushes == 0 or flush_step:
+                assert e_model <= TOL_F32, f"step {t}: vs replay model {e_model:.2e}"
+            else:
+                # after a flush the copies may differ by rare rounding flips (the fp32 and float64
+                # folds straddle a code boundary): the GPU stays far closer to the model than the
+                # format's own error
+                assert e_model <= tol_nonflush / 2, f"step {t}: vs replay model {e_model:.2e}"
+            # the format gate, except where the oracle's own copy model exceeds it on this step
+            gate = TOL_F32 if flush_step else max(tol_nonflush, 1.25 * rel(o_model, o_true))
+            assert e_true <= gate, f"step {t}: vs truth {e_true:.2e} > {gate:.2e}"
+        else:
+            assert rel(o, o_model) <= (TOL_F32 if flushes == 0 else 1e-3), f"step {t}: vs fp16 model {rel(o, o_model):.2e}"
+            assert rel(o, o_true) <= (flushes + 1) * 2.0 ** -10, f"step {t}: vs truth {rel(o, o_true):.2e}"
+        pos, ck = lay.get_pointers()
+        assert pos == [t + 1] * case.Bt and ck == [flushes * case.L] * case.Bt
+        if t % check_every == 0 or flush_step:
+            assert np.array_equal(host(lay.materialize_conv_state())[sample], truth.hist), f"step {t}: conv history"
+            bound = TOL_F32 if master_prec == "fp32" else (flushes + 1) * 2.0 ** -10
+            assert rel(host(lay.materialize_state())[sample], truth.S) <= bound
+    assert lay.check() == rs.RSSM_OK
+    return lay
+
+
+def test_tiny_mixer_fp32():
+    c = workload.MIXER_TINY
+    case = MixCase(c["Bt"], c["H"], c["P"], c["N"], c["G"], c["L"], c["K"], 31)
+    _run(case, c["steps"], range(c["Bt"]), check_every=1)
+
+
+@pytest.mark.parametrize("lockstep", [True, False])
+def test_serving_mixer_fp32(lockstep):
+    """The serving layer with the edges: batch 256, 128 heads, P 64, N 128, 8 groups, L 16, K 4;
+    48 steps (3 flushes), sequences 3 and 250 against the oracle."""
+    c = workload.MIXER
+    case = MixCase(c["Bt"], c["H"], c["P"], c["N"], c["G"], c["L"], c["K"], 32)
+    _run(case, 48, [3, 250], lockstep=lockstep, check_every=16)
+
+
+@pytest.mark.parametrize("read_prec,tol", [("bf16", 2e-2), ("fp8", 6e-2), ("mxfp4", 0.25)])
+def test_mixer_with_read_copy(read_prec, tol):
+    case = MixCase(3, 8, 32, 64, 2, 6, 4, 33)
+    _run(case, 20, range(3), read_prec=read_prec, tol_nonflush=tol)
+
+
+@pytest.mark.parametrize("master_prec", ["fp16", "fp16_sr"])
+def test_mixer_with_fp16_master(master_prec):
+    case = MixCase(3, 8, 32, 64, 2, 6, 4, 34)
+    _run(case, 20, range(3), master_prec=master_prec)
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 6, 100, 32, 3, 5, 3),     # P over two row splits, ragged; K = 3
+    (3, 4, 20, 16, 4, 1, 2),      # one head per group, L = 1 (every step flushes), K = 2
+    (2, 4, 64, 256, 2, 32, 4),    # N = 256 (two B/C channels per thread), L bucket 32
+])
+def test_mixer_shapes(shape):
+    Bt, H, P, N, G, L, K = shape
+    case = MixCase(Bt, H, P, N, G, L, K, 35)
+    _run(case, 2 * L + 3, range(Bt), check_every=3)
+
+
+def test_fresh_history_is_zero():
+    """load_state alone starts every sequence with a zero conv history."""
+    case = MixCase(2, 4, 16, 32, 2, 4, 4, 36)
+    lay = case.layer(history=False)
+    assert not host(lay.materialize_conv_state()).any()
+    truth = oracle.MixerStepwise(case.S0, np.zeros_like(case.h0), case.A, case.D, case.w, case.b, case.bias, case.G)
+    for t in range(6):
+        xbc, z, dt_raw = case.inputs(t)
+        o = host(lay.mixer_step(dev(xbc), dev(z), dev(dt_raw)))
+        assert rel(o, truth.step(xbc, z, dt_raw)) <= TOL_F32
+
+
+def test_conventional_mixer_step():
+    """The baseline with the same edges, against the stepwise mixer truth; its ring of K slots
+    holds position q at slot q mod K (the initial history at positions -3..-1)."""
+    c = workload.MIXER_TINY
+    case = MixCase(c["Bt"], c["H"], c["P"], c["N"], c["G"], c["L"], c["K"], 37)
+    K = case.K
+    cfg = rs.make_config(case.Bt, case.H, case.P, case.N, case.G, d_conv=K)
+    ring = np.zeros((case.Bt, K, case.CD), np.float32)
+    for i in range(K - 1):
+        ring[:, (i - (K - 1)) % K] = case.h0[:, i]
+    ring_d, state = dev(ring), dev(case.S0)
+    truth = oracle.MixerStepwise(case.S0, case.h0, case.A, case.D, case.w, case.b, case.bias, case.G)
+    args = [dev(a) for a in (case.A, case.D, case.w, case.b, case.bias)]
+    for t in range(12):
+        xbc, z, dt_raw = case.inputs(t)
+        o = torch.empty(case.Bt, case.H, case.P, device="cuda")
+        rs.conventional_mixer_step(cfg, state, ring_d, t, dev(xbc), dev(z), dev(dt_raw), *args, o)
+        assert rel(host(o), truth.step(xbc, z, dt_raw)) <= TOL_F32, t
+    assert rel(host(state), truth.S) <= TOL_F32
+
+
+def test_mixer_graph_replay_of_whole_windows():
+    """Lockstep arguments (window slots and the conv ring slot pos mod R) repeat every
+    lcm(L, R) steps: a captured window of L = 8 steps with R = 4 replays correctly, inputs copied
+    into the captured buffers, eager work in between."""
+    case = MixCase(4, 8, 64, 128, 2, 8, 4, 38)
+    lay = case.layer()
+    bufs = [tuple(dev(a) for a in case.inputs(i)) for i in range(case.L)]
+    outs = [torch.empty(case.Bt, case.H, case.P, device="cuda") for _ in range(case.L)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(case.L):
+            lay.mixer_step(*bufs[i], outs[i])
+    truth = oracle.MixerStepwise(case.S0, case.h0, case.A, case.D, case.w, case.b, case.bias, case.G)
+    for r in range(3):
+        for i in range(case.L):
+            for d, src in zip(bufs[i], case.inputs(r * case.L + i)):
+                d.copy_(dev(src))
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(case.L):
+            o_ref = truth.step(*case.inputs(r * case.L + i))
+            assert rel(host(outs[i]), o_ref) <= TOL_F32, f"replay {r} step {i}"
+        assert np.array_equal(host(lay.materialize_conv_state()), truth.hist)
+        _ = torch.ones(1 << 20, device="cuda").sum().item()
+    assert lay.check() == rs.RSSM_OK
