@@ -35,7 +35,7 @@ EXPORTED = (
     "replayssm_load_state", "replayssm_step", "replayssm_flush", "replayssm_spec_verify",
     "replayssm_rollback", "replayssm_set_lockstep", "replayssm_get_pointers", "replayssm_check",
     "replayssm_materialize_state", "replayssm_set_mixer", "replayssm_load_conv_state",
-    "replayssm_materialize_conv_state", "replayssm_mixer_step",
+    "replayssm_materialize_conv_state", "replayssm_mixer_step", "replayssm_mixer_spec_verify",
     "conventional_step", "conventional_mixer_step", "snapshot_spec_verify", "snapshot_commit",
     "replayssm_status_string",
 )
@@ -91,6 +91,7 @@ _sig = {
     "replayssm_load_conv_state": (ctypes.c_int, [_vp, _vp, _vp]),
     "replayssm_materialize_conv_state": (ctypes.c_int, [_vp, _vp, _vp]),
     "replayssm_mixer_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
+    "replayssm_mixer_spec_verify": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "conventional_mixer_step": (ctypes.c_int, [_cfgp, _vp, _vp, _i32] + [_vp] * 9 + [_vp]),
     "conventional_step": (ctypes.c_int, [_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "snapshot_spec_verify": (ctypes.c_int, [_cfgp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -297,6 +298,12 @@ def replayssm_mixer_step(h, xbc, z, dt_raw, o, stream=None):
                                      _ptr(o, name="o"), _stream(stream)), "replayssm_mixer_step")
 
 
+def replayssm_mixer_spec_verify(h, T, xbc, z, dt_raw, o, stream=None):
+    _check(_lib.replayssm_mixer_spec_verify(h, int(T), _ptr(xbc, name="xbc"), _ptr(z, name="z"),
+                                            _ptr(dt_raw, name="dt_raw"), _ptr(o, name="o"), _stream(stream)),
+           "replayssm_mixer_spec_verify")
+
+
 def conventional_mixer_step(cfg: Config, state, conv_ring, t, xbc, z, dt_raw, A, D, conv_w, conv_b, dt_bias, o,
                             stream=None):
     Bt, H, P, K, CD = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_conv, conv_dim(cfg)
@@ -426,6 +433,16 @@ class ReplaySSM:
         if o is None:
             o = torch.empty_like(z)
         replayssm_mixer_step(self.handle, xbc, z, dt_raw, o, stream)
+        return o
+
+    def mixer_spec_verify(self, xbc, z, dt_raw, o=None, stream=None):
+        T = xbc.shape[1]
+        _expect(xbc, (self.batch, T, conv_dim(self.cfg)), "xbc")
+        _expect(z, (self.batch, T, self.nheads, self.headdim), "z")
+        _expect(dt_raw, (self.batch, T, self.nheads), "dt_raw")
+        if o is None:
+            o = torch.empty_like(z)
+        replayssm_mixer_spec_verify(self.handle, T, xbc, z, dt_raw, o, stream)
         return o
 
     # workspace views (inspection)

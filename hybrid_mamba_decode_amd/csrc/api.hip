@@ -458,7 +458,27 @@ rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float *x, cons
     if (h->cfg.batch == 0) return RSSM_OK;
     const TokenIO io{x, B, C, dt, y};
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_verify_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, io, T, st)
+#define CALL(NV) launch_verify_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, io, T, false, st)
+    RSSM_BY_N(h->cfg.dstate, CALL)
+#undef CALL
+}
+
+rssm_status replayssm_mixer_spec_verify(replayssm_t h, int32_t T, const float *xbc, const float *z,
+                                        const float *dt_raw, float *o, void *stream)
+{
+    if (!h || h->cfg.d_conv == 0) return RSSM_E_INVAL;
+    const int bt = h->cfg.batch;
+    if (T < 1 || T > h->cfg.max_draft) return RSSM_E_INVAL;
+    if (!ok_ptr4(xbc, bt) || !ok_ptr4(z, bt) || !ok_ptr4(dt_raw, bt) || !ok_ptr4(o, bt)) return RSSM_E_INVAL;
+    if (!h->mixer_set) return RSSM_E_STATE;
+    rssm_status s = ready(h);
+    if (s != RSSM_OK) return s;
+    if (h->pending_T) return RSSM_E_STATE;
+    h->pending_T = T;
+    if (h->cfg.batch == 0) return RSSM_OK;
+    const TokenIO io{nullptr, nullptr, nullptr, dt_raw, o, xbc, z};
+    const hipStream_t st = (hipStream_t)stream;
+#define CALL(NV) launch_verify_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, io, T, true, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
 }

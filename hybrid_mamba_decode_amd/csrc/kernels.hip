@@ -1201,7 +1201,7 @@ struct VerifyLds {
     float decay[TQ];
 };
 
-template <int PREC, int LMAX, int TQ>
+template <int PREC, int LMAX, int TQ, bool MIX>
 __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, int T)
 {
     using G = Geo<NN, PREC>;
@@ -1229,38 +1229,81 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
     }
     const int kw = count0 + T;
     RecSrc src = ring_src(Ld, t, ck, count0);
-    src.fx = io.x + ((size_t)t.b * T * Ld.H + t.h) * Ld.P + t.row0;
-    src.sx = Ld.H * Ld.P;
-    src.fB = io.B + ((size_t)t.b * T * Ld.G + t.g) * NN;
-    src.sB = Ld.G * NN;
-    src.fdt = io.dt + (size_t)t.b * T * Ld.H + t.h;
-    src.sdt = Ld.H;
-
     float cc[TQ][G::VEC];
-#pragma unroll
-    for (int q = 0; q < TQ; ++q) {
-        if (q < T) {
-            load_cchunk<PREC>(cc[q], io.C + (((size_t)t.b * T + q) * Ld.G + t.g) * NN, lane);
-        } else {
-#pragma unroll
-            for (int e = 0; e < G::VEC; ++e) cc[q][e] = 0.f;
-        }
-    }
     constexpr int CQS = (TQ * (NN / 4) + kThreads - 1) / kThreads;
-    f32x4 cqr[CQS];
-#pragma unroll
-    for (int i = 0; i < CQS; ++i) {
-        const int e = tid + i * kThreads, q = e / (NN / 4), c = e % (NN / 4);
-        cqr[i] = q < T ? *(const f32x4 *)(io.C + (((size_t)t.b * T + q) * Ld.G + t.g) * NN + 4 * c)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
     WindowRegs<LMAX> wr;
-    issue_window<LMAX>(wr, src, kw, t.nrows);
-    commit_window<LMAX>(s.win, wr, src, kw);
+    if constexpr (!MIX) {
+        src.fx = io.x + ((size_t)t.b * T * Ld.H + t.h) * Ld.P + t.row0;
+        src.sx = Ld.H * Ld.P;
+        src.fB = io.B + ((size_t)t.b * T * Ld.G + t.g) * NN;
+        src.sB = Ld.G * NN;
+        src.fdt = io.dt + (size_t)t.b * T * Ld.H + t.h;
+        src.sdt = Ld.H;
 #pragma unroll
-    for (int i = 0; i < CQS; ++i) {
-        const int e = tid + i * kThreads, q = e / (NN / 4), c = e % (NN / 4);
-        if (q < TQ) *(f32x4 *)&s.Cq[q][4 * c] = cqr[i];
+        for (int q = 0; q < TQ; ++q) {
+            if (q < T) {
+                load_cchunk<PREC>(cc[q], io.C + (((size_t)t.b * T + q) * Ld.G + t.g) * NN, lane);
+            } else {
+#pragma unroll
+                for (int e = 0; e < G::VEC; ++e) cc[q][e] = 0.f;
+            }
+        }
+        f32x4 cqr[CQS];
+#pragma unroll
+        for (int i = 0; i < CQS; ++i) {
+            const int e = tid + i * kThreads, q = e / (NN / 4), c = e % (NN / 4);
+            cqr[i] = q < T ? *(const f32x4 *)(io.C + (((size_t)t.b * T + q) * Ld.G + t.g) * NN + 4 * c)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        issue_window<LMAX>(wr, src, kw, t.nrows);
+        commit_window<LMAX>(s.win, wr, src, kw);
+#pragma unroll
+        for (int i = 0; i < CQS; ++i) {
+            const int e = tid + i * kThreads, q = e / (NN / 4), c = e % (NN / 4);
+            if (q < TQ) *(f32x4 *)&s.Cq[q][4 * c] = cqr[i];
+        }
+    } else {
+        // Mixer edges: the committed records come from the ring; draft q (position pos + q) is
+        // formed here by the causal conv over the ring's history (positions < pos) and the
+        // drafts' raw xBC (positions >= pos), SiLU, softplus dt. The drafts' raw values enter the
+        // ring at slots (pos + q) mod R, which never hold a position the history still needs
+        // (R = K - 1 + T_max).
+        issue_window<LMAX>(wr, src, count0, t.nrows);
+        commit_window<LMAX>(s.win, wr, src, count0);
+        __syncthreads();  // the draft rows below overwrite the window's zero fill
+        const int R = Ld.R, K = Ld.K;
+        const bool leader = t.split == 0 && t.h % Ld.hpg == 0;
+        auto draft_channel = [&](int q, int c) {
+            const float *w = Ld.conv_w + (size_t)c * K;
+            float u = Ld.conv_b[c];
+            for (int i = 0; i < K; ++i) {
+                const int d = q - (K - 1) + i;  // position pos + d (negative before the first token)
+                const int sl = ((pos + d) % R + R) % R;
+                const float v = d >= 0 ? io.xbc[((size_t)t.b * T + d) * Ld.CD + c]
+                                       : Ld.conv_ring[((size_t)t.b * R + sl) * Ld.CD + c];
+                u = fmaf(w[i], v, u);
+            }
+            if (leader || c < Ld.H * Ld.P)
+                Ld.conv_ring[((size_t)t.b * R + (unsigned)(pos + q) % (unsigned)R) * Ld.CD + c] =
+                    io.xbc[((size_t)t.b * T + q) * Ld.CD + c];
+            return silu_f(u);
+        };
+        for (int e = tid; e < T * kRows; e += kThreads) {
+            const int q = e / kRows, p = e % kRows;
+            if (p < t.nrows) s.win.xw[count0 + q][p] = draft_channel(q, t.h * Ld.P + t.row0 + p);
+        }
+        for (int e = tid; e < T * 2 * NN; e += kThreads) {
+            const int q = e / (2 * NN), n = e % (2 * NN);
+            const int c = Ld.H * Ld.P + (n < NN ? t.g * NN + n : Ld.G * NN + t.g * NN + (n - NN));
+            const float v = draft_channel(q, c);
+            if (n < NN) s.win.Bw[count0 + q][n] = v;
+            else s.Cq[q][n - NN] = v;
+        }
+        if (tid < T) s.win.dts[count0 + tid] = softplus_f(io.dt[((size_t)t.b * T + tid) * Ld.H + t.h] + Ld.dt_bias[t.h]);
+        for (int e = tid; e < (TQ - T) * NN; e += kThreads) s.Cq[T + e / NN][e % NN] = 0.f;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < TQ; ++q) load_cchunk<PREC>(cc[q], s.Cq[q], lane);
     }
 
     float part[G::NL * TQ];
@@ -1327,6 +1370,7 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
             float acc = s.decay[q] * s.u[q][lane];
             for (int j = 0; j <= last; ++j) acc = fmaf(s.coef[q][j], s.win.xw[j][lane], acc);
             acc = fmaf(Dh, s.win.xw[last][lane], acc);
+            if constexpr (MIX) acc *= silu_f(io.z[(((size_t)t.b * T + q) * Ld.H + t.h) * Ld.P + t.row0 + lane]);
             io.y[(((size_t)t.b * T + q) * Ld.H + t.h) * Ld.P + t.row0 + lane] = acc;
             Ld.ring_x[(bh * Ld.L + (unsigned)(pos + q) % (unsigned)Ld.L) * Ld.P + t.row0 + lane] = s.win.xw[last][lane];
         }
@@ -1596,19 +1640,19 @@ hipError_t flush_t(const Layer &Ld, int mode, const int *arg, int T, float *out,
     return hipGetLastError();
 }
 
-template <int PREC, int LMAX, int TQ>
+template <int PREC, int LMAX, int TQ, bool MIX>
 hipError_t verify_t(const Layer &Ld, const TokenIO &io, int T, hipStream_t st)
 {
-    hipLaunchKernelGGL((verify_kernel<PREC, LMAX, TQ>), dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, io, T);
+    hipLaunchKernelGGL((verify_kernel<PREC, LMAX, TQ, MIX>), dim3(nblocks(Ld)), dim3(kThreads), 0, st, Ld, io, T);
     return hipGetLastError();
 }
 
-template <int PREC, int LMAX>
+template <int PREC, int LMAX, bool MIX>
 hipError_t verify_tq(const Layer &Ld, const TokenIO &io, int T, hipStream_t st)
 {
-    if (T <= 2) return verify_t<PREC, LMAX, 2>(Ld, io, T, st);
-    if (T <= 4) return verify_t<PREC, LMAX, 4>(Ld, io, T, st);
-    return verify_t<PREC, LMAX, 8>(Ld, io, T, st);
+    if (T <= 2) return verify_t<PREC, LMAX, 2, MIX>(Ld, io, T, st);
+    if (T <= 4) return verify_t<PREC, LMAX, 4, MIX>(Ld, io, T, st);
+    return verify_t<PREC, LMAX, 8, MIX>(Ld, io, T, st);
 }
 
 template <template <int, int> class F, typename... Args>
@@ -1657,10 +1701,15 @@ struct FlushF {
 };
 template <int PREC, int LMAX>
 struct VerifyF {
-    static hipError_t run(const Layer &Ld, const TokenIO &io, int T, hipStream_t st)
+    static hipError_t run(const Layer &Ld, const TokenIO &io, int T, bool mix, hipStream_t st)
     {
-        if constexpr (!kPrecOk<PREC>) return hipErrorInvalidValue;
-        else return verify_tq<PREC, LMAX>(Ld, io, T, st);
+        if constexpr (!kPrecOk<PREC>) {
+            return hipErrorInvalidValue;
+        } else {
+            if (!mix) return verify_tq<PREC, LMAX, false>(Ld, io, T, st);
+            if constexpr (LMAX <= 32) return verify_tq<PREC, LMAX, true>(Ld, io, T, st);
+            else return hipErrorInvalidValue;  // the mixer edges need L <= 32 (host-checked)
+        }
     }
 };
 
@@ -1692,9 +1741,10 @@ hipError_t RSSM_CAT(launch_flush_n, RSSM_N)(int prec, int lmax, const Layer &Ld,
     return by_prec_lmax<FlushF>(prec, lmax, Ld, mode, arg, T, out, st);
 }
 
-hipError_t RSSM_CAT(launch_verify_n, RSSM_N)(int prec, int lmax, const Layer &Ld, const TokenIO &io, int T, hipStream_t st)
+hipError_t RSSM_CAT(launch_verify_n, RSSM_N)(int prec, int lmax, const Layer &Ld, const TokenIO &io, int T, bool mix,
+                                             hipStream_t st)
 {
-    return by_prec_lmax<VerifyF>(prec, lmax, Ld, io, T, st);
+    return by_prec_lmax<VerifyF>(prec, lmax, Ld, io, T, mix, st);
 }
 
 hipError_t RSSM_CAT(launch_load_n, RSSM_N)(int prec, const Layer &Ld, const float *state, hipStream_t st)

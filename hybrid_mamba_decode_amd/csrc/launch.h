@@ -16,7 +16,7 @@ enum { MODE_MASK = 0, MODE_OVERFULL = 1, MODE_MATERIALIZE = 2 };
     hipError_t launch_flush_n##NV(int prec, int lmax, const Layer &Ld, int mode, const int *arg, int T,  \
                                   float *out, hipStream_t st);                                         \
     hipError_t launch_verify_n##NV(int prec, int lmax, const Layer &Ld, const TokenIO &io, int T,       \
-                                   hipStream_t st);                                                    \
+                                   bool mix, hipStream_t st);                                          \
     hipError_t launch_load_n##NV(int prec, const Layer &Ld, const float *state, hipStream_t st);        \
     hipError_t launch_conventional_n##NV(const Layer &Ld, float *state, const TokenIO &io,             \
                                          hipStream_t st);                                              \

@@ -186,7 +186,9 @@ rssm_status replayssm_step(replayssm_t layer, const float *x, const float *B, co
  *   o[h,p] = y[h,p] * silu(z[h,p]).
  * The conv history is the raw xBC of the K-1 committed positions before pos, kept in the
  * workspace ring keyed by position, so a rollback cuts it back with the records (no copy). A
- * mixer handle takes mixer calls: replayssm_step and replayssm_spec_verify return RSSM_E_INVAL. */
+ * mixer handle takes mixer calls: replayssm_step and replayssm_spec_verify return RSSM_E_INVAL.
+ * Lockstep graph capture: the step's arguments (window slots and the ring slot pos mod R)
+ * repeat every lcm(L, R) steps, so a captured run of such a multiple replays correctly. */
 
 /* Give the edge parameters (device fp32, caller-owned, outliving their use): conv_w [CD,K],
  * conv_b [CD], dt_bias [H]. RSSM_E_INVAL on a handle with d_conv = 0 or a NULL / misaligned
@@ -208,6 +210,14 @@ rssm_status replayssm_materialize_conv_state(replayssm_t layer, float *out, void
  * flush rule. Float arrays 4-byte aligned. */
 rssm_status replayssm_mixer_step(replayssm_t layer, const float *xbc, const float *z,
                                  const float *dt_raw, float *o, void *stream);
+
+/* Speculative verify with the mixer edges (as replayssm_spec_verify): T drafts xbc [Bt,T,CD],
+ * z [Bt,T,H,P], dt_raw [Bt,T,H]; draft i's conv runs over the committed history and drafts
+ * 0..i; outputs o [Bt,T,H,P] (gated). The drafts' raw xBC enter the conv ring at slots
+ * (pos + i) mod R; replayssm_rollback then keeps the accepted prefix's history by the pointer
+ * move alone. */
+rssm_status replayssm_mixer_spec_verify(replayssm_t layer, int32_t T, const float *xbc, const float *z,
+                                        const float *dt_raw, float *o, void *stream);
 
 /* Fold every committed record of the selected sequences into the checkpoint (seq_mask: device
  * int32 [Bt], nonzero = flush; NULL = all), rewrite their read copy, set ckpt_pos = pos.

@@ -340,6 +340,12 @@ def test_mixer_entry_points_on_host():
     assert L.replayssm_mixer_step(mix, FAKE + 2, FAKE, FAKE, FAKE, None) == rs.RSSM_E_INVAL
     assert L.replayssm_step(mix, *([FAKE] * 5), None) == rs.RSSM_E_INVAL         # plain calls refused
     assert L.replayssm_spec_verify(mix, 2, *([FAKE] * 5), None) == rs.RSSM_E_INVAL
+    assert L.replayssm_mixer_spec_verify(plain, 2, *io, None) == rs.RSSM_E_INVAL
+    assert L.replayssm_mixer_spec_verify(mix, 3, *io, None) == rs.RSSM_E_INVAL     # T > max_draft
+    assert L.replayssm_mixer_spec_verify(mix, 2, *io, None) == rs.RSSM_OK
+    assert L.replayssm_mixer_step(mix, *io, None) == rs.RSSM_E_STATE              # verify pending
+    assert L.replayssm_load_conv_state(mix, None, None) == rs.RSSM_E_STATE
+    assert L.replayssm_rollback(mix, FAKE, None) == rs.RSSM_OK
     assert L.replayssm_materialize_conv_state(mix, FAKE, None) == rs.RSSM_OK
     assert L.replayssm_materialize_conv_state(mix, FAKE + 2, None) == rs.RSSM_E_INVAL
     for h in (plain, mix):

@@ -188,3 +188,62 @@ def test_mixer_graph_replay_of_whole_windows():
         assert np.array_equal(host(lay.materialize_conv_state()), truth.hist)
         _ = torch.ones(1 << 20, device="cuda").sum().item()
     assert lay.check() == rs.RSSM_OK
+
+
+def _spec_case(case, iters, sample, interleave=True):
+    log(f"[mixer spec] Bt={case.Bt} H={case.H} P={case.P} N={case.N} G={case.G} L={case.L} K={case.K} "
+        f"T={case.Tmax} iters={iters} sample={list(sample)}")
+    T = case.Tmax
+    lay = case.layer()
+    sample = np.asarray(sample)
+    truth = oracle.MixerStepwise(case.S0[sample], case.h0[sample], case.A, case.D, case.w, case.b, case.bias, case.G)
+    model = oracle.MixerReplay(case.S0[sample], case.h0[sample], case.A, case.D, case.w, case.b, case.bias, case.G,
+                               case.L, T, seq_ids=sample)
+    ptr = oracle.MixerReplay(np.zeros((case.Bt, 1, 1, 1), np.float32), np.zeros((case.Bt, case.K - 1, 3), np.float32),
+                             np.array([-1.0], np.float32), np.zeros(1, np.float32), np.zeros((3, case.K), np.float32),
+                             np.zeros(3, np.float32), np.zeros(1, np.float32), 1, case.L, T)   # pointer machine
+    for it in range(iters):
+        if interleave and it % 3 == 2:
+            xbc, z, dt_raw = case.inputs(1000 + it)
+            o = host(lay.mixer_step(dev(xbc), dev(z), dev(dt_raw)))[sample]
+            sub = (xbc[sample], z[sample], dt_raw[sample])
+            assert rel(o, truth.step(*sub)) <= TOL_F32 and rel(o, model.step(*sub)) <= TOL_F32, f"step {it}"
+            ptr.step(np.zeros((case.Bt, 3), np.float32), np.zeros((case.Bt, 1, 1), np.float32), np.zeros((case.Bt, 1), np.float32))
+        else:
+            xbc, z, dt_raw = workload.mixer_draft_inputs(case.seed, it, case.Bt, T, case.H, case.P, case.G, case.N)
+            acc = workload.accepted_counts(case.seed, it, case.Bt, T)
+            acc[it % case.Bt] = T if it % 2 else 0
+            o = host(lay.mixer_spec_verify(dev(xbc), dev(z), dev(dt_raw)))[sample]
+            lay.rollback(dev(acc))
+            sub = (xbc[sample], z[sample], dt_raw[sample])
+            o_true = truth.spec(T, *sub, acc[sample])
+            o_model = model.verify(T, *sub)
+            model.rollback(acc[sample])
+            assert rel(o, o_true) <= TOL_F32, f"verify {it}: vs truth {rel(o, o_true):.2e}"
+            assert rel(o, o_model) <= TOL_F32, f"verify {it}: vs replay model {rel(o, o_model):.2e}"
+            ptr.verify(T, np.zeros((case.Bt, T, 3), np.float32), np.zeros((case.Bt, T, 1, 1), np.float32),
+                       np.zeros((case.Bt, T, 1), np.float32))
+            ptr.rollback(acc)
+        pos, ck = lay.get_pointers()
+        opos, ock = ptr.pointers()
+        assert pos == list(opos) and ck == list(ock), f"iteration {it}: pointers"
+        assert np.array_equal(host(lay.materialize_conv_state())[sample], truth.hist), f"iteration {it}: conv history"
+        assert rel(host(lay.materialize_state())[sample], truth.S) <= TOL_F32
+    assert lay.check() == rs.RSSM_OK
+
+
+@pytest.mark.parametrize("T,L,K", [(1, 4, 4), (3, 7, 4), (4, 16, 3), (8, 16, 4)])
+def test_mixer_spec_verify_rollback(T, L, K):
+    """Verify T drafts through the edges (each draft's conv over the committed history and the
+    drafts before it), roll back by accepted counts 0..T, standard mixer steps interleaved: all
+    T outputs vs the per-draft truth and the replay model, the conv history after each rollback
+    is the accepted prefix's (bit for bit), pointers bit-exact."""
+    case = MixCase(3, 6, 32, 64, 2, L, K, 40 + T, Tmax=T)
+    _spec_case(case, 18, range(3))
+
+
+def test_mixer_spec_serving_batch512_T4():
+    """Batch 512 of the serving layer with the edges, T = 4, L = 16: sequences 7 and 400."""
+    c = workload.MIXER
+    case = MixCase(512, c["H"], c["P"], c["N"], c["G"], c["L"], c["K"], 41, Tmax=4)
+    _spec_case(case, 12, [7, 400])
