@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--kernels-only", action="store_true",
                     help="only the replay steps (for profiler runs)")
-    ap.add_argument("--workload", default="serving", choices=["serving", "spec", "sweep", "gdn"],
+    ap.add_argument("--workload", default="serving", choices=["serving", "spec", "sweep", "gdn", "mixer"],
                     help="serving: the headline line; spec: batch 512, T=4 verify+rollback vs "
                          "per-draft snapshots; sweep: batch x L over a 10-layer stack")
     ap.add_argument("--calib-copy", action="store_true",

@@ -7,6 +7,10 @@ spec:  speculative decode on the serving layer -- batch 512, T = 4 drafts, accep
 gdn:   a Gated DeltaNet layer (32 value heads, 16 key heads, Dv = Dk = 128) at batch 256, L = 16:
        the replay step (non-flush and flush launches, 256 steps = 16 windows) against the
        conventional step, and speculative decode at batch 512, T = 4 against per-draft snapshots.
+mixer: the serving layer with the Mamba-2 mixer edges fused (conv1d width 4 over xBC, softplus
+       dt, output gate), batch 256, L = 16: the fused mixer step (256 steps = 16 windows) against
+       the plain replay step on precomputed x, B, C, dt and the conventional step with the same
+       fused edges.
 sweep: the serving head shape stacked as 10 independent layers, batch in {1, 8, 64, 256, 512} x
        buffer length in {4, 8, 16, 32}, 64 decode steps: per-layer tokens/s of the replay step
        (amortized over whole windows) and of the conventional step, eager and as HIP graphs
@@ -339,8 +343,87 @@ def gdn(args):
     print(json.dumps(out), flush=True)
 
 
+def mixer(args):
+    c = workload.MIXER
+    Bt, L, K = c["Bt"], c["L"], c["K"]
+    CD = rs.conv_dim(rs.make_config(Bt, H, P, N, G))
+    A, D = _layer_params()
+    w, b, bias = (torch.from_numpy(a).cuda() for a in workload.mixer_params(workload.config_seed(8), H, P, G, N, K))
+    g = _gen(8008)
+    S0 = torch.randn(Bt, H, P, N, device="cuda", generator=g)
+    hist = torch.randn(Bt, K - 1, CD, device="cuda", generator=g)
+    pool = [(torch.randn(Bt, CD, device="cuda", generator=g), torch.randn(Bt, H, P, device="cuda", generator=g),
+             torch.randn(Bt, H, device="cuda", generator=g)) for _ in range(16)]
+    plain_pool = [_tokens(g, (Bt,), N) for _ in range(16)]
+    o = torch.empty(Bt, H, P, device="cuda")
+    lay = rs.ReplaySSM(Bt, H, P, N, G, A, D, buffer_len=L, d_conv=K)
+    lay.set_mixer(w, b, bias)
+
+    def mix_step(r):
+        rs.replayssm_mixer_step(lay.handle, *pool[r % len(pool)], o)
+    lay.load_state(S0)
+    lay.load_conv_state(hist)
+    _timed(mix_step, 2 * L)
+    lay.load_state(S0)
+    lay.load_conv_state(hist)
+    steps = 16 * L
+    wall, d = _timed(mix_step, steps)
+    assert lay.check() == rs.RSSM_OK
+    assert torch.isfinite(o).all().item()
+    del lay
+    ks = np.array([r % L + 1 for r in range(steps)])
+    fl = ks == L
+    pb = traffic.mixer_param_bytes(H, P, N, G, K)
+    nf_bytes = np.array([traffic.replay_mixer_nonflush(H, P, N, G, int(k), K) * Bt + pb for k in ks[~fl]])
+    fl_bytes = traffic.replay_mixer_flush_step(H, P, N, G, L, K) * Bt + pb
+    nf_gbps = float((nf_bytes / d[~fl]).mean()) / 1e9
+
+    plain = rs.ReplaySSM(Bt, H, P, N, G, A, D, buffer_len=L)
+
+    def plain_step(r):
+        rs.replayssm_step(plain.handle, *plain_pool[r % len(plain_pool)], o)
+    plain.load_state(S0)
+    _timed(plain_step, 2 * L)
+    plain.load_state(S0)
+    wall_p, dp = _timed(plain_step, steps)
+    del plain
+
+    cfg = rs.make_config(Bt, H, P, N, G, d_conv=K)
+    ring = torch.zeros(Bt, K, CD, device="cuda")
+    cst = S0.clone()
+
+    def conv_step(r):
+        rs.conventional_mixer_step(cfg, cst, ring, r, *pool[r % len(pool)], A, D, w, b, bias, o)
+    _timed(conv_step, 4)
+    wall_c, dc = _timed(conv_step, 64)
+    conv_bytes = traffic.conventional_mixer(H, P, N, G, K) * Bt + pb
+    unfused = np.array([traffic.unfused_mixer_nonflush(H, P, N, G, int(k), K) for k in ks[~fl]]).mean() * Bt
+    out = {
+        "workload": f"Mamba-2 layer decode step with the mixer edges fused (conv1d width {K} over {CD} xBC "
+                    f"channels, softplus dt, output gate), batch {Bt}, 128 heads, P 64, N 128, 8 groups, L {L}, fp32",
+        "replay_mixer": {"tokens_per_s_layer": round(Bt * steps / wall, 1),
+                         "nonflush_mean_us": round(float(d[~fl].mean()) * 1e6, 2),
+                         "nonflush_gbps": round(nf_gbps, 1), "nonflush_frac_of_8tbs": round(nf_gbps / PEAK, 4),
+                         "nonflush_alg_bytes_per_launch": int(nf_bytes.mean()),
+                         "flush_mean_us": round(float(d[fl].mean()) * 1e6, 2),
+                         "flush_gbps": round(fl_bytes / float(d[fl].mean()) / 1e9, 1)},
+        "replay_plain_step": {"tokens_per_s_layer": round(Bt * steps / wall_p, 1),
+                              "nonflush_mean_us": round(float(dp[~fl].mean()) * 1e6, 2),
+                              "flush_mean_us": round(float(dp[fl].mean()) * 1e6, 2)},
+        "conventional_mixer": {"tokens_per_s_layer": round(Bt * 64 / wall_c, 1),
+                               "mean_us": round(float(dc.mean()) * 1e6, 2),
+                               "gbps": round(conv_bytes / float(dc.mean()) / 1e9, 1)},
+        "speedup_vs_conventional_mixer": round((Bt * steps / wall) / (Bt * 64 / wall_c), 3),
+        "edge_cost_vs_plain_step": round(float(d[~fl].mean()) / float(dp[~fl].mean()), 4),
+        "alg_bytes_per_launch_unfused_pipeline_model": int(unfused),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def run(args):
-    if args.workload == "spec":
+    if args.workload == "mixer":
+        mixer(args)
+    elif args.workload == "spec":
         spec(args)
     elif args.workload == "gdn":
         gdn(args)

@@ -385,6 +385,7 @@ rssm_status replayssm_set_mixer(replayssm_t h, const float *conv_w, const float 
     h->dev.conv_w = conv_w;
     h->dev.conv_b = conv_b;
     h->dev.dt_bias = dt_bias;
+    h->dev.wvec = h->cfg.d_conv == 4 && aligned(conv_w, 16);
     h->mixer_set = 1;
     return RSSM_OK;
 }
@@ -589,6 +590,7 @@ rssm_status conventional_mixer_step(const replayssm_config *cfg, float *state, f
     Ld.dt_bias = dt_bias;
     Ld.K = Ld.R = cfg->d_conv;
     Ld.CD = (int)conv_dim(*cfg);
+    Ld.wvec = cfg->d_conv == 4 && aligned(conv_w, 16);
     const TokenIO io{nullptr, nullptr, nullptr, dt_raw, o, xbc, z};
     const int rslot = t % cfg->d_conv;
     const hipStream_t st = (hipStream_t)stream;

@@ -61,6 +61,7 @@ struct Layer {
     const float *conv_b;    // [CD]
     const float *dt_bias;   // [H]
     int K, R, CD;
+    int wvec;               // K == 4 and conv_w 16-byte aligned: a channel's weights in one load
 };
 
 // Per-token inputs of one call (layouts in replayssm.h).
@@ -83,19 +84,59 @@ struct Lockstep {
 __device__ inline float silu_f(float v) { return v / (1.0f + expf(-v)); }
 __device__ inline float softplus_f(float v) { return v > 0.f ? v + log1pf(expf(-v)) : log1pf(expf(v)); }
 
-// One channel c of the causal depthwise conv for sequence b at position pos (ring slot rslot):
-// bias + the K-1 history taps from the ring (oldest first) + this token's raw value `cur`,
-// then SiLU. The ring slots of positions pos-K+1 .. pos-1 are never the one written this step.
-__device__ inline float conv_channel(const Layer &Ld, int b, int c, int rslot, float cur)
+// One conv channel's operands in registers (K <= 4): issued early by conv_issue, consumed by
+// conv_finish, so that the loads go out with a kernel's other early loads.
+struct ConvIn {
+    float cur, wc, b, tap[3], wt[3];
+};
+
+// Ring element of sequence b, channel c, slot sl ([Bt,R,CD]: a wave's channels are contiguous).
+__device__ inline size_t ring_at(const Layer &Ld, int b, int c, int sl)
 {
-    const float *w = Ld.conv_w + (size_t)c * Ld.K;
-    const float *ring = Ld.conv_ring + (size_t)b * Ld.R * Ld.CD + c;
-    float u = fmaf(w[Ld.K - 1], cur, Ld.conv_b[c]);
-    for (int i = 0; i < Ld.K - 1; ++i) {
+    return ((size_t)b * Ld.R + sl) * Ld.CD + c;
+}
+
+// Operands of channel c for sequence b at position pos (ring slot rslot): this token's raw value
+// from raw, its weight and the bias, and the K-1 history taps (oldest first) with their weights.
+// K = 4 with aligned weights: the channel's weights in one 16-byte load. Unused taps
+// (i >= K-1) read slot 0 and weight 0 of the channel, so every address stays inside its rows.
+__device__ inline ConvIn conv_issue(const Layer &Ld, int b, int c, int rslot, const float *raw)
+{
+    ConvIn r;
+    r.cur = raw[c];
+    r.b = Ld.conv_b[c];
+    bool in[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        in[i] = i < Ld.K - 1;
         const int d = Ld.K - 1 - i;  // position pos - d
-        const int sl = rslot >= d ? rslot - d : rslot - d + Ld.R;
-        u = fmaf(w[i], ring[(size_t)sl * Ld.CD], u);
+        const int sl = !in[i] ? 0 : rslot >= d ? rslot - d : rslot - d + Ld.R;
+        const float v = Ld.conv_ring[ring_at(Ld, b, c, sl)];
+        r.tap[i] = in[i] ? v : 0.f;
     }
+    const float *w = Ld.conv_w + (size_t)c * Ld.K;
+    if (Ld.wvec) {
+        const f32x4 w4 = *(const f32x4 *)w;
+        r.wt[0] = w4.x;
+        r.wt[1] = w4.y;
+        r.wt[2] = w4.z;
+        r.wc = w4.w;
+    } else {
+        r.wc = w[Ld.K - 1];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const float wv = w[in[i] ? i : 0];
+            r.wt[i] = in[i] ? wv : 0.f;
+        }
+    }
+    return r;
+}
+
+__device__ inline float conv_finish(const ConvIn &r)
+{
+    float u = fmaf(r.wc, r.cur, r.b);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) u = fmaf(r.wt[i], r.tap[i], u);
     return silu_f(u);
 }
 

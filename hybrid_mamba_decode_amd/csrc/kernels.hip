@@ -626,6 +626,32 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         if (PREC == PREC_FP8) scl_r = Ld.scale[bh0 + (tid < ROWS ? tid / kRows : 0)];
     };
 
+    // Mixer edges: this token's x rows (one per thread), the group's B and C (channels e < 2N,
+    // B first) from the causal conv over the ring's history and this token's raw xBC, and the
+    // gate input z of this thread's output row. Their loads are issued with the window (ahead of
+    // the checkpoint stream in lockstep, so consuming them waits for nothing else); the raw
+    // values enter the ring at slot pos mod R (x channels by every work-group for its rows, B / C
+    // by the group's first work-group) when the results are committed.
+    constexpr int BCT = (2 * NN + kThreads - 1) / kThreads;
+    ConvIn cx, cbc[BCT];
+    float zg = 0.f;
+    int mix_rslot = 0;
+    auto issue_mix = [&](int rslot) {
+        mix_rslot = rslot;
+        const float *raw = io.xbc + (size_t)t.b * Ld.CD;
+        if (tid < ROWS) {  // whole waves: the threads that own an output row
+            const int hh = tid / kRows, p = tid % kRows;
+            const int row = t.row0 + (p < t.nrows ? p : 0);
+            cx = conv_issue(Ld, t.b, (t.h + hh) * Ld.P + row, rslot, raw);
+            zg = io.z[(bh0 + hh) * Ld.P + row];
+        }
+#pragma unroll
+        for (int i = 0; i < BCT; ++i) {
+            const int e = tid + i * kThreads, ee = e < 2 * NN ? e : 0;
+            const int c = Ld.H * Ld.P + (ee < NN ? t.g * NN + ee : Ld.G * NN + t.g * NN + (ee - NN));
+            cbc[i] = conv_issue(Ld, t.b, c, rslot, raw);
+        }
+    };
     if (uni) {
         // window first: its staging and weights then overlap the checkpoint stream
         pslot = ls.pslot;
@@ -634,6 +660,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         if constexpr (kHalfPre)
             if (k > Ld.L - Ld.Tmax) load_master_half();
         issue_window();
+        if constexpr (MIX) issue_mix(ls.rslot);
         if (kPreload) load_state();
     } else {
         // checkpoint stream first; the window addresses wait for this sequence's pointers
@@ -652,42 +679,10 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         if constexpr (kHalfPre)
             if (k > Ld.L - Ld.Tmax) load_master_half();
         issue_window();
+        if constexpr (MIX) issue_mix((int)((unsigned)pos % (unsigned)Ld.R));
     }
     const bool flush = k > Ld.L - Ld.Tmax;
 
-    // Mixer edges: this token's x rows (one per thread), the group's B and C (channels e < 2N,
-    // B first) from the causal conv over the ring's history and this token's raw xBC, and the
-    // gate input z of this thread's output row. The raw values enter the ring at slot pos mod R
-    // (x channels by every work-group for its rows, B / C by the group's first work-group).
-    constexpr int BCT = (2 * NN + kThreads - 1) / kThreads;
-    float mx = 0.f, zg = 0.f, mbc[BCT];
-    if constexpr (MIX) {
-        const int rslot = uni ? ls.rslot : (int)((unsigned)dpos % (unsigned)Ld.R);
-        const float *raw = io.xbc + (size_t)t.b * Ld.CD;
-        float *ring_now = Ld.conv_ring + ((size_t)t.b * Ld.R + rslot) * Ld.CD;
-        if (tid < ROWS) {
-            const int hh = tid / kRows, p = tid % kRows;
-            const bool in = p < t.nrows;
-            const int c = (t.h + hh) * Ld.P + t.row0 + (in ? p : 0);
-            const float cur = raw[c];
-            const float v = conv_channel(Ld, t.b, c, rslot, cur);
-            mx = in ? v : 0.f;
-            zg = io.z[(bh0 + hh) * Ld.P + t.row0 + (in ? p : 0)];
-            if (in) ring_now[c] = cur;
-        }
-        const bool leader = t.split == 0 && t.h % Ld.hpg == 0;
-#pragma unroll
-        for (int i = 0; i < BCT; ++i) {
-            const int e = tid + i * kThreads;
-            mbc[i] = 0.f;
-            if (e < 2 * NN) {
-                const int c = Ld.H * Ld.P + (e < NN ? t.g * NN + e : Ld.G * NN + t.g * NN + (e - NN));
-                const float cur = raw[c];
-                mbc[i] = conv_channel(Ld, t.b, c, rslot, cur);
-                if (leader) ring_now[c] = cur;
-            }
-        }
-    }
     // Pointer update, once per sequence. Lockstep: the work-group owning head 0 checks the device
     // pointers against the window position (a mismatch means they were corrupted: flag, no
     // update) and advances them; device mode: the last work-group of the sequence writes them.
@@ -733,12 +728,24 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         }
     }
     if constexpr (MIX) {
-        if (tid < ROWS) s.xw[k - 1][tid] = mx;
+        if (tid < ROWS) {
+            const int hh = tid / kRows, p = tid % kRows;
+            const bool in = p < t.nrows;
+            s.xw[k - 1][tid] = in ? conv_finish(cx) : 0.f;
+            if (in) Ld.conv_ring[ring_at(Ld, t.b, (t.h + hh) * Ld.P + t.row0 + p, mix_rslot)] = cx.cur;
+        }
+        const bool leader = t.split == 0 && t.h % Ld.hpg == 0;
 #pragma unroll
         for (int i = 0; i < BCT; ++i) {
             const int e = tid + i * kThreads;
-            if (e < NN) s.Bw[k - 1][e] = mbc[i];
-            else if (e < 2 * NN) s.Cq[e - NN] = mbc[i];
+            if (e < 2 * NN) {
+                const float v = conv_finish(cbc[i]);
+                if (e < NN) s.Bw[k - 1][e] = v;
+                else s.Cq[e - NN] = v;
+                if (leader)
+                    Ld.conv_ring[ring_at(Ld, t.b, Ld.H * Ld.P + (e < NN ? t.g * NN + e : Ld.G * NN + t.g * NN + (e - NN)),
+                                         mix_rslot)] = cbc[i].cur;
+            }
         }
     } else {
         if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = cq;
@@ -1280,11 +1287,11 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
                 const int d = q - (K - 1) + i;  // position pos + d (negative before the first token)
                 const int sl = ((pos + d) % R + R) % R;
                 const float v = d >= 0 ? io.xbc[((size_t)t.b * T + d) * Ld.CD + c]
-                                       : Ld.conv_ring[((size_t)t.b * R + sl) * Ld.CD + c];
+                                       : Ld.conv_ring[ring_at(Ld, t.b, c, sl)];
                 u = fmaf(w[i], v, u);
             }
             if (leader || c < Ld.H * Ld.P)
-                Ld.conv_ring[((size_t)t.b * R + (unsigned)(pos + q) % (unsigned)R) * Ld.CD + c] =
+                Ld.conv_ring[ring_at(Ld, t.b, c, (int)((unsigned)(pos + q) % (unsigned)R))] =
                     io.xbc[((size_t)t.b * T + q) * Ld.CD + c];
             return silu_f(u);
         };
@@ -1470,25 +1477,23 @@ __global__ void __launch_bounds__(kThreads) conventional_mixer_kernel(Layer Ld, 
     const float dtv = softplus_f(io.dt[bh] + Ld.dt_bias[t.h]);
     const float a = expf(dtv * Ld.A[t.h]);
     const float *raw = io.xbc + (size_t)t.b * Ld.CD;
-    float *ring_now = Ld.conv_ring + ((size_t)t.b * Ld.R + rslot) * Ld.CD;
     float zg = 0.f;
     if (tid < kRows) {
         const bool in = tid < t.nrows;
         const int c = t.h * Ld.P + t.row0 + (in ? tid : 0);
-        const float cur = raw[c];
-        const float v = conv_channel(Ld, t.b, c, rslot, cur);
-        xs[tid] = in ? v : 0.f;
+        const ConvIn ci = conv_issue(Ld, t.b, c, rslot, raw);
         zg = io.z[bh * Ld.P + t.row0 + (in ? tid : 0)];
-        if (in) ring_now[c] = cur;
+        xs[tid] = in ? conv_finish(ci) : 0.f;
+        if (in) Ld.conv_ring[ring_at(Ld, t.b, c, rslot)] = ci.cur;
     }
     const bool leader = t.split == 0 && t.h % Ld.hpg == 0;
     for (int e = tid; e < 2 * NN; e += kThreads) {
         const int c = Ld.H * Ld.P + (e < NN ? t.g * NN + e : Ld.G * NN + t.g * NN + (e - NN));
-        const float cur = raw[c];
-        const float v = conv_channel(Ld, t.b, c, rslot, cur);
+        const ConvIn ci = conv_issue(Ld, t.b, c, rslot, raw);
+        const float v = conv_finish(ci);
         if (e < NN) bs[e] = v;
         else cs[e - NN] = v;
-        if (leader) ring_now[c] = cur;
+        if (leader) Ld.conv_ring[ring_at(Ld, t.b, c, rslot)] = ci.cur;
     }
     __syncthreads();
     float bc[4], cc[4];

@@ -129,3 +129,49 @@ def gdn_verify(H, G, Dv, Dk, T, k_old):
 
 def gdn_snapshot_verify(H, G, Dv, Dk, T):
     return (1 + T) * gdn_state_bytes(H, Dv, Dk) + T * (gdn_token_input_bytes(H, G, Dv, Dk) + F32 * H * Dv)
+
+
+# ---- Mamba-2 mixer edges (causal conv of width K over CD = H*P + 2*G*N channels; gate z) --------
+def conv_dim(H, P, N, G):
+    return H * P + 2 * G * N
+
+
+def mixer_edge_bytes(H, P, N, G, K):
+    """Per sequence and token, what the edges add to a step: the raw xBC read, its K-1 history
+    taps read and its write into the conv ring, and z read. dt_raw replaces dt and the gated
+    output replaces y, so they are counted where the step counts dt and y."""
+    CD = conv_dim(H, P, N, G)
+    return F32 * (CD + (K - 1) * CD + CD + H * P)
+
+
+def mixer_param_bytes(H, P, N, G, K):
+    """Per launch: conv weights and bias, dt_bias (shared by every sequence)."""
+    CD = conv_dim(H, P, N, G)
+    return F32 * (CD * K + CD + H)
+
+
+def _edge_delta(H, P, N, G, K):
+    # x, B, C are formed in the launch instead of read
+    return mixer_edge_bytes(H, P, N, G, K) - F32 * (H * P + 2 * G * N)
+
+
+def replay_mixer_nonflush(H, P, N, G, k, K, prec="fp32", store_C=True):
+    return replay_nonflush(H, P, N, G, k, prec, store_C) + _edge_delta(H, P, N, G, K)
+
+
+def replay_mixer_flush_step(H, P, N, G, L, K, prec="fp32", master="fp32"):
+    return replay_flush_step(H, P, N, G, L, prec, master) + _edge_delta(H, P, N, G, K)
+
+
+def conventional_mixer(H, P, N, G, K):
+    return conventional(H, P, N, G) + _edge_delta(H, P, N, G, K)
+
+
+def unfused_mixer_nonflush(H, P, N, G, k, K, prec="fp32", store_C=True):
+    """The same token through three launches: an edge kernel (raw xBC, taps and ring write as
+    above, dt_raw read; x, B, C, dt written), the plain replay step, and a gate kernel (y and z
+    read, o written)."""
+    CD = conv_dim(H, P, N, G)
+    edge = F32 * (CD + (K - 1) * CD + CD + H + (H * P + 2 * G * N + H))
+    gate = F32 * 3 * H * P
+    return edge + replay_nonflush(H, P, N, G, k, prec, store_C) + gate

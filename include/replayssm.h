@@ -270,9 +270,10 @@ rssm_status conventional_step(const replayssm_config *cfg, float *state, const f
                               const float *D, float *y, void *stream);
 
 /* Baseline with the mixer edges: conventional_step with the same fused edges as
- * replayssm_mixer_step. conv_ring [Bt,K,CD] (device fp32, in/out) holds the raw xBC of position
- * q in slot q mod K; t >= 0 is this token's position (the caller keeps it; positions before 0
- * are the initial history). K = cfg->d_conv (2..4); state, A, D as conventional_step. */
+ * replayssm_mixer_step. conv_ring [Bt,K,CD] (device fp32, in/out) holds the raw xBC of
+ * position q in slot q mod K; t >= 0 is this token's position (the caller
+ * keeps it; positions before 0 are the initial history). K = cfg->d_conv (2..4); state, A, D as
+ * conventional_step. */
 rssm_status conventional_mixer_step(const replayssm_config *cfg, float *state, float *conv_ring, int32_t t,
                                     const float *xbc, const float *z, const float *dt_raw, const float *A,
                                     const float *D, const float *conv_w, const float *conv_b,

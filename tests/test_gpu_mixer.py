@@ -144,7 +144,7 @@ def test_fresh_history_is_zero():
 
 def test_conventional_mixer_step():
     """The baseline with the same edges, against the stepwise mixer truth; its ring of K slots
-    holds position q at slot q mod K (the initial history at positions -3..-1)."""
+    ([Bt, K, CD]) holds position q at slot q mod K (the initial history at positions -3..-1)."""
     c = workload.MIXER_TINY
     case = MixCase(c["Bt"], c["H"], c["P"], c["N"], c["G"], c["L"], c["K"], 37)
     K = case.K
