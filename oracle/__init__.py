@@ -102,7 +102,9 @@ def lib():
         L.oracle_gdn_step.argtypes = [_i] * 5 + [_f64p] + [_f32p] * 5 + [_f64p]
         L.oracle_gdn_spec_stepwise.argtypes = [_i] * 6 + [_f64p] + [_f32p] * 5 + [_i32p, _f64p]
         L.oracle_gdn_spec_stepwise.restype = _i
-        L.oracle_gdn_create.argtypes = [_i] * 7 + [_f32p]
+        L.oracle_gdn_create.argtypes = [_i] * 7 + [_f32p, _i]
+        L.oracle_gdn_replay_read_copy.argtypes = [ctypes.c_void_p, _f64p]
+        L.oracle_gdn_replay_read_copy.restype = None
         L.oracle_gdn_create.restype = ctypes.c_void_p
         L.oracle_gdn_destroy.argtypes = [ctypes.c_void_p]
         L.oracle_gdn_replay_step.argtypes = [ctypes.c_void_p] + [_f32p] * 5 + [_f64p]
@@ -334,11 +336,13 @@ def gdn_spec_stepwise(S, T, q, k, v, alpha, beta, accepted):
 class GDNReplay:
     """O3g + O4: the GDN replay form (checkpoint + records, backward sweep) and its pointer machine."""
 
-    def __init__(self, S0, G, L, Tmax=1):
+    def __init__(self, S0, G, L, Tmax=1, read_prec=READ_FP32):
+        """read_prec READ_BF16: the checkpoint product of replayed outputs reads a bf16 copy of
+        the checkpoint (reading G4); READ_FP32: the checkpoint itself."""
         S0 = _f32(S0)
         self.Bt, self.H, self.Dv, self.Dk = S0.shape
-        self.G, self.L, self.Tmax = G, L, Tmax
-        self._h = lib().oracle_gdn_create(self.Bt, self.H, G, self.Dv, self.Dk, L, Tmax, S0)
+        self.G, self.L, self.Tmax, self.read_prec = G, L, Tmax, read_prec
+        self._h = lib().oracle_gdn_create(self.Bt, self.H, G, self.Dv, self.Dk, L, Tmax, S0, int(read_prec))
         if not self._h:
             raise ValueError("invalid GDN replay configuration")
 
@@ -386,6 +390,10 @@ class GDNReplay:
 
     def checkpoint(self):
         return self._state(lib().oracle_gdn_replay_checkpoint)
+
+    def read_copy(self):
+        """The decoded bf16 read copy (float64), or None without one."""
+        return self._state(lib().oracle_gdn_replay_read_copy) if self.read_prec else None
 
     def materialize(self):
         return self._state(lib().oracle_gdn_replay_materialize)

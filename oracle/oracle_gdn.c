@@ -21,6 +21,10 @@
  *     z <- q_t;  for j = t, ..., 0:  c_j = beta_j (k_j . z);  z <- alpha_j (z - c_j k_j).
  * A flush folds the records into the checkpoint by applying them in order (the recurrence
  * itself); pointer and flush rules are those of oracle.c (readings R2, R5, R6, R10).
+ * Reading G4: as for Mamba-2 ([AT Pulse] "Technical analysis": a high-precision checkpoint drives
+ * the recurrence, a low-precision copy serves reads), the replay's checkpoint product S_c z may
+ * read a bf16 copy of the checkpoint, written at load and at every flush from the checkpoint
+ * rounded to fp32; flushes fold into the checkpoint itself and read their output from it.
  *
  * Layouts (row-major, last index fastest): q, k [Bt,G,Dk]; v [Bt,H,Dv]; alpha, beta [Bt,H];
  * state [Bt,H,Dv,Dk]; o [Bt,H,Dv]. Spec-decode inputs carry the draft index after the batch
@@ -28,8 +32,13 @@
  * All arithmetic is float64 on the exact fp32 input values.
  */
 #include <math.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* bf16 codec of oracle.c (reading R6 there). */
+uint16_t oracle_bf16_encode(float v);
+float oracle_bf16_decode(uint16_t h);
 
 /* One token of one (sequence, value head): the recurrence G1 on the float64 state S [Dv, Dk]. */
 static void gdn_update_head(int Dv, int Dk, double *S, const float *k, const float *v, double alpha,
@@ -108,7 +117,9 @@ int oracle_gdn_spec_stepwise(int Bt, int H, int G, int Dv, int Dk, int T, double
 /* ------------------------------------------------------------------------------------------- */
 typedef struct oracle_gdn {
     int Bt, H, G, Dv, Dk, L, Tmax;
+    int read_prec;                /* 0: reads from the checkpoint; 1: from its bf16 copy (G4) */
     double *ckpt;                 /* [Bt,H,Dv,Dk] checkpoint */
+    double *rcopy;                /* [Bt,H,Dv,Dk] decoded bf16 copy (read_prec 1) */
     float *rk, *rv, *ra, *rb;     /* records: [Bt,L,G,Dk], [Bt,L,H,Dv], [Bt,L,H] x 2 */
     int *pos, *ckpt_pos;
     int pending_T;
@@ -131,16 +142,29 @@ static void gdn_poison(oracle_gdn *r, int b, int from)
     }
 }
 
-oracle_gdn *oracle_gdn_create(int Bt, int H, int G, int Dv, int Dk, int L, int Tmax, const float *S0)
+/* Reading G4: the read copy of sequence b, from its checkpoint rounded to fp32 (the precision the
+ * layer keeps it in) and encoded to bf16 by nearest even; written at create and at every flush. */
+static void gdn_refresh_copy(oracle_gdn *r, int b)
+{
+    if (!r->read_prec) return;
+    const size_t n = (size_t)r->H * r->Dv * r->Dk;
+    for (size_t i = (size_t)b * n; i < (size_t)(b + 1) * n; ++i)
+        r->rcopy[i] = (double)oracle_bf16_decode(oracle_bf16_encode((float)r->ckpt[i]));
+}
+
+oracle_gdn *oracle_gdn_create(int Bt, int H, int G, int Dv, int Dk, int L, int Tmax, const float *S0, int read_prec)
 {
     if (Bt < 0 || H <= 0 || G <= 0 || H % G || Dv <= 0 || Dk <= 0 || L <= 0 || L > 64 || Tmax <= 0 ||
-        Tmax > L)
+        Tmax > L || read_prec < 0 || read_prec > 1)
         return NULL;
     oracle_gdn *r = (oracle_gdn *)calloc(1, sizeof(oracle_gdn));
     r->Bt = Bt; r->H = H; r->G = G; r->Dv = Dv; r->Dk = Dk; r->L = L; r->Tmax = Tmax;
+    r->read_prec = read_prec;
     const size_t st = (size_t)Bt * H * Dv * Dk;
     r->ckpt = (double *)malloc((st ? st : 1) * sizeof(double));
     for (size_t i = 0; i < st; ++i) r->ckpt[i] = (double)S0[i];
+    r->rcopy = read_prec ? (double *)malloc((st ? st : 1) * sizeof(double)) : NULL;
+    for (int b = 0; b < Bt; ++b) gdn_refresh_copy(r, b);
     r->rk = (float *)malloc(((size_t)Bt * L * G * Dk + 1) * sizeof(float));
     r->rv = (float *)malloc(((size_t)Bt * L * H * Dv + 1) * sizeof(float));
     r->ra = (float *)malloc(((size_t)Bt * L * H + 1) * sizeof(float));
@@ -154,7 +178,7 @@ oracle_gdn *oracle_gdn_create(int Bt, int H, int G, int Dv, int Dk, int L, int T
 void oracle_gdn_destroy(oracle_gdn *r)
 {
     if (!r) return;
-    free(r->ckpt); free(r->rk); free(r->rv); free(r->ra); free(r->rb); free(r->pos); free(r->ckpt_pos);
+    free(r->ckpt); free(r->rcopy); free(r->rk); free(r->rv); free(r->ra); free(r->rb); free(r->pos); free(r->ckpt_pos);
     free(r);
 }
 
@@ -187,7 +211,7 @@ static void gdn_replay_output(const oracle_gdn *r, int b, int last, const float 
             const double a = (double)r->ra[gs_at(r, b, j, h)];
             for (int n = 0; n < r->Dk; ++n) z[n] = a * (z[n] - c[j] * (double)kj[n]);
         }
-        const double *Sc = r->ckpt + ((size_t)b * r->H + h) * (size_t)r->Dv * r->Dk;
+        const double *Sc = (r->read_prec ? r->rcopy : r->ckpt) + ((size_t)b * r->H + h) * (size_t)r->Dv * r->Dk;
         for (int p = 0; p < r->Dv; ++p) {
             double acc = 0.0;
             for (int n = 0; n < r->Dk; ++n) acc += Sc[(size_t)p * r->Dk + n] * z[n];
@@ -217,6 +241,7 @@ static void gdn_flush_seq(oracle_gdn *r, int b)
     gdn_fold_into(r, b, count, r->ckpt);
     r->ckpt_pos[b] = r->pos[b];
     gdn_poison(r, b, 0);
+    gdn_refresh_copy(r, b);
 }
 
 /* Standard decode step: append, pos += 1; flush when more than L - Tmax records are pending and
@@ -317,4 +342,10 @@ void oracle_gdn_replay_materialize(const oracle_gdn *r, double *out)
 {
     memcpy(out, r->ckpt, (size_t)r->Bt * r->H * r->Dv * r->Dk * sizeof(double));
     for (int b = 0; b < r->Bt; ++b) gdn_fold_into(r, b, r->pos[b] - r->ckpt_pos[b], out);
+}
+
+/* The decoded read copy (read_prec 1) into out [Bt,H,Dv,Dk]. */
+void oracle_gdn_replay_read_copy(const oracle_gdn *r, double *out)
+{
+    if (r->read_prec) memcpy(out, r->rcopy, (size_t)r->Bt * r->H * r->Dv * r->Dk * sizeof(double));
 }

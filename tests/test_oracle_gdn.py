@@ -195,3 +195,36 @@ def test_state_machine_rejections():
     rep.rollback(np.array([2], np.int32))
     with pytest.raises(ValueError):
         oracle.GDNReplay(S0, 1, 4, 5)                    # Tmax > L
+
+
+def test_bf16_read_copy_model():
+    """Reading G4 (bf16 read copy): before the first flush every output equals, bit for bit, the
+    fp32-checkpoint replay started from torch's bfloat16 rounding of S0 (a library routine); flush
+    steps read the folded checkpoint, so they equal the fp32-checkpoint replay from S0 itself;
+    after a flush the copy is torch's bfloat16 of the float32-rounded checkpoint; outputs stay
+    within 2e-2 of O1g (bf16's 2^-9 relative rounding over a normwise product)."""
+    import torch
+    cfg = workload.GDN_TINY
+    Bt, H, G, Dv, Dk, L = cfg["Bt"], cfg["H"], cfg["G"], cfg["Dv"], cfg["Dk"], cfg["L"]
+    seed = 27
+    S0 = workload.gdn_initial_state(seed, Bt, H, Dv, Dk)
+    S0_bf = torch.from_numpy(S0).bfloat16().float().numpy()
+    cp = oracle.GDNReplay(S0, G, L, 1, oracle.READ_BF16)
+    from_bf = oracle.GDNReplay(S0_bf, G, L, 1)
+    full = oracle.GDNReplay(S0, G, L, 1)
+    S = S0.astype(np.float64)
+    assert np.array_equal(cp.read_copy(), S0_bf.astype(np.float64))
+    for t in range(3 * L):
+        ins = _inputs(seed, Bt, H, G, Dv, Dk, t)
+        o, o_bf, o_full = cp.step(*ins), from_bf.step(*ins), full.step(*ins)
+        o_true = oracle.gdn_step(S, *ins)
+        if t < L - 1:
+            assert np.array_equal(o, o_bf), t
+        if (t + 1) % L == 0:
+            assert _rel(o, o_full) <= 1e-12, t
+            ck = cp.checkpoint()
+            assert _rel(ck, full.checkpoint()) <= 1e-12
+            want = torch.from_numpy(ck.astype(np.float32)).bfloat16().float().numpy().astype(np.float64)
+            assert np.array_equal(cp.read_copy(), want), t
+        assert _rel(o, o_true) <= 2e-2, t
+    assert _rel(cp.materialize(), S) <= 1e-12
