@@ -61,12 +61,13 @@ class Layout(ctypes.Structure):
 
 class GDNConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "batch", "nheads", "nkheads", "dv", "dk", "buffer_len", "max_draft")]
+        "batch", "nheads", "nkheads", "dv", "dk", "buffer_len", "max_draft", "read_prec")]
 
 
 class GDNLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "master", "ring_k", "ring_v", "ring_a", "ring_b", "pos", "ckpt_pos", "counters", "flag", "total")]
+        "master", "read_copy", "ring_k", "ring_v", "ring_a", "ring_b", "pos", "ckpt_pos", "counters", "flag",
+        "total")]
 
 
 _vp = ctypes.c_void_p
@@ -486,8 +487,9 @@ class ReplaySSM:
 
 # ---- Gated DeltaNet layers (gdnreplay.h) ------------------------------------------------------
 
-def make_gdn_config(batch, nheads, nkheads, dv, dk, buffer_len=16, max_draft=1):
-    return GDNConfig(batch, nheads, nkheads, dv, dk, buffer_len, max_draft)
+def make_gdn_config(batch, nheads, nkheads, dv, dk, buffer_len=16, max_draft=1, read_prec="fp32"):
+    rp = _PREC_NAMES[read_prec] if isinstance(read_prec, str) else int(read_prec)
+    return GDNConfig(batch, nheads, nkheads, dv, dk, buffer_len, max_draft, rp)
 
 
 def gdnreplay_workspace_bytes(cfg: GDNConfig) -> int:
@@ -586,8 +588,8 @@ def gdn_snapshot_spec_verify(cfg: GDNConfig, slots, cur, T, q, k, v, alpha, beta
 class GDNReplay:
     """One Gated DeltaNet layer's decode state kept as checkpoint + record ring, on one GPU."""
 
-    def __init__(self, batch, nheads, nkheads, dv, dk, buffer_len=16, max_draft=1, device="cuda"):
-        self.cfg = make_gdn_config(batch, nheads, nkheads, dv, dk, buffer_len, max_draft)
+    def __init__(self, batch, nheads, nkheads, dv, dk, buffer_len=16, max_draft=1, read_prec="fp32", device="cuda"):
+        self.cfg = make_gdn_config(batch, nheads, nkheads, dv, dk, buffer_len, max_draft, read_prec)
         nbytes = gdnreplay_workspace_bytes(self.cfg)
         if nbytes == 0:
             raise ReplaySSMError(RSSM_E_INVAL, "gdnreplay_workspace_bytes")
@@ -650,6 +652,14 @@ class GDNReplay:
         off = self.layout.master
         n = self.batch * self.nheads * self.dv * self.dk
         return self.workspace[off:off + 4 * n].view(torch.float32).view(self.batch, self.nheads, self.dv, self.dk)
+
+    def read_copy(self):
+        """The bf16 read copy as bit patterns (int16 [Bt,H,Dv,Dk]), or None with fp32 reads."""
+        if self.cfg.read_prec != READ_BF16:
+            return None
+        off = self.layout.read_copy
+        n = self.batch * self.nheads * self.dv * self.dk
+        return self.workspace[off:off + 2 * n].view(torch.int16).view(self.batch, self.nheads, self.dv, self.dk)
 
     def pointer_arrays(self):
         def region(off, n):

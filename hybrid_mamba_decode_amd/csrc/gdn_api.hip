@@ -60,6 +60,7 @@ rssm_status check_config(const gdnreplay_config *c)
     if (s != RSSM_OK) return s;
     if (c->buffer_len < 1 || c->max_draft < 1 || c->max_draft > c->buffer_len) return RSSM_E_INVAL;
     if (c->buffer_len > 64 || c->max_draft > 8) return RSSM_E_UNSUPPORTED;
+    if (c->read_prec != RSSM_READ_FP32 && c->read_prec != RSSM_READ_BF16) return RSSM_E_INVAL;
     return RSSM_OK;
 }
 
@@ -73,6 +74,7 @@ void make_layout(const gdnreplay_config &c, gdnreplay_layout *L)
         return at;
     };
     L->master = take(Bt * H * Dv * Dk * 4);
+    L->read_copy = take(c.read_prec == RSSM_READ_BF16 ? Bt * H * Dv * Dk * 2 : 0);
     L->ring_k = take(Bt * G * Lb * Dk * 4);
     L->ring_v = take(Bt * H * Lb * Dv * 4);
     L->ring_a = take(Bt * H * Lb * 4);
@@ -188,6 +190,8 @@ rssm_status gdnreplay_create(const gdnreplay_config *cfg, void *workspace, size_
     char *ws = (char *)workspace;
     GLayer &d = h->dev;
     d.master = (float *)(ws + lay.master);
+    d.rprec = cfg->read_prec == RSSM_READ_BF16 ? 1 : 0;
+    d.rcopy = d.rprec ? (unsigned short *)(ws + lay.read_copy) : nullptr;
     d.ring_k = (float *)(ws + lay.ring_k);
     d.ring_v = (float *)(ws + lay.ring_v);
     d.ring_a = (float *)(ws + lay.ring_a);

@@ -228,6 +228,40 @@ __device__ inline void load_rows_f32(f32x4 (&vf)[GF::NL], const float *rows, int
     }
 }
 
+// bf16 copy rows in the same geometry: 8 bytes (4 values) per lane and slot, widened exactly.
+__device__ inline void load_rows_bf16(f32x4 (&vf)[GF::NL], const unsigned short *rows, int nrows, int wave, int lane)
+{
+    const int c = lane % GF::LPR;
+#pragma unroll
+    for (int i = 0; i < GF::NL; ++i) {
+        const int r = row_of_f32(i, wave, lane), rr = r < nrows ? r : 0;
+        const u32x2 w = __builtin_nontemporal_load((const u32x2 *)(rows + (size_t)rr * NN + 4 * c));
+        vf[i] = r < nrows ? f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)} : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// The bf16 copy of fp32 rows: each value rounded to nearest, ties to even.
+__device__ inline void store_rows_bf16(unsigned short *rows, const f32x4 (&vf)[GF::NL], int nrows, int wave, int lane)
+{
+    const int c = lane % GF::LPR;
+#pragma unroll
+    for (int i = 0; i < GF::NL; ++i) {
+        const int r = row_of_f32(i, wave, lane);
+        if (r < nrows) {
+            const u32x2 w = {bf16_rne(vf[i].x) | (bf16_rne(vf[i].y) << 16), bf16_rne(vf[i].z) | (bf16_rne(vf[i].w) << 16)};
+            __builtin_nontemporal_store(w, (u32x2 *)(rows + (size_t)r * NN + 4 * c));
+        }
+    }
+}
+
+// Store folded master rows and, with a read copy, its bf16 encoding.
+__device__ inline void store_checkpoint(const GLayer &Ld, size_t elem0, const f32x4 (&vf)[GF::NL], int nrows, int wave,
+                                        int lane)
+{
+    store_rows(Ld.master + elem0, vf, nrows, wave, lane);
+    if (Ld.rprec) store_rows_bf16(Ld.rcopy + elem0, vf, nrows, wave, lane);
+}
+
 // Row dots of the tile with M vectors (vectors[m] in LDS, NN floats each), reduced into
 // u[m * kRows + row].
 template <int M>
@@ -275,14 +309,21 @@ struct GStepLds {
     float u[kRows];
 };
 
-template <int LMAX, bool FLUSH>
+// CP: the checkpoint product reads the bf16 copy (replayed outputs; a flushing sequence reads and
+// folds the fp32 master).
+template <int LMAX, bool FLUSH, bool CP>
 __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO io, Lockstep ls)
 {
     __shared__ GStepLds<LMAX> s;
     const Tile t = gmap_tile(Ld);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh = (size_t)t.b * Ld.H + t.h, bg = (size_t)t.b * Ld.G + t.g;
-    float *rows = Ld.master + (bh * Ld.Dv + t.row0) * NN;
+    const size_t elem0 = (bh * Ld.Dv + t.row0) * NN;
+    float *rows = Ld.master + elem0;
+    auto load_state = [&](f32x4 (&dst)[GF::NL], bool master) {
+        if (CP && !master) load_rows_bf16(dst, Ld.rcopy + elem0, t.nrows, wave, lane);
+        else load_rows_f32(dst, rows, t.nrows, wave, lane);
+    };
 
     // Window in registers first (record j < k-1 from ring slot (cslot + j) mod L, the token's own
     // record fresh), committed to LDS once the state stream is in flight.
@@ -356,14 +397,17 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
 
     f32x4 vf[GF::NL];
     int pos = 0, ck = 0;
+    // With a read copy a flush-capable launch reads the master only for sequences that flush: in
+    // device-pointer mode their pointers come first.
+    constexpr bool kLate = CP && FLUSH;
     if (uni) {
         pslot = ls.pslot;
         cslot = ls.cslot;
         k = ls.k;
         issue_window();
-        load_rows_f32(vf, rows, t.nrows, wave, lane);
+        load_state(vf, FLUSH && k > Ld.L - Ld.Tmax);
     } else {
-        load_rows_f32(vf, rows, t.nrows, wave, lane);  // the checkpoint stream first
+        if (!kLate) load_state(vf, false);  // the checkpoint stream first
         pos = Ld.pos[t.b];
         ck = Ld.ckpt[t.b];
         const int c0 = pos - ck;
@@ -375,6 +419,7 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
         pslot = (int)((unsigned)pos % (unsigned)Ld.L);
         cslot = (int)((unsigned)ck % (unsigned)Ld.L);
         k = c0 + 1;  // records in the window, this token included
+        if (kLate) load_state(vf, k > Ld.L - Ld.Tmax);
         issue_window();
     }
     commit_window();
@@ -403,7 +448,7 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
 
     if (FLUSH && flush) {
         gdn_fold_rows<LMAX>(vf, s.w, k, wave, lane);
-        store_rows(rows, vf, t.nrows, wave, lane);
+        store_checkpoint(Ld, elem0, vf, t.nrows, wave, lane);
         rows_dot<1>(vf, s.q, 1, s.u, wave, lane);
         __syncthreads();
         if (tid < t.nrows) io.o[bh * Ld.Dv + t.row0 + tid] = s.u[tid];
@@ -464,7 +509,7 @@ __global__ void __launch_bounds__(kThreads) gdn_flush_kernel(GLayer Ld, int mode
     if (mode == MODE_MATERIALIZE) {
         store_rows(out + elem0, vf, t.nrows, wave, lane);
     } else {
-        store_rows(Ld.master + elem0, vf, t.nrows, wave, lane);
+        store_checkpoint(Ld, elem0, vf, t.nrows, wave, lane);
         gseq_done(Ld, t.b, pos, pos);
     }
 }
@@ -501,7 +546,7 @@ struct GVerifyLds {
     float u[TQ][kRows];
 };
 
-template <int LMAX, int TQ>
+template <int LMAX, int TQ, bool CP>
 __global__ void __launch_bounds__(kThreads) gdn_verify_kernel(GLayer Ld, GTokenIO io, int T)
 {
     __shared__ GVerifyLds<LMAX, TQ> s;
@@ -509,7 +554,8 @@ __global__ void __launch_bounds__(kThreads) gdn_verify_kernel(GLayer Ld, GTokenI
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh = (size_t)t.b * Ld.H + t.h;
     f32x4 vf[GF::NL];
-    load_rows_f32(vf, Ld.master + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
+    if (CP) load_rows_bf16(vf, Ld.rcopy + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
+    else load_rows_f32(vf, Ld.master + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
     const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
     const int count0 = pos - ck;
     if (!(ck >= 0 && count0 >= 0 && count0 <= Ld.L - Ld.Tmax && count0 + T <= Ld.L)) {
@@ -565,7 +611,7 @@ __global__ void __launch_bounds__(kThreads) gdn_load_kernel(GLayer Ld, const flo
     const size_t elem0 = (((size_t)t.b * Ld.H + t.h) * Ld.Dv + t.row0) * NN;
     f32x4 vf[GF::NL];
     load_rows_f32(vf, state + elem0, t.nrows, wave, lane);
-    store_rows(Ld.master + elem0, vf, t.nrows, wave, lane);
+    store_checkpoint(Ld, elem0, vf, t.nrows, wave, lane);
     if (t.h == 0 && t.split == 0 && threadIdx.x == 0) {
         Ld.pos[t.b] = 0;
         Ld.ckpt[t.b] = 0;
@@ -682,12 +728,18 @@ __global__ void __launch_bounds__(kThreads) gdn_snapshot_kernel(GLayer Ld, float
 
 inline unsigned gblocks(const GLayer &Ld) { return (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)Ld.psplit; }
 
+template <int LMAX, bool CP>
+hipError_t step_lc(const GLayer &Ld, const GTokenIO &io, bool fc, Lockstep ls, hipStream_t st)
+{
+    if (fc) hipLaunchKernelGGL((gdn_step_kernel<LMAX, true, CP>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
+    else hipLaunchKernelGGL((gdn_step_kernel<LMAX, false, CP>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
+    return hipGetLastError();
+}
+
 template <int LMAX>
 hipError_t step_l(const GLayer &Ld, const GTokenIO &io, bool fc, Lockstep ls, hipStream_t st)
 {
-    if (fc) hipLaunchKernelGGL((gdn_step_kernel<LMAX, true>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
-    else hipLaunchKernelGGL((gdn_step_kernel<LMAX, false>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
-    return hipGetLastError();
+    return Ld.rprec ? step_lc<LMAX, true>(Ld, io, fc, ls, st) : step_lc<LMAX, false>(Ld, io, fc, ls, st);
 }
 
 template <int LMAX>
@@ -703,14 +755,20 @@ hipError_t flush_l(const GLayer &Ld, int mode, const int *arg, int T, float *out
     return hipGetLastError();
 }
 
+template <int LMAX, bool CP>
+hipError_t verify_lc(const GLayer &Ld, const GTokenIO &io, int T, hipStream_t st)
+{
+    const dim3 grid(gblocks(Ld)), block(kThreads);
+    if (T <= 2) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 2, CP>), grid, block, 0, st, Ld, io, T);
+    else if (T <= 4) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 4, CP>), grid, block, 0, st, Ld, io, T);
+    else hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 8, CP>), grid, block, 0, st, Ld, io, T);
+    return hipGetLastError();
+}
+
 template <int LMAX>
 hipError_t verify_l(const GLayer &Ld, const GTokenIO &io, int T, hipStream_t st)
 {
-    const dim3 grid(gblocks(Ld)), block(kThreads);
-    if (T <= 2) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 2>), grid, block, 0, st, Ld, io, T);
-    else if (T <= 4) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 4>), grid, block, 0, st, Ld, io, T);
-    else hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 8>), grid, block, 0, st, Ld, io, T);
-    return hipGetLastError();
+    return Ld.rprec ? verify_lc<LMAX, true>(Ld, io, T, st) : verify_lc<LMAX, false>(Ld, io, T, st);
 }
 
 }  // namespace

@@ -10,6 +10,8 @@ namespace rssm {
 // One GDN layer's workspace (passed by value). H value heads of Dv, G key heads of Dk.
 struct GLayer {
     float *master;      // [Bt,H,Dv,Dk] fp32 checkpoint
+    unsigned short *rcopy;  // [Bt,H,Dv,Dk] bf16 read copy (rprec 1), else nullptr
+    int rprec;          // 0: reads from the checkpoint; 1: from the bf16 copy
     float *ring_k;      // [Bt,G,L,Dk]
     float *ring_v;      // [Bt,H,L,Dv]
     float *ring_a;      // [Bt,H,L] gate alpha

@@ -22,7 +22,11 @@
  *     state [Bt,H,Dv,Dk]   o [Bt,H,Dv]
  *     spec-decode inputs: q, k [Bt,T,G,Dk]  v [Bt,T,H,Dv]  alpha, beta [Bt,T,H]  o [Bt,T,H,Dv]
  * Supported: Dk in {16, 32, 64, 128, 256}; Dv a multiple of 4, at most 256; 1 <= L <= 64;
- * 1 <= max_draft <= min(L, 8). Reads are through the fp32 checkpoint.
+ * 1 <= max_draft <= min(L, 8). Reads: through the fp32 checkpoint (read_prec RSSM_READ_FP32), or
+ * through a bf16 copy of it (RSSM_READ_BF16; [AT Pulse] "Technical analysis": a high-precision
+ * checkpoint drives the recurrence, a low-precision copy serves reads): the copy is each
+ * checkpoint value rounded to nearest even, written at load and at every flush; replayed outputs
+ * and verify read it, flushes fold into and read the fp32 checkpoint.
  *
  * Memory, streams and errors as in replayssm.h: the caller owns every device buffer (16-byte
  * aligned float arrays, 4-byte aligned int32 arrays, 256-byte aligned workspace; NULL allowed
@@ -52,11 +56,13 @@ typedef struct {
     int32_t dk;          /* key size Dk */
     int32_t buffer_len;  /* L */
     int32_t max_draft;   /* T_max: 1 = standard decode only */
+    int32_t read_prec;   /* RSSM_READ_FP32 or RSSM_READ_BF16 (others: RSSM_E_INVAL) */
 } gdnreplay_config;
 
 /* Byte offsets of the workspace regions. */
 typedef struct {
     size_t master;    /* fp32 [Bt,H,Dv,Dk] checkpoint, updated only by flushes */
+    size_t read_copy; /* bf16 [Bt,H,Dv,Dk] (0 bytes with fp32 reads) */
     size_t ring_k;    /* fp32 [Bt,G,L,Dk]: record of position q in slot q mod L */
     size_t ring_v;    /* fp32 [Bt,H,L,Dv] */
     size_t ring_a;    /* fp32 [Bt,H,L] alpha */

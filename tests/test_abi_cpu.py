@@ -239,6 +239,9 @@ def test_gdn_workspace_layout():
     assert lay.total == rs.gdnreplay_workspace_bytes(c)
     for name in ("master", "ring_k", "ring_v", "ring_a", "ring_b", "pos", "ckpt_pos", "counters", "flag"):
         assert getattr(lay, name) % 256 == 0
+    assert lay.read_copy == lay.ring_k                                  # fp32 reads: no copy
+    lb = rs.gdnreplay_workspace_layout(gcfg(batch=256, read_prec="bf16"))
+    assert lb.ring_k - lb.read_copy == Bt * H * Dv * Dk * 2               # bf16 copy
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -252,6 +255,8 @@ def test_gdn_workspace_layout():
     (dict(buffer_len=65), rs.RSSM_E_UNSUPPORTED),
     (dict(buffer_len=16, max_draft=9), rs.RSSM_E_UNSUPPORTED),
     (dict(batch=-1), rs.RSSM_E_INVAL),
+    (dict(read_prec=2), rs.RSSM_E_INVAL),
+    (dict(read_prec=-1), rs.RSSM_E_INVAL),
 ])
 def test_gdn_invalid_configs_rejected(kw, status):
     c = gcfg(**kw)

@@ -1,0 +1,115 @@
+"""GPU parity of the Gated DeltaNet path with a bf16 read copy (gdnreplay.h, read_prec bf16)
+against the oracle's replay model with the same copy (reading G4) and the stepwise truth.
+
+Bars: the copy after load equal, bit for bit, to torch's bfloat16 rounding of the initial state;
+until the first flush every output within 1e-5 of the oracle's copy model (the copies are the same
+bits); flush steps (read from the folded fp32 checkpoint) and checkpoints within 1e-5 of the
+truth; after a flush the copy equal bit for bit to torch's bfloat16 of the GPU's own checkpoint,
+outputs within 1e-2 of the model (half bf16's gate: the GPU's fp32 fold and the oracle's float64
+fold can round a value to neighbouring bf16 codes) and within 2e-2 of the truth, or 1.25x the
+model's own error on a step where it exceeds that; pointers bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_mamba_decode_amd as rs
+import oracle
+import workload
+from gpu_harness import dev, host, log, rel
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+GATE = 2e-2
+
+
+def _bf16_bits(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).bfloat16().view(torch.int16).numpy()
+
+
+def _check_outputs(o, o_model, o_true, flushed, flush_step, what):
+    if flush_step:
+        assert rel(o, o_true) <= TOL, f"{what}: flush step vs truth {rel(o, o_true):.2e}"
+        return
+    e_model = rel(o, o_model)
+    assert e_model <= (TOL if not flushed else GATE / 2), f"{what}: vs copy model {e_model:.2e}"
+    gate = max(GATE, 1.25 * rel(o_model, o_true))
+    assert rel(o, o_true) <= gate, f"{what}: vs truth {rel(o, o_true):.2e} > {gate:.2e}"
+
+
+def _run(Bt, H, G, Dv, Dk, L, seed, steps, sample, lockstep=True):
+    log(f"[gdn bf16] Bt={Bt} H={H} G={G} Dv={Dv} Dk={Dk} L={L} steps={steps} sample={list(sample)} lockstep={lockstep}")
+    S0 = workload.gdn_initial_state(seed, Bt, H, Dv, Dk)
+    lay = rs.GDNReplay(Bt, H, G, Dv, Dk, buffer_len=L, read_prec="bf16")
+    lay.set_lockstep(lockstep)
+    lay.load_state(dev(S0))
+    assert np.array_equal(host(lay.read_copy()), _bf16_bits(S0))
+    sample = np.asarray(sample)
+    model = oracle.GDNReplay(S0[sample], G, L, 1, oracle.READ_BF16)
+    S = S0[sample].astype(np.float64)
+    for t in range(steps):
+        ins = workload.gdn_step_inputs(seed, t, Bt, H, G, Dv, Dk)
+        o = host(lay.step(*(dev(a) for a in ins)))[sample]
+        sub = [a[sample] for a in ins]
+        o_true = oracle.gdn_step(S, *sub)
+        o_model = model.step(*sub)
+        flush_step = (t + 1) % L == 0
+        _check_outputs(o, o_model, o_true, t >= L, flush_step, f"step {t}")
+        pos, ck = lay.get_pointers()
+        assert pos == [t + 1] * Bt and ck == [(t + 1) // L * L] * Bt
+        if flush_step:
+            m = host(lay.master())
+            assert rel(m[sample], S) <= TOL, f"step {t}: checkpoint"
+            assert np.array_equal(host(lay.read_copy()), _bf16_bits(m)), f"step {t}: copy of the checkpoint"
+    assert rel(host(lay.materialize_state())[sample], S) <= TOL
+    assert lay.check() == rs.RSSM_OK
+
+
+@pytest.mark.parametrize("lockstep", [True, False])
+def test_gdn_bf16_tiny(lockstep):
+    c = workload.GDN_TINY
+    _run(c["Bt"], c["H"], c["G"], c["Dv"], c["Dk"], c["L"], workload.config_seed(5), 40, range(c["Bt"]), lockstep)
+
+
+def test_gdn_bf16_serving():
+    """Serving GDN layer (batch 256, 32 x 16 heads of 128, L 16): 48 steps, sequences 0 and 200."""
+    c = workload.GDN_SERVING
+    _run(c["Bt"], c["H"], c["G"], c["Dv"], c["Dk"], c["L"], workload.config_seed(6), 48, [0, 200])
+
+
+@pytest.mark.parametrize("shape", [(3, 4, 2, 100, 32, 7), (2, 2, 1, 32, 256, 5), (2, 4, 2, 64, 128, 1)])
+def test_gdn_bf16_shapes(shape):
+    Bt, H, G, Dv, Dk, L = shape
+    _run(Bt, H, G, Dv, Dk, L, 141, 2 * L + 3, range(Bt))
+
+
+@pytest.mark.parametrize("T,L", [(3, 7), (4, 16)])
+def test_gdn_bf16_spec(T, L):
+    """Verify + rollback through the bf16 copy; the commit-time flushes refresh it."""
+    Bt, H, G, Dv, Dk, seed = 3, 4, 2, 32, 64, 151
+    S0 = workload.gdn_initial_state(seed, Bt, H, Dv, Dk)
+    lay = rs.GDNReplay(Bt, H, G, Dv, Dk, buffer_len=L, max_draft=T, read_prec="bf16")
+    lay.load_state(dev(S0))
+    model = oracle.GDNReplay(S0, G, L, T, oracle.READ_BF16)
+    S = S0.astype(np.float64)
+    rng = np.random.default_rng(seed)
+    flushed = False
+    for it in range(24):
+        drafts = workload.gdn_draft_inputs(seed, it, Bt, T, H, G, Dv, Dk)
+        acc = rng.integers(0, T + 1, Bt).astype(np.int32)
+        o = host(lay.spec_verify(*(dev(a) for a in drafts)))
+        lay.rollback(dev(acc))
+        ck_before = model.pointers()[1].copy()
+        o_model = model.verify(T, *drafts)
+        model.rollback(acc)
+        o_true = oracle.gdn_spec_stepwise(S, T, *drafts, acc)
+        _check_outputs(o, o_model, o_true, flushed, False, f"verify {it}")
+        flushed = flushed or bool(np.any(model.pointers()[1] != ck_before))
+        pos, ck = lay.get_pointers()
+        assert pos == list(model.pointers()[0]) and ck == list(model.pointers()[1])
+        assert rel(host(lay.materialize_state()), S) <= TOL
+    assert flushed
+    m = host(lay.master())
+    assert np.array_equal(host(lay.read_copy()), _bf16_bits(m))
+    assert lay.check() == rs.RSSM_OK
