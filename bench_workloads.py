@@ -258,7 +258,8 @@ def gdn(args):
     S0 = torch.randn(Bt, Hv, Dv, Dk, device="cuda", generator=g)
     pool = [_gdn_tokens(g, (Bt,), Hv, Gk, Dv, Dk, rates) for _ in range(8)]
     o = torch.empty(Bt, Hv, Dv, device="cuda")
-    lay = rs.GDNReplay(Bt, Hv, Gk, Dv, Dk, buffer_len=L)
+    prec = args.read_prec if args.read_prec in ("fp32", "bf16") else "fp32"
+    lay = rs.GDNReplay(Bt, Hv, Gk, Dv, Dk, buffer_len=L, read_prec=prec)
     lay.load_state(S0)
 
     def rep_step(r):
@@ -269,8 +270,8 @@ def gdn(args):
     assert lay.check() == rs.RSSM_OK
     ks = np.array([r % L + 1 for r in range(steps)])
     fl = ks == L
-    nf_bytes = np.array([traffic.gdn_replay_nonflush(Hv, Gk, Dv, Dk, int(k)) * Bt for k in ks[~fl]])
-    fl_bytes = traffic.gdn_replay_flush_step(Hv, Gk, Dv, Dk, L) * Bt
+    nf_bytes = np.array([traffic.gdn_replay_nonflush(Hv, Gk, Dv, Dk, int(k), prec) * Bt for k in ks[~fl]])
+    fl_bytes = traffic.gdn_replay_flush_step(Hv, Gk, Dv, Dk, L, prec) * Bt
     cfg = rs.make_gdn_config(Bt, Hv, Gk, Dv, Dk)
     cst = S0.clone()
 
@@ -282,7 +283,7 @@ def gdn(args):
     nf_gbps = float((nf_bytes / d[~fl]).mean()) / 1e9
     out = {
         "workload": f"Gated DeltaNet layer decode step, batch {Bt}, {Hv} value heads x {Gk} key heads, "
-                    f"Dv {Dv}, Dk {Dk}, L {L}, fp32 (2 MiB state per sequence)",
+                    f"Dv {Dv}, Dk {Dk}, L {L}, fp32 checkpoint (2 MiB per sequence), {prec} reads",
         "replay": {"tokens_per_s_layer": round(Bt * steps / wall, 1),
                    "nonflush_mean_us": round(float(d[~fl].mean()) * 1e6, 2),
                    "nonflush_gbps": round(nf_gbps, 1), "nonflush_frac_of_8tbs": round(nf_gbps / PEAK, 4),
@@ -309,7 +310,7 @@ def gdn(args):
     acc = torch.from_numpy(np.stack([workload.accepted_counts(workload.config_seed(7), it, Bt, T)
                                      for it in range(iters)])).cuda()
     od = torch.empty(Bt, T, Hv, Dv, device="cuda")
-    lay = rs.GDNReplay(Bt, Hv, Gk, Dv, Dk, buffer_len=L, max_draft=T)
+    lay = rs.GDNReplay(Bt, Hv, Gk, Dv, Dk, buffer_len=L, max_draft=T, read_prec=prec)
 
     def spec_iter(it):
         rs.gdnreplay_spec_verify(lay.handle, T, *dpool[it % len(dpool)], od)
@@ -335,7 +336,8 @@ def gdn(args):
     cur.zero_()
     wall_s, ds = _timed(snap_iter, iters)
     out = {
-        "workload": f"Gated DeltaNet spec decode, batch {Bt}, T={T}, accepted ~ U{{0..{T}}}, {iters} verify steps, fp32",
+        "workload": f"Gated DeltaNet spec decode, batch {Bt}, T={T}, accepted ~ U{{0..{T}}}, {iters} verify steps, "
+                    f"fp32 checkpoint, {prec} reads",
         "replay": {"accepted_tokens_per_s_layer": round(accepted / wall_r, 1),
                    "verify_plus_rollback_mean_us": round(float(dr.mean()) * 1e6, 2)},
         "snapshot": {"accepted_tokens_per_s_layer": round(accepted / wall_s, 1),

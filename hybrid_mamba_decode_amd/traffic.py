@@ -94,8 +94,8 @@ def snapshot_verify(H, P, N, G, T):
 
 
 # ---- Gated DeltaNet (H value heads of Dv, G key heads of Dk) -------------------------------------
-def gdn_state_bytes(H, Dv, Dk):
-    return F32 * H * Dv * Dk
+def gdn_state_bytes(H, Dv, Dk, prec="fp32"):
+    return int(ELEM[prec] * H * Dv * Dk)
 
 
 def gdn_token_input_bytes(H, G, Dv, Dk):
@@ -108,13 +108,16 @@ def gdn_record_bytes(H, G, Dv, Dk):
     return F32 * (G * Dk + H * Dv + 2 * H)
 
 
-def gdn_replay_nonflush(H, G, Dv, Dk, k):
-    return (gdn_state_bytes(H, Dv, Dk) + gdn_token_input_bytes(H, G, Dv, Dk) + gdn_record_bytes(H, G, Dv, Dk)
+def gdn_replay_nonflush(H, G, Dv, Dk, k, prec="fp32"):
+    """prec: the precision the checkpoint product reads (the fp32 checkpoint or its bf16 copy)."""
+    return (gdn_state_bytes(H, Dv, Dk, prec) + gdn_token_input_bytes(H, G, Dv, Dk) + gdn_record_bytes(H, G, Dv, Dk)
             + F32 * H * Dv + (k - 1) * gdn_record_bytes(H, G, Dv, Dk))
 
 
-def gdn_replay_flush_step(H, G, Dv, Dk, L):
-    return (2 * gdn_state_bytes(H, Dv, Dk) + gdn_token_input_bytes(H, G, Dv, Dk) + F32 * H * Dv
+def gdn_replay_flush_step(H, G, Dv, Dk, L, prec="fp32"):
+    """Read and write the fp32 checkpoint, plus the copy's write with a read copy."""
+    copy = 0 if prec == "fp32" else gdn_state_bytes(H, Dv, Dk, prec)
+    return (2 * gdn_state_bytes(H, Dv, Dk) + copy + gdn_token_input_bytes(H, G, Dv, Dk) + F32 * H * Dv
             + (L - 1) * gdn_record_bytes(H, G, Dv, Dk))
 
 
@@ -122,8 +125,8 @@ def gdn_conventional(H, G, Dv, Dk):
     return 2 * gdn_state_bytes(H, Dv, Dk) + gdn_token_input_bytes(H, G, Dv, Dk) + F32 * H * Dv
 
 
-def gdn_verify(H, G, Dv, Dk, T, k_old):
-    return (gdn_state_bytes(H, Dv, Dk) + T * (gdn_token_input_bytes(H, G, Dv, Dk) + gdn_record_bytes(H, G, Dv, Dk)
+def gdn_verify(H, G, Dv, Dk, T, k_old, prec="fp32"):
+    return (gdn_state_bytes(H, Dv, Dk, prec) + T * (gdn_token_input_bytes(H, G, Dv, Dk) + gdn_record_bytes(H, G, Dv, Dk)
             + F32 * H * Dv) + k_old * gdn_record_bytes(H, G, Dv, Dk))
 
 
