@@ -61,7 +61,9 @@ def parse():
                     help="only the replay steps (for profiler runs)")
     ap.add_argument("--workload", default="serving", choices=["serving", "spec", "sweep", "gdn", "mixer"],
                     help="serving: the headline line; spec: batch 512, T=4 verify+rollback vs "
-                         "per-draft snapshots; sweep: batch x L over a 10-layer stack")
+                         "per-draft snapshots; sweep: batch x L over a 10-layer stack; gdn: a Gated "
+                         "DeltaNet layer (--read-prec fp32|bf16); mixer: the step with the Mamba-2 "
+                         "mixer edges fused")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
     return ap.parse_args()
@@ -70,9 +72,9 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the decode step needs no communication; sharding by sequence or head is described "
-              "in the design notes).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode step "
+              "needs no communication: sequences or head groups shard across GPUs with no collective "
+              "inside the step, so one GPU's share at its real shape is the measurement).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,5 +1,5 @@
 """Shared helpers of the GPU parity tests: device transfer, the normwise error metric, and a
-driver that runs the HIP layer and the float64 oracle side by side on the same seeded inputs."""
+helper that runs the HIP layer and the float64 oracle side by side on the same seeded inputs."""
 import json
 import os
 
