@@ -257,6 +257,14 @@ def test_gdn_spec_small(T, L):
     _run_spec(case, T, 30, range(3), snapshot=True)
 
 
+def test_gdn_maximum_sizes():
+    """Dv 256 (four row splits), Dk 256, L 64: standard steps across a flush, then T 8 verifies."""
+    case = GCase(2, 2, 1, 256, 256, 64, 63)
+    _run(case, 70, range(2), check_state_every=16)
+    spec = GCase(2, 2, 1, 256, 256, 64, 64, Tmax=8)
+    _run_spec(spec, 8, 12, range(2), snapshot=True)
+
+
 def test_gdn_spec_accept_extremes_and_interleaved_steps():
     case = GCase(4, 4, 2, 32, 64, 8, 29, Tmax=3)
     pattern = [np.array([0, 3, 0, 3], np.int32), np.array([3, 3, 3, 3], np.int32), np.array([0, 0, 0, 0], np.int32)]

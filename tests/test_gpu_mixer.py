@@ -242,6 +242,12 @@ def test_mixer_spec_verify_rollback(T, L, K):
     _spec_case(case, 18, range(3))
 
 
+def test_mixer_maximum_sizes():
+    """P 256 (four row splits), N 256, L 32 (the mixer's largest bucket), K 4, T 8."""
+    case = MixCase(2, 2, 256, 256, 1, 32, 4, 65, Tmax=8)
+    _spec_case(case, 10, range(2))
+
+
 def test_mixer_spec_serving_batch512_T4():
     """Batch 512 of the serving layer with the edges, T = 4, L = 16: sequences 7 and 400."""
     c = workload.MIXER

@@ -183,6 +183,7 @@ def test_read_copy_bytes_bit_exact(prec):
     dict(Bt=2, H=8, P=8, N=16, G=4, L=64),      # window bucket 64
     dict(Bt=4, H=16, P=64, N=128, G=2, L=1),    # every step flushes
     dict(Bt=1, H=128, P=64, N=128, G=8, L=16),  # batch 1 at the serving head shape
+    dict(Bt=2, H=2, P=256, N=256, G=1, L=64),   # maximum sizes: P 256 (4 row splits), N 256, L 64
 ])
 def test_shapes_fp32(shape):
     case = Case(shape["Bt"], shape["H"], shape["P"], shape["N"], shape["G"], shape["L"], 123)

@@ -114,6 +114,12 @@ def test_spec_small(T, L):
     _run_spec(case, T, 30, range(3), snapshot=True)
 
 
+def test_spec_maximum_sizes():
+    """T 8 with L 64, P 256 (four row splits) and N 256: the largest supported verify window."""
+    case = Case(2, 2, 256, 256, 1, 64, 61, Tmax=8)
+    _run_spec(case, 8, 20, range(2), snapshot=True)
+
+
 def test_spec_accept_extremes_and_interleaved_steps():
     case = Case(4, 8, 32, 64, 2, 8, 29, Tmax=3)
     pattern = [np.array([0, 3, 0, 3], np.int32), np.array([3, 3, 3, 3], np.int32),
