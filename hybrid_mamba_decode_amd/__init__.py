@@ -352,7 +352,7 @@ class ReplaySSM:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
+        if h and _lib is not None:  # at interpreter exit the module's globals may be gone
             _lib.replayssm_destroy(h)
             self.handle = None
 
@@ -603,7 +603,7 @@ class GDNReplay:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
+        if h and _lib is not None:  # at interpreter exit the module's globals may be gone
             _lib.gdnreplay_destroy(h)
             self.handle = None
 
