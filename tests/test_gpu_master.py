@@ -229,3 +229,32 @@ def test_fp16_sr_master_avoids_stagnation():
             assert np.array_equal(host(lays["fp16_sr"].master()).astype(np.float64), sr.checkpoint()), f"flush at {t}"
     assert bool((lays["fp16"].master() == 1.0).all())
     assert float(host(lays["fp16_sr"].master()).astype(np.float64).mean()) > 1.0 + 16 * 2.0 ** -14
+
+
+@pytest.mark.parametrize("master", ["fp16", "fp16_sr"])
+def test_fp16_master_subnormal_codes(master):
+    """The whole state inside fp16's subnormal range (|v| < 2^-14, spacing 2^-24), where the
+    stochastic rule takes its general path: A = 0, dt in {1/2, 1}, small-integer x, C, B and S0
+    as multiples of 2^-30, so every fold is exact in fp32 and float64 and the fp16 codes after
+    every flush must equal the oracle's bit for bit."""
+    Bt, H, P, N, G, L = 2, 4, 64, 64, 2, 4
+    rng = np.random.default_rng(4242)
+    S0 = (rng.integers(-(1 << 12), (1 << 12) + 1, (Bt, H, P, N)) * 2.0 ** -30).astype(np.float32)
+    A = np.zeros(H, np.float32)
+    D = np.zeros(H, np.float32)
+    lay = rs.ReplaySSM(Bt, H, P, N, G, dev(A), dev(D), buffer_len=L, master_prec=master, sr_seed=123)
+    lay.load_state(dev(S0))
+    rep = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, MASTER_CODE[master], 123)
+    assert np.array_equal(host(lay.master()).astype(np.float64), rep.checkpoint())
+    for t in range(4 * L):
+        x = rng.integers(-3, 4, (Bt, H, P)).astype(np.float32)
+        B = (rng.integers(-64, 65, (Bt, G, N)) * 2.0 ** -30).astype(np.float32)
+        C = rng.integers(-2, 3, (Bt, G, N)).astype(np.float32)
+        dt = rng.choice([0.5, 1.0], (Bt, H)).astype(np.float32)
+        lay.step(dev(x), dev(B), dev(C), dev(dt))
+        rep.step(x, B, C, dt)
+        if (t + 1) % L == 0:
+            m = host(lay.master()).astype(np.float64)
+            assert np.max(np.abs(m)) < 2.0 ** -14
+            assert np.array_equal(m, rep.checkpoint()), f"flush at step {t}"
+    assert lay.check() == rs.RSSM_OK
