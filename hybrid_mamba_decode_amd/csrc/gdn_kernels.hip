@@ -39,20 +39,24 @@ constexpr int ZPL = NN >= 64 ? NN / 64 : 1;  // sweep vector elements per lane (
 // State row held by load slot i of a lane (f32 geometry).
 __device__ inline int row_of_f32(int i, int wave, int lane) { return i * GF::RPB + wave * GF::RPI + lane / GF::LPR; }
 
-__device__ inline Tile gmap_tile(const GLayer &Ld)
+// Tiles of RT value rows, `splits` = ceil(Dv / RT) per (sequence, value head).
+template <int RT>
+__device__ inline Tile gmap_tile_rows(const GLayer &Ld, int splits)
 {
     const unsigned nblk = gridDim.x, i = blockIdx.x;
     const unsigned id = (nblk % 8u == 0u) ? (i % 8u) * (nblk / 8u) + i / 8u : i;
     Tile t;
-    t.split = (int)(id % (unsigned)Ld.psplit);
-    const unsigned bh = id / (unsigned)Ld.psplit;
+    t.split = (int)(id % (unsigned)splits);
+    const unsigned bh = id / (unsigned)splits;
     t.h = (int)(bh % (unsigned)Ld.H);
     t.b = (int)(bh / (unsigned)Ld.H);
     t.g = t.h / Ld.hpg;
-    t.row0 = t.split * kRows;
-    t.nrows = min(kRows, Ld.Dv - t.row0);
+    t.row0 = t.split * RT;
+    t.nrows = min(RT, Ld.Dv - t.row0);
     return t;
 }
+
+__device__ inline Tile gmap_tile(const GLayer &Ld) { return gmap_tile_rows<kRows>(Ld, Ld.psplit); }
 
 __device__ inline void graise(const GLayer &Ld, unsigned bits)
 {
@@ -61,11 +65,11 @@ __device__ inline void graise(const GLayer &Ld, unsigned bits)
 
 // Per-sequence completion (as seq_done in device.h): the last work-group of sequence b to finish
 // writes the new pointers and re-arms the counter.
-__device__ inline void gseq_done(const GLayer &Ld, int b, int new_pos, int new_ckpt)
+__device__ inline void gseq_done(const GLayer &Ld, int b, int new_pos, int new_ckpt, int splits)
 {
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned expected = (unsigned)(Ld.H * Ld.psplit);
+        const unsigned expected = (unsigned)(Ld.H * splits);
         const unsigned prev = __hip_atomic_fetch_add(&Ld.counter[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (prev + 1u == expected) {
             Ld.pos[b] = new_pos;
@@ -75,11 +79,16 @@ __device__ inline void gseq_done(const GLayer &Ld, int b, int new_pos, int new_c
     }
 }
 
-template <int LMAX>
+__device__ inline void gseq_done(const GLayer &Ld, int b, int new_pos, int new_ckpt)
+{
+    gseq_done(Ld, b, new_pos, new_ckpt, Ld.psplit);
+}
+
+template <int LMAX, int RT = kRows>
 struct GWin {
-    float K[LMAX][NN] __attribute__((aligned(16)));     // k_j of the key head
-    float V[LMAX][kRows] __attribute__((aligned(16)));  // v_j, this work-group's rows
-    float a[LMAX], b[LMAX];                             // alpha_j, beta_j of the value head
+    float K[LMAX][NN] __attribute__((aligned(16)));  // k_j of the key head
+    float V[LMAX][RT] __attribute__((aligned(16)));  // v_j, this work-group's RT rows
+    float a[LMAX], b[LMAX];                          // alpha_j, beta_j of the value head
 };
 
 // Stage records 0..k-1 of the window in LDS: record j < nring from ring slot (ck + j) mod L, the
@@ -141,8 +150,8 @@ __device__ inline float row_allreduce(float v) { return group_sum<GF::LPR>(v); }
 // Backward sweep of one query over records last..0 in the calling wave: z <- q; c_j = beta_j
 // (k_j . z); z <- alpha_j (z - c_j k_j). Writes c_j to c[j] and the final z to z_out (lane 0 and
 // lanes holding z elements; wave-wide shuffles, so the whole wave must call it).
-template <int LMAX>
-__device__ inline void gdn_sweep(const GWin<LMAX> &w, const float *q, int last, float *c, float *z_out, int lane)
+template <int LMAX, int RT>
+__device__ inline void gdn_sweep(const GWin<LMAX, RT> &w, const float *q, int last, float *c, float *z_out, int lane)
 {
     float z[ZPL];
 #pragma unroll
@@ -300,14 +309,150 @@ __device__ inline void rows_dot(const f32x4 (&vf)[GF::NL], const float *vectors,
 // "What happened": the checkpoint is updated when the buffer fills); those apply all records to
 // the fp32 master and read o from the folded state (no record is stored for that token).
 // ==========================================================================================
-template <int LMAX>
+template <int LMAX, int RT = kRows>
 struct GStepLds {
-    GWin<LMAX> w;
+    GWin<LMAX, RT> w;
     float q[NN] __attribute__((aligned(16)));
     float z[NN] __attribute__((aligned(16)));
     float c[LMAX];
-    float u[kRows];
+    float u[RT];
 };
+
+// The step's window staged through registers: issued before the checkpoint stream (global loads
+// complete in issue order, so the window can be written to LDS while the stream is still in
+// flight) and committed to LDS afterwards. Record j < k-1 comes from ring slot (cslot + j) mod L,
+// record k-1 (this token) and q from the call's inputs; v covers the tile's RT rows.
+template <int LMAX, int RT>
+struct StepWindow {
+    static constexpr int KS = (LMAX * NN / 4 + kThreads - 1) / kThreads;
+    static constexpr int KCH = KS < 8 ? KS : 8;  // k slots held at once; the rest load at commit
+    static constexpr int VS = (LMAX * RT / 4 + kThreads - 1) / kThreads;
+    f32x4 kr[KCH], vr[VS], qr;
+    float ar, br;
+    size_t bh, bg;
+    const float *rk, *rv;  // ring k of the key head; ring v at the tile's first row
+    int cslot, k, tid;
+
+    __device__ StepWindow(const GLayer &Ld, const Tile &t, int tid_) : tid(tid_)
+    {
+        bh = (size_t)t.b * Ld.H + t.h;
+        bg = (size_t)t.b * Ld.G + t.g;
+        rk = Ld.ring_k + bg * Ld.L * NN;
+        rv = Ld.ring_v + bh * Ld.L * Ld.Dv + t.row0;
+    }
+    __device__ int slot_of(const GLayer &Ld, int j) const { return (int)((unsigned)(cslot + j) % (unsigned)Ld.L); }
+    __device__ const float *kaddr(const GLayer &Ld, const GTokenIO &io, int j, int c4) const
+    {
+        return (j < k - 1 ? rk + (size_t)slot_of(Ld, j) * NN : io.k + bg * NN) + 4 * c4;
+    }
+
+    __device__ void issue(const GLayer &Ld, const GTokenIO &io, const Tile &t, int cslot_, int k_)
+    {
+        cslot = cslot_;
+        k = k_;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sl = 0; sl < KCH; ++sl) {
+            const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+            const f32x4 val = *(const f32x4 *)kaddr(Ld, io, j < k ? j : k - 1, c4);
+            kr[sl] = j < k ? val : zero;
+        }
+#pragma unroll
+        for (int sl = 0; sl < VS; ++sl) {
+            const int e = tid + sl * kThreads, j = e / (RT / 4), c4 = e % (RT / 4);
+            const bool in = j < k && 4 * c4 < t.nrows;
+            const float *src = (in && j < k - 1) ? rv + (size_t)slot_of(Ld, j) * Ld.Dv + 4 * c4
+                                                 : io.v + bh * Ld.Dv + t.row0 + (in ? 4 * c4 : 0);
+            const f32x4 val = *(const f32x4 *)src;
+            vr[sl] = in ? val : zero;
+        }
+        const bool in = tid < k;
+        const bool ring = in && tid < k - 1;
+        const size_t ri = bh * Ld.L + (ring ? slot_of(Ld, tid) : 0);
+        const float a = ring ? Ld.ring_a[ri] : io.alpha[bh];
+        const float b = ring ? Ld.ring_b[ri] : io.beta[bh];
+        ar = in ? a : 0.f;
+        br = in ? b : 0.f;
+        const f32x4 q = *(const f32x4 *)(io.q + bg * NN + 4 * (tid % (NN / 4)));
+        qr = tid < NN / 4 ? q : zero;
+    }
+
+    __device__ void commit(GWin<LMAX, RT> &w, float *q, const GLayer &Ld, const GTokenIO &io)
+    {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s0 = 0; s0 < KS; s0 += KCH) {
+            if (s0 > 0) {
+#pragma unroll
+                for (int sl = 0; sl < KCH; ++sl) {
+                    const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+                    kr[sl] = (s0 + sl < KS && j < k) ? *(const f32x4 *)kaddr(Ld, io, j, c4) : zero;
+                }
+            }
+#pragma unroll
+            for (int sl = 0; sl < KCH; ++sl) {
+                const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+                if (s0 + sl < KS && j < LMAX) *(f32x4 *)&w.K[j][4 * c4] = kr[sl];
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < VS; ++sl) {
+            const int e = tid + sl * kThreads, j = e / (RT / 4), c4 = e % (RT / 4);
+            if (j < LMAX) *(f32x4 *)&w.V[j][4 * c4] = vr[sl];
+        }
+        if (tid < LMAX) {
+            w.a[tid] = ar;
+            w.b[tid] = br;
+        }
+        if (tid < NN / 4) *(f32x4 *)&q[4 * tid] = qr;
+    }
+};
+
+// Pointer update once per sequence after a step. Lockstep: the first tile of head 0 checks the
+// device pointers against the window position (a mismatch raises the flag) and advances them;
+// otherwise the last work-group of the sequence writes them.
+__device__ inline void step_advance(const GLayer &Ld, const Tile &t, bool uni, int pslot, int cslot, int k,
+                                    bool flush, int pos, int ck, int splits)
+{
+    if (uni) {
+        if (t.h == 0 && t.split == 0 && threadIdx.x == 0) {
+            const int dp = Ld.pos[t.b], dc = Ld.ckpt[t.b];
+            const bool ok = dc >= 0 && dp - dc == k - 1 && (int)((unsigned)dp % (unsigned)Ld.L) == pslot &&
+                            (int)((unsigned)dc % (unsigned)Ld.L) == cslot;
+            if (ok) {
+                Ld.pos[t.b] = dp + 1;
+                Ld.ckpt[t.b] = flush ? dp + 1 : dc;
+            } else {
+                __hip_atomic_fetch_or(Ld.flag, FLAG_POINTERS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    } else {
+        gseq_done(Ld, t.b, pos + 1, flush ? pos + 1 : ck, splits);
+    }
+}
+
+// Replayed output o = S_c z + sum_j c_j v_j from the row dots in s.u, and the token's record
+// appended at ring slot pslot (v by every tile, alpha / beta by the first tile, k by the first
+// tile of the key head's first value head).
+template <int LMAX, int RT>
+__device__ inline void step_output_append(const GStepLds<LMAX, RT> &s, const GLayer &Ld, const GTokenIO &io,
+                                          const Tile &t, int pslot, int k)
+{
+    const int tid = threadIdx.x;
+    const size_t bh = (size_t)t.b * Ld.H + t.h, bg = (size_t)t.b * Ld.G + t.g;
+    if (tid < t.nrows) {
+        float acc = s.u[tid];
+        for (int j = 0; j < k; ++j) acc = fmaf(s.c[j], s.w.V[j][tid], acc);
+        io.o[bh * Ld.Dv + t.row0 + tid] = acc;
+        Ld.ring_v[(bh * Ld.L + pslot) * Ld.Dv + t.row0 + tid] = s.w.V[k - 1][tid];
+    }
+    if (t.split == 0 && tid == 0) {
+        Ld.ring_a[bh * Ld.L + pslot] = s.w.a[k - 1];
+        Ld.ring_b[bh * Ld.L + pslot] = s.w.b[k - 1];
+    }
+    if (t.split == 0 && t.h % Ld.hpg == 0 && tid < NN / 4)
+        *(f32x4 *)(Ld.ring_k + (bg * Ld.L + pslot) * NN + 4 * tid) = *(const f32x4 *)&s.w.K[k - 1][4 * tid];
+}
 
 // CP: the checkpoint product reads the bf16 copy (replayed outputs; a flushing sequence reads and
 // folds the fp32 master).
@@ -317,7 +462,7 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
     __shared__ GStepLds<LMAX> s;
     const Tile t = gmap_tile(Ld);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t bh = (size_t)t.b * Ld.H + t.h, bg = (size_t)t.b * Ld.G + t.g;
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
     const size_t elem0 = (bh * Ld.Dv + t.row0) * NN;
     float *rows = Ld.master + elem0;
     auto load_state = [&](f32x4 (&dst)[GF::NL], bool master) {
@@ -325,76 +470,9 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
         else load_rows_f32(dst, rows, t.nrows, wave, lane);
     };
 
-    // Window in registers first (record j < k-1 from ring slot (cslot + j) mod L, the token's own
-    // record fresh), committed to LDS once the state stream is in flight.
-    constexpr int KS = (LMAX * NN / 4 + kThreads - 1) / kThreads;
-    constexpr int KCH = KS < 8 ? KS : 8;
-    constexpr int VS = (LMAX * kRows / 4 + kThreads - 1) / kThreads;
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const float *rk = Ld.ring_k + bg * Ld.L * NN;
-    const float *rv = Ld.ring_v + bh * Ld.L * Ld.Dv + t.row0;
+    StepWindow<LMAX, kRows> win(Ld, t, tid);
     const bool uni = ls.k > 0;
     int pslot = 0, cslot = 0, k = 1;
-    auto slot_of = [&](int j) { return (int)((unsigned)(cslot + j) % (unsigned)Ld.L); };
-    f32x4 kr[KCH], vr[VS], qr;
-    float ar = 0.f, br = 0.f;
-    auto kaddr = [&](int j, int c4) { return (j < k - 1 ? rk + (size_t)slot_of(j) * NN : io.k + bg * NN) + 4 * c4; };
-    auto issue_window = [&]() {
-#pragma unroll
-        for (int sl = 0; sl < KCH; ++sl) {
-            const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
-            const f32x4 val = *(const f32x4 *)kaddr(j < k ? j : k - 1, c4);
-            kr[sl] = j < k ? val : zero;
-        }
-#pragma unroll
-        for (int sl = 0; sl < VS; ++sl) {
-            const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
-            const bool in = j < k && 4 * c4 < t.nrows;
-            const float *src = (in && j < k - 1) ? rv + (size_t)slot_of(j) * Ld.Dv + 4 * c4
-                                                 : io.v + bh * Ld.Dv + t.row0 + (in ? 4 * c4 : 0);
-            const f32x4 val = *(const f32x4 *)src;
-            vr[sl] = in ? val : zero;
-        }
-        {
-            const bool in = tid < k;
-            const bool ring = in && tid < k - 1;
-            const size_t ri = bh * Ld.L + (ring ? slot_of(tid) : 0);
-            const float a = ring ? Ld.ring_a[ri] : io.alpha[bh];
-            const float b = ring ? Ld.ring_b[ri] : io.beta[bh];
-            ar = in ? a : 0.f;
-            br = in ? b : 0.f;
-            const f32x4 q = *(const f32x4 *)(io.q + bg * NN + 4 * (tid % (NN / 4)));
-            qr = tid < NN / 4 ? q : zero;
-        }
-    };
-    auto commit_window = [&]() {
-#pragma unroll
-        for (int s0 = 0; s0 < KS; s0 += KCH) {
-            if (s0 > 0) {
-#pragma unroll
-                for (int sl = 0; sl < KCH; ++sl) {
-                    const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
-                    kr[sl] = (s0 + sl < KS && j < k) ? *(const f32x4 *)kaddr(j, c4) : zero;
-                }
-            }
-#pragma unroll
-            for (int sl = 0; sl < KCH; ++sl) {
-                const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
-                if (s0 + sl < KS && j < LMAX) *(f32x4 *)&s.w.K[j][4 * c4] = kr[sl];
-            }
-        }
-#pragma unroll
-        for (int sl = 0; sl < VS; ++sl) {
-            const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
-            if (j < LMAX) *(f32x4 *)&s.w.V[j][4 * c4] = vr[sl];
-        }
-        if (tid < LMAX) {
-            s.w.a[tid] = ar;
-            s.w.b[tid] = br;
-        }
-        if (tid < NN / 4) *(f32x4 *)&s.q[4 * tid] = qr;
-    };
-
     f32x4 vf[GF::NL];
     int pos = 0, ck = 0;
     // With a read copy a flush-capable launch reads the master only for sequences that flush: in
@@ -404,7 +482,7 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
         pslot = ls.pslot;
         cslot = ls.cslot;
         k = ls.k;
-        issue_window();
+        win.issue(Ld, io, t, cslot, k);
         load_state(vf, FLUSH && k > Ld.L - Ld.Tmax);
     } else {
         if (!kLate) load_state(vf, false);  // the checkpoint stream first
@@ -420,31 +498,11 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
         cslot = (int)((unsigned)ck % (unsigned)Ld.L);
         k = c0 + 1;  // records in the window, this token included
         if (kLate) load_state(vf, k > Ld.L - Ld.Tmax);
-        issue_window();
+        win.issue(Ld, io, t, cslot, k);
     }
-    commit_window();
+    win.commit(s.w, s.q, Ld, io);
     __syncthreads();
     const bool flush = k > Ld.L - Ld.Tmax;
-    // Pointer update once per sequence. Lockstep: the work-group of head 0 checks the device
-    // pointers against the window position (a mismatch raises the flag) and advances them;
-    // otherwise the last work-group of the sequence writes them.
-    auto advance_pointers = [&]() {
-        if (uni) {
-            if (t.h == 0 && t.split == 0 && tid == 0) {
-                const int dp = Ld.pos[t.b], dc = Ld.ckpt[t.b];
-                const bool ok = dc >= 0 && dp - dc == k - 1 && (int)((unsigned)dp % (unsigned)Ld.L) == pslot &&
-                                (int)((unsigned)dc % (unsigned)Ld.L) == cslot;
-                if (ok) {
-                    Ld.pos[t.b] = dp + 1;
-                    Ld.ckpt[t.b] = flush ? dp + 1 : dc;
-                } else {
-                    __hip_atomic_fetch_or(Ld.flag, FLAG_POINTERS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-        } else {
-            gseq_done(Ld, t.b, pos + 1, flush ? pos + 1 : ck);
-        }
-    };
 
     if (FLUSH && flush) {
         gdn_fold_rows<LMAX>(vf, s.w, k, wave, lane);
@@ -452,7 +510,7 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
         rows_dot<1>(vf, s.q, 1, s.u, wave, lane);
         __syncthreads();
         if (tid < t.nrows) io.o[bh * Ld.Dv + t.row0 + tid] = s.u[tid];
-        advance_pointers();
+        step_advance(Ld, t, uni, pslot, cslot, k, true, pos, ck, Ld.psplit);
         return;
     }
 
@@ -462,19 +520,86 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
     __syncthreads();
     rows_dot<1>(vf, s.z, 1, s.u, wave, lane);
     __syncthreads();
-    if (tid < t.nrows) {
-        float acc = s.u[tid];
-        for (int j = 0; j < k; ++j) acc = fmaf(s.c[j], s.w.V[j][tid], acc);
-        io.o[bh * Ld.Dv + t.row0 + tid] = acc;
-        Ld.ring_v[(bh * Ld.L + pslot) * Ld.Dv + t.row0 + tid] = s.w.V[k - 1][tid];
+    step_output_append(s, Ld, io, t, pslot, k);
+    step_advance(Ld, t, uni, pslot, cslot, k, flush, pos, ck, Ld.psplit);
+}
+
+// Non-flush step reading the bf16 copy with one work-group per kRowsC = 128 value rows (a whole
+// head at Dv = 128): 16-byte loads of 8 values per lane, so each work-group streams twice the
+// bytes of a 64-row tile for the same fixed window cost, and the backward sweep runs once per
+// head instead of once per 64 rows. Used for Dk <= 128 and windows of up to 32 records (the LDS
+// window of 128 rows stays under 64 KiB).
+constexpr int kRowsC = 128;
+using GB = Geo<NN, PREC_BF16>;
+constexpr int NLC = (kRowsC + GB::RPB - 1) / GB::RPB;  // copy load slots per lane
+constexpr bool kCopyTiles = NN <= 128;
+static_assert(!kCopyTiles || NLC <= GB::LPR || NLC == 1, "transpose-reduce needs NLC <= LPR");
+
+template <int LMAX>
+__global__ void __launch_bounds__(kThreads) gdn_step_copy_kernel(GLayer Ld, GTokenIO io, Lockstep ls, int splits)
+{
+    __shared__ GStepLds<LMAX, kRowsC> s;
+    const Tile t = gmap_tile_rows<kRowsC>(Ld, splits);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    const unsigned short *rows = Ld.rcopy + (bh * Ld.Dv + t.row0) * NN;
+    const int c = lane % GB::LPR;  // this lane's 8 values of a row: 8c .. 8c+7
+    auto row_of = [&](int i) { return i * GB::RPB + wave * GB::RPI + lane / GB::LPR; };
+    u32x4 raw[NLC];
+    auto load_state = [&]() {
+#pragma unroll
+        for (int i = 0; i < NLC; ++i) {
+            const int r = row_of(i);
+            raw[i] = r < t.nrows ? load_nt(rows + (size_t)r * NN + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    StepWindow<LMAX, kRowsC> win(Ld, t, tid);
+    const bool uni = ls.k > 0;
+    int pslot, cslot, k, pos = 0, ck = 0;
+    if (uni) {
+        pslot = ls.pslot;
+        cslot = ls.cslot;
+        k = ls.k;
+        win.issue(Ld, io, t, cslot, k);
+        load_state();
+    } else {
+        load_state();  // the copy stream first
+        pos = Ld.pos[t.b];
+        ck = Ld.ckpt[t.b];
+        const int c0 = pos - ck;
+        if (!(ck >= 0 && c0 >= 0 && c0 + 1 <= Ld.L - Ld.Tmax)) {  // no sequence of this launch flushes
+            graise(Ld, FLAG_POINTERS);
+            gseq_done(Ld, t.b, pos, ck, splits);
+            return;
+        }
+        pslot = (int)((unsigned)pos % (unsigned)Ld.L);
+        cslot = (int)((unsigned)ck % (unsigned)Ld.L);
+        k = c0 + 1;
+        win.issue(Ld, io, t, cslot, k);
     }
-    if (t.split == 0 && tid == 0) {
-        Ld.ring_a[bh * Ld.L + pslot] = s.w.a[k - 1];
-        Ld.ring_b[bh * Ld.L + pslot] = s.w.b[k - 1];
+    win.commit(s.w, s.q, Ld, io);
+    __syncthreads();
+    if (wave == 0) gdn_sweep<LMAX>(s.w, s.q, k - 1, s.c, s.z, lane);
+    __syncthreads();
+
+    // S_c z: each lane's 8 widened values against z[8c .. 8c+7], summed over the row's lanes.
+    float part[NLC];
+#pragma unroll
+    for (int i = 0; i < NLC; ++i) part[i] = chunk_dot<PREC_BF16>(raw[i], &s.z[8 * c]);
+    transpose_reduce<NLC, GB::LPR>(part, lane);
+    bool writer;
+    const int first = tr_first<NLC, GB::LPR>(lane, &writer);
+    if (writer) {
+#pragma unroll
+        for (int e = 0; e < tr_count<NLC, GB::LPR>(); ++e) {
+            const int r = row_of(first + e);
+            if (r < kRowsC) s.u[r] = part[e];
+        }
     }
-    if (t.split == 0 && t.h % Ld.hpg == 0 && tid < NN / 4)
-        *(f32x4 *)(Ld.ring_k + (bg * Ld.L + pslot) * NN + 4 * tid) = *(const f32x4 *)&s.w.K[k - 1][4 * tid];
-    advance_pointers();
+    __syncthreads();
+    step_output_append(s, Ld, io, t, pslot, k);
+    step_advance(Ld, t, uni, pslot, cslot, k, false, pos, ck, splits);
 }
 
 // ==========================================================================================
@@ -731,6 +856,14 @@ inline unsigned gblocks(const GLayer &Ld) { return (unsigned)Ld.Bt * (unsigned)L
 template <int LMAX, bool CP>
 hipError_t step_lc(const GLayer &Ld, const GTokenIO &io, bool fc, Lockstep ls, hipStream_t st)
 {
+    if constexpr (CP && kCopyTiles && LMAX <= 32) {
+        if (!fc) {
+            const int splits = (Ld.Dv + kRowsC - 1) / kRowsC;
+            const unsigned grid = (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)splits;
+            hipLaunchKernelGGL((gdn_step_copy_kernel<LMAX>), dim3(grid), dim3(kThreads), 0, st, Ld, io, ls, splits);
+            return hipGetLastError();
+        }
+    }
     if (fc) hipLaunchKernelGGL((gdn_step_kernel<LMAX, true, CP>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
     else hipLaunchKernelGGL((gdn_step_kernel<LMAX, false, CP>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
     return hipGetLastError();

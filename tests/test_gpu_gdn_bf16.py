@@ -78,10 +78,18 @@ def test_gdn_bf16_serving():
     _run(c["Bt"], c["H"], c["G"], c["Dv"], c["Dk"], c["L"], workload.config_seed(6), 48, [0, 200])
 
 
-@pytest.mark.parametrize("shape", [(3, 4, 2, 100, 32, 7), (2, 2, 1, 32, 256, 5), (2, 4, 2, 64, 128, 1)])
+@pytest.mark.parametrize("shape", [
+    (3, 4, 2, 100, 32, 7, True),     # one ragged 128-row tile
+    (2, 2, 1, 32, 256, 5, True),     # Dk 256: 64-row tiles
+    (2, 4, 2, 64, 128, 1, True),     # L 1: every step flushes
+    (3, 4, 2, 200, 64, 20, False),   # two 128-row tiles (128 + 72), L 32 bucket, device pointers
+    (2, 2, 2, 256, 16, 9, True),     # Dk 16, two full 128-row tiles
+    (2, 2, 1, 128, 128, 40, False),  # L 64 bucket: 64-row tiles
+])
 def test_gdn_bf16_shapes(shape):
-    Bt, H, G, Dv, Dk, L = shape
-    _run(Bt, H, G, Dv, Dk, L, 141, 2 * L + 3, range(Bt))
+    """Replayed steps with 128-row copy tiles (Dk <= 128, L <= 32) and with 64-row tiles."""
+    Bt, H, G, Dv, Dk, L, lockstep = shape
+    _run(Bt, H, G, Dv, Dk, L, 141, 2 * L + 3, range(Bt), lockstep)
 
 
 @pytest.mark.parametrize("T,L", [(3, 7), (4, 16)])
