@@ -232,8 +232,8 @@ __device__ inline void load_rows_f32(f32x4 (&vf)[GF::NL], const float *rows, int
     const int c = lane % GF::LPR;
 #pragma unroll
     for (int i = 0; i < GF::NL; ++i) {
-        const int r = row_of_f32(i, wave, lane);
-        vf[i] = r < nrows ? as_f32x4(load_nt(rows + (size_t)r * NN + 4 * c)) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = row_of_f32(i, wave, lane), rr = r < nrows ? r : 0;
+        vf[i] = as_f32x4(load_nt(rows + (size_t)rr * NN + 4 * c));
     }
 }
 
@@ -245,7 +245,7 @@ __device__ inline void load_rows_bf16(f32x4 (&vf)[GF::NL], const unsigned short 
     for (int i = 0; i < GF::NL; ++i) {
         const int r = row_of_f32(i, wave, lane), rr = r < nrows ? r : 0;
         const u32x2 w = __builtin_nontemporal_load((const u32x2 *)(rows + (size_t)rr * NN + 4 * c));
-        vf[i] = r < nrows ? f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)} : f32x4{0.f, 0.f, 0.f, 0.f};
+        vf[i] = f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
     }
 }
 
@@ -550,7 +550,7 @@ __global__ void __launch_bounds__(kThreads) gdn_step_copy_kernel(GLayer Ld, GTok
 #pragma unroll
         for (int i = 0; i < NLC; ++i) {
             const int r = row_of(i);
-            raw[i] = r < t.nrows ? load_nt(rows + (size_t)r * NN + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+            raw[i] = load_nt(rows + (size_t)(r < t.nrows ? r : 0) * NN + 8 * c);
         }
     };
 

@@ -58,7 +58,9 @@ constexpr int kVEC = Geo<NN, PREC>::VEC;
 
 // ------------------------------------------------------------------------------------------
 // State rows of this work-group: slot i of a lane covers row i*RPB + wave*RPI + lane/LPR,
-// elements [(lane % LPR) * VEC, +VEC). Rows at or beyond nrows read as zero.
+// elements [(lane % LPR) * VEC, +VEC). Lanes of rows at or beyond nrows read row 0 instead
+// (every load is issued unconditionally, so a wait never covers more loads than it needs):
+// rows are independent in every use, and those rows are never stored or reduced across.
 // ------------------------------------------------------------------------------------------
 template <int PREC>
 __device__ inline void load_rows(u32x4 (&v)[kNL<PREC>], const char *rows, int nrows,
@@ -68,14 +70,13 @@ __device__ inline void load_rows(u32x4 (&v)[kNL<PREC>], const char *rows, int nr
     const int c = lane % G::LPR;
 #pragma unroll
     for (int i = 0; i < G::NL; ++i) {
-        const int r = i * G::RPB + wave * G::RPI + lane / G::LPR;
-        v[i] = (r < nrows) ? load_nt(rows + byte_off<PREC>((size_t)r * NN + (size_t)c * G::VEC))
-                           : u32x4{0u, 0u, 0u, 0u};
+        const int r = i * G::RPB + wave * G::RPI + lane / G::LPR, rr = r < nrows ? r : 0;
+        v[i] = load_nt(rows + byte_off<PREC>((size_t)rr * NN + (size_t)c * G::VEC));
     }
 }
 
 // MXFP4 block-scale codes of the chunks load_rows reads (a chunk is one block); rows at or
-// beyond nrows get 127 (scale 1; their sums are never used).
+// beyond nrows read row 0's codes, like their chunks (their sums are never used).
 template <int PREC>
 __device__ inline void load_mxscales(unsigned (&sc)[kNL<PREC>], const unsigned char *rows, int nrows,
                                      int wave, int lane)
@@ -85,7 +86,7 @@ __device__ inline void load_mxscales(unsigned (&sc)[kNL<PREC>], const unsigned c
 #pragma unroll
     for (int i = 0; i < G::NL; ++i) {
         const int r = i * G::RPB + wave * G::RPI + lane / G::LPR;
-        sc[i] = r < nrows ? rows[(size_t)r * (NN / 32) + c] : 127u;
+        sc[i] = rows[(size_t)(r < nrows ? r : 0) * (NN / 32) + c];
     }
 }
 
@@ -291,7 +292,8 @@ __device__ inline void write_copy_rows(const Layer &Ld, size_t bh, size_t elem0,
 #pragma unroll
         for (int i = 0; i < GF::NL; ++i) {
             const f32x4 f = vf[i];
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+            const float m = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
+            if (row_of<PREC_F32>(i, wave, lane) < nrows) amax = fmaxf(amax, m);
         }
         amax = block_max(amax, red);
         const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
@@ -395,14 +397,10 @@ __device__ inline void load_master_rows(const Layer &Ld, size_t elem0, f32x4 (&v
         const unsigned short *base = (const unsigned short *)Ld.master + elem0;
 #pragma unroll
         for (int i = 0; i < GF::NL; ++i) {
-            const int r = row_of<PREC_F32>(i, wave, lane);
-            if (r < nrows) {
-                const u32x2 w = __builtin_nontemporal_load((const u32x2 *)(base + (size_t)r * NN + 4 * c));
-                const f32x2 lo = f16x2_to_f32(w.x), hi = f16x2_to_f32(w.y);
-                vf[i] = f32x4{lo.x, lo.y, hi.x, hi.y};
-            } else {
-                vf[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            const int r = row_of<PREC_F32>(i, wave, lane), rr = r < nrows ? r : 0;
+            const u32x2 w = __builtin_nontemporal_load((const u32x2 *)(base + (size_t)rr * NN + 4 * c));
+            const f32x2 lo = f16x2_to_f32(w.x), hi = f16x2_to_f32(w.y);
+            vf[i] = f32x4{lo.x, lo.y, hi.x, hi.y};
         }
     }
 }
@@ -1221,9 +1219,8 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
     u32x4 v[G::NL];
 #pragma unroll
     for (int i = 0; i < G::NL; ++i) {
-        const int r = row_of<PREC>(i, wave, lane);
-        v[i] = r < t.nrows ? load_nt(rbase + chunk_off<PREC>(bh, t.row0 + r, lane % G::LPR, Ld.P))
-                           : u32x4{0u, 0u, 0u, 0u};
+        const int r = row_of<PREC>(i, wave, lane), rr = r < t.nrows ? r : 0;
+        v[i] = load_nt(rbase + chunk_off<PREC>(bh, t.row0 + rr, lane % G::LPR, Ld.P));
     }
     unsigned sc[G::NL];
     if constexpr (PREC == PREC_FP4) load_mxscales<PREC>(sc, Ld.mxscale + elem0 / 32, t.nrows, wave, lane);
