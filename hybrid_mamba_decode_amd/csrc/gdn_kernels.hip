@@ -677,10 +677,10 @@ __global__ void __launch_bounds__(kThreads) gdn_verify_kernel(GLayer Ld, GTokenI
     __shared__ GVerifyLds<LMAX, TQ> s;
     const Tile t = gmap_tile(Ld);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t bh = (size_t)t.b * Ld.H + t.h;
-    f32x4 vf[GF::NL];
-    if (CP) load_rows_bf16(vf, Ld.rcopy + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
-    else load_rows_f32(vf, Ld.master + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
+    const size_t bh = (size_t)t.b * Ld.H + t.h, bg = (size_t)t.b * Ld.G + t.g;
+    // Pointers first, then the window and the queries into registers, then the checkpoint stream:
+    // global loads complete in issue order, so the window reaches LDS and the T backward sweeps
+    // run while the stream is still in flight.
     const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
     const int count0 = pos - ck;
     if (!(ck >= 0 && count0 >= 0 && count0 <= Ld.L - Ld.Tmax && count0 + T <= Ld.L)) {
@@ -689,12 +689,86 @@ __global__ void __launch_bounds__(kThreads) gdn_verify_kernel(GLayer Ld, GTokenI
     }
     const int kw = count0 + T;
     const size_t bT = (size_t)t.b * T;
-    stage_window<LMAX>(s.w, Ld, t, ck, count0, kw, io.k + (bT * Ld.G + t.g) * NN, Ld.G * NN,
-                       io.v + (bT * Ld.H + t.h) * Ld.Dv + t.row0, Ld.H * Ld.Dv, io.alpha + bT * Ld.H + t.h,
-                       io.beta + bT * Ld.H + t.h, Ld.H);
-    for (int e = tid; e < T * (NN / 4); e += kThreads) {
-        const int q = e / (NN / 4), c4 = e % (NN / 4);
-        *(f32x4 *)&s.q[q][4 * c4] = *(const f32x4 *)(io.q + ((bT + q) * Ld.G + t.g) * NN + 4 * c4);
+    // record j < count0 from ring slot (ck + j) mod L, record count0 + q from draft q's inputs
+    const float *rk = Ld.ring_k + bg * Ld.L * NN;
+    const float *rv = Ld.ring_v + bh * Ld.L * Ld.Dv + t.row0;
+    auto slot_of = [&](int j) { return (int)((unsigned)(ck + j) % (unsigned)Ld.L); };
+    auto kaddr = [&](int j) {
+        return j < count0 ? rk + (size_t)slot_of(j) * NN : io.k + ((bT + (j - count0)) * Ld.G + t.g) * NN;
+    };
+    constexpr int KS = (LMAX * NN / 4 + kThreads - 1) / kThreads;
+    constexpr int KCH = KS < 8 ? KS : 8;  // k slots held at once; the rest load at commit
+    constexpr int VS = (LMAX * kRows / 4 + kThreads - 1) / kThreads;
+    constexpr int QS = (TQ * NN / 4 + kThreads - 1) / kThreads;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 kr[KCH], vr[VS], qr[QS];
+    float ar = 0.f, br = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < KCH; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+        const f32x4 val = *(const f32x4 *)(kaddr(j < kw ? j : kw - 1) + 4 * c4);
+        kr[sl] = j < kw ? val : zero;
+    }
+#pragma unroll
+    for (int sl = 0; sl < VS; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
+        const bool in = j < kw && 4 * c4 < t.nrows;
+        const int jj = in ? j : 0, cc = in ? 4 * c4 : 0;
+        const float *src = jj < count0 ? rv + (size_t)slot_of(jj) * Ld.Dv + cc
+                                       : io.v + ((bT + (jj - count0)) * Ld.H + t.h) * Ld.Dv + t.row0 + cc;
+        const f32x4 val = *(const f32x4 *)src;
+        vr[sl] = in ? val : zero;
+    }
+    {
+        const bool in = tid < kw;
+        const int jj = in ? tid : 0;
+        const size_t ri = jj < count0 ? bh * Ld.L + slot_of(jj) : 0;
+        const size_t fi = jj < count0 ? 0 : (bT + (jj - count0)) * Ld.H + t.h;
+        const float a = jj < count0 ? Ld.ring_a[ri] : io.alpha[fi];
+        const float b = jj < count0 ? Ld.ring_b[ri] : io.beta[fi];
+        ar = in ? a : 0.f;
+        br = in ? b : 0.f;
+    }
+#pragma unroll
+    for (int sl = 0; sl < QS; ++sl) {
+        const int e = tid + sl * kThreads, q = e / (NN / 4), c4 = e % (NN / 4);
+        const int qq = q < T ? q : 0;
+        const f32x4 val = *(const f32x4 *)(io.q + ((bT + qq) * Ld.G + t.g) * NN + 4 * c4);
+        qr[sl] = q < T ? val : zero;
+    }
+    f32x4 vf[GF::NL];
+    if (CP) load_rows_bf16(vf, Ld.rcopy + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
+    else load_rows_f32(vf, Ld.master + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
+
+    // Commit the window and the queries to LDS (k rows beyond the first KCH slots load here).
+#pragma unroll
+    for (int s0 = 0; s0 < KS; s0 += KCH) {
+        if (s0 > 0) {
+#pragma unroll
+            for (int sl = 0; sl < KCH; ++sl) {
+                const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+                kr[sl] = (s0 + sl < KS && j < kw) ? *(const f32x4 *)(kaddr(j) + 4 * c4) : zero;
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < KCH; ++sl) {
+            const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+            if (s0 + sl < KS && j < LMAX) *(f32x4 *)&s.w.K[j][4 * c4] = kr[sl];
+        }
+    }
+#pragma unroll
+    for (int sl = 0; sl < VS; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
+        if (j < LMAX) *(f32x4 *)&s.w.V[j][4 * c4] = vr[sl];
+    }
+    if (tid < LMAX) {
+        s.w.a[tid] = ar;
+        s.w.b[tid] = br;
+    }
+#pragma unroll
+    for (int sl = 0; sl < QS; ++sl) {
+        const int e = tid + sl * kThreads, q = e / (NN / 4), c4 = e % (NN / 4);
+        if (q < TQ) *(f32x4 *)&s.q[q][4 * c4] = qr[sl];
     }
     __syncthreads();
     for (int q = wave; q < T; q += kWaves) gdn_sweep<LMAX>(s.w, s.q[q], count0 + q, s.c[q], s.z[q], lane);
