@@ -227,6 +227,9 @@ __device__ inline void store_rows(float *rows, const f32x4 (&vf)[GF::NL], int nr
     }
 }
 
+// fp32 rows of a tile, one 16-byte load per lane and slot, all issued unconditionally: lanes of rows
+// at or beyond nrows read row 0 again (rows are independent in every use, and those are never
+// stored), so the issue sequence is straight-line and no wait covers more loads than it needs.
 __device__ inline void load_rows_f32(f32x4 (&vf)[GF::NL], const float *rows, int nrows, int wave, int lane)
 {
     const int c = lane % GF::LPR;
@@ -237,7 +240,8 @@ __device__ inline void load_rows_f32(f32x4 (&vf)[GF::NL], const float *rows, int
     }
 }
 
-// bf16 copy rows in the same geometry: 8 bytes (4 values) per lane and slot, widened exactly.
+// bf16 copy rows in the same geometry: 8 bytes (4 values) per lane and slot, widened exactly (rows
+// beyond the tile as in load_rows_f32).
 __device__ inline void load_rows_bf16(f32x4 (&vf)[GF::NL], const unsigned short *rows, int nrows, int wave, int lane)
 {
     const int c = lane % GF::LPR;
