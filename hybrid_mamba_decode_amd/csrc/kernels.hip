@@ -919,10 +919,10 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
     int pslot = 0, cslot = 0, k = 1;
     auto slot_of = [&](int j) { return (int)((unsigned)(cslot + j) % (unsigned)Ld.L); };
 
-    // 3. Window. Issued in two groups so that the staging registers of the first are free before
-    //    the second is loaded: (a) the group's B rows and C_t, staged through LDS, and (lane j)
-    //    dt_j of this head; (b) this lane's x_j (record j of its row, 0 beyond the window) and the
-    //    token's x, loaded after (a) is committed.
+    // 3. Window, in two groups: (a) the group's B rows and C_t, staged through LDS, and (lane j)
+    //    dt_j of this head, issued with the checkpoint stream; (b) this lane's x_j (record j of its
+    //    row, 0 beyond the window) and the token's x, loaded after the row dots, so that no x
+    //    register is held while the stream is in flight (record reads mostly hit the caches).
     constexpr int BS = (LMAX * NN / 4 + kThreads - 1) / kThreads;
     constexpr int BCH = BS < 8 ? BS : 8;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -1001,7 +1001,6 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
         }
     }
     if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = cq;
-    issue_x();
     // w_j = dt_j * exp(A * sum_{i>j} dt_i), decay = exp(A * sum_i dt_i): suffix sums by shuffles
     float wj, decay;
     {
@@ -1076,6 +1075,7 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
     }
     float u = u0 + u1;
     if constexpr (PREC == PREC_FP8) u *= Ld.scale[bh];
+    issue_x();
 
     if (bad) {
         raise_flag(Ld, FLAG_POINTERS);
