@@ -19,6 +19,7 @@
 //                         buffer fills and reads their output from the folded state
 //   gdn_flush_kernel      explicit flush, rollback commit, or materialize
 //   gdn_verify_kernel     output-only evaluation of T draft tokens + tentative append
+//   gdn_step_copy_kernel, gdn_verify_copy_kernel   the same through the bf16 copy, 128-row tiles
 //   gdn_load_kernel       master <- state, pointers reset
 //   gdn_conventional_kernel   read-update-write baseline
 //   gdn_snapshot_kernel   per-draft snapshot baseline (one read, T writes)
@@ -666,133 +667,142 @@ __global__ void gdn_advance_kernel(GLayer Ld, const int *accepted, int T)
 // checkpoint rows serves all T queries: U = S_c [z_1 .. z_T]. Drafts are appended tentatively at
 // slots (pos + q) mod L; no pointer moves.
 // ==========================================================================================
-template <int LMAX, int TQ>
+template <int LMAX, int TQ, int RT = kRows>
 struct GVerifyLds {
-    GWin<LMAX> w;
+    GWin<LMAX, RT> w;
     float q[TQ][NN] __attribute__((aligned(16)));
     float z[TQ][NN] __attribute__((aligned(16)));
     float c[TQ][LMAX];
-    float u[TQ][kRows];
+    float u[TQ][RT];
 };
 
-template <int LMAX, int TQ, bool CP>
-__global__ void __launch_bounds__(kThreads) gdn_verify_kernel(GLayer Ld, GTokenIO io, int T)
-{
-    __shared__ GVerifyLds<LMAX, TQ> s;
-    const Tile t = gmap_tile(Ld);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t bh = (size_t)t.b * Ld.H + t.h, bg = (size_t)t.b * Ld.G + t.g;
-    // Pointers first, then the window and the queries into registers, then the checkpoint stream:
-    // global loads complete in issue order, so the window reaches LDS and the T backward sweeps
-    // run while the stream is still in flight.
-    const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
-    const int count0 = pos - ck;
-    if (!(ck >= 0 && count0 >= 0 && count0 <= Ld.L - Ld.Tmax && count0 + T <= Ld.L)) {
-        graise(Ld, FLAG_POINTERS);
-        return;
-    }
-    const int kw = count0 + T;
-    const size_t bT = (size_t)t.b * T;
-    // record j < count0 from ring slot (ck + j) mod L, record count0 + q from draft q's inputs
-    const float *rk = Ld.ring_k + bg * Ld.L * NN;
-    const float *rv = Ld.ring_v + bh * Ld.L * Ld.Dv + t.row0;
-    auto slot_of = [&](int j) { return (int)((unsigned)(ck + j) % (unsigned)Ld.L); };
-    auto kaddr = [&](int j) {
-        return j < count0 ? rk + (size_t)slot_of(j) * NN : io.k + ((bT + (j - count0)) * Ld.G + t.g) * NN;
-    };
-    constexpr int KS = (LMAX * NN / 4 + kThreads - 1) / kThreads;
-    constexpr int KCH = KS < 8 ? KS : 8;  // k slots held at once; the rest load at commit
-    constexpr int VS = (LMAX * kRows / 4 + kThreads - 1) / kThreads;
-    constexpr int QS = (TQ * NN / 4 + kThreads - 1) / kThreads;
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+// The verify's window through registers: the count0 committed records from the ring (record j at
+// slot (ck + j) mod L), then the T drafts from the call's inputs, and the T queries. Issued before
+// the checkpoint stream (global loads complete in issue order), committed to LDS after it.
+template <int LMAX, int TQ, int RT>
+struct VerifyWindow {
+    static constexpr int KS = (LMAX * NN / 4 + kThreads - 1) / kThreads;
+    static constexpr int KCH = KS < 8 ? KS : 8;  // k slots held at once; the rest load at commit
+    static constexpr int VS = (LMAX * RT / 4 + kThreads - 1) / kThreads;
+    static constexpr int QS = (TQ * NN / 4 + kThreads - 1) / kThreads;
     f32x4 kr[KCH], vr[VS], qr[QS];
-    float ar = 0.f, br = 0.f;
-#pragma unroll
-    for (int sl = 0; sl < KCH; ++sl) {
-        const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
-        const f32x4 val = *(const f32x4 *)(kaddr(j < kw ? j : kw - 1) + 4 * c4);
-        kr[sl] = j < kw ? val : zero;
-    }
-#pragma unroll
-    for (int sl = 0; sl < VS; ++sl) {
-        const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
-        const bool in = j < kw && 4 * c4 < t.nrows;
-        const int jj = in ? j : 0, cc = in ? 4 * c4 : 0;
-        const float *src = jj < count0 ? rv + (size_t)slot_of(jj) * Ld.Dv + cc
-                                       : io.v + ((bT + (jj - count0)) * Ld.H + t.h) * Ld.Dv + t.row0 + cc;
-        const f32x4 val = *(const f32x4 *)src;
-        vr[sl] = in ? val : zero;
-    }
-    {
-        const bool in = tid < kw;
-        const int jj = in ? tid : 0;
-        const size_t ri = jj < count0 ? bh * Ld.L + slot_of(jj) : 0;
-        const size_t fi = jj < count0 ? 0 : (bT + (jj - count0)) * Ld.H + t.h;
-        const float a = jj < count0 ? Ld.ring_a[ri] : io.alpha[fi];
-        const float b = jj < count0 ? Ld.ring_b[ri] : io.beta[fi];
-        ar = in ? a : 0.f;
-        br = in ? b : 0.f;
-    }
-#pragma unroll
-    for (int sl = 0; sl < QS; ++sl) {
-        const int e = tid + sl * kThreads, q = e / (NN / 4), c4 = e % (NN / 4);
-        const int qq = q < T ? q : 0;
-        const f32x4 val = *(const f32x4 *)(io.q + ((bT + qq) * Ld.G + t.g) * NN + 4 * c4);
-        qr[sl] = q < T ? val : zero;
-    }
-    f32x4 vf[GF::NL];
-    if (CP) load_rows_bf16(vf, Ld.rcopy + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
-    else load_rows_f32(vf, Ld.master + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
+    float ar, br;
+    const float *rk, *rv;
+    size_t bh, bT;
+    int ck, count0, kw, T, tid;
 
-    // Commit the window and the queries to LDS (k rows beyond the first KCH slots load here).
+    __device__ int slot_of(const GLayer &Ld, int j) const { return (int)((unsigned)(ck + j) % (unsigned)Ld.L); }
+    __device__ const float *kaddr(const GLayer &Ld, const GTokenIO &io, const Tile &t, int j) const
+    {
+        return j < count0 ? rk + (size_t)slot_of(Ld, j) * NN : io.k + ((bT + (j - count0)) * Ld.G + t.g) * NN;
+    }
+
+    __device__ void issue(const GLayer &Ld, const GTokenIO &io, const Tile &t, int ck_, int count0_, int T_)
+    {
+        tid = threadIdx.x;
+        ck = ck_;
+        count0 = count0_;
+        T = T_;
+        kw = count0 + T;
+        bh = (size_t)t.b * Ld.H + t.h;
+        bT = (size_t)t.b * T;
+        rk = Ld.ring_k + ((size_t)t.b * Ld.G + t.g) * Ld.L * NN;
+        rv = Ld.ring_v + bh * Ld.L * Ld.Dv + t.row0;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s0 = 0; s0 < KS; s0 += KCH) {
-        if (s0 > 0) {
+        for (int sl = 0; sl < KCH; ++sl) {
+            const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+            const f32x4 val = *(const f32x4 *)(kaddr(Ld, io, t, j < kw ? j : kw - 1) + 4 * c4);
+            kr[sl] = j < kw ? val : zero;
+        }
+#pragma unroll
+        for (int sl = 0; sl < VS; ++sl) {
+            const int e = tid + sl * kThreads, j = e / (RT / 4), c4 = e % (RT / 4);
+            const bool in = j < kw && 4 * c4 < t.nrows;
+            const int jj = in ? j : 0, cc = in ? 4 * c4 : 0;
+            const float *src = jj < count0 ? rv + (size_t)slot_of(Ld, jj) * Ld.Dv + cc
+                                           : io.v + ((bT + (jj - count0)) * Ld.H + t.h) * Ld.Dv + t.row0 + cc;
+            const f32x4 val = *(const f32x4 *)src;
+            vr[sl] = in ? val : zero;
+        }
+        {
+            const bool in = tid < kw;
+            const int jj = in ? tid : 0;
+            const size_t ri = jj < count0 ? bh * Ld.L + slot_of(Ld, jj) : 0;
+            const size_t fi = jj < count0 ? 0 : (bT + (jj - count0)) * Ld.H + t.h;
+            const float a = jj < count0 ? Ld.ring_a[ri] : io.alpha[fi];
+            const float b = jj < count0 ? Ld.ring_b[ri] : io.beta[fi];
+            ar = in ? a : 0.f;
+            br = in ? b : 0.f;
+        }
+#pragma unroll
+        for (int sl = 0; sl < QS; ++sl) {
+            const int e = tid + sl * kThreads, q = e / (NN / 4), c4 = e % (NN / 4);
+            const int qq = q < T ? q : 0;
+            const f32x4 val = *(const f32x4 *)(io.q + ((bT + qq) * Ld.G + t.g) * NN + 4 * c4);
+            qr[sl] = q < T ? val : zero;
+        }
+    }
+
+    __device__ void commit(GVerifyLds<LMAX, TQ, RT> &s, const GLayer &Ld, const GTokenIO &io, const Tile &t)
+    {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s0 = 0; s0 < KS; s0 += KCH) {
+            if (s0 > 0) {
+#pragma unroll
+                for (int sl = 0; sl < KCH; ++sl) {
+                    const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+                    kr[sl] = (s0 + sl < KS && j < kw) ? *(const f32x4 *)(kaddr(Ld, io, t, j) + 4 * c4) : zero;
+                }
+            }
 #pragma unroll
             for (int sl = 0; sl < KCH; ++sl) {
                 const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
-                kr[sl] = (s0 + sl < KS && j < kw) ? *(const f32x4 *)(kaddr(j) + 4 * c4) : zero;
+                if (s0 + sl < KS && j < LMAX) *(f32x4 *)&s.w.K[j][4 * c4] = kr[sl];
             }
         }
 #pragma unroll
-        for (int sl = 0; sl < KCH; ++sl) {
-            const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
-            if (s0 + sl < KS && j < LMAX) *(f32x4 *)&s.w.K[j][4 * c4] = kr[sl];
+        for (int sl = 0; sl < VS; ++sl) {
+            const int e = tid + sl * kThreads, j = e / (RT / 4), c4 = e % (RT / 4);
+            if (j < LMAX) *(f32x4 *)&s.w.V[j][4 * c4] = vr[sl];
+        }
+        if (tid < LMAX) {
+            s.w.a[tid] = ar;
+            s.w.b[tid] = br;
+        }
+#pragma unroll
+        for (int sl = 0; sl < QS; ++sl) {
+            const int e = tid + sl * kThreads, q = e / (NN / 4), c4 = e % (NN / 4);
+            if (q < TQ) *(f32x4 *)&s.q[q][4 * c4] = qr[sl];
         }
     }
-#pragma unroll
-    for (int sl = 0; sl < VS; ++sl) {
-        const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
-        if (j < LMAX) *(f32x4 *)&s.w.V[j][4 * c4] = vr[sl];
-    }
-    if (tid < LMAX) {
-        s.w.a[tid] = ar;
-        s.w.b[tid] = br;
-    }
-#pragma unroll
-    for (int sl = 0; sl < QS; ++sl) {
-        const int e = tid + sl * kThreads, q = e / (NN / 4), c4 = e % (NN / 4);
-        if (q < TQ) *(f32x4 *)&s.q[q][4 * c4] = qr[sl];
-    }
-    __syncthreads();
-    for (int q = wave; q < T; q += kWaves) gdn_sweep<LMAX>(s.w, s.q[q], count0 + q, s.c[q], s.z[q], lane);
-    __syncthreads();
-    rows_dot<TQ>(vf, &s.z[0][0], T, &s.u[0][0], wave, lane);
-    __syncthreads();
-    for (int q = wave; q < T; q += kWaves) {
-        if (lane < t.nrows) {
+};
+
+// Outputs of a verify from the row dots in s.u and the window (o_q = S_c z_q + sum_j c_qj v_j for
+// the tile's rows), and the T drafts appended at ring slots (pos + q) mod L (v by every tile,
+// alpha / beta by the first tile, k by the first tile of the key head's first value head).
+template <int LMAX, int TQ, int RT>
+__device__ inline void verify_output_append(const GVerifyLds<LMAX, TQ, RT> &s, const GLayer &Ld, const GTokenIO &io,
+                                            const Tile &t, int pos, int count0, int T)
+{
+    const int tid = threadIdx.x;
+    const size_t bh = (size_t)t.b * Ld.H + t.h, bT = (size_t)t.b * T;
+    for (int e = tid; e < T * RT; e += kThreads) {
+        const int q = e / RT, r = e % RT;
+        if (r < t.nrows) {
             const int last = count0 + q;
-            float acc = s.u[q][lane];
-            for (int j = 0; j <= last; ++j) acc = fmaf(s.c[q][j], s.w.V[j][lane], acc);
-            io.o[((bT + q) * Ld.H + t.h) * Ld.Dv + t.row0 + lane] = acc;
+            float acc = s.u[q][r];
+            for (int j = 0; j <= last; ++j) acc = fmaf(s.c[q][j], s.w.V[j][r], acc);
+            io.o[((bT + q) * Ld.H + t.h) * Ld.Dv + t.row0 + r] = acc;
             const int slot = (int)((unsigned)(pos + q) % (unsigned)Ld.L);
-            Ld.ring_v[(bh * Ld.L + slot) * Ld.Dv + t.row0 + lane] = s.w.V[last][lane];
+            Ld.ring_v[(bh * Ld.L + slot) * Ld.Dv + t.row0 + r] = s.w.V[last][r];
         }
-        if (t.split == 0 && lane == 0) {
-            const int slot = (int)((unsigned)(pos + q) % (unsigned)Ld.L);
-            Ld.ring_a[bh * Ld.L + slot] = s.w.a[count0 + q];
-            Ld.ring_b[bh * Ld.L + slot] = s.w.b[count0 + q];
-        }
+    }
+    if (t.split == 0 && tid < T) {
+        const int slot = (int)((unsigned)(pos + tid) % (unsigned)Ld.L);
+        Ld.ring_a[bh * Ld.L + slot] = s.w.a[count0 + tid];
+        Ld.ring_b[bh * Ld.L + slot] = s.w.b[count0 + tid];
     }
     if (t.split == 0 && t.h % Ld.hpg == 0) {
         for (int e = tid; e < T * (NN / 4); e += kThreads) {
@@ -802,6 +812,86 @@ __global__ void __launch_bounds__(kThreads) gdn_verify_kernel(GLayer Ld, GTokenI
                 *(const f32x4 *)&s.w.K[count0 + q][4 * c4];
         }
     }
+}
+
+template <int LMAX, int TQ, bool CP>
+__global__ void __launch_bounds__(kThreads) gdn_verify_kernel(GLayer Ld, GTokenIO io, int T)
+{
+    __shared__ GVerifyLds<LMAX, TQ> s;
+    const Tile t = gmap_tile(Ld);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    // Pointers first, then the window and the queries into registers, then the checkpoint stream:
+    // global loads complete in issue order, so the window reaches LDS and the T backward sweeps
+    // run while the stream is still in flight.
+    const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
+    const int count0 = pos - ck;
+    if (!(ck >= 0 && count0 >= 0 && count0 <= Ld.L - Ld.Tmax && count0 + T <= Ld.L)) {
+        graise(Ld, FLAG_POINTERS);
+        return;
+    }
+    VerifyWindow<LMAX, TQ, kRows> win;
+    win.issue(Ld, io, t, ck, count0, T);
+    f32x4 vf[GF::NL];
+    if (CP) load_rows_bf16(vf, Ld.rcopy + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
+    else load_rows_f32(vf, Ld.master + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
+    win.commit(s, Ld, io, t);
+    __syncthreads();
+    for (int q = wave; q < T; q += kWaves) gdn_sweep<LMAX>(s.w, s.q[q], count0 + q, s.c[q], s.z[q], lane);
+    __syncthreads();
+    rows_dot<TQ>(vf, &s.z[0][0], T, &s.u[0][0], wave, lane);
+    __syncthreads();
+    verify_output_append(s, Ld, io, t, pos, count0, T);
+}
+
+// Verify through the bf16 copy with one work-group per 128 value rows (as gdn_step_copy_kernel):
+// 16-byte loads of 8 values per lane, the T sweeps once per head.
+template <int LMAX, int TQ>
+__global__ void __launch_bounds__(kThreads) gdn_verify_copy_kernel(GLayer Ld, GTokenIO io, int T, int splits)
+{
+    __shared__ GVerifyLds<LMAX, TQ, kRowsC> s;
+    const Tile t = gmap_tile_rows<kRowsC>(Ld, splits);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
+    const int count0 = pos - ck;
+    if (!(ck >= 0 && count0 >= 0 && count0 <= Ld.L - Ld.Tmax && count0 + T <= Ld.L)) {
+        graise(Ld, FLAG_POINTERS);
+        return;
+    }
+    VerifyWindow<LMAX, TQ, kRowsC> win;
+    win.issue(Ld, io, t, ck, count0, T);
+    const unsigned short *rows = Ld.rcopy + (bh * Ld.Dv + t.row0) * NN;
+    const int c = lane % GB::LPR;  // this lane's 8 values of a row: 8c .. 8c+7
+    auto row_of = [&](int i) { return i * GB::RPB + wave * GB::RPI + lane / GB::LPR; };
+    u32x4 raw[NLC];
+#pragma unroll
+    for (int i = 0; i < NLC; ++i) {
+        const int r = row_of(i);
+        raw[i] = load_nt(rows + (size_t)(r < t.nrows ? r : 0) * NN + 8 * c);
+    }
+    win.commit(s, Ld, io, t);
+    __syncthreads();
+    for (int q = wave; q < T; q += kWaves) gdn_sweep<LMAX>(s.w, s.q[q], count0 + q, s.c[q], s.z[q], lane);
+    __syncthreads();
+    // S_c z_q for every query: each lane's 8 widened values against z_q[8c .. 8c+7].
+    float part[NLC * TQ];
+#pragma unroll
+    for (int q = 0; q < TQ; ++q)
+#pragma unroll
+        for (int i = 0; i < NLC; ++i) part[q * NLC + i] = q < T ? chunk_dot<PREC_BF16>(raw[i], &s.z[q][8 * c]) : 0.f;
+    transpose_reduce<NLC * TQ, GB::LPR>(part, lane);
+    bool writer;
+    const int first = tr_first<NLC * TQ, GB::LPR>(lane, &writer);
+    if (writer) {
+#pragma unroll
+        for (int e = 0; e < tr_count<NLC * TQ, GB::LPR>(); ++e) {
+            const int idx = first + e, q = idx / NLC, r = row_of(idx % NLC);
+            if (q < T && r < kRowsC) s.u[q][r] = part[e];
+        }
+    }
+    __syncthreads();
+    verify_output_append(s, Ld, io, t, pos, count0, T);
 }
 
 // ==========================================================================================
@@ -969,6 +1059,14 @@ hipError_t flush_l(const GLayer &Ld, int mode, const int *arg, int T, float *out
 template <int LMAX, bool CP>
 hipError_t verify_lc(const GLayer &Ld, const GTokenIO &io, int T, hipStream_t st)
 {
+    if constexpr (CP && kCopyTiles && LMAX <= 32) {
+        const int splits = (Ld.Dv + kRowsC - 1) / kRowsC;
+        const dim3 grid((unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)splits), block(kThreads);
+        if (T <= 2) hipLaunchKernelGGL((gdn_verify_copy_kernel<LMAX, 2>), grid, block, 0, st, Ld, io, T, splits);
+        else if (T <= 4) hipLaunchKernelGGL((gdn_verify_copy_kernel<LMAX, 4>), grid, block, 0, st, Ld, io, T, splits);
+        else hipLaunchKernelGGL((gdn_verify_copy_kernel<LMAX, 8>), grid, block, 0, st, Ld, io, T, splits);
+        return hipGetLastError();
+    }
     const dim3 grid(gblocks(Ld)), block(kThreads);
     if (T <= 2) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 2, CP>), grid, block, 0, st, Ld, io, T);
     else if (T <= 4) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 4, CP>), grid, block, 0, st, Ld, io, T);

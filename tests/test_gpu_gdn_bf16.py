@@ -92,10 +92,17 @@ def test_gdn_bf16_shapes(shape):
     _run(Bt, H, G, Dv, Dk, L, 141, 2 * L + 3, range(Bt), lockstep)
 
 
-@pytest.mark.parametrize("T,L", [(3, 7), (4, 16)])
-def test_gdn_bf16_spec(T, L):
-    """Verify + rollback through the bf16 copy; the commit-time flushes refresh it."""
-    Bt, H, G, Dv, Dk, seed = 3, 4, 2, 32, 64, 151
+@pytest.mark.parametrize("T,L,Dv,Dk", [
+    (3, 7, 32, 64),      # one ragged 128-row tile
+    (4, 16, 32, 64),
+    (8, 16, 200, 128),   # two 128-row tiles (128 + 72), the widest draft bucket
+    (2, 32, 128, 32),    # L 32 bucket
+    (4, 40, 64, 128),    # L 64 bucket: 64-row tiles
+])
+def test_gdn_bf16_spec(T, L, Dv, Dk):
+    """Verify + rollback through the bf16 copy (128-row tiles for Dk <= 128 and L <= 32, 64-row
+    tiles otherwise); the commit-time flushes refresh it."""
+    Bt, H, G, seed = 3, 4, 2, 151
     S0 = workload.gdn_initial_state(seed, Bt, H, Dv, Dk)
     lay = rs.GDNReplay(Bt, H, G, Dv, Dk, buffer_len=L, max_draft=T, read_prec="bf16")
     lay.load_state(dev(S0))
@@ -103,7 +110,7 @@ def test_gdn_bf16_spec(T, L):
     S = S0.astype(np.float64)
     rng = np.random.default_rng(seed)
     flushed = False
-    for it in range(24):
+    for it in range(24 if L <= 16 else 2 * L + 8):  # long enough for a commit-time flush
         drafts = workload.gdn_draft_inputs(seed, it, Bt, T, H, G, Dv, Dk)
         acc = rng.integers(0, T + 1, Bt).astype(np.int32)
         o = host(lay.spec_verify(*(dev(a) for a in drafts)))
