@@ -630,10 +630,57 @@ __global__ void __launch_bounds__(kThreads) gdn_flush_kernel(GLayer Ld, int mode
     else if (mode == MODE_MASK) fold = (arg == nullptr || arg[t.b] != 0) && count > 0;
     else fold = true;
     if (!fold) return;
+    // The window (every record from the ring: record j at slot (ck + j) mod L) into registers
+    // first, then the checkpoint rows; the window reaches LDS while the rows are in flight.
+    constexpr int KS = (LMAX * NN / 4 + kThreads - 1) / kThreads;
+    constexpr int KCH = KS < 8 ? KS : 8;  // k slots held at once; the rest load at the commit
+    constexpr int VS = (LMAX * kRows / 4 + kThreads - 1) / kThreads;
+    const int tid = threadIdx.x;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const float *rk = Ld.ring_k + ((size_t)t.b * Ld.G + t.g) * Ld.L * NN;
+    const float *rv = Ld.ring_v + bh * Ld.L * Ld.Dv + t.row0;
+    auto slot_of = [&](int j) { return (int)((unsigned)(ck + (j < count ? j : 0)) % (unsigned)Ld.L); };
+    f32x4 kr[KCH], vr[VS];
+#pragma unroll
+    for (int sl = 0; sl < KCH; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+        const f32x4 val = *(const f32x4 *)(rk + (size_t)slot_of(j) * NN + 4 * c4);
+        kr[sl] = j < count ? val : zero;
+    }
+#pragma unroll
+    for (int sl = 0; sl < VS; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
+        const bool in = j < count && 4 * c4 < t.nrows;
+        const f32x4 val = *(const f32x4 *)(rv + (size_t)slot_of(j) * Ld.Dv + (in ? 4 * c4 : 0));
+        vr[sl] = in ? val : zero;
+    }
+    const float ar = Ld.ring_a[bh * Ld.L + slot_of(tid)], br = Ld.ring_b[bh * Ld.L + slot_of(tid)];
     f32x4 vf[GF::NL];
     load_rows_f32(vf, Ld.master + elem0, t.nrows, wave, lane);
-    // every record comes from the ring (nring = count); the fresh-input pointers are never read
-    stage_window<LMAX>(w, Ld, t, ck, count, count, Ld.ring_k, 0, Ld.ring_v, 0, Ld.ring_a, Ld.ring_b, 0);
+#pragma unroll
+    for (int s0 = 0; s0 < KS; s0 += KCH) {
+        if (s0 > 0) {
+#pragma unroll
+            for (int sl = 0; sl < KCH; ++sl) {
+                const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+                kr[sl] = (s0 + sl < KS && j < count) ? *(const f32x4 *)(rk + (size_t)slot_of(j) * NN + 4 * c4) : zero;
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < KCH; ++sl) {
+            const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+            if (s0 + sl < KS && j < LMAX) *(f32x4 *)&w.K[j][4 * c4] = kr[sl];
+        }
+    }
+#pragma unroll
+    for (int sl = 0; sl < VS; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
+        if (j < LMAX) *(f32x4 *)&w.V[j][4 * c4] = vr[sl];
+    }
+    if (tid < LMAX) {
+        w.a[tid] = tid < count ? ar : 0.f;
+        w.b[tid] = tid < count ? br : 0.f;
+    }
     __syncthreads();
     gdn_fold_rows<LMAX>(vf, w, count, wave, lane);
     if (mode == MODE_MATERIALIZE) {
