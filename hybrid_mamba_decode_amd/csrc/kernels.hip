@@ -513,7 +513,10 @@ __device__ inline Tile map_heads(const Layer &Ld, int hpb)
     return t;
 }
 
-template <int PREC, int LMAX, int ROWS, bool FLUSH, bool MIX>
+// FLUSH: 0 = no sequence of the launch flushes; 1 = some may (their buffer fills); 2 = every
+// sequence flushes (a lockstep flush step with an fp32 master and a narrow read copy: the master
+// rows are issued right behind the window, and the replay path is not compiled in).
+template <int PREC, int LMAX, int ROWS, int FLUSH, bool MIX>
 __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lockstep ls)
 {
     using G = Geo<NN, PREC>;
@@ -557,6 +560,9 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     // position says this step flushes, ahead of the window loads: a work-group then has as many
     // checkpoint bytes in flight as one fp32 head gives.
     constexpr bool kHalfPre = FLUSH && HPB == 2;
+    constexpr bool kAll = FLUSH == 2;
+    static_assert(!kAll || (HPB == 1 && !kPreload), "all-flush launches: one head, master rows issued early");
+    f32x4 mf[kAll ? GF::NL : 1];
     u32x2 mh[kHalfPre ? HPB : 1][GF::NL];
     auto load_master_half = [&]() {
         const int cf4 = lane % GF::LPR;
@@ -660,6 +666,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         issue_window();
         if constexpr (MIX) issue_mix(ls.rslot);
         if (kPreload) load_state();
+        if constexpr (kAll) load_master_rows(Ld, (bh0 * Ld.P + t.row0) * NN, mf, t.nrows, wave, lane);
     } else {
         // checkpoint stream first; the window addresses wait for this sequence's pointers
         if (kPreload) load_state();
@@ -680,6 +687,12 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         if constexpr (MIX) issue_mix((int)((unsigned)pos % (unsigned)Ld.R));
     }
     const bool flush = k > Ld.L - Ld.Tmax;
+    if constexpr (kAll) {
+        if (!(uni && flush)) {  // launched only for lockstep flush steps
+            raise_flag(Ld, FLAG_POINTERS);
+            return;
+        }
+    }
 
     // Pointer update, once per sequence. Lockstep: the work-group owning head 0 checks the device
     // pointers against the window position (a mismatch means they were corrupted: flag, no
@@ -789,6 +802,9 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
                     const f32x2 lo = f16x2_to_f32(mh[hh][i].x), hi = f16x2_to_f32(mh[hh][i].y);
                     vf[i] = f32x4{lo.x, lo.y, hi.x, hi.y};
                 }
+            } else if constexpr (kAll) {
+#pragma unroll
+                for (int i = 0; i < GF::NL; ++i) vf[i] = mf[i];
             } else {
                 load_master_rows(Ld, elem0, vf, t.nrows, wave, lane);
             }
@@ -811,55 +827,57 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         return;
     }
 
-    // 6. Replay: the scores B_j . C_t times every head's weights (GS threads per record; LDS
-    //    only, while the checkpoint rows may still be in flight), then the row dots with C_t
-    //    through the read copy.
-    if (!kPreload) load_state();
-    if constexpr (MIX) load_cchunk<PREC>(cc, s.Cq, lane);
-    {
-        constexpr int GS = kThreads / LMAX;
-        const int j = tid / GS, sub = tid % GS;
-        float gj = 0.f;
-        for (int n = sub; n < NN; n += GS) gj = fmaf(s.Bw[j][n], s.Cq[n], gj);
-#pragma unroll
-        for (int o = GS / 2; o >= 1; o >>= 1) gj += __shfl_xor(gj, o, 64);
-        if (sub == 0)
-#pragma unroll
-            for (int hh = 0; hh < HPB; ++hh) s.coef[hh][j] = s.w[hh][j] * gj;
-    }
-    float part[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        part[i] = chunk_dot<PREC>(v[i], cc);
-        if constexpr (PREC == PREC_FP4) part[i] = mx_scaled(part[i], sc[i]);
-    }
-    {
-        transpose_reduce<NL, G::LPR>(part, lane);
-        bool writer;
-        const int first = tr_first<NL, G::LPR>(lane, &writer);
-        const int r = first * G::RPB + wave * G::RPI + lane / G::LPR;
-        if (writer && r < ROWS) s.u[r] = part[0];
-    }
-    __syncthreads();
+    if constexpr (!kAll) {
+        // 6. Replay: the scores B_j . C_t times every head's weights (GS threads per record; LDS
+        //    only, while the checkpoint rows may still be in flight), then the row dots with C_t
+        //    through the read copy.
+        if (!kPreload) load_state();
+        if constexpr (MIX) load_cchunk<PREC>(cc, s.Cq, lane);
+        {
+            constexpr int GS = kThreads / LMAX;
+            const int j = tid / GS, sub = tid % GS;
+            float gj = 0.f;
+            for (int n = sub; n < NN; n += GS) gj = fmaf(s.Bw[j][n], s.Cq[n], gj);
+    #pragma unroll
+            for (int o = GS / 2; o >= 1; o >>= 1) gj += __shfl_xor(gj, o, 64);
+            if (sub == 0)
+    #pragma unroll
+                for (int hh = 0; hh < HPB; ++hh) s.coef[hh][j] = s.w[hh][j] * gj;
+        }
+        float part[NL];
+    #pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            part[i] = chunk_dot<PREC>(v[i], cc);
+            if constexpr (PREC == PREC_FP4) part[i] = mx_scaled(part[i], sc[i]);
+        }
+        {
+            transpose_reduce<NL, G::LPR>(part, lane);
+            bool writer;
+            const int first = tr_first<NL, G::LPR>(lane, &writer);
+            const int r = first * G::RPB + wave * G::RPI + lane / G::LPR;
+            if (writer && r < ROWS) s.u[r] = part[0];
+        }
+        __syncthreads();
 
-    // 7. Combine and append.
-    if (tid < ROWS && tid % kRows < t.nrows) {
-        const int hh = tid / kRows, p = tid % kRows;
-        float acc = s.decay[hh] * (s.u[tid] * scl_r);
-#pragma unroll 4
-        for (int j = 0; j < k; ++j) acc = fmaf(s.coef[hh][j], s.xw[j][tid], acc);
-        const float xt = s.xw[k - 1][tid];
-        acc = fmaf(Ld.D[t.h + hh], xt, acc);
-        io.y[(bh0 + hh) * Ld.P + t.row0 + p] = MIX ? acc * silu_f(zg) : acc;
-        Ld.ring_x[((bh0 + hh) * Ld.L + pslot) * Ld.P + t.row0 + p] = xt;
+        // 7. Combine and append.
+        if (tid < ROWS && tid % kRows < t.nrows) {
+            const int hh = tid / kRows, p = tid % kRows;
+            float acc = s.decay[hh] * (s.u[tid] * scl_r);
+    #pragma unroll 4
+            for (int j = 0; j < k; ++j) acc = fmaf(s.coef[hh][j], s.xw[j][tid], acc);
+            const float xt = s.xw[k - 1][tid];
+            acc = fmaf(Ld.D[t.h + hh], xt, acc);
+            io.y[(bh0 + hh) * Ld.P + t.row0 + p] = MIX ? acc * silu_f(zg) : acc;
+            Ld.ring_x[((bh0 + hh) * Ld.L + pslot) * Ld.P + t.row0 + p] = xt;
+        }
+        if (t.split == 0 && wave < HPB && lane == k - 1) Ld.ring_dt[(bh0 + wave) * Ld.L + pslot] = dtj;
+        if (t.split == 0 && t.h % Ld.hpg == 0 && tid < NN / 4) {
+            const size_t off = (((size_t)t.b * Ld.G + t.g) * Ld.L + pslot) * NN + 4 * tid;
+            *(f32x4 *)(Ld.ring_B + off) = *(const f32x4 *)&s.Bw[k - 1][4 * tid];
+            if (Ld.ring_C) *(f32x4 *)(Ld.ring_C + off) = *(const f32x4 *)&s.Cq[4 * tid];
+        }
+        advance_pointers();
     }
-    if (t.split == 0 && wave < HPB && lane == k - 1) Ld.ring_dt[(bh0 + wave) * Ld.L + pslot] = dtj;
-    if (t.split == 0 && t.h % Ld.hpg == 0 && tid < NN / 4) {
-        const size_t off = (((size_t)t.b * Ld.G + t.g) * Ld.L + pslot) * NN + 4 * tid;
-        *(f32x4 *)(Ld.ring_B + off) = *(const f32x4 *)&s.Bw[k - 1][4 * tid];
-        if (Ld.ring_C) *(f32x4 *)(Ld.ring_C + off) = *(const f32x4 *)&s.Cq[4 * tid];
-    }
-    advance_pointers();
 }
 
 // ==========================================================================================
@@ -1586,7 +1604,7 @@ __global__ void __launch_bounds__(kThreads) snapshot_verify_kernel(Layer Ld, flo
 // ------------------------------------------------------------------------------------------
 inline unsigned nblocks(const Layer &Ld) { return (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)Ld.psplit; }
 
-template <int PREC, int LMAX, int ROWS, bool FLUSH, bool MIX>
+template <int PREC, int LMAX, int ROWS, int FLUSH, bool MIX>
 hipError_t step_rows(const Layer &Ld, const TokenIO &io, Lockstep ls, hipStream_t st)
 {
     const unsigned grid = nblocks(Ld) / (ROWS / kRows);
@@ -1613,6 +1631,9 @@ hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockst
         if constexpr (LMAX <= 32)
             if (Ld.mprec != MASTER_F32 && Ld.psplit == 1 && Ld.hpg % 2 == 0)
                 return step_rows<PREC, LMAX, 2 * kRows, true, MIX>(Ld, io, ls, st);
+        // lockstep flush step, fp32 master, narrow copy: every sequence flushes
+        if constexpr (PREC == PREC_BF16 || PREC == PREC_FP8 || PREC == PREC_FP4)
+            if (ls.k > 0 && Ld.mprec == MASTER_F32) return step_rows<PREC, LMAX, kRows, 2, MIX>(Ld, io, ls, st);
         return step_rows<PREC, LMAX, kRows, true, MIX>(Ld, io, ls, st);
     }
     if constexpr (!MIX && (PREC == PREC_FP8 || PREC == PREC_FP4) && LMAX == 16 && NN <= 128) {
