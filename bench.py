@@ -172,7 +172,7 @@ def main():
                                f"{prec} read path" + ("" if mprec == "fp32" else f", {mprec} master"),
                    "batch": Bt, "buffer_len": L, "read_prec": prec, "master_prec": mprec},
         "roofline": {
-            "kernel": "replay step, non-flush (step_kernel<prec, L bucket 16, rows, false>)",
+            "kernel": "replay step, non-flush (step_kernel<prec, L bucket 16, rows, 0>; narrow_step_kernel for fp8 / MXFP4)",
             "bound": "hbm",
             "achieved": round(nf_gbps, 1),
             "peak": HBM_PEAK_GBPS,
