@@ -100,7 +100,8 @@ def main():
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     A_d, D_d = dev(A), dev(D)
     S0_d = dev(S0)
-    pool = [tuple(dev(a) for a in workload.step_inputs(seed, t, Bt, H, P, N, G)) for t in range(args.pool)]
+    host_pool = [workload.step_inputs(seed, t, Bt, H, P, N, G) for t in range(args.pool)]
+    pool = [tuple(dev(a) for a in tok) for tok in host_pool]
     y = torch.empty(Bt, H, P, device="cuda")
 
     lay = rs.ReplaySSM(Bt, H, P, N, G, A_d, D_d, buffer_len=L, read_prec=prec, master_prec=mprec,
@@ -129,6 +130,10 @@ def main():
     wall = time.perf_counter() - t0
     assert lay.check() == rs.RSSM_OK
     assert torch.isfinite(y).all().item()
+    # parity of the timed run: the last step's outputs and the state after it, for a few
+    # sequences, against the float64 stepwise oracle run over the same K tokens
+    timed_y = y.clone()
+    timed_state = lay.materialize_state() if not args.kernels_only else None
 
     # The same K steps again without the per-launch timing events (each event adds a short gap
     # between launches); reported beside `value`, which keeps the instrumented timed region.
@@ -152,6 +157,11 @@ def main():
     fl_gbps = (bytes_fl * is_flush.sum()) / durs[is_flush].sum() / 1e9 if is_flush.any() else None
     amort_bytes = traffic.replay_window_amortized(H, P, N, G, L, prec, master=mstore) * Bt
     value = Bt * K / wall
+    # one whole window from the per-launch event means (k = 1 .. L-1 replayed, then the flush
+    # step): independent of how K falls on window boundaries
+    window_us = None
+    if all((ks == kk).any() for kk in range(1, L + 1)):
+        window_us = sum(float(durs[ks == kk].mean()) for kk in range(1, L + 1)) * 1e6
 
     result = {
         "metric": "SSM decode tokens/s/layer at batch 256 + achieved HBM GB/s (% of peak)",
@@ -183,6 +193,7 @@ def main():
             "alg_bytes_per_launch": int(bytes_nf[nf].mean()),
         },
         "tokens_per_s_without_launch_events": round(Bt * K / wall_plain, 1),
+        "tokens_per_s_window_amortized": round(Bt * L / (window_us * 1e-6), 1) if window_us else None,
         "hbm_gbps_all_steps": round((bytes_nf[nf].sum() + bytes_fl * is_flush.sum()) / durs.sum() / 1e9, 1),
         "alg_bytes_per_step_amortized": int(amort_bytes),
         "nonflush_us_by_k": {int(kk): round(float(durs[ks == kk].mean()) * 1e6, 1) for kk in range(1, L)
@@ -231,31 +242,72 @@ def main():
         result["speedup_vs_conventional"] = round(value / conv_tps, 3)
         del state
 
+    if not args.kernels_only:
+        result["timed_run_parity"] = timed_parity(host_pool, K, A, D, S0, timed_y.cpu().numpy(),
+                                                  timed_state.cpu().numpy(), prec, mprec)
     if not args.no_cpu_baseline and not args.kernels_only:
-        result["cpu_baseline"] = cpu_baseline(args, workload, H, P, N, G, Bt, seed, A, D, S0)
+        result["cpu_baseline"] = cpu_baseline(args, host_pool, Bt, A, D, S0)
 
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(args, workload, H, P, N, G, Bt, seed, A, D, S0):
+def timed_parity(host_pool, K, A, D, S0, y, state, prec, mprec):
+    """Normwise error (max |diff| / max |ref|) of the timed run's last outputs and final state
+    against the float64 stepwise oracle over the same K tokens, for four sampled sequences."""
+    import oracle
+    Bt = S0.shape[0]
+    sample = np.array(sorted({0, Bt // 3, (2 * Bt) // 3, Bt - 1}))
+    S = S0[sample].astype(np.float64)
+    pool = [tuple(np.ascontiguousarray(a[sample]) for a in tok) for tok in host_pool]
+    y_ref = None
+    for k in range(K):
+        y_ref = oracle.step(S, *pool[k % len(pool)], A, D)
+    err = lambda a, r: float(np.max(np.abs(a - r)) / np.max(np.abs(r)))
+    return {"sequences": [int(b) for b in sample], "last_step_output_err": err(y[sample], y_ref),
+            "final_state_err": err(state[sample], S), "read_prec": prec, "master_prec": mprec,
+            "note": "normwise relative error vs the float64 stepwise oracle"}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(args, host_pool, Bt, A, D, S0):
     """The float64 stepwise oracle on the host cores: the full batch of the same layer, decode
     steps cycling through the same pool of seeded token sets as the GPU leg, until about
-    --cpu-seconds of oracle time have run. Only the oracle calls are timed."""
+    --cpu-seconds of oracle time have run, on the oracle's OpenMP threads; then the same on one
+    thread for a third of that time. Only the oracle calls are timed."""
     import oracle
-    S = S0.astype(np.float64)
-    pool = [workload.step_inputs(seed, s, Bt, H, P, N, G) for s in range(min(args.pool, 32))]
-    steps, el = 0, 0.0
-    while el < args.cpu_seconds and steps < 100000:
-        tok = pool[steps % len(pool)]
-        t0 = time.perf_counter()
-        oracle.step(S, *tok, A, D)
-        el += time.perf_counter() - t0
-        steps += 1
+    pool = host_pool[:32]
+
+    def timed(budget):
+        S = S0.astype(np.float64)
+        steps, el = 0, 0.0
+        while el < budget and steps < 100000:
+            tok = pool[steps % len(pool)]
+            t0 = time.perf_counter()
+            oracle.step(S, *tok, A, D)
+            el += time.perf_counter() - t0
+            steps += 1
+        return steps, el
+
+    threads = oracle.threads()    # OMP_NUM_THREADS, else every core the process may use
+    steps, el = timed(args.cpu_seconds)
+    oracle.set_threads(1)
+    steps1, el1 = timed(args.cpu_seconds / 3)
+    oracle.set_threads(threads)
     return {"value": round(Bt * steps / el, 1), "unit": "tokens/s/layer",
-            "cores": oracle.threads(), "kind": "oracle",
+            "cores": threads, "kind": "oracle", "cpu_model": _cpu_model(),
+            "one_thread": {"value": round(Bt * steps1 / el1, 1), "steps": steps1, "seconds": round(el1, 1)},
             "sample": f"full batch {Bt} of the same layer, {steps} decode steps over a pool of "
                       f"{len(pool)} token sets, float64 stepwise recurrence (OpenMP over sequence x "
-                      f"head), {el:.1f} s"}
+                      f"head, {threads} threads), {el:.1f} s; then {steps1} steps on 1 thread, {el1:.1f} s"}
 
 
 if __name__ == "__main__":

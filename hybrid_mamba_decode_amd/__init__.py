@@ -37,7 +37,7 @@ EXPORTED = (
     "replayssm_materialize_state", "replayssm_set_mixer", "replayssm_load_conv_state",
     "replayssm_materialize_conv_state", "replayssm_mixer_step", "replayssm_mixer_spec_verify",
     "conventional_step", "conventional_mixer_step", "snapshot_spec_verify", "snapshot_commit",
-    "replayssm_status_string",
+    "snapshot_spec_step", "replayssm_status_string",
 )
 GDN_EXPORTED = (
     "gdnreplay_workspace_bytes", "gdnreplay_workspace_layout", "gdnreplay_create", "gdnreplay_destroy",
@@ -97,6 +97,7 @@ _sig = {
     "conventional_step": (ctypes.c_int, [_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "snapshot_spec_verify": (ctypes.c_int, [_cfgp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "snapshot_commit": (ctypes.c_int, [_cfgp, _vp, _vp, _i32, _vp]),
+    "snapshot_spec_step": (ctypes.c_int, [_cfgp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "replayssm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdnreplay_workspace_bytes": (ctypes.c_size_t, [_gcfgp]),
     "gdnreplay_workspace_layout": (ctypes.c_int, [_gcfgp, ctypes.POINTER(GDNLayout)]),
@@ -280,6 +281,21 @@ def snapshot_commit(cfg: Config, cur, accepted, T, stream=None):
            "snapshot_commit")
 
 
+def snapshot_spec_step(cfg: Config, slots, cur, T, x, B, C, dt, A, D, y, accepted, stream=None):
+    """snapshot_spec_verify then snapshot_commit, as one call of the C ABI."""
+    _check_token_shapes(cfg, x, B, C, dt, (T,))
+    _expect(slots, (cfg.batch, T + 1, cfg.nheads, cfg.headdim, cfg.dstate), "slots")
+    _expect(cur, (cfg.batch,), "cur")
+    _expect(y, (cfg.batch, T, cfg.nheads, cfg.headdim), "y")
+    _expect(A, (cfg.nheads,), "A")
+    _expect(D, (cfg.nheads,), "D")
+    _expect(accepted, (cfg.batch,), "accepted")
+    _check(_lib.snapshot_spec_step(ctypes.byref(cfg), _ptr(slots, name="slots"), _ptr(cur, torch.int32, "cur"),
+                                   int(T), _ptr(x, name="x"), _ptr(B, name="B"), _ptr(C, name="C"),
+                                   _ptr(dt, name="dt"), _ptr(A, name="A"), _ptr(D, name="D"), _ptr(y, name="y"),
+                                   _ptr(accepted, torch.int32, "accepted"), _stream(stream)), "snapshot_spec_step")
+
+
 def replayssm_set_mixer(h, conv_w, conv_b, dt_bias):
     _check(_lib.replayssm_set_mixer(h, _ptr(conv_w, name="conv_w"), _ptr(conv_b, name="conv_b"),
                                     _ptr(dt_bias, name="dt_bias")), "replayssm_set_mixer")
@@ -370,6 +386,7 @@ class ReplaySSM:
             _expect(t, s, n)
         if y is None:
             y = torch.empty_like(x)
+        _expect(y, self._tok()[0], "y")
         replayssm_step(self.handle, x, B, C, dt, y, stream)
         return y
 
@@ -382,6 +399,7 @@ class ReplaySSM:
             _expect(t, s, n)
         if y is None:
             y = torch.empty_like(x)
+        _expect(y, self._tok((T,))[0], "y")
         replayssm_spec_verify(self.handle, T, x, B, C, dt, y, stream)
         return y
 
@@ -402,6 +420,7 @@ class ReplaySSM:
         if out is None:
             out = torch.empty((self.batch, self.nheads, self.headdim, self.dstate),
                               dtype=torch.float32, device=self.workspace.device)
+        _expect(out, (self.batch, self.nheads, self.headdim, self.dstate), "out")
         replayssm_materialize_state(self.handle, out, stream)
         return out
 
@@ -424,6 +443,7 @@ class ReplaySSM:
         if out is None:
             out = torch.empty((self.batch, self.cfg.d_conv - 1, conv_dim(self.cfg)), dtype=torch.float32,
                               device=self.workspace.device)
+        _expect(out, (self.batch, self.cfg.d_conv - 1, conv_dim(self.cfg)), "out")
         replayssm_materialize_conv_state(self.handle, out, stream)
         return out
 
@@ -433,6 +453,7 @@ class ReplaySSM:
         _expect(dt_raw, (self.batch, self.nheads), "dt_raw")
         if o is None:
             o = torch.empty_like(z)
+        _expect(o, (self.batch, self.nheads, self.headdim), "o")
         replayssm_mixer_step(self.handle, xbc, z, dt_raw, o, stream)
         return o
 
@@ -443,6 +464,7 @@ class ReplaySSM:
         _expect(dt_raw, (self.batch, T, self.nheads), "dt_raw")
         if o is None:
             o = torch.empty_like(z)
+        _expect(o, (self.batch, T, self.nheads, self.headdim), "o")
         replayssm_mixer_spec_verify(self.handle, T, xbc, z, dt_raw, o, stream)
         return o
 
@@ -645,6 +667,7 @@ class GDNReplay:
     def materialize_state(self, out=None, stream=None):
         if out is None:
             out = torch.empty(self.batch, self.nheads, self.dv, self.dk, device=self.workspace.device)
+        _expect(out, (self.batch, self.nheads, self.dv, self.dk), "out")
         gdnreplay_materialize_state(self.handle, out, stream)
         return out
 

@@ -30,9 +30,12 @@ struct replayssm_layer {
     int cmin, cmax;
     // Lockstep: after a load, standard steps and unmasked flushes keep every sequence at the same
     // window position, known here as (pos mod L, ckpt_pos mod L, pending count); the step kernel
-    // takes it as arguments. These values repeat with every whole window, so a captured window
-    // replays correctly. A rollback or a masked flush makes sequences diverge: from then on
-    // kernels read the device pointers.
+    // takes it as arguments. With T_max = 1 and no mixer edges these values repeat every L steps,
+    // so a captured run of whole windows replays correctly; with the mixer edges the conv ring
+    // slot pos mod R repeats every R steps, so a captured run must span a multiple of lcm(L, R)
+    // steps. A replay whose arguments no longer match the device pointers (or ring slot) raises
+    // the device flag. A rollback or a masked flush makes sequences diverge: from then on kernels
+    // read the device pointers.
     int uni, pslot, cslot, lcount;
     int upos;         // lockstep: the common pos (the mixer edges' conv ring slot is upos mod R)
     int lockstep_ok;  // replayssm_set_lockstep: the fast path may be used at all
@@ -630,6 +633,21 @@ rssm_status snapshot_commit(const replayssm_config *cfg, int32_t *cur, const int
     if (!ok_ptr4(cur, cfg->batch) || !ok_ptr4(accepted, cfg->batch)) return RSSM_E_INVAL;
     if (cfg->batch == 0) return RSSM_OK;
     return hip_status(launch_snapshot_commit(cur, accepted, T, cfg->batch, (hipStream_t)stream));
+}
+
+rssm_status snapshot_spec_step(const replayssm_config *cfg, float *slots, int32_t *cur, int32_t T,
+                               const float *x, const float *B, const float *C, const float *dt,
+                               const float *A, const float *D, float *y, const int32_t *accepted,
+                               void *stream)
+{
+    // every argument check of both halves before the first launch
+    const rssm_status s = check_shape(cfg);
+    if (s != RSSM_OK) return s;
+    if (T < 1 || T > 8) return RSSM_E_INVAL;
+    if (!ok_ptr4(accepted, cfg->batch)) return RSSM_E_INVAL;
+    const rssm_status v = snapshot_spec_verify(cfg, slots, cur, T, x, B, C, dt, A, D, y, stream);
+    if (v != RSSM_OK) return v;
+    return snapshot_commit(cfg, cur, accepted, T, stream);
 }
 
 const char *replayssm_status_string(rssm_status s)

@@ -695,14 +695,17 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     }
 
     // Pointer update, once per sequence. Lockstep: the work-group owning head 0 checks the device
-    // pointers against the window position (a mismatch means they were corrupted: flag, no
-    // update) and advances them; device mode: the last work-group of the sequence writes them.
+    // pointers against the window position -- and, with the mixer edges, the conv ring slot -- (a
+    // mismatch means they were corrupted, or a captured graph replays arguments that no longer
+    // match: flag, no update) and advances them; device mode: the last work-group of the sequence
+    // writes them.
     auto advance_pointers = [&]() {
         if (uni) {
             if (t.h == 0 && t.split == 0 && tid == 0) {
                 const int dp = Ld.pos[t.b], dc = Ld.ckpt[t.b];
                 const bool ok = dc >= 0 && dp - dc == k - 1 && (int)((unsigned)dp % (unsigned)Ld.L) == pslot &&
-                                (int)((unsigned)dc % (unsigned)Ld.L) == cslot;
+                                (int)((unsigned)dc % (unsigned)Ld.L) == cslot &&
+                                (!MIX || (int)((unsigned)dp % (unsigned)Ld.R) == ls.rslot);
                 if (ok) {
                     Ld.pos[t.b] = dp + 1;
                     Ld.ckpt[t.b] = flush ? dp + 1 : dc;

@@ -23,8 +23,8 @@
  *     spec-decode inputs: q, k [Bt,T,G,Dk]  v [Bt,T,H,Dv]  alpha, beta [Bt,T,H]  o [Bt,T,H,Dv]
  * Supported: Dk in {16, 32, 64, 128, 256}; Dv a multiple of 4, at most 256; 1 <= L <= 64;
  * 1 <= max_draft <= min(L, 8). Reads: through the fp32 checkpoint (read_prec RSSM_READ_FP32), or
- * through a bf16 copy of it (RSSM_READ_BF16; [AT Pulse] "Technical analysis": a high-precision
- * checkpoint drives the recurrence, a low-precision copy serves reads): the copy is each
+ * through a bf16 copy of it (RSSM_READ_BF16; [AT Pulse] "Technical analysis": the recurrence
+ * updates a full-precision checkpoint while replayed reads may use a narrower copy): the copy is each
  * checkpoint value rounded to nearest even, written at load and at every flush; replayed outputs
  * and verify read it, flushes fold into and read the fp32 checkpoint.
  *

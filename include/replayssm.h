@@ -188,7 +188,9 @@ rssm_status replayssm_step(replayssm_t layer, const float *x, const float *B, co
  * workspace ring keyed by position, so a rollback cuts it back with the records (no copy). A
  * mixer handle takes mixer calls: replayssm_step and replayssm_spec_verify return RSSM_E_INVAL.
  * Lockstep graph capture: the step's arguments (window slots and the ring slot pos mod R)
- * repeat every lcm(L, R) steps, so a captured run of such a multiple replays correctly. */
+ * repeat every lcm(L, R) steps, so a captured run of such a multiple replays correctly; a replay
+ * whose ring slot no longer matches pos mod R raises the device flag (RSSM_E_STATE from
+ * replayssm_check), as a mismatched window position does. */
 
 /* Give the edge parameters (device fp32, caller-owned, outliving their use): conv_w [CD,K],
  * conv_b [CD], dt_bias [H]. RSSM_E_INVAL on a handle with d_conv = 0 or a NULL / misaligned
@@ -292,6 +294,17 @@ rssm_status snapshot_spec_verify(const replayssm_config *cfg, float *slots, cons
  * outside [0, T] leave cur unchanged. */
 rssm_status snapshot_commit(const replayssm_config *cfg, int32_t *cur, const int32_t *accepted,
                             int32_t T, void *stream);
+
+/* Baseline for speculative decoding with per-draft snapshots as one call ([Clarity] "What
+ * happened" and claim ledger [13]): snapshot_spec_verify followed by snapshot_commit on the same
+ * stream. slots [Bt,T+1,H,P,N] and cur [Bt] as there; drafts x [Bt,T,H,P], B, C [Bt,T,G,N],
+ * dt [Bt,T,H]; y [Bt,T,H,P] gets all T outputs; accepted [Bt] (device int32, each in [0, T])
+ * then moves cur[b] to (cur[b] + accepted[b]) mod (T+1). Accepted counts outside [0, T] leave
+ * that sequence's cur unchanged. Argument errors are reported before either launch. */
+rssm_status snapshot_spec_step(const replayssm_config *cfg, float *slots, int32_t *cur, int32_t T,
+                               const float *x, const float *B, const float *C, const float *dt,
+                               const float *A, const float *D, float *y, const int32_t *accepted,
+                               void *stream);
 
 /* Static description of a status code. */
 const char *replayssm_status_string(rssm_status status);

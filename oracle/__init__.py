@@ -94,11 +94,15 @@ def lib():
         L.oracle_replay_rollback.restype = _i
         L.oracle_replay_flush.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.oracle_replay_flush.restype = _i
+        L.oracle_replay_set_checkpoint.argtypes = [ctypes.c_void_p, _f32p, ctypes.c_void_p, _i]
+        L.oracle_replay_set_checkpoint.restype = _i
         L.oracle_replay_pointers.argtypes = [ctypes.c_void_p, _i32p, _i32p]
         L.oracle_replay_checkpoint.argtypes = [ctypes.c_void_p, _f64p]
         L.oracle_replay_read_copy.argtypes = [ctypes.c_void_p, _f64p]
         L.oracle_replay_materialize.argtypes = [ctypes.c_void_p, _f64p]
         L.oracle_threads.restype = _i
+        L.oracle_set_threads.argtypes = [_i]
+        L.oracle_set_threads.restype = None
         L.oracle_gdn_step.argtypes = [_i] * 5 + [_f64p] + [_f32p] * 5 + [_f64p]
         L.oracle_gdn_spec_stepwise.argtypes = [_i] * 6 + [_f64p] + [_f32p] * 5 + [_i32p, _f64p]
         L.oracle_gdn_spec_stepwise.restype = _i
@@ -115,6 +119,8 @@ def lib():
         L.oracle_gdn_replay_rollback.restype = _i
         L.oracle_gdn_replay_flush.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.oracle_gdn_replay_flush.restype = _i
+        L.oracle_gdn_replay_set_checkpoint.argtypes = [ctypes.c_void_p, _f32p]
+        L.oracle_gdn_replay_set_checkpoint.restype = _i
         L.oracle_gdn_replay_pointers.argtypes = [ctypes.c_void_p, _i32p, _i32p]
         L.oracle_gdn_replay_checkpoint.argtypes = [ctypes.c_void_p, _f64p]
         L.oracle_gdn_replay_materialize.argtypes = [ctypes.c_void_p, _f64p]
@@ -129,6 +135,11 @@ def _f32(a):
 def threads() -> int:
     """OpenMP threads the oracle uses (OMP_NUM_THREADS or the cores available)."""
     return int(lib().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Use n OpenMP threads from now on (timing the oracle on a given core count)."""
+    lib().oracle_set_threads(int(n))
 
 
 def step(S, x, B, C, dt, A, D):
@@ -209,6 +220,22 @@ class Replay:
             rc = lib().oracle_replay_flush(self._h, m.ctypes.data_as(ctypes.c_void_p))
         if rc != 0:
             raise RuntimeError("oracle replay: flush rejected by the state machine")
+
+    def set_checkpoint(self, S, rows=None):
+        """Continue from fp32 checkpoint values (taken as they are; records and pointers stay),
+        with the read copy re-encoded from them: S [Bt,H,P,N] for every sequence, or S
+        [len(rows),H,P,N] for the sequences listed in rows."""
+        S = _f32(S)
+        n = self.Bt if rows is None else len(rows)
+        if S.shape != (n, self.H, self.P, self.N):
+            raise ValueError("checkpoint shape mismatch")
+        if rows is None:
+            rc = lib().oracle_replay_set_checkpoint(self._h, S, None, n)
+        else:
+            idx = np.ascontiguousarray(rows, dtype=np.int32)
+            rc = lib().oracle_replay_set_checkpoint(self._h, S, idx.ctypes.data_as(ctypes.c_void_p), n)
+        if rc != 0:
+            raise RuntimeError("oracle replay: set_checkpoint while a verify is pending, or a bad row")
 
     def pointers(self):
         pos = np.empty(self.Bt, np.int32)
@@ -377,6 +404,15 @@ class GDNReplay:
         if rc != 0:
             raise RuntimeError("oracle GDN replay: flush rejected by the state machine")
 
+    def set_checkpoint(self, S):
+        """Continue from the fp32 checkpoint S [Bt,H,Dv,Dk] (taken as it is; records and pointers
+        stay), with the read copy re-encoded from it."""
+        S = _f32(S)
+        if S.shape != (self.Bt, self.H, self.Dv, self.Dk):
+            raise ValueError("checkpoint shape mismatch")
+        if lib().oracle_gdn_replay_set_checkpoint(self._h, S) != 0:
+            raise RuntimeError("oracle GDN replay: set_checkpoint while a verify is pending")
+
     def pointers(self):
         pos = np.empty(self.Bt, np.int32)
         ck = np.empty(self.Bt, np.int32)
@@ -474,9 +510,12 @@ class MixerStepwise:
     def edge(self, hist, xbc, dt_raw):
         return mixer_edge(hist, xbc, dt_raw, self.w, self.b, self.bias, self.H, self.P, self.G, self.N)
 
-    def step(self, xbc, z, dt_raw):
+    def step(self, xbc, z, dt_raw, with_y=False):
+        """The gated output o; with with_y, (y, o): the SSM output before the gate as well."""
         x, B, C, dt = self.edge(self.hist, xbc, dt_raw)
-        return mixer_gate(step(self.S, x, B, C, dt, self.A, self.D), z)
+        y = step(self.S, x, B, C, dt, self.A, self.D)
+        o = mixer_gate(y, z)
+        return (y, o) if with_y else o
 
     def spec(self, T, xbc, z, dt_raw, accepted):
         """All T draft outputs (xbc [Bt,T,CD], z [Bt,T,H,P], dt_raw [Bt,T,H]); the state and the
@@ -529,6 +568,9 @@ class MixerReplay:
                            self.w, self.b, self.bias, self.H, self.P, self.G, self.N)
                 self.hist[b:b + 1] = one
         self._drafts = None
+
+    def set_checkpoint(self, S, rows=None):
+        self.rep.set_checkpoint(S, rows)
 
     def pointers(self):
         return self.rep.pointers()

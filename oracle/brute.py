@@ -8,7 +8,7 @@ Pure Python loops, no numpy arithmetic, so these serve as pins for the float64 o
              + sum_{j<=t} dt_j * exp(A_h * sum_{j<i<=t} dt_i) * (B_j . C_t) * x_j[p]
              + D_h * x_t[p]
   This is what unrolling the update-then-read recurrence over a window gives ([AT Pulse]
-  "Technical analysis": the recurrence is unrolled over a window; [Clarity] claim ledger [17]).
+  "Technical analysis" and [Clarity] claim ledger [17]: the recurrence expanded across a window).
   Sums use math.fsum (exactly rounded), exponentials math.exp.
 * ``exact_stepwise_A0``: the stepwise recurrence in exact rational arithmetic for A = 0, where
   the decay is exactly 1 and every value is a small dyadic rational.

@@ -415,12 +415,11 @@ void oracle_encode_f16(const float *in, uint16_t *out, size_t n, int stochastic,
 /* ------------------------------------------------------------------------------------------- */
 /* O3 + O4: the replay form with its pointer and flush state machine.                           */
 /*                                                                                             */
-/* [AT Pulse] "Technical analysis": the recurrence is unrolled over a window of L tokens; most  */
-/* steps form the output from the checkpoint plus the buffered records and store only the new  */
-/* record; a flush every L steps folds the buffer into the checkpoint; rolling back rejected    */
-/* drafts is a move of the buffer pointer. [Clarity] claim ledger [17], [18]: over a window the */
-/* state is a checkpoint plus a small buffer of recent input records; non-flush steps append    */
-/* and compute the output without storing a state.                                             */
+/* [AT Pulse] "Technical analysis" and [Clarity] claim ledger [17], [18]: the state of a       */
+/* sequence is kept as a checkpoint together with the input records of the tokens since it;    */
+/* an ordinary step derives its output from both by expanding the recurrence across those      */
+/* records and writes nothing but its own record; once L records have gathered they are        */
+/* merged into the checkpoint; discarding rejected drafts only moves the buffer pointer.       */
 /*                                                                                             */
 /* Unrolling O1 from the checkpoint S_c (all tokens before c folded) over records c..t gives,   */
 /* per (b, h), with g = g(h):                                                                   */
@@ -751,6 +750,29 @@ int oracle_replay_rollback(oracle_replay *r, const int *accepted)
     return 0;
 }
 
+/* Replace checkpoints by given fp32 values, held as they are (no rounding to the master       */
+/* precision), and re-encode the read copy from them; records and pointers stay. rows == NULL:  */
+/* S is [Bt,H,P,N] and every sequence is set; else S is [nrows,H,P,N] and its row i sets       */
+/* sequence rows[i]. A test uses it to continue the replay-form model from the GPU's own        */
+/* checkpoint after a flush: the model then reads exactly the copy the layer must hold (the     */
+/* master encoded by R6/R7), so later replayed outputs can be compared at fp32 rounding.        */
+/* Returns 0, or -1 while a verify is pending or for a row index out of range.                  */
+int oracle_replay_set_checkpoint(oracle_replay *r, const float *S, const int *rows, int nrows)
+{
+    if (r->pending_T) return -1;
+    if (!rows) nrows = r->Bt;
+    for (int i = 0; i < nrows; ++i)
+        if (rows && (rows[i] < 0 || rows[i] >= r->Bt)) return -1;
+    const size_t seq = (size_t)r->H * r->P * r->N;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < nrows; ++i) {
+        const int b = rows ? rows[i] : i;
+        for (size_t e = 0; e < seq; ++e) r->ckpt[(size_t)b * seq + e] = (double)S[(size_t)i * seq + e];
+        refresh_copy(r, b);
+    }
+    return 0;
+}
+
 /* Explicit flush of the selected sequences (all when mask is NULL). */
 int oracle_replay_flush(oracle_replay *r, const int *seq_mask)
 {
@@ -791,5 +813,15 @@ int oracle_threads(void)
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Threads for later parallel regions (n >= 1); for timing the oracle on a given core count. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }

@@ -21,8 +21,9 @@
  *     z <- q_t;  for j = t, ..., 0:  c_j = beta_j (k_j . z);  z <- alpha_j (z - c_j k_j).
  * A flush folds the records into the checkpoint by applying them in order (the recurrence
  * itself); pointer and flush rules are those of oracle.c (readings R2, R5, R6, R10).
- * Reading G4: as for Mamba-2 ([AT Pulse] "Technical analysis": a high-precision checkpoint drives
- * the recurrence, a low-precision copy serves reads), the replay's checkpoint product S_c z may
+ * Reading G4: as for Mamba-2 ([AT Pulse] "Technical analysis": the recurrence is folded into a
+ * full-precision checkpoint while replayed reads may use a narrower copy of it), the replay's
+ * checkpoint product S_c z may
  * read a bf16 copy of the checkpoint, written at load and at every flush from the checkpoint
  * rounded to fp32; flushes fold into the checkpoint itself and read their output from it.
  *
@@ -324,6 +325,20 @@ int oracle_gdn_replay_flush(oracle_gdn *r, const int *seq_mask)
     if (r->pending_T) return -1;
     for (int b = 0; b < r->Bt; ++b)
         if (!seq_mask || seq_mask[b]) gdn_flush_seq(r, b);
+    return 0;
+}
+
+/* Replace every sequence's checkpoint by the fp32 values S [Bt,H,Dv,Dk] as they are, with the */
+/* read copy re-encoded from them; records and pointers stay (a test continues the model from   */
+/* the GPU's own checkpoint after a flush). Returns 0, or -1 while a verify is pending.         */
+int oracle_gdn_replay_set_checkpoint(oracle_gdn *r, const float *S)
+{
+    if (r->pending_T) return -1;
+    const size_t n = (size_t)r->Bt * r->H * r->Dv * r->Dk;
+#pragma omp parallel for schedule(static)
+    for (size_t i = 0; i < n; ++i) r->ckpt[i] = (double)S[i];
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < r->Bt; ++b) gdn_refresh_copy(r, b);
     return 0;
 }
 

@@ -1,8 +1,5 @@
 """Shared helpers of the GPU parity tests: device transfer, the normwise error metric, and a
 helper that runs the HIP layer and the float64 oracle side by side on the same seeded inputs."""
-import json
-import os
-
 import numpy as np
 import torch
 
@@ -13,28 +10,26 @@ PREC_CODE = {"fp32": oracle.READ_FP32, "bf16": oracle.READ_BF16, "fp8": oracle.R
              "mxfp4": oracle.READ_MXFP4}
 MASTER_CODE = {"fp32": oracle.MASTER_FP32, "fp16": oracle.MASTER_FP16, "fp16_sr": oracle.MASTER_FP16_SR}
 
-_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "mxfp4_codes.json")
-with open(_GOLDEN) as _f:
-    _E2M1 = np.array(json.load(_f)["e2m1_values"], np.float64)   # hand-derived code table
-
-
-def decode_copy(lay, prec, sample):
-    """Values of the layer's read copy for the sampled sequences, float64, decoded without the
-    oracle: bf16 by bit shift, fp8 by PyTorch's float8_e4m3fn, MXFP4 by the hand-derived E2M1
-    table times 2^(scale code - 127)."""
+def assert_copy_encodes(lay, prec, m, sample, what=""):
+    """The layer's read copy of the sampled sequences is, bit for bit, the oracle's encoder (O7)
+    applied to the fp32 checkpoint values m [len(sample),H,P,N] -- normally the GPU's own master
+    right after a flush; fp8 per-head scales and MXFP4 scale codes too."""
     idx = torch.as_tensor(np.asarray(sample), device="cuda")
+    got = host(lay.read_copy()[idx])
+    m = np.ascontiguousarray(m, np.float32)
     if prec == "bf16":
-        c = host(lay.read_copy()[idx]).view(np.uint16).astype(np.uint32) << 16
-        return c.view(np.float32).astype(np.float64)
-    if prec == "fp8":
-        v = host(lay.read_copy()[idx].view(torch.float8_e4m3fn).float()).astype(np.float64)
-        return v * host(lay.scales()[idx]).astype(np.float64)[:, :, None, None]
-    if prec == "mxfp4":
-        b = host(lay.read_copy()[idx])
-        codes = np.stack([b & 15, b >> 4], axis=-1).reshape(b.shape[:-1] + (b.shape[-1] * 2,))
-        sc = host(lay.scales()[idx]).astype(np.int64) - 127
-        return np.ldexp(_E2M1[codes], np.repeat(sc, 32, axis=-1))
-    raise ValueError(prec)
+        ok = np.array_equal(got, oracle.bf16_encode(m).view(np.int16))
+        assert ok, f"{what}: bf16 copy differs from the encoded master"
+    elif prec == "fp8":
+        codes, scales = oracle.e4m3_encode_tiles(m, m.shape[2] * m.shape[3])
+        assert np.array_equal(host(lay.scales()[idx]).reshape(-1), scales), f"{what}: fp8 scales differ"
+        assert np.array_equal(got.reshape(-1), codes), f"{what}: fp8 codes differ from the encoded master"
+    elif prec == "mxfp4":
+        codes, scales = oracle.mxfp4_encode(m)
+        assert np.array_equal(host(lay.scales()[idx]), scales), f"{what}: MXFP4 scale codes differ"
+        assert np.array_equal(got, codes), f"{what}: MXFP4 codes differ from the encoded master"
+    else:
+        raise ValueError(prec)
 
 
 def dev(a, dtype=None):

@@ -203,6 +203,71 @@ def test_baselines_validate():
     assert L.snapshot_spec_verify(ctypes.byref(c1), None, FAKE, 4, *([FAKE] * 7), None) == rs.RSSM_E_INVAL
 
 
+def test_snapshot_spec_step_validates_before_launch():
+    """The one-call snapshot baseline checks every argument of both halves before any launch."""
+    L = rs._lib
+    c, c1 = cfg(), cfg(batch=1)
+    args = [FAKE] * 7                                  # x, B, C, dt, A, D, y
+    assert L.snapshot_spec_step(ctypes.byref(c), FAKE, FAKE, 4, *args, FAKE, None) == rs.RSSM_OK   # batch 0
+    assert L.snapshot_spec_step(ctypes.byref(c), FAKE, FAKE, 0, *args, FAKE, None) == rs.RSSM_E_INVAL
+    assert L.snapshot_spec_step(ctypes.byref(c), FAKE, FAKE, 9, *args, FAKE, None) == rs.RSSM_E_INVAL
+    assert L.snapshot_spec_step(ctypes.byref(c1), FAKE, FAKE, 4, *args, None, None) == rs.RSSM_E_INVAL
+    assert L.snapshot_spec_step(ctypes.byref(c1), FAKE, FAKE, 4, *args, FAKE + 2, None) == rs.RSSM_E_INVAL
+    assert L.snapshot_spec_step(ctypes.byref(c1), FAKE, None, 4, *args, FAKE, None) == rs.RSSM_E_INVAL
+    assert L.snapshot_spec_step(ctypes.byref(c1), FAKE + 4, FAKE, 4, *args, FAKE, None) == rs.RSSM_E_INVAL
+    assert L.snapshot_spec_step(ctypes.byref(cfg(dstate=24)), FAKE, FAKE, 4, *args, FAKE, None) == \
+        rs.RSSM_E_UNSUPPORTED
+    assert L.snapshot_spec_step(None, FAKE, FAKE, 4, *args, FAKE, None) == rs.RSSM_E_INVAL
+
+
+def _shape_only(cls, **attrs):
+    """An instance carrying shapes only (no handle, no workspace): enough for the binding's
+    argument checks, which all run before the first library call."""
+    obj = object.__new__(cls)
+    obj.handle = None
+    for k, v in attrs.items():
+        setattr(obj, k, v)
+    return obj
+
+
+def test_binding_rejects_wrong_output_shapes():
+    """Caller-supplied outputs of the wrong shape raise ValueError before any library call (an
+    undersized buffer would otherwise let a kernel write past its end)."""
+    import torch
+    Bt, H, P, N, G, T, K = 2, 4, 16, 32, 2, 3, 4
+    lay = _shape_only(rs.ReplaySSM, batch=Bt, nheads=H, headdim=P, dstate=N, ngroups=G,
+                      cfg=rs.make_config(Bt, H, P, N, G, max_draft=T, d_conv=K))
+    e = torch.empty
+    tok = (e(Bt, H, P), e(Bt, G, N), e(Bt, G, N), e(Bt, H))
+    with pytest.raises(ValueError, match="y has shape"):
+        lay.step(*tok, y=e(Bt, H, P - 4))
+    drafts = (e(Bt, T, H, P), e(Bt, T, G, N), e(Bt, T, G, N), e(Bt, T, H))
+    with pytest.raises(ValueError, match="y has shape"):
+        lay.spec_verify(*drafts, y=e(Bt, H, P))
+    with pytest.raises(ValueError, match="out has shape"):
+        lay.materialize_state(out=e(Bt, H, P, N // 2))
+    CD = rs.conv_dim(lay.cfg)
+    with pytest.raises(ValueError, match="o has shape"):
+        lay.mixer_step(e(Bt, CD), e(Bt, H, P), e(Bt, H), o=e(Bt, H, P - 1))
+    with pytest.raises(ValueError, match="o has shape"):
+        lay.mixer_spec_verify(e(Bt, T, CD), e(Bt, T, H, P), e(Bt, T, H), o=e(Bt, T, H, P + 1))
+    with pytest.raises(ValueError, match="out has shape"):
+        lay.materialize_conv_state(out=e(Bt, K, CD))
+    gl = _shape_only(rs.GDNReplay, batch=Bt, nheads=H, nkheads=G, dv=P, dk=N,
+                     cfg=rs.make_gdn_config(Bt, H, G, P, N, max_draft=T))
+    with pytest.raises(ValueError, match="out has shape"):
+        gl.materialize_state(out=e(Bt, H, P, N - 1))
+    q = e(Bt, G, N)
+    with pytest.raises(ValueError, match="o has shape"):
+        gl.step(q, q, e(Bt, H, P), e(Bt, H), e(Bt, H), o=e(Bt, H, P // 2))
+    slots, cur = e(Bt, T + 1, H, P, N), e(Bt, dtype=torch.int32)
+    A = e(H)
+    with pytest.raises(ValueError, match="y has shape"):
+        rs.snapshot_spec_step(lay.cfg, slots, cur, T, *drafts, A, A, e(Bt, T, H, P - 4), cur)
+    with pytest.raises(ValueError, match="accepted has shape"):
+        rs.snapshot_spec_step(lay.cfg, slots, cur, T, *drafts, A, A, e(Bt, T, H, P), e(Bt + 1, dtype=torch.int32))
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(rs.replayssm_status_string(s), str) and rs.replayssm_status_string(s)

@@ -228,3 +228,25 @@ def test_bf16_read_copy_model():
             assert np.array_equal(cp.read_copy(), want), t
         assert _rel(o, o_true) <= 2e-2, t
     assert _rel(cp.materialize(), S) <= 1e-12
+
+
+def test_set_checkpoint_restarts_the_model():
+    """Continuing the GDN replay model from a given fp32 checkpoint after a flush equals a fresh
+    model loaded with it (bf16 copy re-encoded from the given values): outputs equal bit for bit;
+    and torch's bfloat16 of the given checkpoint is the new copy."""
+    import torch
+    Bt, H, G, Dv, Dk, L = 2, 4, 2, 16, 32, 4
+    seed = 31
+    S0 = workload.gdn_initial_state(seed, Bt, H, Dv, Dk)
+    a = oracle.GDNReplay(S0, G, L, 1, oracle.READ_BF16)
+    for t in range(L):
+        a.step(*_inputs(seed, Bt, H, G, Dv, Dk, t))
+    S1 = a.checkpoint().astype(np.float32)
+    S1[0, 1, 2, 3] = np.float32(-2.5)
+    a.set_checkpoint(S1)
+    want = torch.from_numpy(S1).bfloat16().float().numpy().astype(np.float64)
+    assert np.array_equal(a.read_copy(), want)
+    b = oracle.GDNReplay(S1, G, L, 1, oracle.READ_BF16)
+    for t in range(L, 2 * L - 1):
+        ins = _inputs(seed, Bt, H, G, Dv, Dk, t)
+        assert np.array_equal(a.step(*ins), b.step(*ins)), t

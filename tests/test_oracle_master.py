@@ -168,8 +168,8 @@ def test_stochastic_rounding_avoids_stagnation():
 
 @pytest.mark.parametrize("master", [oracle.MASTER_FP16, oracle.MASTER_FP16_SR])
 def test_rounding_at_flushes_only_compounds_less(master):
-    """[Clarity] "Why it matters": a state written on fewer steps gives its rounding error fewer
-    chances to re-enter the recurrence. With the same fp16 state, the replay form at L = 1 rounds
+    """[Clarity] "Why it matters": when the state is stored less often, its rounding is fed back
+    into the recurrence less often. With the same fp16 state, the replay form at L = 1 rounds
     on every step (the conventional step) and at L = 16 on every 16th: over 128 steps its rms
     state and output errors against float64 must be well below (here < 0.6x; measured 0.25-0.39x
     over seeds) those of rounding every step."""

@@ -247,3 +247,74 @@ def test_dual_precision_model(read_prec):
                 assert not np.array_equal(rep.read_copy(), copy0)
         if t == L - 2:
             assert np.array_equal(rep.read_copy(), copy0)
+
+
+@pytest.mark.parametrize("read_prec", [oracle.READ_FP32, oracle.READ_BF16, oracle.READ_FP8, oracle.READ_MXFP4])
+def test_set_checkpoint_restarts_the_model(read_prec):
+    """Continuing the replay model from a given fp32 checkpoint after a flush is the same as a
+    fresh model loaded with that state: outputs and decoded read copies equal bit for bit (the
+    read copy is re-encoded from the given values, the records and pointers are kept)."""
+    Bt, H, P, N, G, L = 2, 4, 16, 32, 2, 4
+    seed = 404
+    S0, A, D = _setup(seed, Bt, H, P, N, G)
+    a = oracle.Replay(S0, A, D, G, L, 1, read_prec)
+    for t in range(L):
+        a.step(*workload.step_inputs(seed, t, Bt, H, P, N, G))
+    assert np.all(a.pointers()[1] == L)
+    # a checkpoint that is not the model's own: the fold rounded to fp32, one value nudged
+    S1 = a.checkpoint().astype(np.float32)
+    S1[1, 2, 3, 4] = np.float32(S1[1, 2, 3, 4] * 1.5 + 0.25)
+    a.set_checkpoint(S1)
+    assert np.array_equal(a.checkpoint(), S1.astype(np.float64))
+    b = oracle.Replay(S1, A, D, G, L, 1, read_prec)
+    assert np.array_equal(a.read_copy(), b.read_copy())
+    for t in range(L, 2 * L - 1):
+        ins = workload.step_inputs(seed, t, Bt, H, P, N, G)
+        assert np.array_equal(a.step(*ins), b.step(*ins)), f"step {t}"
+
+
+def test_set_checkpoint_changes_outputs_by_the_decayed_term():
+    """Closed form: after a flush (empty window), replacing one checkpoint value S[b,h,p,n] by
+    S + d changes the next replayed output only at (b, h, p), by exp(A_h dt_t) * d * C_t[b,g,n];
+    every other output is unchanged."""
+    Bt, H, P, N, G, L = 2, 4, 8, 16, 2, 3
+    seed = 405
+    S0, A, D = _setup(seed, Bt, H, P, N, G)
+    ref = oracle.Replay(S0, A, D, G, L, 1)
+    mod = oracle.Replay(S0, A, D, G, L, 1)
+    for t in range(L):
+        ins = workload.step_inputs(seed, t, Bt, H, P, N, G)
+        ref.step(*ins)
+        mod.step(*ins)
+    S1 = ref.checkpoint().astype(np.float32)
+    ref.set_checkpoint(S1)
+    b, h, p, n, d = 1, 3, 5, 7, 0.75
+    S2 = S1.copy()
+    S2[b, h, p, n] += np.float32(d)
+    d = float(S2[b, h, p, n]) - float(S1[b, h, p, n])
+    mod.set_checkpoint(S2)
+    x, B, C, dt = workload.step_inputs(seed, L, Bt, H, P, N, G)
+    y0, y1 = ref.step(x, B, C, dt), mod.step(x, B, C, dt)
+    g = h // (H // G)
+    expect = np.exp(float(A[h]) * float(dt[b, h])) * d * float(C[b, g, n])
+    diff = y1 - y0
+    assert abs(diff[b, h, p] - expect) <= 1e-12 * max(1.0, abs(expect))
+    diff[b, h, p] = 0.0
+    assert np.all(diff == 0.0)
+
+
+def test_set_checkpoint_of_selected_rows():
+    """Setting the checkpoints of listed sequences leaves the others exactly as they were."""
+    Bt, H, P, N, G, L = 3, 2, 8, 32, 1, 4
+    seed = 406
+    S0, A, D = _setup(seed, Bt, H, P, N, G)
+    a = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP8)
+    before_ck, before_copy = a.checkpoint(), a.read_copy()
+    S1 = (S0[[2, 0]] * np.float32(0.5)).astype(np.float32)
+    a.set_checkpoint(S1, [2, 0])
+    ck, cp = a.checkpoint(), a.read_copy()
+    assert np.array_equal(ck[[2, 0]], S1.astype(np.float64))
+    assert np.array_equal(ck[1], before_ck[1]) and np.array_equal(cp[1], before_copy[1])
+    assert np.array_equal(cp[[2, 0]], oracle.Replay(S1, A, D, G, L, 1, oracle.READ_FP8).read_copy())
+    with pytest.raises(RuntimeError):
+        a.set_checkpoint(S1, [2, 3])
