@@ -513,6 +513,7 @@ class MixerStepwise:
     def step(self, xbc, z, dt_raw, with_y=False):
         """The gated output o; with with_y, (y, o): the SSM output before the gate as well."""
         x, B, C, dt = self.edge(self.hist, xbc, dt_raw)
+        self.last_edge = (x, B, C, dt)   # this token's SSM inputs, as the edge formed them
         y = step(self.S, x, B, C, dt, self.A, self.D)
         o = mixer_gate(y, z)
         return (y, o) if with_y else o
