@@ -444,14 +444,14 @@ def philox4x32_10(ctr, key):
     return out
 
 
-def f16_encode(a, r24=None):
-    """fp16 codes (uint16) of fp32 values: nearest even, or stochastic with 24-bit randoms r24."""
+def f16_encode(a, r16=None):
+    """fp16 codes (uint16) of fp32 values: nearest even, or stochastic with 16-bit randoms r16."""
     a = _f32(a)
     out = np.empty(a.shape, np.uint16)
-    if r24 is None:
+    if r16 is None:
         lib().oracle_encode_f16(a.reshape(-1), out.reshape(-1), a.size, 0, None)
     else:
-        r = np.ascontiguousarray(r24, dtype=np.uint32).reshape(-1)
+        r = np.ascontiguousarray(r16, dtype=np.uint32).reshape(-1)
         assert r.size == a.size
         lib().oracle_encode_f16(a.reshape(-1), out.reshape(-1), a.size, 1, r.ctypes.data_as(ctypes.c_void_p))
     return out

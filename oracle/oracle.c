@@ -47,12 +47,15 @@
  *       fold is computed at full precision from the fp16 checkpoint and the records, rounded to
  *       fp32, clamped to +-65504 and rounded to fp16 either to nearest even or stochastically:
  *       with q the fp16 value toward zero and ulp the fp16 spacing above it, the magnitude rounds
- *       up iff r < (|v| - |q|) / ulp * 2^24, r the top 24 bits of a Philox4x32-10 word (Salmon et
- *       al., SC'11) with counter (element / 4, sequence, new ckpt_pos, 0), key (seed, 0), word
- *       element % 4 (elements numbered h*P*N + p*N + n within the sequence). That threshold is
- *       exact in fp32; the rounding is unbiased over r (to within 2^-24 of a spacing for |v| below
- *       2^-25, where the threshold is not an integer). Reads and the read copy then come from
- *       the fp16 checkpoint; a flush step's output is read from the rounded checkpoint.
+ *       up iff r < (|v| - |q|) / ulp * 2^16, r a 16-bit random integer: Philox4x32-10 (Salmon et
+ *       al., SC'11) with counter (element / 8, sequence, new ckpt_pos, 0) and key (seed, 0) gives
+ *       eight 16-bit fields, element e taking bits 16*(e % 2) .. +15 of word (e % 8) / 2 (elements
+ *       numbered h*P*N + p*N + n within the sequence). The threshold is exact in fp32. In fp16's
+ *       normal range an fp32 magnitude has 13 bits below the fp16 spacing, so the threshold is a
+ *       multiple of 8 and the rounding is exactly unbiased over r -- the same distribution as any
+ *       wider random integer gives; below 2^-17 (deep in fp16's subnormal range) fp32 keeps finer
+ *       bits and the bias is below 2^-16 of a spacing. Reads and the read copy then come from the
+ *       fp16 checkpoint; a flush step's output is read from the rounded checkpoint.
  *
  * Layouts (row-major, last index fastest): x [Bt,H,P]; B, C [Bt,G,N]; dt [Bt,H]; A, D [H];
  * state [Bt,H,P,N]; y [Bt,H,P]. Spec-decode inputs carry the draft index after the batch index:
@@ -392,8 +395,8 @@ uint16_t oracle_f16_encode_rne(float v)
     return (uint16_t)(f16_code_of(out) | (sign << 15));
 }
 
-/* Round an fp32 value to fp16 stochastically with the 24-bit random integer r24 (reading R8). */
-uint16_t oracle_f16_encode_sr(float v, uint32_t r24)
+/* Round an fp32 value to fp16 stochastically with the 16-bit random integer r16 (reading R8). */
+uint16_t oracle_f16_encode_sr(float v, uint32_t r16)
 {
     double t = (double)v, mag = fabs(t);
     int sign = signbit(t) ? 1 : 0;
@@ -401,15 +404,15 @@ uint16_t oracle_f16_encode_sr(float v, uint32_t r24)
     double q = f16_toward_zero(mag);
     double out = q;
     if (mag > q) {
-        double threshold = (mag - q) / f16_spacing(q) * 16777216.0; /* exact */
-        if ((double)r24 < threshold) out = q + f16_spacing(q);
+        double threshold = (mag - q) / f16_spacing(q) * 65536.0; /* exact */
+        if ((double)r16 < threshold) out = q + f16_spacing(q);
     }
     return (uint16_t)(f16_code_of(out) | (sign << 15));
 }
 
-void oracle_encode_f16(const float *in, uint16_t *out, size_t n, int stochastic, const uint32_t *r24)
+void oracle_encode_f16(const float *in, uint16_t *out, size_t n, int stochastic, const uint32_t *r16)
 {
-    for (size_t i = 0; i < n; ++i) out[i] = stochastic ? oracle_f16_encode_sr(in[i], r24[i]) : oracle_f16_encode_rne(in[i]);
+    for (size_t i = 0; i < n; ++i) out[i] = stochastic ? oracle_f16_encode_sr(in[i], r16[i]) : oracle_f16_encode_rne(in[i]);
 }
 
 /* ------------------------------------------------------------------------------------------- */
@@ -477,17 +480,18 @@ static void round_master(oracle_replay *r, int b, int ck, int stochastic)
 {
     const size_t n = (size_t)r->H * r->P * r->N;
     double *m = r->ckpt + (size_t)b * n;
-    for (size_t e = 0; e < n; e += 4) {
+    for (size_t e = 0; e < n; e += 8) {
         uint32_t words[4] = {0, 0, 0, 0};
         if (r->master_prec == 2 && stochastic) {
-            const uint32_t ctr[4] = {(uint32_t)(e / 4), (uint32_t)r->seq_id[b], (uint32_t)ck, 0u};
+            const uint32_t ctr[4] = {(uint32_t)(e / 8), (uint32_t)r->seq_id[b], (uint32_t)ck, 0u};
             const uint32_t key[2] = {r->seed, 0u};
             oracle_philox4x32_10(ctr, key, words);
         }
-        for (int w = 0; w < 4 && e + w < n; ++w) {
+        for (int w = 0; w < 8 && e + w < n; ++w) {
             const float v = (float)m[e + w];
+            const uint32_t r16 = (words[w / 2] >> (16 * (w % 2))) & 0xFFFFu;
             if (r->master_prec == 0) m[e + w] = (double)v;
-            else if (r->master_prec == 2 && stochastic) m[e + w] = (double)oracle_f16_decode(oracle_f16_encode_sr(v, words[w] >> 8));
+            else if (r->master_prec == 2 && stochastic) m[e + w] = (double)oracle_f16_decode(oracle_f16_encode_sr(v, r16));
             else m[e + w] = (double)oracle_f16_decode(oracle_f16_encode_rne(v));
         }
     }

@@ -53,7 +53,7 @@ def test_f16_decode_vs_numpy():
 
 
 def _threshold(v):
-    """Round-up threshold of stochastic rounding: (|v| - q) / ulp * 2^24 as an exact Fraction,
+    """Round-up threshold of stochastic rounding: (|v| - q) / ulp * 2^16 as an exact Fraction,
     with q = the fp16 magnitude toward zero (numpy) and ulp the gap to the next one."""
     a = abs(float(np.float32(v)))
     q16 = np.float16(a)
@@ -61,34 +61,41 @@ def _threshold(v):
         q16 = np.nextafter(q16, np.float16(0))
     nxt = np.nextafter(q16, np.float16(np.inf))
     q, up = Fraction(float(q16)), Fraction(float(nxt))
-    return (Fraction(a) - q) / (up - q) * 2 ** 24, float(q16), float(nxt)
+    return (Fraction(a) - q) / (up - q) * 2 ** 16, float(q16), float(nxt)
 
 
 def test_stochastic_rounding_threshold_and_unbiasedness():
-    """The magnitude rounds up iff r24 < T (T exact, an integer except deep in fp16's subnormal
-    range, |v| < 2^-25, where fp32 keeps finer bits than the fp16 spacing). Hence the mean over all
-    2^24 values of r24 is within 2^-24 of a spacing of v, and exactly v whenever T is an integer.
-    Representable values never change."""
+    """The magnitude rounds up iff r16 < T (T exact). In fp16's normal range an fp32 value has
+    13 bits below the fp16 spacing, so T is a multiple of 8 and the mean over all 2^16 values of
+    r16 is exactly v -- the same distribution a wider random integer would give. T is an integer
+    except deep in the subnormal range (|v| < 2^-17, where fp32 keeps finer bits than 2^-16 of
+    the spacing 2^-24); there the mean is within 2^-16 of a spacing of v. Representable values
+    never change."""
     rng = np.random.default_rng(3)
     v = (rng.standard_normal(400) * np.exp2(rng.integers(-30, 14, 400))).astype(np.float32)
     v = np.concatenate([v, np.float16(rng.standard_normal(50)).astype(np.float32)])
-    n_int = 0
+    n_int = n_normal = 0
     for x in v:
         T, q, nxt = _threshold(x)
-        assert 0 <= T < 2 ** 24
-        c = -(-T.numerator // T.denominator)              # ceil(T): the number of r24 that round up
+        assert 0 <= T < 2 ** 16
+        c = -(-T.numerator // T.denominator)              # ceil(T): the number of r16 that round up
         sign = -1.0 if x < 0 else 1.0
-        rs = np.array(sorted({0, max(c - 1, 0), min(c, 2 ** 24 - 1), min(c + 1, 2 ** 24 - 1), 2 ** 24 - 1}), np.uint32)
+        rs = np.array(sorted({0, max(c - 1, 0), min(c, 2 ** 16 - 1), min(c + 1, 2 ** 16 - 1), 2 ** 16 - 1}), np.uint32)
         got = oracle.f16_decode(oracle.f16_encode(np.full(len(rs), x, np.float32), rs)).astype(np.float64)
         want = [sign * (nxt if Fraction(int(r)) < T else q) for r in rs]
         assert np.array_equal(got, np.array(want)), (x, T)
-        mean = Fraction(c) * Fraction(nxt) + Fraction(2 ** 24 - c) * Fraction(q)   # times 2^24
-        err = abs(mean - Fraction(abs(float(x))) * 2 ** 24)
+        mean = Fraction(c) * Fraction(nxt) + Fraction(2 ** 16 - c) * Fraction(q)   # times 2^16
+        err = abs(mean - Fraction(abs(float(x))) * 2 ** 16)
         assert err <= Fraction(nxt) - Fraction(q)
+        if abs(float(x)) >= 2.0 ** -14:
+            assert T.denominator == 1 and T.numerator % 8 == 0, (x, T)
+            n_normal += 1
+        if abs(float(x)) >= 2.0 ** -17:
+            assert T.denominator == 1, (x, T)
         if T.denominator == 1:
             assert err == 0
             n_int += 1
-    assert n_int > 300
+    assert n_int > 300 and n_normal > 200
 
 
 def test_fp16_master_dual_model():
@@ -117,11 +124,13 @@ def test_fp16_master_dual_model():
     v32 = ref.checkpoint().astype(np.float32)           # fp32 fold of the same records
     assert np.array_equal(rne.checkpoint(), v32.astype(np.float16).astype(np.float64))
     flat = v32.reshape(Bt, -1)
-    words = np.empty_like(flat, dtype=np.uint32)
+    r16 = np.empty_like(flat, dtype=np.uint32)
     for b in range(Bt):
-        for g in range(flat.shape[1] // 4):
-            words[b, 4 * g:4 * g + 4] = oracle.philox4x32_10([g, b, L, 0], [77, 0])
-    want = oracle.f16_decode(oracle.f16_encode(flat, words >> 8)).astype(np.float64).reshape(S0.shape)
+        for g in range(flat.shape[1] // 8):
+            w = oracle.philox4x32_10([g, b, L, 0], [77, 0])
+            # element 8g + i: the low half of word i // 2 for even i, the high half for odd i
+            r16[b, 8 * g:8 * g + 8] = [(int(w[i // 2]) >> (16 * (i % 2))) & 0xFFFF for i in range(8)]
+    want = oracle.f16_decode(oracle.f16_encode(flat, r16)).astype(np.float64).reshape(S0.shape)
     assert np.array_equal(sr.checkpoint(), want)
     assert not np.array_equal(sr.checkpoint(), rne.checkpoint())
 
