@@ -254,12 +254,14 @@ __device__ inline float chunk_dot<PREC_F16>(u32x4 v, const float *c)
 // ------------------------------------------------------------------------------------------
 // fp16 master rounding. Nearest even by gfx950's converter (values clamped to +-65504 first).
 // Stochastic: with q the fp16 magnitude toward zero from |v| and ulp the spacing above it, round
-// up iff r24 < (|v| - q) / ulp * 2^24. Both factors are exact in fp32 (Sterbenz; scaling by a
-// power of two), so the decision is exact; the rounding is unbiased over r24 (to within 2^-24 of
-// a spacing for |v| < 2^-25, where the threshold is not an integer).
-// r24 = top 24 bits of Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2,
-// 3", SC'11) of counter (element / 4, sequence, new ckpt_pos, 0) and key (seed, 0); word
-// element % 4 (elements numbered h*P*N + p*N + n within the sequence).
+// up iff r16 < (|v| - q) / ulp * 2^16. Both factors are exact in fp32 (Sterbenz; scaling by a
+// power of two), so the decision is exact. In fp16's normal range the threshold is a multiple of
+// 8 (fp32 keeps 13 bits below the fp16 spacing), so the rounding is exactly unbiased over r16;
+// below 2^-17 the bias is under 2^-16 of a spacing.
+// r16 = 16-bit field of Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2,
+// 3", SC'11) of counter (element / 8, sequence, new ckpt_pos, 0) and key (seed, 0): element e
+// takes bits 16 * (e % 2) .. +15 of word (e % 8) / 2 (elements numbered h*P*N + p*N + n within
+// the sequence).
 // ------------------------------------------------------------------------------------------
 __device__ inline unsigned short f16_bits(float v) { return __builtin_bit_cast(unsigned short, (_Float16)v); }
 __device__ inline float f16_value(unsigned short h) { return (float)__builtin_bit_cast(_Float16, h); }
@@ -269,15 +271,15 @@ __device__ inline unsigned short f16_rne(float v)
     return f16_bits(fminf(fmaxf(v, -65504.0f), 65504.0f));
 }
 
-__device__ inline unsigned short f16_sr(float v, unsigned r24)
+__device__ inline unsigned short f16_sr(float v, unsigned r16)
 {
     const float a = fminf(fabsf(v), 65504.0f);
     if (a >= 0x1p-14f) {
         // fp16 normal range: the spacing is 2^13 fp32 spacings of a and |v| - q is the low 13 bits
-        // of a's encoding (low13 of them), so the rule reads r24 < low13 * 2^11, i.e.
-        // (r24 >> 11) < low13: adding 2^13 - 1 - (r24 >> 11) to the encoding carries into bit 13
+        // of a's encoding (low13 of them), so the rule reads r16 < low13 * 2^3, i.e.
+        // (r16 >> 3) < low13: adding 2^13 - 1 - (r16 >> 3) to the encoding carries into bit 13
         // exactly then; the truncated sum is the chosen fp16 value, converted exactly.
-        const unsigned u = (__float_as_uint(a) + (0x1FFFu - (r24 >> 11))) & ~0x1FFFu;
+        const unsigned u = (__float_as_uint(a) + (0x1FFFu - (r16 >> 3))) & ~0x1FFFu;
         return (unsigned short)(f16_bits(__uint_as_float(u)) | (__float_as_uint(v) >> 31 << 15));
     }
     unsigned short h = f16_bits(a);  // nearest even
@@ -288,7 +290,7 @@ __device__ inline unsigned short f16_sr(float v, unsigned r24)
     }
     if (a > q) {
         const float ulp = f16_value((unsigned short)(h + 1)) - q;
-        if ((float)r24 < (a - q) * (16777216.0f / ulp)) h = (unsigned short)(h + 1);
+        if ((float)r16 < (a - q) * (65536.0f / ulp)) h = (unsigned short)(h + 1);
     }
     return (unsigned short)(h | (__float_as_uint(v) >> 31 << 15));
 }

@@ -425,12 +425,15 @@ __device__ inline void store_master_rows(const Layer &Ld, int b, size_t elem0, i
         const f32x4 f = vf[i];
         unsigned short h0, h1, h2, h3;
         if (stochastic) {
+            // the lane's four elements e .. e+3 are one half of an 8-element Philox group: words
+            // 0, 1 for the lower half, 2, 3 for the upper, low 16 bits first
             const size_t e = elem0 - seq0 + (size_t)r * NN + 4 * c;  // element within the sequence
-            const U32x4 rnd = philox4x32_10((unsigned)(e / 4), (unsigned)b, (unsigned)newck, 0u, Ld.sr_seed, 0u);
-            h0 = f16_sr(f.x, rnd.x >> 8);
-            h1 = f16_sr(f.y, rnd.y >> 8);
-            h2 = f16_sr(f.z, rnd.z >> 8);
-            h3 = f16_sr(f.w, rnd.w >> 8);
+            const U32x4 rnd = philox4x32_10((unsigned)(e / 8), (unsigned)b, (unsigned)newck, 0u, Ld.sr_seed, 0u);
+            const unsigned w0 = (e & 4) ? rnd.z : rnd.x, w1 = (e & 4) ? rnd.w : rnd.y;
+            h0 = f16_sr(f.x, w0 & 0xFFFFu);
+            h1 = f16_sr(f.y, w0 >> 16);
+            h2 = f16_sr(f.z, w1 & 0xFFFFu);
+            h3 = f16_sr(f.w, w1 >> 16);
         } else {
             h0 = f16_rne(f.x);
             h1 = f16_rne(f.y);

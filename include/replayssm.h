@@ -91,12 +91,13 @@ typedef enum {
  *   FP16     IEEE binary16, rounded to nearest even at load and at every flush (values clamped to
  *            +-65504). Reads with read_prec FP32 then come from the fp16 master itself.
  *   FP16_SR  as FP16 at load; at every flush each value rounds stochastically: with q the fp16
- *            magnitude toward zero and ulp the spacing above it, up iff r < (|v| - q) / ulp * 2^24,
- *            r = top 24 bits of word (e mod 4) of Philox4x32-10 (Salmon et al., SC'11) with counter
- *            (e / 4, sequence, new ckpt_pos, 0) and key (sr_seed, 0), e = h*P*N + p*N + n.
- *            Unbiased over r (to 2^-24 of a spacing below 2^-25); deterministic for a given
- *            seed. Standard steps use the device pointers (the lockstep fast path is off) so
- *            that every flush knows its ckpt_pos.
+ *            magnitude toward zero and ulp the spacing above it, up iff r < (|v| - q) / ulp * 2^16,
+ *            r = bits 16*(e mod 2) .. +15 of word (e mod 8) / 2 of Philox4x32-10 (Salmon et al.,
+ *            SC'11) with counter (e / 8, sequence, new ckpt_pos, 0) and key (sr_seed, 0),
+ *            e = h*P*N + p*N + n. Exactly unbiased over r in fp16's normal range (an fp32 value has
+ *            13 bits below the fp16 spacing), within 2^-16 of a spacing below 2^-17; deterministic
+ *            for a given seed. Standard steps use the device pointers (the lockstep fast path is
+ *            off) so that every flush knows its ckpt_pos.
  * The stored layout stays [Bt,H,P,N]; RSSM_E_INVAL for a value outside 0..2. */
 typedef enum { RSSM_MASTER_FP32 = 0, RSSM_MASTER_FP16 = 1, RSSM_MASTER_FP16_SR = 2 } rssm_master_prec;
 
