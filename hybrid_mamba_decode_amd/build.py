@@ -17,9 +17,11 @@ LIB = os.path.join(PKG, "libreplayssm.so")
 STATE_SIZES = (16, 32, 64, 128, 256)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed-fp32 VALU ops are kept out of the device code (plain float code only).
+# Packed-fp32 VALU ops are kept out of the device code (plain float code only). MFMA
+# accumulators are kept in ordinary VGPRs (no copies to and from the accumulation registers).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _run(cmd, verbose):

@@ -347,11 +347,12 @@ rssm_status do_step(replayssm_t h, const TokenIO &io, bool mix, void *stream)
     if (h->pending_T) return RSSM_E_STATE;
     const int lim = h->cfg.buffer_len - h->cfg.max_draft;
     bool flush_capable = h->cmax + 1 > lim;
+    bool all_flush = h->cmin + 1 > lim;  // the lower bound already fills: every sequence flushes
     Lockstep ls{0, 0, 0, 0};
     if (h->uni) {
         ls = Lockstep{h->pslot, h->cslot, h->lcount + 1, h->dev.R > 0 ? h->upos % h->dev.R : 0};
         h->upos += 1;
-        flush_capable = h->lcount + 1 > lim;  // every sequence flushes, or none does
+        flush_capable = all_flush = h->lcount + 1 > lim;  // every sequence flushes, or none does
         h->pslot = (h->pslot + 1) % h->cfg.buffer_len;
         if (flush_capable) {
             h->lcount = 0;
@@ -363,7 +364,7 @@ rssm_status do_step(replayssm_t h, const TokenIO &io, bool mix, void *stream)
     commit_bounds(h, 1, 1);
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_step_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, io, flush_capable, mix, ls, st)
+#define CALL(NV) launch_step_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, io, flush_capable, all_flush, mix, ls, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
 }

@@ -140,6 +140,14 @@ __device__ inline float conv_finish(const ConvIn &r)
     return silu_f(u);
 }
 
+// Ring slot of the record j places after the one in slot `base` (base < L, 0 <= j < L): one
+// compare and subtract instead of an integer division by the runtime L.
+__device__ inline int ring_slot(int base, int j, int L)
+{
+    const int sl = base + j;
+    return sl >= L ? sl - L : sl;
+}
+
 // Device flag bits.
 enum : unsigned { FLAG_POINTERS = 1u, FLAG_ACCEPTED = 2u };
 
@@ -310,7 +318,9 @@ __device__ inline U32x4 philox4x32_10(unsigned c0, unsigned c1, unsigned c2, uns
         // one 32x32 -> 64-bit multiply per product (v_mad_u64_u32), high and low halves
         const unsigned long long p0 = (unsigned long long)0xD2511F53u * c0;
         const unsigned long long p1 = (unsigned long long)0xCD9E8D57u * c2;
-        const unsigned n0 = (unsigned)(p1 >> 32) ^ c1 ^ k0, n2 = (unsigned)(p0 >> 32) ^ c3 ^ k1;
+        // three-input xor in one v_bitop3_b32 (truth table 0x96 = a ^ b ^ c)
+        const unsigned n0 = __builtin_amdgcn_bitop3_b32((unsigned)(p1 >> 32), c1, k0, 0x96);
+        const unsigned n2 = __builtin_amdgcn_bitop3_b32((unsigned)(p0 >> 32), c3, k1, 0x96);
         c0 = n0;
         c1 = (unsigned)p1;
         c2 = n2;

@@ -103,7 +103,8 @@ __device__ inline void stage_window(GWin<LMAX> &w, const GLayer &Ld, const Tile 
     const size_t bh = (size_t)t.b * Ld.H + t.h;
     const float *rk = Ld.ring_k + ((size_t)t.b * Ld.G + t.g) * Ld.L * NN;
     const float *rv = Ld.ring_v + bh * Ld.L * Ld.Dv + t.row0;
-    auto slot = [&](int j) { return (int)((unsigned)(ck + j) % (unsigned)Ld.L); };
+    const int cs0 = (int)((unsigned)ck % (unsigned)Ld.L);
+    auto slot = [&](int j) { return ring_slot(cs0, j, Ld.L); };  // record j (< L)
     for (int e = tid; e < k * (NN / 4); e += kThreads) {
         const int j = e / (NN / 4), c4 = e % (NN / 4);
         const float *src = j < nring ? rk + (size_t)slot(j) * NN : fk + (size_t)(j - nring) * sk;
@@ -345,7 +346,7 @@ struct StepWindow {
         rk = Ld.ring_k + bg * Ld.L * NN;
         rv = Ld.ring_v + bh * Ld.L * Ld.Dv + t.row0;
     }
-    __device__ int slot_of(const GLayer &Ld, int j) const { return (int)((unsigned)(cslot + j) % (unsigned)Ld.L); }
+    __device__ int slot_of(const GLayer &Ld, int j) const { return ring_slot(cslot, j, Ld.L); }  // j < L
     __device__ const float *kaddr(const GLayer &Ld, const GTokenIO &io, int j, int c4) const
     {
         return (j < k - 1 ? rk + (size_t)slot_of(Ld, j) * NN : io.k + bg * NN) + 4 * c4;
@@ -639,7 +640,8 @@ __global__ void __launch_bounds__(kThreads) gdn_flush_kernel(GLayer Ld, int mode
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const float *rk = Ld.ring_k + ((size_t)t.b * Ld.G + t.g) * Ld.L * NN;
     const float *rv = Ld.ring_v + bh * Ld.L * Ld.Dv + t.row0;
-    auto slot_of = [&](int j) { return (int)((unsigned)(ck + (j < count ? j : 0)) % (unsigned)Ld.L); };
+    const int cs0 = (int)((unsigned)ck % (unsigned)Ld.L);
+    auto slot_of = [&](int j) { return ring_slot(cs0, j < count ? j : 0, Ld.L); };
     f32x4 kr[KCH], vr[VS];
 #pragma unroll
     for (int sl = 0; sl < KCH; ++sl) {
@@ -736,9 +738,9 @@ struct VerifyWindow {
     float ar, br;
     const float *rk, *rv;
     size_t bh, bT;
-    int ck, count0, kw, T, tid;
+    int cslot, count0, kw, T, tid;  // cslot = ckpt_pos mod L
 
-    __device__ int slot_of(const GLayer &Ld, int j) const { return (int)((unsigned)(ck + j) % (unsigned)Ld.L); }
+    __device__ int slot_of(const GLayer &Ld, int j) const { return ring_slot(cslot, j, Ld.L); }  // j < L
     __device__ const float *kaddr(const GLayer &Ld, const GTokenIO &io, const Tile &t, int j) const
     {
         return j < count0 ? rk + (size_t)slot_of(Ld, j) * NN : io.k + ((bT + (j - count0)) * Ld.G + t.g) * NN;
@@ -747,7 +749,7 @@ struct VerifyWindow {
     __device__ void issue(const GLayer &Ld, const GTokenIO &io, const Tile &t, int ck_, int count0_, int T_)
     {
         tid = threadIdx.x;
-        ck = ck_;
+        cslot = (int)((unsigned)ck_ % (unsigned)Ld.L);
         count0 = count0_;
         T = T_;
         kw = count0 + T;
@@ -835,6 +837,7 @@ __device__ inline void verify_output_append(const GVerifyLds<LMAX, TQ, RT> &s, c
 {
     const int tid = threadIdx.x;
     const size_t bh = (size_t)t.b * Ld.H + t.h, bT = (size_t)t.b * T;
+    const int pslot0 = (int)((unsigned)pos % (unsigned)Ld.L);  // draft q goes to slot (pos + q) mod L
     for (int e = tid; e < T * RT; e += kThreads) {
         const int q = e / RT, r = e % RT;
         if (r < t.nrows) {
@@ -842,19 +845,19 @@ __device__ inline void verify_output_append(const GVerifyLds<LMAX, TQ, RT> &s, c
             float acc = s.u[q][r];
             for (int j = 0; j <= last; ++j) acc = fmaf(s.c[q][j], s.w.V[j][r], acc);
             io.o[((bT + q) * Ld.H + t.h) * Ld.Dv + t.row0 + r] = acc;
-            const int slot = (int)((unsigned)(pos + q) % (unsigned)Ld.L);
+            const int slot = ring_slot(pslot0, q, Ld.L);
             Ld.ring_v[(bh * Ld.L + slot) * Ld.Dv + t.row0 + r] = s.w.V[last][r];
         }
     }
     if (t.split == 0 && tid < T) {
-        const int slot = (int)((unsigned)(pos + tid) % (unsigned)Ld.L);
+        const int slot = ring_slot(pslot0, tid, Ld.L);
         Ld.ring_a[bh * Ld.L + slot] = s.w.a[count0 + tid];
         Ld.ring_b[bh * Ld.L + slot] = s.w.b[count0 + tid];
     }
     if (t.split == 0 && t.h % Ld.hpg == 0) {
         for (int e = tid; e < T * (NN / 4); e += kThreads) {
             const int q = e / (NN / 4), c4 = e % (NN / 4);
-            const int slot = (int)((unsigned)(pos + q) % (unsigned)Ld.L);
+            const int slot = ring_slot(pslot0, q, Ld.L);
             *(f32x4 *)(Ld.ring_k + (((size_t)t.b * Ld.G + t.g) * Ld.L + slot) * NN + 4 * c4) =
                 *(const f32x4 *)&s.w.K[count0 + q][4 * c4];
         }

@@ -139,8 +139,8 @@ struct RecSrc {
     const float *rx, *rB, *rdt;   // this (sequence, head / group)'s ring rows, slot 0
     const float *fx, *fB, *fdt;   // first fresh record
     int sx, sB, sdt;              // stride between fresh records (floats)
-    int ck, L, P, nring;
-    __device__ int slot(int j) const { return (int)((unsigned)(ck + j) % (unsigned)L); }
+    int cslot, L, P, nring;  // cslot = ck mod L
+    __device__ int slot(int j) const { return ring_slot(cslot, j, L); }
     __device__ const float *x(int j) const
     {
         return j < nring ? rx + (size_t)slot(j) * P : fx + (size_t)(j - nring) * sx;
@@ -161,7 +161,7 @@ __device__ inline RecSrc ring_src(const Layer &Ld, const Tile &t, int ck, int nr
     s.rdt = Ld.ring_dt + bh * Ld.L;
     s.fx = s.fB = s.fdt = nullptr;
     s.sx = s.sB = s.sdt = 0;
-    s.ck = ck; s.L = Ld.L; s.P = Ld.P; s.nring = nring;
+    s.cslot = (int)((unsigned)ck % (unsigned)Ld.L); s.L = Ld.L; s.P = Ld.P; s.nring = nring;
     return s;
 }
 
@@ -556,7 +556,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     //    Otherwise: this sequence's device pointers, validated before any address is formed.
     const bool uni = ls.k > 0;
     int pslot = 0, cslot = 0, k = 1, dpos = 0;  // dpos: this sequence's pos (device-pointer mode)
-    auto slot_of = [&](int j) { return (int)((unsigned)(cslot + j) % (unsigned)Ld.L); };  // record j
+    auto slot_of = [&](int j) { return ring_slot(cslot, j, Ld.L); };  // record j (< L)
 
     // Two-head flush launches serve fp16 masters only (the host picks them so). Both heads' master
     // rows (8 bytes per lane and slot, in the fold's geometry) are issued as soon as the window
@@ -941,7 +941,7 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
     // 2. Pointers (as in step_kernel: lockstep arguments, or this sequence's device pointers).
     const bool uni = ls.k > 0;
     int pslot = 0, cslot = 0, k = 1;
-    auto slot_of = [&](int j) { return (int)((unsigned)(cslot + j) % (unsigned)Ld.L); };
+    auto slot_of = [&](int j) { return ring_slot(cslot, j, Ld.L); };  // record j (< L)
 
     // 3. Window, in two groups: (a) the group's B rows and C_t, staged through LDS, and (lane j)
     //    dt_j of this head, issued with the checkpoint stream; (b) this lane's x_j (record j of its
@@ -1135,6 +1135,348 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
     } else {
         const int pos = Ld.pos[t.b], ck = Ld.ckpt[t.b];
         seq_done(Ld, t.b, pos + 1, ck, HPB);
+    }
+}
+
+// ==========================================================================================
+// Flush step of an fp16 master when every sequence of the launch flushes (lockstep decoding, or
+// a host bound showing every buffer fills): fold all k records of the window into the master
+// ([WittyWires] "What happened": the checkpoint is updated when the buffer fills), round it to
+// fp16 (nearest even or stochastic, reading R13), rewrite the read copy and read y from the
+// stored master. The fold S' = decay * S + sum_j (w_j x_j) (outer) B_j is a rank-k update, a
+// dense contraction: it runs on MFMA (v_mfma_f32_16x16x4_f32), leaving the VALU to the fp16
+// conversions, the rounding and its Philox stream.
+//
+// One work-group per (sequence, head), P <= 64: wave w owns rows 16w .. 16w+15. The product is
+// formed transposed, D^T[n][p] += sum_j B_j[n] * (w_j x_j[p]), so that an MFMA tile's column is a
+// row p of the state (lane l: p = 16w + l % 16) and its four output registers are four
+// consecutive n of that row. Tile (q, hf) maps its row r to n = 32q + 8(r / 4) + 4hf + r % 4:
+// lane group g = l / 16 then holds n = 32q + 8g .. 32q + 8g + 7 of tiles (q, 0) and (q, 1) --
+// eight consecutive fp16 values, one 16-byte load and store per q, and one Philox4x32-10 call
+// for the eight 16-bit fields of its stochastic rounding. Per load instruction a wave reads 16
+// rows x 64 contiguous bytes.
+// ==========================================================================================
+template <int LMAX>
+struct LpFlushLds {
+    float xw[LMAX][kRows] __attribute__((aligned(16)));  // x of each record, this head's rows
+    float Bw[LMAX][NN + 4] __attribute__((aligned(16))); // B of each record; padded: the four lane
+                                                         // groups of a wave read four records
+    float Cq[NN] __attribute__((aligned(16)));           // C of this token
+    float w[LMAX];
+    float decay;
+    float red[kWaves];
+};
+
+template <int PREC, int LMAX, bool SR>
+__global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, TokenIO io, Lockstep ls)
+{
+    static_assert(PREC >= 0 && NN >= 32 && NN % 32 == 0, "lane groups cover 32 consecutive n per load slot");
+    constexpr int NQ = NN >= 32 ? NN / 32 : 1;  // 16-byte fp16 loads per lane (eight values each)
+    __shared__ LpFlushLds<LMAX> s;
+    const Tile t = map_tile(Ld);  // psplit == 1 (host-checked): the work-group owns the head
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c16 = lane & 15, g = lane >> 4;
+    const int pl = wave * 16 + c16;  // this lane's state row (the MFMA column)
+    const bool prow = pl < t.nrows;
+    const int pr = prow ? pl : 0;    // rows beyond P read row 0 and store nothing
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    const size_t rowe = (bh * Ld.P + pr) * NN;  // element offset of this lane's row
+
+    // 1. Pointers: the window position (lockstep arguments, or this sequence's device pointers,
+    //    validated before any address is formed). Every sequence of the launch must flush.
+    const bool uni = ls.k > 0;
+    int cslot = 0, k = 1, dpos = 0, dck = 0;
+    if (uni) {
+        cslot = ls.cslot;
+        k = ls.k;
+        if (!(k > Ld.L - Ld.Tmax && k <= Ld.L)) {  // the host launches this kernel for flush steps only
+            raise_flag(Ld, FLAG_POINTERS);
+            return;
+        }
+    } else {
+        dpos = Ld.pos[t.b];
+        dck = Ld.ckpt[t.b];
+        const int c0 = dpos - dck;
+        if (!(dck >= 0 && c0 >= 0 && c0 <= Ld.L - Ld.Tmax && c0 + 1 > Ld.L - Ld.Tmax)) {
+            raise_flag(Ld, FLAG_POINTERS);
+            seq_done(Ld, t.b, dpos, dck);
+            return;
+        }
+        cslot = (int)((unsigned)dck % (unsigned)Ld.L);
+        k = c0 + 1;
+    }
+    auto slot_of = [&](int j) { return ring_slot(cslot, j, Ld.L); };  // record j (< L)
+
+    // 2. Window loads into registers (x rows, the group's B rows, this token's C, dt in wave 0),
+    //    then the master rows: committing the window waits only for the window's loads.
+    constexpr int XS = (LMAX * kRows / 4 + kThreads - 1) / kThreads;
+    constexpr int BS = (LMAX * NN / 4 + kThreads - 1) / kThreads;
+    constexpr int BCH = BS < 8 ? BS : 8;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const float *rx = Ld.ring_x + bh * Ld.L * Ld.P;
+    const float *rB = Ld.ring_B + ((size_t)t.b * Ld.G + t.g) * Ld.L * NN;
+    const float *fx = io.x + bh * Ld.P;
+    const float *fB = io.B + ((size_t)t.b * Ld.G + t.g) * NN;
+    const float *Ct = io.C + ((size_t)t.b * Ld.G + t.g) * NN;
+    f32x4 xv[XS], bv[BCH], cq;
+    float dtj = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < XS; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
+        const bool in = j < k && 4 * c4 < t.nrows;
+        const float *src = (in && j < k - 1) ? rx + (size_t)slot_of(j) * Ld.P + 4 * c4 : fx + (in ? 4 * c4 : 0);
+        const f32x4 val = *(const f32x4 *)src;
+        xv[sl] = in ? val : zero;
+    }
+#pragma unroll
+    for (int sl = 0; sl < BCH; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+        const float *src = (j < k - 1 ? rB + (size_t)slot_of(j) * NN : fB) + 4 * c4;
+        const f32x4 val = *(const f32x4 *)src;
+        bv[sl] = j < k ? val : zero;
+    }
+    {
+        const f32x4 val = *(const f32x4 *)(Ct + 4 * (tid % (NN / 4)));
+        cq = tid < NN / 4 ? val : zero;
+    }
+    if (wave == 0) {
+        const bool in = lane < k;
+        const float val = (in && lane < k - 1) ? Ld.ring_dt[bh * Ld.L + slot_of(lane)] : io.dt[bh];
+        dtj = in ? val : 0.f;
+    }
+    const float Ah = Ld.A[t.h];
+    u32x4 mv[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+        mv[q] = load_nt((const unsigned short *)Ld.master + rowe + 32 * q + 8 * g);
+
+    // 3. Commit the window to LDS; the window's weights in wave 0 (suffix sums of dt by lane
+    //    shuffles: w_j = dt_j exp(A sum_{i>j} dt_i), decay = exp(A sum_i dt_i)).
+#pragma unroll
+    for (int sl = 0; sl < XS; ++sl) {
+        const int e = tid + sl * kThreads, j = e / (kRows / 4), c4 = e % (kRows / 4);
+        if (j < LMAX) *(f32x4 *)&s.xw[j][4 * c4] = xv[sl];
+    }
+#pragma unroll
+    for (int s0 = 0; s0 < BS; s0 += BCH) {
+        if (s0 > 0) {
+#pragma unroll
+            for (int sl = 0; sl < BCH; ++sl) {
+                const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+                const float *src = j < k - 1 ? rB + (size_t)slot_of(j) * NN : fB;
+                bv[sl] = (s0 + sl < BS && j < k) ? *(const f32x4 *)(src + 4 * c4) : zero;
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < BCH; ++sl) {
+            const int e = tid + (s0 + sl) * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
+            if (s0 + sl < BS && j < LMAX) *(f32x4 *)&s.Bw[j][4 * c4] = bv[sl];
+        }
+    }
+    if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = cq;
+    if (wave == 0) {
+        float sfx = dtj;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float nb = __shfl_down(sfx, o, 64);
+            sfx += lane + o < 64 ? nb : 0.f;
+        }
+        const float nxt = __shfl_down(sfx, 1, 64);
+        const float tail = lane + 1 < 64 ? nxt : 0.f;
+        if (lane < LMAX) s.w[lane] = lane < k ? dtj * expf(Ah * tail) : 0.f;
+        if (lane == 0) s.decay = expf(Ah * sfx);
+    }
+    __syncthreads();
+
+    // 4. S' = decay * S + sum_j B_j (outer) (w_j x_j), transposed, on MFMA: the accumulators start
+    //    as decay * S (the master rows, converted exactly), then one MFMA per tile and four records.
+    const float decay = s.decay;
+    f32x4 acc[NQ][2];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const f32x2 a = f16x2_to_f32(mv[q].x), b = f16x2_to_f32(mv[q].y);
+        const f32x2 c = f16x2_to_f32(mv[q].z), d = f16x2_to_f32(mv[q].w);
+        acc[q][0] = f32x4{a.x, a.y, b.x, b.y} * decay;
+        acc[q][1] = f32x4{c.x, c.y, d.x, d.y} * decay;
+    }
+    const int ksteps = (k + 3) / 4;
+    for (int kk = 0; kk < ksteps; ++kk) {
+        const int j = 4 * kk + g;  // this lane group's record
+        const bool jin = j < k;
+        const int jr = jin ? j : 0;
+        const float bop = jin ? s.w[jr] * s.xw[jr][pl] : 0.f;  // (w_j x_j)[p]
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int n = 32 * q + 8 * (c16 >> 2) + 4 * hf + (c16 & 3);  // tile row c16
+                const float aop = jin ? s.Bw[jr][n] : 0.f;                    // B_j[n]
+                acc[q][hf] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, bop, acc[q][hf], 0, 0, 0);
+            }
+    }
+
+    // 5. Round to fp16 and store the master; acc then holds the stored values (the flush's
+    //    output and the read copy come from the checkpoint as stored). In fp16's normal range
+    //    both roundings are integer operations on the fp32 encoding whose result is the rounded
+    //    value itself, exact in fp32 (13 low mantissa bits cleared): nearest even adds
+    //    0xFFF + bit 13; the stochastic rule adds 2^13 - 1 - (r16 >> 3) (see f16_sr). The codes
+    //    are then packed by the round-toward-zero converter, exact on representable values. A
+    //    wave with a value below 2^-14 redoes those values with the general routines.
+    const unsigned newck = (unsigned)(dpos + 1);  // stochastic rounding runs in device-pointer mode
+    const size_t seq0 = (size_t)t.b * Ld.H * Ld.P * NN;
+    unsigned short *mdst = (unsigned short *)Ld.master + rowe + 8 * g;
+    unsigned wd[NQ][4];  // SR: the eight 16-bit fields of each group of eight values
+    if constexpr (SR) {
+        const unsigned e8 = (unsigned)((rowe - seq0) / 8) + (unsigned)g;  // first group's counter
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const U32x4 rnd = philox4x32_10(e8 + 4u * q, (unsigned)t.b, newck, 0u, Ld.sr_seed, 0u);
+            wd[q][0] = rnd.x; wd[q][1] = rnd.y; wd[q][2] = rnd.z; wd[q][3] = rnd.w;
+        }
+    }
+    bool sub = false;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            f32x4 &a = acc[q][hf];
+            float r[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * hf + i;  // element within the group of eight
+                const float c = __builtin_amdgcn_fmed3f(r[i], -65504.0f, 65504.0f);
+                const unsigned u = __float_as_uint(c);
+                // SR: the 13-bit complement of r16 >> 3 is bits 3 .. 15 of the field, inverted
+                unsigned add;
+                if constexpr (SR) add = (~wd[q][e / 2] >> (3 + 16 * (e % 2))) & 0x1FFFu;
+                else add = 0xFFFu + ((u >> 13) & 1u);
+                sub |= fabsf(c) < 0x1p-14f;
+                r[i] = __uint_as_float((u + add) & ~0x1FFFu);
+            }
+            // keep the unrounded values for the rare fix-up below
+            if (__builtin_expect(__builtin_amdgcn_ballot_w64(sub) != 0, 0)) {
+                const float o[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * hf + i;
+                    if (fabsf(o[i]) < 0x1p-14f) {
+                        unsigned short hc;
+                        if constexpr (SR) hc = f16_sr(o[i], (wd[q][e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+                        else hc = f16_rne(o[i]);
+                        r[i] = f16_value(hc);
+                    }
+                }
+                sub = false;
+            }
+            a = f32x4{r[0], r[1], r[2], r[3]};
+        }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        if (prow) {
+            const f32x4 a = acc[q][0], b = acc[q][1];
+            u32x4 pk;
+            pk.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
+            pk.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a.z, a.w));
+            pk.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
+            pk.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(b.z, b.w));
+            store_nt(mdst + 32 * q, pk);
+        }
+    }
+
+    // 6. Read copy from the stored master.
+    if constexpr (PREC == PREC_BF16) {
+        unsigned short *dst = (unsigned short *)Ld.rcopy + rowe + 8 * g;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const f32x4 a = acc[q][0], b = acc[q][1];
+            const u32x4 pk = {bf16_rne(a.x) | (bf16_rne(a.y) << 16), bf16_rne(a.z) | (bf16_rne(a.w) << 16),
+                              bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16)};
+            if (prow) *(u32x4 *)(dst + 32 * q) = pk;
+        }
+    } else if constexpr (PREC == PREC_FP8) {
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const f32x4 a = acc[q][hf];
+                const float m = fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w)));
+                amax = prow ? fmaxf(amax, m) : amax;
+            }
+        amax = block_max(amax, s.red);
+        const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
+        const float inv = 1.0f / scale;
+        unsigned char *dst = (unsigned char *)Ld.rcopy;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const f32x4 a = acc[q][0], b = acc[q][1];
+            const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            float c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(f[i] * inv, -448.0f), 448.0f);
+            int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+            lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+            int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+            hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+            const int n0 = 32 * q + 8 * g;  // 16-value chunk n0 / 16, byte n0 % 16 within it
+            if (prow) *(u32x2 *)(dst + chunk_off<PREC_FP8>(bh, pr, n0 / 16, Ld.P) + n0 % 16) = u32x2{(unsigned)lo, (unsigned)hi};
+        }
+        if (tid == 0) Ld.scale[bh] = scale;
+    } else if constexpr (PREC == PREC_FP4) {
+        // block q (32 consecutive n of the row) is spread over the four lane groups of this row
+        unsigned char *dst = (unsigned char *)Ld.rcopy;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const f32x4 a = acc[q][0], b = acc[q][1];
+            float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                               fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+            amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+            const unsigned code = mx_code_of(amax);
+            const unsigned lo = mx_encode4(a, code), hi = mx_encode4(b, code);
+            if (prow) {
+                *(unsigned *)(dst + chunk_off<PREC_FP4>(bh, pr, q, Ld.P) + 4 * g) = lo | (hi << 16);
+                if (g == 0) Ld.mxscale[(bh * Ld.P + pr) * (NN / 32) + q] = (unsigned char)code;
+            }
+        }
+    }
+
+    // 7. y = S_stored[p,:] . C_t + D x_t: partial dots over the lane's n, summed over the four
+    //    lane groups of the row.
+    float yp = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const f32x4 c0 = *(const f32x4 *)&s.Cq[32 * q + 8 * g];
+        const f32x4 c1 = *(const f32x4 *)&s.Cq[32 * q + 8 * g + 4];
+        const f32x4 a = acc[q][0], b = acc[q][1];
+        yp = fmaf(a.x, c0.x, yp);
+        yp = fmaf(a.y, c0.y, yp);
+        yp = fmaf(a.z, c0.z, yp);
+        yp = fmaf(a.w, c0.w, yp);
+        yp = fmaf(b.x, c1.x, yp);
+        yp = fmaf(b.y, c1.y, yp);
+        yp = fmaf(b.z, c1.z, yp);
+        yp = fmaf(b.w, c1.w, yp);
+    }
+    yp += __shfl_xor(yp, 16, 64);
+    yp += __shfl_xor(yp, 32, 64);
+    if (g == 0 && prow) io.y[bh * Ld.P + pl] = fmaf(Ld.D[t.h], s.xw[k - 1][pl], yp);
+
+    // 8. Pointers (the token's record is folded already: nothing is appended).
+    if (uni) {
+        if (t.h == 0 && tid == 0) {
+            const int dp = Ld.pos[t.b], dc = Ld.ckpt[t.b];
+            const bool ok = dc >= 0 && dp - dc == k - 1 && (int)((unsigned)dp % (unsigned)Ld.L) == ls.pslot &&
+                            (int)((unsigned)dc % (unsigned)Ld.L) == cslot;
+            if (ok) {
+                Ld.pos[t.b] = dp + 1;
+                Ld.ckpt[t.b] = dp + 1;
+            } else {
+                __hip_atomic_fetch_or(Ld.flag, FLAG_POINTERS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    } else {
+        seq_done(Ld, t.b, dpos + 1, dpos + 1);
     }
 }
 
@@ -1392,6 +1734,7 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
 
     // Combine: wave q mod 4 forms query q's output rows; then the tentative appends.
     const float Dh = Ld.D[t.h];
+    const int pslot0 = (int)((unsigned)pos % (unsigned)Ld.L);  // draft q goes to slot (pos + q) mod L
     for (int q = wave; q < T; q += kWaves) {
         if (lane < t.nrows) {
             const int last = count0 + q;
@@ -1400,14 +1743,14 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
             acc = fmaf(Dh, s.win.xw[last][lane], acc);
             if constexpr (MIX) acc *= silu_f(io.z[(((size_t)t.b * T + q) * Ld.H + t.h) * Ld.P + t.row0 + lane]);
             io.y[(((size_t)t.b * T + q) * Ld.H + t.h) * Ld.P + t.row0 + lane] = acc;
-            Ld.ring_x[(bh * Ld.L + (unsigned)(pos + q) % (unsigned)Ld.L) * Ld.P + t.row0 + lane] = s.win.xw[last][lane];
+            Ld.ring_x[(bh * Ld.L + ring_slot(pslot0, q, Ld.L)) * Ld.P + t.row0 + lane] = s.win.xw[last][lane];
         }
-        if (t.split == 0 && lane == 0) Ld.ring_dt[bh * Ld.L + (unsigned)(pos + q) % (unsigned)Ld.L] = s.win.dts[count0 + q];
+        if (t.split == 0 && lane == 0) Ld.ring_dt[bh * Ld.L + ring_slot(pslot0, q, Ld.L)] = s.win.dts[count0 + q];
     }
     if (t.split == 0 && t.h % Ld.hpg == 0) {
         for (int e = tid; e < T * (NN / 4); e += kThreads) {
             const int q = e / (NN / 4), c4 = e % (NN / 4);
-            const size_t off = (((size_t)t.b * Ld.G + t.g) * Ld.L + (unsigned)(pos + q) % (unsigned)Ld.L) * NN + 4 * c4;
+            const size_t off = (((size_t)t.b * Ld.G + t.g) * Ld.L + ring_slot(pslot0, q, Ld.L)) * NN + 4 * c4;
             *(f32x4 *)(Ld.ring_B + off) = *(const f32x4 *)&s.win.Bw[count0 + q][4 * c4];
             if (Ld.ring_C) *(f32x4 *)(Ld.ring_C + off) = *(const f32x4 *)&s.Cq[q][4 * c4];
         }
@@ -1629,10 +1972,22 @@ hipError_t step_rows(const Layer &Ld, const TokenIO &io, Lockstep ls, hipStream_
 // issued together keep the flush's bytes in flight (one head each: 2.6 TB/s on the flush step).
 // MIX: the mixer edges fused in (no one-row-per-lane variant).
 template <int PREC, int LMAX, bool MIX>
-hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, Lockstep ls, hipStream_t st)
+hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, bool all_flush, Lockstep ls,
+                  hipStream_t st)
 {
     constexpr int wide = PREC == PREC_F32 ? 1 : (PREC == PREC_BF16 || PREC == PREC_F16) ? 2 : 4;  // fp8, fp4: 4
     if (flush_capable) {
+        // fp16 master, every sequence flushes: the fold on MFMA, one work-group per head
+        if constexpr (!MIX && NN >= 32)
+            if (all_flush && Ld.mprec != MASTER_F32 && Ld.psplit == 1 && (Ld.mprec != MASTER_F16_SR || ls.k == 0)) {
+                if (Ld.mprec == MASTER_F16_SR)
+                    hipLaunchKernelGGL((lp_flush_step_kernel<PREC, LMAX, true>), dim3(nblocks(Ld)), dim3(kThreads), 0,
+                                       st, Ld, io, ls);
+                else
+                    hipLaunchKernelGGL((lp_flush_step_kernel<PREC, LMAX, false>), dim3(nblocks(Ld)), dim3(kThreads), 0,
+                                       st, Ld, io, ls);
+                return hipGetLastError();
+            }
         // fp16 master: two heads per work-group with the master rows issued early (see step_kernel)
         if constexpr (LMAX <= 32)
             if (Ld.mprec != MASTER_F32 && Ld.psplit == 1 && Ld.hpg % 2 == 0)
@@ -1709,13 +2064,13 @@ hipError_t by_prec_lmax(int prec, int lmax, Args... args)
 
 template <int PREC, int LMAX>
 struct StepF {
-    static hipError_t run(const Layer &Ld, const TokenIO &io, bool fc, bool mix, Lockstep ls, hipStream_t st)
+    static hipError_t run(const Layer &Ld, const TokenIO &io, bool fc, bool af, bool mix, Lockstep ls, hipStream_t st)
     {
         if constexpr (!kPrecOk<PREC>) {
             return hipErrorInvalidValue;
         } else {
-            if (!mix) return step_t<PREC, LMAX, false>(Ld, io, fc, ls, st);
-            if constexpr (LMAX <= 32) return step_t<PREC, LMAX, true>(Ld, io, fc, ls, st);
+            if (!mix) return step_t<PREC, LMAX, false>(Ld, io, fc, af, ls, st);
+            if constexpr (LMAX <= 32) return step_t<PREC, LMAX, true>(Ld, io, fc, af, ls, st);
             else return hipErrorInvalidValue;  // the mixer edges need L <= 32 (host-checked)
         }
     }
@@ -1760,9 +2115,9 @@ hipError_t load_p(const Layer &Ld, const float *state, hipStream_t st)
 #define RSSM_CAT(a, b) RSSM_CAT2(a, b)
 
 hipError_t RSSM_CAT(launch_step_n, RSSM_N)(int prec, int lmax, const Layer &Ld, const TokenIO &io, bool flush_capable,
-                                           bool mix, Lockstep ls, hipStream_t st)
+                                           bool all_flush, bool mix, Lockstep ls, hipStream_t st)
 {
-    return by_prec_lmax<StepF>(prec, lmax, Ld, io, flush_capable, mix, ls, st);
+    return by_prec_lmax<StepF>(prec, lmax, Ld, io, flush_capable, all_flush, mix, ls, st);
 }
 
 hipError_t RSSM_CAT(launch_flush_n, RSSM_N)(int prec, int lmax, const Layer &Ld, int mode, const int *arg, int T, float *out, hipStream_t st)

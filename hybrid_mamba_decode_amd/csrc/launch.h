@@ -12,7 +12,8 @@ enum { MODE_MASK = 0, MODE_OVERFULL = 1, MODE_MATERIALIZE = 2 };
 
 #define RSSM_DECLARE_LAUNCHERS(NV)                                                                     \
     hipError_t launch_step_n##NV(int prec, int lmax, const Layer &Ld, const TokenIO &io,               \
-                                 bool flush_capable, bool mix, Lockstep ls, hipStream_t st);           \
+                                 bool flush_capable, bool all_flush, bool mix, Lockstep ls,            \
+                                 hipStream_t st);                                                      \
     hipError_t launch_flush_n##NV(int prec, int lmax, const Layer &Ld, int mode, const int *arg, int T,  \
                                   float *out, hipStream_t st);                                         \
     hipError_t launch_verify_n##NV(int prec, int lmax, const Layer &Ld, const TokenIO &io, int T,       \
