@@ -12,6 +12,7 @@
 #include <cstring>
 #include <new>
 
+#include "host_state.h"
 #include "launch.h"
 
 using namespace rssm;
@@ -21,34 +22,16 @@ struct replayssm_layer {
     replayssm_layout lay;
     Layer dev;
     int lmax;       // window bucket for kernel instances (16, 32 or 64)
-    int loaded;     // replayssm_load_state has run
-    int poisoned;   // device flag observed: refuse work until the next load
-    int pending_T;  // drafts of an unresolved verify, else 0
-    // Host hint: bounds on the number of pending committed records over all sequences. Exact for
-    // lockstep decoding, conservative otherwise; it only selects the kernel variant (whether a
-    // launch may meet a flush). The device decides every flush per sequence, bit-exactly.
-    int cmin, cmax;
-    // Lockstep: after a load, standard steps and unmasked flushes keep every sequence at the same
-    // window position, known here as (pos mod L, ckpt_pos mod L, pending count); the step kernel
-    // takes it as arguments. With T_max = 1 and no mixer edges these values repeat every L steps,
-    // so a captured run of whole windows replays correctly; with the mixer edges the conv ring
-    // slot pos mod R repeats every R steps, so a captured run must span a multiple of lcm(L, R)
-    // steps. A replay whose arguments no longer match the device pointers (or ring slot) raises
-    // the device flag. A rollback or a masked flush makes sequences diverge: from then on kernels
-    // read the device pointers.
-    int uni, pslot, cslot, lcount;
-    int upos;         // lockstep: the common pos (the mixer edges' conv ring slot is upos mod R)
-    int lockstep_ok;  // replayssm_set_lockstep: the fast path may be used at all
-    int mixer_set;    // replayssm_set_mixer has given the edge parameters
+    // Host state machine (host_state.h). Lockstep arguments: with T_max = 1 and no mixer edges they
+    // repeat every L steps, so a captured run of whole windows replays correctly; with the mixer
+    // edges the conv ring slot pos mod R repeats every R steps, so a captured run must span a
+    // multiple of lcm(L, R) steps. A replay whose arguments no longer match the device pointers
+    // (or ring slot) raises the device flag.
+    HostState hs;
+    int mixer_set;  // replayssm_set_mixer has given the edge parameters
 };
 
 namespace {
-
-constexpr size_t kAlign = 256;
-
-size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
-
-bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool supported_n(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
 
@@ -99,12 +82,8 @@ void make_layout(const replayssm_config &c, replayssm_layout *L)
     const size_t Bt = (size_t)c.batch, H = c.nheads, P = c.headdim, N = c.dstate, G = c.ngroups,
                  Lb = c.buffer_len;
     const size_t elems = Bt * H * P * N;
-    size_t off = 0;
-    auto take = [&](size_t bytes) {
-        const size_t at = off;
-        off = align_up(off + bytes);
-        return at;
-    };
+    RegionCarver rc;
+    auto take = [&](size_t bytes) { return rc.take(bytes); };
     L->master = take(elems * (c.master_prec == RSSM_MASTER_FP32 ? 4 : 2));
     const int rp = c.read_prec;
     L->read_copy = take(rp == RSSM_READ_BF16 ? elems * 2 : rp == RSSM_READ_FP8_E4M3 ? elems
@@ -119,7 +98,7 @@ void make_layout(const replayssm_config &c, replayssm_layout *L)
     L->ckpt_pos = take(Bt * 4);
     L->counters = take(Bt * 4);
     L->flag = take(4);
-    L->total = off;
+    L->total = rc.off;
 }
 
 // A Layer carrying only shapes and A/D, for the baselines.
@@ -139,8 +118,6 @@ Layer shape_layer(const replayssm_config &c, const float *A, const float *D)
     L.psplit = psplit_of(c);
     return L;
 }
-
-rssm_status hip_status(hipError_t e) { return e == hipSuccess ? RSSM_OK : RSSM_E_HIP; }
 
 // Snapshot baseline commit: the committed slot moves forward by the accepted count, modulo the
 // T + 1 slots. One thread per sequence; out-of-range counts leave the slot unchanged.
@@ -171,30 +148,7 @@ hipError_t launch_snapshot_commit(int *cur, const int *accepted, int T, int Bt, 
 rssm_status ready(replayssm_t h)
 {
     if (!h) return RSSM_E_INVAL;
-    if (!h->loaded || h->poisoned) return RSSM_E_STATE;
-    return RSSM_OK;
-}
-
-// Device array arguments: 16-byte aligned and non-NULL; with batch 0 (empty arrays) NULL is
-// accepted too.
-bool ok_ptr(const void *p, int batch) { return p ? aligned(p, 16) : batch == 0; }
-bool ok_ptr4(const void *p, int batch) { return p ? aligned(p, 4) : batch == 0; }
-
-// Bounds on the pending-record count after every sequence commits `lo..hi` more records and
-// those with more than L - Tmax pending flush.
-void commit_bounds(replayssm_t h, int lo, int hi)
-{
-    const int lim = h->cfg.buffer_len - h->cfg.max_draft;
-    const int nmin = h->cmin + lo, nmax = h->cmax + hi;
-    if (nmax <= lim) {
-        h->cmin = nmin;
-        h->cmax = nmax;
-    } else if (nmin > lim) {
-        h->cmin = h->cmax = 0;
-    } else {
-        h->cmin = 0;
-        h->cmax = lim;
-    }
+    return h->hs.ready();
 }
 
 // Conv history of every sequence, relative to its device pos: row i (oldest first) is the raw
@@ -222,19 +176,7 @@ hipError_t launch_conv_hist(const Layer &Ld, const float *hist, float *out, hipS
     return hipGetLastError();
 }
 
-rssm_status read_flag(replayssm_t h, hipStream_t st)
-{
-    if (hipStreamSynchronize(st) != hipSuccess) return RSSM_E_HIP;
-    unsigned flag = 0;
-    if (h->cfg.batch > 0) {
-        if (hipMemcpy(&flag, h->dev.flag, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) return RSSM_E_HIP;
-    }
-    if (flag) {
-        h->poisoned = 1;
-        return RSSM_E_STATE;
-    }
-    return RSSM_OK;
-}
+rssm_status read_flag(replayssm_t h, hipStream_t st) { return h->hs.read_flag(h->dev.flag, h->cfg.batch, st); }
 
 }  // namespace
 
@@ -267,11 +209,11 @@ rssm_status replayssm_create(const replayssm_config *cfg, void *workspace, size_
     if (!A || !D || !aligned(A, 4) || !aligned(D, 4)) return RSSM_E_INVAL;
     replayssm_layout lay;
     make_layout(*cfg, &lay);
-    if (!workspace || !aligned(workspace, kAlign) || bytes < lay.total) return RSSM_E_WORKSPACE;
-    replayssm_layer *h = new (std::nothrow) replayssm_layer;
+    if (!workspace || !aligned(workspace, kWsAlign) || bytes < lay.total) return RSSM_E_WORKSPACE;
+    replayssm_layer *h = new (std::nothrow) replayssm_layer();
     if (!h) return RSSM_E_INVAL;
-    std::memset(h, 0, sizeof(*h));
     h->cfg = *cfg;
+    h->hs.init(cfg->buffer_len, cfg->max_draft);
     h->lay = lay;
     char *ws = (char *)workspace;
     Layer &d = h->dev;
@@ -304,7 +246,6 @@ rssm_status replayssm_create(const replayssm_config *cfg, void *workspace, size_
     d.R = conv_slots(*cfg);
     d.CD = (int)conv_dim(*cfg);
     h->lmax = cfg->buffer_len <= 16 ? 16 : cfg->buffer_len <= 32 ? 32 : 64;
-    h->lockstep_ok = 1;
     *out = h;
     return RSSM_OK;
 }
@@ -319,12 +260,8 @@ rssm_status replayssm_load_state(replayssm_t h, const float *state, void *stream
 {
     if (!h) return RSSM_E_INVAL;
     if (!ok_ptr(state, h->cfg.batch)) return RSSM_E_INVAL;
-    h->loaded = 1;
-    h->poisoned = 0;
-    h->pending_T = 0;
-    h->cmin = h->cmax = 0;
-    h->uni = h->lockstep_ok && h->cfg.master_prec != RSSM_MASTER_FP16_SR;
-    h->pslot = h->cslot = h->lcount = h->upos = 0;
+    // a stochastically rounded master keys its stream by each sequence's device ckpt_pos
+    h->hs.on_load(h->cfg.master_prec != RSSM_MASTER_FP16_SR);
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
     rssm_status s = RSSM_OK;
@@ -344,27 +281,12 @@ rssm_status do_step(replayssm_t h, const TokenIO &io, bool mix, void *stream)
 {
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (h->pending_T) return RSSM_E_STATE;
-    const int lim = h->cfg.buffer_len - h->cfg.max_draft;
-    bool flush_capable = h->cmax + 1 > lim;
-    bool all_flush = h->cmin + 1 > lim;  // the lower bound already fills: every sequence flushes
-    Lockstep ls{0, 0, 0, 0};
-    if (h->uni) {
-        ls = Lockstep{h->pslot, h->cslot, h->lcount + 1, h->dev.R > 0 ? h->upos % h->dev.R : 0};
-        h->upos += 1;
-        flush_capable = all_flush = h->lcount + 1 > lim;  // every sequence flushes, or none does
-        h->pslot = (h->pslot + 1) % h->cfg.buffer_len;
-        if (flush_capable) {
-            h->lcount = 0;
-            h->cslot = h->pslot;
-        } else {
-            h->lcount += 1;
-        }
-    }
-    commit_bounds(h, 1, 1);
+    if (h->hs.pending_T) return RSSM_E_STATE;
+    const StepPlan p = h->hs.begin_step();
+    const Lockstep ls{p.pslot, p.cslot, p.k, p.k > 0 && h->dev.R > 0 ? p.upos % h->dev.R : 0};
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) launch_step_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, io, flush_capable, all_flush, mix, ls, st)
+#define CALL(NV) launch_step_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, io, p.flush_capable, p.all_flush, mix, ls, st)
     RSSM_BY_N(h->cfg.dstate, CALL)
 #undef CALL
 }
@@ -400,7 +322,7 @@ rssm_status replayssm_load_conv_state(replayssm_t h, const float *hist, void *st
     if (hist && !aligned(hist, 4)) return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (h->pending_T) return RSSM_E_STATE;
+    if (h->hs.pending_T) return RSSM_E_STATE;
     if (h->cfg.batch == 0) return RSSM_OK;
     return hip_status(launch_conv_hist(h->dev, hist, nullptr, (hipStream_t)stream));
 }
@@ -411,7 +333,7 @@ rssm_status replayssm_materialize_conv_state(replayssm_t h, float *out, void *st
     if (!ok_ptr4(out, h->cfg.batch)) return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (h->pending_T) return RSSM_E_STATE;
+    if (h->hs.pending_T) return RSSM_E_STATE;
     if (h->cfg.batch == 0) return RSSM_OK;
     return hip_status(launch_conv_hist(h->dev, nullptr, out, (hipStream_t)stream));
 }
@@ -432,15 +354,8 @@ rssm_status replayssm_flush(replayssm_t h, const int32_t *seq_mask, void *stream
     if (seq_mask && !aligned(seq_mask, 4)) return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (h->pending_T) return RSSM_E_STATE;
-    if (!seq_mask) {
-        h->cmin = h->cmax = 0;
-        h->lcount = 0;
-        h->cslot = h->pslot;
-    } else {
-        h->cmin = 0;
-        h->uni = 0;
-    }
+    if (h->hs.pending_T) return RSSM_E_STATE;
+    h->hs.on_flush(seq_mask != nullptr);
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) launch_flush_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, MODE_MASK, seq_mask, 0, nullptr, st)
@@ -458,8 +373,8 @@ rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float *x, cons
         return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (h->pending_T) return RSSM_E_STATE;
-    h->pending_T = T;
+    if (h->hs.pending_T) return RSSM_E_STATE;
+    h->hs.pending_T = T;
     if (h->cfg.batch == 0) return RSSM_OK;
     const TokenIO io{x, B, C, dt, y};
     const hipStream_t st = (hipStream_t)stream;
@@ -478,8 +393,8 @@ rssm_status replayssm_mixer_spec_verify(replayssm_t h, int32_t T, const float *x
     if (!h->mixer_set) return RSSM_E_STATE;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (h->pending_T) return RSSM_E_STATE;
-    h->pending_T = T;
+    if (h->hs.pending_T) return RSSM_E_STATE;
+    h->hs.pending_T = T;
     if (h->cfg.batch == 0) return RSSM_OK;
     const TokenIO io{nullptr, nullptr, nullptr, dt_raw, o, xbc, z};
     const hipStream_t st = (hipStream_t)stream;
@@ -494,11 +409,9 @@ rssm_status replayssm_rollback(replayssm_t h, const int32_t *accepted, void *str
     if (!ok_ptr4(accepted, h->cfg.batch)) return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (!h->pending_T) return RSSM_E_STATE;
-    const int T = h->pending_T;
-    h->pending_T = 0;
-    h->uni = 0;
-    commit_bounds(h, 0, T);
+    if (!h->hs.pending_T) return RSSM_E_STATE;
+    const int T = h->hs.pending_T;
+    h->hs.on_rollback(T);
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) launch_flush_n##NV(kernel_prec(h->cfg), h->lmax, h->dev, MODE_OVERFULL, accepted, T, nullptr, st)
@@ -509,15 +422,14 @@ rssm_status replayssm_rollback(replayssm_t h, const int32_t *accepted, void *str
 rssm_status replayssm_set_lockstep(replayssm_t h, int enable)
 {
     if (!h || (enable != 0 && enable != 1)) return RSSM_E_INVAL;
-    h->lockstep_ok = enable;
-    if (!enable) h->uni = 0;
+    h->hs.set_lockstep(enable);
     return RSSM_OK;
 }
 
 rssm_status replayssm_get_pointers(replayssm_t h, int32_t *pos, int32_t *ckpt_pos, void *stream)
 {
     if (!h) return RSSM_E_INVAL;
-    if (!h->loaded) return RSSM_E_STATE;
+    if (!h->hs.loaded) return RSSM_E_STATE;
     const hipStream_t st = (hipStream_t)stream;
     const rssm_status s = read_flag(h, st);
     if (s != RSSM_OK) return s;
@@ -531,8 +443,7 @@ rssm_status replayssm_get_pointers(replayssm_t h, int32_t *pos, int32_t *ckpt_po
 rssm_status replayssm_check(replayssm_t h, void *stream)
 {
     if (!h) return RSSM_E_INVAL;
-    if (!h->loaded) return RSSM_E_STATE;
-    if (h->poisoned) return RSSM_E_STATE;
+    if (!h->hs.loaded || h->hs.poisoned) return RSSM_E_STATE;
     return read_flag(h, (hipStream_t)stream);
 }
 

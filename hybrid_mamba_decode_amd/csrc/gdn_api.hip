@@ -10,6 +10,7 @@
 #include <new>
 
 #include "gdn_launch.h"
+#include "host_state.h"
 
 using namespace rssm;
 
@@ -17,31 +18,14 @@ struct gdnreplay_layer {
     gdnreplay_config cfg;
     gdnreplay_layout lay;
     GLayer dev;
-    int lmax;       // window bucket of the kernel instances (16, 32 or 64)
-    int loaded;     // gdnreplay_load_state has run
-    int poisoned;   // device flag observed: refuse work until the next load
-    int pending_T;  // drafts of an unresolved verify, else 0
-    // Bounds on the pending-record count over all sequences: they only choose whether a step
-    // launch may meet a flush (the device decides each flush per sequence).
-    int cmin, cmax;
-    // Lockstep: after a load, standard steps and unmasked flushes keep every sequence at the same
-    // window position (pos mod L, ckpt_pos mod L, pending count), tracked here and passed to the
-    // step kernel; a rollback or masked flush ends it until the next load.
-    int uni, pslot, cslot, lcount;
-    int lockstep_ok;
+    int lmax;      // window bucket of the kernel instances (16, 32 or 64)
+    HostState hs;  // host state machine (host_state.h), as for the Mamba-2 handle
 };
 
 namespace {
 
-constexpr size_t kAlign = 256;
-
-size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
-bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
-bool ok_ptr(const void *p, int batch) { return p ? aligned(p, 16) : batch == 0; }
-bool ok_ptr4(const void *p, int batch) { return p ? aligned(p, 4) : batch == 0; }
 bool supported_dk(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
 int psplit_of(const gdnreplay_config &c) { return (c.dv + kRows - 1) / kRows; }
-rssm_status hip_status(hipError_t e) { return e == hipSuccess ? RSSM_OK : RSSM_E_HIP; }
 
 rssm_status check_shape(const gdnreplay_config *c)
 {
@@ -67,12 +51,8 @@ rssm_status check_config(const gdnreplay_config *c)
 void make_layout(const gdnreplay_config &c, gdnreplay_layout *L)
 {
     const size_t Bt = (size_t)c.batch, H = c.nheads, G = c.nkheads, Dv = c.dv, Dk = c.dk, Lb = c.buffer_len;
-    size_t off = 0;
-    auto take = [&](size_t bytes) {
-        const size_t at = off;
-        off = align_up(off + bytes);
-        return at;
-    };
+    RegionCarver rc;
+    auto take = [&](size_t bytes) { return rc.take(bytes); };
     L->master = take(Bt * H * Dv * Dk * 4);
     L->read_copy = take(c.read_prec == RSSM_READ_BF16 ? Bt * H * Dv * Dk * 2 : 0);
     L->ring_k = take(Bt * G * Lb * Dk * 4);
@@ -83,7 +63,7 @@ void make_layout(const gdnreplay_config &c, gdnreplay_layout *L)
     L->ckpt_pos = take(Bt * 4);
     L->counters = take(Bt * 4);
     L->flag = take(4);
-    L->total = off;
+    L->total = rc.off;
 }
 
 // A GLayer carrying shapes only, for the baselines.
@@ -115,37 +95,10 @@ GLayer shape_layer(const gdnreplay_config &c)
 rssm_status ready(gdnreplay_t h)
 {
     if (!h) return RSSM_E_INVAL;
-    if (!h->loaded || h->poisoned) return RSSM_E_STATE;
-    return RSSM_OK;
+    return h->hs.ready();
 }
 
-void commit_bounds(gdnreplay_t h, int lo, int hi)
-{
-    const int lim = h->cfg.buffer_len - h->cfg.max_draft;
-    const int nmin = h->cmin + lo, nmax = h->cmax + hi;
-    if (nmax <= lim) {
-        h->cmin = nmin;
-        h->cmax = nmax;
-    } else if (nmin > lim) {
-        h->cmin = h->cmax = 0;
-    } else {
-        h->cmin = 0;
-        h->cmax = lim;
-    }
-}
-
-rssm_status read_flag(gdnreplay_t h, hipStream_t st)
-{
-    if (hipStreamSynchronize(st) != hipSuccess) return RSSM_E_HIP;
-    unsigned flag = 0;
-    if (h->cfg.batch > 0 && hipMemcpy(&flag, h->dev.flag, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess)
-        return RSSM_E_HIP;
-    if (flag) {
-        h->poisoned = 1;
-        return RSSM_E_STATE;
-    }
-    return RSSM_OK;
-}
+rssm_status read_flag(gdnreplay_t h, hipStream_t st) { return h->hs.read_flag(h->dev.flag, h->cfg.batch, st); }
 
 bool ok_io(int bt, const float *q, const float *k, const float *v, const float *a, const float *b, const float *o)
 {
@@ -181,11 +134,11 @@ rssm_status gdnreplay_create(const gdnreplay_config *cfg, void *workspace, size_
     if (s != RSSM_OK) return s;
     gdnreplay_layout lay;
     make_layout(*cfg, &lay);
-    if (!workspace || !aligned(workspace, kAlign) || bytes < lay.total) return RSSM_E_WORKSPACE;
-    gdnreplay_layer *h = new (std::nothrow) gdnreplay_layer;
+    if (!workspace || !aligned(workspace, kWsAlign) || bytes < lay.total) return RSSM_E_WORKSPACE;
+    gdnreplay_layer *h = new (std::nothrow) gdnreplay_layer();
     if (!h) return RSSM_E_INVAL;
-    std::memset(h, 0, sizeof(*h));
     h->cfg = *cfg;
+    h->hs.init(cfg->buffer_len, cfg->max_draft);
     h->lay = lay;
     char *ws = (char *)workspace;
     GLayer &d = h->dev;
@@ -209,7 +162,6 @@ rssm_status gdnreplay_create(const gdnreplay_config *cfg, void *workspace, size_
     d.hpg = cfg->nheads / cfg->nkheads;
     d.psplit = psplit_of(*cfg);
     h->lmax = cfg->buffer_len <= 16 ? 16 : cfg->buffer_len <= 32 ? 32 : 64;
-    h->lockstep_ok = 1;
     *out = h;
     return RSSM_OK;
 }
@@ -224,12 +176,7 @@ rssm_status gdnreplay_load_state(gdnreplay_t h, const float *state, void *stream
 {
     if (!h) return RSSM_E_INVAL;
     if (!ok_ptr(state, h->cfg.batch)) return RSSM_E_INVAL;
-    h->loaded = 1;
-    h->poisoned = 0;
-    h->pending_T = 0;
-    h->cmin = h->cmax = 0;
-    h->uni = h->lockstep_ok;
-    h->pslot = h->cslot = h->lcount = 0;
+    h->hs.on_load(true);
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) gdn_launch_load_n##NV(h->dev, state, st)
@@ -244,26 +191,13 @@ rssm_status gdnreplay_step(gdnreplay_t h, const float *q, const float *k, const 
     if (!ok_io(h->cfg.batch, q, k, v, alpha, beta, o)) return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (h->pending_T) return RSSM_E_STATE;
-    const int lim = h->cfg.buffer_len - h->cfg.max_draft;
-    bool flush_capable = h->cmax + 1 > lim;
-    Lockstep ls{0, 0, 0};
-    if (h->uni) {
-        ls = Lockstep{h->pslot, h->cslot, h->lcount + 1};
-        flush_capable = h->lcount + 1 > lim;  // every sequence flushes, or none does
-        h->pslot = (h->pslot + 1) % h->cfg.buffer_len;
-        if (flush_capable) {
-            h->lcount = 0;
-            h->cslot = h->pslot;
-        } else {
-            h->lcount += 1;
-        }
-    }
-    commit_bounds(h, 1, 1);
+    if (h->hs.pending_T) return RSSM_E_STATE;
+    const StepPlan p = h->hs.begin_step();
+    const Lockstep ls{p.pslot, p.cslot, p.k};
     if (h->cfg.batch == 0) return RSSM_OK;
     const GTokenIO io{q, k, v, alpha, beta, o};
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) gdn_launch_step_n##NV(h->lmax, h->dev, io, flush_capable, ls, st)
+#define CALL(NV) gdn_launch_step_n##NV(h->lmax, h->dev, io, p.flush_capable, ls, st)
     GDN_BY_N(h->cfg.dk, CALL)
 #undef CALL
 }
@@ -274,15 +208,8 @@ rssm_status gdnreplay_flush(gdnreplay_t h, const int32_t *seq_mask, void *stream
     if (seq_mask && !aligned(seq_mask, 4)) return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (h->pending_T) return RSSM_E_STATE;
-    if (!seq_mask) {
-        h->cmin = h->cmax = 0;
-        h->lcount = 0;
-        h->cslot = h->pslot;
-    } else {
-        h->cmin = 0;
-        h->uni = 0;
-    }
+    if (h->hs.pending_T) return RSSM_E_STATE;
+    h->hs.on_flush(seq_mask != nullptr);
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) gdn_launch_flush_n##NV(h->lmax, h->dev, MODE_MASK, seq_mask, 0, nullptr, st)
@@ -298,8 +225,8 @@ rssm_status gdnreplay_spec_verify(gdnreplay_t h, int32_t T, const float *q, cons
     if (!ok_io(h->cfg.batch, q, k, v, alpha, beta, o)) return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (h->pending_T) return RSSM_E_STATE;
-    h->pending_T = T;
+    if (h->hs.pending_T) return RSSM_E_STATE;
+    h->hs.pending_T = T;
     if (h->cfg.batch == 0) return RSSM_OK;
     const GTokenIO io{q, k, v, alpha, beta, o};
     const hipStream_t st = (hipStream_t)stream;
@@ -314,11 +241,9 @@ rssm_status gdnreplay_rollback(gdnreplay_t h, const int32_t *accepted, void *str
     if (!ok_ptr4(accepted, h->cfg.batch)) return RSSM_E_INVAL;
     rssm_status s = ready(h);
     if (s != RSSM_OK) return s;
-    if (!h->pending_T) return RSSM_E_STATE;
-    const int T = h->pending_T;
-    h->pending_T = 0;
-    h->uni = 0;
-    commit_bounds(h, 0, T);
+    if (!h->hs.pending_T) return RSSM_E_STATE;
+    const int T = h->hs.pending_T;
+    h->hs.on_rollback(T);
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
 #define CALL(NV) gdn_launch_flush_n##NV(h->lmax, h->dev, MODE_OVERFULL, accepted, T, nullptr, st)
@@ -329,15 +254,14 @@ rssm_status gdnreplay_rollback(gdnreplay_t h, const int32_t *accepted, void *str
 rssm_status gdnreplay_set_lockstep(gdnreplay_t h, int enable)
 {
     if (!h || (enable != 0 && enable != 1)) return RSSM_E_INVAL;
-    h->lockstep_ok = enable;
-    if (!enable) h->uni = 0;
+    h->hs.set_lockstep(enable);
     return RSSM_OK;
 }
 
 rssm_status gdnreplay_get_pointers(gdnreplay_t h, int32_t *pos, int32_t *ckpt_pos, void *stream)
 {
     if (!h) return RSSM_E_INVAL;
-    if (!h->loaded) return RSSM_E_STATE;
+    if (!h->hs.loaded) return RSSM_E_STATE;
     const rssm_status s = read_flag(h, (hipStream_t)stream);
     if (s != RSSM_OK) return s;
     const size_t bytes = (size_t)h->cfg.batch * sizeof(int32_t);
@@ -350,7 +274,7 @@ rssm_status gdnreplay_get_pointers(gdnreplay_t h, int32_t *pos, int32_t *ckpt_po
 rssm_status gdnreplay_check(gdnreplay_t h, void *stream)
 {
     if (!h) return RSSM_E_INVAL;
-    if (!h->loaded || h->poisoned) return RSSM_E_STATE;
+    if (!h->hs.loaded || h->hs.poisoned) return RSSM_E_STATE;
     return read_flag(h, (hipStream_t)stream);
 }
 

@@ -41,13 +41,18 @@ _sz = ctypes.c_size_t
 
 
 def lib():
-    """Load liboracle.so, building it first if it is missing or older than its source."""
+    """Load liboracle.so, building it first if it is missing or older than its source. The
+    environment variable RSSM_ORACLE_LIB names another build to load instead (the sanitizer
+    build of the tests)."""
     global _lib
     if _lib is None:
-        srcs = [os.path.join(_HERE, f) for f in ("oracle.c", "oracle_gdn.c", "oracle_mixer.c")]
-        if not os.path.exists(_LIB_PATH) or any(os.path.getmtime(_LIB_PATH) < os.path.getmtime(f) for f in srcs):
-            _build.build()
-        L = ctypes.CDLL(_LIB_PATH)
+        path = os.environ.get("RSSM_ORACLE_LIB")
+        if not path:
+            path = _LIB_PATH
+            srcs = [os.path.join(_HERE, f) for f in ("oracle.c", "oracle_gdn.c", "oracle_mixer.c")]
+            if not os.path.exists(path) or any(os.path.getmtime(path) < os.path.getmtime(f) for f in srcs):
+                _build.build()
+        L = ctypes.CDLL(path)
         L.oracle_step.argtypes = [_i] * 5 + [_f64p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f64p]
         L.oracle_step.restype = None
         L.oracle_silu.argtypes = [ctypes.c_double]

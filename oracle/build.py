@@ -11,14 +11,18 @@ SRCS = [os.path.join(HERE, f) for f in ("oracle.c", "oracle_gdn.c", "oracle_mixe
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-shared", "-fPIC", "-Wall", "-Wextra", "-o", LIB + ".tmp", *SRCS, "-lm"]
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+    """Compile the oracle into `out`. sanitize: an AddressSanitizer + UndefinedBehaviorSanitizer
+    build (host code, gcc) for the tests that run the oracle's pins under the sanitizers."""
+    opt = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"]
+    cmd = ["gcc", *opt, "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-shared", "-fPIC", "-Wall", "-Wextra", "-o", out + ".tmp", *SRCS, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
