@@ -71,6 +71,8 @@ def lib():
         L.oracle_encode_bf16.argtypes = [_f32p, _u16p, _sz]
         L.oracle_encode_e4m3_tiles.argtypes = [_f32p, _u8p, _f32p, _sz, _sz]
         L.oracle_encode_e4m3_at.argtypes = [_f32p, _u8p, _sz, ctypes.c_float]
+        L.oracle_e4m3_encode_sr.argtypes = [ctypes.c_float, ctypes.c_uint32]
+        L.oracle_e4m3_encode_sr.restype = ctypes.c_uint8
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_decode.restype = ctypes.c_float
         L.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
@@ -172,7 +174,7 @@ def spec_stepwise(S, T, x, B, C, dt, A, D, accepted):
 
 
 READ_FP32, READ_BF16, READ_FP8, READ_MXFP4 = 0, 1, 2, 3
-MASTER_FP32, MASTER_FP16, MASTER_FP16_SR = 0, 1, 2
+MASTER_FP32, MASTER_FP16, MASTER_FP16_SR, MASTER_FP8, MASTER_FP8_SR = 0, 1, 2, 3, 4
 
 
 class Replay:
@@ -289,6 +291,15 @@ def e4m3_encode_at(a, inv_scale=1.0):
     out = np.empty(a.shape, np.uint8)
     lib().oracle_encode_e4m3_at(a.reshape(-1), out.reshape(-1), a.size, float(inv_scale))
     return out
+
+
+def e4m3_encode_sr(a, r16):
+    """E4M3FN codes (uint8) of fp32 values already divided by their scale, rounded
+    stochastically with the 16-bit random integers r16 (reading R9)."""
+    a = _f32(a).reshape(-1)
+    r = np.asarray(r16, np.uint32).reshape(-1)
+    assert r.size == a.size
+    return np.array([lib().oracle_e4m3_encode_sr(float(x), int(y)) for x, y in zip(a, r)], np.uint8)
 
 
 def e4m3_decode_table():

@@ -56,6 +56,14 @@
  *       wider random integer gives; below 2^-17 (deep in fp16's subnormal range) fp32 keeps finer
  *       bits and the bias is below 2^-16 of a spacing. Reads and the read copy then come from the
  *       fp16 checkpoint; a flush step's output is read from the rounded checkpoint.
+ *   R9  FP8 master recurrence (the pages' FP8 alternative to the FP16 recurrence, [AT Pulse]
+ *       "Claims and evidence"): the checkpoint itself is kept as OCP E4M3FN codes with one fp32
+ *       scale per (sequence, head), in the format of the fp8 read copy (R6): scale = amax / 448
+ *       of the fold rounded to fp32 (1 if amax is 0), a = v * (1 / scale) in fp32, clamped to
+ *       +-448. A load rounds a to nearest even; a flush to nearest even (FP8) or stochastically
+ *       (FP8_SR): with q the E4M3 magnitude toward zero and ulp the code spacing above it, the
+ *       magnitude rounds up iff r16 < (|a| - q) / ulp * 2^16, with the 16-bit fields of R8's
+ *       Philox stream. The checkpoint's value is code * scale; reads come from it directly.
  *
  * Layouts (row-major, last index fastest): x [Bt,H,P]; B, C [Bt,G,N]; dt [Bt,H]; A, D [H];
  * state [Bt,H,P,N]; y [Bt,H,P]. Spec-decode inputs carry the draft index after the batch index:
@@ -205,6 +213,33 @@ uint8_t oracle_e4m3_encode_scaled(float v)
         code = (uint8_t)(((qe + 7) << 3) | m);
     }
     return (uint8_t)(code | (sign ? 0x80 : 0));
+}
+
+/* Stochastic rounding to E4M3FN of an fp32 value already divided by the scale (reading R9):   */
+/* clamp to +-448; with q the code magnitude toward zero and ulp the spacing of its binade (the   */
+/* subnormal step 2^-9 below 2^-6), round up iff r16 < (|v| - q) / ulp * 2^16 (exact in float64). */
+/* q + ulp may be the next binade's first code; the sign is kept (a negative that stays at zero  */
+/* is -0).                                                                                        */
+uint8_t oracle_e4m3_encode_sr(float v, uint32_t r16)
+{
+    double t = (double)v;
+    int neg = t < 0.0 || (t == 0.0 && signbit(t));
+    double mag = fabs(t);
+    if (mag > 448.0) mag = 448.0;
+    int e;
+    if (mag < ldexp(1.0, -6)) {
+        e = -6;
+    } else {
+        e = (int)floor(log2(mag));
+        if (ldexp(1.0, e) > mag) e -= 1;
+        if (ldexp(1.0, e + 1) <= mag) e += 1;
+    }
+    double spacing = ldexp(1.0, e - 3);
+    double q = floor(mag / spacing) * spacing;
+    double out = q;
+    if (mag > q && (double)r16 < (mag - q) / spacing * 65536.0) out = q + spacing;
+    /* out is an E4M3 magnitude: its nearest-even encoding is its own code */
+    return oracle_e4m3_encode_scaled((float)(neg ? -out : out));
 }
 
 /* Per-(sequence, head) scale for the fp8 read copy (reading R6): scale = amax / 448 in fp32,    */
@@ -440,7 +475,8 @@ void oracle_encode_f16(const float *in, uint16_t *out, size_t n, int stochastic,
 
 typedef struct oracle_replay {
     int Bt, H, P, N, G, L, Tmax, read_prec; /* 0 fp32 master, 1 bf16, 2 fp8 e4m3, 3 mxfp4 */
-    int master_prec;                        /* 0 fp32, 1 fp16 nearest even, 2 fp16 stochastic (R8) */
+    int master_prec;                        /* 0 fp32, 1 fp16 nearest even, 2 fp16 stochastic (R8),
+                                               3 fp8 nearest even, 4 fp8 stochastic (R9) */
     uint32_t seed;
     int *seq_id;                            /* [Bt] sequence index in the Philox counter */
     double *A, *D;                          /* [H] */
@@ -480,6 +516,34 @@ static void round_master(oracle_replay *r, int b, int ck, int stochastic)
 {
     const size_t n = (size_t)r->H * r->P * r->N;
     double *m = r->ckpt + (size_t)b * n;
+    if (r->master_prec >= 3) { /* fp8 (R9): per-head scale of the fold rounded to fp32 */
+        const size_t tile = (size_t)r->P * r->N;
+        float *v = (float *)malloc(tile * sizeof(float));
+        for (int h = 0; h < r->H; ++h) {
+            double *mh = m + (size_t)h * tile;
+            for (size_t i = 0; i < tile; ++i) v[i] = (float)mh[i];
+            const float scale = oracle_e4m3_scale(v, tile);
+            const float inv = 1.0f / scale;
+            for (size_t i = 0; i < tile; i += 8) {
+                const size_t e = (size_t)h * tile + i; /* element within the sequence */
+                uint32_t words[4] = {0, 0, 0, 0};
+                if (r->master_prec == 4 && stochastic) {
+                    const uint32_t ctr[4] = {(uint32_t)(e / 8), (uint32_t)r->seq_id[b], (uint32_t)ck, 0u};
+                    const uint32_t key[2] = {r->seed, 0u};
+                    oracle_philox4x32_10(ctr, key, words);
+                }
+                for (int w = 0; w < 8 && i + w < tile; ++w) {
+                    const float a = v[i + w] * inv;
+                    const uint32_t r16 = (words[w / 2] >> (16 * (w % 2))) & 0xFFFFu;
+                    const uint8_t code = (r->master_prec == 4 && stochastic) ? oracle_e4m3_encode_sr(a, r16)
+                                                                           : oracle_e4m3_encode_scaled(a);
+                    mh[i + w] = (double)oracle_e4m3_decode(code) * (double)scale;
+                }
+            }
+        }
+        free(v);
+        return;
+    }
     for (size_t e = 0; e < n; e += 8) {
         uint32_t words[4] = {0, 0, 0, 0};
         if (r->master_prec == 2 && stochastic) {
@@ -535,7 +599,8 @@ oracle_replay *oracle_replay_create(int Bt, int H, int P, int N, int G, int L, i
 {
     if (Bt < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G || L <= 0 || L > 64 ||
         Tmax <= 0 || Tmax > L || read_prec < 0 || read_prec > 3 || (read_prec == 3 && N % 32) ||
-        master_prec < 0 || master_prec > 2 || (master_prec != 0 && N % 4))
+        master_prec < 0 || master_prec > 4 || (master_prec != 0 && N % 4) || (master_prec >= 3 && N % 8) ||
+        (master_prec >= 3 && read_prec != 0))
         return NULL;
     oracle_replay *r = (oracle_replay *)calloc(1, sizeof(oracle_replay));
     r->Bt = Bt; r->H = H; r->P = P; r->N = N; r->G = G; r->L = L; r->Tmax = Tmax;

@@ -1,11 +1,11 @@
-"""Pins for the oracle's low-precision master (reading R8 of oracle.c): the Philox4x32-10 stream,
-fp16 rounding to nearest even, stochastic rounding, and the dual model that keeps the checkpoint
-in fp16.
+"""Pins for the oracle's low-precision master (readings R8 and R9 of oracle.c): the Philox4x32-10
+stream, fp16 and E4M3 rounding to nearest even and stochastically, and the dual models that keep
+the checkpoint in fp16 or in fp8.
 
 Independent references: the generator's published known-answer vectors
-(tests/golden/philox_kat.json), numpy's float16 conversion (a library routine), fp16 neighbours
-and thresholds computed with numpy.nextafter and exact fractions, and an fp32-master replay whose
-flushed checkpoint numpy rounds to fp16.
+(tests/golden/philox_kat.json), numpy's float16 and PyTorch's float8_e4m3fn conversions (library
+routines), neighbours and thresholds computed with numpy.nextafter, the library's E4M3 code table
+and exact fractions, and an fp32-master replay whose flushed checkpoint the libraries round.
 """
 import json
 import os
@@ -201,3 +201,147 @@ def test_rounding_at_flushes_only_compounds_less(master):
             errs.append(rms(r.step(*ins), y_true))
         res[L] = (rms(r.materialize(), S), float(np.mean(errs)))
     assert res[16][0] < 0.6 * res[1][0] and res[16][1] < 0.6 * res[1][1], res
+
+
+def _e4m3_values():
+    """Non-negative finite E4M3FN values, ascending, from PyTorch's float8_e4m3fn (a library
+    conversion, independent of the oracle's codec)."""
+    import torch
+    t = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    return t.astype(np.float64)
+
+
+def test_e4m3_stochastic_rounding_threshold():
+    """Reading R9 of oracle.c: the magnitude rounds up to the next E4M3 value iff r16 < T,
+    T = (|a| - q) / (next - q) * 2^16 exactly (q the E4M3 value toward zero, from the library's code table);
+    values beyond +-448 clamp to 448; representable values never change. An fp32 value keeps 20
+    bits below E4M3's spacing, so T is a multiple of 1/16 in the normal range and the mean over
+    all 2^16 values of r16 is within 2^-16 of a spacing of the value (exact where T is an
+    integer)."""
+    vals = _e4m3_values()
+    rng = np.random.default_rng(5)
+    a = (rng.standard_normal(600) * np.exp2(rng.integers(-12, 10, 600))).astype(np.float32)
+    a = np.concatenate([a, vals[rng.integers(0, len(vals), 40)].astype(np.float32),
+                        np.float32([448.0, 500.0, -1e6, 2.0 ** -9, 2.0 ** -10, 0.0])])
+    table = oracle.e4m3_decode_table().astype(np.float64)
+    n_frac = 0
+    for x in a:
+        m = min(abs(float(x)), 448.0)
+        k = int(np.searchsorted(vals, m, side="right")) - 1
+        q = vals[k]
+        sign = -1.0 if (x < 0 or (x == 0 and np.signbit(x))) else 1.0
+        if q == m:
+            rs = np.array([0, 1, 32768, 65535], np.uint32)
+            got = table[oracle.e4m3_encode_sr(np.full(4, x, np.float32), rs)]
+            assert np.all(got == sign * q), x
+            continue
+        nxt = vals[k + 1]
+        T = (Fraction(m) - Fraction(q)) / (Fraction(nxt) - Fraction(q)) * 2 ** 16
+        assert 0 < T < 2 ** 16
+        if m >= 2.0 ** -6:
+            assert (T * 16).denominator == 1, (x, T)
+        c = -(-T.numerator // T.denominator)
+        rs = np.array(sorted({0, max(c - 1, 0), min(c, 2 ** 16 - 1), min(c + 1, 2 ** 16 - 1), 2 ** 16 - 1}), np.uint32)
+        got = table[oracle.e4m3_encode_sr(np.full(len(rs), x, np.float32), rs)]
+        want = [sign * (nxt if Fraction(int(r)) < T else q) for r in rs]
+        assert np.array_equal(got, np.array(want)), (x, T)
+        mean = Fraction(c) * Fraction(nxt) + Fraction(2 ** 16 - c) * Fraction(q)    # times 2^16
+        err = abs(mean - Fraction(m) * 2 ** 16)
+        assert err < Fraction(nxt) - Fraction(q)
+        if T.denominator == 1:
+            assert err == 0
+        else:
+            n_frac += 1
+    assert n_frac > 100
+
+
+def _e4m3_nearest_per_head(S):
+    """S [Bt,H,P,N] rounded to E4M3FN per (sequence, head) by the fp8 read copy's recipe, with
+    PyTorch's float8_e4m3fn conversion for the rounding: scale = amax / 448 in fp32 (1 if 0)."""
+    import torch
+    S = np.asarray(S, np.float32)
+    amax = np.abs(S).max(axis=(2, 3), keepdims=True)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    a = np.clip(S * (np.float32(1.0) / scale), -448.0, 448.0).astype(np.float32)
+    q = torch.from_numpy(a).to(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    return q * scale.astype(np.float64), scale, a
+
+
+def test_fp8_master_dual_model():
+    """Reading R9 of oracle.c: after load the checkpoint is the nearest-even E4M3 of S0 with
+    the per-head scale; after the first flush, the nearest-even E4M3 of an fp32-master replay's checkpoint
+    started from that state; with stochastic rounding each value is its E4M3 neighbour toward
+    zero or away, chosen by the Philox field of its element as for the fp16 master. The outputs
+    stay within 0.07 of the stepwise truth's largest value (fp8's half step is 2^-4)."""
+    Bt, H, P, N, G, L = 2, 4, 16, 32, 2, 4
+    seed = 21
+    S0 = workload.initial_state(seed, Bt, H, P, N)
+    A, D = workload.layer_params(seed, H)
+    S8, _, _ = _e4m3_nearest_per_head(S0)
+    rne = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP8)
+    sr = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP8_SR, seed=77)
+    ref = oracle.Replay(S8.astype(np.float32), A, D, G, L, 1)
+    assert np.array_equal(rne.checkpoint(), S8)
+    assert np.array_equal(sr.checkpoint(), S8)
+    S = S0.astype(np.float64)
+    for t in range(L):
+        ins = workload.step_inputs(seed, t, Bt, H, P, N, G)
+        y_true = oracle.step(S, *ins, A, D)
+        for r in (rne, sr):
+            y = r.step(*ins)
+            assert np.abs(y - y_true).max() / np.abs(y_true).max() <= 0.07
+        ref.step(*ins)
+    v32 = ref.checkpoint().astype(np.float32)
+    want_rne, scale, a = _e4m3_nearest_per_head(v32)
+    assert np.array_equal(rne.checkpoint(), want_rne)
+    vals = _e4m3_values()
+    flat_a = a.reshape(Bt, -1)
+    got = (sr.checkpoint() / scale.astype(np.float64)).reshape(Bt, -1)
+    ups = 0
+    for b in range(Bt):
+        for g in range(flat_a.shape[1] // 8):
+            w = oracle.philox4x32_10([g, b, L, 0], [77, 0])
+            for i in range(8):
+                e = 8 * g + i
+                r16 = (int(w[i // 2]) >> (16 * (i % 2))) & 0xFFFF
+                m = abs(float(flat_a[b, e]))
+                k = int(np.searchsorted(vals, m, side="right")) - 1
+                q = vals[k]
+                if q == m:
+                    want = q
+                else:
+                    T = (Fraction(m) - Fraction(q)) / (Fraction(vals[k + 1]) - Fraction(q)) * 2 ** 16
+                    want = vals[k + 1] if Fraction(r16) < T else q
+                    ups += want != q
+                assert abs(got[b, e]) == want and (got[b, e] == 0 or np.sign(got[b, e]) == np.sign(flat_a[b, e])), (b, e)
+    assert ups > 100
+    assert not np.array_equal(sr.checkpoint(), rne.checkpoint())
+
+
+def test_fp8_master_stochastic_rounding_avoids_stagnation():
+    """Reading R9 of oracle.c on workload.stagnation_case with the state at 0.5 and row p = 0
+    fixed (x = 0 there) holding the anchor 1.0, so the per-head scale stays amax / 448 = 1/448 and the body
+    sits on the E4M3 value 224 (spacing 16, i.e. 1/28 of state). Each flush adds 2^-14 = 0.027
+    of a scaled unit: nearest even loses every increment, stochastic rounding keeps them in
+    expectation -- after 64 flushes the body's mean is within 10 standard deviations (binomial,
+    p = 0.027 / 16 per flush and value) of 0.5 + 64 * 2^-14."""
+    (Bt, H, P, N, G, L), S0, A, D, (x, B, C, dt) = workload.stagnation_case()
+    S0 = np.full_like(S0, 0.5)
+    S0[:, :, 0, :] = 1.0
+    x = x.copy()
+    x[:, :, 0] = 0.0
+    tok = (x, B, C, dt)
+    rne = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP8)
+    sr = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP8_SR, seed=9)
+    flushes = 64
+    for _ in range(flushes * L):
+        rne.step(*tok)
+        sr.step(*tok)
+    scale = float(np.float32(1.0) / np.float32(448.0))
+    assert np.all(rne.checkpoint()[:, :, 0, :] == 448 * scale)
+    assert np.all(rne.checkpoint()[:, :, 1:, :] == 224 * scale)
+    m = sr.checkpoint()[:, :, 1:, :]
+    truth = 0.5 + flushes * 2.0 ** -14
+    p = (2.0 ** -14 * 448) / 16
+    sd = 16 * scale * np.sqrt(flushes * p * (1 - p) / m.size)
+    assert abs(float(m.mean()) - truth) <= 10 * sd, (float(m.mean()), truth, sd)
