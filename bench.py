@@ -11,7 +11,7 @@ per launch / its mean duration from HIP events on the launch stream), the same-r
 read-update-write step, and the float64 CPU oracle timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--read-prec fp32|bf16|fp8|mxfp4]
-                  [--master-prec fp32|fp16|fp16_sr] [--no-cpu-baseline] [--kernels-only]
+                  [--master-prec fp32|fp16|fp16_sr|fp8|fp8_sr] [--no-cpu-baseline] [--kernels-only]
 """
 import argparse
 import json
@@ -49,8 +49,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--read-prec", default="fp32", choices=["fp32", "bf16", "fp8", "mxfp4"])
-    ap.add_argument("--master-prec", default="fp32", choices=["fp32", "fp16", "fp16_sr"],
-                    help="checkpoint precision: fp16 rounds to nearest even at each flush, fp16_sr "
+    ap.add_argument("--master-prec", default="fp32", choices=["fp32", "fp16", "fp16_sr", "fp8", "fp8_sr"],
+                    help="checkpoint precision: fp16 / fp8 (E4M3 codes with a per-head scale; reads "
+                         "then come from it) round to nearest even at each flush, the _sr forms "
                          "stochastically")
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--buffer-len", type=int, default=16)
@@ -91,7 +92,7 @@ def main():
     Bt, L = args.batch, args.buffer_len
     prec = args.read_prec
     mprec = args.master_prec
-    mstore = "fp32" if mprec == "fp32" else "fp16"
+    mstore = mprec.split("_")[0]                       # the master's storage: fp32, fp16 or fp8
     src = traffic.read_source(prec, mstore)            # precision the replay reads the state in
     tkey = prec if mprec == "fp32" else f"{prec}+master_{mprec}"
     seed = workload.config_seed(1)
@@ -173,7 +174,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("f32" if mprec == "fp32" else "f16") + (" master" if prec != "fp32" or mprec != "fp32" else "")
+        "dtype": {"fp32": "f32", "fp16": "f16", "fp8": "fp8 e4m3"}[mstore]
+                 + (" master" if prec != "fp32" or mprec != "fp32" else "")
                  + ("" if prec == "fp32" else f" + {prec} read copy"),
         "data": "synthetic (seeded; value distributions of the layer definition)",
         "config": {"workload": f"one Mamba-2 layer decode step, batch {Bt}, 128 heads, headdim 64, "
@@ -181,7 +183,8 @@ def main():
                                f"{prec} read path" + ("" if mprec == "fp32" else f", {mprec} master"),
                    "batch": Bt, "buffer_len": L, "read_prec": prec, "master_prec": mprec},
         "roofline": {
-            "kernel": "replay step, non-flush (step_kernel<prec, L bucket 16, rows, 0>; narrow_step_kernel for fp8 / MXFP4)",
+            "kernel": "replay step, non-flush (step_kernel<prec, L bucket 16, rows, 0>; narrow_step_kernel for fp8 / MXFP4"
+                      " reads, an fp8 master's included)",
             "bound": "hbm",
             "achieved": round(nf_gbps, 1),
             "peak": HBM_PEAK_GBPS,

@@ -27,8 +27,9 @@ RSSM_OK, RSSM_E_INVAL, RSSM_E_WORKSPACE, RSSM_E_HIP, RSSM_E_STATE, RSSM_E_UNSUPP
 READ_FP32, READ_BF16, READ_FP8_E4M3, READ_MXFP4 = 0, 1, 2, 3
 _PREC_NAMES = {"fp32": READ_FP32, "bf16": READ_BF16, "fp8": READ_FP8_E4M3, "fp8_e4m3": READ_FP8_E4M3,
                "mxfp4": READ_MXFP4, "fp4": READ_MXFP4}
-MASTER_FP32, MASTER_FP16, MASTER_FP16_SR = 0, 1, 2
-_MASTER_NAMES = {"fp32": MASTER_FP32, "fp16": MASTER_FP16, "fp16_sr": MASTER_FP16_SR}
+MASTER_FP32, MASTER_FP16, MASTER_FP16_SR, MASTER_FP8, MASTER_FP8_SR = 0, 1, 2, 3, 4
+_MASTER_NAMES = {"fp32": MASTER_FP32, "fp16": MASTER_FP16, "fp16_sr": MASTER_FP16_SR, "fp8": MASTER_FP8,
+                 "fp8_sr": MASTER_FP8_SR}
 
 EXPORTED = (
     "replayssm_workspace_bytes", "replayssm_workspace_layout", "replayssm_create", "replayssm_destroy",
@@ -478,9 +479,15 @@ class ReplaySSM:
         return self.workspace[off:off + nbytes].view(dtype).view(*shape)
 
     def master(self):
-        """The checkpoint as stored: float32, or float16 for an fp16 master."""
+        """The checkpoint as stored: float32, float16 for an fp16 master, or for an fp8 master its
+        E4M3FN codes uint8 [Bt,H,P,N] in row-major order (a reordered copy of the chunked codes;
+        the per-head scales are `scales()`)."""
+        Bt, H, P, N = self.batch, self.nheads, self.headdim, self.dstate
+        if self.cfg.master_prec in (MASTER_FP8, MASTER_FP8_SR):
+            raw = self.region("master", torch.uint8, (Bt, H, N // 16, P, 16))
+            return raw.permute(0, 1, 3, 2, 4).contiguous().view(Bt, H, P, N)
         dt = torch.float32 if self.cfg.master_prec == MASTER_FP32 else torch.float16
-        return self.region("master", dt, (self.batch, self.nheads, self.headdim, self.dstate))
+        return self.region("master", dt, (Bt, H, P, N))
 
     def read_copy(self):
         """The read copy in row-major order: bf16 bits int16 [Bt,H,P,N], fp8 codes uint8
@@ -497,7 +504,8 @@ class ReplaySSM:
         return None
 
     def scales(self):
-        """fp8: fp32 per-head scales [Bt,H]; MXFP4: E8M0 block-scale bytes [Bt,H,P,N/32]."""
+        """fp8 copy or fp8 master: fp32 per-head scales [Bt,H]; MXFP4: E8M0 block-scale bytes
+        [Bt,H,P,N/32]."""
         if self.cfg.read_prec == READ_MXFP4:
             return self.region("scale", torch.uint8, (self.batch, self.nheads, self.headdim, self.dstate // 32))
         return self.region("scale", torch.float32, (self.batch, self.nheads))

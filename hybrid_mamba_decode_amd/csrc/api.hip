@@ -61,7 +61,11 @@ rssm_status check_config(const replayssm_config *c)
     if (c->buffer_len > 64 || c->max_draft > 8) return RSSM_E_UNSUPPORTED;
     if (c->read_prec == RSSM_READ_FP8_E4M3 && c->headdim > kRows) return RSSM_E_UNSUPPORTED;
     if (c->read_prec == RSSM_READ_MXFP4 && c->dstate < 32) return RSSM_E_UNSUPPORTED;
-    if (c->master_prec < RSSM_MASTER_FP32 || c->master_prec > RSSM_MASTER_FP16_SR) return RSSM_E_INVAL;
+    if (c->master_prec < RSSM_MASTER_FP32 || c->master_prec > RSSM_MASTER_FP8_SR) return RSSM_E_INVAL;
+    // an fp8 master is its own read copy: no second copy; the head's amax needs its P rows in one
+    // work-group, as the fp8 copy does
+    if (c->master_prec >= RSSM_MASTER_FP8 && c->read_prec != RSSM_READ_FP32) return RSSM_E_INVAL;
+    if (c->master_prec >= RSSM_MASTER_FP8 && c->headdim > kRows) return RSSM_E_UNSUPPORTED;
     if (c->d_conv < 0 || c->d_conv == 1) return RSSM_E_INVAL;
     if (c->d_conv > 4 || (c->d_conv > 0 && c->buffer_len > 32)) return RSSM_E_UNSUPPORTED;
     return RSSM_OK;
@@ -71,9 +75,16 @@ rssm_status check_config(const replayssm_config *c)
 size_t conv_dim(const replayssm_config &c) { return (size_t)c.nheads * c.headdim + 2 * (size_t)c.ngroups * c.dstate; }
 int conv_slots(const replayssm_config &c) { return c.d_conv > 0 ? c.d_conv - 1 + c.max_draft : 0; }
 
-// Read precision of the kernels: the copy's, or the fp16 master read directly.
+bool fp8_master(const replayssm_config &c) { return c.master_prec >= RSSM_MASTER_FP8; }
+bool sr_master(const replayssm_config &c)
+{
+    return c.master_prec == RSSM_MASTER_FP16_SR || c.master_prec == RSSM_MASTER_FP8_SR;
+}
+
+// Read precision of the kernels: the copy's, or the fp16 / fp8 master read directly.
 int kernel_prec(const replayssm_config &c)
 {
+    if (fp8_master(c)) return PREC_FP8;
     return c.read_prec == RSSM_READ_FP32 && c.master_prec != RSSM_MASTER_FP32 ? PREC_F16 : c.read_prec;
 }
 
@@ -84,9 +95,11 @@ void make_layout(const replayssm_config &c, replayssm_layout *L)
     const size_t elems = Bt * H * P * N;
     RegionCarver rc;
     auto take = [&](size_t bytes) { return rc.take(bytes); };
-    L->master = take(elems * (c.master_prec == RSSM_MASTER_FP32 ? 4 : 2));
-    const int rp = c.read_prec;
-    L->read_copy = take(rp == RSSM_READ_BF16 ? elems * 2 : rp == RSSM_READ_FP8_E4M3 ? elems
+    // an fp8 master takes the fp8 copy's layout (chunked codes) in the master region and its
+    // per-head scales in the scale region
+    L->master = take(elems * (c.master_prec == RSSM_MASTER_FP32 ? 4 : fp8_master(c) ? 1 : 2));
+    const int rp = fp8_master(c) ? RSSM_READ_FP8_E4M3 : c.read_prec;
+    L->read_copy = take(fp8_master(c) ? 0 : rp == RSSM_READ_BF16 ? elems * 2 : rp == RSSM_READ_FP8_E4M3 ? elems
                         : rp == RSSM_READ_MXFP4 ? elems / 2 : 0);
     L->scale = take(rp == RSSM_READ_FP8_E4M3 ? Bt * H * 4 : rp == RSSM_READ_MXFP4 ? elems / 32 : 0);
     L->ring_x = take(Bt * H * Lb * P * 4);
@@ -218,8 +231,9 @@ rssm_status replayssm_create(const replayssm_config *cfg, void *workspace, size_
     char *ws = (char *)workspace;
     Layer &d = h->dev;
     d.master = (float *)(ws + lay.master);
-    d.rcopy = cfg->read_prec == RSSM_READ_FP32 ? nullptr : (void *)(ws + lay.read_copy);
-    d.scale = cfg->read_prec == RSSM_READ_FP8_E4M3 ? (float *)(ws + lay.scale) : nullptr;
+    d.rcopy = fp8_master(*cfg) ? (void *)(ws + lay.master)
+              : cfg->read_prec == RSSM_READ_FP32 ? nullptr : (void *)(ws + lay.read_copy);
+    d.scale = cfg->read_prec == RSSM_READ_FP8_E4M3 || fp8_master(*cfg) ? (float *)(ws + lay.scale) : nullptr;
     d.mxscale = cfg->read_prec == RSSM_READ_MXFP4 ? (unsigned char *)(ws + lay.scale) : nullptr;
     d.ring_x = (float *)(ws + lay.ring_x);
     d.ring_B = (float *)(ws + lay.ring_B);
@@ -261,7 +275,7 @@ rssm_status replayssm_load_state(replayssm_t h, const float *state, void *stream
     if (!h) return RSSM_E_INVAL;
     if (!ok_ptr(state, h->cfg.batch)) return RSSM_E_INVAL;
     // a stochastically rounded master keys its stream by each sequence's device ckpt_pos
-    h->hs.on_load(h->cfg.master_prec != RSSM_MASTER_FP16_SR);
+    h->hs.on_load(!sr_master(h->cfg));
     if (h->cfg.batch == 0) return RSSM_OK;
     const hipStream_t st = (hipStream_t)stream;
     rssm_status s = RSSM_OK;

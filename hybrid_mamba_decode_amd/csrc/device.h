@@ -28,8 +28,9 @@ constexpr int kRows = 64;
 // Read precisions of the replay kernels. PREC_F16 reads an fp16 master directly (no copy).
 enum { PREC_F32 = 0, PREC_BF16 = 1, PREC_FP8 = 2, PREC_FP4 = 3, PREC_F16 = 4 };
 
-// Master (checkpoint) precisions: fp32, or fp16 rounded to nearest even / stochastically.
-enum { MASTER_F32 = 0, MASTER_F16 = 1, MASTER_F16_SR = 2 };
+// Master (checkpoint) precisions: fp32, fp16 or fp8 (E4M3FN codes with a per-head scale, kept in
+// the fp8 read copy's place), the narrow ones rounded to nearest even / stochastically.
+enum { MASTER_F32 = 0, MASTER_F16 = 1, MASTER_F16_SR = 2, MASTER_F8 = 3, MASTER_F8_SR = 4 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -301,6 +302,22 @@ __device__ inline unsigned short f16_sr(float v, unsigned r16)
         if ((float)r16 < (a - q) * (65536.0f / ulp)) h = (unsigned short)(h + 1);
     }
     return (unsigned short)(h | (__float_as_uint(v) >> 31 << 15));
+}
+
+// Stochastic rounding of a (already divided by the scale and clamped to +-448) onto the E4M3FN
+// grid, with the same 16-bit rule: up iff r16 < (|a| - q) / ulp * 2^16. Returns the chosen E4M3
+// value as fp32 (the converter then encodes it exactly). For |a| >= 2^-6 the spacing is 2^20
+// fp32 spacings of a, so the rule reads (r16 << 4) < low20 and one carry into bit 20 decides it;
+// below, the spacing is 2^-9 and a * 2^9 splits exactly into its floor and fraction.
+__device__ inline float e4m3_sr(float a, unsigned r16)
+{
+    const unsigned u = __float_as_uint(a), sgn = u & 0x80000000u, m = u & 0x7FFFFFFFu;
+    if (m >= 0x3C800000u)  // 2^-6
+        return __uint_as_float(((m + (0xFFFFFu - (r16 << 4))) & ~0xFFFFFu) | sgn);
+    const float t = __uint_as_float(m) * 512.0f;
+    const float fl = floorf(t);
+    const float q = (float)r16 < (t - fl) * 65536.0f ? fl + 1.0f : fl;
+    return __uint_as_float(__float_as_uint(q * (1.0f / 512.0f)) | sgn);
 }
 
 struct U32x4 {

@@ -383,11 +383,29 @@ __device__ inline void store_rows_f32(float *rows, const f32x4 (&vf)[GF::NL], in
     }
 }
 
-// Master rows in f32 geometry: fp32 16-byte loads, or fp16 8-byte loads converted exactly.
+// Master rows in f32 geometry: fp32 16-byte loads, fp16 8-byte loads converted exactly, or fp8
+// codes (4 per lane and row, from the head's 16-byte chunks) decoded and times the head's scale.
 __device__ inline void load_master_rows(const Layer &Ld, size_t elem0, f32x4 (&vf)[GF::NL], int nrows, int wave,
                                         int lane)
 {
     const int c = lane % GF::LPR;
+    if (Ld.mprec >= MASTER_F8) {
+        const size_t bh = elem0 / ((size_t)Ld.P * NN);
+        const int row0 = (int)(elem0 / NN - bh * (size_t)Ld.P);
+        const unsigned char *src = (const unsigned char *)Ld.rcopy;
+        const float scale = Ld.scale[bh];
+        const int n = 4 * c;
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            const int r = row_of<PREC_F32>(i, wave, lane), rr = r < nrows ? r : 0;
+            const unsigned w = __builtin_nontemporal_load(
+                (const unsigned *)(src + chunk_off<PREC_FP8>(bh, row0 + rr, n / 16, Ld.P) + n % 16));
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+            vf[i] = f32x4{lo.x * scale, lo.y * scale, hi.x * scale, hi.y * scale};
+        }
+        return;
+    }
     if (Ld.mprec == MASTER_F32) {
         u32x4 m[GF::NL];
         load_rows<PREC_F32>(m, (const char *)(Ld.master + elem0), nrows, wave, lane);
@@ -447,6 +465,76 @@ __device__ inline void store_master_rows(const Layer &Ld, int b, size_t elem0, i
         }
     }
 }
+
+// Store a head's folded fp32 rows vf into an fp8 master (the fp8 read copy's format): the head's
+// amax over the work-group (which owns all P rows), scale = amax / 448 (1 if 0), a = v * (1 /
+// scale) clamped to +-448, coded to nearest even -- or, when `stochastic`, by e4m3_sr with the
+// 16-bit Philox fields of the fp16 master (counter (e / 8, sequence b, newck, 0)). vf receives
+// code * scale, the values the checkpoint now holds; there is no separate read copy to refresh.
+__device__ inline void store_master_fp8_rows(const Layer &Ld, int b, size_t bh, size_t elem0, int newck,
+                                             bool stochastic, f32x4 (&vf)[GF::NL], int nrows, int wave, int lane,
+                                             float *red)
+{
+    const int c = lane % GF::LPR;
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < GF::NL; ++i) {
+        const f32x4 f = vf[i];
+        const float m = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
+        if (row_of<PREC_F32>(i, wave, lane) < nrows) amax = fmaxf(amax, m);
+    }
+    amax = block_max(amax, red);
+    const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
+    const float inv = 1.0f / scale;
+    unsigned char *dst = (unsigned char *)Ld.rcopy;
+    const int row0 = (int)(elem0 / NN - bh * (size_t)Ld.P);
+    const size_t seq0 = (size_t)b * Ld.H * Ld.P * NN;
+    const int n = 4 * c;
+#pragma unroll
+    for (int i = 0; i < GF::NL; ++i) {
+        const int r = row_of<PREC_F32>(i, wave, lane);
+        const f32x4 f = vf[i];
+        float a0 = fminf(fmaxf(f.x * inv, -448.0f), 448.0f);
+        float a1 = fminf(fmaxf(f.y * inv, -448.0f), 448.0f);
+        float a2 = fminf(fmaxf(f.z * inv, -448.0f), 448.0f);
+        float a3 = fminf(fmaxf(f.w * inv, -448.0f), 448.0f);
+        if (stochastic) {
+            // the lane's four elements are one half of an 8-element Philox group (as for fp16)
+            const size_t e = elem0 - seq0 + (size_t)r * NN + n;
+            const U32x4 rnd = philox4x32_10((unsigned)(e / 8), (unsigned)b, (unsigned)newck, 0u, Ld.sr_seed, 0u);
+            const unsigned w0 = (e & 4) ? rnd.z : rnd.x, w1 = (e & 4) ? rnd.w : rnd.y;
+            a0 = e4m3_sr(a0, w0 & 0xFFFFu);
+            a1 = e4m3_sr(a1, w0 >> 16);
+            a2 = e4m3_sr(a2, w1 & 0xFFFFu);
+            a3 = e4m3_sr(a3, w1 >> 16);
+        }
+        int q = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+        q = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, q, true);
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(q, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(q, true);
+        vf[i] = f32x4{lo.x * scale, lo.y * scale, hi.x * scale, hi.y * scale};
+        if (r < nrows) *(unsigned *)(dst + chunk_off<PREC_FP8>(bh, row0 + r, n / 16, Ld.P) + n % 16) = (unsigned)q;
+    }
+    if (threadIdx.x == 0) Ld.scale[bh] = scale;
+}
+
+// Commit a head's folded rows: store them at the master's precision (vf then holds the stored
+// values) and refresh the read copy from them -- or, with an fp8 master, which is its own read
+// copy, encode them once.
+template <int PREC>
+__device__ inline void commit_rows(const Layer &Ld, int b, size_t bh, size_t elem0, int newck, bool stochastic,
+                                   f32x4 (&vf)[GF::NL], int nrows, int wave, int lane, float *red)
+{
+    if constexpr (PREC == PREC_FP8)
+        if (Ld.mprec >= MASTER_F8) {
+            store_master_fp8_rows(Ld, b, bh, elem0, newck, stochastic, vf, nrows, wave, lane, red);
+            return;
+        }
+    store_master_rows(Ld, b, elem0, newck, stochastic, vf, nrows, wave, lane);
+    write_copy_rows<PREC>(Ld, bh, elem0, vf, nrows, wave, lane, red);
+}
+
+__device__ inline bool sr_master(const Layer &Ld) { return Ld.mprec == MASTER_F16_SR || Ld.mprec == MASTER_F8_SR; }
 
 // Append one record (LDS row j of the window, C from Cq) into ring slot `slot`. The head's x
 // rows and dt are written by each (sequence, head) work-group (dt by split 0 only); B and C by
@@ -815,8 +903,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
                 load_master_rows(Ld, elem0, vf, t.nrows, wave, lane);
             }
             fold_head<LMAX, ROWS>(vf, s.xw, s.Bw, s.w[hh], s.decay[hh], hh * kRows, k, wave, lane);
-            store_master_rows(Ld, t.b, elem0, dpos + 1, Ld.mprec == MASTER_F16_SR, vf, t.nrows, wave, lane);
-            write_copy_rows<PREC>(Ld, bh0 + hh, elem0, vf, t.nrows, wave, lane, s.red);
+            commit_rows<PREC>(Ld, t.b, bh0 + hh, elem0, dpos + 1, sr_master(Ld), vf, t.nrows, wave, lane, s.red);
             float part[GF::NL];
 #pragma unroll
             for (int i = 0; i < GF::NL; ++i) part[i] = chunk_dot<PREC_F32>(as_u32x4(vf[i]), cf);
@@ -1530,8 +1617,7 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(Layer Ld, int mode, con
         if (mode == MODE_MATERIALIZE) {
             store_rows_f32(out + elem0, vf, t.nrows, wave, lane);
         } else {
-            store_master_rows(Ld, t.b, elem0, pos, Ld.mprec == MASTER_F16_SR, vf, t.nrows, wave, lane);
-            write_copy_rows<PREC>(Ld, bh, elem0, vf, t.nrows, wave, lane, s.red);
+            commit_rows<PREC>(Ld, t.b, bh, elem0, pos, sr_master(Ld), vf, t.nrows, wave, lane, s.red);
         }
     }
     if (mode != MODE_MATERIALIZE) seq_done(Ld, t.b, pos, pos);
@@ -1773,8 +1859,7 @@ __global__ void __launch_bounds__(kThreads) load_state_kernel(Layer Ld, const fl
     f32x4 vf[GF::NL];
 #pragma unroll
     for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(m[i]);
-    store_master_rows(Ld, t.b, elem0, 0, false, vf, t.nrows, wave, lane);  // fp16: nearest even at load
-    write_copy_rows<PREC>(Ld, bh, elem0, vf, t.nrows, wave, lane, red);
+    commit_rows<PREC>(Ld, t.b, bh, elem0, 0, false, vf, t.nrows, wave, lane, red);  // nearest even at load
     if (t.h == 0 && t.split == 0 && threadIdx.x == 0) {
         Ld.pos[t.b] = 0;
         Ld.ckpt[t.b] = 0;
@@ -1979,7 +2064,8 @@ hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, bool a
     if (flush_capable) {
         // fp16 master, every sequence flushes: the fold on MFMA, one work-group per head
         if constexpr (!MIX && NN >= 32)
-            if (all_flush && Ld.mprec != MASTER_F32 && Ld.psplit == 1 && (Ld.mprec != MASTER_F16_SR || ls.k == 0)) {
+            if (all_flush && (Ld.mprec == MASTER_F16 || Ld.mprec == MASTER_F16_SR) && Ld.psplit == 1 &&
+                (Ld.mprec != MASTER_F16_SR || ls.k == 0)) {
                 if (Ld.mprec == MASTER_F16_SR)
                     hipLaunchKernelGGL((lp_flush_step_kernel<PREC, LMAX, true>), dim3(nblocks(Ld)), dim3(kThreads), 0,
                                        st, Ld, io, ls);
@@ -1990,7 +2076,7 @@ hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, bool a
             }
         // fp16 master: two heads per work-group with the master rows issued early (see step_kernel)
         if constexpr (LMAX <= 32)
-            if (Ld.mprec != MASTER_F32 && Ld.psplit == 1 && Ld.hpg % 2 == 0)
+            if ((Ld.mprec == MASTER_F16 || Ld.mprec == MASTER_F16_SR) && Ld.psplit == 1 && Ld.hpg % 2 == 0)
                 return step_rows<PREC, LMAX, 2 * kRows, true, MIX>(Ld, io, ls, st);
         // lockstep flush step, fp32 master, narrow copy: every sequence flushes
         if constexpr (PREC == PREC_BF16 || PREC == PREC_FP8 || PREC == PREC_FP4)

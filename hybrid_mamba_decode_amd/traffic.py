@@ -7,7 +7,8 @@ and the per-head fp8 scales of a read are tiny and are counted where they are pa
 
 Shapes: H heads, P headdim, N state, G groups; `k` = records in the window including the current
 token (1..L). `prec` is the precision reads come from (the read copy's, or the master's when reads
-use no copy) and `master` the checkpoint's own ("fp32" or "fp16").
+use no copy) and `master` the checkpoint's own ("fp32", "fp16", or "fp8": E4M3 codes with their
+per-head scales, which reads then use directly).
 """
 
 F32 = 4

@@ -98,8 +98,28 @@ typedef enum {
  *            13 bits below the fp16 spacing), within 2^-16 of a spacing below 2^-17; deterministic
  *            for a given seed. Standard steps use the device pointers (the lockstep fast path is
  *            off) so that every flush knows its ckpt_pos.
- * The stored layout stays [Bt,H,P,N]; RSSM_E_INVAL for a value outside 0..2. */
-typedef enum { RSSM_MASTER_FP32 = 0, RSSM_MASTER_FP16 = 1, RSSM_MASTER_FP16_SR = 2 } rssm_master_prec;
+ *   FP8      ([AT Pulse] "Claims and evidence" names FP8 beside FP16 for the recurrence) the
+ *            checkpoint is kept in the FP8_E4M3 read copy's own format: E4M3FN codes with one
+ *            fp32 scale per (sequence, head), scale = amax / 448 of the folded values (1 if 0),
+ *            codes of value * (1 / scale) clamped to +-448, rounded to nearest even at load and at
+ *            every flush. Its value is code * scale; reads come from it directly, so read_prec must
+ *            be FP32 (RSSM_E_INVAL otherwise: there is no second copy) and headdim <= 64
+ *            (RSSM_E_UNSUPPORTED otherwise, as for the fp8 copy).
+ *   FP8_SR   as FP8 at load; at every flush the scaled value rounds stochastically on the E4M3
+ *            grid by FP16_SR's rule and Philox fields (q the E4M3 magnitude toward zero, ulp the
+ *            code spacing above it, 2^-9 below 2^-6): an fp32 value keeps 20 bits below E4M3's
+ *            spacing, so the mean over r is within 2^-16 of a spacing of the value. Lockstep off
+ *            as for FP16_SR.
+ * The fp32 and fp16 layouts are [Bt,H,P,N]; an fp8 master's codes take the fp8 copy's chunked
+ * layout (see replayssm_layout.read_copy) in the master region, its scales the scale region.
+ * RSSM_E_INVAL for a value outside 0..4. */
+typedef enum {
+    RSSM_MASTER_FP32 = 0,
+    RSSM_MASTER_FP16 = 1,
+    RSSM_MASTER_FP16_SR = 2,
+    RSSM_MASTER_FP8 = 3,
+    RSSM_MASTER_FP8_SR = 4
+} rssm_master_prec;
 
 typedef struct {
     int32_t batch;       /* Bt >= 0 (0: every call is a no-op) */
@@ -112,20 +132,22 @@ typedef struct {
     int32_t read_prec;   /* rssm_read_prec: precision of the checkpoint copy that serves reads */
     int32_t store_C;     /* 1: records also keep C (the record is (x, B, C, dt)); 0: (x, B, dt) */
     int32_t master_prec; /* rssm_master_prec: precision of the checkpoint itself */
-    int32_t sr_seed;     /* key of the stochastic-rounding stream (RSSM_MASTER_FP16_SR) */
+    int32_t sr_seed;     /* key of the stochastic-rounding stream (RSSM_MASTER_FP16_SR, FP8_SR) */
     int32_t d_conv;      /* K: 0 = plain step inputs; 2..4 = the mixer edges are fused in (see
                             replayssm_mixer_step; requires buffer_len <= 32) */
 } replayssm_config;
 
 /* Byte offsets of the workspace regions (for inspection by tests and tools). */
 typedef struct {
-    size_t master;     /* checkpoint [Bt,H,P,N], fp32 or fp16 (master_prec) -- updated only by flushes */
+    size_t master;     /* checkpoint [Bt,H,P,N], fp32 or fp16 (master_prec), or fp8 codes in the
+                          read copy's chunked layout -- updated only by flushes */
     size_t read_copy;  /* bf16 [Bt,H,P,N] row-major; fp8 e4m3fn codes or MXFP4 code bytes in
                           16-byte chunks (16 fp8 / 32 fp4 values of one row), per head ordered
                           [N/VEC][P]: chunk q of row p of head (b,h) at byte offset
                           ((b*H + h)*P*N*s) + (q*P + p)*16, s = 1 (fp8) or 1/2 (fp4);
                           0 bytes for fp32 reads */
-    size_t scale;      /* fp8: fp32 [Bt,H] per-head scales; MXFP4: E8M0 bytes [Bt,H,P,N/32];
+    size_t scale;      /* fp8 copy or fp8 master: fp32 [Bt,H] per-head scales; MXFP4: E8M0 bytes
+                          [Bt,H,P,N/32];
                           0 bytes otherwise */
     size_t ring_x;     /* fp32 [Bt,H,L,P]: record of absolute position q sits in slot q mod L */
     size_t ring_B;     /* fp32 [Bt,G,L,N] */

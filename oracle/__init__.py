@@ -103,6 +103,10 @@ def lib():
         L.oracle_replay_flush.restype = _i
         L.oracle_replay_set_checkpoint.argtypes = [ctypes.c_void_p, _f32p, ctypes.c_void_p, _i]
         L.oracle_replay_set_checkpoint.restype = _i
+        L.oracle_replay_master_fp8.argtypes = [ctypes.c_void_p, _u8p, _f32p]
+        L.oracle_replay_master_fp8.restype = _i
+        L.oracle_replay_set_master_fp8.argtypes = [ctypes.c_void_p, _u8p, _f32p, ctypes.c_void_p, _i]
+        L.oracle_replay_set_master_fp8.restype = _i
         L.oracle_replay_pointers.argtypes = [ctypes.c_void_p, _i32p, _i32p]
         L.oracle_replay_checkpoint.argtypes = [ctypes.c_void_p, _f64p]
         L.oracle_replay_read_copy.argtypes = [ctypes.c_void_p, _f64p]
@@ -243,6 +247,28 @@ class Replay:
             rc = lib().oracle_replay_set_checkpoint(self._h, S, idx.ctypes.data_as(ctypes.c_void_p), n)
         if rc != 0:
             raise RuntimeError("oracle replay: set_checkpoint while a verify is pending, or a bad row")
+
+    def fp8_master(self):
+        """fp8 master (reading R9): E4M3FN codes uint8 [Bt,H,P,N] and fp32 scales [Bt,H]."""
+        codes = np.empty((self.Bt, self.H, self.P, self.N), np.uint8)
+        scales = np.empty((self.Bt, self.H), np.float32)
+        if lib().oracle_replay_master_fp8(self._h, codes, scales) != 0:
+            raise RuntimeError("oracle replay: not an fp8 master")
+        return codes, scales
+
+    def set_master_fp8(self, codes, scales, rows=None):
+        """fp8 master: continue from codes [n,H,P,N] times scales [n,H] (exact), for every
+        sequence or for the sequences listed in rows (records and pointers stay)."""
+        n = self.Bt if rows is None else len(rows)
+        codes = np.ascontiguousarray(codes, np.uint8)
+        scales = _f32(scales)
+        if codes.shape != (n, self.H, self.P, self.N) or scales.shape != (n, self.H):
+            raise ValueError("fp8 master shape mismatch")
+        idx = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+        rc = lib().oracle_replay_set_master_fp8(self._h, codes, scales,
+                                                None if idx is None else idx.ctypes.data_as(ctypes.c_void_p), n)
+        if rc != 0:
+            raise RuntimeError("oracle replay: set_master_fp8 while a verify is pending, a bad row, or not fp8")
 
     def pointers(self):
         pos = np.empty(self.Bt, np.int32)

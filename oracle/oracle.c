@@ -475,6 +475,7 @@ void oracle_encode_f16(const float *in, uint16_t *out, size_t n, int stochastic,
 
 typedef struct oracle_replay {
     int Bt, H, P, N, G, L, Tmax, read_prec; /* 0 fp32 master, 1 bf16, 2 fp8 e4m3, 3 mxfp4 */
+    float *mscale;                          /* fp8 master: per-(sequence, head) scale [Bt,H] */
     int master_prec;                        /* 0 fp32, 1 fp16 nearest even, 2 fp16 stochastic (R8),
                                                3 fp8 nearest even, 4 fp8 stochastic (R9) */
     uint32_t seed;
@@ -524,6 +525,7 @@ static void round_master(oracle_replay *r, int b, int ck, int stochastic)
             for (size_t i = 0; i < tile; ++i) v[i] = (float)mh[i];
             const float scale = oracle_e4m3_scale(v, tile);
             const float inv = 1.0f / scale;
+            r->mscale[(size_t)b * r->H + h] = scale;
             for (size_t i = 0; i < tile; i += 8) {
                 const size_t e = (size_t)h * tile + i; /* element within the sequence */
                 uint32_t words[4] = {0, 0, 0, 0};
@@ -612,6 +614,7 @@ oracle_replay *oracle_replay_create(int Bt, int H, int P, int N, int G, int L, i
     r->D = (double *)malloc(H * sizeof(double));
     for (int h = 0; h < H; ++h) { r->A[h] = A[h]; r->D[h] = D[h]; }
     r->ckpt = (double *)malloc((st ? st : 1) * sizeof(double));
+    r->mscale = (float *)calloc((size_t)Bt * H + 1, sizeof(float));
     for (size_t i = 0; i < st; ++i) r->ckpt[i] = (double)S0[i];
     r->rcopy = read_prec ? (double *)malloc((st ? st : 1) * sizeof(double)) : NULL;
     r->rx = (float *)malloc(((size_t)Bt * L * H * P + 1) * sizeof(float));
@@ -637,6 +640,7 @@ void oracle_replay_destroy(oracle_replay *r)
 {
     if (!r) return;
     free(r->seq_id);
+    free(r->mscale);
     free(r->A); free(r->D); free(r->ckpt); free(r->rcopy);
     free(r->rx); free(r->rB); free(r->rC); free(r->rdt); free(r->pos); free(r->ckpt_pos);
     free(r);
@@ -838,6 +842,46 @@ int oracle_replay_set_checkpoint(oracle_replay *r, const float *S, const int *ro
         const int b = rows ? rows[i] : i;
         for (size_t e = 0; e < seq; ++e) r->ckpt[(size_t)b * seq + e] = (double)S[(size_t)i * seq + e];
         refresh_copy(r, b);
+    }
+    return 0;
+}
+
+/* fp8 master (reading R9): export E4M3FN codes [Bt,H,P,N] and scales [Bt,H] -- each value is    */
+/* code * scale exactly, so its code is the nearest-even code of value / scale. -1 otherwise.     */
+int oracle_replay_master_fp8(const oracle_replay *r, uint8_t *codes, float *scales)
+{
+    if (r->master_prec < 3) return -1;
+    const size_t tile = (size_t)r->P * r->N;
+    for (size_t bh = 0; bh < (size_t)r->Bt * r->H; ++bh) {
+        const float s = r->mscale[bh];
+        scales[bh] = s;
+        for (size_t i = 0; i < tile; ++i)
+            codes[bh * tile + i] = oracle_e4m3_encode_scaled((float)(r->ckpt[bh * tile + i] / (double)s));
+    }
+    return 0;
+}
+
+/* fp8 master: set the checkpoints of sequences rows[0..nrows) (all when rows is NULL) to     */
+/* codes [nrows,H,P,N] times scales [nrows,H], exactly in float64; records and pointers stay. */
+/* A test continues the model from the GPU's own fp8 master this way. -1 while a verify is    */
+/* pending, for a row out of range, or for another master precision.                         */
+int oracle_replay_set_master_fp8(oracle_replay *r, const uint8_t *codes, const float *scales, const int *rows,
+                                 int nrows)
+{
+    if (r->pending_T || r->master_prec < 3) return -1;
+    if (!rows) nrows = r->Bt;
+    for (int i = 0; i < nrows; ++i)
+        if (rows && (rows[i] < 0 || rows[i] >= r->Bt)) return -1;
+    const size_t tile = (size_t)r->P * r->N;
+    for (int i = 0; i < nrows; ++i) {
+        const int b = rows ? rows[i] : i;
+        for (int h = 0; h < r->H; ++h) {
+            const float s = scales[(size_t)i * r->H + h];
+            r->mscale[(size_t)b * r->H + h] = s;
+            for (size_t e = 0; e < tile; ++e)
+                r->ckpt[((size_t)b * r->H + h) * tile + e] =
+                    (double)oracle_e4m3_decode(codes[((size_t)i * r->H + h) * tile + e]) * (double)s;
+        }
     }
     return 0;
 }

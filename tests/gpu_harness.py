@@ -8,7 +8,60 @@ import workload
 
 PREC_CODE = {"fp32": oracle.READ_FP32, "bf16": oracle.READ_BF16, "fp8": oracle.READ_FP8,
              "mxfp4": oracle.READ_MXFP4}
-MASTER_CODE = {"fp32": oracle.MASTER_FP32, "fp16": oracle.MASTER_FP16, "fp16_sr": oracle.MASTER_FP16_SR}
+MASTER_CODE = {"fp32": oracle.MASTER_FP32, "fp16": oracle.MASTER_FP16, "fp16_sr": oracle.MASTER_FP16_SR,
+               "fp8": oracle.MASTER_FP8, "fp8_sr": oracle.MASTER_FP8_SR}
+
+
+def fp8_master(lay, sample):
+    """An fp8 master's E4M3FN codes [n,H,P,N] and per-head scales [n,H] of the sampled rows."""
+    idx = torch.as_tensor(np.asarray(sample), device="cuda")
+    return host(lay.master()[idx]), host(lay.scales()[idx])
+
+
+def master_values(lay, master, sample):
+    """The sampled rows of the stored checkpoint as float64 values (fp8: code * scale, exact)."""
+    if master in ("fp8", "fp8_sr"):
+        codes, scales = fp8_master(lay, sample)
+        return oracle.e4m3_decode_table().astype(np.float64)[codes] * scales[:, :, None, None].astype(np.float64)
+    idx = torch.as_tensor(np.asarray(sample), device="cuda")
+    return host(lay.master()[idx]).astype(np.float64)
+
+
+def reseed(rep, lay, master, sample, rows=None):
+    """Continue the oracle's replay model rep from the GPU's own stored checkpoint: every sampled
+    row, or the model rows `rows` (indices into sample)."""
+    sel = np.asarray(sample) if rows is None else np.asarray(sample)[rows]
+    if master in ("fp8", "fp8_sr"):
+        codes, scales = fp8_master(lay, sel)
+        rep.set_master_fp8(codes, scales, rows)
+    else:
+        idx = torch.as_tensor(sel, device="cuda")
+        rep.set_checkpoint(host(lay.master()[idx]).astype(np.float32), rows)
+
+
+def _e4m3_order(codes):
+    c = np.asarray(codes, np.int64)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def check_fp8_flush(lay, rep, sample, what, rows=None):
+    """An fp8 master after a flush vs the model's fold of the same checkpoint and records: scales
+    within 2^-20 relative (the two folds of a head's largest value may differ in their last
+    bits), at most 1e-3 of the codes differ, each by one step of the E4M3 grid. Returns the
+    fraction of differing codes."""
+    sel = np.asarray(sample) if rows is None else np.asarray(sample)[rows]
+    codes, scales = fp8_master(lay, sel)
+    mc, ms = rep.fp8_master()
+    if rows is not None:
+        mc, ms = mc[rows], ms[rows]
+    assert np.all(np.abs(scales.astype(np.float64) / ms - 1.0) <= 2.0 ** -20), f"{what}: fp8 master scales"
+    diff = codes != mc
+    flips = float(np.mean(diff))
+    assert flips <= 1e-3, f"{what}: {flips:.2e} of the fp8 master codes differ from the model's"
+    if diff.any():
+        gap = np.abs(_e4m3_order(codes[diff]) - _e4m3_order(mc[diff]))
+        assert int(gap.max()) <= 1, f"{what}: fp8 codes {int(gap.max())} steps apart"
+    return flips
 
 def assert_copy_encodes(lay, prec, m, sample, what=""):
     """The layer's read copy of the sampled sequences is, bit for bit, the oracle's encoder (O7)

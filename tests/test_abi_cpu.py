@@ -66,6 +66,11 @@ def test_workspace_layout_serving_shape():
     assert lh.read_copy - lh.master == Bt * H * P * N * 2          # fp16 master
     assert lh.scale - lh.read_copy == Bt * H * P * N * 2
     assert lh.total < lb.total + Bt * H * P * N * 4
+    for m in ("fp8", "fp8_sr"):                                     # fp8 master: its own read copy
+        l8m = rs.replayssm_workspace_layout(cfg(batch=256, master_prec=m))
+        assert l8m.read_copy - l8m.master == Bt * H * P * N           # one code byte per value
+        assert l8m.scale == l8m.read_copy                             # no second copy
+        assert l8m.ring_x - l8m.scale == Bt * H * 4                   # fp32 per-head scales
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -83,7 +88,10 @@ def test_workspace_layout_serving_shape():
     (dict(read_prec="mxfp4", dstate=16), rs.RSSM_E_UNSUPPORTED),
     (dict(batch=-1), rs.RSSM_E_INVAL),
     (dict(store_C=2), rs.RSSM_E_INVAL),
-    (dict(master_prec=3), rs.RSSM_E_INVAL),
+    (dict(master_prec=5), rs.RSSM_E_INVAL),
+    (dict(master_prec="fp8", read_prec="bf16"), rs.RSSM_E_INVAL),
+    (dict(master_prec="fp8_sr", read_prec="fp8"), rs.RSSM_E_INVAL),
+    (dict(master_prec="fp8", headdim=128), rs.RSSM_E_UNSUPPORTED),
     (dict(master_prec=-1), rs.RSSM_E_INVAL),
     (dict(d_conv=1), rs.RSSM_E_INVAL),
     (dict(d_conv=-1), rs.RSSM_E_INVAL),

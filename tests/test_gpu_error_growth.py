@@ -4,7 +4,8 @@ every sequence compared).
 
 Paths, run side by side on the same inputs: the fp32 master read directly; an fp32 master with a
 bf16, fp8 e4m3 or MXFP4 read copy; an fp16 master rounded to nearest even or stochastically; the
-stochastic fp16 master with an MXFP4 read copy. Two curves per path and step:
+stochastic fp16 master with an MXFP4 read copy; an fp8 master (reads from its codes) rounded to
+nearest even or stochastically. Two curves per path and step:
 * normwise: max |y - y_true| / max |y_true| over the step's [Bt,H,P] outputs (the bar of the
   parity tests);
 * vs the state term: max |y - y_true| / max |S_t . C_t|, where S_t . C_t = y_true - D x_t is the
@@ -16,7 +17,9 @@ stochastic fp16 master with an MXFP4 read copy. Two curves per path and step:
 may use a narrower copy of it, so the copy's rounding does not accumulate): for each read copy the
 per-window maximum on the state-term scale must stay flat -- every window within a factor of 2 of
 the first -- while the normwise error stays within the copy's gate. The fp16 masters round the
-checkpoint itself at each flush; their bound is that of test_gpu_master.py. With the environment
+checkpoint itself at each flush; their bound is that of test_gpu_master.py. The fp8 masters are
+held to reading R9's bound (test_gpu_master_fp8.py): 1/28 for the load plus 1/28 (nearest even)
+or 1/14 (stochastic) per flush done. With the environment
 variable RSSM_ERROR_CURVE_OUT set, the curves are written there as JSON.
 """
 import json
@@ -34,7 +37,9 @@ pytestmark = pytest.mark.gpu
 PATHS = [  # (name, read copy, master)
     ("fp32", "fp32", "fp32"), ("bf16", "bf16", "fp32"), ("fp8", "fp8", "fp32"), ("mxfp4", "mxfp4", "fp32"),
     ("fp16", "fp32", "fp16"), ("fp16_sr", "fp32", "fp16_sr"), ("fp16_sr+mxfp4", "mxfp4", "fp16_sr"),
+    ("fp8 master", "fp32", "fp8"), ("fp8_sr master", "fp32", "fp8_sr"),
 ]
+FP8_STEP = {"fp8": 1.0 / 28, "fp8_sr": 1.0 / 14}   # per flush; the load adds 1/28 (reading R9)
 GATE = {"fp32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "mxfp4": 0.25}
 
 
@@ -77,6 +82,10 @@ def test_error_growth_dual_precision_workload():
                 ratio = win / win[0]
                 assert ratio.max() <= 2.0 and ratio.min() >= 0.5, \
                     f"{name}: read error not flat over the windows: {ratio.min():.2f} .. {ratio.max():.2f}"
+        if master in FP8_STEP:
+            k = np.arange(nw.shape[0] * L).reshape(-1, L) // L + (np.arange(L) == L - 1)   # flushes done
+            bound = 1.0 / 28 + k * FP8_STEP[master]
+            assert np.all(nw <= bound), f"{name}: normwise {float((nw / bound).max()):.2f} of the bound"
     out = os.environ.get("RSSM_ERROR_CURVE_OUT")
     if out:
         with open(out, "w") as f:

@@ -10,7 +10,8 @@ read copy or master: after each flush the model continues from the GPU's own mas
 encoding must then be the GPU's read copy bit for bit. Against the truth, a read copy's error is
 bounded on the SSM output y before the gate (bf16 2e-2, fp8 6e-2, MXFP4 0.25 of max |y|); the gate
 multiplies each value by silu(z), so the test holds max |o - o_true| to that gate times
-max |y_true| * max |silu(z)|. fp16 masters at the bars of their own tests.
+max |y_true| * max |silu(z)|. fp16 and fp8 masters at the bars of their own tests (fp8 on the
+gated scale).
 """
 import numpy as np
 import pytest
@@ -19,7 +20,8 @@ import torch
 import hybrid_mamba_decode_amd as rs
 import oracle
 import workload
-from gpu_harness import MASTER_CODE, PREC_CODE, assert_copy_encodes, dev, host, log, rel
+from gpu_harness import (MASTER_CODE, PREC_CODE, assert_copy_encodes, check_fp8_flush, dev, host, log, master_values,
+                         rel, reseed)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,14 +79,15 @@ def _run(case, steps, sample, read_prec="fp32", master_prec="fp32", lockstep=Tru
         o_model = model.step(*sub)
         flushes = (t + 1) // case.L
         flush_step = (t + 1) % case.L == 0
-        fp16_flush = master_prec != "fp32" and flush_step
-        if fp16_flush:
-            # an fp16 flush rounds the fold, where the GPU's fp32 fold and the oracle's float64
-            # fold may straddle a rounding point: the output is checked against the stored master
-            m16 = host(lay.master())[sample].astype(np.float32)
+        fp8 = master_prec in ("fp8", "fp8_sr")
+        lowp_flush = master_prec != "fp32" and flush_step
+        if lowp_flush:
+            # a low-precision flush rounds the fold, where the GPU's fp32 fold and the oracle's
+            # float64 fold may straddle a rounding point: the output is checked against the stored
+            # master
             x_e, B_e, C_e, _ = truth.last_edge
-            y_m = oracle.step(m16.astype(np.float64), x_e, B_e, C_e, np.zeros_like(truth.last_edge[3]),
-                              case.A, case.D)
+            y_m = oracle.step(master_values(lay, master_prec, sample), x_e, B_e, C_e,
+                              np.zeros_like(truth.last_edge[3]), case.A, case.D)
             e_model = rel(o, oracle.mixer_gate(y_m, sub[1]))
         else:
             e_model = rel(o, o_model)
@@ -97,15 +100,26 @@ def _run(case, steps, sample, read_prec="fp32", master_prec="fp32", lockstep=Tru
                 e_g = gated_err(o, o_true, y_true, sub[1])
                 worst_gated = max(worst_gated, e_g)
                 assert e_g <= tol_nonflush, f"step {t}: vs truth {e_g:.2e} > {tol_nonflush:.2e}"
+        elif fp8:
+            # reading R9's bound on the state (load 1/28, each flush 1/28 or 1/14 of the head's
+            # largest value), on the SSM output's scale before the gate
+            bound = (1 + flushes * (1 if master_prec == "fp8" else 2)) / 28
+            e_g = gated_err(o, o_true, y_true, sub[1])
+            worst_gated = max(worst_gated, e_g)
+            assert e_g <= bound, f"step {t}: vs truth {e_g:.2e} > {bound:.2e}"
         else:
             assert rel(o, o_true) <= (flushes + 1) * 2.0 ** -10, f"step {t}: vs truth {rel(o, o_true):.2e}"
         pos, ck = lay.get_pointers()
         assert pos == [t + 1] * case.Bt and ck == [flushes * case.L] * case.Bt
         if t % check_every == 0 or flush_step:
             assert np.array_equal(host(lay.materialize_conv_state())[sample], truth.hist), f"step {t}: conv history"
-            bound = TOL_F32 if master_prec == "fp32" else (flushes + 1) * 2.0 ** -10
+            bound = TOL_F32 if master_prec == "fp32" else (
+                (1 + flushes * (1 if master_prec == "fp8" else 2)) / 28 if fp8 else (flushes + 1) * 2.0 ** -10)
             assert rel(host(lay.materialize_state())[sample], truth.S) <= bound
-        if flush_step:
+        if flush_step and fp8:
+            check_fp8_flush(lay, model.rep, sample, f"step {t}")
+            reseed(model.rep, lay, master_prec, sample)
+        elif flush_step:
             m = host(lay.master())[sample].astype(np.float32)
             if master_prec != "fp32":
                 diff = m.astype(np.float64) != model.checkpoint()
@@ -139,8 +153,8 @@ def test_mixer_with_read_copy(read_prec, tol):
     _run(case, 20, range(3), read_prec=read_prec, tol_nonflush=tol)
 
 
-@pytest.mark.parametrize("master_prec", ["fp16", "fp16_sr"])
-def test_mixer_with_fp16_master(master_prec):
+@pytest.mark.parametrize("master_prec", ["fp16", "fp16_sr", "fp8", "fp8_sr"])
+def test_mixer_with_lowp_master(master_prec):
     case = MixCase(3, 8, 32, 64, 2, 6, 4, 34)
     _run(case, 20, range(3), master_prec=master_prec)
 
