@@ -345,3 +345,37 @@ def test_fp8_master_stochastic_rounding_avoids_stagnation():
     p = (2.0 ** -14 * 448) / 16
     sd = 16 * scale * np.sqrt(flushes * p * (1 - p) / m.size)
     assert abs(float(m.mean()) - truth) <= 10 * sd, (float(m.mean()), truth, sd)
+
+
+def test_fp8_master_export_and_import():
+    """Reading R9's state as codes and scales: the exported codes times the scales are the
+    checkpoint exactly (decoded with the library's E4M3 table); importing a row's codes and scales
+    into a second replay at the same position reproduces that row, and both replays then flush
+    identically."""
+    Bt, H, P, N, G, L = 3, 2, 8, 32, 1, 4
+    seed = 31
+    S0 = workload.initial_state(seed, Bt, H, P, N)
+    A, D = workload.layer_params(seed, H)
+    a = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP8_SR, seed=6)
+    b = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP8_SR, seed=6)
+    import torch
+    table = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for t in range(L + 1):
+        ins = workload.step_inputs(seed, t, Bt, H, P, N, G)
+        a.step(*ins)
+        if t < L - 1:
+            b.step(*ins)
+    codes, scales = a.fp8_master()
+    assert np.array_equal(table[codes] * scales[:, :, None, None].astype(np.float64), a.checkpoint())
+    with pytest.raises(RuntimeError):
+        oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP16).fp8_master()
+    # b is one token short of a's flush; it takes a's post-flush state for rows 2 and 0 after
+    # stepping through the same flush itself, then both continue in lockstep
+    b.step(*workload.step_inputs(seed, L - 1, Bt, H, P, N, G))
+    b.step(*workload.step_inputs(seed, L, Bt, H, P, N, G))
+    b.set_master_fp8(codes[[2, 0]], scales[[2, 0]], [2, 0])
+    assert np.array_equal(b.checkpoint(), a.checkpoint())
+    for t in range(L + 1, 2 * L + 2):
+        ins = workload.step_inputs(seed, t, Bt, H, P, N, G)
+        assert np.array_equal(a.step(*ins), b.step(*ins))
+    assert np.array_equal(b.checkpoint(), a.checkpoint())
