@@ -931,14 +931,14 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
             const int j = tid / GS, sub = tid % GS;
             float gj = 0.f;
             for (int n = sub; n < NN; n += GS) gj = fmaf(s.Bw[j][n], s.Cq[n], gj);
-    #pragma unroll
+#pragma unroll
             for (int o = GS / 2; o >= 1; o >>= 1) gj += __shfl_xor(gj, o, 64);
             if (sub == 0)
-    #pragma unroll
+#pragma unroll
                 for (int hh = 0; hh < HPB; ++hh) s.coef[hh][j] = s.w[hh][j] * gj;
         }
         float part[NL];
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < NL; ++i) {
             part[i] = chunk_dot<PREC>(v[i], cc);
             if constexpr (PREC == PREC_FP4) part[i] = mx_scaled(part[i], sc[i]);
@@ -956,7 +956,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         if (tid < ROWS && tid % kRows < t.nrows) {
             const int hh = tid / kRows, p = tid % kRows;
             float acc = s.decay[hh] * (s.u[tid] * scl_r);
-    #pragma unroll 4
+#pragma unroll 4
             for (int j = 0; j < k; ++j) acc = fmaf(s.coef[hh][j], s.xw[j][tid], acc);
             const float xt = s.xw[k - 1][tid];
             acc = fmaf(Ld.D[t.h + hh], xt, acc);
@@ -1226,22 +1226,24 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
 }
 
 // ==========================================================================================
-// Flush step of an fp16 master when every sequence of the launch flushes (lockstep decoding, or
-// a host bound showing every buffer fills): fold all k records of the window into the master
-// ([WittyWires] "What happened": the checkpoint is updated when the buffer fills), round it to
-// fp16 (nearest even or stochastic, reading R13), rewrite the read copy and read y from the
-// stored master. The fold S' = decay * S + sum_j (w_j x_j) (outer) B_j is a rank-k update, a
-// dense contraction: it runs on MFMA (v_mfma_f32_16x16x4_f32), leaving the VALU to the fp16
-// conversions, the rounding and its Philox stream.
+// Flush step of an fp16 or fp8 master when every sequence of the launch flushes (lockstep
+// decoding, or a host bound showing every buffer fills): fold all k records of the window into
+// the master ([WittyWires] "What happened": the checkpoint is updated when the buffer fills),
+// round it to fp16 (nearest even or stochastic) and rewrite the read copy -- or, F8M, encode it
+// to E4M3 codes with the head's new scale (nearest even or stochastic), the fp8 master being its
+// own read copy -- and read y from the stored master. The fold S' = decay * S + sum_j (w_j x_j)
+// (outer) B_j is a rank-k update, a dense contraction: it runs on MFMA
+// (v_mfma_f32_16x16x4_f32), leaving the VALU to the conversions, the rounding and its Philox
+// stream.
 //
 // One work-group per (sequence, head), P <= 64: wave w owns rows 16w .. 16w+15. The product is
 // formed transposed, D^T[n][p] += sum_j B_j[n] * (w_j x_j[p]), so that an MFMA tile's column is a
 // row p of the state (lane l: p = 16w + l % 16) and its four output registers are four
 // consecutive n of that row. Tile (q, hf) maps its row r to n = 32q + 8(r / 4) + 4hf + r % 4:
 // lane group g = l / 16 then holds n = 32q + 8g .. 32q + 8g + 7 of tiles (q, 0) and (q, 1) --
-// eight consecutive fp16 values, one 16-byte load and store per q, and one Philox4x32-10 call
-// for the eight 16-bit fields of its stochastic rounding. Per load instruction a wave reads 16
-// rows x 64 contiguous bytes.
+// eight consecutive fp16 values, one 16-byte load and store per q (fp8 codes: 8 bytes of the
+// row's chunk), and one Philox4x32-10 call for the eight 16-bit fields of its stochastic
+// rounding. Per fp16 load instruction a wave reads 16 rows x 64 contiguous bytes.
 // ==========================================================================================
 template <int LMAX>
 struct LpFlushLds {
@@ -1254,10 +1256,11 @@ struct LpFlushLds {
     float red[kWaves];
 };
 
-template <int PREC, int LMAX, bool SR>
+template <int PREC, int LMAX, bool SR, bool F8M>
 __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, TokenIO io, Lockstep ls)
 {
     static_assert(PREC >= 0 && NN >= 32 && NN % 32 == 0, "lane groups cover 32 consecutive n per load slot");
+    static_assert(!F8M || PREC == PREC_FP8, "an fp8 master is read as the fp8 copy");
     constexpr int NQ = NN >= 32 ? NN / 32 : 1;  // 16-byte fp16 loads per lane (eight values each)
     __shared__ LpFlushLds<LMAX> s;
     const Tile t = map_tile(Ld);  // psplit == 1 (host-checked): the work-group owns the head
@@ -1332,10 +1335,24 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
         dtj = in ? val : 0.f;
     }
     const float Ah = Ld.A[t.h];
-    u32x4 mv[NQ];
+    // master rows: eight fp16 values (16 bytes) per q, or with an fp8 master eight codes (8 bytes
+    // of the row's chunk n0 / 16) and the head's scale
+    u32x4 mv[F8M ? 1 : NQ];
+    u32x2 m8[F8M ? NQ : 1];
+    float mscale = 1.0f;
+    if constexpr (F8M) {
+        const unsigned char *src = (const unsigned char *)Ld.rcopy;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
-        mv[q] = load_nt((const unsigned short *)Ld.master + rowe + 32 * q + 8 * g);
+        for (int q = 0; q < NQ; ++q) {
+            const int n0 = 32 * q + 8 * g;
+            m8[q] = __builtin_nontemporal_load((const u32x2 *)(src + chunk_off<PREC_FP8>(bh, pr, n0 / 16, Ld.P) + n0 % 16));
+        }
+        mscale = Ld.scale[bh];
+    } else {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            mv[q] = load_nt((const unsigned short *)Ld.master + rowe + 32 * q + 8 * g);
+    }
 
     // 3. Commit the window to LDS; the window's weights in wave 0 (suffix sums of dt by lane
     //    shuffles: w_j = dt_j exp(A sum_{i>j} dt_i), decay = exp(A sum_i dt_i)).
@@ -1381,10 +1398,20 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
     f32x4 acc[NQ][2];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        const f32x2 a = f16x2_to_f32(mv[q].x), b = f16x2_to_f32(mv[q].y);
-        const f32x2 c = f16x2_to_f32(mv[q].z), d = f16x2_to_f32(mv[q].w);
-        acc[q][0] = f32x4{a.x, a.y, b.x, b.y} * decay;
-        acc[q][1] = f32x4{c.x, c.y, d.x, d.y} * decay;
+        if constexpr (F8M) {
+            const float sd = mscale * decay;
+            const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8[q].x, false);
+            const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8[q].x, true);
+            const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8[q].y, false);
+            const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8[q].y, true);
+            acc[q][0] = f32x4{a.x, a.y, b.x, b.y} * sd;
+            acc[q][1] = f32x4{c.x, c.y, d.x, d.y} * sd;
+        } else {
+            const f32x2 a = f16x2_to_f32(mv[q].x), b = f16x2_to_f32(mv[q].y);
+            const f32x2 c = f16x2_to_f32(mv[q].z), d = f16x2_to_f32(mv[q].w);
+            acc[q][0] = f32x4{a.x, a.y, b.x, b.y} * decay;
+            acc[q][1] = f32x4{c.x, c.y, d.x, d.y} * decay;
+        }
     }
     const int ksteps = (k + 3) / 4;
     for (int kk = 0; kk < ksteps; ++kk) {
@@ -1402,16 +1429,8 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
             }
     }
 
-    // 5. Round to fp16 and store the master; acc then holds the stored values (the flush's
-    //    output and the read copy come from the checkpoint as stored). In fp16's normal range
-    //    both roundings are integer operations on the fp32 encoding whose result is the rounded
-    //    value itself, exact in fp32 (13 low mantissa bits cleared): nearest even adds
-    //    0xFFF + bit 13; the stochastic rule adds 2^13 - 1 - (r16 >> 3) (see f16_sr). The codes
-    //    are then packed by the round-toward-zero converter, exact on representable values. A
-    //    wave with a value below 2^-14 redoes those values with the general routines.
     const unsigned newck = (unsigned)(dpos + 1);  // stochastic rounding runs in device-pointer mode
     const size_t seq0 = (size_t)t.b * Ld.H * Ld.P * NN;
-    unsigned short *mdst = (unsigned short *)Ld.master + rowe + 8 * g;
     unsigned wd[NQ][4];  // SR: the eight 16-bit fields of each group of eight values
     if constexpr (SR) {
         const unsigned e8 = (unsigned)((rowe - seq0) / 8) + (unsigned)g;  // first group's counter
@@ -1421,66 +1440,10 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
             wd[q][0] = rnd.x; wd[q][1] = rnd.y; wd[q][2] = rnd.z; wd[q][3] = rnd.w;
         }
     }
-    bool sub = false;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            f32x4 &a = acc[q][hf];
-            float r[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = 4 * hf + i;  // element within the group of eight
-                const float c = __builtin_amdgcn_fmed3f(r[i], -65504.0f, 65504.0f);
-                const unsigned u = __float_as_uint(c);
-                // SR: the 13-bit complement of r16 >> 3 is bits 3 .. 15 of the field, inverted
-                unsigned add;
-                if constexpr (SR) add = (~wd[q][e / 2] >> (3 + 16 * (e % 2))) & 0x1FFFu;
-                else add = 0xFFFu + ((u >> 13) & 1u);
-                sub |= fabsf(c) < 0x1p-14f;
-                r[i] = __uint_as_float((u + add) & ~0x1FFFu);
-            }
-            // keep the unrounded values for the rare fix-up below
-            if (__builtin_expect(__builtin_amdgcn_ballot_w64(sub) != 0, 0)) {
-                const float o[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = 4 * hf + i;
-                    if (fabsf(o[i]) < 0x1p-14f) {
-                        unsigned short hc;
-                        if constexpr (SR) hc = f16_sr(o[i], (wd[q][e / 2] >> (16 * (e % 2))) & 0xFFFFu);
-                        else hc = f16_rne(o[i]);
-                        r[i] = f16_value(hc);
-                    }
-                }
-                sub = false;
-            }
-            a = f32x4{r[0], r[1], r[2], r[3]};
-        }
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        if (prow) {
-            const f32x4 a = acc[q][0], b = acc[q][1];
-            u32x4 pk;
-            pk.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
-            pk.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a.z, a.w));
-            pk.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
-            pk.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(b.z, b.w));
-            store_nt(mdst + 32 * q, pk);
-        }
-    }
-
-    // 6. Read copy from the stored master.
-    if constexpr (PREC == PREC_BF16) {
-        unsigned short *dst = (unsigned short *)Ld.rcopy + rowe + 8 * g;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const f32x4 a = acc[q][0], b = acc[q][1];
-            const u32x4 pk = {bf16_rne(a.x) | (bf16_rne(a.y) << 16), bf16_rne(a.z) | (bf16_rne(a.w) << 16),
-                              bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16)};
-            if (prow) *(u32x4 *)(dst + 32 * q) = pk;
-        }
-    } else if constexpr (PREC == PREC_FP8) {
+    if constexpr (F8M) {
+        // 5'. fp8 master: the head's amax, scale = amax / 448, codes of value / scale to nearest
+        //     even (the converter) or by the 16-bit stochastic rule (e4m3_sr), stored in the
+        //     row's chunks; acc then holds code * scale, the checkpoint as stored.
         float amax = 0.f;
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
@@ -1500,30 +1463,135 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
             const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
             float c[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(f[i] * inv, -448.0f), 448.0f);
+            for (int i = 0; i < 8; ++i) {
+                c[i] = fminf(fmaxf(f[i] * inv, -448.0f), 448.0f);
+                if constexpr (SR) c[i] = e4m3_sr(c[i], (wd[q][i / 2] >> (16 * (i % 2))) & 0xFFFFu);
+            }
             int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
             lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
             int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
             hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
-            const int n0 = 32 * q + 8 * g;  // 16-value chunk n0 / 16, byte n0 % 16 within it
+            const int n0 = 32 * q + 8 * g;
             if (prow) *(u32x2 *)(dst + chunk_off<PREC_FP8>(bh, pr, n0 / 16, Ld.P) + n0 % 16) = u32x2{(unsigned)lo, (unsigned)hi};
+            const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), d1 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+            const f32x2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), d3 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+            acc[q][0] = f32x4{d0.x, d0.y, d1.x, d1.y} * scale;
+            acc[q][1] = f32x4{d2.x, d2.y, d3.x, d3.y} * scale;
         }
         if (tid == 0) Ld.scale[bh] = scale;
-    } else if constexpr (PREC == PREC_FP4) {
-        // block q (32 consecutive n of the row) is spread over the four lane groups of this row
-        unsigned char *dst = (unsigned char *)Ld.rcopy;
+    } else {
+        // 5. Round to fp16 and store the master; acc then holds the stored values (the flush's
+        //    output and the read copy come from the checkpoint as stored). In fp16's normal range
+        //    both roundings are integer operations on the fp32 encoding whose result is the rounded
+        //    value itself, exact in fp32 (13 low mantissa bits cleared): nearest even adds
+        //    0xFFF + bit 13; the stochastic rule adds 2^13 - 1 - (r16 >> 3) (see f16_sr). The codes
+        //    are then packed by the round-toward-zero converter, exact on representable values. A
+        //    wave with a value below 2^-14 redoes those values with the general routines.
+        unsigned short *mdst = (unsigned short *)Ld.master + rowe + 8 * g;
+        bool sub = false;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x4 &a = acc[q][hf];
+                float r[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * hf + i;  // element within the group of eight
+                    const float c = __builtin_amdgcn_fmed3f(r[i], -65504.0f, 65504.0f);
+                    const unsigned u = __float_as_uint(c);
+                    // SR: the 13-bit complement of r16 >> 3 is bits 3 .. 15 of the field, inverted
+                    unsigned add;
+                    if constexpr (SR) add = (~wd[q][e / 2] >> (3 + 16 * (e % 2))) & 0x1FFFu;
+                    else add = 0xFFFu + ((u >> 13) & 1u);
+                    sub |= fabsf(c) < 0x1p-14f;
+                    r[i] = __uint_as_float((u + add) & ~0x1FFFu);
+                }
+                // keep the unrounded values for the rare fix-up below
+                if (__builtin_expect(__builtin_amdgcn_ballot_w64(sub) != 0, 0)) {
+                    const float o[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 4 * hf + i;
+                        if (fabsf(o[i]) < 0x1p-14f) {
+                            unsigned short hc;
+                            if constexpr (SR) hc = f16_sr(o[i], (wd[q][e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+                            else hc = f16_rne(o[i]);
+                            r[i] = f16_value(hc);
+                        }
+                    }
+                    sub = false;
+                }
+                a = f32x4{r[0], r[1], r[2], r[3]};
+            }
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const f32x4 a = acc[q][0], b = acc[q][1];
-            float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
-                               fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-            amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-            const unsigned code = mx_code_of(amax);
-            const unsigned lo = mx_encode4(a, code), hi = mx_encode4(b, code);
             if (prow) {
-                *(unsigned *)(dst + chunk_off<PREC_FP4>(bh, pr, q, Ld.P) + 4 * g) = lo | (hi << 16);
-                if (g == 0) Ld.mxscale[(bh * Ld.P + pr) * (NN / 32) + q] = (unsigned char)code;
+                const f32x4 a = acc[q][0], b = acc[q][1];
+                u32x4 pk;
+                pk.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
+                pk.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a.z, a.w));
+                pk.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
+                pk.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(b.z, b.w));
+                store_nt(mdst + 32 * q, pk);
+            }
+        }
+
+        // 6. Read copy from the stored master.
+        if constexpr (PREC == PREC_BF16) {
+            unsigned short *dst = (unsigned short *)Ld.rcopy + rowe + 8 * g;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const f32x4 a = acc[q][0], b = acc[q][1];
+                const u32x4 pk = {bf16_rne(a.x) | (bf16_rne(a.y) << 16), bf16_rne(a.z) | (bf16_rne(a.w) << 16),
+                                  bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16)};
+                if (prow) *(u32x4 *)(dst + 32 * q) = pk;
+            }
+        } else if constexpr (PREC == PREC_FP8) {
+            float amax = 0.f;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const f32x4 a = acc[q][hf];
+                    const float m = fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w)));
+                    amax = prow ? fmaxf(amax, m) : amax;
+                }
+            amax = block_max(amax, s.red);
+            const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
+            const float inv = 1.0f / scale;
+            unsigned char *dst = (unsigned char *)Ld.rcopy;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const f32x4 a = acc[q][0], b = acc[q][1];
+                const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                float c[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(f[i] * inv, -448.0f), 448.0f);
+                int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+                lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+                hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+                const int n0 = 32 * q + 8 * g;  // 16-value chunk n0 / 16, byte n0 % 16 within it
+                if (prow) *(u32x2 *)(dst + chunk_off<PREC_FP8>(bh, pr, n0 / 16, Ld.P) + n0 % 16) = u32x2{(unsigned)lo, (unsigned)hi};
+            }
+            if (tid == 0) Ld.scale[bh] = scale;
+        } else if constexpr (PREC == PREC_FP4) {
+            // block q (32 consecutive n of the row) is spread over the four lane groups of this row
+            unsigned char *dst = (unsigned char *)Ld.rcopy;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const f32x4 a = acc[q][0], b = acc[q][1];
+                float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                                   fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+                amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+                amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+                const unsigned code = mx_code_of(amax);
+                const unsigned lo = mx_encode4(a, code), hi = mx_encode4(b, code);
+                if (prow) {
+                    *(unsigned *)(dst + chunk_off<PREC_FP4>(bh, pr, q, Ld.P) + 4 * g) = lo | (hi << 16);
+                    if (g == 0) Ld.mxscale[(bh * Ld.P + pr) * (NN / 32) + q] = (unsigned char)code;
+                }
             }
         }
     }
@@ -2067,11 +2135,23 @@ hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, bool a
             if (all_flush && (Ld.mprec == MASTER_F16 || Ld.mprec == MASTER_F16_SR) && Ld.psplit == 1 &&
                 (Ld.mprec != MASTER_F16_SR || ls.k == 0)) {
                 if (Ld.mprec == MASTER_F16_SR)
-                    hipLaunchKernelGGL((lp_flush_step_kernel<PREC, LMAX, true>), dim3(nblocks(Ld)), dim3(kThreads), 0,
-                                       st, Ld, io, ls);
+                    hipLaunchKernelGGL((lp_flush_step_kernel<PREC, LMAX, true, false>), dim3(nblocks(Ld)), dim3(kThreads),
+                                       0, st, Ld, io, ls);
                 else
-                    hipLaunchKernelGGL((lp_flush_step_kernel<PREC, LMAX, false>), dim3(nblocks(Ld)), dim3(kThreads), 0,
-                                       st, Ld, io, ls);
+                    hipLaunchKernelGGL((lp_flush_step_kernel<PREC, LMAX, false, false>), dim3(nblocks(Ld)),
+                                       dim3(kThreads), 0, st, Ld, io, ls);
+                return hipGetLastError();
+            }
+        // fp8 master, every sequence flushes: the same MFMA fold, read from and encoded to E4M3
+        if constexpr (!MIX && NN >= 32 && PREC == PREC_FP8)
+            if (all_flush && (Ld.mprec == MASTER_F8 || Ld.mprec == MASTER_F8_SR) && Ld.psplit == 1 &&
+                (Ld.mprec != MASTER_F8_SR || ls.k == 0)) {
+                if (Ld.mprec == MASTER_F8_SR)
+                    hipLaunchKernelGGL((lp_flush_step_kernel<PREC, LMAX, true, true>), dim3(nblocks(Ld)), dim3(kThreads),
+                                       0, st, Ld, io, ls);
+                else
+                    hipLaunchKernelGGL((lp_flush_step_kernel<PREC, LMAX, false, true>), dim3(nblocks(Ld)),
+                                       dim3(kThreads), 0, st, Ld, io, ls);
                 return hipGetLastError();
             }
         // fp16 master: two heads per work-group with the master rows issued early (see step_kernel)

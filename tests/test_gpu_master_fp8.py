@@ -270,3 +270,54 @@ def test_fp8_sr_master_avoids_stagnation():
     assert np.all(rne[:, :, 1:, :] == 0.4375) and np.all(rne[:, :, 0, :] == 0.875)
     m = master_values(lays["fp8_sr"], "fp8_sr", sample)[:, :, 1:, :]
     assert float(m.mean()) > 0.4375 + 16 * 2.0 ** -14
+
+
+@pytest.mark.parametrize("master", ["fp8", "fp8_sr"])
+def test_fp8_master_staggered_flushes(master):
+    """Speculative rounds with random accepted counts leave the sequences at different window
+    positions; the standard steps that follow then flush some sequences and not others in one
+    launch (the per-sequence flush path). Per step and sequence: outputs of sequences that did
+    not flush within 1e-5 of the model; those that flushed have their codes checked as in
+    standard decode and their output read from the stored master; pointers bit-exact."""
+    T, L = 3, 7
+    case = Case(5, 6, 48, 64, 2, L, 505)
+    lay = case.layer(Tmax=T, master_prec=master, sr_seed=21)
+    sample = np.arange(case.Bt)
+    model = oracle.Replay(case.S0, case.A, case.D, case.G, L, T, oracle.READ_FP32, MASTER_CODE[master], 21,
+                          seq_ids=sample)
+    for it in range(5):
+        x, B, C, dt = case.draft_inputs(it, T)
+        acc = workload.accepted_counts(case.seed, it, case.Bt, T)
+        lay.spec_verify(dev(x), dev(B), dev(C), dev(dt))
+        lay.rollback(dev(acc))
+        ck_before = model.pointers()[1].copy()
+        model.verify(T, x, B, C, dt)
+        model.rollback(acc)
+        moved = np.nonzero(model.pointers()[1] != ck_before)[0]
+        if moved.size:
+            check_fp8_flush(lay, model, sample, f"round {it}", rows=moved)
+            reseed(model, lay, master, sample, rows=moved)
+    pos0 = model.pointers()[0]
+    assert len(set((pos0 - model.pointers()[1]).tolist())) > 1, "rounds left every sequence at one position"
+    mixed = 0
+    for t in range(2 * L):
+        x, B, C, dt = case.step_inputs(100 + t)
+        y = host(lay.step(dev(x), dev(B), dev(C), dev(dt)))
+        ck_before = model.pointers()[1].copy()
+        y_model = model.step(x, B, C, dt)
+        pos, ck = lay.get_pointers()
+        opos, ock = model.pointers()
+        assert pos == list(opos) and ck == list(ock), f"step {t}: pointers"
+        fl = ock != ck_before
+        mixed += bool(fl.any() and not fl.all())
+        if (~fl).any():
+            assert rel(y[~fl], y_model[~fl]) <= TOL_F32, f"step {t}: non-flushing sequences vs model"
+        if fl.any():
+            rows = np.nonzero(fl)[0]
+            check_fp8_flush(lay, model, sample, f"step {t}", rows=rows)
+            m = master_values(lay, master, rows)
+            y_m = oracle.step(m, x[rows], B[rows], C[rows], np.zeros_like(dt[rows]), case.A, case.D)
+            assert rel(y[rows], y_m) <= TOL_F32, f"step {t}: flushed sequences vs the stored master"
+            reseed(model, lay, master, sample, rows=rows)
+    assert mixed >= 2, "no step flushed some sequences and not others"
+    assert lay.check() == rs.RSSM_OK
