@@ -344,8 +344,8 @@ __device__ inline void write_copy_rows(const Layer &Ld, size_t bh, size_t elem0,
 }
 
 // Fold `k` staged records into one head's fp32 rows vf (f32 geometry), in registers:
-// S' = decay * S + sum_j (w_j * x_j[p]) * B_j[n]   ([AT Pulse] "Technical analysis": a flush
-// folds the buffer into the checkpoint). xw rows of this head start at column `col0`. Records
+// S' = decay * S + sum_j (w_j * x_j[p]) * B_j[n]   ([AT Pulse] "Technical analysis": at a flush
+// the buffered records are absorbed into the checkpoint). xw rows of this head start at column `col0`. Records
 // are the outer loop, so each lane reads its B chunk of a record once for all its rows.
 template <int LMAX, int XCOLS>
 __device__ inline void fold_head(f32x4 (&vf)[GF::NL], const float (&xw)[LMAX][XCOLS], const float (&Bw)[LMAX][NN],
