@@ -504,11 +504,11 @@ class ReplaySSM:
         return None
 
     def scales(self):
-        """fp8 copy or fp8 master: fp32 per-head scales [Bt,H]; MXFP4: E8M0 block-scale bytes
-        [Bt,H,P,N/32]."""
+        """fp8 copy or fp8 master: fp32 scales [Bt,H,ceil(P/64)], one per block of 64 rows;
+        MXFP4: E8M0 block-scale bytes [Bt,H,P,N/32]."""
         if self.cfg.read_prec == READ_MXFP4:
             return self.region("scale", torch.uint8, (self.batch, self.nheads, self.headdim, self.dstate // 32))
-        return self.region("scale", torch.float32, (self.batch, self.nheads))
+        return self.region("scale", torch.float32, (self.batch, self.nheads, (self.headdim + 63) // 64))
 
     def pointer_arrays(self):
         return (self.region("pos", torch.int32, (self.batch,)),

@@ -249,20 +249,21 @@ class Replay:
             raise RuntimeError("oracle replay: set_checkpoint while a verify is pending, or a bad row")
 
     def fp8_master(self):
-        """fp8 master (reading R9): E4M3FN codes uint8 [Bt,H,P,N] and fp32 scales [Bt,H]."""
+        """fp8 master (reading R9): E4M3FN codes uint8 [Bt,H,P,N] and fp32 scales
+        [Bt,H,ceil(P/64)] (one per block of 64 rows)."""
         codes = np.empty((self.Bt, self.H, self.P, self.N), np.uint8)
-        scales = np.empty((self.Bt, self.H), np.float32)
+        scales = np.empty((self.Bt, self.H, (self.P + 63) // 64), np.float32)
         if lib().oracle_replay_master_fp8(self._h, codes, scales) != 0:
             raise RuntimeError("oracle replay: not an fp8 master")
         return codes, scales
 
     def set_master_fp8(self, codes, scales, rows=None):
-        """fp8 master: continue from codes [n,H,P,N] times scales [n,H] (exact), for every
-        sequence or for the sequences listed in rows (records and pointers stay)."""
+        """fp8 master: continue from codes [n,H,P,N] times scales [n,H,ceil(P/64)] (exact), for
+        every sequence or for the sequences listed in rows (records and pointers stay)."""
         n = self.Bt if rows is None else len(rows)
         codes = np.ascontiguousarray(codes, np.uint8)
         scales = _f32(scales)
-        if codes.shape != (n, self.H, self.P, self.N) or scales.shape != (n, self.H):
+        if codes.shape != (n, self.H, self.P, self.N) or scales.shape != (n, self.H, (self.P + 63) // 64):
             raise ValueError("fp8 master shape mismatch")
         idx = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
         rc = lib().oracle_replay_set_master_fp8(self._h, codes, scales,
@@ -310,6 +311,25 @@ def e4m3_encode_tiles(a, tile_elems):
     scales = np.empty(ntiles, np.float32)
     lib().oracle_encode_e4m3_tiles(a, codes, scales, ntiles, tile_elems)
     return codes, scales
+
+
+def e4m3_encode_rows(a):
+    """The fp8 read copy of states a [..., P, N] (reading R6): one scale per block of 64
+    consecutive rows p. Returns (codes uint8 [..., P, N], scales f32 [..., ceil(P/64)])."""
+    a = _f32(a)
+    P, N = a.shape[-2], a.shape[-1]
+    lead = a.shape[:-2]
+    flat = a.reshape(-1, P, N)
+    nblk = (P + 63) // 64
+    codes = np.empty(flat.shape, np.uint8)
+    scales = np.empty((flat.shape[0], nblk), np.float32)
+    for kb in range(nblk):
+        p0, p1 = 64 * kb, min(64 * kb + 64, P)
+        blk = np.ascontiguousarray(flat[:, p0:p1, :])
+        c, sc = e4m3_encode_tiles(blk, (p1 - p0) * N)
+        codes[:, p0:p1, :] = c.reshape(blk.shape)
+        scales[:, kb] = sc
+    return codes.reshape(a.shape), scales.reshape(*lead, nblk)
 
 
 def e4m3_encode_at(a, inv_scale=1.0):
@@ -406,8 +426,9 @@ class GDNReplay:
     """O3g + O4: the GDN replay form (checkpoint + records, backward sweep) and its pointer machine."""
 
     def __init__(self, S0, G, L, Tmax=1, read_prec=READ_FP32):
-        """read_prec READ_BF16: the checkpoint product of replayed outputs reads a bf16 copy of
-        the checkpoint (reading G4); READ_FP32: the checkpoint itself."""
+        """read_prec READ_BF16 / READ_FP8 / READ_MXFP4: the checkpoint product of replayed
+        outputs reads a copy of the checkpoint in that format (reading G4); READ_FP32: the
+        checkpoint itself."""
         S0 = _f32(S0)
         self.Bt, self.H, self.Dv, self.Dk = S0.shape
         self.G, self.L, self.Tmax, self.read_prec = G, L, Tmax, read_prec

@@ -30,9 +30,10 @@
  *   R5  spec-decode buffer capacity is L; after a commit the layer flushes when more than L - T
  *       records are pending, so T drafts always fit; with T = 1 this is rule R2.
  *   R6  read copy: bf16 by round-to-nearest-even, or OCP fp8 E4M3FN with one fp32 scale per
- *       (sequence, head) = amax/448 (1 when amax is 0), values multiplied by 1/scale in fp32,
- *       clamped to +-448 and rounded to nearest even, or OCP MXFP4 (reading R7). It is written
- *       from the master when a state is loaded and at every flush, never otherwise.
+ *       (sequence, head, block of 64 consecutive rows p -- rows 64i .. 64i + 63, the whole head
+ *       when P <= 64) = amax/448 of the block (1 when amax is 0), values multiplied by 1/scale in
+ *       fp32, clamped to +-448 and rounded to nearest even, or OCP MXFP4 (reading R7). It is
+ *       written from the master when a state is loaded and at every flush, never otherwise.
  *   R7  MXFP4 read copy (the pages' 4-bit state reads are NVFP4, which has no gfx950 form; MXFP4
  *       is the OCP microscaling format gfx950 converts natively): per state row, blocks of 32
  *       consecutive n share one E8M0 scale; elements are FP4 E2M1. Scale and rounding follow the
@@ -58,8 +59,8 @@
  *       fp16 checkpoint; a flush step's output is read from the rounded checkpoint.
  *   R9  FP8 master recurrence (the pages' FP8 alternative to the FP16 recurrence, [AT Pulse]
  *       "Claims and evidence"): the checkpoint itself is kept as OCP E4M3FN codes with one fp32
- *       scale per (sequence, head), in the format of the fp8 read copy (R6): scale = amax / 448
- *       of the fold rounded to fp32 (1 if amax is 0), a = v * (1 / scale) in fp32, clamped to
+ *       scale per (sequence, head, 64-row block), in the format of the fp8 read copy (R6): scale
+ *       = amax / 448 of the block's fold rounded to fp32 (1 if amax is 0), a = v * (1 / scale) in fp32, clamped to
  *       +-448. A load rounds a to nearest even; a flush to nearest even (FP8) or stochastically
  *       (FP8_SR): with q the E4M3 magnitude toward zero and ulp the code spacing above it, the
  *       magnitude rounds up iff r16 < (|a| - q) / ulp * 2^16, with the 16-bit fields of R8's
@@ -475,7 +476,8 @@ void oracle_encode_f16(const float *in, uint16_t *out, size_t n, int stochastic,
 
 typedef struct oracle_replay {
     int Bt, H, P, N, G, L, Tmax, read_prec; /* 0 fp32 master, 1 bf16, 2 fp8 e4m3, 3 mxfp4 */
-    float *mscale;                          /* fp8 master: per-(sequence, head) scale [Bt,H] */
+    float *mscale;                          /* fp8 master: scale per (sequence, head, 64-row block)
+                                               [Bt,H,ceil(P/64)] */
     int master_prec;                        /* 0 fp32, 1 fp16 nearest even, 2 fp16 stochastic (R8),
                                                3 fp8 nearest even, 4 fp8 stochastic (R9) */
     uint32_t seed;
@@ -517,29 +519,34 @@ static void round_master(oracle_replay *r, int b, int ck, int stochastic)
 {
     const size_t n = (size_t)r->H * r->P * r->N;
     double *m = r->ckpt + (size_t)b * n;
-    if (r->master_prec >= 3) { /* fp8 (R9): per-head scale of the fold rounded to fp32 */
+    if (r->master_prec >= 3) { /* fp8 (R9): per-block scale of the fold rounded to fp32 */
         const size_t tile = (size_t)r->P * r->N;
+        const int nblk = (r->P + 63) / 64;
         float *v = (float *)malloc(tile * sizeof(float));
         for (int h = 0; h < r->H; ++h) {
             double *mh = m + (size_t)h * tile;
             for (size_t i = 0; i < tile; ++i) v[i] = (float)mh[i];
-            const float scale = oracle_e4m3_scale(v, tile);
-            const float inv = 1.0f / scale;
-            r->mscale[(size_t)b * r->H + h] = scale;
-            for (size_t i = 0; i < tile; i += 8) {
-                const size_t e = (size_t)h * tile + i; /* element within the sequence */
-                uint32_t words[4] = {0, 0, 0, 0};
-                if (r->master_prec == 4 && stochastic) {
-                    const uint32_t ctr[4] = {(uint32_t)(e / 8), (uint32_t)r->seq_id[b], (uint32_t)ck, 0u};
-                    const uint32_t key[2] = {r->seed, 0u};
-                    oracle_philox4x32_10(ctr, key, words);
-                }
-                for (int w = 0; w < 8 && i + w < tile; ++w) {
-                    const float a = v[i + w] * inv;
-                    const uint32_t r16 = (words[w / 2] >> (16 * (w % 2))) & 0xFFFFu;
-                    const uint8_t code = (r->master_prec == 4 && stochastic) ? oracle_e4m3_encode_sr(a, r16)
-                                                                           : oracle_e4m3_encode_scaled(a);
-                    mh[i + w] = (double)oracle_e4m3_decode(code) * (double)scale;
+            for (int kb = 0; kb < nblk; ++kb) {
+                const size_t i0 = (size_t)kb * 64 * r->N;
+                const size_t i1 = (size_t)(kb * 64 + 64 < r->P ? kb * 64 + 64 : r->P) * r->N;
+                const float scale = oracle_e4m3_scale(v + i0, i1 - i0);
+                const float inv = 1.0f / scale;
+                r->mscale[((size_t)b * r->H + h) * nblk + kb] = scale;
+                for (size_t i = i0; i < i1; i += 8) {
+                    const size_t e = (size_t)h * tile + i; /* element within the sequence */
+                    uint32_t words[4] = {0, 0, 0, 0};
+                    if (r->master_prec == 4 && stochastic) {
+                        const uint32_t ctr[4] = {(uint32_t)(e / 8), (uint32_t)r->seq_id[b], (uint32_t)ck, 0u};
+                        const uint32_t key[2] = {r->seed, 0u};
+                        oracle_philox4x32_10(ctr, key, words);
+                    }
+                    for (int w = 0; w < 8 && i + w < i1; ++w) {
+                        const float a = v[i + w] * inv;
+                        const uint32_t r16 = (words[w / 2] >> (16 * (w % 2))) & 0xFFFFu;
+                        const uint8_t code = (r->master_prec == 4 && stochastic) ? oracle_e4m3_encode_sr(a, r16)
+                                                                               : oracle_e4m3_encode_scaled(a);
+                        mh[i + w] = (double)oracle_e4m3_decode(code) * (double)scale;
+                    }
                 }
             }
         }
@@ -586,10 +593,13 @@ static void refresh_copy(oracle_replay *r, int b)
             free(codes);
             free(sc);
         } else {
-            float s = oracle_e4m3_scale(f, tile);
-            float inv = 1.0f / s;
-            for (size_t i = 0; i < tile; ++i)
-                c[i] = (double)oracle_e4m3_decode(oracle_e4m3_encode_scaled(f[i] * inv)) * (double)s;
+            for (int p0 = 0; p0 < r->P; p0 += 64) { /* one scale per block of 64 rows */
+                const size_t i0 = (size_t)p0 * r->N, i1 = (size_t)(p0 + 64 < r->P ? p0 + 64 : r->P) * r->N;
+                const float s = oracle_e4m3_scale(f + i0, i1 - i0);
+                const float inv = 1.0f / s;
+                for (size_t i = i0; i < i1; ++i)
+                    c[i] = (double)oracle_e4m3_decode(oracle_e4m3_encode_scaled(f[i] * inv)) * (double)s;
+            }
         }
     }
     free(f);
@@ -614,7 +624,7 @@ oracle_replay *oracle_replay_create(int Bt, int H, int P, int N, int G, int L, i
     r->D = (double *)malloc(H * sizeof(double));
     for (int h = 0; h < H; ++h) { r->A[h] = A[h]; r->D[h] = D[h]; }
     r->ckpt = (double *)malloc((st ? st : 1) * sizeof(double));
-    r->mscale = (float *)calloc((size_t)Bt * H + 1, sizeof(float));
+    r->mscale = (float *)calloc((size_t)Bt * H * ((P + 63) / 64) + 1, sizeof(float));
     for (size_t i = 0; i < st; ++i) r->ckpt[i] = (double)S0[i];
     r->rcopy = read_prec ? (double *)malloc((st ? st : 1) * sizeof(double)) : NULL;
     r->rx = (float *)malloc(((size_t)Bt * L * H * P + 1) * sizeof(float));
@@ -846,25 +856,27 @@ int oracle_replay_set_checkpoint(oracle_replay *r, const float *S, const int *ro
     return 0;
 }
 
-/* fp8 master (reading R9): export E4M3FN codes [Bt,H,P,N] and scales [Bt,H] -- each value is    */
-/* code * scale exactly, so its code is the nearest-even code of value / scale. -1 otherwise.     */
+/* fp8 master (reading R9): export E4M3FN codes [Bt,H,P,N] and scales [Bt,H,ceil(P/64)] -- each */
+/* value is code * scale exactly, so its code is the nearest-even code of value / scale.        */
+/* -1 for another master precision.                                                             */
 int oracle_replay_master_fp8(const oracle_replay *r, uint8_t *codes, float *scales)
 {
     if (r->master_prec < 3) return -1;
-    const size_t tile = (size_t)r->P * r->N;
-    for (size_t bh = 0; bh < (size_t)r->Bt * r->H; ++bh) {
-        const float s = r->mscale[bh];
-        scales[bh] = s;
-        for (size_t i = 0; i < tile; ++i)
-            codes[bh * tile + i] = oracle_e4m3_encode_scaled((float)(r->ckpt[bh * tile + i] / (double)s));
-    }
+    const int nblk = (r->P + 63) / 64;
+    for (size_t bh = 0; bh < (size_t)r->Bt * r->H; ++bh)
+        for (int p = 0; p < r->P; ++p) {
+            const float s = r->mscale[bh * nblk + p / 64];
+            const size_t row = (bh * r->P + p) * r->N;
+            for (int n = 0; n < r->N; ++n) codes[row + n] = oracle_e4m3_encode_scaled((float)(r->ckpt[row + n] / (double)s));
+        }
+    memcpy(scales, r->mscale, (size_t)r->Bt * r->H * nblk * sizeof(float));
     return 0;
 }
 
 /* fp8 master: set the checkpoints of sequences rows[0..nrows) (all when rows is NULL) to     */
-/* codes [nrows,H,P,N] times scales [nrows,H], exactly in float64; records and pointers stay. */
-/* A test continues the model from the GPU's own fp8 master this way. -1 while a verify is    */
-/* pending, for a row out of range, or for another master precision.                         */
+/* codes [nrows,H,P,N] times scales [nrows,H,ceil(P/64)], exactly in float64; records and      */
+/* pointers stay. A test continues the model from the GPU's own fp8 master this way. -1 while  */
+/* a verify is pending, for a row out of range, or for another master precision.             */
 int oracle_replay_set_master_fp8(oracle_replay *r, const uint8_t *codes, const float *scales, const int *rows,
                                  int nrows)
 {
@@ -872,16 +884,17 @@ int oracle_replay_set_master_fp8(oracle_replay *r, const uint8_t *codes, const f
     if (!rows) nrows = r->Bt;
     for (int i = 0; i < nrows; ++i)
         if (rows && (rows[i] < 0 || rows[i] >= r->Bt)) return -1;
-    const size_t tile = (size_t)r->P * r->N;
+    const int nblk = (r->P + 63) / 64;
     for (int i = 0; i < nrows; ++i) {
         const int b = rows ? rows[i] : i;
-        for (int h = 0; h < r->H; ++h) {
-            const float s = scales[(size_t)i * r->H + h];
-            r->mscale[(size_t)b * r->H + h] = s;
-            for (size_t e = 0; e < tile; ++e)
-                r->ckpt[((size_t)b * r->H + h) * tile + e] =
-                    (double)oracle_e4m3_decode(codes[((size_t)i * r->H + h) * tile + e]) * (double)s;
-        }
+        for (int h = 0; h < r->H; ++h)
+            for (int p = 0; p < r->P; ++p) {
+                const float s = scales[((size_t)i * r->H + h) * nblk + p / 64];
+                r->mscale[((size_t)b * r->H + h) * nblk + p / 64] = s;
+                const size_t src = (((size_t)i * r->H + h) * r->P + p) * r->N;
+                const size_t dst = (((size_t)b * r->H + h) * r->P + p) * r->N;
+                for (int n = 0; n < r->N; ++n) r->ckpt[dst + n] = (double)oracle_e4m3_decode(codes[src + n]) * (double)s;
+            }
     }
     return 0;
 }

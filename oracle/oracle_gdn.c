@@ -23,9 +23,12 @@
  * itself); pointer and flush rules are those of oracle.c (readings R2, R5, R6, R10).
  * Reading G4: as for Mamba-2 ([AT Pulse] "Technical analysis": the recurrence is folded into a
  * full-precision checkpoint while replayed reads may use a narrower copy of it), the replay's
- * checkpoint product S_c z may
- * read a bf16 copy of the checkpoint, written at load and at every flush from the checkpoint
- * rounded to fp32; flushes fold into the checkpoint itself and read their output from it.
+ * checkpoint product S_c z may read a copy of the checkpoint, written at load and at every flush
+ * from the checkpoint rounded to fp32, in one of oracle.c's read-copy formats with the value
+ * index p as the row and the key index n as the column: bf16; fp8 E4M3FN with one scale per
+ * (sequence, value head, block of 64 value rows) (reading R6 there); MXFP4 with one E8M0 scale
+ * per 32 consecutive key indices of a row (reading R7 there; Dk a multiple of 32). Flushes fold
+ * into the checkpoint itself and read their output from it.
  *
  * Layouts (row-major, last index fastest): q, k [Bt,G,Dk]; v [Bt,H,Dv]; alpha, beta [Bt,H];
  * state [Bt,H,Dv,Dk]; o [Bt,H,Dv]. Spec-decode inputs carry the draft index after the batch
@@ -37,9 +40,14 @@
 #include <stdlib.h>
 #include <string.h>
 
-/* bf16 codec of oracle.c (reading R6 there). */
+/* Read-copy codecs of oracle.c (readings R6, R7 there). */
 uint16_t oracle_bf16_encode(float v);
 float oracle_bf16_decode(uint16_t h);
+float oracle_e4m3_scale(const float *tile, size_t n);
+uint8_t oracle_e4m3_encode_scaled(float v);
+float oracle_e4m3_decode(uint8_t code);
+void oracle_encode_mxfp4(const float *in, uint8_t *codes, uint8_t *scales, size_t nblocks);
+void oracle_decode_mxfp4(const uint8_t *codes, const uint8_t *scales, double *out, size_t nblocks);
 
 /* One token of one (sequence, value head): the recurrence G1 on the float64 state S [Dv, Dk]. */
 static void gdn_update_head(int Dv, int Dk, double *S, const float *k, const float *v, double alpha,
@@ -118,9 +126,10 @@ int oracle_gdn_spec_stepwise(int Bt, int H, int G, int Dv, int Dk, int T, double
 /* ------------------------------------------------------------------------------------------- */
 typedef struct oracle_gdn {
     int Bt, H, G, Dv, Dk, L, Tmax;
-    int read_prec;                /* 0: reads from the checkpoint; 1: from its bf16 copy (G4) */
+    int read_prec;                /* 0: reads from the checkpoint; 1 / 2 / 3: from its bf16 / fp8 /
+                                     MXFP4 copy (G4) */
     double *ckpt;                 /* [Bt,H,Dv,Dk] checkpoint */
-    double *rcopy;                /* [Bt,H,Dv,Dk] decoded bf16 copy (read_prec 1) */
+    double *rcopy;                /* [Bt,H,Dv,Dk] decoded copy (read_prec > 0) */
     float *rk, *rv, *ra, *rb;     /* records: [Bt,L,G,Dk], [Bt,L,H,Dv], [Bt,L,H] x 2 */
     int *pos, *ckpt_pos;
     int pending_T;
@@ -144,19 +153,43 @@ static void gdn_poison(oracle_gdn *r, int b, int from)
 }
 
 /* Reading G4: the read copy of sequence b, from its checkpoint rounded to fp32 (the precision the
- * layer keeps it in) and encoded to bf16 by nearest even; written at create and at every flush. */
+ * layer keeps it in), encoded and decoded back; written at create and at every flush. */
 static void gdn_refresh_copy(oracle_gdn *r, int b)
 {
     if (!r->read_prec) return;
-    const size_t n = (size_t)r->H * r->Dv * r->Dk;
-    for (size_t i = (size_t)b * n; i < (size_t)(b + 1) * n; ++i)
-        r->rcopy[i] = (double)oracle_bf16_decode(oracle_bf16_encode((float)r->ckpt[i]));
+    const size_t tile = (size_t)r->Dv * r->Dk;
+    float *f = (float *)malloc(tile * sizeof(float));
+    for (int h = 0; h < r->H; ++h) {
+        const size_t off = ((size_t)b * r->H + h) * tile;
+        for (size_t i = 0; i < tile; ++i) f[i] = (float)r->ckpt[off + i];
+        double *c = r->rcopy + off;
+        if (r->read_prec == 1) {
+            for (size_t i = 0; i < tile; ++i) c[i] = (double)oracle_bf16_decode(oracle_bf16_encode(f[i]));
+        } else if (r->read_prec == 2) {
+            for (int p0 = 0; p0 < r->Dv; p0 += 64) { /* one scale per block of 64 value rows */
+                const size_t i0 = (size_t)p0 * r->Dk, i1 = (size_t)(p0 + 64 < r->Dv ? p0 + 64 : r->Dv) * r->Dk;
+                const float s = oracle_e4m3_scale(f + i0, i1 - i0);
+                const float inv = 1.0f / s;
+                for (size_t i = i0; i < i1; ++i)
+                    c[i] = (double)oracle_e4m3_decode(oracle_e4m3_encode_scaled(f[i] * inv)) * (double)s;
+            }
+        } else {
+            /* blocks of 32 along the key index never cross a row, since Dk is a multiple of 32 */
+            const size_t nb = tile / 32;
+            uint8_t *codes = (uint8_t *)malloc(nb * 16), *sc = (uint8_t *)malloc(nb);
+            oracle_encode_mxfp4(f, codes, sc, nb);
+            oracle_decode_mxfp4(codes, sc, c, nb);
+            free(codes);
+            free(sc);
+        }
+    }
+    free(f);
 }
 
 oracle_gdn *oracle_gdn_create(int Bt, int H, int G, int Dv, int Dk, int L, int Tmax, const float *S0, int read_prec)
 {
     if (Bt < 0 || H <= 0 || G <= 0 || H % G || Dv <= 0 || Dk <= 0 || L <= 0 || L > 64 || Tmax <= 0 ||
-        Tmax > L || read_prec < 0 || read_prec > 1)
+        Tmax > L || read_prec < 0 || read_prec > 3 || (read_prec == 3 && Dk % 32))
         return NULL;
     oracle_gdn *r = (oracle_gdn *)calloc(1, sizeof(oracle_gdn));
     r->Bt = Bt; r->H = H; r->G = G; r->Dv = Dv; r->Dk = Dk; r->L = L; r->Tmax = Tmax;
@@ -359,7 +392,7 @@ void oracle_gdn_replay_materialize(const oracle_gdn *r, double *out)
     for (int b = 0; b < r->Bt; ++b) gdn_fold_into(r, b, r->pos[b] - r->ckpt_pos[b], out);
 }
 
-/* The decoded read copy (read_prec 1) into out [Bt,H,Dv,Dk]. */
+/* The decoded read copy (read_prec > 0) into out [Bt,H,Dv,Dk]. */
 void oracle_gdn_replay_read_copy(const oracle_gdn *r, double *out)
 {
     if (r->read_prec) memcpy(out, r->rcopy, (size_t)r->Bt * r->H * r->Dv * r->Dk * sizeof(double));

@@ -12,6 +12,11 @@ MASTER_CODE = {"fp32": oracle.MASTER_FP32, "fp16": oracle.MASTER_FP16, "fp16_sr"
                "fp8": oracle.MASTER_FP8, "fp8_sr": oracle.MASTER_FP8_SR}
 
 
+def row_scales(scales, P):
+    """Per-block fp8 scales [..., ceil(P/64)] as float64 per row [..., P, 1] (block = 64 rows)."""
+    return np.repeat(np.asarray(scales, np.float64), 64, axis=-1)[..., :P, None]
+
+
 def fp8_master(lay, sample):
     """An fp8 master's E4M3FN codes [n,H,P,N] and per-head scales [n,H] of the sampled rows."""
     idx = torch.as_tensor(np.asarray(sample), device="cuda")
@@ -22,7 +27,7 @@ def master_values(lay, master, sample):
     """The sampled rows of the stored checkpoint as float64 values (fp8: code * scale, exact)."""
     if master in ("fp8", "fp8_sr"):
         codes, scales = fp8_master(lay, sample)
-        return oracle.e4m3_decode_table().astype(np.float64)[codes] * scales[:, :, None, None].astype(np.float64)
+        return oracle.e4m3_decode_table().astype(np.float64)[codes] * row_scales(scales, codes.shape[2])
     idx = torch.as_tensor(np.asarray(sample), device="cuda")
     return host(lay.master()[idx]).astype(np.float64)
 
@@ -74,8 +79,8 @@ def assert_copy_encodes(lay, prec, m, sample, what=""):
         ok = np.array_equal(got, oracle.bf16_encode(m).view(np.int16))
         assert ok, f"{what}: bf16 copy differs from the encoded master"
     elif prec == "fp8":
-        codes, scales = oracle.e4m3_encode_tiles(m, m.shape[2] * m.shape[3])
-        assert np.array_equal(host(lay.scales()[idx]).reshape(-1), scales), f"{what}: fp8 scales differ"
+        codes, scales = oracle.e4m3_encode_rows(m)
+        assert np.array_equal(host(lay.scales()[idx]), scales), f"{what}: fp8 scales differ"
         assert np.array_equal(got.reshape(-1), codes), f"{what}: fp8 codes differ from the encoded master"
     elif prec == "mxfp4":
         codes, scales = oracle.mxfp4_encode(m)

@@ -250,3 +250,80 @@ def test_set_checkpoint_restarts_the_model():
     for t in range(L, 2 * L - 1):
         ins = _inputs(seed, Bt, H, G, Dv, Dk, t)
         assert np.array_equal(a.step(*ins), b.step(*ins)), t
+
+
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _mxfp4_round_trip(S):
+    """OCP MX v1.0 FP4 by its definition, in numpy: blocks of 32 consecutive values of the last
+    axis, scale 2^(E - 2) with E the unbiased exponent of the block's amax read from its fp32
+    bits (an all-zero block takes the smallest scale), each value / scale to the nearest E2M1
+    magnitude with ties to the even code, clamped to 6, sign kept."""
+    S = np.asarray(S, np.float32)
+    blk = S.reshape(-1, 32).astype(np.float64)
+    amax = np.abs(blk).max(axis=1).astype(np.float32)
+    ebits = ((amax.view(np.uint32) >> 23) & 0xFF).astype(np.int64)
+    code = np.maximum(ebits - 2, 0)
+    scale = np.exp2((code - 127).astype(np.float64))[:, None]
+    a = np.minimum(np.abs(blk) / scale, 6.0)
+    d = np.abs(a[..., None] - _E2M1)
+    best = d.min(axis=-1, keepdims=True)
+    cand = np.where(d == best, np.arange(8), 99)
+    ties_even = np.where(cand % 2 == 0, cand, 99).min(axis=-1)
+    idx = np.where(ties_even < 99, ties_even, cand.min(axis=-1))
+    return (np.sign(blk) * _E2M1[idx] * scale).reshape(S.shape)
+
+
+def _fp8_round_trip(S):
+    """The fp8 copy by its recipe with PyTorch's float8_e4m3fn conversion: one scale amax / 448
+    per block of 64 value rows of each (sequence, value head)."""
+    import torch
+    S = np.asarray(S, np.float32)
+    out = np.empty(S.shape, np.float64)
+    for p0 in range(0, S.shape[2], 64):
+        blk = S[:, :, p0:p0 + 64, :]
+        amax = np.abs(blk).max(axis=(2, 3), keepdims=True)
+        scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+        a = np.clip(blk * (np.float32(1.0) / scale), -448.0, 448.0).astype(np.float32)
+        out[:, :, p0:p0 + 64, :] = torch.from_numpy(a).to(torch.float8_e4m3fn).double().numpy() * scale
+    return out
+
+
+@pytest.mark.parametrize("read_prec,gate", [(oracle.READ_FP8, 6e-2), (oracle.READ_MXFP4, 0.25)])
+def test_narrow_read_copy_models(read_prec, gate):
+    """Reading G4 with the fp8 and MXFP4 copies (Dv = 80: two fp8 scale blocks, one partial; Dk =
+    64: two MX blocks per row): the copy equals the format's definition applied to S0 (fp8 per
+    64 value rows with PyTorch's e4m3 conversion; MXFP4 by the OCP rule in numpy); before the
+    first flush every output equals the fp32-checkpoint replay started from that decoded copy --
+    bit for bit for MXFP4, within 1e-6 for fp8, whose decoded values fp32 rounds; flush steps
+    read the folded checkpoint (= the fp32 replay from S0); after a
+    flush the copy is the definition applied to the float32-rounded checkpoint; outputs stay
+    within the copy's gate of O1g."""
+    Bt, H, G, Dv, Dk, L = 2, 4, 2, 80, 64, 4
+    seed = 29
+    S0 = workload.gdn_initial_state(seed, Bt, H, Dv, Dk)
+    enc = _fp8_round_trip if read_prec == oracle.READ_FP8 else _mxfp4_round_trip
+    S0_c = enc(S0)
+    cp = oracle.GDNReplay(S0, G, L, 1, read_prec)
+    from_c = oracle.GDNReplay(S0_c.astype(np.float32), G, L, 1)
+    full = oracle.GDNReplay(S0, G, L, 1)
+    # MXFP4 values (E2M1 times a power of two) are fp32 numbers, so the fp32 replay from the copy
+    # is the same model bit for bit; an fp8 value code * scale carries up to 28 significant bits,
+    # which the fp32 start state rounds (2^-24 relative)
+    exact = bool(np.array_equal(S0_c.astype(np.float32).astype(np.float64), S0_c))
+    assert exact == (read_prec == oracle.READ_MXFP4)
+    S = S0.astype(np.float64)
+    assert np.array_equal(cp.read_copy(), S0_c)
+    for t in range(3 * L):
+        ins = _inputs(seed, Bt, H, G, Dv, Dk, t)
+        o, o_c, o_full = cp.step(*ins), from_c.step(*ins), full.step(*ins)
+        o_true = oracle.gdn_step(S, *ins)
+        if t < L - 1:
+            assert np.array_equal(o, o_c) if exact else _rel(o, o_c) <= 1e-6, t
+        if (t + 1) % L == 0:
+            assert _rel(o, o_full) <= 1e-12, t
+            assert np.array_equal(cp.read_copy(), enc(cp.checkpoint().astype(np.float32))), t
+        assert _rel(o, o_true) <= gate, t
+    with pytest.raises(ValueError):
+        oracle.GDNReplay(workload.gdn_initial_state(seed, 1, 2, 16, 16), 1, 4, 1, oracle.READ_MXFP4)

@@ -366,7 +366,8 @@ def test_fp8_master_export_and_import():
         if t < L - 1:
             b.step(*ins)
     codes, scales = a.fp8_master()
-    assert np.array_equal(table[codes] * scales[:, :, None, None].astype(np.float64), a.checkpoint())
+    assert scales.shape == (Bt, H, 1)
+    assert np.array_equal(table[codes] * scales[:, :, :, None].astype(np.float64), a.checkpoint())
     with pytest.raises(RuntimeError):
         oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP16).fp8_master()
     # b is one token short of a's flush; it takes a's post-flush state for rows 2 and 0 after
@@ -379,3 +380,23 @@ def test_fp8_master_export_and_import():
         ins = workload.step_inputs(seed, t, Bt, H, P, N, G)
         assert np.array_equal(a.step(*ins), b.step(*ins))
     assert np.array_equal(b.checkpoint(), a.checkpoint())
+
+
+def test_fp8_master_blocks_of_64_rows():
+    """Reading R9 with P = 100: the fp8 master's load takes the fp8 copy's per-block scales (rows
+    0..63 and 64..99), codes against PyTorch's float8_e4m3fn of each block over its amax / 448."""
+    import torch
+    Bt, H, P, N, G, L = 2, 2, 100, 32, 1, 4
+    seed = 73
+    S0 = workload.initial_state(seed, Bt, H, P, N)
+    A, D = workload.layer_params(seed, H)
+    r = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP32, oracle.MASTER_FP8)
+    codes, scales = r.fp8_master()
+    assert scales.shape == (Bt, H, 2)
+    for kb, (p0, p1) in enumerate([(0, 64), (64, 100)]):
+        blk = S0[:, :, p0:p1, :]
+        scale = (np.abs(blk).max(axis=(2, 3)) / np.float32(448.0)).astype(np.float32)
+        assert np.array_equal(scales[:, :, kb], scale)
+        a = np.clip(blk * (np.float32(1.0) / scale[:, :, None, None]), -448.0, 448.0).astype(np.float32)
+        want = torch.from_numpy(a).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(codes[:, :, p0:p1, :], want), f"block {kb}"

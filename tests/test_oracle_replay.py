@@ -318,3 +318,31 @@ def test_set_checkpoint_of_selected_rows():
     assert np.array_equal(cp[[2, 0]], oracle.Replay(S1, A, D, G, L, 1, oracle.READ_FP8).read_copy())
     with pytest.raises(RuntimeError):
         a.set_checkpoint(S1, [2, 3])
+
+
+def test_fp8_copy_scales_per_64_row_block():
+    """Reading R6 for P > 64: the fp8 copy of a head with P = 100 rows takes one scale per block
+    of 64 rows (rows 0..63 and 64..99), each amax / 448 of its block; codes against PyTorch's
+    float8_e4m3fn of the block divided by its scale (a library rounding), both blocks. A state
+    whose two blocks differ in magnitude by 2^10 keeps the small block at full fp8 resolution
+    (a per-head scale would flush most of it to zero)."""
+    import torch
+    Bt, H, P, N, G, L = 2, 3, 100, 32, 1, 4
+    seed = 71
+    S0, A, D = _setup(seed, Bt, H, P, N, G)
+    S0[:, :, 64:, :] *= 2.0 ** -10
+    rep = oracle.Replay(S0, A, D, G, L, 1, oracle.READ_FP8)
+    got = rep.read_copy()
+    for kb, (p0, p1) in enumerate([(0, 64), (64, 100)]):
+        blk = S0[:, :, p0:p1, :]
+        amax = np.abs(blk).max(axis=(2, 3), keepdims=True)
+        scale = (amax / np.float32(448.0)).astype(np.float32)
+        a = np.clip(blk * (np.float32(1.0) / scale), -448.0, 448.0).astype(np.float32)
+        q = torch.from_numpy(a).to(torch.float8_e4m3fn).double().numpy()
+        assert np.array_equal(got[:, :, p0:p1, :], q * scale.astype(np.float64)), f"block {kb}"
+    small = got[:, :, 64:, :]
+    assert np.mean(small == 0) < 0.01
+    codes, scales = oracle.e4m3_encode_rows(S0)
+    assert scales.shape == (Bt, H, 2)
+    table = oracle.e4m3_decode_table().astype(np.float64)
+    assert np.array_equal(table[codes] * np.repeat(scales, 64, axis=-1)[..., :P, None], got)
