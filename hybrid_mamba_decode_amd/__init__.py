@@ -67,8 +67,8 @@ class GDNConfig(ctypes.Structure):
 
 class GDNLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "master", "read_copy", "ring_k", "ring_v", "ring_a", "ring_b", "pos", "ckpt_pos", "counters", "flag",
-        "total")]
+        "master", "read_copy", "scale", "ring_k", "ring_v", "ring_a", "ring_b", "pos", "ckpt_pos", "counters",
+        "flag", "total")]
 
 
 _vp = ctypes.c_void_p
@@ -685,12 +685,30 @@ class GDNReplay:
         return self.workspace[off:off + 4 * n].view(torch.float32).view(self.batch, self.nheads, self.dv, self.dk)
 
     def read_copy(self):
-        """The bf16 read copy as bit patterns (int16 [Bt,H,Dv,Dk]), or None with fp32 reads."""
-        if self.cfg.read_prec != READ_BF16:
-            return None
+        """The read copy in row-major order (value rows of Dk key columns): bf16 bits int16
+        [Bt,H,Dv,Dk] (a view of the workspace), fp8 codes uint8 [Bt,H,Dv,Dk] or MXFP4 code bytes
+        uint8 [Bt,H,Dv,Dk/2] (reordered copies of the chunked codes); None with fp32 reads."""
+        Bt, H, Dv, Dk = self.batch, self.nheads, self.dv, self.dk
         off = self.layout.read_copy
-        n = self.batch * self.nheads * self.dv * self.dk
-        return self.workspace[off:off + 2 * n].view(torch.int16).view(self.batch, self.nheads, self.dv, self.dk)
+        if self.cfg.read_prec == READ_BF16:
+            return self.workspace[off:off + 2 * Bt * H * Dv * Dk].view(torch.int16).view(Bt, H, Dv, Dk)
+        if self.cfg.read_prec in (READ_FP8_E4M3, READ_MXFP4):
+            row_bytes = Dk if self.cfg.read_prec == READ_FP8_E4M3 else Dk // 2
+            raw = self.workspace[off:off + Bt * H * Dv * row_bytes].view(Bt, H, row_bytes // 16, Dv, 16)
+            return raw.permute(0, 1, 3, 2, 4).contiguous().view(Bt, H, Dv, row_bytes)
+        return None
+
+    def scales(self):
+        """fp8: fp32 scales [Bt,H,ceil(Dv/64)]; MXFP4: E8M0 block-scale bytes [Bt,H,Dv,Dk/32];
+        None otherwise."""
+        Bt, H, Dv, Dk = self.batch, self.nheads, self.dv, self.dk
+        off = self.layout.scale
+        if self.cfg.read_prec == READ_FP8_E4M3:
+            nb = (Dv + 63) // 64
+            return self.workspace[off:off + 4 * Bt * H * nb].view(torch.float32).view(Bt, H, nb)
+        if self.cfg.read_prec == READ_MXFP4:
+            return self.workspace[off:off + Bt * H * Dv * Dk // 32].view(Bt, H, Dv, Dk // 32)
+        return None
 
     def pointer_arrays(self):
         def region(off, n):

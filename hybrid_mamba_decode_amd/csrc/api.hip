@@ -59,13 +59,10 @@ rssm_status check_config(const replayssm_config *c)
     if (c->read_prec < RSSM_READ_FP32 || c->read_prec > RSSM_READ_MXFP4) return RSSM_E_INVAL;
     if (c->store_C != 0 && c->store_C != 1) return RSSM_E_INVAL;
     if (c->buffer_len > 64 || c->max_draft > 8) return RSSM_E_UNSUPPORTED;
-    if (c->read_prec == RSSM_READ_FP8_E4M3 && c->headdim > kRows) return RSSM_E_UNSUPPORTED;
     if (c->read_prec == RSSM_READ_MXFP4 && c->dstate < 32) return RSSM_E_UNSUPPORTED;
     if (c->master_prec < RSSM_MASTER_FP32 || c->master_prec > RSSM_MASTER_FP8_SR) return RSSM_E_INVAL;
-    // an fp8 master is its own read copy: no second copy; the head's amax needs its P rows in one
-    // work-group, as the fp8 copy does
+    // an fp8 master is its own read copy: no second copy
     if (c->master_prec >= RSSM_MASTER_FP8 && c->read_prec != RSSM_READ_FP32) return RSSM_E_INVAL;
-    if (c->master_prec >= RSSM_MASTER_FP8 && c->headdim > kRows) return RSSM_E_UNSUPPORTED;
     if (c->d_conv < 0 || c->d_conv == 1) return RSSM_E_INVAL;
     if (c->d_conv > 4 || (c->d_conv > 0 && c->buffer_len > 32)) return RSSM_E_UNSUPPORTED;
     return RSSM_OK;
@@ -101,7 +98,7 @@ void make_layout(const replayssm_config &c, replayssm_layout *L)
     const int rp = fp8_master(c) ? RSSM_READ_FP8_E4M3 : c.read_prec;
     L->read_copy = take(fp8_master(c) ? 0 : rp == RSSM_READ_BF16 ? elems * 2 : rp == RSSM_READ_FP8_E4M3 ? elems
                         : rp == RSSM_READ_MXFP4 ? elems / 2 : 0);
-    L->scale = take(rp == RSSM_READ_FP8_E4M3 ? Bt * H * 4 : rp == RSSM_READ_MXFP4 ? elems / 32 : 0);
+    L->scale = take(rp == RSSM_READ_FP8_E4M3 ? Bt * H * psplit_of(c) * 4 : rp == RSSM_READ_MXFP4 ? elems / 32 : 0);
     L->ring_x = take(Bt * H * Lb * P * 4);
     L->ring_B = take(Bt * G * Lb * N * 4);
     L->ring_C = take(c.store_C ? Bt * G * Lb * N * 4 : 0);

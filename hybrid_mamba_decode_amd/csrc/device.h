@@ -536,4 +536,123 @@ __device__ inline void raise_flag(const Layer &Ld, unsigned bits)
 
 __device__ inline float fast_exp(float v) { return __expf(v); }
 
+// ------------------------------------------------------------------------------------------
+// State arrays and read copies, shared by the Mamba-2 (P rows of N) and Gated DeltaNet (Dv value
+// rows of Dk key columns) kernels.
+//
+// Byte offset of element e of a state array in precision PREC (fp4: two elements per byte; e is
+// always a chunk start, hence even).
+// ------------------------------------------------------------------------------------------
+template <int PREC>
+constexpr size_t state_byte_off(size_t e)
+{
+    return PREC == PREC_F32 ? e * 4 : (PREC == PREC_BF16 || PREC == PREC_F16) ? e * 2 : PREC == PREC_FP8 ? e : e / 2;
+}
+
+// Byte offset of 16-byte chunk q (elements [q*VEC, (q+1)*VEC)) of row p of head bh in a state
+// array of precision PREC with N columns and P rows per head. The fp32 master and the bf16 copy
+// are row-major ([P][N] per head). The fp8 and MXFP4 copies are chunk-column-major per head
+// ([N/VEC][P] chunks): one wave instruction over 64 consecutive rows of one chunk column then
+// reads 1 KiB contiguously, which is what a one-row-per-lane kernel issues; lane-along-N kernels
+// read them in runs of RPI rows (128-256 bytes).
+template <int N, int PREC>
+__device__ inline size_t state_chunk_off(size_t bh, int p, int q, int P)
+{
+    using G = Geo<N, PREC>;
+    const size_t head = state_byte_off<PREC>(bh * (size_t)P * N);
+    if constexpr (PREC == PREC_FP8 || PREC == PREC_FP4) return head + ((size_t)q * P + p) * 16;
+    else return head + ((size_t)p * (N / G::VEC) + q) * 16;
+}
+
+// A layer's read copy as a write destination: codes, fp8 scales [Bt,H,psplit] (one per block of
+// kRows rows), MXFP4 scale bytes [Bt,H,P,N/32], rows per head and row blocks per head.
+struct CopyDst {
+    void *rcopy;
+    float *scale;
+    unsigned char *mxscale;
+    int P, psplit;
+};
+
+// Read-copy writer for fp32 rows of one work-group's tile held in f32 geometry (vf; lane slot i
+// holds row i*RPB + wave*RPI + lane/LPR, four values from n = 4 (lane % LPR)), the tile's first
+// element at `elem0` of head bh. The tile is one block of kRows rows (tiles start at row 0).
+// bf16: each value to nearest even. fp8: the block's scale = amax / 448 over the work-group, codes
+// RNE-saturated by gfx950's converter. MXFP4: one E8M0 scale per 32 values of a row.
+template <int N, int PREC>
+__device__ inline void write_copy_rows_n(const CopyDst &d, size_t bh, size_t elem0,
+                                         const f32x4 (&vf)[Geo<N, PREC_F32>::NL], int nrows, int wave, int lane,
+                                         float *red)
+{
+    using GF = Geo<N, PREC_F32>;
+    const int c = lane % GF::LPR;
+    auto row_of = [&](int i) { return i * GF::RPB + wave * GF::RPI + lane / GF::LPR; };
+    if constexpr (PREC == PREC_BF16) {
+        unsigned short *dst = (unsigned short *)d.rcopy + elem0;
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            const int r = row_of(i);
+            if (r < nrows) {
+                const f32x4 f = vf[i];
+                u32x2 pk;
+                pk.x = bf16_rne(f.x) | (bf16_rne(f.y) << 16);
+                pk.y = bf16_rne(f.z) | (bf16_rne(f.w) << 16);
+                *(u32x2 *)(dst + (size_t)r * N + 4 * c) = pk;
+            }
+        }
+    } else if constexpr (PREC == PREC_FP8) {
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            const f32x4 f = vf[i];
+            const float m = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
+            if (row_of(i) < nrows) amax = fmaxf(amax, m);
+        }
+        amax = block_max(amax, red);
+        const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
+        const float inv = 1.0f / scale;
+        unsigned char *dst = (unsigned char *)d.rcopy;
+        const int row0 = (int)(elem0 / N - bh * (size_t)d.P);
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            const int r = row_of(i);
+            if (r < nrows) {
+                const f32x4 f = vf[i];
+                // clamp to the largest finite code, then the converter rounds to nearest even
+                // (four codes per dword, two per instruction)
+                const float a0 = fminf(fmaxf(f.x * inv, -448.0f), 448.0f);
+                const float a1 = fminf(fmaxf(f.y * inv, -448.0f), 448.0f);
+                const float a2 = fminf(fmaxf(f.z * inv, -448.0f), 448.0f);
+                const float a3 = fminf(fmaxf(f.w * inv, -448.0f), 448.0f);
+                int q = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+                q = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, q, true);
+                const int n = 4 * c;
+                *(unsigned *)(dst + state_chunk_off<N, PREC_FP8>(bh, row0 + r, n / 16, d.P) + n % 16) = (unsigned)q;
+            }
+        }
+        if (threadIdx.x == 0) d.scale[bh * d.psplit + row0 / kRows] = scale;
+    } else if constexpr (PREC == PREC_FP4) {
+        // One 32-value block = 8 consecutive lanes of a row (4 values each); its amax by three
+        // lane exchanges, then each lane encodes its 4 values into 2 bytes and the block's first
+        // lane writes the scale byte.
+        unsigned char *dst = (unsigned char *)d.rcopy;
+        unsigned char *sdst = d.mxscale + elem0 / 32;
+        const int row0 = (int)(elem0 / N - bh * (size_t)d.P);
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            const int r = row_of(i);
+            const f32x4 f = vf[i];
+            float amax = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
+            amax = group_max(amax, 8);
+            const unsigned code = mx_code_of(amax);
+            if (r < nrows) {
+                const int n = 4 * c;
+                *(unsigned short *)(dst + state_chunk_off<N, PREC_FP4>(bh, row0 + r, n / 32, d.P) + (n % 32) / 2) =
+                    mx_encode4(f, code);
+                if (c % 8 == 0) sdst[((size_t)r * N + n) / 32] = (unsigned char)code;
+            }
+        }
+        (void)red;
+    }
+}
+
 }  // namespace rssm

@@ -44,7 +44,8 @@ rssm_status check_config(const gdnreplay_config *c)
     if (s != RSSM_OK) return s;
     if (c->buffer_len < 1 || c->max_draft < 1 || c->max_draft > c->buffer_len) return RSSM_E_INVAL;
     if (c->buffer_len > 64 || c->max_draft > 8) return RSSM_E_UNSUPPORTED;
-    if (c->read_prec != RSSM_READ_FP32 && c->read_prec != RSSM_READ_BF16) return RSSM_E_INVAL;
+    if (c->read_prec < RSSM_READ_FP32 || c->read_prec > RSSM_READ_MXFP4) return RSSM_E_INVAL;
+    if (c->read_prec == RSSM_READ_MXFP4 && c->dk < 32) return RSSM_E_UNSUPPORTED;  // blocks of 32 key columns
     return RSSM_OK;
 }
 
@@ -53,8 +54,12 @@ void make_layout(const gdnreplay_config &c, gdnreplay_layout *L)
     const size_t Bt = (size_t)c.batch, H = c.nheads, G = c.nkheads, Dv = c.dv, Dk = c.dk, Lb = c.buffer_len;
     RegionCarver rc;
     auto take = [&](size_t bytes) { return rc.take(bytes); };
-    L->master = take(Bt * H * Dv * Dk * 4);
-    L->read_copy = take(c.read_prec == RSSM_READ_BF16 ? Bt * H * Dv * Dk * 2 : 0);
+    const size_t elems = Bt * H * Dv * Dk;
+    const int rp = c.read_prec;
+    L->master = take(elems * 4);
+    L->read_copy = take(rp == RSSM_READ_BF16 ? elems * 2 : rp == RSSM_READ_FP8_E4M3 ? elems
+                        : rp == RSSM_READ_MXFP4 ? elems / 2 : 0);
+    L->scale = take(rp == RSSM_READ_FP8_E4M3 ? Bt * H * psplit_of(c) * 4 : rp == RSSM_READ_MXFP4 ? elems / 32 : 0);
     L->ring_k = take(Bt * G * Lb * Dk * 4);
     L->ring_v = take(Bt * H * Lb * Dv * 4);
     L->ring_a = take(Bt * H * Lb * 4);
@@ -143,8 +148,12 @@ rssm_status gdnreplay_create(const gdnreplay_config *cfg, void *workspace, size_
     char *ws = (char *)workspace;
     GLayer &d = h->dev;
     d.master = (float *)(ws + lay.master);
-    d.rprec = cfg->read_prec == RSSM_READ_BF16 ? 1 : 0;
-    d.rcopy = d.rprec ? (unsigned short *)(ws + lay.read_copy) : nullptr;
+    static_assert(PREC_BF16 == RSSM_READ_BF16 && PREC_FP8 == RSSM_READ_FP8_E4M3 && PREC_FP4 == RSSM_READ_MXFP4,
+                  "read precisions map onto the kernels' codes");
+    d.rprec = cfg->read_prec;
+    d.rcopy = d.rprec ? (void *)(ws + lay.read_copy) : nullptr;
+    d.scale = d.rprec == PREC_FP8 ? (float *)(ws + lay.scale) : nullptr;
+    d.mxscale = d.rprec == PREC_FP4 ? (unsigned char *)(ws + lay.scale) : nullptr;
     d.ring_k = (float *)(ws + lay.ring_k);
     d.ring_v = (float *)(ws + lay.ring_v);
     d.ring_a = (float *)(ws + lay.ring_a);

@@ -19,7 +19,8 @@
 //                         buffer fills and reads their output from the folded state
 //   gdn_flush_kernel      explicit flush, rollback commit, or materialize
 //   gdn_verify_kernel     output-only evaluation of T draft tokens + tentative append
-//   gdn_step_copy_kernel, gdn_verify_copy_kernel   the same through the bf16 copy, 128-row tiles
+//   gdn_step_copy_kernel, gdn_verify_copy_kernel   the same through a bf16 / fp8 / MXFP4 copy,
+//                         128-row tiles
 //   gdn_load_kernel       master <- state, pointers reset
 //   gdn_conventional_kernel   read-update-write baseline
 //   gdn_snapshot_kernel   per-draft snapshot baseline (one read, T writes)
@@ -255,26 +256,59 @@ __device__ inline void load_rows_bf16(f32x4 (&vf)[GF::NL], const unsigned short 
     }
 }
 
-// The bf16 copy of fp32 rows: each value rounded to nearest, ties to even.
-__device__ inline void store_rows_bf16(unsigned short *rows, const f32x4 (&vf)[GF::NL], int nrows, int wave, int lane)
+// Store folded master rows of head bh and, with a read copy, their encoding (write_copy_rows_n:
+// bf16, fp8 with this 64-row block's scale, MXFP4). red: kWaves floats of LDS for the fp8 amax.
+__device__ inline void store_checkpoint(const GLayer &Ld, size_t bh, size_t elem0, const f32x4 (&vf)[GF::NL],
+                                        int nrows, int wave, int lane, float *red)
 {
-    const int c = lane % GF::LPR;
-#pragma unroll
-    for (int i = 0; i < GF::NL; ++i) {
-        const int r = row_of_f32(i, wave, lane);
-        if (r < nrows) {
-            const u32x2 w = {bf16_rne(vf[i].x) | (bf16_rne(vf[i].y) << 16), bf16_rne(vf[i].z) | (bf16_rne(vf[i].w) << 16)};
-            __builtin_nontemporal_store(w, (u32x2 *)(rows + (size_t)r * NN + 4 * c));
-        }
+    store_rows(Ld.master + elem0, vf, nrows, wave, lane);
+    const CopyDst d{Ld.rcopy, Ld.scale, Ld.mxscale, Ld.Dv, Ld.psplit};
+    switch (Ld.rprec) {
+    case PREC_BF16: write_copy_rows_n<NN, PREC_BF16>(d, bh, elem0, vf, nrows, wave, lane, red); break;
+    case PREC_FP8: write_copy_rows_n<NN, PREC_FP8>(d, bh, elem0, vf, nrows, wave, lane, red); break;
+    case PREC_FP4:
+        if constexpr (NN >= 32) write_copy_rows_n<NN, PREC_FP4>(d, bh, elem0, vf, nrows, wave, lane, red);
+        break;
+    default: break;
     }
 }
 
-// Store folded master rows and, with a read copy, its bf16 encoding.
-__device__ inline void store_checkpoint(const GLayer &Ld, size_t elem0, const f32x4 (&vf)[GF::NL], int nrows, int wave,
-                                        int lane)
+// Rows of a tile of head bh through the read copy, decoded exactly into f32 geometry (4 values
+// per lane and slot; rows beyond the tile as in load_rows_f32): bf16 widened; fp8 codes (4 bytes
+// of the row's chunk) times the block's scale; MXFP4 codes (2 bytes) times 2^(code - 127) of
+// their block.
+template <int RP>
+__device__ inline void load_rows_copy(f32x4 (&vf)[GF::NL], const GLayer &Ld, size_t bh, int row0, int nrows, int wave,
+                                      int lane)
 {
-    store_rows(Ld.master + elem0, vf, nrows, wave, lane);
-    if (Ld.rprec) store_rows_bf16(Ld.rcopy + elem0, vf, nrows, wave, lane);
+    const int n = 4 * (lane % GF::LPR);
+    if constexpr (RP == PREC_BF16) {
+        load_rows_bf16(vf, (const unsigned short *)Ld.rcopy + (bh * Ld.Dv + row0) * NN, nrows, wave, lane);
+    } else if constexpr (RP == PREC_FP8) {
+        const unsigned char *src = (const unsigned char *)Ld.rcopy;
+        const float scale = Ld.scale[bh * Ld.psplit + row0 / kRows];
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            const int r = row_of_f32(i, wave, lane), rr = r < nrows ? r : 0;
+            const unsigned w = __builtin_nontemporal_load(
+                (const unsigned *)(src + state_chunk_off<NN, PREC_FP8>(bh, row0 + rr, n / 16, Ld.Dv) + n % 16));
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+            vf[i] = f32x4{lo.x * scale, lo.y * scale, hi.x * scale, hi.y * scale};
+        }
+    } else if constexpr (RP == PREC_FP4) {
+        const unsigned char *src = (const unsigned char *)Ld.rcopy;
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) {
+            const int r = row_of_f32(i, wave, lane), rr = r < nrows ? r : 0;
+            const unsigned w = __builtin_nontemporal_load((const unsigned short *)(
+                src + state_chunk_off<NN, PREC_FP4>(bh, row0 + rr, n / 32, Ld.Dv) + (n % 32) / 2));
+            const unsigned code = Ld.mxscale[(bh * Ld.Dv + row0 + rr) * (NN / 32) + n / 32];
+            const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+            const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+            vf[i] = f32x4{mx_scaled(a.x, code), mx_scaled(a.y, code), mx_scaled(b.x, code), mx_scaled(b.y, code)};
+        }
+    }
 }
 
 // Row dots of the tile with M vectors (vectors[m] in LDS, NN floats each), reduced into
@@ -322,6 +356,7 @@ struct GStepLds {
     float z[NN] __attribute__((aligned(16)));
     float c[LMAX];
     float u[RT];
+    float red[kWaves];
 };
 
 // The step's window staged through registers: issued before the checkpoint stream (global loads
@@ -460,11 +495,12 @@ __device__ inline void step_output_append(const GStepLds<LMAX, RT> &s, const GLa
         *(f32x4 *)(Ld.ring_k + (bg * Ld.L + pslot) * NN + 4 * tid) = *(const f32x4 *)&s.w.K[k - 1][4 * tid];
 }
 
-// CP: the checkpoint product reads the bf16 copy (replayed outputs; a flushing sequence reads and
-// folds the fp32 master).
-template <int LMAX, bool FLUSH, bool CP>
+// RP: the read copy's precision (PREC_F32: none). With a copy the checkpoint product reads it
+// (replayed outputs); a flushing sequence reads and folds the fp32 master.
+template <int LMAX, bool FLUSH, int RP>
 __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO io, Lockstep ls)
 {
+    constexpr bool CP = RP != PREC_F32;
     __shared__ GStepLds<LMAX> s;
     const Tile t = gmap_tile(Ld);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -472,7 +508,7 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
     const size_t elem0 = (bh * Ld.Dv + t.row0) * NN;
     float *rows = Ld.master + elem0;
     auto load_state = [&](f32x4 (&dst)[GF::NL], bool master) {
-        if (CP && !master) load_rows_bf16(dst, Ld.rcopy + elem0, t.nrows, wave, lane);
+        if (CP && !master) load_rows_copy<RP>(dst, Ld, bh, t.row0, t.nrows, wave, lane);
         else load_rows_f32(dst, rows, t.nrows, wave, lane);
     };
 
@@ -512,7 +548,7 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
 
     if (FLUSH && flush) {
         gdn_fold_rows<LMAX>(vf, s.w, k, wave, lane);
-        store_checkpoint(Ld, elem0, vf, t.nrows, wave, lane);
+        store_checkpoint(Ld, bh, elem0, vf, t.nrows, wave, lane, s.red);
         rows_dot<1>(vf, s.q, 1, s.u, wave, lane);
         __syncthreads();
         if (tid < t.nrows) io.o[bh * Ld.Dv + t.row0 + tid] = s.u[tid];
@@ -530,35 +566,69 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
     step_advance(Ld, t, uni, pslot, cslot, k, flush, pos, ck, Ld.psplit);
 }
 
-// Non-flush step reading the bf16 copy with one work-group per kRowsC = 128 value rows (a whole
-// head at Dv = 128): 16-byte loads of 8 values per lane, so each work-group streams twice the
-// bytes of a 64-row tile for the same fixed window cost, and the backward sweep runs once per
-// head instead of once per 64 rows. Used for Dk <= 128 and windows of up to 32 records (the LDS
-// window of 128 rows stays under 64 KiB).
+// Non-flush step reading the copy (bf16, fp8 or MXFP4) with one work-group per kRowsC = 128 value
+// rows (a whole head at Dv = 128): 16-byte loads of one chunk per lane (8 bf16, 16 fp8 or 32 fp4
+// values), so each work-group streams twice the rows of a 64-row tile for the same fixed window
+// cost, and the backward sweep runs once per head instead of once per 64 rows. Used for Dk <= 128
+// and windows of up to 32 records (the LDS window of 128 rows stays under 64 KiB).
 constexpr int kRowsC = 128;
-using GB = Geo<NN, PREC_BF16>;
-constexpr int NLC = (kRowsC + GB::RPB - 1) / GB::RPB;  // copy load slots per lane
-constexpr bool kCopyTiles = NN <= 128;
-static_assert(!kCopyTiles || NLC <= GB::LPR || NLC == 1, "transpose-reduce needs NLC <= LPR");
+template <int RP>
+struct CopyTile {
+    using G = Geo<NN, RP>;
+    static constexpr int NL = (kRowsC + G::RPB - 1) / G::RPB;  // copy load slots per lane
+    static_assert(NL <= G::LPR || NL == 1 || G::LPR == 1, "transpose-reduce needs NL <= LPR");
+};
+template <int RP>
+constexpr bool kCopyTiles = NN <= 128 && RP != PREC_F32 && (RP != PREC_FP4 || NN >= 32);
 
-template <int LMAX>
+// The copy rows of a 128-row tile: raw chunks (and MXFP4 block-scale codes) per lane and slot;
+// rows beyond the tile read its first row.
+template <int RP>
+struct CopyRows {
+    using G = Geo<NN, RP>;
+    static constexpr int NL = CopyTile<RP>::NL;
+    u32x4 raw[NL];
+    unsigned sc[RP == PREC_FP4 ? NL : 1];
+    __device__ static int row_of(int i, int wave, int lane) { return i * G::RPB + wave * G::RPI + lane / G::LPR; }
+    __device__ void load(const GLayer &Ld, const Tile &t, size_t bh, int wave, int lane)
+    {
+        const int c = lane % G::LPR;
+        const char *base = (const char *)Ld.rcopy;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int r = row_of(i, wave, lane), rr = r < t.nrows ? r : 0;
+            raw[i] = load_nt(base + state_chunk_off<NN, RP>(bh, t.row0 + rr, c, Ld.Dv));
+            if constexpr (RP == PREC_FP4) sc[i] = Ld.mxscale[(bh * Ld.Dv + t.row0 + rr) * (NN / 32) + c];
+        }
+    }
+    // Row dot of slot i with the vector z (NN floats in LDS), before the fp8 block scale.
+    __device__ float dot(int i, const float *z, int lane) const
+    {
+        const int c = lane % G::LPR;
+        const float p = chunk_dot<RP>(raw[i], z + G::VEC * c);
+        if constexpr (RP == PREC_FP4) return mx_scaled(p, sc[i]);
+        else return p;
+    }
+    // The finished row sum of tile row r: times its 64-row block's scale for fp8 (rows beyond the
+    // tile, whose sums are never used, read the tile's first block).
+    __device__ static float finish(const GLayer &Ld, const Tile &t, size_t bh, int r, float sum)
+    {
+        if constexpr (RP == PREC_FP8) return sum * Ld.scale[bh * Ld.psplit + (t.row0 + (r < t.nrows ? r : 0)) / kRows];
+        else return sum;
+    }
+};
+
+template <int LMAX, int RP>
 __global__ void __launch_bounds__(kThreads) gdn_step_copy_kernel(GLayer Ld, GTokenIO io, Lockstep ls, int splits)
 {
+    using CR = CopyRows<RP>;
+    using G = typename CR::G;
+    constexpr int NLC = CR::NL;
     __shared__ GStepLds<LMAX, kRowsC> s;
     const Tile t = gmap_tile_rows<kRowsC>(Ld, splits);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh = (size_t)t.b * Ld.H + t.h;
-    const unsigned short *rows = Ld.rcopy + (bh * Ld.Dv + t.row0) * NN;
-    const int c = lane % GB::LPR;  // this lane's 8 values of a row: 8c .. 8c+7
-    auto row_of = [&](int i) { return i * GB::RPB + wave * GB::RPI + lane / GB::LPR; };
-    u32x4 raw[NLC];
-    auto load_state = [&]() {
-#pragma unroll
-        for (int i = 0; i < NLC; ++i) {
-            const int r = row_of(i);
-            raw[i] = load_nt(rows + (size_t)(r < t.nrows ? r : 0) * NN + 8 * c);
-        }
-    };
+    CR cr;
 
     StepWindow<LMAX, kRowsC> win(Ld, t, tid);
     const bool uni = ls.k > 0;
@@ -568,9 +638,9 @@ __global__ void __launch_bounds__(kThreads) gdn_step_copy_kernel(GLayer Ld, GTok
         cslot = ls.cslot;
         k = ls.k;
         win.issue(Ld, io, t, cslot, k);
-        load_state();
+        cr.load(Ld, t, bh, wave, lane);
     } else {
-        load_state();  // the copy stream first
+        cr.load(Ld, t, bh, wave, lane);  // the copy stream first
         pos = Ld.pos[t.b];
         ck = Ld.ckpt[t.b];
         const int c0 = pos - ck;
@@ -589,18 +659,18 @@ __global__ void __launch_bounds__(kThreads) gdn_step_copy_kernel(GLayer Ld, GTok
     if (wave == 0) gdn_sweep<LMAX>(s.w, s.q, k - 1, s.c, s.z, lane);
     __syncthreads();
 
-    // S_c z: each lane's 8 widened values against z[8c .. 8c+7], summed over the row's lanes.
+    // S_c z: each lane's chunk against the matching slice of z, summed over the row's lanes.
     float part[NLC];
 #pragma unroll
-    for (int i = 0; i < NLC; ++i) part[i] = chunk_dot<PREC_BF16>(raw[i], &s.z[8 * c]);
-    transpose_reduce<NLC, GB::LPR>(part, lane);
+    for (int i = 0; i < NLC; ++i) part[i] = cr.dot(i, s.z, lane);
+    transpose_reduce<NLC, G::LPR>(part, lane);
     bool writer;
-    const int first = tr_first<NLC, GB::LPR>(lane, &writer);
+    const int first = tr_first<NLC, G::LPR>(lane, &writer);
     if (writer) {
 #pragma unroll
-        for (int e = 0; e < tr_count<NLC, GB::LPR>(); ++e) {
-            const int r = row_of(first + e);
-            if (r < kRowsC) s.u[r] = part[e];
+        for (int e = 0; e < tr_count<NLC, G::LPR>(); ++e) {
+            const int r = CR::row_of(first + e, wave, lane);
+            if (r < kRowsC) s.u[r] = CR::finish(Ld, t, bh, r, part[e]);
         }
     }
     __syncthreads();
@@ -615,6 +685,7 @@ template <int LMAX>
 __global__ void __launch_bounds__(kThreads) gdn_flush_kernel(GLayer Ld, int mode, const int *arg, float *out)
 {
     __shared__ GWin<LMAX> w;
+    __shared__ float red[kWaves];
     const Tile t = gmap_tile(Ld);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const size_t bh = (size_t)t.b * Ld.H + t.h;
@@ -688,7 +759,7 @@ __global__ void __launch_bounds__(kThreads) gdn_flush_kernel(GLayer Ld, int mode
     if (mode == MODE_MATERIALIZE) {
         store_rows(out + elem0, vf, t.nrows, wave, lane);
     } else {
-        store_checkpoint(Ld, elem0, vf, t.nrows, wave, lane);
+        store_checkpoint(Ld, bh, elem0, vf, t.nrows, wave, lane, red);
         gseq_done(Ld, t.b, pos, pos);
     }
 }
@@ -864,7 +935,7 @@ __device__ inline void verify_output_append(const GVerifyLds<LMAX, TQ, RT> &s, c
     }
 }
 
-template <int LMAX, int TQ, bool CP>
+template <int LMAX, int TQ, int RP>
 __global__ void __launch_bounds__(kThreads) gdn_verify_kernel(GLayer Ld, GTokenIO io, int T)
 {
     __shared__ GVerifyLds<LMAX, TQ> s;
@@ -883,7 +954,7 @@ __global__ void __launch_bounds__(kThreads) gdn_verify_kernel(GLayer Ld, GTokenI
     VerifyWindow<LMAX, TQ, kRows> win;
     win.issue(Ld, io, t, ck, count0, T);
     f32x4 vf[GF::NL];
-    if (CP) load_rows_bf16(vf, Ld.rcopy + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
+    if constexpr (RP != PREC_F32) load_rows_copy<RP>(vf, Ld, bh, t.row0, t.nrows, wave, lane);
     else load_rows_f32(vf, Ld.master + (bh * Ld.Dv + t.row0) * NN, t.nrows, wave, lane);
     win.commit(s, Ld, io, t);
     __syncthreads();
@@ -894,11 +965,14 @@ __global__ void __launch_bounds__(kThreads) gdn_verify_kernel(GLayer Ld, GTokenI
     verify_output_append(s, Ld, io, t, pos, count0, T);
 }
 
-// Verify through the bf16 copy with one work-group per 128 value rows (as gdn_step_copy_kernel):
-// 16-byte loads of 8 values per lane, the T sweeps once per head.
-template <int LMAX, int TQ>
+// Verify through the copy with one work-group per 128 value rows (as gdn_step_copy_kernel): one
+// 16-byte chunk per lane and slot, the T sweeps once per head.
+template <int LMAX, int TQ, int RP>
 __global__ void __launch_bounds__(kThreads) gdn_verify_copy_kernel(GLayer Ld, GTokenIO io, int T, int splits)
 {
+    using CR = CopyRows<RP>;
+    using G = typename CR::G;
+    constexpr int NLC = CR::NL;
     __shared__ GVerifyLds<LMAX, TQ, kRowsC> s;
     const Tile t = gmap_tile_rows<kRowsC>(Ld, splits);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -911,33 +985,26 @@ __global__ void __launch_bounds__(kThreads) gdn_verify_copy_kernel(GLayer Ld, GT
     }
     VerifyWindow<LMAX, TQ, kRowsC> win;
     win.issue(Ld, io, t, ck, count0, T);
-    const unsigned short *rows = Ld.rcopy + (bh * Ld.Dv + t.row0) * NN;
-    const int c = lane % GB::LPR;  // this lane's 8 values of a row: 8c .. 8c+7
-    auto row_of = [&](int i) { return i * GB::RPB + wave * GB::RPI + lane / GB::LPR; };
-    u32x4 raw[NLC];
-#pragma unroll
-    for (int i = 0; i < NLC; ++i) {
-        const int r = row_of(i);
-        raw[i] = load_nt(rows + (size_t)(r < t.nrows ? r : 0) * NN + 8 * c);
-    }
+    CR cr;
+    cr.load(Ld, t, bh, wave, lane);
     win.commit(s, Ld, io, t);
     __syncthreads();
     for (int q = wave; q < T; q += kWaves) gdn_sweep<LMAX>(s.w, s.q[q], count0 + q, s.c[q], s.z[q], lane);
     __syncthreads();
-    // S_c z_q for every query: each lane's 8 widened values against z_q[8c .. 8c+7].
+    // S_c z_q for every query: each lane's chunk against the matching slice of z_q.
     float part[NLC * TQ];
 #pragma unroll
     for (int q = 0; q < TQ; ++q)
 #pragma unroll
-        for (int i = 0; i < NLC; ++i) part[q * NLC + i] = q < T ? chunk_dot<PREC_BF16>(raw[i], &s.z[q][8 * c]) : 0.f;
-    transpose_reduce<NLC * TQ, GB::LPR>(part, lane);
+        for (int i = 0; i < NLC; ++i) part[q * NLC + i] = q < T ? cr.dot(i, s.z[q], lane) : 0.f;
+    transpose_reduce<NLC * TQ, G::LPR>(part, lane);
     bool writer;
-    const int first = tr_first<NLC * TQ, GB::LPR>(lane, &writer);
+    const int first = tr_first<NLC * TQ, G::LPR>(lane, &writer);
     if (writer) {
 #pragma unroll
-        for (int e = 0; e < tr_count<NLC * TQ, GB::LPR>(); ++e) {
-            const int idx = first + e, q = idx / NLC, r = row_of(idx % NLC);
-            if (q < T && r < kRowsC) s.u[q][r] = part[e];
+        for (int e = 0; e < tr_count<NLC * TQ, G::LPR>(); ++e) {
+            const int idx = first + e, q = idx / NLC, r = CR::row_of(idx % NLC, wave, lane);
+            if (q < T && r < kRowsC) s.u[q][r] = CR::finish(Ld, t, bh, r, part[e]);
         }
     }
     __syncthreads();
@@ -949,12 +1016,14 @@ __global__ void __launch_bounds__(kThreads) gdn_verify_copy_kernel(GLayer Ld, GT
 // ==========================================================================================
 __global__ void __launch_bounds__(kThreads) gdn_load_kernel(GLayer Ld, const float *state)
 {
+    __shared__ float red[kWaves];
     const Tile t = gmap_tile(Ld);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const size_t elem0 = (((size_t)t.b * Ld.H + t.h) * Ld.Dv + t.row0) * NN;
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    const size_t elem0 = (bh * Ld.Dv + t.row0) * NN;
     f32x4 vf[GF::NL];
     load_rows_f32(vf, state + elem0, t.nrows, wave, lane);
-    store_checkpoint(Ld, elem0, vf, t.nrows, wave, lane);
+    store_checkpoint(Ld, bh, elem0, vf, t.nrows, wave, lane, red);
     if (t.h == 0 && t.split == 0 && threadIdx.x == 0) {
         Ld.pos[t.b] = 0;
         Ld.ckpt[t.b] = 0;
@@ -1071,26 +1140,52 @@ __global__ void __launch_bounds__(kThreads) gdn_snapshot_kernel(GLayer Ld, float
 
 inline unsigned gblocks(const GLayer &Ld) { return (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)Ld.psplit; }
 
-template <int LMAX, bool CP>
+template <int LMAX, int RP>
 hipError_t step_lc(const GLayer &Ld, const GTokenIO &io, bool fc, Lockstep ls, hipStream_t st)
 {
-    if constexpr (CP && kCopyTiles && LMAX <= 32) {
+    if constexpr (kCopyTiles<RP> && LMAX <= 32) {
         if (!fc) {
             const int splits = (Ld.Dv + kRowsC - 1) / kRowsC;
             const unsigned grid = (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)splits;
-            hipLaunchKernelGGL((gdn_step_copy_kernel<LMAX>), dim3(grid), dim3(kThreads), 0, st, Ld, io, ls, splits);
+            hipLaunchKernelGGL((gdn_step_copy_kernel<LMAX, RP>), dim3(grid), dim3(kThreads), 0, st, Ld, io, ls, splits);
             return hipGetLastError();
         }
     }
-    if (fc) hipLaunchKernelGGL((gdn_step_kernel<LMAX, true, CP>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
-    else hipLaunchKernelGGL((gdn_step_kernel<LMAX, false, CP>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
+    if (fc) hipLaunchKernelGGL((gdn_step_kernel<LMAX, true, RP>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
+    else hipLaunchKernelGGL((gdn_step_kernel<LMAX, false, RP>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
     return hipGetLastError();
 }
+
+// The copy precisions a key size supports (MXFP4: blocks of 32 key columns, Dk >= 32).
+template <template <int> class F, typename... Args>
+hipError_t by_rprec(int rprec, Args &&...args)
+{
+    switch (rprec) {
+    case PREC_F32: return F<PREC_F32>::run(args...);
+    case PREC_BF16: return F<PREC_BF16>::run(args...);
+    case PREC_FP8: return F<PREC_FP8>::run(args...);
+    case PREC_FP4:
+        if constexpr (NN >= 32) return F<PREC_FP4>::run(args...);
+        return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int LMAX>
+struct StepL {
+    template <int RP>
+    struct F {
+        static hipError_t run(const GLayer &Ld, const GTokenIO &io, bool fc, Lockstep ls, hipStream_t st)
+        {
+            return step_lc<LMAX, RP>(Ld, io, fc, ls, st);
+        }
+    };
+};
 
 template <int LMAX>
 hipError_t step_l(const GLayer &Ld, const GTokenIO &io, bool fc, Lockstep ls, hipStream_t st)
 {
-    return Ld.rprec ? step_lc<LMAX, true>(Ld, io, fc, ls, st) : step_lc<LMAX, false>(Ld, io, fc, ls, st);
+    return by_rprec<StepL<LMAX>::template F>(Ld.rprec, Ld, io, fc, ls, st);
 }
 
 template <int LMAX>
@@ -1106,28 +1201,39 @@ hipError_t flush_l(const GLayer &Ld, int mode, const int *arg, int T, float *out
     return hipGetLastError();
 }
 
-template <int LMAX, bool CP>
+template <int LMAX, int RP>
 hipError_t verify_lc(const GLayer &Ld, const GTokenIO &io, int T, hipStream_t st)
 {
-    if constexpr (CP && kCopyTiles && LMAX <= 32) {
+    if constexpr (kCopyTiles<RP> && LMAX <= 32) {
         const int splits = (Ld.Dv + kRowsC - 1) / kRowsC;
         const dim3 grid((unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)splits), block(kThreads);
-        if (T <= 2) hipLaunchKernelGGL((gdn_verify_copy_kernel<LMAX, 2>), grid, block, 0, st, Ld, io, T, splits);
-        else if (T <= 4) hipLaunchKernelGGL((gdn_verify_copy_kernel<LMAX, 4>), grid, block, 0, st, Ld, io, T, splits);
-        else hipLaunchKernelGGL((gdn_verify_copy_kernel<LMAX, 8>), grid, block, 0, st, Ld, io, T, splits);
+        if (T <= 2) hipLaunchKernelGGL((gdn_verify_copy_kernel<LMAX, 2, RP>), grid, block, 0, st, Ld, io, T, splits);
+        else if (T <= 4) hipLaunchKernelGGL((gdn_verify_copy_kernel<LMAX, 4, RP>), grid, block, 0, st, Ld, io, T, splits);
+        else hipLaunchKernelGGL((gdn_verify_copy_kernel<LMAX, 8, RP>), grid, block, 0, st, Ld, io, T, splits);
         return hipGetLastError();
     }
     const dim3 grid(gblocks(Ld)), block(kThreads);
-    if (T <= 2) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 2, CP>), grid, block, 0, st, Ld, io, T);
-    else if (T <= 4) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 4, CP>), grid, block, 0, st, Ld, io, T);
-    else hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 8, CP>), grid, block, 0, st, Ld, io, T);
+    if (T <= 2) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 2, RP>), grid, block, 0, st, Ld, io, T);
+    else if (T <= 4) hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 4, RP>), grid, block, 0, st, Ld, io, T);
+    else hipLaunchKernelGGL((gdn_verify_kernel<LMAX, 8, RP>), grid, block, 0, st, Ld, io, T);
     return hipGetLastError();
 }
 
 template <int LMAX>
+struct VerifyL {
+    template <int RP>
+    struct F {
+        static hipError_t run(const GLayer &Ld, const GTokenIO &io, int T, hipStream_t st)
+        {
+            return verify_lc<LMAX, RP>(Ld, io, T, st);
+        }
+    };
+};
+
+template <int LMAX>
 hipError_t verify_l(const GLayer &Ld, const GTokenIO &io, int T, hipStream_t st)
 {
-    return Ld.rprec ? verify_lc<LMAX, true>(Ld, io, T, st) : verify_lc<LMAX, false>(Ld, io, T, st);
+    return by_rprec<VerifyL<LMAX>::template F>(Ld.rprec, Ld, io, T, st);
 }
 
 }  // namespace

@@ -10,8 +10,11 @@ namespace rssm {
 // One GDN layer's workspace (passed by value). H value heads of Dv, G key heads of Dk.
 struct GLayer {
     float *master;      // [Bt,H,Dv,Dk] fp32 checkpoint
-    unsigned short *rcopy;  // [Bt,H,Dv,Dk] bf16 read copy (rprec 1), else nullptr
-    int rprec;          // 0: reads from the checkpoint; 1: from the bf16 copy
+    void *rcopy;        // read copy, else nullptr: bf16 [Bt,H,Dv,Dk] row-major, or fp8 / MXFP4 codes
+                        // in 16-byte chunks, chunk-column-major per head (state_chunk_off)
+    int rprec;          // PREC_F32 (reads from the checkpoint), PREC_BF16, PREC_FP8 or PREC_FP4
+    float *scale;       // fp8: [Bt,H,psplit], one per 64 value rows
+    unsigned char *mxscale;  // MXFP4: [Bt,H,Dv,Dk/32] E8M0 block-scale codes
     float *ring_k;      // [Bt,G,L,Dk]
     float *ring_v;      // [Bt,H,L,Dv]
     float *ring_a;      // [Bt,H,L] gate alpha

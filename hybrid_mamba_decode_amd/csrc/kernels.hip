@@ -24,31 +24,20 @@ namespace {
 constexpr int NN = RSSM_N;
 using GF = Geo<NN, PREC_F32>;  // fp32 geometry (master tile, records)
 
-// Byte offset of element e of a state array in precision PREC (fp4: two elements per byte; e is
-// always a chunk start, hence even).
 template <int PREC>
 constexpr size_t byte_off(size_t e)
 {
-    return PREC == PREC_F32 ? e * 4 : (PREC == PREC_BF16 || PREC == PREC_F16) ? e * 2 : PREC == PREC_FP8 ? e : e / 2;
+    return state_byte_off<PREC>(e);
 }
 
 // MXFP4 needs N >= 32 (a scale block is 32 consecutive n of one row).
 template <int PREC>
 constexpr bool kPrecOk = !(PREC == PREC_FP4 && NN < 32);
 
-// Byte offset of 16-byte chunk q (elements [q*VEC, (q+1)*VEC)) of row p of head bh in a state
-// array of precision PREC. The fp32 master and the bf16 copy are row-major ([P][N] per head).
-// The fp8 and MXFP4 copies are chunk-column-major per head ([N/VEC][P] chunks): one wave
-// instruction over 64 consecutive rows of one chunk column then reads 1 KiB contiguously, which
-// is what the one-row-per-lane step kernel issues; lane-along-N kernels read them in runs of
-// RPI rows (128-256 bytes).
 template <int PREC>
 __device__ inline size_t chunk_off(size_t bh, int p, int q, int P)
 {
-    using G = Geo<NN, PREC>;
-    const size_t head = byte_off<PREC>(bh * (size_t)P * NN);
-    if constexpr (PREC == PREC_FP8 || PREC == PREC_FP4) return head + ((size_t)q * P + p) * 16;
-    else return head + ((size_t)p * (NN / G::VEC) + q) * 16;
+    return state_chunk_off<NN, PREC>(bh, p, q, P);
 }
 
 template <int PREC>
@@ -264,83 +253,13 @@ __device__ inline void window_weights(const Window<LMAX> &w, const float *Cq, in
     if (last < 0 && threadIdx.x == 0) *decay = 1.0f;
 }
 
-// ------------------------------------------------------------------------------------------
-// Read-copy writer for fp32 rows held in f32 geometry (vf), dst rows at element `elem0`.
-// bf16: round each value to nearest even. fp8: per-(sequence, head) scale = amax / 448 over the
-// whole head tile (the caller guarantees the work-group owns all P rows), codes RNE-saturated.
-// ------------------------------------------------------------------------------------------
+// Read-copy writer for fp32 rows held in f32 geometry (device.h: write_copy_rows_n).
 template <int PREC>
-__device__ inline void write_copy_rows(const Layer &Ld, size_t bh, size_t elem0, const f32x4 (&vf)[GF::NL],
-                                       int nrows, int wave, int lane, float *red)
+__device__ inline void write_copy_rows(const Layer &Ld, size_t bh, size_t elem0, const f32x4 (&vf)[GF::NL], int nrows,
+                                       int wave, int lane, float *red)
 {
-    const int c = lane % GF::LPR;
-    if constexpr (PREC == PREC_BF16) {
-        unsigned short *dst = (unsigned short *)Ld.rcopy + elem0;
-#pragma unroll
-        for (int i = 0; i < GF::NL; ++i) {
-            const int r = row_of<PREC_F32>(i, wave, lane);
-            if (r < nrows) {
-                const f32x4 f = vf[i];
-                u32x2 pk;
-                pk.x = bf16_rne(f.x) | (bf16_rne(f.y) << 16);
-                pk.y = bf16_rne(f.z) | (bf16_rne(f.w) << 16);
-                *(u32x2 *)(dst + (size_t)r * NN + 4 * c) = pk;
-            }
-        }
-    } else if constexpr (PREC == PREC_FP8) {
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < GF::NL; ++i) {
-            const f32x4 f = vf[i];
-            const float m = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
-            if (row_of<PREC_F32>(i, wave, lane) < nrows) amax = fmaxf(amax, m);
-        }
-        amax = block_max(amax, red);
-        const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
-        const float inv = 1.0f / scale;
-        unsigned char *dst = (unsigned char *)Ld.rcopy;
-        const int row0 = (int)(elem0 / NN - bh * (size_t)Ld.P);
-#pragma unroll
-        for (int i = 0; i < GF::NL; ++i) {
-            const int r = row_of<PREC_F32>(i, wave, lane);
-            if (r < nrows) {
-                const f32x4 f = vf[i];
-                // clamp to the largest finite code, then gfx950's converter rounds to nearest even
-                // (four codes per dword, two per instruction)
-                const float a0 = fminf(fmaxf(f.x * inv, -448.0f), 448.0f);
-                const float a1 = fminf(fmaxf(f.y * inv, -448.0f), 448.0f);
-                const float a2 = fminf(fmaxf(f.z * inv, -448.0f), 448.0f);
-                const float a3 = fminf(fmaxf(f.w * inv, -448.0f), 448.0f);
-                int q = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-                q = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, q, true);
-                const int n = 4 * c;
-                *(unsigned *)(dst + chunk_off<PREC_FP8>(bh, row0 + r, n / 16, Ld.P) + n % 16) = (unsigned)q;
-            }
-        }
-        if (threadIdx.x == 0) Ld.scale[bh] = scale;
-    } else if constexpr (PREC == PREC_FP4) {
-        // One 32-value block = 8 consecutive lanes of a row (4 values each); its amax by three
-        // lane exchanges, then each lane encodes its 4 values into 2 bytes and the block's first
-        // lane writes the scale byte.
-        unsigned char *dst = (unsigned char *)Ld.rcopy;
-        unsigned char *sdst = Ld.mxscale + elem0 / 32;
-        const int row0 = (int)(elem0 / NN - bh * (size_t)Ld.P);
-#pragma unroll
-        for (int i = 0; i < GF::NL; ++i) {
-            const int r = row_of<PREC_F32>(i, wave, lane);
-            const f32x4 f = vf[i];
-            float amax = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
-            amax = group_max(amax, 8);
-            const unsigned code = mx_code_of(amax);
-            if (r < nrows) {
-                const int n = 4 * c;
-                *(unsigned short *)(dst + chunk_off<PREC_FP4>(bh, row0 + r, n / 32, Ld.P) + (n % 32) / 2) =
-                    mx_encode4(f, code);
-                if (c % 8 == 0) sdst[((size_t)r * NN + n) / 32] = (unsigned char)code;
-            }
-        }
-        (void)red;
-    }
+    write_copy_rows_n<NN, PREC>(CopyDst{Ld.rcopy, Ld.scale, Ld.mxscale, Ld.P, Ld.psplit}, bh, elem0, vf, nrows, wave,
+                                lane, red);
 }
 
 // Fold `k` staged records into one head's fp32 rows vf (f32 geometry), in registers:
@@ -393,7 +312,7 @@ __device__ inline void load_master_rows(const Layer &Ld, size_t elem0, f32x4 (&v
         const size_t bh = elem0 / ((size_t)Ld.P * NN);
         const int row0 = (int)(elem0 / NN - bh * (size_t)Ld.P);
         const unsigned char *src = (const unsigned char *)Ld.rcopy;
-        const float scale = Ld.scale[bh];
+        const float scale = Ld.scale[bh * Ld.psplit + row0 / kRows];
         const int n = 4 * c;
 #pragma unroll
         for (int i = 0; i < GF::NL; ++i) {
@@ -515,7 +434,7 @@ __device__ inline void store_master_fp8_rows(const Layer &Ld, int b, size_t bh, 
         vf[i] = f32x4{lo.x * scale, lo.y * scale, hi.x * scale, hi.y * scale};
         if (r < nrows) *(unsigned *)(dst + chunk_off<PREC_FP8>(bh, row0 + r, n / 16, Ld.P) + n % 16) = (unsigned)q;
     }
-    if (threadIdx.x == 0) Ld.scale[bh] = scale;
+    if (threadIdx.x == 0) Ld.scale[bh * Ld.psplit + row0 / kRows] = scale;
 }
 
 // Commit a head's folded rows: store them at the master's precision (vf then holds the stored
@@ -718,7 +637,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
             const float a = Ld.A[t.h + hw];
             Aw = wave < HPB ? a : 0.f;
         }
-        if (PREC == PREC_FP8) scl_r = Ld.scale[bh0 + (tid < ROWS ? tid / kRows : 0)];
+        if (PREC == PREC_FP8) scl_r = Ld.scale[(bh0 + (tid < ROWS ? tid / kRows : 0)) * Ld.psplit + t.split];
     };
 
     // Mixer edges: this token's x rows (one per thread), the group's B and C (channels e < 2N,
@@ -1185,7 +1104,7 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
         }
     }
     float u = u0 + u1;
-    if constexpr (PREC == PREC_FP8) u *= Ld.scale[bh];
+    if constexpr (PREC == PREC_FP8) u *= Ld.scale[bh];  // P <= 64 here: one scale block per head
     issue_x();
 
     if (bad) {
@@ -1838,7 +1757,7 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
             part[q * G::NL + i] = chunk_dot<PREC>(v[i], cc[q]);
             if constexpr (PREC == PREC_FP4) part[q * G::NL + i] = mx_scaled(part[q * G::NL + i], sc[i]);
         }
-    const float scl = PREC == PREC_FP8 ? Ld.scale[bh] : 1.0f;
+    const float scl = PREC == PREC_FP8 ? Ld.scale[bh * Ld.psplit + t.split] : 1.0f;
     rows_to_lds<PREC, G::NL * TQ>(part, &s.u[0][0], kRows, T, G::NL, scl, wave, lane);
     __syncthreads();
 

@@ -23,10 +23,14 @@
  *     spec-decode inputs: q, k [Bt,T,G,Dk]  v [Bt,T,H,Dv]  alpha, beta [Bt,T,H]  o [Bt,T,H,Dv]
  * Supported: Dk in {16, 32, 64, 128, 256}; Dv a multiple of 4, at most 256; 1 <= L <= 64;
  * 1 <= max_draft <= min(L, 8). Reads: through the fp32 checkpoint (read_prec RSSM_READ_FP32), or
- * through a bf16 copy of it (RSSM_READ_BF16; [AT Pulse] "Technical analysis": the recurrence
- * updates a full-precision checkpoint while replayed reads may use a narrower copy): the copy is each
- * checkpoint value rounded to nearest even, written at load and at every flush; replayed outputs
- * and verify read it, flushes fold into and read the fp32 checkpoint.
+ * through a narrower copy of it ([AT Pulse] "Technical analysis": the recurrence updates a
+ * full-precision checkpoint while replayed reads may use a narrower copy; "Capabilities and
+ * access": FP8 and 4-bit reads), in the formats of replayssm.h with the value index as the row
+ * and the key index as the column: RSSM_READ_BF16 (each value to nearest even), RSSM_READ_FP8_E4M3
+ * (one fp32 scale per (sequence, value head, block of 64 value rows)), RSSM_READ_MXFP4 (one E8M0
+ * scale per 32 consecutive key columns of a row; Dk >= 32, else RSSM_E_UNSUPPORTED). The copy is
+ * written at load and at every flush; replayed outputs and verify read it, flushes fold into and
+ * read the fp32 checkpoint.
  *
  * Memory, streams and errors as in replayssm.h: the caller owns every device buffer (16-byte
  * aligned float arrays, 4-byte aligned int32 arrays, 256-byte aligned workspace; NULL allowed
@@ -56,13 +60,16 @@ typedef struct {
     int32_t dk;          /* key size Dk */
     int32_t buffer_len;  /* L */
     int32_t max_draft;   /* T_max: 1 = standard decode only */
-    int32_t read_prec;   /* RSSM_READ_FP32 or RSSM_READ_BF16 (others: RSSM_E_INVAL) */
+    int32_t read_prec;   /* rssm_read_prec (outside 0..3: RSSM_E_INVAL) */
 } gdnreplay_config;
 
 /* Byte offsets of the workspace regions. */
 typedef struct {
     size_t master;    /* fp32 [Bt,H,Dv,Dk] checkpoint, updated only by flushes */
-    size_t read_copy; /* bf16 [Bt,H,Dv,Dk] (0 bytes with fp32 reads) */
+    size_t read_copy; /* bf16 [Bt,H,Dv,Dk] row-major; fp8 / MXFP4 codes in 16-byte chunks (16 fp8 /
+                         32 fp4 values of one row), per head ordered [Dk/VEC][Dv] as in
+                         replayssm_layout.read_copy; 0 bytes with fp32 reads */
+    size_t scale;     /* fp8: fp32 [Bt,H,ceil(Dv/64)]; MXFP4: E8M0 bytes [Bt,H,Dv,Dk/32]; else 0 bytes */
     size_t ring_k;    /* fp32 [Bt,G,L,Dk]: record of position q in slot q mod L */
     size_t ring_v;    /* fp32 [Bt,H,L,Dv] */
     size_t ring_a;    /* fp32 [Bt,H,L] alpha */

@@ -71,7 +71,8 @@ typedef enum {
  * ([AT Pulse] lede, "Capabilities and access" and "Claims and evidence"), a format gfx950 has no
  * instructions for; the copies here are gfx950-native formats:
  *   BF16      round to nearest even.
- *   FP8_E4M3  OCP E4M3FN codes, one fp32 scale per (sequence, head) = amax / 448 (1 if amax = 0);
+ *   FP8_E4M3  OCP E4M3FN codes, one fp32 scale per (sequence, head, block of 64 consecutive rows
+ *             p -- the whole head when headdim <= 64) = amax / 448 of the block (1 if amax = 0);
  *             codes = RNE of value / scale clamped to +-448.
  *   MXFP4     OCP MX v1.0 FP4 (E2M1) codes in blocks of 32 consecutive n of a row, one E8M0 scale
  *             byte per block: scale = 2^(e - 127) with e = max(biased fp32 exponent of the block's
@@ -100,11 +101,11 @@ typedef enum {
  *            off) so that every flush knows its ckpt_pos.
  *   FP8      ([AT Pulse] "Claims and evidence" names FP8 beside FP16 for the recurrence) the
  *            checkpoint is kept in the FP8_E4M3 read copy's own format: E4M3FN codes with one
- *            fp32 scale per (sequence, head), scale = amax / 448 of the folded values (1 if 0),
- *            codes of value * (1 / scale) clamped to +-448, rounded to nearest even at load and at
- *            every flush. Its value is code * scale; reads come from it directly, so read_prec must
- *            be FP32 (RSSM_E_INVAL otherwise: there is no second copy) and headdim <= 64
- *            (RSSM_E_UNSUPPORTED otherwise, as for the fp8 copy).
+ *            fp32 scale per (sequence, head, 64-row block), scale = amax / 448 of the block's
+ *            folded values (1 if 0), codes of value * (1 / scale) clamped to +-448, rounded to
+ *            nearest even at load and at every flush. Its value is code * scale; reads come from
+ *            it directly, so read_prec must be FP32 (RSSM_E_INVAL otherwise: there is no second
+ *            copy).
  *   FP8_SR   as FP8 at load; at every flush the scaled value rounds stochastically on the E4M3
  *            grid by FP16_SR's rule and Philox fields (q the E4M3 magnitude toward zero, ulp the
  *            code spacing above it, 2^-9 below 2^-6): an fp32 value keeps 20 bits below E4M3's
@@ -146,8 +147,8 @@ typedef struct {
                           [N/VEC][P]: chunk q of row p of head (b,h) at byte offset
                           ((b*H + h)*P*N*s) + (q*P + p)*16, s = 1 (fp8) or 1/2 (fp4);
                           0 bytes for fp32 reads */
-    size_t scale;      /* fp8 copy or fp8 master: fp32 [Bt,H] per-head scales; MXFP4: E8M0 bytes
-                          [Bt,H,P,N/32];
+    size_t scale;      /* fp8 copy or fp8 master: fp32 [Bt,H,ceil(P/64)] scales, one per 64-row
+                          block; MXFP4: E8M0 bytes [Bt,H,P,N/32];
                           0 bytes otherwise */
     size_t ring_x;     /* fp32 [Bt,H,L,P]: record of absolute position q sits in slot q mod L */
     size_t ring_B;     /* fp32 [Bt,G,L,N] */

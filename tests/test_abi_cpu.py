@@ -70,7 +70,9 @@ def test_workspace_layout_serving_shape():
         l8m = rs.replayssm_workspace_layout(cfg(batch=256, master_prec=m))
         assert l8m.read_copy - l8m.master == Bt * H * P * N           # one code byte per value
         assert l8m.scale == l8m.read_copy                             # no second copy
-        assert l8m.ring_x - l8m.scale == Bt * H * 4                   # fp32 per-head scales
+        assert l8m.ring_x - l8m.scale == Bt * H * 4                   # fp32 scale per head (P <= 64)
+    l8w = rs.replayssm_workspace_layout(cfg(batch=256, read_prec="fp8", headdim=100))
+    assert l8w.ring_x - l8w.scale == Bt * H * 2 * 4                   # two 64-row blocks per head
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -84,14 +86,12 @@ def test_workspace_layout_serving_shape():
     (dict(buffer_len=65), rs.RSSM_E_UNSUPPORTED),
     (dict(buffer_len=16, max_draft=9), rs.RSSM_E_UNSUPPORTED),
     (dict(read_prec=4), rs.RSSM_E_INVAL),
-    (dict(read_prec="fp8", headdim=128), rs.RSSM_E_UNSUPPORTED),
     (dict(read_prec="mxfp4", dstate=16), rs.RSSM_E_UNSUPPORTED),
     (dict(batch=-1), rs.RSSM_E_INVAL),
     (dict(store_C=2), rs.RSSM_E_INVAL),
     (dict(master_prec=5), rs.RSSM_E_INVAL),
     (dict(master_prec="fp8", read_prec="bf16"), rs.RSSM_E_INVAL),
     (dict(master_prec="fp8_sr", read_prec="fp8"), rs.RSSM_E_INVAL),
-    (dict(master_prec="fp8", headdim=128), rs.RSSM_E_UNSUPPORTED),
     (dict(master_prec=-1), rs.RSSM_E_INVAL),
     (dict(d_conv=1), rs.RSSM_E_INVAL),
     (dict(d_conv=-1), rs.RSSM_E_INVAL),
@@ -312,9 +312,16 @@ def test_gdn_workspace_layout():
     assert lay.total == rs.gdnreplay_workspace_bytes(c)
     for name in ("master", "ring_k", "ring_v", "ring_a", "ring_b", "pos", "ckpt_pos", "counters", "flag"):
         assert getattr(lay, name) % 256 == 0
-    assert lay.read_copy == lay.ring_k                                  # fp32 reads: no copy
+    assert lay.read_copy == lay.scale == lay.ring_k                     # fp32 reads: no copy
     lb = rs.gdnreplay_workspace_layout(gcfg(batch=256, read_prec="bf16"))
-    assert lb.ring_k - lb.read_copy == Bt * H * Dv * Dk * 2               # bf16 copy
+    assert lb.scale - lb.read_copy == Bt * H * Dv * Dk * 2                # bf16 copy
+    assert lb.ring_k == lb.scale
+    l8 = rs.gdnreplay_workspace_layout(gcfg(batch=256, read_prec="fp8"))
+    assert l8.scale - l8.read_copy == Bt * H * Dv * Dk                    # one byte per value
+    assert l8.ring_k - l8.scale == Bt * H * ((Dv + 63) // 64) * 4         # a scale per 64 value rows
+    l4 = rs.gdnreplay_workspace_layout(gcfg(batch=256, read_prec="mxfp4"))
+    assert l4.scale - l4.read_copy == Bt * H * Dv * Dk // 2               # two codes per byte
+    assert l4.ring_k - l4.scale == Bt * H * Dv * Dk // 32                 # an E8M0 byte per 32 values
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -328,8 +335,9 @@ def test_gdn_workspace_layout():
     (dict(buffer_len=65), rs.RSSM_E_UNSUPPORTED),
     (dict(buffer_len=16, max_draft=9), rs.RSSM_E_UNSUPPORTED),
     (dict(batch=-1), rs.RSSM_E_INVAL),
-    (dict(read_prec=2), rs.RSSM_E_INVAL),
+    (dict(read_prec=4), rs.RSSM_E_INVAL),
     (dict(read_prec=-1), rs.RSSM_E_INVAL),
+    (dict(read_prec="mxfp4", dk=16), rs.RSSM_E_UNSUPPORTED),
 ])
 def test_gdn_invalid_configs_rejected(kw, status):
     c = gcfg(**kw)

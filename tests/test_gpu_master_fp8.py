@@ -100,9 +100,11 @@ def test_serving_fp8_master(master):
     _run(case, 64, range(c["Bt"]), master, check_state_every=32)
 
 
-@pytest.mark.parametrize("shape", [(3, 6, 24, 64, 2, 6), (2, 4, 64, 256, 1, 5), (5, 2, 40, 32, 2, 1)])
+@pytest.mark.parametrize("shape", [(3, 6, 24, 64, 2, 6), (2, 4, 64, 256, 1, 5), (5, 2, 40, 32, 2, 1),
+                                   (2, 3, 100, 64, 1, 5)])
 def test_fp8_master_shapes(shape):
-    """Ragged P (24, 40: rows past the tile's end), N = 256 and 32, L = 1 (every step flushes)."""
+    """Ragged P (24, 40: rows past the tile's end), N = 256 and 32, L = 1 (every step flushes),
+    P = 100 (two scale blocks per head, the per-row flush path)."""
     case = Case(*shape, 77)
     _run(case, 12, range(shape[0]), "fp8_sr", check_state_every=3)
 

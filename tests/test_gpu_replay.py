@@ -133,9 +133,9 @@ def test_read_copy_bytes_bit_exact(prec):
         exp = oracle.bf16_encode(case.S0).view(np.int16)
         assert np.array_equal(got, exp)
     elif prec == "fp8":
-        codes, scales = oracle.e4m3_encode_tiles(case.S0, case.P * case.N)
-        assert np.array_equal(got.reshape(-1), codes)
-        assert np.array_equal(host(lay.scales()).reshape(-1), scales)
+        codes, scales = oracle.e4m3_encode_rows(case.S0)
+        assert np.array_equal(got, codes)
+        assert np.array_equal(host(lay.scales()), scales)
     else:
         codes, scales = oracle.mxfp4_encode(case.S0)
         assert np.array_equal(got, codes)
@@ -174,9 +174,9 @@ def test_read_copy_bytes_bit_exact(prec):
         assert np.array_equal(host(lay2.scales()), scales)
         assert np.array_equal(got, codes)
     else:
-        codes, scales = oracle.e4m3_encode_tiles(S, P * N)
-        assert np.array_equal(host(lay2.scales()).reshape(-1), scales)
-        assert np.array_equal(got.reshape(-1), codes)
+        codes, scales = oracle.e4m3_encode_rows(S)
+        assert np.array_equal(host(lay2.scales()), scales)
+        assert np.array_equal(got, codes)
 
 
 @pytest.mark.parametrize("shape", [
@@ -207,6 +207,22 @@ def test_shapes_dual_precision(prec, tol):
 def test_shapes_mxfp4(shape):
     case = Case(shape["Bt"], shape["H"], shape["P"], shape["N"], shape["G"], shape["L"], 77)
     _run_replay(case, shape["L"] + 4, range(shape["Bt"]), read_prec="mxfp4", tol=TOL_FP4)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(Bt=3, H=5, P=100, N=64, G=1, L=7),     # two scale blocks, the second ragged (36 rows)
+    dict(Bt=2, H=4, P=128, N=128, G=2, L=16),   # two full blocks
+    dict(Bt=2, H=2, P=256, N=32, G=1, L=5),     # four blocks
+])
+def test_shapes_fp8_blocks_of_64_rows(shape):
+    """fp8 copies with P > 64 (one scale per 64-row block): the copy written at load bit-exact
+    with the oracle's per-block encoder, scales [Bt,H,ceil(P/64)] included; then the replay run,
+    whose same-copy checks re-encode the GPU's master after every flush."""
+    case = Case(shape["Bt"], shape["H"], shape["P"], shape["N"], shape["G"], shape["L"], 88)
+    lay = case.layer("fp8")
+    assert tuple(lay.scales().shape) == (case.Bt, case.H, (case.P + 63) // 64)
+    assert_copy_encodes(lay, "fp8", case.S0, range(case.Bt), "load")
+    _run_replay(case, 2 * shape["L"] + 3, range(shape["Bt"]), read_prec="fp8", tol=TOL_FP8, check_state_every=4)
 
 
 def test_spec_handle_standard_steps_and_no_C():

@@ -160,6 +160,12 @@ def test_spec_dual_precision(prec, tol):
     _run_spec(case, 4, 40, range(2), read_prec=prec, tol=tol)
 
 
+def test_spec_fp8_blocks_of_64_rows():
+    """Spec verify and rollback through an fp8 copy with P = 128 (two scale blocks per head)."""
+    case = Case(2, 4, 128, 64, 2, 8, 43, Tmax=3)
+    _run_spec(case, 3, 30, range(2), read_prec="fp8", tol=6e-2)
+
+
 def test_rollback_flags_bad_accept_count():
     """An accepted count above T sets the device flag; that sequence is left unchanged."""
     case = Case(2, 4, 16, 16, 1, 8, 3, Tmax=2)
