@@ -63,7 +63,7 @@ def parse():
     ap.add_argument("--workload", default="serving", choices=["serving", "spec", "sweep", "gdn", "mixer"],
                     help="serving: the headline line; spec: batch 512, T=4 verify+rollback vs "
                          "per-draft snapshots; sweep: batch x L over a 10-layer stack; gdn: a Gated "
-                         "DeltaNet layer (--read-prec fp32|bf16); mixer: the step with the Mamba-2 "
+                         "DeltaNet layer (--read-prec fp32|bf16|fp8|mxfp4); mixer: the step with the Mamba-2 "
                          "mixer edges fused")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")

@@ -258,7 +258,7 @@ def gdn(args):
     S0 = torch.randn(Bt, Hv, Dv, Dk, device="cuda", generator=g)
     pool = [_gdn_tokens(g, (Bt,), Hv, Gk, Dv, Dk, rates) for _ in range(8)]
     o = torch.empty(Bt, Hv, Dv, device="cuda")
-    prec = args.read_prec if args.read_prec in ("fp32", "bf16") else "fp32"
+    prec = args.read_prec
     lay = rs.GDNReplay(Bt, Hv, Gk, Dv, Dk, buffer_len=L, read_prec=prec)
     lay.load_state(S0)
 

@@ -21,11 +21,11 @@ def read_source(read_prec, master="fp32"):
 
 
 def state_bytes(H, P, N, prec="fp32"):
-    """One state (or read copy) of H heads: fp8 adds its fp32 per-head scales, MXFP4 its E8M0
-    byte per block of 32 values."""
+    """One state (or read copy) of H heads: fp8 adds its fp32 scales (one per 64 rows of a head),
+    MXFP4 its E8M0 byte per block of 32 values."""
     b = int(H * P * N * ELEM[prec])
     if prec == "fp8":
-        b += H * F32
+        b += H * ((P + 63) // 64) * F32
     elif prec == "mxfp4":
         b += H * P * N // 32
     return b
@@ -96,7 +96,8 @@ def snapshot_verify(H, P, N, G, T):
 
 # ---- Gated DeltaNet (H value heads of Dv, G key heads of Dk) -------------------------------------
 def gdn_state_bytes(H, Dv, Dk, prec="fp32"):
-    return int(ELEM[prec] * H * Dv * Dk)
+    """One GDN state or read copy (value rows of Dk key columns), scales included as for Mamba-2."""
+    return state_bytes(H, Dv, Dk, prec)
 
 
 def gdn_token_input_bytes(H, G, Dv, Dk):
@@ -110,7 +111,7 @@ def gdn_record_bytes(H, G, Dv, Dk):
 
 
 def gdn_replay_nonflush(H, G, Dv, Dk, k, prec="fp32"):
-    """prec: the precision the checkpoint product reads (the fp32 checkpoint or its bf16 copy)."""
+    """prec: the precision the checkpoint product reads (the fp32 checkpoint or its copy)."""
     return (gdn_state_bytes(H, Dv, Dk, prec) + gdn_token_input_bytes(H, G, Dv, Dk) + gdn_record_bytes(H, G, Dv, Dk)
             + F32 * H * Dv + (k - 1) * gdn_record_bytes(H, G, Dv, Dk))
 
