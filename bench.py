@@ -60,11 +60,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--kernels-only", action="store_true",
                     help="only the replay steps (for profiler runs)")
-    ap.add_argument("--workload", default="serving", choices=["serving", "spec", "sweep", "gdn", "mixer"],
+    ap.add_argument("--workload", default="serving", choices=["serving", "spec", "sweep", "gdn", "mixer", "ceilings"],
                     help="serving: the headline line; spec: batch 512, T=4 verify+rollback vs "
                          "per-draft snapshots; sweep: batch x L over a 10-layer stack; gdn: a Gated "
                          "DeltaNet layer (--read-prec fp32|bf16|fp8|mxfp4); mixer: the step with the Mamba-2 "
-                         "mixer edges fused")
+                         "mixer edges fused; ceilings: read / copy / read-modify-write bandwidth of plain "
+                         "PyTorch kernels")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
     return ap.parse_args()

@@ -428,8 +428,39 @@ def mixer(args):
         _calib_copy()
 
 
+def ceilings(args):
+    """Bandwidth ceilings on this GPU, the context for the replay kernels' fractions of 8 TB/s:
+    the streaming probes of libbwprobe.so (32 KiB contiguous per work-group, 16-byte
+    non-temporal accesses: the checkpoint stream's pattern without its arithmetic) -- a read of
+    2 GiB, a copy of 1 GiB and an in-place read-modify-write of 1 GiB -- and, beside them, the
+    same three through plain PyTorch kernels (torch.amax, copy_, mul_). Each figure is the median
+    of 20 launches after 5 warm-up launches, in TB/s of bytes moved."""
+    from hybrid_mamba_decode_amd import bwprobe
+    n = 1 << 28                                    # 1 GiB of fp32
+    x = torch.randn(2 * n, device="cuda")
+    a, b = x[:n], torch.empty(n, device="cuda")
+    sink = torch.empty(2 * n // 2048, device="cuda")
+
+    def rate(fn, nbytes):
+        _timed(fn, 5)
+        _, d = _timed(fn, 20)
+        return round(nbytes / float(np.median(d)) / 1e12, 3)
+
+    out = {"probe": {"read_tbs": rate(lambda r: bwprobe.read(x, sink), 8 * n),
+                     "copy_tbs": rate(lambda r: bwprobe.copy(a, b), 8 * n),
+                     "rmw_tbs": rate(lambda r: bwprobe.rmw(a, 1.0), 8 * n)},
+           "torch": {"read_tbs": rate(lambda r: torch.amax(x), 8 * n),
+                     "copy_tbs": rate(lambda r: b.copy_(a), 8 * n),
+                     "rmw_tbs": rate(lambda r: a.mul_(1.0), 8 * n)},
+           "peak_tbs": PEAK / 1e3}
+    print(json.dumps({"workload": "bandwidth ceilings: streaming probes (32 KiB per work-group, "
+                                  "non-temporal 16-byte accesses) and plain PyTorch kernels", **out}), flush=True)
+
+
 def run(args):
-    if args.workload == "mixer":
+    if args.workload == "ceilings":
+        ceilings(args)
+    elif args.workload == "mixer":
         mixer(args)
     elif args.workload == "spec":
         spec(args)

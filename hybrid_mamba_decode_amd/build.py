@@ -1,4 +1,5 @@
-"""Build libreplayssm.so (HIP, gfx950) in-tree.
+"""Build libreplayssm.so (HIP, gfx950) in-tree, and the benchmark's bandwidth probes
+(libbwprobe.so).
 
 kernels.hip (Mamba-2) and gdn_kernels.hip (Gated DeltaNet) are compiled once per supported state
 / key size N (in parallel), api.hip and gdn_api.hip once, and the objects are linked into
@@ -14,6 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libreplayssm.so")
+PROBE_LIB = os.path.join(PKG, "libbwprobe.so")  # bandwidth probes for the benchmark's ceilings
 STATE_SIZES = (16, 32, 64, 128, 256)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -55,6 +57,8 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
             f.result()
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs], verbose)
     os.replace(LIB + ".tmp", LIB)
+    _run([HIPCC, *FLAGS, "-shared", "-o", PROBE_LIB + ".tmp", os.path.join(CSRC, "bwprobe.hip")], verbose)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 
