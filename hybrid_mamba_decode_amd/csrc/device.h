@@ -573,39 +573,37 @@ struct CopyDst {
     int P, psplit;
 };
 
-// Read-copy writer for fp32 rows of one work-group's tile held in f32 geometry (vf; lane slot i
-// holds row i*RPB + wave*RPI + lane/LPR, four values from n = 4 (lane % LPR)), the tile's first
-// element at `elem0` of head bh. The tile is one block of kRows rows (tiles start at row 0).
-// bf16: each value to nearest even. fp8: the block's scale = amax / 448 over the work-group, codes
-// RNE-saturated by gfx950's converter. MXFP4: one E8M0 scale per 32 values of a row.
-template <int N, int PREC>
-__device__ inline void write_copy_rows_n(const CopyDst &d, size_t bh, size_t elem0,
-                                         const f32x4 (&vf)[Geo<N, PREC_F32>::NL], int nrows, int wave, int lane,
-                                         float *red)
+// Read-copy writer for fp32 values of one work-group's tile held in 4-value units: unit u of a
+// lane holds the four consecutive values n .. n + 3 of tile row r, with (r, n) = at(u). The tile's
+// first element is `elem0` of head bh, and it is one block of kRows rows (tiles start at row 0);
+// the work-group holds every value of its tile's valid rows (r < nrows) exactly once. For MXFP4
+// the eight units of a 32-value block sit, in order of n, in eight consecutive lanes with the
+// same u. bf16: each value to nearest even. fp8: the block's scale = amax / 448 over the
+// work-group, codes RNE-saturated by gfx950's converter. MXFP4: one E8M0 scale per 32 values.
+template <int N, int PREC, int NU, class At>
+__device__ inline void write_copy_units(const CopyDst &d, size_t bh, size_t elem0, const f32x4 (&vf)[NU], int nrows,
+                                        At at, float *red)
 {
-    using GF = Geo<N, PREC_F32>;
-    const int c = lane % GF::LPR;
-    auto row_of = [&](int i) { return i * GF::RPB + wave * GF::RPI + lane / GF::LPR; };
     if constexpr (PREC == PREC_BF16) {
         unsigned short *dst = (unsigned short *)d.rcopy + elem0;
 #pragma unroll
-        for (int i = 0; i < GF::NL; ++i) {
-            const int r = row_of(i);
-            if (r < nrows) {
-                const f32x4 f = vf[i];
+        for (int u = 0; u < NU; ++u) {
+            const int2 rn = at(u);
+            if (rn.x < nrows) {
+                const f32x4 f = vf[u];
                 u32x2 pk;
                 pk.x = bf16_rne(f.x) | (bf16_rne(f.y) << 16);
                 pk.y = bf16_rne(f.z) | (bf16_rne(f.w) << 16);
-                *(u32x2 *)(dst + (size_t)r * N + 4 * c) = pk;
+                *(u32x2 *)(dst + (size_t)rn.x * N + rn.y) = pk;
             }
         }
     } else if constexpr (PREC == PREC_FP8) {
         float amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < GF::NL; ++i) {
-            const f32x4 f = vf[i];
+        for (int u = 0; u < NU; ++u) {
+            const f32x4 f = vf[u];
             const float m = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
-            if (row_of(i) < nrows) amax = fmaxf(amax, m);
+            if (at(u).x < nrows) amax = fmaxf(amax, m);
         }
         amax = block_max(amax, red);
         const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
@@ -613,10 +611,10 @@ __device__ inline void write_copy_rows_n(const CopyDst &d, size_t bh, size_t ele
         unsigned char *dst = (unsigned char *)d.rcopy;
         const int row0 = (int)(elem0 / N - bh * (size_t)d.P);
 #pragma unroll
-        for (int i = 0; i < GF::NL; ++i) {
-            const int r = row_of(i);
-            if (r < nrows) {
-                const f32x4 f = vf[i];
+        for (int u = 0; u < NU; ++u) {
+            const int2 rn = at(u);
+            if (rn.x < nrows) {
+                const f32x4 f = vf[u];
                 // clamp to the largest finite code, then the converter rounds to nearest even
                 // (four codes per dword, two per instruction)
                 const float a0 = fminf(fmaxf(f.x * inv, -448.0f), 448.0f);
@@ -625,34 +623,46 @@ __device__ inline void write_copy_rows_n(const CopyDst &d, size_t bh, size_t ele
                 const float a3 = fminf(fmaxf(f.w * inv, -448.0f), 448.0f);
                 int q = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
                 q = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, q, true);
-                const int n = 4 * c;
-                *(unsigned *)(dst + state_chunk_off<N, PREC_FP8>(bh, row0 + r, n / 16, d.P) + n % 16) = (unsigned)q;
+                *(unsigned *)(dst + state_chunk_off<N, PREC_FP8>(bh, row0 + rn.x, rn.y / 16, d.P) + rn.y % 16) =
+                    (unsigned)q;
             }
         }
         if (threadIdx.x == 0) d.scale[bh * d.psplit + row0 / kRows] = scale;
     } else if constexpr (PREC == PREC_FP4) {
-        // One 32-value block = 8 consecutive lanes of a row (4 values each); its amax by three
-        // lane exchanges, then each lane encodes its 4 values into 2 bytes and the block's first
-        // lane writes the scale byte.
+        // A 32-value block is 8 consecutive lanes (4 values each): its amax by three lane
+        // exchanges, then each lane encodes its 4 values into 2 bytes and the block's first lane
+        // writes the scale byte.
         unsigned char *dst = (unsigned char *)d.rcopy;
         unsigned char *sdst = d.mxscale + elem0 / 32;
         const int row0 = (int)(elem0 / N - bh * (size_t)d.P);
 #pragma unroll
-        for (int i = 0; i < GF::NL; ++i) {
-            const int r = row_of(i);
-            const f32x4 f = vf[i];
+        for (int u = 0; u < NU; ++u) {
+            const int2 rn = at(u);
+            const f32x4 f = vf[u];
             float amax = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
             amax = group_max(amax, 8);
             const unsigned code = mx_code_of(amax);
-            if (r < nrows) {
-                const int n = 4 * c;
-                *(unsigned short *)(dst + state_chunk_off<N, PREC_FP4>(bh, row0 + r, n / 32, d.P) + (n % 32) / 2) =
-                    mx_encode4(f, code);
-                if (c % 8 == 0) sdst[((size_t)r * N + n) / 32] = (unsigned char)code;
+            if (rn.x < nrows) {
+                *(unsigned short *)(dst + state_chunk_off<N, PREC_FP4>(bh, row0 + rn.x, rn.y / 32, d.P) +
+                                    (rn.y % 32) / 2) = mx_encode4(f, code);
+                if (rn.y % 32 == 0) sdst[((size_t)rn.x * N + rn.y) / 32] = (unsigned char)code;
             }
         }
         (void)red;
     }
+}
+
+// The same for f32 geometry (Geo<N, PREC_F32>: unit i of a lane is row i*RPB + wave*RPI +
+// lane/LPR, values from n = 4 (lane % LPR)).
+template <int N, int PREC>
+__device__ inline void write_copy_rows_n(const CopyDst &d, size_t bh, size_t elem0,
+                                         const f32x4 (&vf)[Geo<N, PREC_F32>::NL], int nrows, int wave, int lane,
+                                         float *red)
+{
+    using GF = Geo<N, PREC_F32>;
+    const int c = lane % GF::LPR;
+    auto at = [&](int i) { return int2{i * GF::RPB + wave * GF::RPI + lane / GF::LPR, 4 * c}; };
+    write_copy_units<N, PREC, GF::NL>(d, bh, elem0, vf, nrows, at, red);
 }
 
 }  // namespace rssm

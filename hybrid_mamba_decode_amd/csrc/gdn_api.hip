@@ -206,7 +206,7 @@ rssm_status gdnreplay_step(gdnreplay_t h, const float *q, const float *k, const 
     if (h->cfg.batch == 0) return RSSM_OK;
     const GTokenIO io{q, k, v, alpha, beta, o};
     const hipStream_t st = (hipStream_t)stream;
-#define CALL(NV) gdn_launch_step_n##NV(h->lmax, h->dev, io, p.flush_capable, ls, st)
+#define CALL(NV) gdn_launch_step_n##NV(h->lmax, h->dev, io, p.flush_capable, p.all_flush, ls, st)
     GDN_BY_N(h->cfg.dk, CALL)
 #undef CALL
 }

@@ -566,6 +566,149 @@ __global__ void __launch_bounds__(kThreads) gdn_step_kernel(GLayer Ld, GTokenIO 
     step_advance(Ld, t, uni, pslot, cslot, k, flush, pos, ck, Ld.psplit);
 }
 
+// ==========================================================================================
+// Flush step when every sequence of the launch flushes (lockstep decoding, or a host bound showing
+// every buffer fills), Dk >= 128: the fold with 16 values per lane, LW = Dk / 16 lanes per row
+// (8 at Dk = 128), lane c of a row holding chunks c + LW i (i = 0..3, four consecutive key
+// columns each), so every load instruction still reads 128 contiguous bytes of each row. The
+// delta rule's per-record row dot S_row . k_j then needs a reduction over LW lanes -- three
+// exchange steps at Dk = 128 instead of five over the 32 lanes of the f32 geometry -- which is
+// most of the fold's VALU work. Same arithmetic as gdn_fold_rows (records applied in order).
+// ==========================================================================================
+constexpr int kW = 16;                          // values per lane and row
+constexpr int kLW = NN / kW;                    // lanes per row
+constexpr int kRW = kThreads / (kLW > 0 ? kLW : 1);  // rows per work-group instruction
+constexpr int kNW = (kRows + kRW - 1) / kRW;    // row slots per lane
+constexpr bool kWideFold = NN >= 128;
+
+template <int LMAX>
+__global__ void __launch_bounds__(kThreads) gdn_flush_step_kernel(GLayer Ld, GTokenIO io, Lockstep ls)
+{
+    static_assert(kWideFold, "16 values per lane: Dk >= 128 (an MXFP4 block is 8 consecutive lanes)");
+    __shared__ GStepLds<LMAX> s;
+    const Tile t = gmap_tile(Ld);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const size_t bh = (size_t)t.b * Ld.H + t.h;
+    const size_t elem0 = (bh * Ld.Dv + t.row0) * NN;
+    const int c = tid % kLW;
+    auto row_of = [&](int sl) { return sl * kRW + tid / kLW; };  // tile row of slot sl
+    auto ncol = [&](int i) { return 4 * (c + kLW * i); };         // first key column of chunk i
+
+    // 1. Pointers and window (as gdn_step_kernel), then the master rows.
+    StepWindow<LMAX, kRows> win(Ld, t, tid);
+    const bool uni = ls.k > 0;
+    int pslot = 0, cslot = 0, k = 1, pos = 0, ck = 0;
+    if (uni) {
+        pslot = ls.pslot;
+        cslot = ls.cslot;
+        k = ls.k;
+        if (!(k > Ld.L - Ld.Tmax && k <= Ld.L)) {  // the host launches this kernel for flush steps only
+            graise(Ld, FLAG_POINTERS);
+            return;
+        }
+    } else {
+        pos = Ld.pos[t.b];
+        ck = Ld.ckpt[t.b];
+        const int c0 = pos - ck;
+        if (!(ck >= 0 && c0 >= 0 && c0 <= Ld.L - Ld.Tmax && c0 + 1 > Ld.L - Ld.Tmax)) {
+            graise(Ld, FLAG_POINTERS);
+            gseq_done(Ld, t.b, pos, ck);
+            return;
+        }
+        pslot = (int)((unsigned)pos % (unsigned)Ld.L);
+        cslot = (int)((unsigned)ck % (unsigned)Ld.L);
+        k = c0 + 1;
+    }
+    win.issue(Ld, io, t, cslot, k);
+    f32x4 vf[kNW][4];
+#pragma unroll
+    for (int sl = 0; sl < kNW; ++sl) {
+        const int r = row_of(sl), rr = r < t.nrows ? r : 0;
+        const float *rowp = Ld.master + elem0 + (size_t)rr * NN;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vf[sl][i] = as_f32x4(load_nt(rowp + ncol(i)));
+    }
+    win.commit(s.w, s.q, Ld, io);
+    __syncthreads();
+
+    // 2. Fold: S_row <- alpha_j (S_row - beta_j (S_row . k_j) k_j) + beta_j v_j[row] k_j, j in order.
+    int rowc[kNW];
+#pragma unroll
+    for (int sl = 0; sl < kNW; ++sl) rowc[sl] = row_of(sl) < kRows ? row_of(sl) : 0;
+    for (int j = 0; j < k; ++j) {
+        f32x4 kv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kv[i] = *(const f32x4 *)&s.w.K[j][ncol(i)];
+        const float aj = s.w.a[j], bj = s.w.b[j];
+#pragma unroll
+        for (int sl = 0; sl < kNW; ++sl) {
+            float part = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                part = fmaf(vf[sl][i].x, kv[i].x, part);
+                part = fmaf(vf[sl][i].y, kv[i].y, part);
+                part = fmaf(vf[sl][i].z, kv[i].z, part);
+                part = fmaf(vf[sl][i].w, kv[i].w, part);
+            }
+            const float sk = group_sum<kLW>(part);
+            // alpha (S - beta sk k) + beta v k = alpha S + (beta v - alpha beta sk) k
+            const float coef = bj * (s.w.V[j][rowc[sl]] - aj * sk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vf[sl][i].x = fmaf(coef, kv[i].x, aj * vf[sl][i].x);
+                vf[sl][i].y = fmaf(coef, kv[i].y, aj * vf[sl][i].y);
+                vf[sl][i].z = fmaf(coef, kv[i].z, aj * vf[sl][i].z);
+                vf[sl][i].w = fmaf(coef, kv[i].w, aj * vf[sl][i].w);
+            }
+        }
+    }
+
+    // 3. Store the master, encode the read copy, o = S_new q.
+#pragma unroll
+    for (int sl = 0; sl < kNW; ++sl) {
+        const int r = row_of(sl);
+        if (r < t.nrows) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) store_nt(Ld.master + elem0 + (size_t)r * NN + ncol(i), as_u32x4(vf[sl][i]));
+        }
+    }
+    {
+        f32x4 units[kNW * 4];
+#pragma unroll
+        for (int u = 0; u < kNW * 4; ++u) units[u] = vf[u / 4][u % 4];
+        auto at = [&](int u) { return int2{row_of(u / 4), ncol(u % 4)}; };
+        const CopyDst d{Ld.rcopy, Ld.scale, Ld.mxscale, Ld.Dv, Ld.psplit};
+        switch (Ld.rprec) {
+        case PREC_BF16: write_copy_units<NN, PREC_BF16, kNW * 4>(d, bh, elem0, units, t.nrows, at, s.red); break;
+        case PREC_FP8: write_copy_units<NN, PREC_FP8, kNW * 4>(d, bh, elem0, units, t.nrows, at, s.red); break;
+        case PREC_FP4: write_copy_units<NN, PREC_FP4, kNW * 4>(d, bh, elem0, units, t.nrows, at, s.red); break;
+        default: break;
+        }
+    }
+    {
+        f32x4 qv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[i] = *(const f32x4 *)&s.q[ncol(i)];
+#pragma unroll
+        for (int sl = 0; sl < kNW; ++sl) {
+            float part = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                part = fmaf(vf[sl][i].x, qv[i].x, part);
+                part = fmaf(vf[sl][i].y, qv[i].y, part);
+                part = fmaf(vf[sl][i].z, qv[i].z, part);
+                part = fmaf(vf[sl][i].w, qv[i].w, part);
+            }
+            const float o = group_sum<kLW>(part);
+            const int r = row_of(sl);
+            if (c == 0 && r < t.nrows) io.o[bh * Ld.Dv + t.row0 + r] = o;
+        }
+    }
+    // 4. Pointers (the token's record is folded already: nothing is appended).
+    step_advance(Ld, t, uni, pslot, cslot, k, true, pos, ck, Ld.psplit);
+    (void)lane;
+}
+
 // Non-flush step reading the copy (bf16, fp8 or MXFP4) with one work-group per kRowsC = 128 value
 // rows (a whole head at Dv = 128): 16-byte loads of one chunk per lane (8 bf16, 16 fp8 or 32 fp4
 // values), so each work-group streams twice the rows of a 64-row tile for the same fixed window
@@ -1141,8 +1284,14 @@ __global__ void __launch_bounds__(kThreads) gdn_snapshot_kernel(GLayer Ld, float
 inline unsigned gblocks(const GLayer &Ld) { return (unsigned)Ld.Bt * (unsigned)Ld.H * (unsigned)Ld.psplit; }
 
 template <int LMAX, int RP>
-hipError_t step_lc(const GLayer &Ld, const GTokenIO &io, bool fc, Lockstep ls, hipStream_t st)
+hipError_t step_lc(const GLayer &Ld, const GTokenIO &io, bool fc, bool all_flush, Lockstep ls, hipStream_t st)
 {
+    if constexpr (kWideFold) {
+        if (fc && all_flush) {
+            hipLaunchKernelGGL((gdn_flush_step_kernel<LMAX>), dim3(gblocks(Ld)), dim3(kThreads), 0, st, Ld, io, ls);
+            return hipGetLastError();
+        }
+    }
     if constexpr (kCopyTiles<RP> && LMAX <= 32) {
         if (!fc) {
             const int splits = (Ld.Dv + kRowsC - 1) / kRowsC;
@@ -1175,17 +1324,17 @@ template <int LMAX>
 struct StepL {
     template <int RP>
     struct F {
-        static hipError_t run(const GLayer &Ld, const GTokenIO &io, bool fc, Lockstep ls, hipStream_t st)
+        static hipError_t run(const GLayer &Ld, const GTokenIO &io, bool fc, bool af, Lockstep ls, hipStream_t st)
         {
-            return step_lc<LMAX, RP>(Ld, io, fc, ls, st);
+            return step_lc<LMAX, RP>(Ld, io, fc, af, ls, st);
         }
     };
 };
 
 template <int LMAX>
-hipError_t step_l(const GLayer &Ld, const GTokenIO &io, bool fc, Lockstep ls, hipStream_t st)
+hipError_t step_l(const GLayer &Ld, const GTokenIO &io, bool fc, bool af, Lockstep ls, hipStream_t st)
 {
-    return by_rprec<StepL<LMAX>::template F>(Ld.rprec, Ld, io, fc, ls, st);
+    return by_rprec<StepL<LMAX>::template F>(Ld.rprec, Ld, io, fc, af, ls, st);
 }
 
 template <int LMAX>
@@ -1242,12 +1391,12 @@ hipError_t verify_l(const GLayer &Ld, const GTokenIO &io, int T, hipStream_t st)
 #define RSSM_CAT(a, b) RSSM_CAT2(a, b)
 
 hipError_t RSSM_CAT(gdn_launch_step_n, RSSM_N)(int lmax, const GLayer &Ld, const GTokenIO &io, bool flush_capable,
-                                               Lockstep ls, hipStream_t st)
+                                               bool all_flush, Lockstep ls, hipStream_t st)
 {
     switch (lmax) {
-    case 16: return step_l<16>(Ld, io, flush_capable, ls, st);
-    case 32: return step_l<32>(Ld, io, flush_capable, ls, st);
-    case 64: return step_l<64>(Ld, io, flush_capable, ls, st);
+    case 16: return step_l<16>(Ld, io, flush_capable, all_flush, ls, st);
+    case 32: return step_l<32>(Ld, io, flush_capable, all_flush, ls, st);
+    case 64: return step_l<64>(Ld, io, flush_capable, all_flush, ls, st);
     default: return hipErrorInvalidValue;
     }
 }

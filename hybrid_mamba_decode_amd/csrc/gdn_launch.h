@@ -34,7 +34,7 @@ struct GTokenIO {
 
 #define RSSM_DECLARE_GDN_LAUNCHERS(NV)                                                                       \
     hipError_t gdn_launch_step_n##NV(int lmax, const GLayer &Ld, const GTokenIO &io, bool flush_capable,     \
-                                     Lockstep ls, hipStream_t st);                                           \
+                                     bool all_flush, Lockstep ls, hipStream_t st);                           \
     hipError_t gdn_launch_flush_n##NV(int lmax, const GLayer &Ld, int mode, const int *arg, int T, float *out, \
                                       hipStream_t st);                                                       \
     hipError_t gdn_launch_verify_n##NV(int lmax, const GLayer &Ld, const GTokenIO &io, int T, hipStream_t st);  \
