@@ -965,9 +965,8 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
 #pragma unroll
         for (int sl = 0; sl < BCH; ++sl) {
             const int e = tid + sl * kThreads, j = e / (NN / 4), c4 = e % (NN / 4);
-            const float *src = (j < k - 1 ? rB + (size_t)slot_of(j) * NN : fB) + 4 * c4;
-            const f32x4 val = *(const f32x4 *)src;
-            bv[sl] = j < k ? val : zero;
+            if (j < k) bv[sl] = *(const f32x4 *)((j < k - 1 ? rB + (size_t)slot_of(j) * NN : fB) + 4 * c4);
+            else bv[sl] = zero;
         }
         {
             const f32x4 val = *(const f32x4 *)(Ct + 4 * (tid % (NN / 4)));
@@ -980,16 +979,17 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
             Ah = Ld.A[h];
         }
     };
+    // k is the same for the work-group's heads (one sequence): the record loops below branch on
+    // it uniformly, so a short window costs only its own records.
     auto issue_x = [&]() {
         const float *fx = io.x + bh * Ld.P + p;
         const float *rx = Ld.ring_x + bh * Ld.L * Ld.P + p;
+        xt = *fx;
 #pragma unroll
         for (int j = 0; j < LMAX; ++j) {
-            const float *src = j < k - 1 ? rx + (size_t)slot_of(j) * Ld.P : fx;
-            const float val = *src;
-            xj[j] = j < k ? val : 0.f;
+            if (j < k - 1) xj[j] = rx[(size_t)slot_of(j) * Ld.P];
+            else xj[j] = j == k - 1 ? xt : 0.f;
         }
-        xt = *fx;
     };
 
     // Invalid device pointers are only noted here and reported after the row dots (with safe
@@ -1051,7 +1051,8 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
         constexpr int GS = kThreads / LMAX;
         const int j = tid / GS, sub = tid % GS;
         float gj = 0.f;
-        for (int n = sub; n < NN; n += GS) gj = fmaf(s.Bw[j][n], s.Cq[n], gj);
+        if (j < k)
+            for (int n = sub; n < NN; n += GS) gj = fmaf(s.Bw[j][n], s.Cq[n], gj);
 #pragma unroll
         for (int o = GS / 2; o >= 1; o >>= 1) gj += __shfl_xor(gj, o, 64);
         if (sub == 0) s.g[j] = gj;
@@ -1060,14 +1061,16 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
     const float cj = lane < LMAX ? wj * s.g[lane < LMAX ? lane : 0] : 0.f;  // lane j: w_j * g_j
 
     // 6. Row dot S_c[p,:] . C_t through the copy. C_t's chunk-column slice is the same for every
-    //    lane: broadcast reads of the staged C. The empty asm ties each chunk's decode to the
-    //    running sums, so chunks are decoded one at a time instead of all at once (which would
-    //    hold N decoded values per lane).
+    //    lane: it is read from global memory at a wave-uniform address, which the compiler serves
+    //    by scalar loads into SGPRs (operands of the FMAs; no LDS traffic, no C registers per
+    //    lane -- broadcast LDS reads of the staged C cost 8 LDS cycles per 16 bytes). The empty asm
+    //    ties each chunk's decode to the running sums, so chunks are decoded one at a time
+    //    instead of all at once (which would hold N decoded values per lane).
     float u0 = 0.f, u1 = 0.f;
 #pragma unroll
     for (int q = 0; q < NC; ++q) {
         asm("" : "+v"(v[q]), "+v"(u0), "+v"(u1));
-        const float *cs = s.Cq + q * G::VEC;
+        const float *cs = Ct + q * G::VEC;
         const unsigned w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -1117,7 +1120,7 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
     float acc = decay * u;
 #pragma unroll
     for (int j = 0; j < LMAX; ++j)
-        acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(cj), j)), xj[j], acc);
+        if (j < k) acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(cj), j)), xj[j], acc);
     acc = fmaf(Ld.D[h], xt, acc);
     if (prow) {
         io.y[bh * Ld.P + p] = acc;
