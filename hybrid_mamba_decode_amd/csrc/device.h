@@ -423,10 +423,111 @@ __device__ inline unsigned short mx_encode4(f32x4 f, unsigned code)
 }
 
 // ------------------------------------------------------------------------------------------
+// Cross-lane exchanges that stay in the VALU. On gfx950 a __shfl_* lowers to ds_bpermute: an
+// LDS round trip plus address arithmetic per call, which serializes reductions inside record
+// loops. Within a row of 16 lanes DPP moves the data; across rows and halves of the wave the
+// permlane swaps do (v_permlane16_swap / v_permlane32_swap, new in gfx950).
+// ------------------------------------------------------------------------------------------
+// DPP move of v (dpp_ctrl CTRL); a lane whose source lies outside its row reads 0.
+template <int CTRL>
+__device__ inline float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Both values of the lane pair (l, l ^ O), O = 16 or 32, from one swap of two copies of v: the
+// lane with bit O clear holds its own value in .x and its partner's in .y, the other lane the
+// reverse (the swap exchanges the odd rows of the first copy with the even rows of the second,
+// or the upper half of the first with the lower half of the second).
+template <int O>
+__device__ inline f32x2 pair_far(float v)
+{
+    static_assert(O == 16 || O == 32, "permlane swaps exchange rows of 16 or halves of 32");
+    const unsigned u = __float_as_uint(v);
+    if constexpr (O == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+    }
+}
+
+// Value of lane l ^ O for O = 1, 2, 16, 32. For O = 4 and 8 the partner is l ^ 7 and l ^ 15 (the
+// half-row and row mirrors): still a lane whose bit O differs and whose bits above O agree, so a
+// butterfly or transpose that runs its offsets from high to low down to 1 pairs the same sets.
+template <int O>
+__device__ inline float partner(float v, int lane)
+{
+    if constexpr (O == 1) return dpp_f<0xB1>(v);        // quad_perm [1,0,3,2]
+    else if constexpr (O == 2) return dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    else if constexpr (O == 4) return dpp_f<0x141>(v);  // row_half_mirror
+    else if constexpr (O == 8) return dpp_f<0x140>(v);  // row_mirror
+    else {
+        const f32x2 p = pair_far<O>(v);
+        return (lane & O) ? p.x : p.y;
+    }
+}
+
+// Sum over aligned groups of W lanes (W a power of two, <= 64); every lane of a group receives
+// the same value (each exchange adds a symmetric pair).
+template <int W>
+__device__ inline float group_sum(float v)
+{
+    if constexpr (W >= 64) { const f32x2 p = pair_far<32>(v); v = p.x + p.y; }
+    if constexpr (W >= 32) { const f32x2 p = pair_far<16>(v); v = p.x + p.y; }
+    if constexpr (W >= 16) v += dpp_f<0x140>(v);
+    if constexpr (W >= 8) v += dpp_f<0x141>(v);
+    if constexpr (W >= 4) v += dpp_f<0x4E>(v);
+    if constexpr (W >= 2) v += dpp_f<0xB1>(v);
+    return v;
+}
+
+template <int W>
+__device__ inline float group_max(float v)
+{
+    if constexpr (W >= 64) { const f32x2 p = pair_far<32>(v); v = fmaxf(p.x, p.y); }
+    if constexpr (W >= 32) { const f32x2 p = pair_far<16>(v); v = fmaxf(p.x, p.y); }
+    if constexpr (W >= 16) v = fmaxf(v, dpp_f<0x140>(v));
+    if constexpr (W >= 8) v = fmaxf(v, dpp_f<0x141>(v));
+    if constexpr (W >= 4) v = fmaxf(v, dpp_f<0x4E>(v));
+    if constexpr (W >= 2) v = fmaxf(v, dpp_f<0xB1>(v));
+    return v;
+}
+
+// Inclusive suffix sums over the window's lanes: lane l receives sum_{i >= l} v_i. Records sit
+// in lanes 0 .. W-1 (W the window bound) and every other lane of the wave holds 0. For W <= 16
+// the four row shifts of the first row suffice (row_shl: lane l reads l + o, 0 past the row's
+// end); `next` receives the suffix sum from lane l + 1.
+template <int W>
+__device__ inline float suffix_sum(float v, int lane, float *next)
+{
+    if constexpr (W <= 16) {
+        v += dpp_f<0x101>(v);
+        v += dpp_f<0x102>(v);
+        v += dpp_f<0x104>(v);
+        v += dpp_f<0x108>(v);
+        *next = dpp_f<0x101>(v);
+    } else {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float nb = __shfl_down(v, o, 64);
+            v += lane + o < 64 ? nb : 0.f;
+        }
+        const float nxt = __shfl_down(v, 1, 64);
+        *next = lane + 1 < 64 ? nxt : 0.f;
+    }
+    return v;
+}
+
+// Lane 0's value, in every lane (a scalar read of the register).
+__device__ inline float lane0(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)); }
+
+// ------------------------------------------------------------------------------------------
 // Transpose-reduce. Each lane holds M partial sums (M a power of two); the LPR consecutive lanes
 // of a row group must each sum over the group. At every exchange step with lane offset o the
-// pair (l, l^o) splits its list: the lane with bit o clear keeps the first half and receives the
-// partner's first half, the other keeps the second half. Once one value is left, the remaining
+// pair (l, partner<o>(l)) splits its list: the lane with bit o clear keeps the first half and
+// receives the partner's first half, the other keeps the second half. Once one value is left, the remaining
 // offsets are plain butterflies. Afterwards a lane holds max(1, M/LPR) complete sums: those of
 // list entries [first, first + count) with first = its selected bits, see tr_first().
 // ------------------------------------------------------------------------------------------
@@ -442,11 +543,11 @@ struct TransposeStep {
                 for (int m = 0; m < half; ++m) {
                     const float send = upper ? v[m] : v[half + m];
                     const float keep = upper ? v[half + m] : v[m];
-                    v[m] = keep + __shfl_xor(send, O, 64);
+                    v[m] = keep + partner<O>(send, lane);
                 }
                 TransposeStep<M, O / 2, half>::run(v, lane);
             } else {
-                v[0] += __shfl_xor(v[0], O, 64);
+                v[0] += partner<O>(v[0], lane);
                 TransposeStep<M, O / 2, 1>::run(v, lane);
             }
         }
@@ -481,16 +582,10 @@ __device__ inline int tr_first(int lane, bool *writer)
 template <int M, int LPR>
 constexpr int tr_count() { return M / LPR > 1 ? M / LPR : 1; }
 
-__device__ inline float group_max(float v, int width)
-{
-    for (int o = width / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
 // Block-wide max of a non-negative value (all threads return it). `red` holds kWaves floats.
 __device__ inline float block_max(float v, float *red)
 {
-    v = group_max(v, 64);
+    v = group_max<64>(v);
     const int wave = threadIdx.x / 64;
     if ((threadIdx.x & 63) == 0) red[wave] = v;
     __syncthreads();
@@ -640,7 +735,7 @@ __device__ inline void write_copy_units(const CopyDst &d, size_t bh, size_t elem
             const int2 rn = at(u);
             const f32x4 f = vf[u];
             float amax = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
-            amax = group_max(amax, 8);
+            amax = group_max<8>(amax);
             const unsigned code = mx_code_of(amax);
             if (rn.x < nrows) {
                 *(unsigned short *)(dst + state_chunk_off<N, PREC_FP4>(bh, row0 + rn.x, rn.y / 32, d.P) +

@@ -124,29 +124,6 @@ __device__ inline void stage_window(GWin<LMAX> &w, const GLayer &Ld, const Tile 
     }
 }
 
-// Sum over aligned groups of W lanes (W a power of two, <= 64); every lane of a group receives
-// it. Lane exchanges by DPP within a row of 16 (quad permutes, then half-row and row mirrors:
-// after the quad steps a lane's value is its quad's sum, and a mirror pairs each lane with a
-// lane of the other half), a ds_swizzle xor 16 across the two rows of 32, and one ds_bpermute
-// across the halves of the wave.
-template <int CTRL>
-__device__ inline float dpp_mov(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-template <int W>
-__device__ inline float group_sum(float v)
-{
-    if constexpr (W >= 2) v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
-    if constexpr (W >= 4) v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
-    if constexpr (W >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror
-    if constexpr (W >= 16) v += dpp_mov<0x140>(v);  // row_mirror
-    if constexpr (W >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // xor 16
-    if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
-    return v;
-}
-
 // Sum of a value over the LPR consecutive lanes of a row (all of them receive it).
 __device__ inline float row_allreduce(float v) { return group_sum<GF::LPR>(v); }
 

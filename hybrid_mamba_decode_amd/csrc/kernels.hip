@@ -239,8 +239,7 @@ __device__ inline void window_weights(const Window<LMAX> &w, const float *Cq, in
     if (SCORES) {
         if (j <= last)
             for (int n = sub; n < NN; n += GS) g = fmaf(w.Bw[j][n], Cq[n], g);
-#pragma unroll
-        for (int o = GS / 2; o >= 1; o >>= 1) g += __shfl_xor(g, o, 64);
+        g = group_sum<GS>(g);
     }
     if (sub == 0 && j <= last) {
         float tail = 0.f;
@@ -780,15 +779,9 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     //    "Technical analysis": the recurrence unrolled over the window).
     float wj = 0.f;
     if (wave < HPB) {
-        float sfx = dtj;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float nb = __shfl_down(sfx, o, 64);
-            sfx += lane + o < 64 ? nb : 0.f;
-        }
-        const float nxt = __shfl_down(sfx, 1, 64);
-        const float tail = lane + 1 < 64 ? nxt : 0.f;
-        const float total = __shfl(sfx, 0, 64);
+        float tail;
+        const float sfx = suffix_sum<LMAX>(dtj, lane, &tail);
+        const float total = lane0(sfx);
         wj = lane < k ? dtj * expf(Aw * tail) : 0.f;
         if (lane < LMAX) s.w[wave][lane] = wj;
         if (lane == 0) s.decay[wave] = expf(Aw * total);
@@ -850,8 +843,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
             const int j = tid / GS, sub = tid % GS;
             float gj = 0.f;
             for (int n = sub; n < NN; n += GS) gj = fmaf(s.Bw[j][n], s.Cq[n], gj);
-#pragma unroll
-            for (int o = GS / 2; o >= 1; o >>= 1) gj += __shfl_xor(gj, o, 64);
+            gj = group_sum<GS>(gj);
             if (sub == 0)
 #pragma unroll
                 for (int hh = 0; hh < HPB; ++hh) s.coef[hh][j] = s.w[hh][j] * gj;
@@ -1034,16 +1026,10 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
     // w_j = dt_j * exp(A * sum_{i>j} dt_i), decay = exp(A * sum_i dt_i): suffix sums by shuffles
     float wj, decay;
     {
-        float sfx = dtj;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float nb = __shfl_down(sfx, o, 64);
-            sfx += lane + o < 64 ? nb : 0.f;
-        }
-        const float nxt = __shfl_down(sfx, 1, 64);
-        const float tail = lane + 1 < 64 ? nxt : 0.f;
+        float tail;
+        const float sfx = suffix_sum<LMAX>(dtj, lane, &tail);
         wj = lane < k ? dtj * expf(Ah * tail) : 0.f;
-        decay = expf(Ah * __shfl(sfx, 0, 64));
+        decay = expf(Ah * lane0(sfx));
     }
     __syncthreads();
     // 5. Scores g_j = B_j . C_t (GS threads per record).
@@ -1053,8 +1039,7 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
         float gj = 0.f;
         if (j < k)
             for (int n = sub; n < NN; n += GS) gj = fmaf(s.Bw[j][n], s.Cq[n], gj);
-#pragma unroll
-        for (int o = GS / 2; o >= 1; o >>= 1) gj += __shfl_xor(gj, o, 64);
+        gj = group_sum<GS>(gj);
         if (sub == 0) s.g[j] = gj;
     }
     __syncthreads();
@@ -1301,14 +1286,8 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
     }
     if (tid < NN / 4) *(f32x4 *)&s.Cq[4 * tid] = cq;
     if (wave == 0) {
-        float sfx = dtj;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float nb = __shfl_down(sfx, o, 64);
-            sfx += lane + o < 64 ? nb : 0.f;
-        }
-        const float nxt = __shfl_down(sfx, 1, 64);
-        const float tail = lane + 1 < 64 ? nxt : 0.f;
+        float tail;
+        const float sfx = suffix_sum<LMAX>(dtj, lane, &tail);
         if (lane < LMAX) s.w[lane] = lane < k ? dtj * expf(Ah * tail) : 0.f;
         if (lane == 0) s.decay = expf(Ah * sfx);
     }
@@ -1506,8 +1485,9 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
                 const f32x4 a = acc[q][0], b = acc[q][1];
                 float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
                                    fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-                amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-                amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+                const f32x2 a16 = pair_far<16>(amax);  // the row's four lane groups
+                const f32x2 a32 = pair_far<32>(fmaxf(a16.x, a16.y));
+                amax = fmaxf(a32.x, a32.y);
                 const unsigned code = mx_code_of(amax);
                 const unsigned lo = mx_encode4(a, code), hi = mx_encode4(b, code);
                 if (prow) {
@@ -1535,8 +1515,9 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
         yp = fmaf(b.z, c1.z, yp);
         yp = fmaf(b.w, c1.w, yp);
     }
-    yp += __shfl_xor(yp, 16, 64);
-    yp += __shfl_xor(yp, 32, 64);
+    const f32x2 y16 = pair_far<16>(yp);
+    const f32x2 y32 = pair_far<32>(y16.x + y16.y);
+    yp = y32.x + y32.y;
     if (g == 0 && prow) io.y[bh * Ld.P + pl] = fmaf(Ld.D[t.h], s.xw[k - 1][pl], yp);
 
     // 8. Pointers (the token's record is folded already: nothing is appended).
@@ -1779,8 +1760,7 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
         }
 #pragma unroll
         for (int q = 0; q < TQ; ++q)
-#pragma unroll
-            for (int o = GS / 2; o >= 1; o >>= 1) g[q] += __shfl_xor(g[q], o, 64);
+            g[q] = group_sum<GS>(g[q]);
         if (sub == 0)
 #pragma unroll
             for (int q = 0; q < TQ; ++q) s.gq[q][j] = g[q];
@@ -1793,15 +1773,9 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
     for (int q = wave; q < T; q += kWaves) {
         const int last = count0 + q;
         const float d = lane <= last && lane < LMAX ? s.win.dts[lane] : 0.f;
-        float sfx = d;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float nb = __shfl_down(sfx, o, 64);
-            sfx += lane + o < 64 ? nb : 0.f;
-        }
-        const float nxt = __shfl_down(sfx, 1, 64);
-        const float tail = lane + 1 < 64 ? nxt : 0.f;
-        const float total = __shfl(sfx, 0, 64);
+        float tail;
+        const float sfx = suffix_sum<LMAX>(d, lane, &tail);
+        const float total = lane0(sfx);
         if (lane < LMAX) s.coef[q][lane] = lane <= last ? d * expf(A * tail) * s.gq[q][lane] : 0.f;
         if (lane == 0) s.decay[q] = expf(A * total);
     }
