@@ -1261,6 +1261,21 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
             mv[q] = load_nt((const unsigned short *)Ld.master + rowe + 32 * q + 8 * g);
     }
 
+    // SR: the Philox words depend on positions only; they are drawn while the window and master
+    // loads are in flight (the empty asm keeps the compiler from sinking them past the barrier).
+    const unsigned newck = (unsigned)(dpos + 1);  // stochastic rounding runs in device-pointer mode
+    const size_t seq0 = (size_t)t.b * Ld.H * Ld.P * NN;
+    unsigned wd[NQ][4];  // SR: the eight 16-bit fields of each group of eight values
+    if constexpr (SR) {
+        const unsigned e8 = (unsigned)((rowe - seq0) / 8) + (unsigned)g;  // first group's counter
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const U32x4 rnd = philox4x32_10(e8 + 4u * q, (unsigned)t.b, newck, 0u, Ld.sr_seed, 0u);
+            wd[q][0] = rnd.x; wd[q][1] = rnd.y; wd[q][2] = rnd.z; wd[q][3] = rnd.w;
+            asm volatile("" : "+v"(wd[q][0]), "+v"(wd[q][1]), "+v"(wd[q][2]), "+v"(wd[q][3]));
+        }
+    }
+
     // 3. Commit the window to LDS; the window's weights in wave 0 (suffix sums of dt by lane
     //    shuffles: w_j = dt_j exp(A sum_{i>j} dt_i), decay = exp(A sum_i dt_i)).
 #pragma unroll
@@ -1330,17 +1345,6 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
             }
     }
 
-    const unsigned newck = (unsigned)(dpos + 1);  // stochastic rounding runs in device-pointer mode
-    const size_t seq0 = (size_t)t.b * Ld.H * Ld.P * NN;
-    unsigned wd[NQ][4];  // SR: the eight 16-bit fields of each group of eight values
-    if constexpr (SR) {
-        const unsigned e8 = (unsigned)((rowe - seq0) / 8) + (unsigned)g;  // first group's counter
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const U32x4 rnd = philox4x32_10(e8 + 4u * q, (unsigned)t.b, newck, 0u, Ld.sr_seed, 0u);
-            wd[q][0] = rnd.x; wd[q][1] = rnd.y; wd[q][2] = rnd.z; wd[q][3] = rnd.w;
-        }
-    }
     if constexpr (F8M) {
         // 5'. fp8 master: the head's amax, scale = amax / 448, codes of value / scale to nearest
         //     even (the converter) or by the 16-bit stochastic rule (e4m3_sr), stored in the
