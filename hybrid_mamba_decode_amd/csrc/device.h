@@ -401,10 +401,11 @@ __device__ inline float mx_scaled(float part, unsigned code) { return __builtin_
 // MXFP4 encode of four consecutive fp32 values of one block, given the block's amax: returns the
 // E8M0 code; `codes` gets the two code bytes (element order low nibble first). Scale exponent =
 // max(biased exponent of amax - 2, 0), so every value / scale is below 8; the division is exact
-// (multiplication by 2^(127 - code), a normal fp32 for codes 0..253). Quotients of magnitude
-// below 0.25 are set to a signed zero first (they round to zero; this keeps fp32 denormals out
-// of the converter); gfx950's v_cvt_scalef32_pk_fp4_f32 then rounds to nearest even and clamps
-// to +-6 (checked on the GPU against that rule over dense sweeps of [2^-4, 8], ties included).
+// (multiplication by 2^(127 - code), a normal fp32 for codes 0..253; a product that underflows
+// is below 0.25 either way). gfx950's v_cvt_scalef32_pk_fp4_f32 rounds to nearest even and
+// clamps to +-6 (checked on the GPU against that rule over dense sweeps of [2^-4, 8], ties
+// included); every fp32 value of magnitude below 0.25 -- signed zeros and denormals too -- gives
+// the signed zero code (0 or 8: checked on the GPU over all 2 x 1,048,576,000 of them).
 __device__ inline unsigned mx_code_of(float amax)
 {
     const int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
@@ -414,9 +415,7 @@ __device__ inline unsigned mx_code_of(float amax)
 __device__ inline unsigned short mx_encode4(f32x4 f, unsigned code)
 {
     const float inv = __uint_as_float((254u - code) << 23);  // 2^(127 - code)
-    float a[4] = {f.x * inv, f.y * inv, f.z * inv, f.w * inv};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = fabsf(a[i]) < 0.25f ? copysignf(0.0f, a[i]) : a[i];
+    const float a[4] = {f.x * inv, f.y * inv, f.z * inv, f.w * inv};
     const unsigned lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a[0], a[1], 1.0f, 0) & 0xFFu;
     const unsigned hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a[2], a[3], 1.0f, 0) & 0xFFu;
     return (unsigned short)(lo | (hi << 8));
