@@ -1725,30 +1725,9 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
     }
     __syncthreads();  // s.Cq complete
 
-    // S_c C_q one query at a time (its C chunk from LDS): the tile's rows stay in registers while a
-    // pass holds one chunk set and NL partial sums -- 62 registers at fp32 against 78 with every
-    // query's chunks and partial sums live at once, so 8 waves per SIMD instead of 6.
-    constexpr int QB = 1;
-    const float scl = PREC == PREC_FP8 ? Ld.scale[bh * Ld.psplit + t.split] : 1.0f;
-#pragma unroll
-    for (int q0 = 0; q0 < TQ; q0 += QB) {
-        if (q0 >= T) break;
-        float cc[QB][G::VEC];
-#pragma unroll
-        for (int q = 0; q < QB; ++q) load_cchunk<PREC>(cc[q], s.Cq[q0 + q], lane);
-        float part[G::NL * QB];
-#pragma unroll
-        for (int q = 0; q < QB; ++q)
-#pragma unroll
-            for (int i = 0; i < G::NL; ++i) {
-                part[q * G::NL + i] = chunk_dot<PREC>(v[i], cc[q]);
-                if constexpr (PREC == PREC_FP4) part[q * G::NL + i] = mx_scaled(part[q * G::NL + i], sc[i]);
-            }
-        rows_to_lds<PREC, G::NL * QB>(part, &s.u[q0][0], kRows, T - q0, G::NL, scl, wave, lane);
-    }
-    __syncthreads();
-
-    // Scores B_j . C_q for every query: GS threads per record, the B row read once for all q.
+    // Scores B_j . C_q for every query (GS threads per record, the B row read once for all q) and
+    // the window weights come first: they need only the window, so they run while the tile's rows
+    // are still arriving, and the row products follow.
     {
         constexpr int GS = kThreads / LMAX;
         const int j = tid / GS, sub = tid % GS;
@@ -1782,6 +1761,29 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(Layer Ld, TokenIO io, 
         const float total = lane0(sfx);
         if (lane < LMAX) s.coef[q][lane] = lane <= last ? d * expf(A * tail) * s.gq[q][lane] : 0.f;
         if (lane == 0) s.decay[q] = expf(A * total);
+    }
+    __syncthreads();
+
+    // S_c C_q one query at a time (its C chunk from LDS): the tile's rows stay in registers while a
+    // pass holds one chunk set and NL partial sums -- 62 registers at fp32 against 78 with every
+    // query's chunks and partial sums live at once, so 8 waves per SIMD instead of 6.
+    constexpr int QB = 1;
+    const float scl = PREC == PREC_FP8 ? Ld.scale[bh * Ld.psplit + t.split] : 1.0f;
+#pragma unroll
+    for (int q0 = 0; q0 < TQ; q0 += QB) {
+        if (q0 >= T) break;
+        float cc[QB][G::VEC];
+#pragma unroll
+        for (int q = 0; q < QB; ++q) load_cchunk<PREC>(cc[q], s.Cq[q0 + q], lane);
+        float part[G::NL * QB];
+#pragma unroll
+        for (int q = 0; q < QB; ++q)
+#pragma unroll
+            for (int i = 0; i < G::NL; ++i) {
+                part[q * G::NL + i] = chunk_dot<PREC>(v[i], cc[q]);
+                if constexpr (PREC == PREC_FP4) part[q * G::NL + i] = mx_scaled(part[q * G::NL + i], sc[i]);
+            }
+        rows_to_lds<PREC, G::NL * QB>(part, &s.u[q0][0], kRows, T - q0, G::NL, scl, wave, lane);
     }
     __syncthreads();
 
