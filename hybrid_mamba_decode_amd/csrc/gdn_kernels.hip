@@ -124,8 +124,25 @@ __device__ inline void stage_window(GWin<LMAX> &w, const GLayer &Ld, const Tile 
     }
 }
 
+// Sum over aligned groups of W lanes for the record loops below (every lane of a group receives
+// it): DPP within the row of 16, then ds_swizzle (xor 16) and ds_bpermute (xor 32) -- in these
+// dependent per-record chains the LDS-pipe exchanges measured faster than gfx950's permlane swaps
+// that device.h's group_sum uses (spec verify + commit at batch 512, T 4: 352 -> 338 us fp32,
+// 292 -> 284 us bf16).
+template <int W>
+__device__ inline float record_sum(float v)
+{
+    if constexpr (W >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+    if constexpr (W >= 16) v += dpp_f<0x140>(v); // row_mirror
+    if constexpr (W >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // xor 16
+    if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
 // Sum of a value over the LPR consecutive lanes of a row (all of them receive it).
-__device__ inline float row_allreduce(float v) { return group_sum<GF::LPR>(v); }
+__device__ inline float row_allreduce(float v) { return record_sum<GF::LPR>(v); }
 
 // Backward sweep of one query over records last..0 in the calling wave: z <- q; c_j = beta_j
 // (k_j . z); z <- alpha_j (z - c_j k_j). Writes c_j to c[j] and the final z to z_out (lane 0 and
@@ -146,7 +163,7 @@ __device__ inline void gdn_sweep(const GWin<LMAX, RT> &w, const float *q, int la
             const int n = lane + 64 * e;
             if (n < NN) part = fmaf(z[e], w.K[j][n], part);
         }
-        part = group_sum<64>(part);
+        part = record_sum<64>(part);
         const float cj = w.b[j] * part;
         const float aj = w.a[j];
 #pragma unroll
