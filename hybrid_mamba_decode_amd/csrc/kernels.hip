@@ -1489,9 +1489,9 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
                 const f32x4 a = acc[q][0], b = acc[q][1];
                 float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
                                    fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-                const f32x2 a16 = pair_far<16>(amax);  // the row's four lane groups
-                const f32x2 a32 = pair_far<32>(fmaxf(a16.x, a16.y));
-                amax = fmaxf(a32.x, a32.y);
+                // the row's four lane groups: LDS-pipe exchanges keep these off the VALU
+                amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(amax), 0x401F)));
+                amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
                 const unsigned code = mx_code_of(amax);
                 const unsigned lo = mx_encode4(a, code), hi = mx_encode4(b, code);
                 if (prow) {
@@ -1519,9 +1519,8 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
         yp = fmaf(b.z, c1.z, yp);
         yp = fmaf(b.w, c1.w, yp);
     }
-    const f32x2 y16 = pair_far<16>(yp);
-    const f32x2 y32 = pair_far<32>(y16.x + y16.y);
-    yp = y32.x + y32.y;
+    yp += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(yp), 0x401F));  // xor 16
+    yp += __shfl_xor(yp, 32, 64);
     if (g == 0 && prow) io.y[bh * Ld.P + pl] = fmaf(Ld.D[t.h], s.xw[k - 1][pl], yp);
 
     // 8. Pointers (the token's record is folded already: nothing is appended).
