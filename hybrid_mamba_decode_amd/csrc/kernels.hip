@@ -1154,13 +1154,20 @@ __global__ void __launch_bounds__(kThreads) narrow_step_kernel(Layer Ld, TokenIO
 // ==========================================================================================
 template <int LMAX>
 struct LpFlushLds {
-    float xw[LMAX][kRows] __attribute__((aligned(16)));  // x of each record, this head's rows
-    float Bw[LMAX][NN + 4] __attribute__((aligned(16))); // B of each record; padded: the four lane
-                                                         // groups of a wave read four records
-    float Cq[NN] __attribute__((aligned(16)));           // C of this token
     float w[LMAX];
     float decay;
     float red[kWaves];
+    union {
+        struct {
+            float xw[LMAX][kRows] __attribute__((aligned(16)));  // x of each record, this head's rows
+            float Bw[LMAX][NN + 4] __attribute__((aligned(16))); // B of each record; padded: the four
+                                                                 // lane groups of a wave read four records
+            float Cq[NN] __attribute__((aligned(16)));           // C of this token
+        };
+        // once the window is consumed: each wave's 16 stored fp16 rows, 16 bytes of padding per
+        // row so that the staging writes (16 rows at one column) spread over the banks
+        unsigned char tp[kWaves][16 * (2 * NN + 16)] __attribute__((aligned(16)));
+    };
 };
 
 template <int PREC, int LMAX, bool SR, bool F8M>
@@ -1345,6 +1352,28 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
             }
     }
 
+    // 7. y = S_stored[p,:] . C_t + D x_t: partial dots over the lane's n, summed over the four
+    //    lane groups of the row (acc holds the checkpoint as stored).
+    auto write_output = [&]() {
+        float yp = 0.f;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const f32x4 c0 = *(const f32x4 *)&s.Cq[32 * q + 8 * g];
+            const f32x4 c1 = *(const f32x4 *)&s.Cq[32 * q + 8 * g + 4];
+            const f32x4 a = acc[q][0], b = acc[q][1];
+            yp = fmaf(a.x, c0.x, yp);
+            yp = fmaf(a.y, c0.y, yp);
+            yp = fmaf(a.z, c0.z, yp);
+            yp = fmaf(a.w, c0.w, yp);
+            yp = fmaf(b.x, c1.x, yp);
+            yp = fmaf(b.y, c1.y, yp);
+            yp = fmaf(b.z, c1.z, yp);
+            yp = fmaf(b.w, c1.w, yp);
+        }
+        yp += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(yp), 0x401F));  // xor 16
+        yp += __shfl_xor(yp, 32, 64);
+        if (g == 0 && prow) io.y[bh * Ld.P + pl] = fmaf(Ld.D[t.h], s.xw[k - 1][pl], yp);
+    };
     if constexpr (F8M) {
         // 5'. fp8 master: the head's amax, scale = amax / 448, codes of value / scale to nearest
         //     even (the converter) or by the 16-bit stochastic rule (e4m3_sr), stored in the
@@ -1392,7 +1421,6 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
         //    0xFFF + bit 13; the stochastic rule adds 2^13 - 1 - (r16 >> 3) (see f16_sr). The codes
         //    are then packed by the round-toward-zero converter, exact on representable values. A
         //    wave with a value below 2^-14 redoes those values with the general routines.
-        unsigned short *mdst = (unsigned short *)Ld.master + rowe + 8 * g;
         bool sub = false;
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
@@ -1429,16 +1457,50 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
                 }
                 a = f32x4{r[0], r[1], r[2], r[3]};
             }
+        write_output();
+        // Nearest even: the codes go out in whole rows. A lane's 16 bytes per q cover 64 bytes of
+        // each of 16 rows per store instruction (half lines, which the counters show written back
+        // at 1.1-1.3x the bytes), so each wave stages its 16 rows through LDS (the window's space,
+        // free once every wave has formed its output) and writes them back as 4 rows = 1 KiB per
+        // instruction: 253-259 -> 220-227 us at batch 256. The stochastic variants are bound by
+        // their VALU work rather than by HBM, and there the extra barrier and LDS round trip cost
+        // more than they save (fp16 SR 309-312 -> 314-317 us): they store the fragments directly.
+        if constexpr (SR) {
+            unsigned short *mdst = (unsigned short *)Ld.master + rowe + 8 * g;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            if (prow) {
+            for (int q = 0; q < NQ; ++q) {
+                if (prow) {
+                    const f32x4 a = acc[q][0], b = acc[q][1];
+                    u32x4 pk;
+                    pk.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
+                    pk.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a.z, a.w));
+                    pk.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
+                    pk.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(b.z, b.w));
+                    store_nt(mdst + 32 * q, pk);
+                }
+            }
+        } else {
+            __syncthreads();
+            constexpr int RB = 2 * NN + 16;  // staged row bytes (padded)
+            constexpr int GR = 2 * NN / 16;  // 16-byte granules per row
+            unsigned char *tw = s.tp[wave];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
                 const f32x4 a = acc[q][0], b = acc[q][1];
                 u32x4 pk;
                 pk.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
                 pk.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a.z, a.w));
                 pk.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
                 pk.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(b.z, b.w));
-                store_nt(mdst + 32 * q, pk);
+                *(u32x4 *)(tw + c16 * RB + 2 * (32 * q + 8 * g)) = pk;
+            }
+            // a wave reads back only the rows it staged (its LDS accesses stay in order)
+            unsigned char *mrow = (unsigned char *)Ld.master + (bh * Ld.P + wave * 16) * (2 * NN);
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int e = i * 64 + lane, r = e / GR, c = e % GR;
+                const u32x4 v = *(const u32x4 *)(tw + r * RB + 16 * c);
+                if (wave * 16 + r < t.nrows) store_nt(mrow + r * (2 * NN) + 16 * c, v);
             }
         }
 
@@ -1502,26 +1564,7 @@ __global__ void __launch_bounds__(kThreads) lp_flush_step_kernel(Layer Ld, Token
         }
     }
 
-    // 7. y = S_stored[p,:] . C_t + D x_t: partial dots over the lane's n, summed over the four
-    //    lane groups of the row.
-    float yp = 0.f;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const f32x4 c0 = *(const f32x4 *)&s.Cq[32 * q + 8 * g];
-        const f32x4 c1 = *(const f32x4 *)&s.Cq[32 * q + 8 * g + 4];
-        const f32x4 a = acc[q][0], b = acc[q][1];
-        yp = fmaf(a.x, c0.x, yp);
-        yp = fmaf(a.y, c0.y, yp);
-        yp = fmaf(a.z, c0.z, yp);
-        yp = fmaf(a.w, c0.w, yp);
-        yp = fmaf(b.x, c1.x, yp);
-        yp = fmaf(b.y, c1.y, yp);
-        yp = fmaf(b.z, c1.z, yp);
-        yp = fmaf(b.w, c1.w, yp);
-    }
-    yp += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(yp), 0x401F));  // xor 16
-    yp += __shfl_xor(yp, 32, 64);
-    if (g == 0 && prow) io.y[bh * Ld.P + pl] = fmaf(Ld.D[t.h], s.xw[k - 1][pl], yp);
+    if constexpr (F8M) write_output();
 
     // 8. Pointers (the token's record is folded already: nothing is appended).
     if (uni) {
