@@ -303,10 +303,20 @@ __device__ inline void store_rows_f32(float *rows, const f32x4 (&vf)[GF::NL], in
 
 // Master rows in f32 geometry: fp32 16-byte loads, fp16 8-byte loads converted exactly, or fp8
 // codes (4 per lane and row, from the head's 16-byte chunks) decoded and times the head's scale.
+// F32M: the caller knows the master is fp32 (fp32 read path, all-flush launches), so the other
+// formats' code is not compiled in (it would raise the kernel's register count).
+template <bool F32M = false>
 __device__ inline void load_master_rows(const Layer &Ld, size_t elem0, f32x4 (&vf)[GF::NL], int nrows, int wave,
                                         int lane)
 {
     const int c = lane % GF::LPR;
+    if (F32M || Ld.mprec == MASTER_F32) {
+        u32x4 m[GF::NL];
+        load_rows<PREC_F32>(m, (const char *)(Ld.master + elem0), nrows, wave, lane);
+#pragma unroll
+        for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(m[i]);
+        return;
+    }
     if (Ld.mprec >= MASTER_F8) {
         const size_t bh = elem0 / ((size_t)Ld.P * NN);
         const int row0 = (int)(elem0 / NN - bh * (size_t)Ld.P);
@@ -324,20 +334,13 @@ __device__ inline void load_master_rows(const Layer &Ld, size_t elem0, f32x4 (&v
         }
         return;
     }
-    if (Ld.mprec == MASTER_F32) {
-        u32x4 m[GF::NL];
-        load_rows<PREC_F32>(m, (const char *)(Ld.master + elem0), nrows, wave, lane);
+    const unsigned short *base = (const unsigned short *)Ld.master + elem0;
 #pragma unroll
-        for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(m[i]);
-    } else {
-        const unsigned short *base = (const unsigned short *)Ld.master + elem0;
-#pragma unroll
-        for (int i = 0; i < GF::NL; ++i) {
-            const int r = row_of<PREC_F32>(i, wave, lane), rr = r < nrows ? r : 0;
-            const u32x2 w = __builtin_nontemporal_load((const u32x2 *)(base + (size_t)rr * NN + 4 * c));
-            const f32x2 lo = f16x2_to_f32(w.x), hi = f16x2_to_f32(w.y);
-            vf[i] = f32x4{lo.x, lo.y, hi.x, hi.y};
-        }
+    for (int i = 0; i < GF::NL; ++i) {
+        const int r = row_of<PREC_F32>(i, wave, lane), rr = r < nrows ? r : 0;
+        const u32x2 w = __builtin_nontemporal_load((const u32x2 *)(base + (size_t)rr * NN + 4 * c));
+        const f32x2 lo = f16x2_to_f32(w.x), hi = f16x2_to_f32(w.y);
+        vf[i] = f32x4{lo.x, lo.y, hi.x, hi.y};
     }
 }
 
@@ -439,10 +442,15 @@ __device__ inline void store_master_fp8_rows(const Layer &Ld, int b, size_t bh, 
 // Commit a head's folded rows: store them at the master's precision (vf then holds the stored
 // values) and refresh the read copy from them -- or, with an fp8 master, which is its own read
 // copy, encode them once.
-template <int PREC>
+template <int PREC, bool F32M = false>
 __device__ inline void commit_rows(const Layer &Ld, int b, size_t bh, size_t elem0, int newck, bool stochastic,
                                    f32x4 (&vf)[GF::NL], int nrows, int wave, int lane, float *red)
 {
+    if constexpr (F32M) {  // the launch guarantees an fp32 master: no rounding code compiled in
+        store_rows_f32(Ld.master + elem0, vf, nrows, wave, lane);
+        write_copy_rows<PREC>(Ld, bh, elem0, vf, nrows, wave, lane, red);
+        return;
+    }
     if constexpr (PREC == PREC_FP8)
         if (Ld.mprec >= MASTER_F8) {
             store_master_fp8_rows(Ld, b, bh, elem0, newck, stochastic, vf, nrows, wave, lane, red);
@@ -570,6 +578,9 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     // checkpoint bytes in flight as one fp32 head gives.
     constexpr bool kHalfPre = FLUSH && HPB == 2;
     constexpr bool kAll = FLUSH == 2;
+    // fp32 master known at compile time: all-flush launches (host-checked) and the fp32 read path
+    // (an fp16 or fp8 master is read through the F16 / FP8 kernels)
+    constexpr bool kF32M = kAll || PREC == PREC_F32;
     static_assert(!kAll || (HPB == 1 && !kPreload), "all-flush launches: one head, master rows issued early");
     f32x4 mf[kAll ? GF::NL : 1];
     u32x2 mh[kHalfPre ? HPB : 1][GF::NL];
@@ -675,7 +686,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
         issue_window();
         if constexpr (MIX) issue_mix(ls.rslot);
         if (kPreload) load_state();
-        if constexpr (kAll) load_master_rows(Ld, (bh0 * Ld.P + t.row0) * NN, mf, t.nrows, wave, lane);
+        if constexpr (kAll) load_master_rows<true>(Ld, (bh0 * Ld.P + t.row0) * NN, mf, t.nrows, wave, lane);
     } else {
         // checkpoint stream first; the window addresses wait for this sequence's pointers
         if (kPreload) load_state();
@@ -812,10 +823,10 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
 #pragma unroll
                 for (int i = 0; i < GF::NL; ++i) vf[i] = mf[i];
             } else {
-                load_master_rows(Ld, elem0, vf, t.nrows, wave, lane);
+                load_master_rows<kF32M>(Ld, elem0, vf, t.nrows, wave, lane);
             }
             fold_head<LMAX, ROWS>(vf, s.xw, s.Bw, s.w[hh], s.decay[hh], hh * kRows, k, wave, lane);
-            commit_rows<PREC>(Ld, t.b, bh0 + hh, elem0, dpos + 1, sr_master(Ld), vf, t.nrows, wave, lane, s.red);
+            commit_rows<PREC, kF32M>(Ld, t.b, bh0 + hh, elem0, dpos + 1, sr_master(Ld), vf, t.nrows, wave, lane, s.red);
             float part[GF::NL];
 #pragma unroll
             for (int i = 0; i < GF::NL; ++i) part[i] = chunk_dot<PREC_F32>(as_u32x4(vf[i]), cf);
@@ -1870,7 +1881,7 @@ __global__ void __launch_bounds__(kThreads) load_state_kernel(Layer Ld, const fl
     f32x4 vf[GF::NL];
 #pragma unroll
     for (int i = 0; i < GF::NL; ++i) vf[i] = as_f32x4(m[i]);
-    commit_rows<PREC>(Ld, t.b, bh, elem0, 0, false, vf, t.nrows, wave, lane, red);  // nearest even at load
+    commit_rows<PREC, PREC == PREC_F32>(Ld, t.b, bh, elem0, 0, false, vf, t.nrows, wave, lane, red);  // nearest even at load
     if (t.h == 0 && t.split == 0 && threadIdx.x == 0) {
         Ld.pos[t.b] = 0;
         Ld.ckpt[t.b] = 0;
