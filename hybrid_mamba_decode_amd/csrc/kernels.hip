@@ -532,7 +532,8 @@ __device__ inline Tile map_heads(const Layer &Ld, int hpb)
 
 // FLUSH: 0 = no sequence of the launch flushes; 1 = some may (their buffer fills); 2 = every
 // sequence flushes (a lockstep flush step with an fp32 master and a narrow read copy: the master
-// rows are issued right behind the window, and the replay path is not compiled in).
+// rows are issued right behind the window, and the replay path is not compiled in); 3 = as 1 with
+// a narrow read copy and an fp32 master (the master code carries no fp16 / fp8-master paths).
 template <int PREC, int LMAX, int ROWS, int FLUSH, bool MIX>
 __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lockstep ls)
 {
@@ -580,7 +581,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(Layer Ld, TokenIO io, Lo
     constexpr bool kAll = FLUSH == 2;
     // fp32 master known at compile time: all-flush launches (host-checked) and the fp32 read path
     // (an fp16 or fp8 master is read through the F16 / FP8 kernels)
-    constexpr bool kF32M = kAll || PREC == PREC_F32;
+    constexpr bool kF32M = FLUSH >= 2 || PREC == PREC_F32;
     static_assert(!kAll || (HPB == 1 && !kPreload), "all-flush launches: one head, master rows issued early");
     f32x4 mf[kAll ? GF::NL : 1];
     u32x2 mh[kHalfPre ? HPB : 1][GF::NL];
@@ -2114,7 +2115,10 @@ hipError_t step_t(const Layer &Ld, const TokenIO &io, bool flush_capable, bool a
                 return step_rows<PREC, LMAX, 2 * kRows, true, MIX>(Ld, io, ls, st);
         // lockstep flush step, fp32 master, narrow copy: every sequence flushes
         if constexpr (PREC == PREC_BF16 || PREC == PREC_FP8 || PREC == PREC_FP4)
-            if (ls.k > 0 && Ld.mprec == MASTER_F32) return step_rows<PREC, LMAX, kRows, 2, MIX>(Ld, io, ls, st);
+            if (Ld.mprec == MASTER_F32) {
+                if (ls.k > 0) return step_rows<PREC, LMAX, kRows, 2, MIX>(Ld, io, ls, st);
+                return step_rows<PREC, LMAX, kRows, 3, MIX>(Ld, io, ls, st);
+            }
         return step_rows<PREC, LMAX, kRows, true, MIX>(Ld, io, ls, st);
     }
     if constexpr (!MIX && (PREC == PREC_FP8 || PREC == PREC_FP4) && LMAX == 16 && NN <= 128) {
